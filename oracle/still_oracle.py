@@ -1,0 +1,473 @@
+"""fp64 CPU oracle for one STILL intra-layer hybrid attention layer.
+
+TEST INFRASTRUCTURE ONLY. This module is imported by the tests, by the smoke check and
+by the CPU-baseline leg of the benchmark. The library (the HIP path behind the C ABI)
+never imports, links or calls it, and it shares no code with that path.
+
+Pages cited below (the method's only description):
+  [P1] "仅0.04B！哈工深首创同层混合架构STILL，极低成本线性化LLM" (PaperWeekly repost),
+       sections "Self-Saliency Score", "Norm-Preserved Feature Map（NP-Map）",
+       "Chunk-Wise并行+延迟选择", and the paragraph before "STILL三大创新".
+  [P2] "STILL: Content-Aware Intra-Layer Hybrid Attention Cuts Memory 80%, Speeds
+       Prefill 83%" (picx.dev), summary and the 机器之心 excerpt.
+  [P3] "STILL от HIT Shenzhen: гибридное внимание внутри слоя выбирает токены по
+       содержанию" (news piece), section on why hybrids are called pseudo-hybrid.
+  [P4] "STILL: Selecting Tokens for Intra-Layer Hybrid Attention to Linearize LLMs"
+       (research-map summary), sections Problem and Approach.
+
+Readings taken where the pages are silent (each is exercised by a test):
+  * window W_i = {max(0, i-w+1), ..., i}: length w, causal, contains i itself;
+  * logits a_ij = q_i . k_j / sqrt(D) for both the saliency and the softmax branch;
+  * saliency s_i = KL(q_i || p_i) where p_i is the window softmax with the diagonal and
+    q_i the one without it; this equals -log(1 - p_ii) = LSE(W_i) - LSE(W_i minus i),
+    and is +inf when W_i = {i};
+  * GQA: query head hq uses KV head hq // G (G = Hq / Hkv); routing is per KV head on the
+    sum of the G query heads' saliency;
+  * routing: in every complete chunk of C tokens the top_k largest saliencies are
+    selected, ties to the lower index; a selection affects only queries of later chunks;
+    tokens of an incomplete final chunk are never selected;
+  * token j is in query i's softmax set iff j > i - w, or j lies in an earlier chunk and
+    was selected; every other j <= i goes to linear attention;
+  * NP-Map phi(x) = |x| * m / |m|,  m = elu(W_h x) + 1 (alpha = 1), W_h [d_f, D] per KV
+    head, shared by queries and keys; phi(0) = 0;
+  * fusion with one shared normaliser:
+      o_i = (sum_SA e^{a_ij - M} v_j + e^{-M} sum_LA (phi(q_i).phi(k_j)) v_j)
+            / (sum_SA e^{a_ij - M} + e^{-M} sum_LA phi(q_i).phi(k_j)),
+    M = max over the softmax set (0 when that set is empty); o_i = 0 if the denominator is 0.
+
+Parity pins: every function here is pinned in tests/test_oracle_pins.py against closed
+forms, library routines (torch SDPA / ELU in fp64) and hand-derived cases.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "lse", "saliency", "route", "route_margins", "np_map", "sa_mask_row", "brute",
+    "brute_rows", "attend", "DecodeOracle",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def lse(a: np.ndarray, axis: int = -1) -> np.ndarray:
+    """log(sum(exp(a))) along an axis; an all -inf (empty) slice gives -inf."""
+    a = _f64(a)
+    m = np.max(a, axis=axis, keepdims=True)
+    finite = np.isfinite(m)
+    m0 = np.where(finite, m, 0.0)
+    with np.errstate(divide="ignore"):
+        r = np.log(np.sum(np.exp(a - m0), axis=axis, keepdims=True)) + m0
+    r = np.where(finite, r, -np.inf)
+    return np.squeeze(r, axis=axis)
+
+
+def _check_group(Hq: int, Hkv: int) -> int:
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("n_q_heads must be a positive multiple of n_kv_heads")
+    return Hq // Hkv
+
+
+# --------------------------------------------------------------------------------------
+# Self-Saliency Score  ([P1] section "Self-Saliency Score"; [P4] section Approach)
+# --------------------------------------------------------------------------------------
+
+def _saliency_one_head(q: np.ndarray, k: np.ndarray, window: int) -> np.ndarray:
+    """s_i for one query head: q [T,D], k [T,D] -> [T].
+
+    Token i attends over its causal window once with and once without its own (diagonal)
+    key; the divergence between the two window distributions is its saliency. In log-sum-
+    exp form: s_i = LSE_{j in W_i} a_ij - LSE_{j in W_i, j != i} a_ij.
+    """
+    T, D = q.shape
+    a = np.full((T, window), -np.inf)  # a[i, o] = a_{i, i-o}; o = 0 is the diagonal
+    for o in range(min(window, T)):
+        a[o:, o] = np.einsum("td,td->t", q[o:], k[: T - o]) / math.sqrt(D)
+    with_diag = lse(a, axis=1)
+    without_diag = lse(a[:, 1:], axis=1) if window > 1 else np.full(T, -np.inf)
+    return with_diag - without_diag  # -inf subtracted -> +inf for a one-token window
+
+
+def saliency(q, k, window: int):
+    """Self-Saliency Score per query head and per KV head.
+
+    q [B,T,Hq,D], k [B,T,Hkv,D] -> (s_kv [B,Hkv,T], s_q [B,Hq,T]); s_kv sums the G query
+    heads of each group (reading for GQA, module header).
+    """
+    q, k = _f64(q), _f64(k)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = _check_group(Hq, Hkv)
+    if window < 1:
+        raise ValueError("saliency needs a window of at least one token")
+    s_q = np.empty((B, Hq, T))
+    for b in range(B):
+        for hq in range(Hq):
+            s_q[b, hq] = _saliency_one_head(q[b, :, hq], k[b, :, hq // G], window)
+    s_kv = s_q.reshape(B, Hkv, G, T).sum(axis=2)
+    return s_kv, s_q
+
+
+# --------------------------------------------------------------------------------------
+# Chunk-wise routing  ([P1] section "Chunk-Wise并行+延迟选择"; [P4] section Approach)
+# --------------------------------------------------------------------------------------
+
+def route(s_kv, chunk: int, top_k: int):
+    """Per complete chunk, select the top_k tokens by saliency (ties -> lower index).
+
+    s_kv [B,Hkv,T] -> (sel_idx [B,Hkv,T//chunk,top_k] int64 ascending positions,
+                       sel [B,Hkv,T] bool). Tokens of an incomplete last chunk stay False.
+    """
+    s_kv = _f64(s_kv)
+    B, H, T = s_kv.shape
+    if not (0 <= top_k <= chunk):
+        raise ValueError("top_k must lie in [0, chunk]")
+    n_full = T // chunk
+    sel_idx = np.zeros((B, H, n_full, top_k), dtype=np.int64)
+    sel = np.zeros((B, H, T), dtype=bool)
+    idx = np.arange(chunk)
+    for b in range(B):
+        for h in range(H):
+            for c in range(n_full):
+                seg = s_kv[b, h, c * chunk:(c + 1) * chunk]
+                order = np.lexsort((idx, -seg))  # saliency descending, then index ascending
+                pick = np.sort(order[:top_k]) + c * chunk
+                sel_idx[b, h, c] = pick
+                sel[b, h, pick] = True
+    return sel_idx, sel
+
+
+def route_margins(s_kv, chunk: int, top_k: int) -> np.ndarray:
+    """Per complete chunk, the gap between the k-th and (k+1)-th largest saliency.
+
+    [B,Hkv,T//chunk]; +inf when top_k is 0 or chunk (no competing token), and 0 on ties.
+    A selection whose margin exceeds a device's saliency error is unique on that device.
+    """
+    s_kv = _f64(s_kv)
+    B, H, T = s_kv.shape
+    n_full = T // chunk
+    out = np.full((B, H, n_full), np.inf)
+    if top_k == 0 or top_k == chunk:
+        return out
+    for b in range(B):
+        for h in range(H):
+            for c in range(n_full):
+                seg = np.sort(s_kv[b, h, c * chunk:(c + 1) * chunk])[::-1]
+                hi, lo = seg[top_k - 1], seg[top_k]
+                if np.isinf(hi):
+                    out[b, h, c] = 0.0 if np.isinf(lo) else np.inf
+                else:
+                    out[b, h, c] = hi - lo
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# NP-Map  ([P1] section "Norm-Preserved Feature Map（NP-Map）"; [P4] section Approach)
+# --------------------------------------------------------------------------------------
+
+def np_map(x, w) -> np.ndarray:
+    """phi(x) = |x|_2 * m / |m|_2 with m = elu(W x) + 1.
+
+    The map keeps the direction from a one-layer positive feature map and puts back the
+    original vector's norm. x [..., D], w [d_f, D] -> [..., d_f]. m > 0 elementwise, so the
+    division is always defined, and phi(0) = 0.
+    """
+    x, w = _f64(x), _f64(w)
+    z = x @ w.T
+    m = np.where(z > 0.0, z + 1.0, np.exp(np.minimum(z, 0.0)))  # elu(z) + 1, alpha = 1
+    nx = np.linalg.norm(x, axis=-1, keepdims=True)
+    nm = np.linalg.norm(m, axis=-1, keepdims=True)
+    return nx * m / nm
+
+
+# --------------------------------------------------------------------------------------
+# Partition and fused output  ([P1] paragraph before "STILL三大创新" and section NP-Map;
+# [P2] excerpt; [P3] on linear attention's fixed-size state)
+# --------------------------------------------------------------------------------------
+
+def sa_mask_row(i: int, window: int, chunk: int, sel_row: np.ndarray) -> np.ndarray:
+    """Softmax-set membership of keys j = 0..i for query i (bool [i+1])."""
+    j = np.arange(i + 1)
+    in_window = j > i - window
+    selected_past = (j // chunk < i // chunk) & sel_row[: i + 1]
+    return in_window | selected_past
+
+
+def _check_cfg(window: int, chunk: int, top_k: int):
+    if window < 0 or chunk < 1 or not (0 <= top_k <= chunk):
+        raise ValueError("bad window/chunk/top_k")
+    if window == 0 and top_k != 0:
+        raise ValueError("a zero window has no saliency, so top_k must be 0")
+
+
+def _routing(q, k, window, chunk, top_k, sel):
+    B, T, _, _ = q.shape
+    Hkv = k.shape[2]
+    if sel is not None:
+        return np.asarray(sel, dtype=bool)
+    if top_k == 0:
+        return np.zeros((B, Hkv, T), dtype=bool)
+    s_kv, _ = saliency(q, k, window)
+    return route(s_kv, chunk, top_k)[1]
+
+
+def _row(qi, phiq_i, kk, vv, phik, sa, D):
+    """Output of one query row given its softmax-set mask over keys 0..i."""
+    a = kk @ qi / math.sqrt(D)
+    la = ~sa
+    M = a[sa].max() if sa.any() else 0.0
+    w_sa = np.exp(a[sa] - M)
+    w_la = math.exp(-M) * (phik[la] @ phiq_i)
+    num = w_sa @ vv[sa] + w_la @ vv[la]
+    den = w_sa.sum() + w_la.sum()
+    return num / den if den > 0.0 else np.zeros(vv.shape[1])
+
+
+def brute(q, k, v, w_phi, window: int, chunk: int, top_k: int, sel=None) -> np.ndarray:
+    """Literal per-query form: for every (i, j <= i) decide SA or LA, then fuse.
+
+    q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] -> out [B,T,Hq,D] fp64.
+    sel [B,Hkv,T] bool overrides the saliency routing when given.
+    """
+    _check_cfg(window, chunk, top_k)
+    q, k, v, w_phi = _f64(q), _f64(k), _f64(v), _f64(w_phi)
+    B, T, Hq, D = q.shape
+    G = _check_group(Hq, k.shape[2])
+    sel = _routing(q, k, window, chunk, top_k, sel)
+    out = np.zeros_like(q)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            phiq = np_map(q[b, :, hq], w_phi[h])
+            phik = np_map(k[b, :, h], w_phi[h])
+            for i in range(T):
+                sa = sa_mask_row(i, window, chunk, sel[b, h])
+                out[b, i, hq] = _row(q[b, i, hq], phiq[i], k[b, : i + 1, h], v[b, : i + 1, h],
+                                     phik[: i + 1], sa, D)
+    return out
+
+
+def brute_rows(q, k, v, w_phi, window: int, chunk: int, sel, rows) -> np.ndarray:
+    """The literal per-query form for selected rows only.
+
+    rows: iterable of (b, hq, i). Returns [len(rows), D]. sel [B,Hkv,T] bool is required
+    (compute it once with saliency + route for long sequences).
+    """
+    q, k, v, w_phi = _f64(q), _f64(k), _f64(v), _f64(w_phi)
+    _, _, Hq, D = q.shape
+    G = _check_group(Hq, k.shape[2])
+    sel = np.asarray(sel, dtype=bool)
+    res = []
+    for (b, hq, i) in rows:
+        h = hq // G
+        phiq_i = np_map(q[b, i, hq], w_phi[h])
+        phik = np_map(k[b, : i + 1, h], w_phi[h])
+        sa = sa_mask_row(i, window, chunk, sel[b, h])
+        res.append(_row(q[b, i, hq], phiq_i, k[b, : i + 1, h], v[b, : i + 1, h], phik, sa, D))
+    return np.array(res)
+
+
+def attend(q, k, v, w_phi, window: int, chunk: int, top_k: int, sel=None,
+           heads=None, return_routing: bool = False):
+    """Chunk-wise form of the same layer ([P1] section "Chunk-Wise并行+延迟选择").
+
+    Queries are taken one chunk at a time. Keys lying before the first window position of
+    the chunk (j <= i0 - w) are outside every window of the chunk: the selected ones join
+    the softmax set, the others are summed once into the linear-attention state
+    S = sum phi(k_j) v_j^T, z = sum phi(k_j). Keys from there up to the chunk's end get a
+    per-query mask. Output as in brute(); the two agree to rounding.
+
+    heads: optional list of query-head indices to compute (others are left zero).
+    Returns out [B,T,Hq,D] (and (s_kv, sel) if return_routing).
+    """
+    _check_cfg(window, chunk, top_k)
+    q, k, v, w_phi = _f64(q), _f64(k), _f64(v), _f64(w_phi)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = _check_group(Hq, Hkv)
+    F = w_phi.shape[1]
+    s_kv = None
+    if sel is None and top_k > 0:
+        s_kv, _ = saliency(q, k, window)
+        sel = route(s_kv, chunk, top_k)[1]
+    elif sel is None:
+        sel = np.zeros((B, Hkv, T), dtype=bool)
+    sel = np.asarray(sel, dtype=bool)
+    out = np.zeros_like(q)
+    n_chunks = -(-T // chunk)
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for hq in (range(Hq) if heads is None else heads):
+            h = hq // G
+            kk, vv = k[b, :, h], v[b, :, h]
+            phik = np_map(kk, w_phi[h])
+            sel_h = sel[b, h]
+            S = np.zeros((F, D))
+            z = np.zeros(F)
+            folded = 0
+            for c in range(n_chunks):
+                i0, i1 = c * chunk, min(T, (c + 1) * chunk)
+                far_end = max(0, i0 - window + 1)  # keys [0, far_end) are out of every window
+                new = np.arange(folded, far_end)
+                la_new = new[~sel_h[new]]
+                S += phik[la_new].T @ vv[la_new]
+                z += phik[la_new].sum(axis=0)
+                folded = far_end
+                sa_far = np.flatnonzero(sel_h[:far_end])
+                near = np.arange(far_end, i1)
+                Qc = q[b, i0:i1, hq]
+                phiq = np_map(Qc, w_phi[h])
+                I = np.arange(i0, i1)[:, None]
+                J = near[None, :]
+                visible = J <= I
+                sa_near = visible & ((J > I - window) | ((J // chunk < c) & sel_h[near][None, :]))
+                la_near = visible & ~sa_near
+                a_far = Qc @ kk[sa_far].T * inv_sqrt_d
+                a_near = np.where(sa_near, Qc @ kk[near].T * inv_sqrt_d, -np.inf)
+                M = np.maximum(a_far.max(axis=1, initial=-np.inf), a_near.max(axis=1, initial=-np.inf))
+                M = np.where(np.isfinite(M), M, 0.0)[:, None]
+                e_far = np.exp(a_far - M)
+                e_near = np.where(sa_near, np.exp(a_near - M), 0.0)
+                lw_near = np.where(la_near, phiq @ phik[near].T, 0.0)
+                scale_la = np.exp(-M)
+                num = e_far @ vv[sa_far] + e_near @ vv[near] + scale_la * (phiq @ S + lw_near @ vv[near])
+                den = (e_far.sum(axis=1) + e_near.sum(axis=1))[:, None] + \
+                    scale_la * ((phiq @ z) + lw_near.sum(axis=1))[:, None]
+                safe = den > 0.0
+                out[b, i0:i1, hq] = np.where(safe, num / np.where(safe, den, 1.0), 0.0)
+    if return_routing:
+        return out, s_kv, sel
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Decode with chunk-granular delayed selection  ([P1] section "Chunk-Wise并行+延迟选择";
+# [P4] section Approach; [P3] on the fixed-size state of linear attention)
+# --------------------------------------------------------------------------------------
+
+class DecodeOracle:
+    """Token-by-token replay of the layer with an explicit decode state.
+
+    State per (batch, KV head): a compact list of selected tokens from chunks <= c-2 (the
+    softmax cache), the raw keys/values of chunks c-1 and c (the ring), the selection of
+    chunk c-1, the running saliency of chunk c, and the linear-attention state (S, z) of
+    every unselected token of chunks <= c-2. When a chunk completes, its top_k tokens are
+    chosen, and the chunk before it is folded: selected rows join the cache, the rest join
+    (S, z). Needs 1 <= window <= chunk (or window = 0 with top_k = 0).
+    """
+
+    def __init__(self, w_phi, n_q_heads: int, window: int, chunk: int, top_k: int):
+        _check_cfg(window, chunk, top_k)
+        if window > chunk:
+            raise ValueError("the decode state holds two chunks, so window <= chunk")
+        self.w = _f64(w_phi)
+        self.Hkv, self.F, self.D = self.w.shape
+        self.Hq = n_q_heads
+        self.G = _check_group(n_q_heads, self.Hkv)
+        self.window, self.chunk, self.top_k = window, chunk, top_k
+        self.B = None
+        self.t = 0
+
+    def _init(self, B):
+        H, D, F, C = self.Hkv, self.D, self.F, self.chunk
+        self.B = B
+        self.cache_k = [[np.zeros((0, D)) for _ in range(H)] for _ in range(B)]
+        self.cache_v = [[np.zeros((0, D)) for _ in range(H)] for _ in range(B)]
+        self.S = np.zeros((B, H, F, D))
+        self.z = np.zeros((B, H, F))
+        self.ring_k = np.zeros((B, H, 2, C, D))  # [.., 0] = chunk c-1, [.., 1] = chunk c
+        self.ring_v = np.zeros((B, H, 2, C, D))
+        self.prev_sel = np.zeros((B, H, C), dtype=bool)
+        self.cur_s = np.zeros((B, H, C))
+        self.sel_idx = []  # per completed chunk: [B,H,top_k] absolute positions
+
+    def step(self, q_t, k_t, v_t) -> np.ndarray:
+        """q_t [B,Hq,D], k_t/v_t [B,Hkv,D] for token i = self.t -> out [B,Hq,D]."""
+        q_t, k_t, v_t = _f64(q_t), _f64(k_t), _f64(v_t)
+        B = q_t.shape[0]
+        if self.B is None:
+            self._init(B)
+        C, w, D, G = self.chunk, self.window, self.D, self.G
+        i = self.t
+        c, r = divmod(i, C)
+        self.ring_k[:, :, 1, r] = k_t
+        self.ring_v[:, :, 1, r] = v_t
+        out = np.zeros((B, self.Hq, D))
+        inv = 1.0 / math.sqrt(D)
+        for b in range(B):
+            for h in range(self.Hkv):
+                W = self.w[h]
+                # keys of chunk c-1 (only if it exists) and chunk c up to i
+                prev_k = self.ring_k[b, h, 0] if c > 0 else np.zeros((0, D))
+                prev_v = self.ring_v[b, h, 0] if c > 0 else np.zeros((0, D))
+                cur_k = self.ring_k[b, h, 1, : r + 1]
+                cur_v = self.ring_v[b, h, 1, : r + 1]
+                p_prev = np.arange(prev_k.shape[0])
+                sa_prev = (p_prev > r + C - w) | self.prev_sel[b, h, : prev_k.shape[0]]
+                p_cur = np.arange(r + 1)
+                sa_cur = p_cur > r - w
+                ck, cv = self.cache_k[b][h], self.cache_v[b][h]
+                s_sum = 0.0
+                for g in range(G):
+                    qv = q_t[b, h * G + g]
+                    # saliency of token i over its window (all inside the ring)
+                    if w >= 1:
+                        win_prev = prev_k[p_prev > r + C - w]
+                        win_cur = cur_k[p_cur > r - w]
+                        logits = np.concatenate([win_prev @ qv, win_cur @ qv]) * inv
+                        rest = logits[:-1]  # the window without the diagonal (last entry)
+                        s_sum += lse(logits) - (lse(rest) if rest.size else -np.inf)
+                    phiq = np_map(qv, W)
+                    keys_sa = np.concatenate([ck, prev_k[sa_prev], cur_k[sa_cur]])
+                    vals_sa = np.concatenate([cv, prev_v[sa_prev], cur_v[sa_cur]])
+                    keys_la = np.concatenate([prev_k[~sa_prev], cur_k[~sa_cur]])
+                    vals_la = np.concatenate([prev_v[~sa_prev], cur_v[~sa_cur]])
+                    a = keys_sa @ qv * inv
+                    M = a.max() if a.size else 0.0
+                    e = np.exp(a - M)
+                    lw = np_map(keys_la, W) @ phiq if keys_la.size else np.zeros(0)
+                    num = e @ vals_sa + math.exp(-M) * (phiq @ self.S[b, h] + lw @ vals_la)
+                    den = e.sum() + math.exp(-M) * (phiq @ self.z[b, h] + lw.sum())
+                    out[b, h * G + g] = num / den if den > 0.0 else 0.0
+                self.cur_s[b, h, r] = s_sum
+        self.t += 1
+        if r == C - 1:
+            self._complete_chunk(c)
+        return out
+
+    def _complete_chunk(self, c: int):
+        C, k = self.chunk, self.top_k
+        B, H = self.B, self.Hkv
+        # fold chunk c-1: selected rows -> softmax cache, the rest -> (S, z)
+        if c > 0:
+            for b in range(B):
+                for h in range(H):
+                    sel = self.prev_sel[b, h]
+                    pk, pv = self.ring_k[b, h, 0], self.ring_v[b, h, 0]
+                    self.cache_k[b][h] = np.concatenate([self.cache_k[b][h], pk[sel]])
+                    self.cache_v[b][h] = np.concatenate([self.cache_v[b][h], pv[sel]])
+                    phik = np_map(pk[~sel], self.w[h])
+                    self.S[b, h] += phik.T @ pv[~sel]
+                    self.z[b, h] += phik.sum(axis=0)
+        # select the top_k of chunk c by its saliency
+        idx = np.arange(C)
+        new_sel = np.zeros((B, H, C), dtype=bool)
+        picks = np.zeros((B, H, k), dtype=np.int64)
+        for b in range(B):
+            for h in range(H):
+                order = np.lexsort((idx, -self.cur_s[b, h]))
+                pick = np.sort(order[:k])
+                new_sel[b, h, pick] = True
+                picks[b, h] = pick + c * C
+        self.sel_idx.append(picks)
+        self.prev_sel = new_sel
+        self.ring_k[:, :, 0] = self.ring_k[:, :, 1]
+        self.ring_v[:, :, 0] = self.ring_v[:, :, 1]
+        self.ring_k[:, :, 1] = 0.0
+        self.ring_v[:, :, 1] = 0.0
+        self.cur_s[:] = 0.0
