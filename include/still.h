@@ -1,0 +1,183 @@
+/*
+ * still.h -- C ABI of an MI355X (gfx950) implementation of one STILL intra-layer hybrid
+ * attention layer: self-saliency routing, softmax attention over the local window plus
+ * the routed tokens, NP-Map linear attention over every other past token, one fused
+ * output.
+ *
+ * Pages that define the operation:
+ *   [P1] "仅0.04B！哈工深首创同层混合架构STILL，极低成本线性化LLM" (PaperWeekly repost):
+ *        sections "Self-Saliency Score", "Norm-Preserved Feature Map（NP-Map）",
+ *        "Chunk-Wise并行+延迟选择", and the paragraph before "STILL三大创新".
+ *   [P4] "STILL: Selecting Tokens for Intra-Layer Hybrid Attention to Linearize LLMs"
+ *        (research-map summary), section Approach.
+ *
+ * The pages leave these points open; the library fixes them as follows.
+ *   window      W_i = {max(0, i-w+1) .. i}, causal, contains i.
+ *   logits      a_ij = q_i . k_j / sqrt(head_dim), for saliency and the softmax branch.
+ *   saliency    s_i = KL(no-diagonal window softmax || window softmax) = -log(1 - p_ii),
+ *               +inf for a one-token window; per KV head, the G = n_q_heads/n_kv_heads
+ *               query heads of the group are summed in order g = 0..G-1 (query head hq
+ *               belongs to KV head hq / G).
+ *   routing     each complete chunk of `chunk` tokens selects its top_k tokens by s, ties
+ *               to the lower position; the selection is used only by later chunks; an
+ *               incomplete final chunk is never selected.
+ *   partition   key j <= i is in query i's softmax set iff j > i - w, or j lies in an
+ *               earlier chunk and was selected; all other keys go to linear attention.
+ *   NP-Map      phi(x) = |x| * m / |m|, m = elu(W_h x) + 1 (alpha 1), W_h [feat_dim,
+ *               head_dim] per KV head, shared by queries and keys.
+ *   output      o_i = (sum_SA e^{a_ij} v_j + sum_LA (phi(q_i).phi(k_j)) v_j)
+ *                     / (sum_SA e^{a_ij} + sum_LA phi(q_i).phi(k_j))     (shared normaliser);
+ *               0 if the denominator is 0 (only possible with window 0 and q_i = 0).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are device memory owned by the caller, 16-byte aligned, contiguous
+ *     in the stated layout, and are not retained after the call returns.
+ *   - The library never allocates device memory and never synchronises: all work is
+ *     enqueued on `stream`, so results are ready when the stream reaches them.
+ *   - Validation errors are returned before anything is enqueued, and no output is
+ *     touched. STILL_ERR_HIP means a launch failed; outputs are then undefined.
+ *   - There is no global state: calls on distinct streams with distinct workspaces and
+ *     caches may run concurrently. Calls sharing a workspace or cache must be ordered.
+ */
+#ifndef STILL_H
+#define STILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, w_phi and out. */
+typedef enum still_dtype { STILL_F32 = 0, STILL_BF16 = 1 } still_dtype;
+
+/* Status codes (0 = success). */
+enum {
+  STILL_OK = 0,
+  STILL_ERR_INVALID_ARG = -1,         /* null / misaligned pointer, inconsistent sizes */
+  STILL_ERR_UNSUPPORTED = -2,         /* valid layer, but not a shape these kernels cover */
+  STILL_ERR_WORKSPACE_TOO_SMALL = -3,
+  STILL_ERR_CACHE_FULL = -4,          /* decode cache holds max_tokens tokens already */
+  STILL_ERR_CACHE_MISMATCH = -5,      /* cache built for another configuration */
+  STILL_ERR_HIP = -6
+};
+
+/* Layer configuration. Supported by the kernels: chunk = 64; head_dim in {64, 128};
+ * feat_dim in {64, 128}; 0 <= window <= chunk; 0 <= top_k <= chunk; top_k = 0 when
+ * window = 0; n_q_heads a multiple of n_kv_heads; any seq_len >= 1. STILL_F32 is
+ * supported with head_dim = feat_dim = 64 (the reference-precision path). */
+typedef struct still_config {
+  int32_t batch;
+  int32_t seq_len;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t feat_dim;
+  int32_t window;
+  int32_t chunk;
+  int32_t top_k;
+  int32_t dtype; /* still_dtype */
+} still_config;
+
+/* Decode state for batched token-by-token generation with chunk-delayed selection
+ * ([P1] section "Chunk-Wise并行+延迟选择"). A host-side record of device sub-buffers
+ * carved from one caller buffer by still_cache_init. Fields are read-only for callers.
+ * With c the chunk of the next token: sel_k/sel_v hold the selected rows of chunks
+ * <= c-2 in (chunk, position) order; ring_k/ring_v hold the raw rows of chunks c-1 and
+ * c (chunk j in slot j % 2); state_s/state_z hold the linear-attention state
+ * sum phi(k) v^T and sum phi(k) over the unselected tokens of chunks <= c-2. */
+typedef struct still_cache {
+  still_config cfg;     /* configuration the cache was built for (seq_len ignored) */
+  int64_t max_tokens;   /* capacity per sequence */
+  int64_t n_tokens;     /* tokens held per sequence = position of the next token */
+  int64_t sel_capacity; /* rows per (batch, KV head) in sel_k / sel_v */
+  void* sel_k;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype */
+  void* sel_v;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype */
+  void* ring_k;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
+  void* ring_v;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
+  float* state_s;       /* [batch, n_kv_heads, feat_dim, head_dim] fp32 */
+  float* state_z;       /* [batch, n_kv_heads, feat_dim] fp32 */
+  uint64_t* sel_mask;   /* [batch, n_kv_heads, 2] selection bit masks of ring slots */
+  float* cur_saliency;  /* [batch, n_kv_heads, chunk] saliency of the current chunk */
+} still_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char* still_status_string(int status);
+
+/* Bytes of scratch still_prefill needs for `cfg` (0 if cfg is invalid). */
+size_t still_prefill_workspace_bytes(const still_config* cfg);
+
+/* One causal STILL layer over a whole sequence (prefill).
+ *   q      [batch, seq_len, n_q_heads, head_dim]   dtype
+ *   k, v   [batch, seq_len, n_kv_heads, head_dim]  dtype   (post-RoPE keys/values)
+ *   w_phi  [n_kv_heads, feat_dim, head_dim]        dtype   (NP-Map weight per KV head)
+ *   out    [batch, seq_len, n_q_heads, head_dim]   dtype   (written, RNE for bf16)
+ *   routing_in    optional [batch, n_kv_heads, seq_len/chunk, top_k] int32: if non-null,
+ *                 these ascending, distinct in-chunk positions replace the saliency
+ *                 selection (an override for testing the attention alone; entries outside
+ *                 their chunk are ignored, which leaves that slot's softmax row undefined).
+ *   saliency_out  optional [batch, n_kv_heads, seq_len] fp32: the group-summed saliency
+ *                 (requires window >= 1).
+ *   sel_idx_out   optional [batch, n_kv_heads, seq_len/chunk, top_k] int32: the selected
+ *                 positions of every complete chunk, ascending.
+ *   cache         optional: if non-null, a cache from still_cache_init for this config
+ *                 with n_tokens == 0; it is left holding the state after seq_len tokens.
+ *   workspace     device scratch of at least still_prefill_workspace_bytes(cfg) bytes.
+ * Returns STILL_OK or a negative status. */
+int still_prefill(const still_config* cfg, const void* q, const void* k, const void* v,
+                  const void* w_phi, void* out, const int32_t* routing_in,
+                  float* saliency_out, int32_t* sel_idx_out, still_cache* cache,
+                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* still_prefill with timing events: if `events` is non-null it must hold 4 events created
+ * by the caller; they are recorded on `stream` before the per-chunk preparation kernel,
+ * before the chunk-state scan, before the fused attention kernel and after it, so
+ * hipEventElapsedTime between consecutive events gives each kernel's duration. */
+int still_prefill_timed(const still_config* cfg, const void* q, const void* k, const void* v,
+                        const void* w_phi, void* out, const int32_t* routing_in,
+                        float* saliency_out, int32_t* sel_idx_out, still_cache* cache,
+                        void* workspace, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* events);
+
+/* The per-chunk top-k alone: saliency [batch, n_kv_heads, seq_len] fp32 (device) ->
+ * sel_idx_out [batch, n_kv_heads, seq_len/chunk, top_k] int32, ascending positions,
+ * ties to the lower position ([P1] section "Chunk-Wise并行+延迟选择"). */
+int still_select_topk(const still_config* cfg, const float* saliency, int32_t* sel_idx_out,
+                      hipStream_t stream);
+
+/* The NP-Map alone ([P1] section "Norm-Preserved Feature Map（NP-Map）"; [P4] section
+ * Approach): x [batch, seq_len, n_kv_heads, head_dim] dtype -> phi_out [batch, seq_len,
+ * n_kv_heads, feat_dim] fp32, with W_h = w_phi[h]. */
+int still_feature_map(const still_config* cfg, const void* x, const void* w_phi,
+                      float* phi_out, hipStream_t stream);
+
+/* Bytes of device memory a decode cache of `max_tokens` tokens per sequence needs. */
+size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens);
+
+/* Carve a cache from `dev_buf` (>= still_cache_bytes bytes) and clear it on `stream`.
+ * Fills *out; n_tokens starts at 0. */
+int still_cache_init(const still_config* cfg, int64_t max_tokens, void* dev_buf,
+                     size_t bytes, still_cache* out, hipStream_t stream);
+
+/* Bytes of scratch still_decode_step needs for `cfg` and a cache of max_tokens. */
+size_t still_decode_workspace_bytes(const still_config* cfg, int64_t max_tokens);
+
+/* One generated token for every sequence of the batch, all at position cache->n_tokens
+ * ([P1] section "Chunk-Wise并行+延迟选择": selection delayed to chunk granularity).
+ *   q [batch, n_q_heads, head_dim], k/v [batch, n_kv_heads, head_dim], out like q.
+ * The token's saliency is accumulated; when it completes its chunk, that chunk's top_k
+ * tokens are chosen and the chunk before it is folded: selected rows are appended to the
+ * softmax cache, the others join the linear-attention state. cfg->seq_len is ignored.
+ * Advances cache->n_tokens by one on success. */
+int still_decode_step(const still_config* cfg, still_cache* cache, const void* q,
+                      const void* k, const void* v, const void* w_phi, void* out,
+                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STILL_H */

@@ -1,0 +1,233 @@
+// C ABI of the STILL layer: validation, workspace carving and the launch sequence.
+// Every check happens before anything is enqueued; the library never allocates.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/still.h"
+#include "still_launch.hpp"
+
+using still::Dims;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_cfg(const still_config* c, bool use_seq) {
+  if (!c) return STILL_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1) return STILL_ERR_INVALID_ARG;
+  if (use_seq && c->seq_len < 1) return STILL_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads != 0) return STILL_ERR_INVALID_ARG;
+  if (c->dtype != STILL_F32 && c->dtype != STILL_BF16) return STILL_ERR_INVALID_ARG;
+  if (c->head_dim < 1 || c->feat_dim < 1 || c->chunk < 1) return STILL_ERR_INVALID_ARG;
+  if (c->window < 0 || c->top_k < 0 || c->top_k > c->chunk) return STILL_ERR_INVALID_ARG;
+  if (c->window == 0 && c->top_k != 0) return STILL_ERR_INVALID_ARG;
+  if (c->chunk != 64 || c->window > c->chunk) return STILL_ERR_UNSUPPORTED;
+  if (!still::shape_supported(c->dtype == STILL_BF16, c->head_dim, c->feat_dim)) return STILL_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(c->batch) * c->n_kv_heads > 65535) return STILL_ERR_UNSUPPORTED;
+  if (use_seq) {
+    const int64_t n_chunks = (static_cast<int64_t>(c->seq_len) + 63) / 64;
+    const int64_t g = c->n_q_heads / c->n_kv_heads;
+    const int64_t nw = g < 4 ? g : 4;
+    const int64_t gsplit = (g + nw - 1) / nw;
+    if (n_chunks * c->batch * c->n_kv_heads * gsplit > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
+  }
+  return STILL_OK;
+}
+
+Dims dims_of(const still_config* c) {
+  Dims d;
+  d.B = c->batch;
+  d.T = c->seq_len;
+  d.Hq = c->n_q_heads;
+  d.Hkv = c->n_kv_heads;
+  d.G = c->n_q_heads / c->n_kv_heads;
+  d.D = c->head_dim;
+  d.DF = c->feat_dim;
+  d.window = c->window;
+  d.topk = c->top_k;
+  d.nC = (c->seq_len + 63) / 64;
+  d.nCc = c->seq_len / 64;
+  d.R = c->feat_dim * c->head_dim + c->feat_dim;
+  d.bf16 = c->dtype == STILL_BF16 ? 1 : 0;
+  return d;
+}
+
+size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4; }
+
+struct WsLayout {
+  size_t sal, selmask, ksel, vsel, phik, states, total;
+};
+
+WsLayout ws_layout(const still_config* c) {
+  const Dims d = dims_of(c);
+  const size_t bh = static_cast<size_t>(d.B) * d.Hkv;
+  const size_t es = elem_bytes(c);
+  WsLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.sal = take(bh * d.T * sizeof(float));
+  L.selmask = take(bh * d.nC * sizeof(uint64_t));
+  L.ksel = take(bh * d.nCc * d.topk * d.D * es);
+  L.vsel = take(bh * d.nCc * d.topk * d.D * es);
+  L.phik = take(bh * d.T * d.DF * es);
+  L.states = take(bh * d.nC * d.R * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* still_status_string(int status) {
+  switch (status) {
+    case STILL_OK: return "ok";
+    case STILL_ERR_INVALID_ARG: return "invalid argument";
+    case STILL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case STILL_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case STILL_ERR_CACHE_FULL: return "decode cache full";
+    case STILL_ERR_CACHE_MISMATCH: return "decode cache built for another configuration";
+    case STILL_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t still_prefill_workspace_bytes(const still_config* cfg) {
+  if (check_cfg(cfg, true) != STILL_OK) return 0;
+  return ws_layout(cfg).total;
+}
+
+int still_prefill_timed(const still_config* cfg, const void* q, const void* k, const void* v,
+                        const void* w_phi, void* out, const int32_t* routing_in,
+                        float* saliency_out, int32_t* sel_idx_out, still_cache* cache,
+                        void* workspace, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* events) {
+  const int st = check_cfg(cfg, true);
+  if (st != STILL_OK) return st;
+  if (!q || !k || !v || !w_phi || !out || !workspace) return STILL_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, w_phi, static_cast<const void*>(out), static_cast<const void*>(workspace)})
+    if (!aligned(p, 16)) return STILL_ERR_INVALID_ARG;
+  for (const void* p : {static_cast<const void*>(routing_in), static_cast<const void*>(saliency_out),
+                        static_cast<const void*>(sel_idx_out)})
+    if (p && !aligned(p, 4)) return STILL_ERR_INVALID_ARG;
+  if (saliency_out && cfg->window < 1) return STILL_ERR_INVALID_ARG;
+  if (cache) return STILL_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(cfg);
+  if (ws_bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+
+  const Dims d = dims_of(cfg);
+  char* ws = static_cast<char*>(workspace);
+  still::PrepArgs pa;
+  pa.d = d;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.w = w_phi;
+  pa.routing_in = cfg->top_k > 0 ? routing_in : nullptr;
+  pa.sal = saliency_out ? saliency_out : reinterpret_cast<float*>(ws + L.sal);
+  pa.selmask = reinterpret_cast<uint64_t*>(ws + L.selmask);
+  pa.sel_idx = sel_idx_out;
+  pa.ksel = ws + L.ksel;
+  pa.vsel = ws + L.vsel;
+  pa.phik = ws + L.phik;
+  pa.states = reinterpret_cast<float*>(ws + L.states);
+  if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (still::launch_prep(pa, stream) != hipSuccess) return STILL_ERR_HIP;
+  if (events && hipEventRecord(events[1], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (still::launch_scan(d, pa.states, stream) != hipSuccess) return STILL_ERR_HIP;
+  if (events && hipEventRecord(events[2], stream) != hipSuccess) return STILL_ERR_HIP;
+
+  still::AttnArgs aa;
+  aa.d = d;
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.w = w_phi;
+  aa.selmask = pa.selmask;
+  aa.ksel = pa.ksel;
+  aa.vsel = pa.vsel;
+  aa.phik = pa.phik;
+  aa.states = pa.states;
+  aa.out = out;
+  aa.nw = d.G < 4 ? d.G : 4;
+  aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
+  if (still::launch_attn(aa, stream) != hipSuccess) return STILL_ERR_HIP;
+  if (events && hipEventRecord(events[3], stream) != hipSuccess) return STILL_ERR_HIP;
+  return STILL_OK;
+}
+
+int still_prefill(const still_config* cfg, const void* q, const void* k, const void* v,
+                  const void* w_phi, void* out, const int32_t* routing_in,
+                  float* saliency_out, int32_t* sel_idx_out, still_cache* cache,
+                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return still_prefill_timed(cfg, q, k, v, w_phi, out, routing_in, saliency_out, sel_idx_out, cache,
+                             workspace, ws_bytes, stream, nullptr);
+}
+
+int still_select_topk(const still_config* cfg, const float* saliency, int32_t* sel_idx_out,
+                      hipStream_t stream) {
+  const int st = check_cfg(cfg, true);
+  if (st != STILL_OK) return st;
+  if (!saliency || !sel_idx_out || !aligned(saliency, 4) || !aligned(sel_idx_out, 4)) return STILL_ERR_INVALID_ARG;
+  const Dims d = dims_of(cfg);
+  return still::launch_topk(d, saliency, sel_idx_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+}
+
+int still_feature_map(const still_config* cfg, const void* x, const void* w_phi, float* phi_out,
+                      hipStream_t stream) {
+  const int st = check_cfg(cfg, true);
+  if (st != STILL_OK) return st;
+  if (!x || !w_phi || !phi_out || !aligned(x, 16) || !aligned(w_phi, 16) || !aligned(phi_out, 4))
+    return STILL_ERR_INVALID_ARG;
+  const Dims d = dims_of(cfg);
+  return still::launch_feature_map(d, x, w_phi, phi_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+}
+
+size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens) {
+  (void)cfg;
+  (void)max_tokens;
+  return 0;
+}
+
+int still_cache_init(const still_config* cfg, int64_t max_tokens, void* dev_buf, size_t bytes,
+                     still_cache* out, hipStream_t stream) {
+  (void)cfg;
+  (void)max_tokens;
+  (void)dev_buf;
+  (void)bytes;
+  (void)out;
+  (void)stream;
+  return STILL_ERR_UNSUPPORTED;
+}
+
+size_t still_decode_workspace_bytes(const still_config* cfg, int64_t max_tokens) {
+  (void)cfg;
+  (void)max_tokens;
+  return 0;
+}
+
+int still_decode_step(const still_config* cfg, still_cache* cache, const void* q, const void* k,
+                      const void* v, const void* w_phi, void* out, void* workspace,
+                      size_t ws_bytes, hipStream_t stream) {
+  (void)cfg;
+  (void)cache;
+  (void)q;
+  (void)k;
+  (void)v;
+  (void)w_phi;
+  (void)out;
+  (void)workspace;
+  (void)ws_bytes;
+  (void)stream;
+  return STILL_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Device primitives shared by the STILL kernels (gfx950, wave64).
+//
+// MFMA convention used everywhere: a "fragment" is 8 elements per lane feeding one
+// 16x16x32 contraction step. For lane l, write r16 = l % 16 and grp = l / 16.
+//   A operand: row r16 of the 16-row tile, 8 of the 32 k-indices chosen by grp.
+//   B operand: column r16 of the 16-column tile, the same 8 k-indices.
+//   Accumulator (f32x4): element i holds D[row = 4*grp + i][col = r16].
+// Which 8 k-indices a lane group holds only has to agree between A and B, so two
+// assignments are used:
+//   SK ("straight"):  k = 8*grp + e                        (16-byte contiguous loads)
+//   PK ("permuted"):  k = 16*(e/4) + 4*grp + (e%4)          (matches the accumulator
+//                     layout of a previous 16x16 product, so a result can be fed back as
+//                     an operand without leaving registers)
+// bf16 uses one v_mfma_f32_16x16x32_bf16 per step; fp32 uses eight
+// v_mfma_f32_16x16x4_f32 (element e of every lane in the e-th instruction), which
+// contracts exactly the same index set.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace still {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) bf16 bf16x8;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInf = __builtin_huge_valf();
+
+template <typename T> struct Tr;
+
+template <> struct Tr<bf16> {
+  using frag = bf16x8;
+  using quad = bf16x4;
+  static __device__ __forceinline__ frag zero() { return frag{}; }
+  static __device__ __forceinline__ frag load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  static __device__ __forceinline__ quad load4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  static __device__ __forceinline__ void store8(bf16* p, frag x) { *reinterpret_cast<bf16x8*>(p) = x; }
+  static __device__ __forceinline__ frag join(quad lo, quad hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  static __device__ __forceinline__ void mma(f32x4& acc, const frag& a, const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+  static __device__ __forceinline__ bf16 from_f(float x) { return static_cast<bf16>(x); }
+};
+
+template <> struct Tr<float> {
+  using frag = f32x8;
+  using quad = f32x4;
+  static __device__ __forceinline__ frag zero() { return frag{}; }
+  static __device__ __forceinline__ frag load8(const float* p) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  static __device__ __forceinline__ quad load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ void store8(float* p, frag x) {
+    *reinterpret_cast<f32x4*>(p) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    *reinterpret_cast<f32x4*>(p + 4) = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+  }
+  static __device__ __forceinline__ frag join(quad lo, quad hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  static __device__ __forceinline__ void mma(f32x4& acc, const frag& a, const frag& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+
+// ---- wave64 cross-lane helpers -------------------------------------------------------
+
+__device__ __forceinline__ float xor_max_groups(float x) {
+  // max over the 4 lanes {l, l^16, l^32, l^48}
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float xor_sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float xor_sum_16(float x) {
+  // sum over the 16 lanes that share l / 16
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), m, 64);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), m, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t or_reduce_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x |= shfl_xor_u64(x, m);
+  return x;
+}
+
+// softplus(x) = log(1 + e^x), stable for any finite x.
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+
+}  // namespace still

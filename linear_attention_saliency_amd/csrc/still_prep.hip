@@ -1,0 +1,327 @@
+// Per-chunk preparation kernels of the STILL prefill, plus the standalone top-k and
+// NP-Map kernels.
+//
+// prep_kernel, one workgroup per (chunk c, batch b, KV head h), four waves:
+//   1. stage the 128-row key band around chunk c in LDS;
+//   2. Self-Saliency Score of the chunk's 64 tokens for each query head of the group,
+//      summed over the group in head order ([P1] section "Self-Saliency Score");
+//   3. NP-Map of the chunk's keys ([P1] section "Norm-Preserved Feature Map（NP-Map）");
+//   4. top-k routing of a complete chunk, ascending positions, and the gather of the
+//      selected K/V rows into the compact softmax cache ([P1] section
+//      "Chunk-Wise并行+延迟选择");
+//   5. the chunk's linear-attention contribution U_c = sum over its unselected keys of
+//      phi(k) v^T and u_c = sum phi(k) ([P3] on the fixed-size state of linear attention).
+// scan_kernel then turns the U_c into inclusive prefix sums over chunks.
+#include "still_launch.hpp"
+#include "still_route.hpp"
+
+namespace still {
+
+template <typename T, int D, int DF>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  constexpr int LDK = pitch<T>(D);
+  constexpr int FPW = DF / 64;
+  constexpr int V8 = D / 8;
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+
+  __shared__ __attribute__((aligned(16))) T band[128 * LDK];
+  __shared__ float s_part[4][64];
+  __shared__ float s_acc[64];
+  __shared__ float m2part[4 * 64];
+  __shared__ float xn2[64];
+  __shared__ int selpos[64];
+  __shared__ uint64_t s_mask;
+
+  const Dims& d = a.d;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* w = static_cast<const T*>(a.w);
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const long long T_ = d.T;
+  const long long t0 = static_cast<long long>(c) * kChunk;
+  const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
+  const bool complete = nvalid == kChunk;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+
+  // 1. key band: row t <-> position t0 - 63 + t (row 127 is never in a window)
+  for (int idx = tid; idx < 128 * V8; idx += 256) {
+    const int row = idx / V8, c8 = idx % V8;
+    const long long pos = t0 - 63 + row;
+    frag x = TT::zero();
+    if (row < 127 && pos >= 0 && pos < T_) x = TT::load8(k + ((b * T_ + pos) * d.Hkv + h) * D + c8 * 8);
+    TT::store8(band + row * LDK + c8 * 8, x);
+  }
+  __syncthreads();
+
+  // 2. saliency, summed over the group in head order g = 0..G-1
+  if (d.window >= 1) {
+    for (int g0 = 0; g0 < d.G; g0 += 4) {
+      const int g = g0 + wave;
+      if (g < d.G) {
+        const int hq = h * d.G + g;
+#pragma unroll 1
+        for (int qb = 0; qb < 4; ++qb) {
+          frag qf[D / 32];
+          const long long pos = t0 + qb * 16 + r16;
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks)
+            qf[ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
+          const float sv = saliency_qblock<T, D, LDK>(band, qf, qb, d.window, t0 - 63, scale);
+          if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float acc = g0 == 0 ? 0.f : s_acc[lane];
+        const int nw = d.G - g0 < 4 ? d.G - g0 : 4;
+        for (int w2 = 0; w2 < nw; ++w2) acc += s_part[w2][lane];
+        s_acc[lane] = acc;
+      }
+      __syncthreads();
+    }
+    if (tid < nvalid) a.sal[(static_cast<long long>(bh)) * T_ + t0 + tid] = s_acc[tid];
+  }
+
+  // 3. NP-Map of the chunk's keys (band rows 63..126)
+  f32x4 phi[4][FPW];
+  np_map_rows64<T, D, DF, LDK>(band + 63 * LDK, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+
+  // 4. routing of a complete chunk
+  const long long nsel_rows = static_cast<long long>(d.nCc) * d.topk;
+  if (wave == 0) {
+    uint64_t m = 0;
+    if (complete && d.topk > 0) {
+      if (a.routing_in) {
+        uint64_t bit = 0;
+        if (lane < d.topk) {
+          const long long p = a.routing_in[(static_cast<long long>(bh) * d.nCc + c) * d.topk + lane] - t0;
+          if (p >= 0 && p < kChunk) bit = 1ull << p;
+        }
+        m = or_reduce_u64(bit);
+      } else {
+        m = topk_mask(s_acc[lane], d.topk);
+      }
+    }
+    if (lane == 0) {
+      s_mask = m;
+      a.selmask[static_cast<long long>(bh) * d.nC + c] = m;
+    }
+    if ((m >> lane) & 1ull) {
+      const int slot = __popcll(m & ((1ull << lane) - 1ull));
+      selpos[slot] = lane;
+      if (a.sel_idx) a.sel_idx[(static_cast<long long>(bh) * d.nCc + c) * d.topk + slot] = static_cast<int>(t0 + lane);
+    }
+  }
+  __syncthreads();
+  const uint64_t smask = s_mask;
+  if (complete && d.topk > 0) {
+    const int nsel = __popcll(smask);
+    T* ks_ = static_cast<T*>(a.ksel);
+    T* vs_ = static_cast<T*>(a.vsel);
+    for (int idx = tid; idx < d.topk * V8; idx += 256) {
+      const int slot = idx / V8, c8 = idx % V8;
+      const long long dst = (static_cast<long long>(bh) * nsel_rows + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
+      frag kx = TT::zero(), vx = TT::zero();
+      if (slot < nsel) {
+        const long long src = ((b * T_ + t0 + selpos[slot]) * d.Hkv + h) * D + c8 * 8;
+        kx = TT::load8(k + src);
+        vx = TT::load8(v + src);
+      }
+      TT::store8(ks_ + dst, kx);
+      TT::store8(vs_ + dst, vx);
+    }
+  }
+
+  // 5. store phi(k) (rounded to T); keep the rounded values of unselected keys for U_c
+  T* phik = static_cast<T*>(a.phik);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int fi = 0; fi < FPW; ++fi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = kb * 16 + 4 * grp + i;
+        const int f = (wave * FPW + fi) * 16 + r16;
+        const T val = TT::from_f(phi[kb][fi][i]);
+        if (row < nvalid) phik[(static_cast<long long>(bh) * T_ + t0 + row) * DF + f] = val;
+        phi[kb][fi][i] = ((smask >> row) & 1ull) ? 0.f : TT::to_f(val);
+      }
+
+  // 6. U_c^T = V_c^T phi_masked and u_c, for complete chunks
+  if (!complete) return;  // uniform across the workgroup
+  for (int idx = tid; idx < 64 * V8; idx += 256) {
+    const int row = idx / V8, c8 = idx % V8;
+    TT::store8(band + row * LDK + c8 * 8, TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8));
+  }
+  __syncthreads();
+  f32x4 u[D / 16][FPW];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int fi = 0; fi < FPW; ++fi) u[db][fi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    frag pb[FPW];
+#pragma unroll
+    for (int fi = 0; fi < FPW; ++fi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[fi][e] = TT::from_f(phi[2 * ks + e / 4][fi][e % 4]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      frag av;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = band[(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4)) * LDK + db * 16 + r16];
+#pragma unroll
+      for (int fi = 0; fi < FPW; ++fi) TT::mma(u[db][fi], av, pb[fi]);
+    }
+  }
+  float* st = a.states + (static_cast<long long>(bh) * d.nC + c) * d.R;
+#pragma unroll
+  for (int fi = 0; fi < FPW; ++fi) {
+    const int f = (wave * FPW + fi) * 16 + r16;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(st + f * D + db * 16 + 4 * grp) = u[db][fi];
+    float zs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zs += phi[kb][fi][i];
+    zs = xor_sum_groups(zs);
+    if (grp == 0) st[DF * D + f] = zs;
+  }
+}
+
+// Inclusive prefix sum of the chunk records over the complete chunks, in place.
+// One thread per record element; 16 chunk loads in flight per thread.
+__global__ __launch_bounds__(256) void scan_kernel(float* states, int nC, int nCc, int R) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= R) return;
+  float* p = states + static_cast<long long>(blockIdx.y) * nC * R + e;
+  float acc = 0.f;
+  for (int c0 = 0; c0 < nCc; c0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = c0 + j < nCc ? p[static_cast<long long>(c0 + j) * R] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < nCc) {
+        acc += x[j];
+        p[static_cast<long long>(c0 + j) * R] = acc;
+      }
+  }
+}
+
+// Standalone per-chunk top-k: one wave per (complete chunk, batch, KV head).
+__global__ __launch_bounds__(64) void topk_kernel(const float* sal, int32_t* sel_idx, int T, int nCc, int topk) {
+  const int c = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const long long t0 = static_cast<long long>(c) * kChunk;
+  const uint64_t m = topk_mask(sal[static_cast<long long>(bh) * T + t0 + lane], topk);
+  if ((m >> lane) & 1ull) {
+    const int slot = __popcll(m & ((1ull << lane) - 1ull));
+    sel_idx[(static_cast<long long>(bh) * nCc + c) * topk + slot] = static_cast<int>(t0 + lane);
+  }
+}
+
+// Standalone NP-Map: one workgroup per (64-row tile of positions, batch, KV head).
+template <typename T, int D, int DF>
+__global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv, const void* wv, float* phi_out) {
+  constexpr int LDK = pitch<T>(D);
+  constexpr int FPW = DF / 64;
+  constexpr int V8 = D / 8;
+  using TT = Tr<T>;
+  __shared__ __attribute__((aligned(16))) T rows[64 * LDK];
+  __shared__ float m2part[4 * 64];
+  __shared__ float xn2[64];
+  const T* x = static_cast<const T*>(xv);
+  const T* w = static_cast<const T*>(wv);
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / d.Hkv, h = bh % d.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const long long T_ = d.T, t0 = static_cast<long long>(c) * 64;
+  for (int idx = tid; idx < 64 * V8; idx += 256) {
+    const int row = idx / V8, c8 = idx % V8;
+    typename TT::frag val = TT::zero();
+    if (t0 + row < T_) val = TT::load8(x + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8);
+    TT::store8(rows + row * LDK + c8 * 8, val);
+  }
+  __syncthreads();
+  f32x4 phi[4][FPW];
+  np_map_rows64<T, D, DF, LDK>(rows, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int fi = 0; fi < FPW; ++fi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = kb * 16 + 4 * grp + i;
+        const int f = (wave * FPW + fi) * 16 + r16;
+        if (t0 + row < T_) phi_out[((b * T_ + t0 + row) * d.Hkv + h) * DF + f] = phi[kb][fi][i];
+      }
+}
+
+// ------------------------------------------------------------------------ launchers
+
+template <typename T, int D, int DF>
+static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
+  dim3 grid(a.d.nC, a.d.B * a.d.Hkv);
+  hipLaunchKernelGGL((prep_kernel<T, D, DF>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DF>
+static hipError_t fmap_t(const Dims& d, const void* x, const void* w, float* phi, hipStream_t s) {
+  dim3 grid(d.nC, d.B * d.Hkv);
+  hipLaunchKernelGGL((feature_map_kernel<T, D, DF>), grid, dim3(256), 0, s, d, x, w, phi);
+  return hipGetLastError();
+}
+
+bool shape_supported(int bf16, int D, int DF) {
+  if (bf16) return (D == 64 || D == 128) && (DF == 64 || DF == 128);
+  return D == 64 && DF == 64;
+}
+
+#define STILL_DISPATCH(FN, ...)                                                   \
+  do {                                                                            \
+    const Dims& dd_ = (DIMS);                                                     \
+    if (dd_.bf16) {                                                               \
+      if (dd_.D == 64 && dd_.DF == 64) return FN<bf16, 64, 64>(__VA_ARGS__);      \
+      if (dd_.D == 64 && dd_.DF == 128) return FN<bf16, 64, 128>(__VA_ARGS__);    \
+      if (dd_.D == 128 && dd_.DF == 64) return FN<bf16, 128, 64>(__VA_ARGS__);    \
+      if (dd_.D == 128 && dd_.DF == 128) return FN<bf16, 128, 128>(__VA_ARGS__);  \
+    } else if (dd_.D == 64 && dd_.DF == 64) {                                     \
+      return FN<float, 64, 64>(__VA_ARGS__);                                      \
+    }                                                                             \
+    return hipErrorInvalidValue;                                                  \
+  } while (0)
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
+#define DIMS a.d
+  STILL_DISPATCH(prep_t, a, s);
+#undef DIMS
+}
+
+hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float* phi, hipStream_t s) {
+#define DIMS d
+  STILL_DISPATCH(fmap_t, d, x, w, phi, s);
+#undef DIMS
+}
+
+hipError_t launch_scan(const Dims& d, float* states, hipStream_t s) {
+  if (d.nCc == 0) return hipSuccess;
+  dim3 grid((d.R + 255) / 256, d.B * d.Hkv);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, s, states, d.nC, d.nCc, d.R);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Dims& d, const float* sal, int32_t* sel_idx, hipStream_t s) {
+  if (d.nCc == 0 || d.topk == 0) return hipSuccess;
+  dim3 grid(d.nCc, d.B * d.Hkv);
+  hipLaunchKernelGGL(topk_kernel, grid, dim3(64), 0, s, sal, sel_idx, d.T, d.nCc, d.topk);
+  return hipGetLastError();
+}
+
+}  // namespace still

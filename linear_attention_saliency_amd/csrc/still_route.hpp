@@ -1,0 +1,157 @@
+// Saliency, per-chunk top-k and NP-Map device routines.
+//
+// The prefill kernels and the decode kernel call exactly these functions, so a token's
+// saliency (and hence every routing decision) is bit-identical whichever path computed it.
+#pragma once
+
+#include "still_common.hpp"
+
+namespace still {
+
+constexpr int kChunk = 64;
+
+// LDS row pitch (elements) for a row of n elements: 16 bytes of padding.
+template <typename T> constexpr int pitch(int n) { return n + 16 / static_cast<int>(sizeof(T)); }
+
+// Self-Saliency Score of 16 queries of one query head
+// ([P1] section "Self-Saliency Score"; [P4] section Approach).
+//
+// `band` holds 128 key rows (pitch LDK): row t is the key at position band_pos0 + t, with
+// band_pos0 = chunk_start - 63 (rows outside the sequence are zero and masked here).
+// Query r of the chunk (its position is chunk_start + r) sits at band row r + 63, so its
+// window is band rows [r + 64 - w, r + 63]. qf holds the B-operand (SK) fragments of the
+// queries qb*16 .. qb*16+15 (lane r16 <-> query qb*16 + r16).
+//
+// For query i: M' = max over the window without i, Z' = sum over the window without i of
+// e^{a - M'}, and s_i = LSE(W_i) - LSE(W_i \ i) = softplus(a_ii - M' - log Z'), which is
+// +inf when i is alone in its window. Returned in every lane of the query's column.
+template <typename T, int D, int LDK>
+__device__ __forceinline__ float saliency_qblock(const T* band, const typename Tr<T>::frag (&qf)[D / 32],
+                                                 int qb, int window, long long band_pos0, float scale) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  f32x4 acc[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const typename Tr<T>::frag a = Tr<T>::load8(band + ((qb + j) * 16 + r16) * LDK + ks * 32 + grp * 8);
+      Tr<T>::mma(acc[j], a, qf[ks]);
+    }
+  }
+  const int r = qb * 16 + r16;
+  const int diag = r + 63, lo = r + 64 - window;
+  float mx = -kInf, dg = -kInf;
+#pragma unroll
+  for (int j = 0; j < 5; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (qb + j) * 16 + 4 * grp + i;
+      const bool in = row >= lo && row <= diag && band_pos0 + row >= 0;
+      const float a = acc[j][i] * scale;
+      if (in && row == diag) dg = a;
+      if (in && row != diag) mx = fmaxf(mx, a);
+    }
+  mx = xor_max_groups(mx);
+  dg = xor_max_groups(dg);
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < 5; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (qb + j) * 16 + 4 * grp + i;
+      const bool in = row >= lo && row < diag && band_pos0 + row >= 0;
+      if (in) z += expf(acc[j][i] * scale - mx);
+    }
+  z = xor_sum_groups(z);
+  return z > 0.f ? softplus_f(dg - mx - logf(z)) : kInf;
+}
+
+// Top-k of one chunk ([P1] section "Chunk-Wise并行+延迟选择"): lane p holds the
+// saliency of chunk position p (a non-negative float or +inf). A bitonic sort of the
+// 64-bit keys (saliency bits, 63 - p) in descending order leaves rank j in lane j; the
+// first topk ranks are returned as a position bit mask. Equal saliency sorts the lower
+// position first. Every lane of the wave must call.
+__device__ __forceinline__ uint64_t topk_mask(float s, int topk) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | static_cast<uint32_t>(63 - lane);
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor_u64(key, j);
+      const bool desc = (lane & kk) == 0;
+      const bool lower = (lane & j) == 0;
+      key = (lower == desc) ? (key > o ? key : o) : (key < o ? key : o);
+    }
+  const int p = 63 - static_cast<int>(key & 63);
+  return or_reduce_u64(lane < topk ? (1ull << p) : 0ull);
+}
+
+// NP-Map of 64 rows ([P1] section "Norm-Preserved Feature Map（NP-Map）"; [P4] section
+// Approach): phi(x) = |x| m / |m|, m = elu(W_h x) + 1.
+//
+// rows: 64 rows of D elements in LDS (pitch LDK). Wh: W_h in global memory [DF][D].
+// Four waves; wave w owns feature blocks fb = w*FPW + fi (FPW = DF/64). On return
+// phi[kb][fi][i] = phi(row kb*16 + 4*grp + i)[feature fb*16 + r16] in fp32.
+// Scratch in LDS: m2part[4*64], xn2[64]. Contains one __syncthreads(); all 256 threads
+// must call. After it returns no thread reads `rows` again.
+template <typename T, int D, int DF, int LDK>
+__device__ __forceinline__ void np_map_rows64(const T* rows, const T* Wh, float* m2part, float* xn2,
+                                              f32x4 (&phi)[4][DF / 64]) {
+  constexpr int FPW = DF / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  if (tid < 64) {
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) {
+      const float x = Tr<T>::to_f(rows[tid * LDK + d]);
+      s += x * x;
+    }
+    xn2[tid] = s;
+  }
+#pragma unroll
+  for (int fi = 0; fi < FPW; ++fi) {
+    const int fb = wave * FPW + fi;
+    typename Tr<T>::frag wf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) wf[ks] = Tr<T>::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const typename Tr<T>::frag a = Tr<T>::load8(rows + (kb * 16 + r16) * LDK + ks * 32 + grp * 8);
+        Tr<T>::mma(acc, a, wf[ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zv = acc[i];
+        acc[i] = zv > 0.f ? zv + 1.f : expf(zv);  // elu(z) + 1
+      }
+      phi[kb][fi] = acc;
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = 0.f;
+#pragma unroll
+      for (int fi = 0; fi < FPW; ++fi) p += phi[kb][fi][i] * phi[kb][fi][i];
+      p = xor_sum_16(p);
+      if (r16 == 0) m2part[wave * 64 + kb * 16 + 4 * grp + i] = p;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kb * 16 + 4 * grp + i;
+      const float m2 = ((m2part[row] + m2part[64 + row]) + m2part[128 + row]) + m2part[192 + row];
+      const float sc = m2 > 0.f ? sqrtf(xn2[row]) / sqrtf(m2) : 0.f;
+#pragma unroll
+      for (int fi = 0; fi < FPW; ++fi) phi[kb][fi][i] *= sc;
+    }
+}
+
+}  // namespace still

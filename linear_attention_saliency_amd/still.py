@@ -1,0 +1,189 @@
+"""Python binding of libstill.so (argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels; torch is used here only to
+allocate device memory and to name the current HIP stream. If the library is missing
+this module raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libstill.so")
+
+STILL_F32, STILL_BF16 = 0, 1
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace too small",
+          -4: "decode cache full", -5: "decode cache built for another configuration",
+          -6: "HIP launch error"}
+
+EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefill", "still_prefill_timed",
+           "still_select_topk",
+           "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
+           "still_decode_step")
+
+
+class StillError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        super().__init__(f"{what}: status {code} ({STATUS.get(code, 'unknown')})")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "seq_len", "n_q_heads", "n_kv_heads", "head_dim",
+                                               "feat_dim", "window", "chunk", "top_k", "dtype")]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("cfg", Config), ("max_tokens", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
+                ("sel_capacity", ctypes.c_int64),
+                ("sel_k", ctypes.c_void_p), ("sel_v", ctypes.c_void_p), ("ring_k", ctypes.c_void_p),
+                ("ring_v", ctypes.c_void_p), ("state_s", ctypes.c_void_p), ("state_z", ctypes.c_void_p),
+                ("sel_mask", ctypes.c_void_p), ("cur_saliency", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load libstill.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S, V = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    CP = ctypes.POINTER(Config)
+    KP = ctypes.POINTER(Cache)
+    lib.still_status_string.argtypes = [I]
+    lib.still_status_string.restype = ctypes.c_char_p
+    lib.still_prefill_workspace_bytes.argtypes = [CP]
+    lib.still_prefill_workspace_bytes.restype = S
+    lib.still_prefill.argtypes = [CP, P, P, P, P, P, P, P, P, KP, P, S, V]
+    lib.still_prefill.restype = I
+    lib.still_prefill_timed.argtypes = [CP, P, P, P, P, P, P, P, P, KP, P, S, V, P]
+    lib.still_prefill_timed.restype = I
+    lib.still_select_topk.argtypes = [CP, P, P, V]
+    lib.still_select_topk.restype = I
+    lib.still_feature_map.argtypes = [CP, P, P, P, V]
+    lib.still_feature_map.restype = I
+    lib.still_cache_bytes.argtypes = [CP, ctypes.c_int64]
+    lib.still_cache_bytes.restype = S
+    lib.still_cache_init.argtypes = [CP, ctypes.c_int64, P, S, KP, V]
+    lib.still_cache_init.restype = I
+    lib.still_decode_workspace_bytes.argtypes = [CP, ctypes.c_int64]
+    lib.still_decode_workspace_bytes.restype = S
+    lib.still_decode_step.argtypes = [CP, KP, P, P, P, P, P, P, S, V]
+    lib.still_decode_step.restype = I
+    _lib = lib
+    return lib
+
+
+def make_config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k,
+                dtype) -> Config:
+    dt = STILL_BF16 if dtype in (torch.bfloat16, "bf16") else STILL_F32 if dtype in (torch.float32, "f32") else -1
+    return Config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dt)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise StillError(rc, what)
+
+
+def _tensor_cfg(q, k, w_phi, window, chunk, top_k):
+    if q.dim() != 4 or k.dim() != 4 or w_phi.dim() != 3:
+        raise ValueError("q/k must be [B,T,H,D] and w_phi [Hkv,d_f,D]")
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return make_config(B, T, Hq, Hkv, D, w_phi.shape[1], window, chunk, top_k, q.dtype)
+
+
+def workspace_bytes(cfg: Config) -> int:
+    return int(load().still_prefill_workspace_bytes(ctypes.byref(cfg)))
+
+
+class Prefill:
+    """A prepared prefill call: the config and a reusable workspace for fixed shapes."""
+
+    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64):
+        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k)
+        nbytes = workspace_bytes(self.cfg)
+        if nbytes == 0:
+            rc = load().still_prefill(ctypes.byref(self.cfg), None, None, None, None, None, None, None, None,
+                                      None, None, 0, None)
+            _check(rc, "still_prefill config")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+    def __call__(self, q, k, v, w_phi, out, *, routing=None, saliency=None, sel_idx=None, stream=None,
+                 events=None):
+        """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4)."""
+        for t in (q, k, v, w_phi, out):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("tensors must be contiguous device tensors")
+        rc = load().still_prefill_timed(ctypes.byref(self.cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w_phi),
+                                        _ptr(out), _ptr(routing), _ptr(saliency), _ptr(sel_idx), None,
+                                        _ptr(self.workspace), self.workspace.numel(), _stream(stream),
+                                        events)
+        _check(rc, "still_prefill")
+        return out
+
+
+def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing=None,
+            return_saliency: bool = False, return_routing: bool = False):
+    """One STILL layer over whole sequences.
+
+    q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
+    GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection.
+    Returns out (and saliency [B,Hkv,T] fp32, sel_idx [B,Hkv,T//chunk,top_k] int32 on
+    request).
+    """
+    call = Prefill(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk)
+    B, T, _, _ = q.shape
+    Hkv = k.shape[2]
+    out = torch.empty_like(q)
+    sal = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device) if return_saliency else None
+    sel = torch.empty((B, Hkv, T // chunk, top_k), dtype=torch.int32, device=q.device) if return_routing else None
+    if routing is not None:
+        routing = routing.to(device=q.device, dtype=torch.int32).contiguous()
+    call(q, k, v, w_phi, out, routing=routing, saliency=sal, sel_idx=sel)
+    res = [out]
+    if return_saliency:
+        res.append(sal)
+    if return_routing:
+        res.append(sel)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def select_topk(saliency, *, chunk: int, top_k: int, n_q_heads: int = 1, head_dim: int = 64, feat_dim: int = 64,
+                dtype=torch.bfloat16):
+    """Per-chunk top-k of a device saliency tensor [B,Hkv,T] fp32 -> int32 [B,Hkv,T//chunk,top_k]."""
+    B, Hkv, T = saliency.shape
+    cfg = make_config(B, T, Hkv * n_q_heads, Hkv, head_dim, feat_dim, chunk, chunk, top_k, dtype)
+    sel = torch.empty((B, Hkv, T // chunk, top_k), dtype=torch.int32, device=saliency.device)
+    rc = load().still_select_topk(ctypes.byref(cfg), _ptr(saliency.contiguous()), _ptr(sel), _stream())
+    _check(rc, "still_select_topk")
+    return sel
+
+
+def feature_map(x, w_phi):
+    """NP-Map of device rows x [B,T,Hkv,D] with w_phi [Hkv,d_f,D] -> fp32 [B,T,Hkv,d_f]."""
+    B, T, Hkv, D = x.shape
+    F = w_phi.shape[1]
+    cfg = make_config(B, T, Hkv, Hkv, D, F, 64, 64, 0, x.dtype)
+    phi = torch.empty((B, T, Hkv, F), dtype=torch.float32, device=x.device)
+    rc = load().still_feature_map(ctypes.byref(cfg), _ptr(x), _ptr(w_phi), _ptr(phi), _stream())
+    _check(rc, "still_feature_map")
+    return phi
