@@ -59,7 +59,8 @@ Dims dims_of(const still_config* c) {
 size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4; }
 
 struct WsLayout {
-  size_t sal, selmask, ksel, vsel, phik, states, total;
+  size_t sal, selmask, ksel, vselT, vT, phik, states, total;
+  int ntiles_sel;
 };
 
 WsLayout ws_layout(const still_config* c) {
@@ -75,8 +76,10 @@ WsLayout ws_layout(const still_config* c) {
   };
   L.sal = take(bh * d.T * sizeof(float));
   L.selmask = take(bh * d.nC * sizeof(uint64_t));
+  L.ntiles_sel = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
   L.ksel = take(bh * d.nCc * d.topk * d.D * es);
-  L.vsel = take(bh * d.nCc * d.topk * d.D * es);
+  L.vselT = take(bh * L.ntiles_sel * 64 * d.D * es);
+  L.vT = take(bh * d.nC * 64 * d.D * es);
   L.phik = take(bh * d.T * d.DF * es);
   L.states = take(bh * d.nC * d.R * sizeof(float));
   L.total = off;
@@ -136,9 +139,11 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.selmask = reinterpret_cast<uint64_t*>(ws + L.selmask);
   pa.sel_idx = sel_idx_out;
   pa.ksel = ws + L.ksel;
-  pa.vsel = ws + L.vsel;
   pa.phik = ws + L.phik;
   pa.states = reinterpret_cast<float*>(ws + L.states);
+  pa.vT = ws + L.vT;
+  pa.vselT = ws + L.vselT;
+  pa.ntiles_sel = L.ntiles_sel;
   if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
   if (still::launch_prep(pa, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[1], stream) != hipSuccess) return STILL_ERR_HIP;
@@ -149,15 +154,16 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.d = d;
   aa.q = q;
   aa.k = k;
-  aa.v = v;
   aa.w = w_phi;
   aa.selmask = pa.selmask;
   aa.ksel = pa.ksel;
-  aa.vsel = pa.vsel;
+  aa.vselT = pa.vselT;
+  aa.vT = pa.vT;
   aa.phik = pa.phik;
   aa.states = pa.states;
   aa.out = out;
-  aa.nw = d.G < 4 ? d.G : 4;
+  aa.ntiles_sel = L.ntiles_sel;
+  aa.nw = d.G >= 4 ? 4 : (d.G == 3 ? 4 : d.G);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
   if (still::launch_attn(aa, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[3], stream) != hipSuccess) return STILL_ERR_HIP;

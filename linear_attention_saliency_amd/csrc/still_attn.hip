@@ -1,46 +1,145 @@
 // Fused softmax + linear attention of the STILL prefill, with the shared normaliser.
 //
-// One workgroup per (chunk c, batch b, KV head h, head split); wave w handles query head
-// g = split*4 + w of the group for the chunk's 64 queries, so the 4 query heads share
-// every staged key/value tile (GQA packing). For query i = 64c + r the key set splits as
-// ([P1] paragraph before "STILL三大创新", sections "Chunk-Wise并行+延迟选择" and NP-Map;
-// [P2] excerpt):
-//   chunks <= c-2   selected rows (compact softmax cache, no mask) -> softmax;
-//                   the others are folded in the prefix state (S, z) -> linear;
-//   chunk c-1       p > r + 64 - w or selected -> softmax, the rest -> linear;
-//   chunk c         p <= r: p > r - w -> softmax, the rest -> linear.
-// Everything is computed transposed (S^T = K Q^T, O^T += V^T P^T) so that a query is a
-// lane's column: row statistics need no cross-lane traffic beyond the 4 lane groups,
-// and P leaves the softmax in exactly the register layout the PV product consumes.
-// The running max starts at 0 (log2 units) and the linear-attention terms enter the
-// same accumulators scaled by 2^-m, so out = (A + e^{-M} N_LA) / (Z + e^{-M} D_LA) with
-// M = max(0, max logit) -- the shared-normaliser formula with an overflow-safe offset.
+// One workgroup per (chunk c, batch b, KV head h, head split). The workgroup packs up to
+// four query heads of the group (GQA): every staged key/value tile serves all of them.
+// Wave w handles query head (w / WPH) of the split and QW consecutive queries of the
+// chunk (WPH = 64 / QW waves per head).
+//
+// Key sets for query i = 64c + r ([P1] paragraph before "STILL三大创新", sections
+// "Chunk-Wise并行+延迟选择" and NP-Map; [P2] excerpt):
+//   chunks <= c-2  selected rows (compact cache) -> softmax; the rest are folded in the
+//                  inclusive prefix state (S, z) of chunk c-2 -> linear;
+//   chunk c-1      p > r + 64 - w or selected -> softmax, the rest -> linear;
+//   chunk c        p <= r: p > r - w -> softmax, the rest -> linear.
+//
+// Phase 1 (linear attention): N = phi(q) S + sum phi(q).phi(k_j) v_j over the linear keys
+// of chunks c-1 and c, D = phi(q) z + sum phi(q).phi(k_j). The whole linear branch then
+// enters the online softmax as one entry of log-weight log2(D) and value N / D, so the
+// shared-normaliser output  (sum_SA e^a v + N) / (sum_SA e^a + D)  needs no offset and
+// cannot overflow whatever the magnitudes.
+// Phase 2 (softmax): chunk c, chunk c-1, then the compact tiles, 64 keys per tile, with
+// the next tile's global loads in flight (registers) while the current one is computed
+// from LDS (double buffer). The running max is refreshed only when a tile's max exceeds
+// it by more than 8 (log2 units), so most tiles skip the rescale.
+//
+// Everything is computed transposed (S^T = K Q^T, O^T += V^T P^T): a query is a lane's
+// column, so its statistics need only the 4-lane-group reduction, and P leaves the
+// softmax in the register layout the PV product consumes. V tiles arrive transposed and
+// key-permuted from the prep kernel, phi(K) rows feature-permuted, so every LDS operand
+// fragment is a single 16-byte read.
 #include "still_launch.hpp"
+#include "still_layout.hpp"
 #include "still_route.hpp"
 
 namespace still {
 
-template <typename T, int D, int DF>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int LDK = pitch<T>(D);
-  constexpr int LDV = pitch<T>(64);
-  constexpr int LDF = pitch<T>(DF);
-  constexpr int V8 = D / 8;
-  constexpr int F8 = DF / 8;
+// One 64-key softmax tile for one wave, in two 32-key halves (half hs covers key blocks
+// 2hs and 2hs+1, which is exactly k-slice hs of the PV product, so each half runs
+// S^T = K Q^T, mask, online softmax and O^T += V^T P^T on its own and only half a tile
+// of scores is ever live). K rows come from lk, V^T rows from lv. The running max is
+// refreshed only when a half's max exceeds it by more than 8 (log2 units).
+// keep(p, qb): whether key p of the tile is in the softmax set of the lane's query in
+// block qb (used when MASKED).
+template <bool MASKED, typename T, int D, int QB, int LDK, int LDV, typename Keep>
+__device__ __forceinline__ void sa_tile(const T* lk, const T* lv, const typename Tr<T>::frag (&qf)[QB][D / 32],
+                                        f32x4 (&o)[D / 16][QB], float (&m_run)[QB], float (&l_run)[QB],
+                                        float c1, Keep keep) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    f32x4 s[2][QB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kb = 2 * hs + j;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[j][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const frag ka = TT::load8(lk + (kb * 16 + r16) * LDK + ks * 32 + grp * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TT::mma(s[j][qb], ka, qf[qb][ks]);
+      }
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!keep((2 * hs + j) * 16 + 4 * grp + i, qb)) s[j][qb][i] = -kInf;
+    }
+    bool need_any = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float tm = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
+                       fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+      tm = xor_max_groups(tm) * c1;
+      const bool need = tm > m_run[qb] + 8.f;
+      alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
+      m_run[qb] = need ? tm : m_run[qb];
+      need_any |= need;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha[qb];
+      }
+    }
+    frag pf[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mq = m_run[qb] == -kInf ? 0.f : m_run[qb];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __builtin_amdgcn_exp2f(s[e / 4][qb][e % 4] * c1 - mq);
+        l_run[qb] += x;
+        pf[qb][e] = TT::from_f(x);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const frag va = TT::load8(lv + (db * 16 + r16) * LDV + hs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
+    }
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) T k_s[64 * LDK];
-  __shared__ __attribute__((aligned(16))) T vt_s[D * LDV];
-  __shared__ __attribute__((aligned(16))) T pk_s[64 * LDF];
+template <typename T, int D, int DF, int QW, int NH>
+struct AttnCfg {
+  static constexpr int QB = QW / 16;           // 16-query blocks per wave
+  static constexpr int WPH = 64 / QW;          // waves per query head
+  static constexpr int NTHR = 64 * WPH * NH;   // threads per workgroup
+  static constexpr int LDK = pitch<T>(D > DF ? D : DF);
+  static constexpr int LDV = pitch<T>(64);
+  static constexpr int KBUF = 64 * LDK;        // elements of one K / phi(K) stage
+  static constexpr int VBUF = D * LDV;         // elements of one V^T stage
+  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * static_cast<int>(sizeof(T));
+};
+
+template <typename T, int D, int DF, int QW, int NH>
+__global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a) {
+  using C = AttnCfg<T, D, DF, QW, NH>;
+  constexpr int QB = C::QB, WPH = C::WPH, LDK = C::LDK, LDV = C::LDV, NTHR = C::NTHR;
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  T* ldsK = reinterpret_cast<T*>(lds_raw);        // [2][64][LDK]
+  T* ldsV = ldsK + 2 * C::KBUF;                    // [2][D][LDV]
 
   const Dims& d = a.d;
   const T* q = static_cast<const T*>(a.q);
   const T* kk = static_cast<const T*>(a.k);
-  const T* vv = static_cast<const T*>(a.v);
   const T* w = static_cast<const T*>(a.w);
   const T* ksel = static_cast<const T*>(a.ksel);
-  const T* vsel = static_cast<const T*>(a.vsel);
+  const T* vselT = static_cast<const T*>(a.vselT);
+  const T* vT = static_cast<const T*>(a.vT);
   const T* phik = static_cast<const T*>(a.phik);
 
   const int P = d.B * d.Hkv * a.gsplit;
@@ -49,8 +148,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int gs = pi % a.gsplit, bh = pi / a.gsplit;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const int nthr = blockDim.x;
-  const int g = gs * a.nw + wave;
+  constexpr int nthr = NTHR;
+  const int g = gs * NH + wave / WPH;
+  const int qoff = (wave % WPH) * QW;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
   const int hq = h * d.G + (head_ok ? g : d.G - 1);
   const long long T_ = d.T;
@@ -60,21 +160,29 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int win = d.window;
 
   // ---- queries: B-operand fragments (SK over d) -------------------------------------
-  frag qf[4][D / 32];
+  frag qf[QB][D / 32];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const long long pos = t0 + qb * 16 + r16;
+  for (int qb = 0; qb < QB; ++qb) {
+    const long long pos = t0 + qoff + qb * 16 + r16;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
       qf[qb][ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
   }
 
-  // ---- phi(q): W_h Q^T on MFMA, elu+1, norm rescale; B-operand fragments (PK over f) --
-  frag pq[4][DF / 32];
+  f32x4 o[D / 16][QB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // =============================== phase 1: linear attention ===========================
   {
+    // phi(q) = |q| m / |m|, m = elu(W_h q) + 1: B-operand fragments (PK over f)
+    frag pq[QB][DF / 32];
     const T* Wh = w + static_cast<long long>(h) * DF * D;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       f32x4 pacc[DF / 16];
 #pragma unroll
       for (int fb = 0; fb < DF / 16; ++fb) {
@@ -108,194 +216,225 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pq[qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
     }
-  }
 
-  // ---- accumulators; linear attention over the prefix state of chunks <= c-2 ---------
-  f32x4 o[D / 16][4];
-  float m_run[4], l_run[4];
+    float den[QB];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    m_run[qb] = 0.f;
-    l_run[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) den[qb] = 0.f;
+    // prefix state of chunks <= c-2: staged in LDS as S^T[d][pk_pos(f)] (rounded to T)
+    // and z[f] (fp32), with coalesced loads, then contracted on MFMA
+    if (c >= 2) {
+      const float* S = a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R;
+      constexpr int LDS_ = pitch<T>(DF);
+      T* st = ldsK;  // D rows of LDS_ elements: fits in the two K stages (128 rows of >= DF + pad)
+      float* zs = reinterpret_cast<float*>(ldsV);
+      for (int idx = tid; idx < DF * D / 4; idx += nthr) {
+        const int f = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(S + f * D + d4);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (c >= 2) {
-    const float* S = a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R;
-    const float* z = S + DF * D;
-#pragma unroll
-    for (int fs = 0; fs < DF / 32; ++fs) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        frag sa;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sa[e] = TT::from_f(S[(fs * 32 + 16 * (e / 4) + 4 * grp + (e % 4)) * D + db * 16 + r16]);
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
+        for (int j = 0; j < 4; ++j) st[(d4 + j) * LDS_ + pk_pos(f)] = TT::from_f(x[j]);
       }
+      for (int idx = tid; idx < DF; idx += nthr) zs[idx] = S[DF * D + idx];
+      __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float zf = z[fs * 32 + 16 * (e / 4) + 4 * grp + (e % 4)];
+      for (int fs = 0; fs < DF / 32; ++fs) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) l_run[qb] += TT::to_f(pq[qb][fs][e]) * zf;
+        for (int db = 0; db < D / 16; ++db) {
+          const frag sa = TT::load8(st + (db * 16 + r16) * LDS_ + fs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float zf = zs[fs * 32 + 16 * (e / 4) + 4 * grp + (e % 4)];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) den[qb] += TT::to_f(pq[qb][fs][e]) * zf;
+        }
       }
+      __syncthreads();  // the stages are reused below
     }
-  }
-
-  // ---- key tiles ----------------------------------------------------------------------
-  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
-  const int nt_comp = (n_comp + 63) / 64;
-  const int nt = nt_comp + (c >= 1 ? 1 : 0) + 1;
-  const uint64_t selprev = c >= 1 ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
-  const long long sel_rows = static_cast<long long>(d.nCc) * d.topk;
-
-  for (int tt = 0; tt < nt; ++tt) {
-    const int type = tt < nt_comp ? 0 : ((tt == nt_comp && c >= 1) ? 1 : 2);
-    const T* ksrc;
-    const T* vsrc;
-    long long kstride;
-    int nkeys;
-    long long tbase = 0;
-    if (type == 0) {
-      const long long off = (static_cast<long long>(bh) * sel_rows + static_cast<long long>(tt) * 64) * D;
-      ksrc = ksel + off;
-      vsrc = vsel + off;
-      kstride = D;
-      nkeys = n_comp - tt * 64 < 64 ? n_comp - tt * 64 : 64;
-    } else {
-      tbase = type == 1 ? t0 - 64 : t0;
-      const long long off = ((b * T_ + tbase) * d.Hkv + h) * D;
-      ksrc = kk + off;
-      vsrc = vv + off;
-      kstride = static_cast<long long>(d.Hkv) * D;
-      nkeys = type == 1 ? 64 : nvalid;
-    }
-    const bool need_phi = type == 1 || (type == 2 && win < kChunk);
-
-    __syncthreads();  // previous tile fully consumed
-    for (int idx = tid; idx < 64 * V8; idx += nthr) {
-      const int p = idx / V8, c8 = idx % V8;
-      frag kx = TT::zero(), vx = TT::zero();
-      if (p < nkeys) {
-        kx = TT::load8(ksrc + p * kstride + c8 * 8);
-        vx = TT::load8(vsrc + p * kstride + c8 * 8);
-      }
-      TT::store8(k_s + p * LDK + c8 * 8, kx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt_s[(c8 * 8 + e) * LDV + p] = vx[e];
-    }
-    if (need_phi) {
-      for (int idx = tid; idx < 64 * F8; idx += nthr) {
-        const int p = idx / F8, c8 = idx % F8;
+    // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w)
+    const uint64_t selprev = c >= 1 ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
+    const int cc_lo = c >= 1 ? c - 1 : c;
+    const int cc_hi = win < kChunk ? c : c - 1;
+    for (int cc = cc_lo; cc <= cc_hi; ++cc) {
+      const int st = cc - cc_lo;  // LDS stage
+      T* lk = ldsK + st * C::KBUF;
+      T* lv = ldsV + st * C::VBUF;
+      const int nk = cc == c ? nvalid : kChunk;
+      for (int idx = tid; idx < 64 * (DF / 8); idx += nthr) {
+        const int p = idx / (DF / 8), c8 = idx % (DF / 8);
         frag fx = TT::zero();
-        if (p < nkeys) fx = TT::load8(phik + (static_cast<long long>(bh) * T_ + tbase + p) * DF + c8 * 8);
-        TT::store8(pk_s + p * LDF + c8 * 8, fx);
+        if (p < nk) fx = TT::load8(phik + (static_cast<long long>(bh) * T_ + static_cast<long long>(cc) * kChunk + p) * DF + c8 * 8);
+        TT::store8(lk + p * LDK + c8 * 8, fx);
       }
-    }
-    __syncthreads();
-
-    // S^T = K Q^T
-    f32x4 s[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const frag ka = TT::load8(k_s + (kb * 16 + r16) * LDK + ks * 32 + grp * 8);
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) TT::mma(s[kb][qb], ka, qf[qb][ks]);
+      for (int idx = tid; idx < D * 8; idx += nthr) {
+        const int dd = idx / 8, c8 = idx % 8;
+        TT::store8(lv + dd * LDV + c8 * 8, TT::load8(vT + ((static_cast<long long>(bh) * d.nC + cc) * D + dd) * 64 + c8 * 8));
       }
-    }
-    // phi(K) phi(Q)^T where some keys go to linear attention
-    f32x4 ls[4][4];
-    if (need_phi) {
+      __syncthreads();
+      f32x4 ls[4][QB];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int fs = 0; fs < DF / 32; ++fs) {
-          const T* base = pk_s + (kb * 16 + r16) * LDF + fs * 32 + 4 * grp;
-          const frag fa = TT::join(TT::load4(base), TT::load4(base + 16));
+          const frag fa = TT::load8(lk + (kb * 16 + r16) * LDK + fs * 32 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+          for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
         }
       }
-    }
-
-    // online softmax + linear weights, per query column
-    frag pf[2][4];
+      frag pf[2][QB];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int r = qb * 16 + r16;
-      float mx = m_run[qb];
+      for (int qb = 0; qb < QB; ++qb) {
+        const int r = qoff + qb * 16 + r16;
+        float pv[4][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = kb * 16 + 4 * grp + i;
-          bool sa;
-          if (type == 0) sa = p < nkeys;
-          else if (type == 1) sa = (p > r + 64 - win) || ((selprev >> p) & 1ull);
-          else sa = p <= r && p > r - win;
-          if (sa) mx = fmaxf(mx, s[kb][qb][i] * c1);
-        }
-      mx = xor_max_groups(mx);
-      const float alpha = exp2f(m_run[qb] - mx);
-      m_run[qb] = mx;
-      l_run[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
-      const float la_scale = exp2f(-mx);
-      float pv[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = kb * 16 + 4 * grp + i;
-          bool sa, la;
-          if (type == 0) {
-            sa = p < nkeys;
-            la = false;
-          } else if (type == 1) {
-            sa = (p > r + 64 - win) || ((selprev >> p) & 1ull);
-            la = !sa;
-          } else {
-            sa = p <= r && p > r - win;
-            la = p <= r && !sa;
+          for (int i = 0; i < 4; ++i) {
+            const int p = kb * 16 + 4 * grp + i;
+            const bool la = cc == c ? (p <= r - win) : (p <= r + 64 - win && !((selprev >> p) & 1ull));
+            const float x = la ? ls[kb][qb][i] : 0.f;
+            pv[kb][i] = x;
+            den[qb] += x;
           }
-          float x = 0.f;
-          if (sa) x = exp2f(s[kb][qb][i] * c1 - mx);
-          else if (la && need_phi) x = la_scale * ls[kb][qb][i];
-          pv[kb][i] = x;
-          l_run[qb] += x;
-        }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[ks][qb][e] = TT::from_f(pv[2 * ks + e / 4][e % 4]);
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const T* base = vt_s + (db * 16 + r16) * LDV + ks * 32 + 4 * grp;
-        const frag va = TT::join(TT::load4(base), TT::load4(base + 16));
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) TT::mma(o[db][qb], va, pf[ks][qb]);
+          for (int e = 0; e < 8; ++e) pf[ks][qb][e] = TT::from_f(pv[2 * ks + e / 4][e % 4]);
       }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const frag va = TT::load8(lv + (db * 16 + r16) * LDV + ks * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[ks][qb]);
+        }
+    }
+    // the linear branch becomes one online-softmax entry: log-weight log2(D), value N / D
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float dt = xor_sum_groups(den[qb]);
+      const float inv = dt > 0.f ? 1.f / dt : 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db][qb] *= inv;
+      m_run[qb] = dt > 0.f ? __log2f(dt) : -kInf;
+      l_run[qb] = (dt > 0.f && grp == 0) ? 1.f : 0.f;
+    }
+    __syncthreads();  // LDS stages are reused by phase 2
+  }
+
+  // =============================== phase 2: softmax tiles ==============================
+  // 2a. the window tiles (chunk c causal, chunk c-1 mixed), loaded together, masked
+  if (win >= 1) {
+    const int nct = c >= 1 ? 2 : 1;
+    for (int ct = 0; ct < nct; ++ct) {
+      T* lk = ldsK + ct * C::KBUF;
+      T* lv = ldsV + ct * C::VBUF;
+      const long long tb = ct == 0 ? t0 : t0 - 64;
+      const int nk = ct == 0 ? nvalid : 64;
+      for (int idx = tid; idx < 64 * (D / 8); idx += nthr) {
+        const int p = idx / (D / 8), c8 = idx % (D / 8);
+        frag x = TT::zero();
+        if (p < nk) x = TT::load8(kk + ((b * T_ + tb + p) * d.Hkv + h) * D + c8 * 8);
+        TT::store8(lk + p * LDK + c8 * 8, x);
+      }
+      const T* src = vT + (static_cast<long long>(bh) * d.nC + (ct == 0 ? c : c - 1)) * D * 64;
+      for (int idx = tid; idx < D * 8; idx += nthr) {
+        const int dd = idx / 8, c8 = idx % 8;
+        TT::store8(lv + dd * LDV + c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
+      }
+    }
+    __syncthreads();
+    sa_tile<true, T, D, QB, LDK, LDV>(ldsK, ldsV, qf, o, m_run, l_run, c1, [&](int p, int qb) {
+      const int r = qoff + qb * 16 + r16;
+      return p <= r && p > r - win;
+    });
+    if (c >= 1) {
+      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
+      sa_tile<true, T, D, QB, LDK, LDV>(ldsK + C::KBUF, ldsV + C::VBUF, qf, o, m_run, l_run, c1,
+                                        [&](int p, int qb) {
+                                          const int r = qoff + qb * 16 + r16;
+                                          return (p > r + 64 - win) || ((selprev >> p) & 1ull);
+                                        });
+    }
+    __syncthreads();
+  }
+
+  // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
+  //     The next tile's loads are in flight while the current tile is computed.
+  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
+  const int nt_comp = (n_comp + 63) / 64;
+  const T* kbase = ksel + static_cast<long long>(bh) * d.nCc * d.topk * D;
+  const T* vbase = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
+  constexpr int KLD = D / 8;                        // 8-element pieces per K row
+  constexpr int NK16 = 64 * KLD;                    // pieces per K tile
+  constexpr int NV16 = D * 8;                       // pieces per V^T tile
+  constexpr int NPT = (NK16 + NV16 + NTHR - 1) / NTHR;
+  frag pre[NPT];                                    // the next tile, in flight
+  auto issue = [&](int t) {
+    const int rows = n_comp - t * 64;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * NTHR;
+      frag x = TT::zero();
+      if (idx < NK16) {
+        const int p = idx / KLD, c8 = idx % KLD;
+        if (p < rows) x = TT::load8(kbase + (static_cast<long long>(t) * 64 + p) * D + c8 * 8);
+      } else if (idx < NK16 + NV16) {
+        x = TT::load8(vbase + static_cast<long long>(t) * D * 64 + (idx - NK16) * 8);
+      }
+      pre[i] = x;
+    }
+  };
+  auto commit = [&](int stage) {
+    T* lk = ldsK + stage * C::KBUF;
+    T* lv = ldsV + stage * C::VBUF;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * NTHR;
+      if (idx < NK16) {
+        const int p = idx / KLD, c8 = idx % KLD;
+        TT::store8(lk + p * LDK + c8 * 8, pre[i]);
+      } else if (idx < NK16 + NV16) {
+        const int j = idx - NK16, dd = j / 8, c8 = j % 8;
+        TT::store8(lv + dd * LDV + c8 * 8, pre[i]);
+      }
+    }
+  };
+  constexpr bool kPrefetch = NPT <= 4;  // keep the in-flight tile in registers only if it is small
+  if (nt_comp > 0) {
+    issue(0);
+    commit(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < nt_comp; ++t) {
+    const int stage = t & 1;
+    if (kPrefetch && t + 1 < nt_comp) issue(t + 1);
+    const int nk = n_comp - t * 64;
+    if (nk >= 64) {
+      sa_tile<false, T, D, QB, LDK, LDV>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, l_run, c1,
+                                         [](int, int) { return true; });
+    } else {
+      sa_tile<true, T, D, QB, LDK, LDV>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, l_run, c1,
+                                        [nk](int p, int) { return p < nk; });
+    }
+    if (t + 1 < nt_comp) {
+      if (!kPrefetch) issue(t + 1);
+      commit(stage ^ 1);
+    }
+    __syncthreads();
   }
 
   // ---- epilogue: divide by the shared normaliser, write [B,T,Hq,D] ------------------
   T* out = static_cast<T*>(a.out);
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = xor_sum_groups(l_run[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int r = qb * 16 + r16;
+    const int r = qoff + qb * 16 + r16;
     if (head_ok && r < nvalid) {
       T* dst = out + ((b * T_ + t0 + r) * d.Hq + hq) * D + 4 * grp;
 #pragma unroll
@@ -309,23 +448,35 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int D, int DF>
-static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
+template <typename T, int D, int DF, int QW, int NH>
+static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
+  using C = AttnCfg<T, D, DF, QW, NH>;
   const int P = a.d.B * a.d.Hkv * a.gsplit;
   dim3 grid(a.d.nC * P);
-  hipLaunchKernelGGL((attn_kernel<T, D, DF>), grid, dim3(64 * a.nw), 0, s, a);
+  if (C::LDS_BYTES > 65536)  // opt in to more than 64 KiB of LDS (gfx950 has 160 KiB per CU)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, QW, NH>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  hipLaunchKernelGGL((attn_kernel<T, D, DF, QW, NH>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int DF, int QW>
+static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
+  if (a.nw == 4) return attn_nh<T, D, DF, QW, 4>(a, s);
+  if (a.nw == 2) return attn_nh<T, D, DF, QW, 2>(a, s);
+  if (a.nw == 1) return attn_nh<T, D, DF, QW, 1>(a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const Dims& dd = a.d;
   if (dd.bf16) {
-    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64>(a, s);
-    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128>(a, s);
-    if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64>(a, s);
-    if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128>(a, s);
+    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64, 64>(a, s);
+    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128, 64>(a, s);
+    if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64, 32>(a, s);
+    if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128, 32>(a, s);
   } else if (dd.D == 64 && dd.DF == 64) {
-    return attn_t<float, 64, 64>(a, s);
+    return attn_t<float, 64, 64, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -24,25 +24,28 @@ struct PrepArgs {
   float* sal;                 // [B,Hkv,T]
   uint64_t* selmask;          // [B,Hkv,nC]
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
-  void* ksel;                 // [B,Hkv,nCc*topk,D]
-  void* vsel;
-  void* phik;                 // [B,Hkv,T,DF]
+  void* ksel;                 // [B,Hkv,nCc*topk,D]: compact K rows
+  void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
   float* states;              // [B,Hkv,nC,R]
+  void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos
+  void* vselT;                // [B,Hkv,ntiles_sel,D,64]: compact V rows, same tile layout
+  int ntiles_sel;             // ceil(nCc*topk / 64)
 };
 
 struct AttnArgs {
   Dims d;
   const void* q;
   const void* k;
-  const void* v;
   const void* w;
   const uint64_t* selmask;
   const void* ksel;
-  const void* vsel;
+  const void* vselT;
+  const void* vT;
   const void* phik;
   const float* states;  // inclusive prefix over complete chunks
   void* out;
-  int nw;               // waves per workgroup (query heads per workgroup)
+  int ntiles_sel;
+  int nw;               // query heads per workgroup (1, 2 or 4)
   int gsplit;           // workgroups per (b, kv head, chunk)
 };
 

@@ -13,6 +13,7 @@
 //      phi(k) v^T and u_c = sum phi(k) ([P3] on the fixed-size state of linear attention).
 // scan_kernel then turns the U_c into inclusive prefix sums over chunks.
 #include "still_launch.hpp"
+#include "still_layout.hpp"
 #include "still_route.hpp"
 
 namespace still {
@@ -122,22 +123,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (complete && d.topk > 0) {
     const int nsel = __popcll(smask);
     T* ks_ = static_cast<T*>(a.ksel);
-    T* vs_ = static_cast<T*>(a.vsel);
     for (int idx = tid; idx < d.topk * V8; idx += 256) {
       const int slot = idx / V8, c8 = idx % V8;
       const long long dst = (static_cast<long long>(bh) * nsel_rows + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
-      frag kx = TT::zero(), vx = TT::zero();
-      if (slot < nsel) {
-        const long long src = ((b * T_ + t0 + selpos[slot]) * d.Hkv + h) * D + c8 * 8;
-        kx = TT::load8(k + src);
-        vx = TT::load8(v + src);
-      }
+      frag kx = TT::zero();
+      if (slot < nsel) kx = TT::load8(k + ((b * T_ + t0 + selpos[slot]) * d.Hkv + h) * D + c8 * 8);
       TT::store8(ks_ + dst, kx);
-      TT::store8(vs_ + dst, vx);
     }
   }
 
-  // 5. store phi(k) (rounded to T); keep the rounded values of unselected keys for U_c
+  // 5. store phi(k) (rounded to T, features permuted by pk_pos); keep the rounded values
+  //    of unselected keys for U_c
   T* phik = static_cast<T*>(a.phik);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -148,17 +144,56 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const int row = kb * 16 + 4 * grp + i;
         const int f = (wave * FPW + fi) * 16 + r16;
         const T val = TT::from_f(phi[kb][fi][i]);
-        if (row < nvalid) phik[(static_cast<long long>(bh) * T_ + t0 + row) * DF + f] = val;
+        if (row < nvalid) phik[(static_cast<long long>(bh) * T_ + t0 + row) * DF + pk_pos(f)] = val;
         phi[kb][fi][i] = ((smask >> row) & 1ull) ? 0.f : TT::to_f(val);
       }
 
-  // 6. U_c^T = V_c^T phi_masked and u_c, for complete chunks
-  if (!complete) return;  // uniform across the workgroup
+  // 6. V of the chunk: stage in LDS (zero past the sequence end), write the transposed,
+  //    key-permuted copy vT, and the compact transposed copy of the selected rows
   for (int idx = tid; idx < 64 * V8; idx += 256) {
     const int row = idx / V8, c8 = idx % V8;
-    TT::store8(band + row * LDK + c8 * 8, TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8));
+    frag x = TT::zero();
+    if (row < nvalid) x = TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8);
+    TT::store8(band + row * LDK + c8 * 8, x);
   }
   __syncthreads();
+  {
+    T* vt = static_cast<T*>(a.vT) + (static_cast<long long>(bh) * d.nC + c) * D * 64;
+    for (int idx = tid; idx < D * 8; idx += 256) {
+      const int dd = idx / 8, pb = idx % 8;  // output positions 8*pb .. 8*pb+7 of row dd
+      frag x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // position 8*pb + e holds key 32*(pb/4) + 16*(e/4) + 4*(pb%4) + e%4
+        const int key = 32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4);
+        x[e] = band[key * LDK + dd];
+      }
+      TT::store8(vt + dd * 64 + pb * 8, x);
+    }
+    if (complete && d.topk > 0) {
+      T* vs = static_cast<T*>(a.vselT) + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
+      const int nsel = __popcll(smask);
+      for (int idx = tid; idx < d.topk * D; idx += 256) {
+        const int slot = idx / D, dd = idx % D;
+        const long long r = static_cast<long long>(c) * d.topk + slot;  // compact row
+        const T x = slot < nsel ? band[selpos[slot] * LDK + dd] : TT::from_f(0.f);
+        vs[((r / 64) * D + dd) * 64 + pk_pos(static_cast<int>(r % 64))] = x;
+      }
+      // the last compact tile's unused columns are zero (they meet zero weights)
+      const long long n_rows = nsel_rows;
+      if (c == d.nCc - 1 && (n_rows % 64) != 0) {
+        const long long tl = n_rows / 64;
+        const int used = static_cast<int>(n_rows % 64);
+        for (int idx = tid; idx < (64 - used) * D; idx += 256) {
+          const int col = used + idx / D, dd = idx % D;
+          vs[(tl * D + dd) * 64 + pk_pos(col)] = TT::from_f(0.f);
+        }
+      }
+    }
+  }
+
+  // 7. U_c^T = V_c^T phi_masked and u_c, for complete chunks
+  if (!complete) return;  // uniform across the workgroup
   f32x4 u[D / 16][FPW];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
