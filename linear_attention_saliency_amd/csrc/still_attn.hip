@@ -17,97 +17,103 @@
 // enters the online softmax as one entry of log-weight log2(D) and value N / D, so the
 // shared-normaliser output  (sum_SA e^a v + N) / (sum_SA e^a + D)  needs no offset and
 // cannot overflow whatever the magnitudes.
-// Phase 2 (softmax): chunk c, chunk c-1, then the compact tiles, 64 keys per tile, with
-// the next tile's global loads in flight (registers) while the current one is computed
-// from LDS (double buffer). The running max is refreshed only when a tile's max exceeds
-// it by more than 8 (log2 units), so most tiles skip the rescale.
+// Phase 2 (softmax): the two window tiles (masked), then the compact tiles, 64 keys per
+// tile, with the next tile's global loads in flight while the current one is computed
+// from a double-buffered LDS stage. The running max is refreshed only when a tile's max
+// exceeds it by more than 8 (log2 units), so the rescale is rare.
 //
 // Everything is computed transposed (S^T = K Q^T, O^T += V^T P^T): a query is a lane's
 // column, so its statistics need only the 4-lane-group reduction, and P leaves the
-// softmax in the register layout the PV product consumes. V tiles arrive transposed and
-// key-permuted from the prep kernel, phi(K) rows feature-permuted, so every LDS operand
-// fragment is a single 16-byte read.
+// softmax in the register layout the PV product consumes. The row sums of P ride along
+// in the PV product as one extra 16-row block whose A operand is all ones. V tiles arrive
+// transposed and key-permuted from the prep kernel, phi(K) rows feature-permuted, so
+// every LDS operand fragment is a single 16-byte read.
 #include "still_launch.hpp"
 #include "still_layout.hpp"
 #include "still_route.hpp"
 
 namespace still {
 
-// One 64-key softmax tile for one wave, in two 32-key halves (half hs covers key blocks
-// 2hs and 2hs+1, which is exactly k-slice hs of the PV product, so each half runs
-// S^T = K Q^T, mask, online softmax and O^T += V^T P^T on its own and only half a tile
-// of scores is ever live). K rows come from lk, V^T rows from lv. The running max is
-// refreshed only when a half's max exceeds it by more than 8 (log2 units).
+template <typename T> __device__ __forceinline__ typename Tr<T>::frag ones_frag() {
+  typename Tr<T>::frag x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = Tr<T>::from_f(1.0f);
+  return x;
+}
+
+// One 64-key softmax tile for one wave. S^T = K Q^T (K rows from lk), mask (if MASKED),
+// online softmax with a lazily refreshed running max, then O^T += V^T P^T in two 32-key
+// halves (V^T rows from lv). o[D/16][*] is the row-sum block: every entry holds the
+// running denominator of the lane's query.
 // keep(p, qb): whether key p of the tile is in the softmax set of the lane's query in
 // block qb (used when MASKED).
-template <bool MASKED, typename T, int D, int QB, int LDK, int LDV, typename Keep>
+template <bool MASKED, typename T, int D, int QB, typename Keep>
 __device__ __forceinline__ void sa_tile(const T* lk, const T* lv, const typename Tr<T>::frag (&qf)[QB][D / 32],
-                                        f32x4 (&o)[D / 16][QB], float (&m_run)[QB], float (&l_run)[QB],
-                                        float c1, Keep keep) {
+                                        f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB], float c1, Keep keep) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  f32x4 s[4][QB];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(s[kb][qb], ka, qf[qb][ks]);
+    }
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!keep(kb * 16 + 4 * grp + i, qb)) s[kb][qb][i] = -kInf;
+  }
+  bool need_any = false;
+  float alpha[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float tm = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
+                     fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
+    tm = fmaxf(tm, fmaxf(fmaxf(fmaxf(s[2][qb][0], s[2][qb][1]), fmaxf(s[2][qb][2], s[2][qb][3])),
+                         fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), fmaxf(s[3][qb][2], s[3][qb][3]))));
+    tm = xor_max_groups(tm) * c1;
+    const bool need = tm > m_run[qb] + 8.f;
+    alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
+    m_run[qb] = need ? tm : m_run[qb];
+    need_any |= need;
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db <= D / 16; ++db) o[db][qb] *= alpha[qb];
+  }
+  float mq[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mq[qb] = m_run[qb] == -kInf ? 0.f : m_run[qb];
+  const frag one = ones_frag<T>();
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
-    f32x4 s[2][QB];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kb = 2 * hs + j;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[j][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const frag ka = TT::load8(lk + (kb * 16 + r16) * LDK + ks * 32 + grp * 8);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TT::mma(s[j][qb], ka, qf[qb][ks]);
-      }
-    }
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!keep((2 * hs + j) * 16 + 4 * grp + i, qb)) s[j][qb][i] = -kInf;
-    }
-    bool need_any = false;
-    float alpha[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float tm = fmaxf(fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), fmaxf(s[0][qb][2], s[0][qb][3])),
-                       fmaxf(fmaxf(s[1][qb][0], s[1][qb][1]), fmaxf(s[1][qb][2], s[1][qb][3])));
-      tm = xor_max_groups(tm) * c1;
-      const bool need = tm > m_run[qb] + 8.f;
-      alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
-      m_run[qb] = need ? tm : m_run[qb];
-      need_any |= need;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        l_run[qb] *= alpha[qb];
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha[qb];
-      }
-    }
     frag pf[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mq = m_run[qb] == -kInf ? 0.f : m_run[qb];
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = __builtin_amdgcn_exp2f(s[e / 4][qb][e % 4] * c1 - mq);
-        l_run[qb] += x;
-        pf[qb][e] = TT::from_f(x);
-      }
-    }
+      for (int e = 0; e < 8; ++e)
+        pf[qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[2 * hs + e / 4][qb][e % 4] * c1 - mq[qb]));
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const frag va = TT::load8(lv + (db * 16 + r16) * LDV + hs * 32 + grp * 8);
+      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) TT::mma(o[D / 16][qb], one, pf[qb]);
   }
 }
 
@@ -116,22 +122,24 @@ struct AttnCfg {
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
   static constexpr int WPH = 64 / QW;          // waves per query head
   static constexpr int NTHR = 64 * WPH * NH;   // threads per workgroup
-  static constexpr int LDK = pitch<T>(D > DF ? D : DF);
-  static constexpr int LDV = pitch<T>(64);
-  static constexpr int KBUF = 64 * LDK;        // elements of one K / phi(K) stage
-  static constexpr int VBUF = D * LDV;         // elements of one V^T stage
+  static constexpr int KBUF = 64 * (D > DF ? D : DF);  // elements of one K / phi(K) stage
+  static constexpr int VBUF = D * 64;                  // elements of one V^T stage
   static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * static_cast<int>(sizeof(T));
 };
 
 template <typename T, int D, int DF, int QW, int NH>
 __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a) {
   using C = AttnCfg<T, D, DF, QW, NH>;
-  constexpr int QB = C::QB, WPH = C::WPH, LDK = C::LDK, LDV = C::LDV, NTHR = C::NTHR;
+  constexpr int QB = C::QB, WPH = C::WPH, NTHR = C::NTHR;
+  using SK = Swz<T, D>;    // K tile: 64 keys x D
+  using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF; prefix state: D rows x DF
+  using SV = Swz<T, 64>;   // V^T tile: D rows x 64 keys
+  constexpr int NB = D / 16;  // output blocks; block NB holds the row sums
   using TT = Tr<T>;
   using frag = typename TT::frag;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-  T* ldsK = reinterpret_cast<T*>(lds_raw);        // [2][64][LDK]
-  T* ldsV = ldsK + 2 * C::KBUF;                    // [2][D][LDV]
+  T* ldsK = reinterpret_cast<T*>(lds_raw);        // 2 stages of KBUF
+  T* ldsV = ldsK + 2 * C::KBUF;                    // 2 stages of VBUF
 
   const Dims& d = a.d;
   const T* q = static_cast<const T*>(a.q);
@@ -148,7 +156,6 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   const int gs = pi % a.gsplit, bh = pi / a.gsplit;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  constexpr int nthr = NTHR;
   const int g = gs * NH + wave / WPH;
   const int qoff = (wave % WPH) * QW;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
@@ -169,12 +176,12 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
       qf[qb][ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
   }
 
-  f32x4 o[D / 16][QB];
-  float m_run[QB], l_run[QB];
+  f32x4 o[NB + 1][QB];
+  float m_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db <= NB; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // =============================== phase 1: linear attention ===========================
   {
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float zv = pacc[fb][i];
-          const float mv = zv > 0.f ? zv + 1.f : expf(zv);
+          const float mv = zv > 0.f ? zv + 1.f : __builtin_amdgcn_exp2f(zv * kLog2e);
           pacc[fb][i] = mv;
           m2 += mv * mv;
         }
@@ -224,22 +231,21 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
     // and z[f] (fp32), with coalesced loads, then contracted on MFMA
     if (c >= 2) {
       const float* S = a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R;
-      constexpr int LDS_ = pitch<T>(DF);
-      T* st = ldsK;  // D rows of LDS_ elements: fits in the two K stages (128 rows of >= DF + pad)
+      T* st = ldsK;  // D rows of DF elements: fits in the two K stages (128 rows of >= DF)
       float* zs = reinterpret_cast<float*>(ldsV);
-      for (int idx = tid; idx < DF * D / 4; idx += nthr) {
+      for (int idx = tid; idx < DF * D / 4; idx += NTHR) {
         const int f = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
         const f32x4 x = *reinterpret_cast<const f32x4*>(S + f * D + d4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st[(d4 + j) * LDS_ + pk_pos(f)] = TT::from_f(x[j]);
+        for (int j = 0; j < 4; ++j) st[SF::off(d4 + j, pk_pos(f))] = TT::from_f(x[j]);
       }
-      for (int idx = tid; idx < DF; idx += nthr) zs[idx] = S[DF * D + idx];
+      for (int idx = tid; idx < DF; idx += NTHR) zs[idx] = S[DF * D + idx];
       __syncthreads();
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs) {
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const frag sa = TT::load8(st + (db * 16 + r16) * LDS_ + fs * 32 + grp * 8);
+        for (int db = 0; db < NB; ++db) {
+          const frag sa = SF::load8(st, db * 16 + r16, fs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
         }
@@ -261,15 +267,15 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
       T* lk = ldsK + st * C::KBUF;
       T* lv = ldsV + st * C::VBUF;
       const int nk = cc == c ? nvalid : kChunk;
-      for (int idx = tid; idx < 64 * (DF / 8); idx += nthr) {
+      for (int idx = tid; idx < 64 * (DF / 8); idx += NTHR) {
         const int p = idx / (DF / 8), c8 = idx % (DF / 8);
         frag fx = TT::zero();
         if (p < nk) fx = TT::load8(phik + (static_cast<long long>(bh) * T_ + static_cast<long long>(cc) * kChunk + p) * DF + c8 * 8);
-        TT::store8(lk + p * LDK + c8 * 8, fx);
+        SF::store8(lk, p, c8 * 8, fx);
       }
-      for (int idx = tid; idx < D * 8; idx += nthr) {
+      for (int idx = tid; idx < D * 8; idx += NTHR) {
         const int dd = idx / 8, c8 = idx % 8;
-        TT::store8(lv + dd * LDV + c8 * 8, TT::load8(vT + ((static_cast<long long>(bh) * d.nC + cc) * D + dd) * 64 + c8 * 8));
+        SV::store8(lv, dd, c8 * 8, TT::load8(vT + ((static_cast<long long>(bh) * d.nC + cc) * D + dd) * 64 + c8 * 8));
       }
       __syncthreads();
       f32x4 ls[4][QB];
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
         for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int fs = 0; fs < DF / 32; ++fs) {
-          const frag fa = TT::load8(lk + (kb * 16 + r16) * LDK + fs * 32 + grp * 8);
+          const frag fa = SF::load8(lk, kb * 16 + r16, fs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
         }
@@ -305,10 +311,10 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
           for (int e = 0; e < 8; ++e) pf[ks][qb][e] = TT::from_f(pv[2 * ks + e / 4][e % 4]);
       }
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
+      for (int db = 0; db < NB; ++db)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const frag va = TT::load8(lv + (db * 16 + r16) * LDV + ks * 32 + grp * 8);
+          const frag va = SV::load8(lv, db * 16 + r16, ks * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[ks][qb]);
         }
@@ -319,9 +325,10 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
       const float dt = xor_sum_groups(den[qb]);
       const float inv = dt > 0.f ? 1.f / dt : 0.f;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] *= inv;
+      for (int db = 0; db < NB; ++db) o[db][qb] *= inv;
       m_run[qb] = dt > 0.f ? __log2f(dt) : -kInf;
-      l_run[qb] = (dt > 0.f && grp == 0) ? 1.f : 0.f;
+      const float l0 = dt > 0.f ? 1.f : 0.f;
+      o[NB][qb] = f32x4{l0, l0, l0, l0};
     }
     __syncthreads();  // LDS stages are reused by phase 2
   }
@@ -335,30 +342,29 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
       T* lv = ldsV + ct * C::VBUF;
       const long long tb = ct == 0 ? t0 : t0 - 64;
       const int nk = ct == 0 ? nvalid : 64;
-      for (int idx = tid; idx < 64 * (D / 8); idx += nthr) {
+      for (int idx = tid; idx < 64 * (D / 8); idx += NTHR) {
         const int p = idx / (D / 8), c8 = idx % (D / 8);
         frag x = TT::zero();
         if (p < nk) x = TT::load8(kk + ((b * T_ + tb + p) * d.Hkv + h) * D + c8 * 8);
-        TT::store8(lk + p * LDK + c8 * 8, x);
+        SK::store8(lk, p, c8 * 8, x);
       }
       const T* src = vT + (static_cast<long long>(bh) * d.nC + (ct == 0 ? c : c - 1)) * D * 64;
-      for (int idx = tid; idx < D * 8; idx += nthr) {
+      for (int idx = tid; idx < D * 8; idx += NTHR) {
         const int dd = idx / 8, c8 = idx % 8;
-        TT::store8(lv + dd * LDV + c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
+        SV::store8(lv, dd, c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
       }
     }
     __syncthreads();
-    sa_tile<true, T, D, QB, LDK, LDV>(ldsK, ldsV, qf, o, m_run, l_run, c1, [&](int p, int qb) {
+    sa_tile<true, T, D, QB>(ldsK, ldsV, qf, o, m_run, c1, [&](int p, int qb) {
       const int r = qoff + qb * 16 + r16;
       return p <= r && p > r - win;
     });
     if (c >= 1) {
       const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
-      sa_tile<true, T, D, QB, LDK, LDV>(ldsK + C::KBUF, ldsV + C::VBUF, qf, o, m_run, l_run, c1,
-                                        [&](int p, int qb) {
-                                          const int r = qoff + qb * 16 + r16;
-                                          return (p > r + 64 - win) || ((selprev >> p) & 1ull);
-                                        });
+      sa_tile<true, T, D, QB>(ldsK + C::KBUF, ldsV + C::VBUF, qf, o, m_run, c1, [&](int p, int qb) {
+        const int r = qoff + qb * 16 + r16;
+        return (p > r + 64 - win) || ((selprev >> p) & 1ull);
+      });
     }
     __syncthreads();
   }
@@ -367,41 +373,52 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   //     The next tile's loads are in flight while the current tile is computed.
   const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
   const int nt_comp = (n_comp + 63) / 64;
-  const T* kbase = ksel + static_cast<long long>(bh) * d.nCc * d.topk * D;
-  const T* vbase = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
   constexpr int KLD = D / 8;                        // 8-element pieces per K row
   constexpr int NK16 = 64 * KLD;                    // pieces per K tile
   constexpr int NV16 = D * 8;                       // pieces per V^T tile
   constexpr int NPT = (NK16 + NV16 + NTHR - 1) / NTHR;
-  frag pre[NPT];                                    // the next tile, in flight
+  // per-thread piece geometry, fixed across tiles: global offset within a tile, and the
+  // tile row / column the piece lands on in LDS (K row = key, V^T row = d)
+  long long goff[NPT];
+  int prow[NPT], pcol[NPT];
+  bool isk[NPT], live[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int idx = tid + i * NTHR;
+    live[i] = idx < NK16 + NV16;
+    isk[i] = idx < NK16;
+    if (isk[i]) {
+      const int p = idx / KLD, c8 = idx % KLD;
+      goff[i] = static_cast<long long>(p) * D + c8 * 8;
+      prow[i] = p;
+      pcol[i] = c8 * 8;
+    } else {
+      const int j = idx - NK16, dd = j / 8, c8 = j % 8;
+      goff[i] = static_cast<long long>(j) * 8;
+      prow[i] = dd;
+      pcol[i] = c8 * 8;
+    }
+  }
+  const T* kb_ptr = ksel + static_cast<long long>(bh) * d.nCc * d.topk * D;
+  const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
+  frag pre[NPT];  // the next tile, in flight
   auto issue = [&](int t) {
     const int rows = n_comp - t * 64;
+    const T* kt = kb_ptr + static_cast<long long>(t) * 64 * D;
+    const T* vt = vb_ptr + static_cast<long long>(t) * D * 64;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int idx = tid + i * NTHR;
       frag x = TT::zero();
-      if (idx < NK16) {
-        const int p = idx / KLD, c8 = idx % KLD;
-        if (p < rows) x = TT::load8(kbase + (static_cast<long long>(t) * 64 + p) * D + c8 * 8);
-      } else if (idx < NK16 + NV16) {
-        x = TT::load8(vbase + static_cast<long long>(t) * D * 64 + (idx - NK16) * 8);
-      }
+      if (live[i] && (isk[i] ? prow[i] < rows : true)) x = TT::load8((isk[i] ? kt : vt) + goff[i]);
       pre[i] = x;
     }
   };
   auto commit = [&](int stage) {
-    T* lk = ldsK + stage * C::KBUF;
-    T* lv = ldsV + stage * C::VBUF;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int idx = tid + i * NTHR;
-      if (idx < NK16) {
-        const int p = idx / KLD, c8 = idx % KLD;
-        TT::store8(lk + p * LDK + c8 * 8, pre[i]);
-      } else if (idx < NK16 + NV16) {
-        const int j = idx - NK16, dd = j / 8, c8 = j % 8;
-        TT::store8(lv + dd * LDV + c8 * 8, pre[i]);
-      }
+      if (!live[i]) continue;
+      if (isk[i]) SK::store8(ldsK + stage * C::KBUF, prow[i], pcol[i], pre[i]);
+      else SV::store8(ldsV + stage * C::VBUF, prow[i], pcol[i], pre[i]);
     }
   };
   constexpr bool kPrefetch = NPT <= 4;  // keep the in-flight tile in registers only if it is small
@@ -415,10 +432,10 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
     if (kPrefetch && t + 1 < nt_comp) issue(t + 1);
     const int nk = n_comp - t * 64;
     if (nk >= 64) {
-      sa_tile<false, T, D, QB, LDK, LDV>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, l_run, c1,
+      sa_tile<false, T, D, QB>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, c1,
                                          [](int, int) { return true; });
     } else {
-      sa_tile<true, T, D, QB, LDK, LDV>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, l_run, c1,
+      sa_tile<true, T, D, QB>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, c1,
                                         [nk](int p, int) { return p < nk; });
     }
     if (t + 1 < nt_comp) {
@@ -432,13 +449,13 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   T* out = static_cast<T*>(a.out);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = xor_sum_groups(l_run[qb]);
+    const float lt = o[NB][qb][0];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int r = qoff + qb * 16 + r16;
     if (head_ok && r < nvalid) {
       T* dst = out + ((b * T_ + t0 + r) * d.Hq + hq) * D + 4 * grp;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
+      for (int db = 0; db < NB; ++db) {
         typename TT::quad ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = TT::from_f(o[db][qb][i] * inv);
@@ -471,12 +488,12 @@ static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const Dims& dd = a.d;
   if (dd.bf16) {
-    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64, 64>(a, s);
-    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128, 64>(a, s);
+    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64, 32>(a, s);
+    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128, 32>(a, s);
     if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64, 32>(a, s);
     if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128, 32>(a, s);
   } else if (dd.D == 64 && dd.DF == 64) {
-    return attn_t<float, 64, 64, 64>(a, s);
+    return attn_t<float, 64, 64, 32>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -74,20 +74,65 @@ template <> struct Tr<float> {
   static __device__ __forceinline__ float from_f(float x) { return x; }
 };
 
+// ---- LDS tiles ----------------------------------------------------------------------
+// An LDS tile of rows of RL elements, stored in 16-byte granules whose index is XORed
+// with the low bits of the row (granules per row NG; mask 7 for 128-byte rows, 15 for
+// 256-byte and longer rows). Sixteen lanes reading one granule column of sixteen rows,
+// and lanes writing whole rows, then run at full LDS bandwidth on gfx950 (a padded
+// row pitch halves it, an unpadded unswizzled one quarters it: measured).
+template <typename T, int RL>
+struct Swz {
+  static constexpr int EPG = 16 / static_cast<int>(sizeof(T));  // elements per granule
+  static constexpr int NG = RL / EPG;                            // granules per row
+  static constexpr int MASK = NG >= 16 ? 15 : NG - 1;
+  static_assert(RL % EPG == 0 && NG >= 8, "rows must hold at least 8 granules");
+  // element offset of (row, col)
+  static __device__ __forceinline__ int off(int row, int col) {
+    return row * RL + (((col / EPG) ^ (row & MASK)) * EPG) + (col % EPG);
+  }
+  // 8 consecutive elements starting at a column that is a multiple of 8
+  static __device__ __forceinline__ typename Tr<T>::frag load8(const T* base, int row, int col) {
+    if constexpr (EPG == 8) {
+      return Tr<T>::load8(base + off(row, col));
+    } else {
+      return Tr<T>::join(Tr<T>::load4(base + off(row, col)), Tr<T>::load4(base + off(row, col + 4)));
+    }
+  }
+  static __device__ __forceinline__ void store8(T* base, int row, int col, const typename Tr<T>::frag& x) {
+    if constexpr (EPG == 8) {
+      Tr<T>::store8(base + off(row, col), x);
+    } else {
+      *reinterpret_cast<typename Tr<T>::quad*>(base + off(row, col)) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+      *reinterpret_cast<typename Tr<T>::quad*>(base + off(row, col + 4)) = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    }
+  }
+};
+
 // ---- wave64 cross-lane helpers -------------------------------------------------------
 
-__device__ __forceinline__ float xor_max_groups(float x) {
-  // max over the 4 lanes {l, l^16, l^32, l^48}
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+// Reductions over the 4 lanes {l, l^16, l^32, l^48} without LDS traffic:
+// v_permlane16_swap(x, x) leaves {x[l], x[l^16]} in its two results for every lane l,
+// v_permlane32_swap(x, x) leaves {x[l], x[l^32]}; combining the pair reduces one step.
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float xor_sum_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
+__device__ __forceinline__ float xor_max_groups(float x) { return pair32_max(pair16_max(x)); }
+
+__device__ __forceinline__ float xor_sum_groups(float x) { return pair32_sum(pair16_sum(x)); }
 
 __device__ __forceinline__ float xor_sum_16(float x) {
   // sum over the 16 lanes that share l / 16

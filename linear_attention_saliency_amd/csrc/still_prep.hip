@@ -20,13 +20,13 @@ namespace still {
 
 template <typename T, int D, int DF>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-  constexpr int LDK = pitch<T>(D);
   constexpr int FPW = DF / 64;
   constexpr int V8 = D / 8;
   using TT = Tr<T>;
   using frag = typename TT::frag;
+  using SW = Swz<T, D>;
 
-  __shared__ __attribute__((aligned(16))) T band[128 * LDK];
+  __shared__ __attribute__((aligned(16))) T band[128 * D];
   __shared__ float s_part[4][64];
   __shared__ float s_acc[64];
   __shared__ float m2part[4 * 64];
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const long long pos = t0 - 63 + row;
     frag x = TT::zero();
     if (row < 127 && pos >= 0 && pos < T_) x = TT::load8(k + ((b * T_ + pos) * d.Hkv + h) * D + c8 * 8);
-    TT::store8(band + row * LDK + c8 * 8, x);
+    SW::store8(band, row, c8 * 8, x);
   }
   __syncthreads();
 
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks)
             qf[ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
-          const float sv = saliency_qblock<T, D, LDK>(band, qf, qb, d.window, t0 - 63, scale);
+          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale);
           if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
         }
       }
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
   // 3. NP-Map of the chunk's keys (band rows 63..126)
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF, LDK>(band + 63 * LDK, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(band, 63, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
 
   // 4. routing of a complete chunk
   const long long nsel_rows = static_cast<long long>(d.nCc) * d.topk;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int row = idx / V8, c8 = idx % V8;
     frag x = TT::zero();
     if (row < nvalid) x = TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8);
-    TT::store8(band + row * LDK + c8 * 8, x);
+    SW::store8(band, row, c8 * 8, x);
   }
   __syncthreads();
   {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int e = 0; e < 8; ++e) {
         // position 8*pb + e holds key 32*(pb/4) + 16*(e/4) + 4*(pb%4) + e%4
         const int key = 32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4);
-        x[e] = band[key * LDK + dd];
+        x[e] = band[SW::off(key, dd)];
       }
       TT::store8(vt + dd * 64 + pb * 8, x);
     }
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int idx = tid; idx < d.topk * D; idx += 256) {
         const int slot = idx / D, dd = idx % D;
         const long long r = static_cast<long long>(c) * d.topk + slot;  // compact row
-        const T x = slot < nsel ? band[selpos[slot] * LDK + dd] : TT::from_f(0.f);
+        const T x = slot < nsel ? band[SW::off(selpos[slot], dd)] : TT::from_f(0.f);
         vs[((r / 64) * D + dd) * 64 + pk_pos(static_cast<int>(r % 64))] = x;
       }
       // the last compact tile's unused columns are zero (they meet zero weights)
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     for (int db = 0; db < D / 16; ++db) {
       frag av;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = band[(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4)) * LDK + db * 16 + r16];
+      for (int e = 0; e < 8; ++e) av[e] = band[SW::off(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4), db * 16 + r16)];
 #pragma unroll
       for (int fi = 0; fi < FPW; ++fi) TT::mma(u[db][fi], av, pb[fi]);
     }
@@ -265,11 +265,10 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* sal, int32_t* sel
 // Standalone NP-Map: one workgroup per (64-row tile of positions, batch, KV head).
 template <typename T, int D, int DF>
 __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv, const void* wv, float* phi_out) {
-  constexpr int LDK = pitch<T>(D);
   constexpr int FPW = DF / 64;
   constexpr int V8 = D / 8;
   using TT = Tr<T>;
-  __shared__ __attribute__((aligned(16))) T rows[64 * LDK];
+  __shared__ __attribute__((aligned(16))) T rows[64 * D];
   __shared__ float m2part[4 * 64];
   __shared__ float xn2[64];
   const T* x = static_cast<const T*>(xv);
@@ -281,11 +280,11 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
     const int row = idx / V8, c8 = idx % V8;
     typename TT::frag val = TT::zero();
     if (t0 + row < T_) val = TT::load8(x + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8);
-    TT::store8(rows + row * LDK + c8 * 8, val);
+    Swz<T, D>::store8(rows, row, c8 * 8, val);
   }
   __syncthreads();
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF, LDK>(rows, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(rows, 0, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll

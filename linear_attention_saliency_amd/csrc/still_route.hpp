@@ -10,13 +10,11 @@ namespace still {
 
 constexpr int kChunk = 64;
 
-// LDS row pitch (elements) for a row of n elements: 16 bytes of padding.
-template <typename T> constexpr int pitch(int n) { return n + 16 / static_cast<int>(sizeof(T)); }
 
 // Self-Saliency Score of 16 queries of one query head
 // ([P1] section "Self-Saliency Score"; [P4] section Approach).
 //
-// `band` holds 128 key rows (pitch LDK): row t is the key at position band_pos0 + t, with
+// `band` holds 128 key rows (a Swz<T, D> tile): row t is the key at position band_pos0 + t, with
 // band_pos0 = chunk_start - 63 (rows outside the sequence are zero and masked here).
 // Query r of the chunk (its position is chunk_start + r) sits at band row r + 63, so its
 // window is band rows [r + 64 - w, r + 63]. qf holds the B-operand (SK) fragments of the
@@ -25,7 +23,7 @@ template <typename T> constexpr int pitch(int n) { return n + 16 / static_cast<i
 // For query i: M' = max over the window without i, Z' = sum over the window without i of
 // e^{a - M'}, and s_i = LSE(W_i) - LSE(W_i \ i) = softplus(a_ii - M' - log Z'), which is
 // +inf when i is alone in its window. Returned in every lane of the query's column.
-template <typename T, int D, int LDK>
+template <typename T, int D>
 __device__ __forceinline__ float saliency_qblock(const T* band, const typename Tr<T>::frag (&qf)[D / 32],
                                                  int qb, int window, long long band_pos0, float scale) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
@@ -35,7 +33,7 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const typename Tr<T>::frag a = Tr<T>::load8(band + ((qb + j) * 16 + r16) * LDK + ks * 32 + grp * 8);
+      const typename Tr<T>::frag a = Swz<T, D>::load8(band, (qb + j) * 16 + r16, ks * 32 + grp * 8);
       Tr<T>::mma(acc[j], a, qf[ks]);
     }
   }
@@ -91,20 +89,20 @@ __device__ __forceinline__ uint64_t topk_mask(float s, int topk) {
 // NP-Map of 64 rows ([P1] section "Norm-Preserved Feature Map（NP-Map）"; [P4] section
 // Approach): phi(x) = |x| m / |m|, m = elu(W_h x) + 1.
 //
-// rows: 64 rows of D elements in LDS (pitch LDK). Wh: W_h in global memory [DF][D].
+// rows: rows row0 .. row0+63 of a Swz<T, D> LDS tile. Wh: W_h in global memory [DF][D].
 // Four waves; wave w owns feature blocks fb = w*FPW + fi (FPW = DF/64). On return
 // phi[kb][fi][i] = phi(row kb*16 + 4*grp + i)[feature fb*16 + r16] in fp32.
 // Scratch in LDS: m2part[4*64], xn2[64]. Contains one __syncthreads(); all 256 threads
 // must call. After it returns no thread reads `rows` again.
-template <typename T, int D, int DF, int LDK>
-__device__ __forceinline__ void np_map_rows64(const T* rows, const T* Wh, float* m2part, float* xn2,
+template <typename T, int D, int DF>
+__device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const T* Wh, float* m2part, float* xn2,
                                               f32x4 (&phi)[4][DF / 64]) {
   constexpr int FPW = DF / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   if (tid < 64) {
     float s = 0.f;
     for (int d = 0; d < D; ++d) {
-      const float x = Tr<T>::to_f(rows[tid * LDK + d]);
+      const float x = Tr<T>::to_f(rows[Swz<T, D>::off(row0 + tid, d)]);
       s += x * x;
     }
     xn2[tid] = s;
@@ -120,7 +118,7 @@ __device__ __forceinline__ void np_map_rows64(const T* rows, const T* Wh, float*
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const typename Tr<T>::frag a = Tr<T>::load8(rows + (kb * 16 + r16) * LDK + ks * 32 + grp * 8);
+        const typename Tr<T>::frag a = Swz<T, D>::load8(rows, row0 + kb * 16 + r16, ks * 32 + grp * 8);
         Tr<T>::mma(acc, a, wf[ks]);
       }
 #pragma unroll
