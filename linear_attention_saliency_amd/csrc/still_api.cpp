@@ -33,7 +33,7 @@ int check_cfg(const still_config* c, bool use_seq) {
     const int64_t g = c->n_q_heads / c->n_kv_heads;
     const int64_t nw = g < 4 ? g : 4;
     const int64_t gsplit = (g + nw - 1) / nw;
-    if (n_chunks * c->batch * c->n_kv_heads * gsplit > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
+    if (n_chunks * c->batch * c->n_kv_heads * gsplit * 2 > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
   }
   return STILL_OK;
 }

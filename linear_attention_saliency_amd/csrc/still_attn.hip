@@ -1,9 +1,10 @@
 // Fused softmax + linear attention of the STILL prefill, with the shared normaliser.
 //
-// One workgroup per (chunk c, batch b, KV head h, head split). The workgroup packs up to
-// four query heads of the group (GQA): every staged key/value tile serves all of them.
-// Wave w handles query head (w / WPH) of the split and QW consecutive queries of the
-// chunk (WPH = 64 / QW waves per head).
+// One workgroup per (chunk c, batch b, KV head h, head split, query split). The
+// workgroup packs up to four query heads of the group (GQA): every staged key/value tile
+// serves all of them. Wave w handles query head w of the head split, for the QW
+// consecutive queries of its query split (64 / QW query splits per chunk, so two
+// independent workgroups can share a CU and hide each other's barriers).
 //
 // Key sets for query i = 64c + r ([P1] paragraph before "STILL三大创新", sections
 // "Chunk-Wise并行+延迟选择" and NP-Map; [P2] excerpt):
@@ -41,39 +42,64 @@ template <typename T> __device__ __forceinline__ typename Tr<T>::frag ones_frag(
   return x;
 }
 
-// One 64-key softmax tile for one wave. S^T = K Q^T (K rows from lk), mask (if MASKED),
-// online softmax with a lazily refreshed running max, then O^T += V^T P^T in two 32-key
-// halves (V^T rows from lv). o[D/16][*] is the row-sum block: every entry holds the
-// running denominator of the lane's query.
-// keep(p, qb): whether key p of the tile is in the softmax set of the lane's query in
-// block qb (used when MASKED).
-template <bool MASKED, typename T, int D, int QB, typename Keep>
-__device__ __forceinline__ void sa_tile(const T* lk, const T* lv, const typename Tr<T>::frag (&qf)[QB][D / 32],
-                                        f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB], float c1, Keep keep) {
-  using TT = Tr<T>;
-  using frag = typename TT::frag;
+// Scores of one 64-key tile for one wave: s[kb][qb] = S^T block (keys kb*16.., queries
+// qb*16..) = K Q^T, K rows from the Swz<T, D> tile lk.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void qk_tile(const T* lk, const typename Tr<T>::frag (&qf)[QB][D / 32], f32x4 (&s)[4][QB]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
-  f32x4 s[4][QB];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
+      const typename Tr<T>::frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) TT::mma(s[kb][qb], ka, qf[qb][ks]);
+      for (int qb = 0; qb < QB; ++qb) Tr<T>::mma(s[kb][qb], ka, qf[qb][ks]);
     }
   }
-  if constexpr (MASKED) {
+}
+
+// Per-lane key masks. A lane holds keys p = kb*16 + 4*grp + i (kb, i in 0..3) of a
+// 64-key tile; its "key word" has bit kb*4 + i set for the keys it keeps.
+//
+// Keys p with lo <= p <= hi (any integers; empty if lo > hi).
+__device__ __forceinline__ uint32_t range_word(int lo, int hi) {
+  const int g4 = 4 * ((threadIdx.x & 63) >> 4);
+  uint32_t w = 0;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (!keep(kb * 16 + 4 * grp + i, qb)) s[kb][qb][i] = -kInf;
+  for (int kb = 0; kb < 4; ++kb) {
+    const int base = kb * 16 + g4;  // key of element (kb, i = 0)
+    const int nh = min(max(hi - base + 1, 0), 4);
+    const int nl = min(max(lo - base, 0), 4);
+    w |= (((1u << nh) - 1u) & ~((1u << nl) - 1u)) << (4 * kb);
   }
+  return w;
+}
+// Keys whose bit is set in a 64-bit tile mask (bit p <-> key p).
+__device__ __forceinline__ uint32_t bits_word(uint64_t m) {
+  const uint64_t x = m >> (4 * ((threadIdx.x & 63) >> 4));
+  return static_cast<uint32_t>((x & 0xFull) | ((x >> 12) & 0xF0ull) | ((x >> 24) & 0xF00ull) | ((x >> 36) & 0xF000ull));
+}
+
+// scores of keys not set in the lane's key word (one per query block) -> -inf
+template <int QB>
+__device__ __forceinline__ void mask_tile(f32x4 (&s)[4][QB], const uint32_t (&kw)[QB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!(kw[qb] & (1u << (kb * 4 + i)))) s[kb][qb][i] = -kInf;
+}
+
+// Running-max update for a tile: the max is refreshed only when the tile's max exceeds it
+// by more than 8 (log2 units); the accumulators (row-sum block included) are rescaled
+// then, which is rare after the first tiles.
+template <int D, int QB>
+__device__ __forceinline__ void sm_max(const f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB],
+                                       float c1) {
   bool need_any = false;
   float alpha[QB];
 #pragma unroll
@@ -94,10 +120,22 @@ __device__ __forceinline__ void sa_tile(const T* lk, const T* lv, const typename
 #pragma unroll
       for (int db = 0; db <= D / 16; ++db) o[db][qb] *= alpha[qb];
   }
+}
+
+// P = 2^(s*c1 - m) (bf16 for bf16 inputs), then O^T += V^T P^T in two 32-key halves
+// (V^T rows from the Swz<T, 64> tile lv); the all-ones block accumulates the row sums.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void sm_exp_pv(const f32x4 (&s)[4][QB], const T* lv, f32x4 (&o)[D / 16 + 1][QB],
+                                          const float (&m_run)[QB], float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   float mq[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mq[qb] = m_run[qb] == -kInf ? 0.f : m_run[qb];
-  const frag one = ones_frag<T>();
+  frag one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = TT::from_f(1.0f);
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     frag pf[QB];
@@ -120,17 +158,18 @@ __device__ __forceinline__ void sa_tile(const T* lk, const T* lv, const typename
 template <typename T, int D, int DF, int QW, int NH>
 struct AttnCfg {
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
-  static constexpr int WPH = 64 / QW;          // waves per query head
-  static constexpr int NTHR = 64 * WPH * NH;   // threads per workgroup
+  static constexpr int QSPLIT = 64 / QW;       // workgroups per chunk, one per query slice
+  static constexpr int NTHR = 64 * NH;         // threads per workgroup: one wave per head
   static constexpr int KBUF = 64 * (D > DF ? D : DF);  // elements of one K / phi(K) stage
   static constexpr int VBUF = D * 64;                  // elements of one V^T stage
-  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * static_cast<int>(sizeof(T));
+  static constexpr int NSTAGE = 3;
+  static constexpr int LDS_BYTES = NSTAGE * (KBUF + VBUF) * static_cast<int>(sizeof(T));
 };
 
 template <typename T, int D, int DF, int QW, int NH>
-__global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   using C = AttnCfg<T, D, DF, QW, NH>;
-  constexpr int QB = C::QB, WPH = C::WPH, NTHR = C::NTHR;
+  constexpr int QB = C::QB, NTHR = C::NTHR;
   using SK = Swz<T, D>;    // K tile: 64 keys x D
   using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF; prefix state: D rows x DF
   using SV = Swz<T, 64>;   // V^T tile: D rows x 64 keys
@@ -138,8 +177,8 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   using TT = Tr<T>;
   using frag = typename TT::frag;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-  T* ldsK = reinterpret_cast<T*>(lds_raw);        // 2 stages of KBUF
-  T* ldsV = ldsK + 2 * C::KBUF;                    // 2 stages of VBUF
+  T* ldsK = reinterpret_cast<T*>(lds_raw);        // NSTAGE stages of KBUF
+  T* ldsV = ldsK + C::NSTAGE * C::KBUF;            // NSTAGE stages of VBUF
 
   const Dims& d = a.d;
   const T* q = static_cast<const T*>(a.q);
@@ -150,14 +189,19 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   const T* vT = static_cast<const T*>(a.vT);
   const T* phik = static_cast<const T*>(a.phik);
 
-  const int P = d.B * d.Hkv * a.gsplit;
-  const int c = d.nC - 1 - static_cast<int>(blockIdx.x) / P;  // heaviest chunks first
+  // workgroup order: heaviest chunks first; within a chunk, consecutive workgroups take
+  // consecutive (b, h, head split) so that, with 8 XCDs dispatched round-robin, one
+  // XCD's L2 serves a fixed set of KV heads
+  const int BHG = d.B * d.Hkv * a.gsplit;
+  const int P = BHG * C::QSPLIT;
+  const int c = d.nC - 1 - static_cast<int>(blockIdx.x) / P;
   const int pi = static_cast<int>(blockIdx.x) % P;
-  const int gs = pi % a.gsplit, bh = pi / a.gsplit;
+  const int bhg = pi % BHG, qs = pi / BHG;
+  const int gs = bhg % a.gsplit, bh = bhg / a.gsplit;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const int g = gs * NH + wave / WPH;
-  const int qoff = (wave % WPH) * QW;  // first query of this wave within the chunk
+  const int g = gs * NH + wave;
+  const int qoff = qs * QW;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
   const int hq = h * d.G + (head_ok ? g : d.G - 1);
   const long long T_ = d.T;
@@ -290,18 +334,19 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
           for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
         }
       }
+      // linear keys: chunk c-1: p <= r + 64 - w and unselected; chunk c: p <= r - w
+      const uint32_t selw = cc == c ? 0u : bits_word(selprev);
       frag pf[2][QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int r = qoff + qb * 16 + r16;
+        const uint32_t lw = range_word(0, cc == c ? r - win : r + 64 - win) & ~selw;
         float pv[4][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int p = kb * 16 + 4 * grp + i;
-            const bool la = cc == c ? (p <= r - win) : (p <= r + 64 - win && !((selprev >> p) & 1ull));
-            const float x = la ? ls[kb][qb][i] : 0.f;
+            const float x = (lw & (1u << (kb * 4 + i))) ? ls[kb][qb][i] : 0.f;
             pv[kb][i] = x;
             den[qb] += x;
           }
@@ -334,44 +379,7 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   }
 
   // =============================== phase 2: softmax tiles ==============================
-  // 2a. the window tiles (chunk c causal, chunk c-1 mixed), loaded together, masked
-  if (win >= 1) {
-    const int nct = c >= 1 ? 2 : 1;
-    for (int ct = 0; ct < nct; ++ct) {
-      T* lk = ldsK + ct * C::KBUF;
-      T* lv = ldsV + ct * C::VBUF;
-      const long long tb = ct == 0 ? t0 : t0 - 64;
-      const int nk = ct == 0 ? nvalid : 64;
-      for (int idx = tid; idx < 64 * (D / 8); idx += NTHR) {
-        const int p = idx / (D / 8), c8 = idx % (D / 8);
-        frag x = TT::zero();
-        if (p < nk) x = TT::load8(kk + ((b * T_ + tb + p) * d.Hkv + h) * D + c8 * 8);
-        SK::store8(lk, p, c8 * 8, x);
-      }
-      const T* src = vT + (static_cast<long long>(bh) * d.nC + (ct == 0 ? c : c - 1)) * D * 64;
-      for (int idx = tid; idx < D * 8; idx += NTHR) {
-        const int dd = idx / 8, c8 = idx % 8;
-        SV::store8(lv, dd, c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
-      }
-    }
-    __syncthreads();
-    sa_tile<true, T, D, QB>(ldsK, ldsV, qf, o, m_run, c1, [&](int p, int qb) {
-      const int r = qoff + qb * 16 + r16;
-      return p <= r && p > r - win;
-    });
-    if (c >= 1) {
-      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
-      sa_tile<true, T, D, QB>(ldsK + C::KBUF, ldsV + C::VBUF, qf, o, m_run, c1, [&](int p, int qb) {
-        const int r = qoff + qb * 16 + r16;
-        return (p > r + 64 - win) || ((selprev >> p) & 1ull);
-      });
-    }
-    __syncthreads();
-  }
-
-  // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
-  //     The next tile's loads are in flight while the current tile is computed.
-  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
+  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
   const int nt_comp = (n_comp + 63) / 64;
   constexpr int KLD = D / 8;                        // 8-element pieces per K row
   constexpr int NK16 = 64 * KLD;                    // pieces per K tile
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
   }
   const T* kb_ptr = ksel + static_cast<long long>(bh) * d.nCc * d.topk * D;
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
-  frag pre[NPT];  // the next tile, in flight
+  frag pre[NPT];  // a compact tile in flight (global -> registers -> LDS stage)
   auto issue = [&](int t) {
     const int rows = n_comp - t * 64;
     const T* kt = kb_ptr + static_cast<long long>(t) * 64 * D;
@@ -421,28 +429,89 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
       else SV::store8(ldsV + stage * C::VBUF, prow[i], pcol[i], pre[i]);
     }
   };
-  constexpr bool kPrefetch = NPT <= 4;  // keep the in-flight tile in registers only if it is small
-  if (nt_comp > 0) {
-    issue(0);
-    commit(0);
-    __syncthreads();
+
+  // 2a. the window tiles: chunk c (causal) in stage 1, chunk c-1 (mixed) in stage 2.
+  //     The first compact tile's loads are in flight meanwhile.
+  if (win >= 1) {
+    const int nct = c >= 1 ? 2 : 1;
+    for (int ct = 0; ct < nct; ++ct) {
+      T* lk = ldsK + (1 + ct) * C::KBUF;
+      T* lv = ldsV + (1 + ct) * C::VBUF;
+      const long long tb = ct == 0 ? t0 : t0 - 64;
+      const int nk = ct == 0 ? nvalid : 64;
+      for (int idx = tid; idx < 64 * (D / 8); idx += NTHR) {
+        const int p = idx / (D / 8), c8 = idx % (D / 8);
+        frag x = TT::zero();
+        if (p < nk) x = TT::load8(kk + ((b * T_ + tb + p) * d.Hkv + h) * D + c8 * 8);
+        SK::store8(lk, p, c8 * 8, x);
+      }
+      const T* src = vT + (static_cast<long long>(bh) * d.nC + (ct == 0 ? c : c - 1)) * D * 64;
+      for (int idx = tid; idx < D * 8; idx += NTHR) {
+        const int dd = idx / 8, c8 = idx % 8;
+        SV::store8(lv, dd, c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
+      }
+    }
   }
-  for (int t = 0; t < nt_comp; ++t) {
-    const int stage = t & 1;
-    if (kPrefetch && t + 1 < nt_comp) issue(t + 1);
-    const int nk = n_comp - t * 64;
-    if (nk >= 64) {
-      sa_tile<false, T, D, QB>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, c1,
-                                         [](int, int) { return true; });
-    } else {
-      sa_tile<true, T, D, QB>(ldsK + stage * C::KBUF, ldsV + stage * C::VBUF, qf, o, m_run, c1,
-                                        [nk](int p, int) { return p < nk; });
+  if (nt_comp > 0) issue(0);
+  __syncthreads();
+  if (win >= 1) {
+    f32x4 s[4][QB];
+    uint32_t kw[QB];
+    qk_tile<T, D, QB>(ldsK + C::KBUF, qf, s);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {  // chunk c: r - w < p <= r
+      const int r = qoff + qb * 16 + r16;
+      kw[qb] = range_word(r - win + 1, r);
     }
-    if (t + 1 < nt_comp) {
-      if (!kPrefetch) issue(t + 1);
-      commit(stage ^ 1);
+    mask_tile<QB>(s, kw);
+    sm_max<D, QB>(s, o, m_run, c1);
+    sm_exp_pv<T, D, QB>(s, ldsV + C::VBUF, o, m_run, c1);
+    if (c >= 1) {
+      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
+      const uint32_t selw = bits_word(selprev);
+      qk_tile<T, D, QB>(ldsK + 2 * C::KBUF, qf, s);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {  // chunk c-1: p > r + 64 - w, or selected
+        const int r = qoff + qb * 16 + r16;
+        kw[qb] = range_word(r + 65 - win, 63) | selw;
+      }
+      mask_tile<QB>(s, kw);
+      sm_max<D, QB>(s, o, m_run, c1);
+      sm_exp_pv<T, D, QB>(s, ldsV + 2 * C::VBUF, o, m_run, c1);
     }
+  }
+
+  // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
+  //     Three LDS stages: while tile t's softmax runs, tile t+1 is already in LDS, so its
+  //     K Q^T product (MFMA) is independent of the softmax (VALU) and issues interleaved
+  //     with it; tile t+2 is in flight from global memory. One barrier per tile.
+  if (nt_comp > 0) {
+    commit(0);
+    if (nt_comp > 1) issue(1);
     __syncthreads();
+    f32x4 sa[4][QB], sb[4][QB];
+    qk_tile<T, D, QB>(ldsK, qf, sa);
+    auto step = [&](int t, f32x4 (&s_cur)[4][QB], f32x4 (&s_next)[4][QB]) {
+      const int st = t % 3, stn = (t + 1) % 3;
+      if (t + 1 < nt_comp) commit(stn);
+      __syncthreads();
+      if (t + 2 < nt_comp) issue(t + 2);
+      const int nk = n_comp - t * 64;
+      if (nk < 64) {
+        uint32_t kw[QB];
+        const uint32_t rw = range_word(0, nk - 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
+        mask_tile<QB>(s_cur, kw);
+      }
+      sm_max<D, QB>(s_cur, o, m_run, c1);
+      qk_tile<T, D, QB>(ldsK + stn * C::KBUF, qf, s_next);  // the last tile reads a stale stage: unused
+      sm_exp_pv<T, D, QB>(s_cur, ldsV + st * C::VBUF, o, m_run, c1);
+    };
+    for (int t = 0; t < nt_comp; t += 2) {
+      step(t, sa, sb);
+      if (t + 1 < nt_comp) step(t + 1, sb, sa);
+    }
   }
 
   // ---- epilogue: divide by the shared normaliser, write [B,T,Hq,D] ------------------
@@ -468,7 +537,7 @@ __global__ __launch_bounds__(64 * (64 / QW) * NH, 2) void attn_kernel(AttnArgs a
 template <typename T, int D, int DF, int QW, int NH>
 static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
   using C = AttnCfg<T, D, DF, QW, NH>;
-  const int P = a.d.B * a.d.Hkv * a.gsplit;
+  const int P = a.d.B * a.d.Hkv * a.gsplit * C::QSPLIT;
   dim3 grid(a.d.nC * P);
   if (C::LDS_BYTES > 65536)  // opt in to more than 64 KiB of LDS (gfx950 has 160 KiB per CU)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, QW, NH>),

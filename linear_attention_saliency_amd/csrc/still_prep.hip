@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const long long t0 = static_cast<long long>(c) * kChunk;
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
   const bool complete = nvalid == kChunk;
-  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float scale = kLog2e / sqrtf(static_cast<float>(D));  // saliency logits in log2 units
 
   // 1. key band: row t <-> position t0 - 63 + t (row 127 is never in a window)
   for (int idx = tid; idx < 128 * V8; idx += 256) {

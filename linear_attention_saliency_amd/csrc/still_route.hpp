@@ -20,7 +20,8 @@ constexpr int kChunk = 64;
 // window is band rows [r + 64 - w, r + 63]. qf holds the B-operand (SK) fragments of the
 // queries qb*16 .. qb*16+15 (lane r16 <-> query qb*16 + r16).
 //
-// For query i: M' = max over the window without i, Z' = sum over the window without i of
+// For query i (logits in log2 units, scale = log2(e)/sqrt(D)): M' = max over the window
+// without i, Z' = sum over the window without i of
 // e^{a - M'}, and s_i = LSE(W_i) - LSE(W_i \ i) = softplus(a_ii - M' - log Z'), which is
 // +inf when i is alone in its window. Returned in every lane of the query's column.
 template <typename T, int D>
@@ -37,18 +38,19 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
       Tr<T>::mma(acc[j], a, qf[ks]);
     }
   }
+  // logits in log2 units: scale = log2(e) / sqrt(D)
   const int r = qb * 16 + r16;
-  const int diag = r + 63, lo = r + 64 - window;
+  const int diag = r + 63;
+  const int lo = max(r + 64 - window, static_cast<int>(-band_pos0));  // first window row inside the sequence
   float mx = -kInf, dg = -kInf;
 #pragma unroll
   for (int j = 0; j < 5; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (qb + j) * 16 + 4 * grp + i;
-      const bool in = row >= lo && row <= diag && band_pos0 + row >= 0;
       const float a = acc[j][i] * scale;
-      if (in && row == diag) dg = a;
-      if (in && row != diag) mx = fmaxf(mx, a);
+      if (row == diag) dg = a;
+      if (row >= lo && row < diag) mx = fmaxf(mx, a);
     }
   mx = xor_max_groups(mx);
   dg = xor_max_groups(dg);
@@ -58,11 +60,14 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (qb + j) * 16 + 4 * grp + i;
-      const bool in = row >= lo && row < diag && band_pos0 + row >= 0;
-      if (in) z += expf(acc[j][i] * scale - mx);
+      if (row >= lo && row < diag) z += __builtin_amdgcn_exp2f(acc[j][i] * scale - mx);
     }
   z = xor_sum_groups(z);
-  return z > 0.f ? softplus_f(dg - mx - logf(z)) : kInf;
+  // s = ln(1 + 2^x), x = dg - mx - log2 z (log2 units): softplus via exp2 / log2
+  if (!(z > 0.f)) return kInf;
+  const float x = dg - mx - __builtin_amdgcn_logf(z);
+  const float sp = fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x)));
+  return sp * 0.69314718055994531f;
 }
 
 // Top-k of one chunk ([P1] section "Chunk-Wise并行+延迟选择"): lane p holds the
@@ -124,7 +129,7 @@ __device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const T* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float zv = acc[i];
-        acc[i] = zv > 0.f ? zv + 1.f : expf(zv);  // elu(z) + 1
+        acc[i] = zv > 0.f ? zv + 1.f : __builtin_amdgcn_exp2f(zv * kLog2e);  // elu(z) + 1
       }
       phi[kb][fi] = acc;
     }
