@@ -7,7 +7,13 @@ seeded synthetic inputs that are resident in HBM before timing starts.
 A step is one still_prefill call: saliency, per-chunk top-k, gather, NP-Map, chunk
 states, prefix scan and the fused softmax + linear attention. Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--calibrate-copy]
+
+--calibrate-copy runs one device-to-device copy of COPY_BYTES before the steps, so that
+a rocprofv3 --pmc run of this script also records what FETCH_SIZE / WRITE_SIZE read for a
+transfer of known size (the scale applied to the attention kernel's counters).
+The roofline "traffic" field is read from profiles/attn_kernel_traffic.txt when that
+file was measured on the current attention-kernel source (matching SHA-1), else null.
 """
 
 from __future__ import annotations
@@ -26,6 +32,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/s per layer at 16K (bf16); % of HBM/MFMA roofline"
+COPY_BYTES = 256 << 20
+_CSRC = os.path.join(ROOT, "linear_attention_saliency_amd", "csrc")
+# the attention kernel's source and every header it includes
+ATTN_SRCS = [os.path.join(_CSRC, f) for f in ("still_attn.hip", "still_common.hpp", "still_layout.hpp",
+                                              "still_launch.hpp", "still_route.hpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
+
+
+def source_sha1(paths) -> str:
+    import hashlib
+
+    h = hashlib.sha1()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention-kernel launch from the committed counter summary, if it
+    was taken on the current kernel source; None otherwise."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+    except OSError:
+        return None
+    if kv.get("attn_source_sha1", "").strip() != source_sha1(ATTN_SRCS):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
 PEAK_BF16_MFMA = 2.5e15   # dense, FLOP/s
 PEAK_HBM = 8.0e12         # bytes/s
 
@@ -65,23 +99,19 @@ def algorithmic_work(wl, sel_idx: np.ndarray) -> dict:
 
 
 def cpu_baseline(wl, q, k, v, w, sel_idx) -> dict:
-    """The fp64 oracle on KV head 0 (its G query heads) over all tokens, scaled to the layer."""
+    """The fp64 oracle on the whole layer (all KV heads, all tokens), timed on the host."""
     import threadpoolctl
     from oracle import still_oracle as O
 
-    G = wl.n_q_heads // wl.n_kv_heads
-    qs, ks, vs, ws = q[:, :, :G], k[:, :, :1], v[:, :, :1], w[:1]
     t0 = time.perf_counter()
-    s_kv, _ = O.saliency(qs, ks, wl.window)
+    s_kv, _ = O.saliency(q, k, wl.window)
     _, sel = O.route(s_kv, wl.chunk, wl.top_k)
-    O.attend(qs, ks, vs, ws, wl.window, wl.chunk, wl.top_k, sel=sel)
+    O.attend(q, k, v, w, wl.window, wl.chunk, wl.top_k, sel=sel)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    layer_s = dt * wl.n_kv_heads
-    return {"value": wl.batch * wl.seq_len / layer_s, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"KV head 0 of {wl.n_kv_heads} ({G} query heads), all {wl.seq_len} tokens, "
-                      f"{dt:.1f} s, scaled x{wl.n_kv_heads} to the layer; host {os.cpu_count()} CPUs"}
+    return {"value": wl.batch * wl.seq_len / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole layer ({wl.n_kv_heads} KV heads, {wl.n_q_heads} query heads, {wl.seq_len} "
+                      f"tokens) in {dt:.1f} s on a host with {os.cpu_count()} CPUs"}
 
 
 def main() -> int:
@@ -90,6 +120,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (every step is "
@@ -113,6 +144,12 @@ def main() -> int:
     sel_idx = sel.cpu().numpy()
     work = algorithmic_work(wl, sel_idx)
 
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out)
     stream = torch.cuda.current_stream()
@@ -160,7 +197,7 @@ def main() -> int:
                    "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "layer_roofline": {"flops": work["flops"], "bytes": work["bytes"],
                            "mfma_frac": layer_tflops / PEAK_BF16_MFMA, "hbm_frac": layer_gbs / PEAK_HBM,
                            "frac": max(layer_tflops / PEAK_BF16_MFMA, layer_gbs / PEAK_HBM)},

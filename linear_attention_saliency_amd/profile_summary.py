@@ -1,0 +1,63 @@
+"""Summaries of rocprofv3 CSV output for the kernels of this library.
+
+  python -m linear_attention_saliency_amd.profile_summary stats <run_kernel_stats.csv>
+  python -m linear_attention_saliency_amd.profile_summary traffic <fetch_dir> <write_dir> <copy_bytes>
+
+`traffic` reads the counter_collection CSVs of a FETCH_SIZE pass and a WRITE_SIZE pass
+(rocprofv3 --pmc ... -- python3 bench.py --calibrate-copy ...): the copy kernel of known
+size (the launch whose counters are largest among the non-library kernels) gives the
+scale from counter KiB to bytes, which is applied to the attention kernel's mean per
+launch.
+"""
+
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import os
+import sys
+
+
+def stats(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0]
+        lines.append(f"| {short[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    return "\n".join(lines)
+
+
+def _per_kernel(dirpath: str, counter: str):
+    out = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int) -> str:
+    lines = []
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _per_kernel(d, counter)
+        copies = {k: v for k, v in per.items() if "still" not in k}
+        ck = max(copies, key=lambda k: max(copies[k]))
+        scale = copy_bytes / max(copies[ck])  # bytes per counter unit
+        attn = [k for k in per if "attn_kernel" in k]
+        val = sum(per[attn[0]]) / len(per[attn[0]]) * scale
+        total += val
+        lines.append(f"{counter}: copy kernel {ck[:60]} read {max(copies[ck]):.0f} for {copy_bytes} bytes "
+                     f"(scale {scale:.2f} B/unit); attention kernel mean {val / 1e6:.2f} MB per launch")
+    lines.append(f"hbm_bytes_per_launch: {total:.0f}")
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        print(stats(sys.argv[2]))
+    elif sys.argv[1] == "traffic":
+        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4])))
