@@ -86,16 +86,21 @@ typedef struct still_config {
  * ([P1] section "Chunk-Wise并行+延迟选择"). A host-side record of device sub-buffers
  * carved from one caller buffer by still_cache_init. Fields are read-only for callers.
  * With c the chunk of the next token: sel_k/sel_v hold the selected rows of chunks
- * <= c-2 in (chunk, position) order; ring_k/ring_v hold the raw rows of chunks c-1 and
- * c (chunk j in slot j % 2); state_s/state_z hold the linear-attention state
- * sum phi(k) v^T and sum phi(k) over the unselected tokens of chunks <= c-2. */
+ * <= c-2 in (chunk, position) order (compact row n = chunk * top_k + rank; rows of later
+ * chunks may already be present and are not read); ring_k/ring_v hold the raw rows of
+ * chunks c-1 and c (chunk j in slot j % 2); state_s/state_z hold the linear-attention
+ * state sum phi(k) v^T and sum phi(k) over the unselected tokens of chunks <= c-2.
+ * sel_v is stored transposed in tiles of 64 compact rows: element (row n, dim d) is at
+ * [((n / 64) * head_dim + d) * 64 + p(n % 64)], where p(j) = (j & ~31) + 8*((j & 15) >> 2)
+ * + 4*((j >> 4) & 1) + (j & 3) orders each 32-row slice as the MFMA accumulator holds it.
+ * Supported for n_q_heads / n_kv_heads <= 16. */
 typedef struct still_cache {
   still_config cfg;     /* configuration the cache was built for (seq_len ignored) */
   int64_t max_tokens;   /* capacity per sequence */
   int64_t n_tokens;     /* tokens held per sequence = position of the next token */
-  int64_t sel_capacity; /* rows per (batch, KV head) in sel_k / sel_v */
+  int64_t sel_capacity; /* compact rows per (batch, KV head), a multiple of 64 */
   void* sel_k;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype */
-  void* sel_v;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype */
+  void* sel_v;          /* [batch, n_kv_heads, sel_capacity / 64, head_dim, 64] dtype */
   void* ring_k;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
   void* ring_v;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
   float* state_s;       /* [batch, n_kv_heads, feat_dim, head_dim] fp32 */
@@ -123,8 +128,10 @@ size_t still_prefill_workspace_bytes(const still_config* cfg);
  *                 (requires window >= 1).
  *   sel_idx_out   optional [batch, n_kv_heads, seq_len/chunk, top_k] int32: the selected
  *                 positions of every complete chunk, ascending.
- *   cache         optional: if non-null, a cache from still_cache_init for this config
- *                 with n_tokens == 0; it is left holding the state after seq_len tokens.
+ *   cache         optional: if non-null, a cache from still_cache_init for this layer
+ *                 (CACHE_MISMATCH otherwise) with n_tokens == 0 (INVALID_ARG otherwise) and
+ *                 max_tokens >= seq_len (CACHE_FULL otherwise); it is left holding the state
+ *                 after seq_len tokens, ready for still_decode_step.
  *   workspace     device scratch of at least still_prefill_workspace_bytes(cfg) bytes.
  * Returns STILL_OK or a negative status. */
 int still_prefill(const still_config* cfg, const void* q, const void* k, const void* v,
@@ -154,11 +161,13 @@ int still_select_topk(const still_config* cfg, const float* saliency, int32_t* s
 int still_feature_map(const still_config* cfg, const void* x, const void* w_phi,
                       float* phi_out, hipStream_t stream);
 
-/* Bytes of device memory a decode cache of `max_tokens` tokens per sequence needs. */
+/* Bytes of device memory a decode cache of `max_tokens` tokens per sequence needs
+ * (0 if the configuration is invalid or unsupported; cfg->seq_len is ignored). */
 size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens);
 
-/* Carve a cache from `dev_buf` (>= still_cache_bytes bytes) and clear it on `stream`.
- * Fills *out; n_tokens starts at 0. */
+/* Carve a cache from `dev_buf` (256-byte aligned, >= still_cache_bytes bytes, owned by the
+ * caller for the cache's lifetime) and clear it on `stream`. Fills *out; n_tokens starts
+ * at 0. A cache is filled either by still_prefill (cache argument) or token by token. */
 int still_cache_init(const still_config* cfg, int64_t max_tokens, void* dev_buf,
                      size_t bytes, still_cache* out, hipStream_t stream);
 
@@ -175,6 +184,14 @@ size_t still_decode_workspace_bytes(const still_config* cfg, int64_t max_tokens)
 int still_decode_step(const still_config* cfg, still_cache* cache, const void* q,
                       const void* k, const void* v, const void* w_phi, void* out,
                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* still_decode_step with timing events: if `events` is non-null it must hold 3 events
+ * created by the caller, recorded before the compact-cache kernel, before the per-token
+ * kernel and after it. */
+int still_decode_step_timed(const still_config* cfg, still_cache* cache, const void* q,
+                            const void* k, const void* v, const void* w_phi, void* out,
+                            void* workspace, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t* events);
 
 #ifdef __cplusplus
 }

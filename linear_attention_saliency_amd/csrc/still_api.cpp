@@ -77,13 +77,79 @@ WsLayout ws_layout(const still_config* c) {
   L.sal = take(bh * d.T * sizeof(float));
   L.selmask = take(bh * d.nC * sizeof(uint64_t));
   L.ntiles_sel = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
-  L.ksel = take(bh * d.nCc * d.topk * d.D * es);
+  L.ksel = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vselT = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vT = take(bh * d.nC * 64 * d.D * es);
   L.phik = take(bh * d.T * d.DF * es);
   L.states = take(bh * d.nC * d.R * sizeof(float));
   L.total = off;
   return L;
+}
+
+constexpr int kMaxDecodeGroup = 16;  // query heads per KV head the decode kernels handle
+constexpr int kMaxSplit = 64;        // workgroups per (b, KV head) over the compact cache
+constexpr int kSplitTarget = 2048;   // aim for this many split workgroups per decode step
+
+struct CacheLayout {
+  size_t sel_k, sel_v, ring_k, ring_v, state_s, state_z, sel_mask, cur_sal, total;
+  int64_t sel_capacity;  // compact rows per (b, KV head), a multiple of 64
+};
+
+CacheLayout cache_layout(const still_config* c, int64_t max_tokens) {
+  const size_t bh = static_cast<size_t>(c->batch) * c->n_kv_heads;
+  const size_t es = elem_bytes(c);
+  const size_t D = c->head_dim, F = c->feat_dim;
+  CacheLayout L;
+  L.sel_capacity = ((max_tokens / 64) * c->top_k + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.sel_k = take(bh * L.sel_capacity * D * es);
+  L.sel_v = take(bh * L.sel_capacity * D * es);
+  L.ring_k = take(bh * 2 * 64 * D * es);
+  L.ring_v = take(bh * 2 * 64 * D * es);
+  L.state_s = take(bh * F * D * sizeof(float));
+  L.state_z = take(bh * F * sizeof(float));
+  L.sel_mask = take(bh * 2 * sizeof(uint64_t));
+  L.cur_sal = take(bh * 64 * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+int check_cache_cfg(const still_config* c, int64_t max_tokens) {
+  const int st = check_cfg(c, false);
+  if (st != STILL_OK) return st;
+  if (max_tokens < 1 || max_tokens > 0x7fffffffLL) return STILL_ERR_INVALID_ARG;
+  if (c->n_q_heads / c->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
+  return STILL_OK;
+}
+
+bool same_layer(const still_config* a, const still_config* b) {
+  return a->batch == b->batch && a->n_q_heads == b->n_q_heads && a->n_kv_heads == b->n_kv_heads &&
+         a->head_dim == b->head_dim && a->feat_dim == b->feat_dim && a->window == b->window &&
+         a->chunk == b->chunk && a->top_k == b->top_k && a->dtype == b->dtype;
+}
+
+still::CacheView view_of(const still_cache* c) {
+  still::CacheView v;
+  v.sel_k = c->sel_k;
+  v.sel_v = c->sel_v;
+  v.ring_k = c->ring_k;
+  v.ring_v = c->ring_v;
+  v.state_s = c->state_s;
+  v.state_z = c->state_z;
+  v.sel_mask = c->sel_mask;
+  v.cur_sal = c->cur_saliency;
+  v.sel_tiles = static_cast<int>(c->sel_capacity / 64);
+  return v;
+}
+
+size_t decode_ws_bytes(const still_config* c) {
+  const size_t recs = static_cast<size_t>(c->batch) * c->n_kv_heads * kMaxSplit * (c->n_q_heads / c->n_kv_heads);
+  return align_up(recs * 2 * sizeof(float)) + align_up(recs * c->head_dim * sizeof(float));
 }
 
 }  // namespace
@@ -122,7 +188,11 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
                         static_cast<const void*>(sel_idx_out)})
     if (p && !aligned(p, 4)) return STILL_ERR_INVALID_ARG;
   if (saliency_out && cfg->window < 1) return STILL_ERR_INVALID_ARG;
-  if (cache) return STILL_ERR_UNSUPPORTED;
+  if (cache) {
+    if (!same_layer(&cache->cfg, cfg)) return STILL_ERR_CACHE_MISMATCH;
+    if (cache->n_tokens != 0) return STILL_ERR_INVALID_ARG;
+    if (cfg->seq_len > cache->max_tokens) return STILL_ERR_CACHE_FULL;
+  }
   const WsLayout L = ws_layout(cfg);
   if (ws_bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
 
@@ -144,6 +214,11 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.vT = ws + L.vT;
   pa.vselT = ws + L.vselT;
   pa.ntiles_sel = L.ntiles_sel;
+  if (cache && cfg->top_k > 0) {  // the compact rows go straight into the cache
+    pa.ksel = cache->sel_k;
+    pa.vselT = cache->sel_v;
+    pa.ntiles_sel = static_cast<int>(cache->sel_capacity / 64);
+  }
   if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
   if (still::launch_prep(pa, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[1], stream) != hipSuccess) return STILL_ERR_HIP;
@@ -162,11 +237,23 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.phik = pa.phik;
   aa.states = pa.states;
   aa.out = out;
-  aa.ntiles_sel = L.ntiles_sel;
+  aa.ntiles_sel = pa.ntiles_sel;
   aa.nw = d.G >= 4 ? 4 : (d.G == 3 ? 4 : d.G);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
   if (still::launch_attn(aa, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[3], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (cache) {
+    still::ExportArgs ea;
+    ea.d = d;
+    ea.k = k;
+    ea.v = v;
+    ea.sal = pa.sal;
+    ea.selmask = pa.selmask;
+    ea.states = pa.states;
+    ea.c = view_of(cache);
+    if (still::launch_cache_export(ea, stream) != hipSuccess) return STILL_ERR_HIP;
+    cache->n_tokens = cfg->seq_len;
+  }
   return STILL_OK;
 }
 
@@ -198,42 +285,93 @@ int still_feature_map(const still_config* cfg, const void* x, const void* w_phi,
 }
 
 size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens) {
-  (void)cfg;
-  (void)max_tokens;
-  return 0;
+  if (check_cache_cfg(cfg, max_tokens) != STILL_OK) return 0;
+  return cache_layout(cfg, max_tokens).total;
 }
 
 int still_cache_init(const still_config* cfg, int64_t max_tokens, void* dev_buf, size_t bytes,
                      still_cache* out, hipStream_t stream) {
-  (void)cfg;
-  (void)max_tokens;
-  (void)dev_buf;
-  (void)bytes;
-  (void)out;
-  (void)stream;
-  return STILL_ERR_UNSUPPORTED;
+  const int st = check_cache_cfg(cfg, max_tokens);
+  if (st != STILL_OK) return st;
+  if (!dev_buf || !out || !aligned(dev_buf, 256)) return STILL_ERR_INVALID_ARG;
+  const CacheLayout L = cache_layout(cfg, max_tokens);
+  if (bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+  char* base = static_cast<char*>(dev_buf);
+  still_cache c;
+  memset(&c, 0, sizeof(c));
+  c.cfg = *cfg;
+  c.cfg.seq_len = 0;
+  c.max_tokens = max_tokens;
+  c.n_tokens = 0;
+  c.sel_capacity = L.sel_capacity;
+  c.sel_k = base + L.sel_k;
+  c.sel_v = base + L.sel_v;
+  c.ring_k = base + L.ring_k;
+  c.ring_v = base + L.ring_v;
+  c.state_s = reinterpret_cast<float*>(base + L.state_s);
+  c.state_z = reinterpret_cast<float*>(base + L.state_z);
+  c.sel_mask = reinterpret_cast<uint64_t*>(base + L.sel_mask);
+  c.cur_saliency = reinterpret_cast<float*>(base + L.cur_sal);
+  if (still::launch_fill_zero(dev_buf, L.total, stream) != hipSuccess) return STILL_ERR_HIP;
+  *out = c;
+  return STILL_OK;
 }
 
 size_t still_decode_workspace_bytes(const still_config* cfg, int64_t max_tokens) {
-  (void)cfg;
-  (void)max_tokens;
-  return 0;
+  if (check_cache_cfg(cfg, max_tokens) != STILL_OK) return 0;
+  return decode_ws_bytes(cfg);
+}
+
+int still_decode_step_timed(const still_config* cfg, still_cache* cache, const void* q, const void* k,
+                            const void* v, const void* w_phi, void* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  const int st = check_cfg(cfg, false);
+  if (st != STILL_OK) return st;
+  if (!cache || !q || !k || !v || !w_phi || !out || !workspace) return STILL_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, w_phi, static_cast<const void*>(out), static_cast<const void*>(workspace)})
+    if (!aligned(p, 16)) return STILL_ERR_INVALID_ARG;
+  if (!same_layer(&cache->cfg, cfg)) return STILL_ERR_CACHE_MISMATCH;
+  if (cfg->n_q_heads / cfg->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
+  if (cache->n_tokens < 0 || cache->n_tokens >= cache->max_tokens) return STILL_ERR_CACHE_FULL;
+  if (ws_bytes < decode_ws_bytes(cfg)) return STILL_ERR_WORKSPACE_TOO_SMALL;
+
+  still_config c1 = *cfg;
+  c1.seq_len = 1;
+  still::DecodeArgs a;
+  a.d = dims_of(&c1);
+  a.pos = cache->n_tokens;
+  const int64_t chunk = cache->n_tokens / 64;
+  a.nsel = static_cast<int>((chunk >= 1 ? chunk - 1 : 0) * cfg->top_k);
+  const int ntiles = (a.nsel + 63) / 64;
+  const int bhn = cfg->batch * cfg->n_kv_heads;
+  int nsplit = (kSplitTarget + bhn - 1) / bhn;
+  if (nsplit > kMaxSplit) nsplit = kMaxSplit;
+  if (nsplit > ntiles) nsplit = ntiles;
+  if (nsplit < 1) nsplit = 1;
+  a.tiles_per_split = (ntiles + nsplit - 1) / nsplit;
+  if (a.tiles_per_split < 1) a.tiles_per_split = 1;
+  a.nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (a.nsplit < 1) a.nsplit = 1;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.w = w_phi;
+  a.out = out;
+  const size_t recs = static_cast<size_t>(bhn) * kMaxSplit * a.d.G;
+  a.part_ml = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(recs * 2 * sizeof(float)));
+  a.c = view_of(cache);
+  if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (still::launch_decode(a, stream, events ? events[1] : nullptr) != hipSuccess) return STILL_ERR_HIP;
+  if (events && hipEventRecord(events[2], stream) != hipSuccess) return STILL_ERR_HIP;
+  cache->n_tokens += 1;
+  return STILL_OK;
 }
 
 int still_decode_step(const still_config* cfg, still_cache* cache, const void* q, const void* k,
                       const void* v, const void* w_phi, void* out, void* workspace,
                       size_t ws_bytes, hipStream_t stream) {
-  (void)cfg;
-  (void)cache;
-  (void)q;
-  (void)k;
-  (void)v;
-  (void)w_phi;
-  (void)out;
-  (void)workspace;
-  (void)ws_bytes;
-  (void)stream;
-  return STILL_ERR_UNSUPPORTED;
+  return still_decode_step_timed(cfg, cache, q, k, v, w_phi, out, workspace, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

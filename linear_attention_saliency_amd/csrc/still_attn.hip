@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
       pcol[i] = c8 * 8;
     }
   }
-  const T* kb_ptr = ksel + static_cast<long long>(bh) * d.nCc * d.topk * D;
+  const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
   frag pre[NPT];  // a compact tile in flight (global -> registers -> LDS stage)
   auto issue = [&](int t) {

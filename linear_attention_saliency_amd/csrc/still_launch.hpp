@@ -24,12 +24,12 @@ struct PrepArgs {
   float* sal;                 // [B,Hkv,T]
   uint64_t* selmask;          // [B,Hkv,nC]
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
-  void* ksel;                 // [B,Hkv,nCc*topk,D]: compact K rows
+  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
   float* states;              // [B,Hkv,nC,R]
   void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos
   void* vselT;                // [B,Hkv,ntiles_sel,D,64]: compact V rows, same tile layout
-  int ntiles_sel;             // ceil(nCc*topk / 64)
+  int ntiles_sel;             // compact tiles per (b, KV head): >= ceil(nCc*topk / 64)
 };
 
 struct AttnArgs {
@@ -49,11 +49,57 @@ struct AttnArgs {
   int gsplit;           // workgroups per (b, kv head, chunk)
 };
 
+// Device view of a decode cache (layouts as in still_cache; the compact rows use the
+// prefill's tile layout: K rows [B,Hkv,sel_tiles*64,D], V in [B,Hkv,sel_tiles,D,64]).
+struct CacheView {
+  void* sel_k;
+  void* sel_v;
+  void* ring_k;    // [B,Hkv,2,64,D], chunk j in slot j % 2
+  void* ring_v;
+  float* state_s;  // [B,Hkv,DF,D]
+  float* state_z;  // [B,Hkv,DF]
+  uint64_t* sel_mask;  // [B,Hkv,2]
+  float* cur_sal;      // [B,Hkv,64]
+  int sel_tiles;       // compact tiles per (b, KV head)
+};
+
+// Leaves the cache as decode expects it after a prefill of d.T tokens.
+struct ExportArgs {
+  Dims d;
+  const void* k;
+  const void* v;
+  const float* sal;        // [B,Hkv,T] group-summed saliency (unused if window = 0)
+  const uint64_t* selmask; // [B,Hkv,nC]
+  const float* states;     // [B,Hkv,nC,R] inclusive prefix over complete chunks
+  CacheView c;
+};
+
+struct DecodeArgs {
+  Dims d;               // T unused
+  long long pos;        // position of the new token
+  int nsel;             // compact rows visible to this token: max(0, chunk - 1) * topk
+  int nsplit;           // workgroups per (b, KV head) over the compact rows
+  int tiles_per_split;
+  const void* q;        // [B,Hq,D]
+  const void* k;        // [B,Hkv,D]
+  const void* v;
+  const void* w;
+  void* out;            // [B,Hq,D]
+  float* part_ml;       // [B,Hkv,nsplit,G,2]: (max, sum) of each split, log2 units
+  float* part_o;        // [B,Hkv,nsplit,G,D]
+  CacheView c;
+};
+
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_scan(const Dims& d, float* states, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* sal, int32_t* sel_idx, hipStream_t s);
 hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float* phi, hipStream_t s);
+
+hipError_t launch_cache_export(const ExportArgs& a, hipStream_t s);
+// mid: optional event recorded between the compact-cache kernel and the token kernel
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t mid);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // true if the (dtype, D, DF) triple has kernel instantiations
 bool shape_supported(int bf16, int D, int DF);

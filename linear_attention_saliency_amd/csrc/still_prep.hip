@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     T* ks_ = static_cast<T*>(a.ksel);
     for (int idx = tid; idx < d.topk * V8; idx += 256) {
       const int slot = idx / V8, c8 = idx % V8;
-      const long long dst = (static_cast<long long>(bh) * nsel_rows + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
+      const long long dst =
+          (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
       if (slot < nsel) kx = TT::load8(k + ((b * T_ + t0 + selpos[slot]) * d.Hkv + h) * D + c8 * 8);
       TT::store8(ks_ + dst, kx);

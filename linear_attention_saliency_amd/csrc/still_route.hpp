@@ -14,8 +14,10 @@ constexpr int kChunk = 64;
 // Self-Saliency Score of 16 queries of one query head
 // ([P1] section "Self-Saliency Score"; [P4] section Approach).
 //
-// `band` holds 128 key rows (a Swz<T, D> tile): row t is the key at position band_pos0 + t, with
-// band_pos0 = chunk_start - 63 (rows outside the sequence are zero and masked here).
+// `band` holds 128 key rows (a Swz<T, D> tile): band row t is the key at position band_pos0 + t,
+// with band_pos0 = chunk_start - 63 (rows outside the sequence are zero and masked here); it is
+// stored at LDS tile row t + row_base (row_base 0 or 1, so a tile that starts one position
+// earlier can be used as is).
 // Query r of the chunk (its position is chunk_start + r) sits at band row r + 63, so its
 // window is band rows [r + 64 - w, r + 63]. qf holds the B-operand (SK) fragments of the
 // queries qb*16 .. qb*16+15 (lane r16 <-> query qb*16 + r16).
@@ -26,7 +28,8 @@ constexpr int kChunk = 64;
 // +inf when i is alone in its window. Returned in every lane of the query's column.
 template <typename T, int D>
 __device__ __forceinline__ float saliency_qblock(const T* band, const typename Tr<T>::frag (&qf)[D / 32],
-                                                 int qb, int window, long long band_pos0, float scale) {
+                                                 int qb, int window, long long band_pos0, float scale,
+                                                 int row_base = 0) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   f32x4 acc[5];
 #pragma unroll
@@ -34,7 +37,7 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const typename Tr<T>::frag a = Swz<T, D>::load8(band, (qb + j) * 16 + r16, ks * 32 + grp * 8);
+      const typename Tr<T>::frag a = Swz<T, D>::load8(band, (qb + j) * 16 + r16 + row_base, ks * 32 + grp * 8);
       Tr<T>::mma(acc[j], a, qf[ks]);
     }
   }

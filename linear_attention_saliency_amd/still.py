@@ -23,7 +23,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: 
 EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefill", "still_prefill_timed",
            "still_select_topk",
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
-           "still_decode_step")
+           "still_decode_step", "still_decode_step_timed")
 
 
 class StillError(RuntimeError):
@@ -79,6 +79,8 @@ def load():
     lib.still_decode_workspace_bytes.restype = S
     lib.still_decode_step.argtypes = [CP, KP, P, P, P, P, P, P, S, V]
     lib.still_decode_step.restype = I
+    lib.still_decode_step_timed.argtypes = [CP, KP, P, P, P, P, P, P, S, V, P]
+    lib.still_decode_step_timed.restype = I
     _lib = lib
     return lib
 
@@ -127,14 +129,16 @@ class Prefill:
             _check(rc, "still_prefill config")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
-    def __call__(self, q, k, v, w_phi, out, *, routing=None, saliency=None, sel_idx=None, stream=None,
-                 events=None):
-        """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4)."""
+    def __call__(self, q, k, v, w_phi, out, *, routing=None, saliency=None, sel_idx=None, cache=None,
+                 stream=None, events=None):
+        """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4).
+        cache: optional DecodeCache with no tokens; it is left holding the sequence."""
         for t in (q, k, v, w_phi, out):
             if not (t.is_cuda and t.is_contiguous()):
                 raise ValueError("tensors must be contiguous device tensors")
         rc = load().still_prefill_timed(ctypes.byref(self.cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w_phi),
-                                        _ptr(out), _ptr(routing), _ptr(saliency), _ptr(sel_idx), None,
+                                        _ptr(out), _ptr(routing), _ptr(saliency), _ptr(sel_idx),
+                                        None if cache is None else ctypes.byref(cache.c),
                                         _ptr(self.workspace), self.workspace.numel(), _stream(stream),
                                         events)
         _check(rc, "still_prefill")
@@ -142,11 +146,12 @@ class Prefill:
 
 
 def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing=None,
-            return_saliency: bool = False, return_routing: bool = False):
+            return_saliency: bool = False, return_routing: bool = False, cache=None):
     """One STILL layer over whole sequences.
 
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
     GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection.
+    cache: optional empty DecodeCache, left ready to decode token T.
     Returns out (and saliency [B,Hkv,T] fp32, sel_idx [B,Hkv,T//chunk,top_k] int32 on
     request).
     """
@@ -158,7 +163,7 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
     sel = torch.empty((B, Hkv, T // chunk, top_k), dtype=torch.int32, device=q.device) if return_routing else None
     if routing is not None:
         routing = routing.to(device=q.device, dtype=torch.int32).contiguous()
-    call(q, k, v, w_phi, out, routing=routing, saliency=sal, sel_idx=sel)
+    call(q, k, v, w_phi, out, routing=routing, saliency=sal, sel_idx=sel, cache=cache)
     res = [out]
     if return_saliency:
         res.append(sal)
@@ -187,3 +192,70 @@ def feature_map(x, w_phi):
     rc = load().still_feature_map(ctypes.byref(cfg), _ptr(x), _ptr(w_phi), _ptr(phi), _stream())
     _check(rc, "still_feature_map")
     return phi
+
+
+class DecodeCache:
+    """Device decode state of one layer for `batch` sequences of up to `max_tokens` tokens.
+
+    Owns one device buffer (allocated by torch) carved by still_cache_init, plus the
+    decode workspace. `c` is the C record (n_tokens advances with every step).
+    """
+
+    def __init__(self, *, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, feat_dim: int,
+                 window: int, top_k: int, max_tokens: int, dtype=torch.bfloat16, chunk: int = 64,
+                 device="cuda"):
+        lib = load()
+        self.cfg = make_config(batch, 0, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dtype)
+        nbytes = int(lib.still_cache_bytes(ctypes.byref(self.cfg), max_tokens))
+        if nbytes == 0:
+            raise StillError(-2, "still_cache_bytes")
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = Cache()
+        _check(lib.still_cache_init(ctypes.byref(self.cfg), max_tokens, _ptr(self.buffer), nbytes,
+                                    ctypes.byref(self.c), _stream()), "still_cache_init")
+        ws = int(lib.still_decode_workspace_bytes(ctypes.byref(self.cfg), max_tokens))
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.c.n_tokens)
+
+    def tensors(self):
+        """Views of the device state (for inspection): dict of torch tensors."""
+        c, cfg = self.c, self.cfg
+        B, H, D, F = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.feat_dim
+        dt = torch.bfloat16 if cfg.dtype == STILL_BF16 else torch.float32
+        es = 2 if dt == torch.bfloat16 else 4
+        base = self.buffer.data_ptr()
+
+        def view(ptr, shape, dtype, esize):
+            n = 1
+            for x in shape:
+                n *= x
+            off = ptr - base
+            return self.buffer[off:off + n * esize].view(dtype).view(*shape)
+
+        cap = int(c.sel_capacity)
+        return {
+            "sel_k": view(c.sel_k, (B, H, cap, D), dt, es),
+            "sel_v": view(c.sel_v, (B, H, cap // 64, D, 64), dt, es),
+            "ring_k": view(c.ring_k, (B, H, 2, 64, D), dt, es),
+            "ring_v": view(c.ring_v, (B, H, 2, 64, D), dt, es),
+            "state_s": view(c.state_s, (B, H, F, D), torch.float32, 4),
+            "state_z": view(c.state_z, (B, H, F), torch.float32, 4),
+            "sel_mask": view(c.sel_mask, (B, H, 2), torch.int64, 8),
+            "cur_saliency": view(c.cur_saliency, (B, H, 64), torch.float32, 4),
+        }
+
+    def step(self, q, k, v, w_phi, out=None, *, stream=None, events=None):
+        """One token per sequence: q [B,Hq,D], k/v [B,Hkv,D] -> out [B,Hq,D]."""
+        for t in (q, k, v, w_phi):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("tensors must be contiguous device tensors")
+        if out is None:
+            out = torch.empty_like(q)
+        rc = load().still_decode_step_timed(ctypes.byref(self.cfg), ctypes.byref(self.c), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(w_phi), _ptr(out), _ptr(self.workspace),
+                                            self.workspace.numel(), _stream(stream), events)
+        _check(rc, "still_decode_step")
+        return out

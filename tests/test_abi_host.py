@@ -77,3 +77,63 @@ def test_workspace_scales_with_sequence():
     a = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(seq_len=1024)))
     b = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(seq_len=2048)))
     assert 1.8 < b / a < 2.2
+
+
+def _fake_cache(cfg, max_tokens=4096, n_tokens=0):
+    c = still.Cache()
+    c.cfg = cfg
+    c.max_tokens = max_tokens
+    c.n_tokens = n_tokens
+    c.sel_capacity = 64
+    for f in ("sel_k", "sel_v", "ring_k", "ring_v", "state_s", "state_z", "sel_mask", "cur_saliency"):
+        setattr(c, f, 1 << 24)
+    return c
+
+
+def test_cache_bytes_layout():
+    lib = still.load()
+    cfg = _cfg(n_q_heads=32, n_kv_heads=8, head_dim=128, feat_dim=128, top_k=16, batch=32)
+    n = lib.still_cache_bytes(ctypes.byref(cfg), 65600)
+    # compact rows: 1025 complete chunks x 16 rows, rounded up to tiles of 64 rows
+    rows = (65600 // 64 * 16 + 63) // 64 * 64
+    bh = 32 * 8
+    compact = 2 * bh * rows * 128 * 2
+    assert compact <= n < compact + 64 * 1024 * 1024
+    assert lib.still_cache_bytes(ctypes.byref(cfg), 0) == 0
+    assert lib.still_cache_bytes(ctypes.byref(_cfg(n_q_heads=17 * 2, n_kv_heads=2)), 1024) == 0  # group > 16
+    assert lib.still_decode_workspace_bytes(ctypes.byref(cfg), 65600) > 0
+
+
+def test_cache_init_rejects_bad_buffers():
+    lib = still.load()
+    cfg = _cfg()
+    need = lib.still_cache_bytes(ctypes.byref(cfg), 1024)
+    out = still.Cache()
+    assert lib.still_cache_init(ctypes.byref(cfg), 1024, None, need, ctypes.byref(out), None) == -1
+    assert lib.still_cache_init(ctypes.byref(cfg), 1024, ctypes.c_void_p((1 << 20) + 16), need,
+                                ctypes.byref(out), None) == -1
+    assert lib.still_cache_init(ctypes.byref(cfg), 1024, ctypes.c_void_p(1 << 20), need - 1,
+                                ctypes.byref(out), None) == -3
+
+
+def test_decode_step_validation():
+    lib = still.load()
+    cfg = _cfg()
+    p = ctypes.c_void_p(1 << 20)
+    ws = lib.still_decode_workspace_bytes(ctypes.byref(cfg), 4096)
+
+    def step(cache, c=cfg, wsb=ws, q=p):
+        return lib.still_decode_step(ctypes.byref(c), None if cache is None else ctypes.byref(cache), q, p, p, p,
+                                     p, p, wsb, None)
+
+    assert step(None) == -1
+    assert step(_fake_cache(cfg), q=None) == -1
+    assert step(_fake_cache(_cfg(top_k=4))) == -5
+    assert step(_fake_cache(cfg, max_tokens=100, n_tokens=100)) == -4
+    assert step(_fake_cache(cfg), wsb=ws - 1) == -3
+    # prefill into a cache: wrong layer, non-empty cache, too short
+    need = lib.still_prefill_workspace_bytes(ctypes.byref(cfg))
+    for cache, code in ((_fake_cache(_cfg(window=32)), -5), (_fake_cache(cfg, n_tokens=5), -1),
+                        (_fake_cache(cfg, max_tokens=100), -4)):
+        assert lib.still_prefill(ctypes.byref(cfg), p, p, p, p, p, None, None, None, ctypes.byref(cache), p, need,
+                                 None) == code
