@@ -1,13 +1,18 @@
-"""Benchmark of one STILL hybrid attention layer (prefill) on one MI355X.
+"""Benchmark of one STILL hybrid attention layer on one MI355X. Prints one JSON line.
 
-Workload: the Llama-3.2-1B-shaped layer at 16384 tokens (batch 1, 32 query / 8 KV heads,
-head_dim 64, window 64, chunk 64, top_k 8, NP-Map dim 64, bf16 in, fp32 accumulate), on
-seeded synthetic inputs that are resident in HBM before timing starts.
+Default workload: prefill of the Llama-3.2-1B-shaped layer at 16384 tokens (batch 1,
+32 query / 8 KV heads, head_dim 64, window 64, chunk 64, top_k 8, NP-Map dim 64, bf16 in,
+fp32 accumulate), on seeded synthetic inputs that are resident in HBM before timing
+starts. A step is one still_prefill call: saliency, per-chunk top-k, gather, NP-Map,
+chunk states, prefix scan and the fused softmax + linear attention.
 
-A step is one still_prefill call: saliency, per-chunk top-k, gather, NP-Map, chunk
-states, prefix scan and the fused softmax + linear attention. Prints one JSON line.
+--workload selects another layer shape: l8b-4k (Llama-3.1-8B-shaped, 8 x 4096 tokens),
+l8b-64k (1 x 65536 tokens), or l8b-decode: 32 sequences whose 65536-token prefix is put
+into a decode cache by one still_prefill call, then one still_decode_step per generated
+token (a step = one token for all 32 sequences; 64 timed steps cross one chunk boundary,
+so one selection / append / fold is inside the timed window).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--calibrate-copy]
+  python bench.py [--workload W] [--steps K] [--warmup W] [--no-cpu-baseline] [--calibrate-copy]
 
 --calibrate-copy runs one device-to-device copy of COPY_BYTES before the steps, so that
 a rocprofv3 --pmc run of this script also records what FETCH_SIZE / WRITE_SIZE read for a
@@ -38,6 +43,10 @@ _CSRC = os.path.join(ROOT, "linear_attention_saliency_amd", "csrc")
 ATTN_SRCS = [os.path.join(_CSRC, f) for f in ("still_attn.hip", "still_common.hpp", "still_layout.hpp",
                                               "still_launch.hpp", "still_route.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
+# the decode compact-cache kernel's source and the headers it includes
+DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("still_decode.hip", "still_common.hpp", "still_layout.hpp",
+                                                "still_launch.hpp", "still_route.hpp")]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.txt")
 
 
 def source_sha1(paths) -> str:
@@ -50,14 +59,16 @@ def source_sha1(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per attention-kernel launch from the committed counter summary, if it
-    was taken on the current kernel source; None otherwise."""
+def measured_traffic(workload: str, path: str = TRAFFIC_FILE, srcs=ATTN_SRCS):
+    """HBM bytes per launch of the bench's dominant kernel from a committed counter
+    summary, if it was taken on this workload and the current kernel source; else None."""
     try:
-        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        kv = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
     except OSError:
         return None
-    if kv.get("attn_source_sha1", "").strip() != source_sha1(ATTN_SRCS):
+    if kv.get("workload", "").strip() != workload:
+        return None
+    if kv.get("source_sha1", "").strip() != source_sha1(srcs):
         return None
     return float(kv["hbm_bytes_per_launch"])
 PEAK_BF16_MFMA = 2.5e15   # dense, FLOP/s
@@ -114,31 +125,28 @@ def cpu_baseline(wl, q, k, v, w, sel_idx) -> dict:
                       f"tokens) in {dt:.1f} s on a host with {os.cpu_count()} CPUs"}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (every step is "
-              "independent per (batch, KV head), so more GPUs would shard heads with no exchange)",
-              file=sys.stderr)
-        return 2
+def _events(torch, n_steps, per_step):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(per_step)] for _ in range(n_steps)]
+    stream = torch.cuda.current_stream()
+    for step in evs:  # torch creates the underlying HIP event on first record
+        for e in step:
+            e.record(stream)
+    import ctypes
+    handles = [(ctypes.c_void_p * per_step)(*[e.cuda_event for e in step]) for step in evs]
+    torch.cuda.synchronize()
+    return evs, handles
 
-    import torch
 
-    from linear_attention_saliency_amd import still, synth
-
-    wl = synth.L1B_16K
-    q, k, v, w = synth.make_inputs(wl)
+def run_prefill(wl, args, torch, still, synth) -> dict:
     dev = torch.device("cuda:0")
+    q, k, v, w = synth.make_inputs(wl)
     tq, tk, tv, tw = (torch.from_numpy(a).to(dev, torch.bfloat16).contiguous() for a in (q, k, v, w))
+    if not (wl is synth.L1B_16K and not args.no_cpu_baseline):
+        del q, k, v, w
     out = torch.empty_like(tq)
     call = still.Prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, chunk=wl.chunk)
     sel = torch.empty((wl.batch, wl.n_kv_heads, wl.seq_len // wl.chunk, wl.top_k), dtype=torch.int32, device=dev)
+    torch.cuda.reset_peak_memory_stats()
     call(tq, tk, tv, tw, out, sel_idx=sel)
     torch.cuda.synchronize()
     sel_idx = sel.cpu().numpy()
@@ -153,13 +161,7 @@ def main() -> int:
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out)
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for step in evs:  # torch creates the underlying HIP event on first record
-        for e in step:
-            e.record(stream)
-    import ctypes
-    handles = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in step]) for step in evs]
-    torch.cuda.synchronize()
+    evs, handles = _events(torch, args.steps, 4)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -179,8 +181,11 @@ def main() -> int:
     attn_ach = work["attn_flops"] / (attn_ms * 1e-3)
     layer_tflops = work["flops"] / (ms_step * 1e-3)
     layer_gbs = work["bytes"] / (ms_step * 1e-3)
+    esz = 2
+    io_bytes = esz * wl.batch * wl.seq_len * (2 * wl.n_q_heads + 2 * wl.n_kv_heads) * wl.head_dim
     res = {
-        "metric": METRIC,
+        "metric": METRIC if wl is synth.L1B_16K else
+        f"prefill tokens/s per layer ({wl.name}, bf16); % of HBM/MFMA roofline",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -197,15 +202,132 @@ def main() -> int:
                    "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(wl.name)},
         "layer_roofline": {"flops": work["flops"], "bytes": work["bytes"],
                            "mfma_frac": layer_tflops / PEAK_BF16_MFMA, "hbm_frac": layer_gbs / PEAK_HBM,
                            "frac": max(layer_tflops / PEAK_BF16_MFMA, layer_gbs / PEAK_HBM)},
         "kernel_ms": {"prep": prep_ms, "scan": scan_ms, "attn": attn_ms},
+        "memory": {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+                   "io_bytes": int(io_bytes), "workspace_bytes": int(call.workspace.numel()),
+                   "dense_scores_bf16_bytes": int(2 * wl.batch * wl.n_q_heads * wl.seq_len * wl.seq_len)},
         "wall_s": wall,
     }
-    if not args.no_cpu_baseline:
+    if wl is synth.L1B_16K and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, w, sel_idx)
+    return res
+
+
+def run_decode(wl, args, torch, still, synth) -> dict:
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, D, F = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.feat_dim
+    T0, C = wl.seq_len, wl.chunk
+    n_tok = args.warmup + args.steps
+    cache = still.DecodeCache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, feat_dim=F, window=wl.window,
+                              top_k=wl.top_k, max_tokens=T0 + n_tok, dtype=torch.bfloat16, device=dev)
+    # the 64K-token prefix of all sequences goes into the cache through one prefill
+    q, k, v, w = synth.make_inputs_device(wl, dev)
+    out = torch.empty_like(q)
+    call = still.Prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, chunk=C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    call(q, k, v, w, out, cache=cache)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    del q, k, v, out, call
+    torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    # the generated tokens: step t uses [:, t]
+    qs, ks, vs, _ = synth.make_inputs_device(wl, dev, seq_len=n_tok, seed_offset=1)
+    toks = [(qs[:, t].contiguous(), ks[:, t].contiguous(), vs[:, t].contiguous()) for t in range(n_tok)]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    for t in range(args.warmup):
+        cache.step(*toks[t], w, out)
+    stream = torch.cuda.current_stream()
+    evs, handles = _events(torch, args.steps, 3)
+    pos0 = cache.n_tokens
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        cache.step(*toks[args.warmup + s], w, out, events=handles[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = np.array([[step[j].elapsed_time(step[j + 1]) for j in range(2)] for step in evs])
+    split_ms, token_ms = (float(x) for x in k_ms.mean(axis=0))
+
+    # algorithmic bytes: the compact rows each step must read (K and V, bf16), per launch
+    nsel = [max(0, (p // C) - 1) * wl.top_k for p in range(pos0, pos0 + args.steps)]
+    split_bytes = float(np.mean(nsel)) * B * Hkv * 2 * D * 2
+    ring_bytes = B * Hkv * 2 * C * D * 2 * 2      # chunks c-1 and c, K and V
+    state_bytes = B * Hkv * (F * D + F) * 4
+    io_bytes = 2 * (2 * B * Hq * D + 2 * B * Hkv * D) + Hkv * F * D * 2
+    step_bytes = split_bytes + ring_bytes + state_bytes + io_bytes
+    ach = split_bytes / (split_ms * 1e-3)
+    return {
+        "metric": f"decode tokens/s per layer ({wl.name}, bf16); % of HBM roofline",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded (torch generator on the device) N(0,1)/sqrt(D) Q/K/V, W_phi N(0,1/D); bf16",
+        "config": {"workload": wl.name, "batch": B, "context": T0, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "feat_dim": F, "window": wl.window, "chunk": C, "top_k": wl.top_k},
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": ach / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach / PEAK_HBM,
+                     "traffic": measured_traffic(wl.name, DECODE_TRAFFIC_FILE, DECODE_SRCS)},
+        "layer_roofline": {"bytes": step_bytes, "hbm_frac": step_bytes / (ms_step * 1e-3) / PEAK_HBM},
+        "kernel_ms": {"split": split_ms, "token": token_ms},
+        "memory": {"cache_bytes": int(cache.buffer.numel()), "compact_rows_per_head": int(max(nsel)),
+                   "dense_kv_bytes": int(2 * B * Hkv * (T0 + n_tok) * D * 2)},
+        "prefill_into_cache_ms": prefill_ms,
+        "wall_s": wall,
+    }
+
+
+WORKLOAD_NAMES = {"l1b-16k": "L1B_16K", "l8b-4k": "L8B_4K", "l8b-64k": "L8B_64K", "l8b-decode": "L8B_DECODE"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=sorted(WORKLOAD_NAMES), default="l1b-16k")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 64 for decode)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 8 for decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (every step is "
+              "independent per (batch, KV head), so more GPUs would shard heads with no exchange)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from linear_attention_saliency_amd import still, synth
+
+    wl = getattr(synth, WORKLOAD_NAMES[args.workload])
+    decode = wl.decode_steps > 0
+    if args.steps is None:
+        args.steps = 64 if decode else 50
+    if args.warmup is None:
+        args.warmup = 8 if decode else 5
+    res = (run_decode if decode else run_prefill)(wl, args, torch, still, synth)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -1,13 +1,13 @@
 """Summaries of rocprofv3 CSV output for the kernels of this library.
 
   python -m linear_attention_saliency_amd.profile_summary stats <run_kernel_stats.csv>
-  python -m linear_attention_saliency_amd.profile_summary traffic <fetch_dir> <write_dir> <copy_bytes>
+  python -m linear_attention_saliency_amd.profile_summary traffic <fetch_dir> <write_dir> <copy_bytes> [kernel]
 
 `traffic` reads the counter_collection CSVs of a FETCH_SIZE pass and a WRITE_SIZE pass
-(rocprofv3 --pmc ... -- python3 bench.py --calibrate-copy ...): the copy kernel of known
-size (the launch whose counters are largest among the non-library kernels) gives the
-scale from counter KiB to bytes, which is applied to the attention kernel's mean per
-launch.
+(rocprofv3 --pmc ... -- python3 bench.py --calibrate-copy ...): the device-to-device copy
+of known size (the largest launch of the runtime's copyBuffer kernel) gives the scale from
+counter units to bytes, which is applied to the mean per launch of the library kernel
+whose name contains `kernel` (default attn_kernel).
 """
 
 from __future__ import annotations
@@ -39,19 +39,21 @@ def _per_kernel(dirpath: str, counter: str):
     return out
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_bytes: int) -> str:
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn_kernel") -> str:
     lines = []
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _per_kernel(d, counter)
-        copies = {k: v for k, v in per.items() if "still" not in k}
+        copies = {k: v for k, v in per.items() if "copyBuffer" in k}
         ck = max(copies, key=lambda k: max(copies[k]))
         scale = copy_bytes / max(copies[ck])  # bytes per counter unit
-        attn = [k for k in per if "attn_kernel" in k]
-        val = sum(per[attn[0]]) / len(per[attn[0]]) * scale
+        hits = [k for k in per if kernel in k and "still" in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one library kernel matching {kernel!r}, found {hits}")
+        val = sum(per[hits[0]]) / len(per[hits[0]]) * scale
         total += val
         lines.append(f"{counter}: copy kernel {ck[:60]} read {max(copies[ck]):.0f} for {copy_bytes} bytes "
-                     f"(scale {scale:.2f} B/unit); attention kernel mean {val / 1e6:.2f} MB per launch")
+                     f"(scale {scale:.2f} B/unit); {kernel} mean {val / 1e6:.2f} MB per launch")
     lines.append(f"hbm_bytes_per_launch: {total:.0f}")
     return "\n".join(lines)
 
@@ -60,4 +62,4 @@ if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
     elif sys.argv[1] == "traffic":
-        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4])))
+        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), *sys.argv[5:6]))

@@ -120,3 +120,37 @@ def small_case(seed: int, B: int, T: int, Hq: int, Hkv: int, D: int, F: int, win
     wl = Workload(f"case-s{seed}", B, T, Hq, Hkv, D, F, window, chunk, top_k, dtype, seed,
                   n_planted=n_planted, qk_scale=qk_scale)
     return wl, make_inputs(wl)
+
+
+def make_inputs_device(wl: Workload, device, seq_len: int | None = None, batch: int | None = None,
+                       seed_offset: int = 0):
+    """The same distributions drawn on the device with torch's generator (seed wl.seed +
+    seed_offset), for sizes where drawing on the host would dominate a benchmark. Returns
+    device tensors q, k, v, w_phi in wl.dtype. These bits differ from make_inputs'."""
+    import torch
+
+    B = wl.batch if batch is None else batch
+    T = wl.seq_len if seq_len is None else seq_len
+    D, Hq, Hkv, F = wl.head_dim, wl.n_q_heads, wl.n_kv_heads, wl.feat_dim
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed + seed_offset)
+    s = wl.scale()
+
+    def draw(shape, scale):
+        out = torch.empty(shape, dtype=dt, device=device)
+        for b in range(shape[0]):  # one sequence at a time keeps the fp32 temporary small
+            out[b] = (torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32) * scale).to(dt)
+        return out
+
+    q = draw((B, T, Hq, D), s)
+    k = draw((B, T, Hkv, D), s)
+    v = draw((B, T, Hkv, D), 1.0 / math.sqrt(D))
+    n_pl = min(wl.planted(), T)
+    if n_pl > 0:
+        for b in range(B):
+            for h in range(Hkv):
+                pos = torch.randperm(T, generator=g, device=device)[:n_pl]
+                k[b, pos, h, :] = (k[b, pos, h, :].float() * 4.0).to(dt)
+    w = (torch.randn((Hkv, F, D), generator=g, device=device, dtype=torch.float32) / math.sqrt(D)).to(dt)
+    return q.contiguous(), k.contiguous(), v.contiguous(), w.contiguous()
