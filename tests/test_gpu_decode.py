@@ -201,3 +201,41 @@ def test_decode_from_empty_matches_oracle(case):
     err = np.abs(out - ref).max()
     _say(name, "max abs err", err)
     assert err <= TOL[dt], err
+
+
+def test_decode_full_size_sampled():
+    """The batched decode workload at full size (32 sequences, 65536-token prefix put into
+    the cache by one prefill, head_dim 128, top_k 16), in the launch configuration the
+    benchmark times: two decode steps, sampled (sequence, KV head) groups against the
+    per-query oracle on the extended sequences under the device's routing."""
+    wl = synth.L8B_DECODE
+    _say("decode-full", wl.name)
+    dev = torch.device("cuda")
+    B, Hq, Hkv, D, T0, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.seq_len, wl.chunk
+    G = Hq // Hkv
+    n_new = 2
+    cache = _new_cache(wl, T0 + n_new)
+    q, k, v, w = synth.make_inputs_device(wl, dev)
+    out, idx = still.prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, return_routing=True, cache=cache)
+    del q, out
+    qn, kn, vn, _ = synth.make_inputs_device(wl, dev, seq_len=n_new, seed_offset=1)
+    outs = [cache.step(qn[:, t].contiguous(), kn[:, t].contiguous(), vn[:, t].contiguous(), w)
+            for t in range(n_new)]
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    wh = w.float().cpu().numpy()
+    worst = 0.0
+    for (b, h) in ((0, 0), (13, 5), (31, 7)):
+        kb = torch.cat([k[b, :, h], kn[b, :, h]]).float().cpu().numpy()[None, :, None, :]
+        vb = torch.cat([v[b, :, h], vn[b, :, h]]).float().cpu().numpy()[None, :, None, :]
+        qb = np.zeros((1, T0 + n_new, G, D), dtype=np.float32)
+        qb[0, T0:] = qn[b, :, h * G:(h + 1) * G].float().cpu().numpy()
+        selb = np.zeros((1, 1, T0 + n_new), dtype=bool)
+        selb[0, 0, idx[b, h].reshape(-1)] = True
+        rows = [(0, g, T0 + t) for t in range(n_new) for g in range(G)]
+        ref = O.brute_rows(qb, kb, vb, wh[h:h + 1], wl.window, C, selb, rows)
+        got = np.stack([_np(outs[t][b, h * G + g]) for (_, g, i) in rows for t in [i - T0]])
+        err = float(np.abs(got - ref).max())
+        worst = max(worst, err)
+        _say("decode-full", (b, h), "max abs err", err)
+    assert worst <= TOL["bf16"], worst

@@ -210,3 +210,28 @@ def test_headline_shape_sampled():
     err = np.abs(got - ref).max()
     _say("headline sampled max abs err", err)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["L8B_4K", "L8B_64K"])
+def test_8b_shapes_sampled(name):
+    """The Llama-3.1-8B-shaped layers at full size (8 x 4096 and 1 x 65536 tokens, head_dim
+    128, top_k 16): routing of KV head 0 over every chunk against the oracle, and sampled
+    output rows of all heads against the per-query oracle under the device's routing."""
+    wl = getattr(synth, name)
+    _say("8b", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    out, s_gpu, idx_gpu = _run(q, k, v, wp, wl)
+    G = wl.n_q_heads // wl.n_kv_heads
+    s_ref0, _ = O.saliency(q[:, :, :G], k[:, :, :1], wl.window)  # one group keeps the host work small
+    decided, flips = _check_routing(s_gpu[:, :1], idx_gpu[:, :1], s_ref0, wl)
+    _say(wl.name, "KV head 0 decided", decided, "flips", flips)
+    sel = _sel_from_idx(idx_gpu, wl.seq_len)
+    rng = np.random.default_rng(1)
+    T = wl.seq_len
+    rows = [(int(rng.integers(wl.batch)), int(rng.integers(wl.n_q_heads)), int(i)) for i in
+            np.concatenate([rng.integers(0, T, 16), [0, 64, 127, T - 1]])]
+    ref = O.brute_rows(q, k, v, wp, wl.window, wl.chunk, sel, rows)
+    got = np.stack([out[b, i, hq] for (b, hq, i) in rows])
+    err = np.abs(got - ref).max()
+    _say(wl.name, "sampled max abs err", err)
+    assert err <= TOL["bf16"]
