@@ -59,7 +59,7 @@ Dims dims_of(const still_config* c) {
 size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4; }
 
 struct WsLayout {
-  size_t sal, selmask, ksel, vselT, vT, phik, states, total;
+  size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, tilemax, total;
   int ntiles_sel;
 };
 
@@ -82,6 +82,8 @@ WsLayout ws_layout(const still_config* c) {
   L.vT = take(bh * d.nC * 64 * d.D * es);
   L.phik = take(bh * d.T * d.DF * es);
   L.states = take(bh * d.nC * d.R * sizeof(float));
+  L.kmaxc = take(bh * d.nC * sizeof(float));
+  L.tilemax = take(bh * (L.ntiles_sel > 0 ? L.ntiles_sel : 1) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -214,6 +216,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.vT = ws + L.vT;
   pa.vselT = ws + L.vselT;
   pa.ntiles_sel = L.ntiles_sel;
+  pa.kmaxc = reinterpret_cast<float*>(ws + L.kmaxc);
   if (cache && cfg->top_k > 0) {  // the compact rows go straight into the cache
     pa.ksel = cache->sel_k;
     pa.vselT = cache->sel_v;
@@ -222,7 +225,8 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
   if (still::launch_prep(pa, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[1], stream) != hipSuccess) return STILL_ERR_HIP;
-  if (still::launch_scan(d, pa.states, stream) != hipSuccess) return STILL_ERR_HIP;
+  float* tilemax = reinterpret_cast<float*>(ws + L.tilemax);
+  if (still::launch_scan(d, pa.states, pa.kmaxc, tilemax, L.ntiles_sel, stream) != hipSuccess) return STILL_ERR_HIP;
   if (events && hipEventRecord(events[2], stream) != hipSuccess) return STILL_ERR_HIP;
 
   still::AttnArgs aa;
@@ -238,6 +242,8 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.states = pa.states;
   aa.out = out;
   aa.ntiles_sel = pa.ntiles_sel;
+  aa.tilemax = tilemax;
+  aa.tm_stride = L.ntiles_sel;
   aa.nw = d.G >= 4 ? 4 : (d.G == 3 ? 4 : d.G);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
   if (still::launch_attn(aa, stream) != hipSuccess) return STILL_ERR_HIP;

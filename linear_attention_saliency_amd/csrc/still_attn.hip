@@ -19,9 +19,13 @@
 // shared-normaliser output  (sum_SA e^a v + N) / (sum_SA e^a + D)  needs no offset and
 // cannot overflow whatever the magnitudes.
 // Phase 2 (softmax): the two window tiles (masked), then the compact tiles, 64 keys per
-// tile, with the next tile's global loads in flight while the current one is computed
-// from a double-buffered LDS stage. The running max is refreshed only when a tile's max
-// exceeds it by more than 8 (log2 units), so the rescale is rare.
+// tile, in a three-stage LDS pipeline whose copies run straight from memory into LDS. The
+// running max is refreshed only when a tile's max exceeds it by more than 8 (log2 units);
+// a per-tile bound |q| max|k| skips even the max pass when it cannot move.
+//
+// Every tile the fixed part needs (phi(K) and V of chunk c-1, K and V of the window, the
+// prefix state) is copied into its own LDS region at the start, together with the first
+// compact tile, so the workgroup waits for memory once before computing.
 //
 // Everything is computed transposed (S^T = K Q^T, O^T += V^T P^T): a query is a lane's
 // column, so its statistics need only the 4-lane-group reduction, and P leaves the
@@ -155,30 +159,63 @@ __device__ __forceinline__ void sm_exp_pv(const f32x4 (&s)[4][QB], const T* lv, 
   }
 }
 
-template <typename T, int D, int DF, int QW, int NH>
+template <typename T, int D, int DF, int NH>
 struct AttnCfg {
+  static constexpr int QW = 32;                // queries per wave
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
   static constexpr int QSPLIT = 64 / QW;       // workgroups per chunk, one per query slice
   static constexpr int NTHR = 64 * NH;         // threads per workgroup: one wave per head
-  static constexpr int KBUF = 64 * (D > DF ? D : DF);  // elements of one K / phi(K) stage
-  static constexpr int VBUF = D * 64;                  // elements of one V^T stage
-  static constexpr int NSTAGE = 3;
-  static constexpr int LDS_BYTES = NSTAGE * (KBUF + VBUF) * static_cast<int>(sizeof(T));
+  static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
+  static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
+  // the prefix state goes through LDS when it is small (fp32 S^T [D][DF])
+  static constexpr bool STATE_LDS = D == 64 && DF == 64;
+  static constexpr int ST = STATE_LDS ? D * DF * 4 / static_cast<int>(sizeof(T)) : 0;
+  // LDS regions of the fixed part (element offsets); compact stages 1 and 2 reuse them
+  static constexpr int R_PHIP = 0, R_PHIC = FT, R_VP = 2 * FT, R_VC = 2 * FT + VT;
+  static constexpr int R_KC = 2 * FT + 2 * VT, R_KP = R_KC + KT, R_ST = R_KP + KT;
+  // compact pipeline: 4 stages; stage 0 after the fixed regions, stages 1..3 over them
+  static constexpr int NSTAGE = 4;
+  static constexpr int R_P0 = R_ST + ST > 3 * STAGE ? R_ST + ST : 3 * STAGE;
+  static constexpr int LDS_BYTES = (R_P0 + STAGE) * static_cast<int>(sizeof(T));
+  static __device__ __forceinline__ int stage_off(int s) { return s == 0 ? R_P0 : (s - 1) * STAGE; }
+  // buffer->LDS instructions each wave issues per compact tile (1 KiB each)
+  static constexpr int KINS = KT * static_cast<int>(sizeof(T)) / 1024, VINS = VT * static_cast<int>(sizeof(T)) / 1024;
+  static_assert(KINS % NH == 0 && VINS % NH == 0, "tile copies must split evenly over the waves");
+  static constexpr int NL = (KINS + VINS) / NH;
 };
 
-template <typename T, int D, int DF, int QW, int NH>
+// s_waitcnt immediate (gfx9 encoding) that waits for vector memory only, until at most n
+// operations of this wave are outstanding (LDS and scalar counters untouched)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier with compiler-only fences around it: the hardware waits are the
+// caller's (s_waitcnt before it), and no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <typename T> __device__ __forceinline__ typename Tr<T>::frag frag_of(const f32x8& x) {
+  typename Tr<T>::frag y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = Tr<T>::from_f(x[e]);
+  return y;
+}
+
+template <typename T, int D, int DF, int NH>
 __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
-  using C = AttnCfg<T, D, DF, QW, NH>;
-  constexpr int QB = C::QB, NTHR = C::NTHR;
+  using C = AttnCfg<T, D, DF, NH>;
+  constexpr int QB = C::QB, QW = C::QW, NTHR = C::NTHR;
   using SK = Swz<T, D>;    // K tile: 64 keys x D
-  using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF; prefix state: D rows x DF
+  using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF
   using SV = Swz<T, 64>;   // V^T tile: D rows x 64 keys
+  using SS = Swz<float, DF>;  // prefix state S^T: D rows x DF (fp32)
   constexpr int NB = D / 16;  // output blocks; block NB holds the row sums
   using TT = Tr<T>;
   using frag = typename TT::frag;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-  T* ldsK = reinterpret_cast<T*>(lds_raw);        // NSTAGE stages of KBUF
-  T* ldsV = ldsK + C::NSTAGE * C::KBUF;            // NSTAGE stages of VBUF
+  T* L = reinterpret_cast<T*>(lds_raw);
 
   const Dims& d = a.d;
   const T* q = static_cast<const T*>(a.q);
@@ -209,6 +246,45 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
   const float c1 = kLog2e / sqrtf(static_cast<float>(D));
   const int win = d.window;
+  const bool has_prev = c >= 1;
+  const bool la_cur = win < kChunk;  // chunk c holds linear keys (p <= r - w)
+  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
+  const int nt_comp = (n_comp + 63) / 64;
+  const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
+  const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
+  auto issue = [&](int t, int stage) {  // compact tile t -> LDS stage (asynchronous)
+    T* st = L + C::stage_off(stage);
+    dma_tile<T, D, NH>(st, kb_ptr + static_cast<long long>(t) * 64 * D, 64, D, 64);
+    dma_tile<T, 64, NH>(st + C::KT, vb_ptr + static_cast<long long>(t) * D * 64, D, 64, D);
+  };
+
+  // ---- 0. every copy the fixed part needs, plus compact tile 0 -------------------------
+  {
+    const int kvs = d.Hkv * D;  // row stride of k
+    const T* kc = kk + ((b * T_ + t0) * d.Hkv + h) * D;
+    if (has_prev) {
+      dma_tile<T, DF, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + t0 - kChunk) * DF, 64, DF, 64);
+      dma_tile<T, 64, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + c - 1) * D * 64, D, 64, D);
+      if (win >= 1) dma_tile<T, D, NH>(L + C::R_KP, kc - static_cast<long long>(kChunk) * kvs, 64, kvs, 64);
+    }
+    if (la_cur) dma_tile<T, DF, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, 64, DF, nvalid);
+    dma_tile<T, 64, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, D, 64, D);
+    if (win >= 1) dma_tile<T, D, NH>(L + C::R_KC, kc, 64, kvs, nvalid);
+    if constexpr (C::STATE_LDS) {
+      if (c >= 2)
+        dma_tile<float, DF, NH>(reinterpret_cast<float*>(L + C::R_ST),
+                                a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R, D, DF, D);
+    }
+    if (nt_comp > 0) issue(0, 0);
+  }
+  // key-norm bounds of compact tiles 0..255 (lane l of tb[j] holds tile 64 j + l; later
+  // tiles, if any, are treated as unbounded)
+  float tb[4];
+  {
+    const float* tmax = a.tilemax + static_cast<long long>(bh) * a.tm_stride;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tb[j] = 64 * j + lane < nt_comp ? tmax[64 * j + lane] : kInf;
+  }
 
   // ---- queries: B-operand fragments (SK over d) -------------------------------------
   frag qf[QB][D / 32];
@@ -222,6 +298,7 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 
   f32x4 o[NB + 1][QB];
   float m_run[QB];
+  float qn[QB];  // |q| c1: with |k| <= kmax, every logit of a tile is <= qn kmax
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -261,6 +338,7 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         }
       m2 = xor_sum_groups(m2);
       x2 = xor_sum_groups(x2);
+      qn[qb] = sqrtf(x2) * c1 * 1.001f;  // |q| in logit units, with slack for rounding
       const float sc = m2 > 0.f ? sqrtf(x2) / sqrtf(m2) : 0.f;
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs)
@@ -271,57 +349,53 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     float den[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) den[qb] = 0.f;
-    // prefix state of chunks <= c-2: staged in LDS as S^T[d][pk_pos(f)] (rounded to T)
-    // and z[f] (fp32), with coalesced loads, then contracted on MFMA
+    // z of the prefix state (8 consecutive permuted features per lane group)
+    f32x4 zr[DF / 32][2];
+    const float* Sg = a.states + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
     if (c >= 2) {
-      const float* S = a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R;
-      T* st = ldsK;  // D rows of DF elements: fits in the two K stages (128 rows of >= DF)
-      float* zs = reinterpret_cast<float*>(ldsV);
-      for (int idx = tid; idx < DF * D / 4; idx += NTHR) {
-        const int f = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(S + f * D + d4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st[SF::off(d4 + j, pk_pos(f))] = TT::from_f(x[j]);
+      for (int fs = 0; fs < DF / 32; ++fs) {
+        zr[fs][0] = *reinterpret_cast<const f32x4*>(Sg + DF * D + fs * 32 + grp * 8);
+        zr[fs][1] = *reinterpret_cast<const f32x4*>(Sg + DF * D + fs * 32 + grp * 8 + 4);
       }
-      for (int idx = tid; idx < DF; idx += NTHR) zs[idx] = S[DF * D + idx];
-      __syncthreads();
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every region copied at the start has landed
+
+    // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)] (fp32): each A-operand
+    // fragment (row d, the 8 features a lane group holds) is 8 consecutive floats
+    if (c >= 2) {
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs) {
 #pragma unroll
         for (int db = 0; db < NB; ++db) {
-          const frag sa = SF::load8(st, db * 16 + r16, fs * 32 + grp * 8);
+          f32x8 sx;
+          if constexpr (C::STATE_LDS) {
+            sx = SS::load8(reinterpret_cast<const float*>(L + C::R_ST), db * 16 + r16, fs * 32 + grp * 8);
+          } else {
+            const float* src = Sg + (db * 16 + r16) * DF + fs * 32 + grp * 8;
+            sx = Tr<float>::join(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4));
+          }
+          const frag sa = frag_of<T>(sx);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float zf = zs[fs * 32 + 16 * (e / 4) + 4 * grp + (e % 4)];
+          const float zf = zr[fs][e / 4][e % 4];
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) den[qb] += TT::to_f(pq[qb][fs][e]) * zf;
         }
       }
-      __syncthreads();  // the stages are reused below
     }
     // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w)
-    const uint64_t selprev = c >= 1 ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
-    const int cc_lo = c >= 1 ? c - 1 : c;
-    const int cc_hi = win < kChunk ? c : c - 1;
-    for (int cc = cc_lo; cc <= cc_hi; ++cc) {
-      const int st = cc - cc_lo;  // LDS stage
-      T* lk = ldsK + st * C::KBUF;
-      T* lv = ldsV + st * C::VBUF;
-      const int nk = cc == c ? nvalid : kChunk;
-      for (int idx = tid; idx < 64 * (DF / 8); idx += NTHR) {
-        const int p = idx / (DF / 8), c8 = idx % (DF / 8);
-        frag fx = TT::zero();
-        if (p < nk) fx = TT::load8(phik + (static_cast<long long>(bh) * T_ + static_cast<long long>(cc) * kChunk + p) * DF + c8 * 8);
-        SF::store8(lk, p, c8 * 8, fx);
-      }
-      for (int idx = tid; idx < D * 8; idx += NTHR) {
-        const int dd = idx / 8, c8 = idx % 8;
-        SV::store8(lv, dd, c8 * 8, TT::load8(vT + ((static_cast<long long>(bh) * d.nC + cc) * D + dd) * 64 + c8 * 8));
-      }
-      __syncthreads();
+    const uint64_t selprev = has_prev ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
+#pragma unroll
+    for (int cur = 0; cur < 2; ++cur) {
+      if (cur == 0 ? !has_prev : !la_cur) continue;  // uniform
+      const T* lk = L + (cur == 0 ? C::R_PHIP : C::R_PHIC);
+      const T* lv = L + (cur == 0 ? C::R_VP : C::R_VC);
       f32x4 ls[4][QB];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -334,13 +408,12 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
           for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
         }
       }
-      // linear keys: chunk c-1: p <= r + 64 - w and unselected; chunk c: p <= r - w
-      const uint32_t selw = cc == c ? 0u : bits_word(selprev);
+      const uint32_t selw = cur ? 0u : bits_word(selprev);
       frag pf[2][QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int r = qoff + qb * 16 + r16;
-        const uint32_t lw = range_word(0, cc == c ? r - win : r + 64 - win) & ~selw;
+        const uint32_t lw = range_word(0, cur ? r - win : r + 64 - win) & ~selw;
         float pv[4][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -375,127 +448,60 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
       const float l0 = dt > 0.f ? 1.f : 0.f;
       o[NB][qb] = f32x4{l0, l0, l0, l0};
     }
-    __syncthreads();  // LDS stages are reused by phase 2
   }
 
   // =============================== phase 2: softmax tiles ==============================
-  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
-  const int nt_comp = (n_comp + 63) / 64;
-  constexpr int KLD = D / 8;                        // 8-element pieces per K row
-  constexpr int NK16 = 64 * KLD;                    // pieces per K tile
-  constexpr int NV16 = D * 8;                       // pieces per V^T tile
-  constexpr int NPT = (NK16 + NV16 + NTHR - 1) / NTHR;
-  // per-thread piece geometry, fixed across tiles: global offset within a tile, and the
-  // tile row / column the piece lands on in LDS (K row = key, V^T row = d)
-  long long goff[NPT];
-  int prow[NPT], pcol[NPT];
-  bool isk[NPT], live[NPT];
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    const int idx = tid + i * NTHR;
-    live[i] = idx < NK16 + NV16;
-    isk[i] = idx < NK16;
-    if (isk[i]) {
-      const int p = idx / KLD, c8 = idx % KLD;
-      goff[i] = static_cast<long long>(p) * D + c8 * 8;
-      prow[i] = p;
-      pcol[i] = c8 * 8;
-    } else {
-      const int j = idx - NK16, dd = j / 8, c8 = j % 8;
-      goff[i] = static_cast<long long>(j) * 8;
-      prow[i] = dd;
-      pcol[i] = c8 * 8;
-    }
-  }
-  const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
-  const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
-  frag pre[NPT];  // a compact tile in flight (global -> registers -> LDS stage)
-  auto issue = [&](int t) {
-    const int rows = n_comp - t * 64;
-    const T* kt = kb_ptr + static_cast<long long>(t) * 64 * D;
-    const T* vt = vb_ptr + static_cast<long long>(t) * D * 64;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      frag x = TT::zero();
-      if (live[i] && (isk[i] ? prow[i] < rows : true)) x = TT::load8((isk[i] ? kt : vt) + goff[i]);
-      pre[i] = x;
-    }
-  };
-  auto commit = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      if (!live[i]) continue;
-      if (isk[i]) SK::store8(ldsK + stage * C::KBUF, prow[i], pcol[i], pre[i]);
-      else SV::store8(ldsV + stage * C::VBUF, prow[i], pcol[i], pre[i]);
-    }
-  };
-
-  // 2a. the window tiles: chunk c (causal) in stage 1, chunk c-1 (mixed) in stage 2.
-  //     The first compact tile's loads are in flight meanwhile.
-  if (win >= 1) {
-    const int nct = c >= 1 ? 2 : 1;
-    for (int ct = 0; ct < nct; ++ct) {
-      T* lk = ldsK + (1 + ct) * C::KBUF;
-      T* lv = ldsV + (1 + ct) * C::VBUF;
-      const long long tb = ct == 0 ? t0 : t0 - 64;
-      const int nk = ct == 0 ? nvalid : 64;
-      for (int idx = tid; idx < 64 * (D / 8); idx += NTHR) {
-        const int p = idx / (D / 8), c8 = idx % (D / 8);
-        frag x = TT::zero();
-        if (p < nk) x = TT::load8(kk + ((b * T_ + tb + p) * d.Hkv + h) * D + c8 * 8);
-        SK::store8(lk, p, c8 * 8, x);
-      }
-      const T* src = vT + (static_cast<long long>(bh) * d.nC + (ct == 0 ? c : c - 1)) * D * 64;
-      for (int idx = tid; idx < D * 8; idx += NTHR) {
-        const int dd = idx / 8, c8 = idx % 8;
-        SV::store8(lv, dd, c8 * 8, TT::load8(src + dd * 64 + c8 * 8));
-      }
-    }
-  }
-  if (nt_comp > 0) issue(0);
-  __syncthreads();
+  // 2a. the window: chunk c (r - w < p <= r), chunk c-1 (p > r + 64 - w, or selected)
   if (win >= 1) {
     f32x4 s[4][QB];
     uint32_t kw[QB];
-    qk_tile<T, D, QB>(ldsK + C::KBUF, qf, s);
+    qk_tile<T, D, QB>(L + C::R_KC, qf, s);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {  // chunk c: r - w < p <= r
+    for (int qb = 0; qb < QB; ++qb) {
       const int r = qoff + qb * 16 + r16;
       kw[qb] = range_word(r - win + 1, r);
     }
     mask_tile<QB>(s, kw);
     sm_max<D, QB>(s, o, m_run, c1);
-    sm_exp_pv<T, D, QB>(s, ldsV + C::VBUF, o, m_run, c1);
-    if (c >= 1) {
+    sm_exp_pv<T, D, QB>(s, L + C::R_VC, o, m_run, c1);
+    if (has_prev) {
       const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
       const uint32_t selw = bits_word(selprev);
-      qk_tile<T, D, QB>(ldsK + 2 * C::KBUF, qf, s);
+      qk_tile<T, D, QB>(L + C::R_KP, qf, s);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {  // chunk c-1: p > r + 64 - w, or selected
+      for (int qb = 0; qb < QB; ++qb) {
         const int r = qoff + qb * 16 + r16;
         kw[qb] = range_word(r + 65 - win, 63) | selw;
       }
       mask_tile<QB>(s, kw);
       sm_max<D, QB>(s, o, m_run, c1);
-      sm_exp_pv<T, D, QB>(s, ldsV + 2 * C::VBUF, o, m_run, c1);
+      sm_exp_pv<T, D, QB>(s, L + C::R_VP, o, m_run, c1);
     }
   }
 
   // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
-  //     Three LDS stages: while tile t's softmax runs, tile t+1 is already in LDS, so its
-  //     K Q^T product (MFMA) is independent of the softmax (VALU) and issues interleaved
-  //     with it; tile t+2 is in flight from global memory. One barrier per tile.
+  //     Tile t lives in stage t % 4. Tile 0 was copied at the start; tiles 1..3 go into
+  //     the fixed regions once every wave is done with them, and tile t+3 is issued in step
+  //     t, two steps ahead of its first use. In step t each wave waits for its own copies of
+  //     tile t+1 (those of tile t+2 may still be in flight), the barrier makes tile t+1
+  //     visible and frees tile t-1's stage; the K Q^T product of tile t+1 (MFMA) then issues
+  //     interleaved with the softmax of tile t (VALU). Rows past the last compact row of a
+  //     ragged tile are copied too (they lie inside the buffer; their scores are masked and
+  //     their V^T columns are zero or finite).
   if (nt_comp > 0) {
-    commit(0);
-    if (nt_comp > 1) issue(1);
-    __syncthreads();
     f32x4 sa[4][QB], sb[4][QB];
-    qk_tile<T, D, QB>(ldsK, qf, sa);
+    qk_tile<T, D, QB>(L + C::stage_off(0), qf, sa);  // tile 0 landed before phase 1
+    __syncthreads();
+#pragma unroll
+    for (int t = 1; t < 4; ++t)
+      if (t < nt_comp) issue(t, t);
     auto step = [&](int t, f32x4 (&s_cur)[4][QB], f32x4 (&s_next)[4][QB]) {
-      const int st = t % 3, stn = (t + 1) % 3;
-      if (t + 1 < nt_comp) commit(stn);
-      __syncthreads();
-      if (t + 2 < nt_comp) issue(t + 2);
+      if (t + 2 < nt_comp)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      if (t >= 1 && t + 3 < nt_comp) issue(t + 3, (t + 3) & 3);
       const int nk = n_comp - t * 64;
       if (nk < 64) {
         uint32_t kw[QB];
@@ -504,9 +510,20 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
         mask_tile<QB>(s_cur, kw);
       }
-      sm_max<D, QB>(s_cur, o, m_run, c1);
-      qk_tile<T, D, QB>(ldsK + stn * C::KBUF, qf, s_next);  // the last tile reads a stale stage: unused
-      sm_exp_pv<T, D, QB>(s_cur, ldsV + st * C::VBUF, o, m_run, c1);
+      // the running max can only move if some query's bound |q| kmax exceeds it by more
+      // than the lazy threshold; otherwise the max pass would leave everything unchanged
+      const int tj = t >> 6, tl = t & 63;
+      const float kt = tj == 0 ? __builtin_amdgcn_readlane(__float_as_int(tb[0]), tl)
+                     : tj == 1 ? __builtin_amdgcn_readlane(__float_as_int(tb[1]), tl)
+                     : tj == 2 ? __builtin_amdgcn_readlane(__float_as_int(tb[2]), tl)
+                     : tj == 3 ? __builtin_amdgcn_readlane(__float_as_int(tb[3]), tl)
+                               : __float_as_int(kInf);
+      bool far = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) far |= qn[qb] * __int_as_float(kt) > m_run[qb] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(far) != 0) sm_max<D, QB>(s_cur, o, m_run, c1);
+      qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, s_next);  // after the last tile: unused
+      sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o, m_run, c1);
     };
     for (int t = 0; t < nt_comp; t += 2) {
       step(t, sa, sb);
@@ -534,35 +551,35 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int D, int DF, int QW, int NH>
+template <typename T, int D, int DF, int NH>
 static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
-  using C = AttnCfg<T, D, DF, QW, NH>;
+  using C = AttnCfg<T, D, DF, NH>;
   const int P = a.d.B * a.d.Hkv * a.gsplit * C::QSPLIT;
   dim3 grid(a.d.nC * P);
   if (C::LDS_BYTES > 65536)  // opt in to more than 64 KiB of LDS (gfx950 has 160 KiB per CU)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, QW, NH>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, NH>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  hipLaunchKernelGGL((attn_kernel<T, D, DF, QW, NH>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
+  hipLaunchKernelGGL((attn_kernel<T, D, DF, NH>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int D, int DF, int QW>
+template <typename T, int D, int DF>
 static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
-  if (a.nw == 4) return attn_nh<T, D, DF, QW, 4>(a, s);
-  if (a.nw == 2) return attn_nh<T, D, DF, QW, 2>(a, s);
-  if (a.nw == 1) return attn_nh<T, D, DF, QW, 1>(a, s);
+  if (a.nw == 4) return attn_nh<T, D, DF, 4>(a, s);
+  if (a.nw == 2) return attn_nh<T, D, DF, 2>(a, s);
+  if (a.nw == 1) return attn_nh<T, D, DF, 1>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const Dims& dd = a.d;
   if (dd.bf16) {
-    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64, 32>(a, s);
-    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128, 32>(a, s);
-    if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64, 32>(a, s);
-    if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128, 32>(a, s);
+    if (dd.D == 64 && dd.DF == 64) return attn_t<bf16, 64, 64>(a, s);
+    if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128>(a, s);
+    if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64>(a, s);
+    if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128>(a, s);
   } else if (dd.D == 64 && dd.DF == 64) {
-    return attn_t<float, 64, 64, 32>(a, s);
+    return attn_t<float, 64, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -30,6 +30,15 @@ typedef __attribute__((ext_vector_type(8))) bf16 bf16x8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInf = __builtin_huge_valf();
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3); loads through
+// it take a 32-bit per-lane offset plus a wave-uniform offset, and read 0 out of range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
 template <typename T> struct Tr;
 
 template <> struct Tr<bf16> {
@@ -38,6 +47,9 @@ template <> struct Tr<bf16> {
   static __device__ __forceinline__ frag zero() { return frag{}; }
   static __device__ __forceinline__ frag load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
   static __device__ __forceinline__ quad load4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  static __device__ __forceinline__ frag bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
   static __device__ __forceinline__ void store8(bf16* p, frag x) { *reinterpret_cast<bf16x8*>(p) = x; }
   static __device__ __forceinline__ frag join(quad lo, quad hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -59,6 +71,11 @@ template <> struct Tr<float> {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   static __device__ __forceinline__ quad load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ frag bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   static __device__ __forceinline__ void store8(float* p, frag x) {
     *reinterpret_cast<f32x4*>(p) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
     *reinterpret_cast<f32x4*>(p + 4) = __builtin_shufflevector(x, x, 4, 5, 6, 7);
@@ -108,6 +125,39 @@ struct Swz {
   }
 };
 
+// Asynchronous copy of a tile of `rows` rows x RL elements into the Swz<T, RL> LDS tile at
+// `lds`, straight from memory (buffer_load ... lds: no registers involved). Row r of the
+// tile is read at gbase + r * gstride; rows at or beyond `valid_rows` arrive as zeros (the
+// buffer range check). One wave instruction fills 1 KiB of LDS: lane l writes byte 16 l, so
+// the lane fetches the granule that the swizzle stores in that slot. The waves of the
+// workgroup (NW of them) share the instructions. The data is visible to the workgroup
+// after s_waitcnt vmcnt(0) and a barrier.
+template <typename T, int RL, int NW>
+__device__ __forceinline__ void dma_tile(T* lds, const T* gbase, int rows, int gstride, int valid_rows) {
+  constexpr int RB = RL * static_cast<int>(sizeof(T));  // bytes per row
+  constexpr int NGR = RB / 16;                          // 16-byte granules per row
+  constexpr int RPI = 1024 / RB;                        // rows per instruction
+  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
+  static_assert(RB >= 128 && RB <= 1024 && 1024 % RB == 0, "row size");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t nrec =
+      valid_rows > 0 ? static_cast<uint32_t>(((valid_rows - 1) * gstride + RL) * static_cast<int>(sizeof(T))) : 0u;
+  const auto rs = make_rsrc(gbase, nrec);
+  const int nins = rows / RPI;
+  for (int j = wave; j < nins; j += NW) {
+    const int row = j * RPI + lane / NGR;
+    const int g = (lane % NGR) ^ (row & Swz<T, RL>::MASK);
+    const int voff = (row * gstride + g * EPG) * static_cast<int>(sizeof(T));
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS pointers exist only in the device pass
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(lds + j * RPI * RL), 16, voff, 0, 0, 0);
+#else
+    (void)rs;
+    (void)voff;
+#endif
+  }
+}
+
 // ---- wave64 cross-lane helpers -------------------------------------------------------
 
 // Reductions over the 4 lanes {l, l^16, l^32, l^48} without LDS traffic:
@@ -140,6 +190,12 @@ __device__ __forceinline__ float xor_sum_16(float x) {
   x += __shfl_xor(x, 2, 64);
   x += __shfl_xor(x, 4, 64);
   x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
   return x;
 }
 

@@ -26,10 +26,11 @@ struct PrepArgs {
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
   void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
-  float* states;              // [B,Hkv,nC,R]
+  float* states;              // [B,Hkv,nC,R]: S^T [D][DF] with features permuted by pk_pos, then z [DF] permuted
   void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos
   void* vselT;                // [B,Hkv,ntiles_sel,D,64]: compact V rows, same tile layout
   int ntiles_sel;             // compact tiles per (b, KV head): >= ceil(nCc*topk / 64)
+  float* kmaxc;               // [B,Hkv,nC]: largest |k| among each chunk's selected keys
 };
 
 struct AttnArgs {
@@ -45,6 +46,8 @@ struct AttnArgs {
   const float* states;  // inclusive prefix over complete chunks
   void* out;
   int ntiles_sel;
+  const float* tilemax; // [B,Hkv,tm_stride]: largest |k| in each compact tile
+  int tm_stride;
   int nw;               // query heads per workgroup (1, 2 or 4)
   int gsplit;           // workgroups per (b, kv head, chunk)
 };
@@ -91,7 +94,9 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
-hipError_t launch_scan(const Dims& d, float* states, hipStream_t s);
+// prefix sums of the chunk records, and the per-tile key-norm bound from kmaxc
+hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* tilemax, int tm_stride,
+                       hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* sal, int32_t* sel_idx, hipStream_t s);
 hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float* phi, hipStream_t s);

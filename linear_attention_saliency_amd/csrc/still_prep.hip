@@ -108,9 +108,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         m = topk_mask(s_acc[lane], d.topk);
       }
     }
+    // the largest key norm among the selected keys (xn2 holds |k|^2 of the chunk's rows)
+    const float kn = wave_max64(((m >> lane) & 1ull) ? xn2[lane] : 0.f);
     if (lane == 0) {
       s_mask = m;
       a.selmask[static_cast<long long>(bh) * d.nC + c] = m;
+      a.kmaxc[static_cast<long long>(bh) * d.nC + c] = sqrtf(kn);
     }
     if ((m >> lane) & 1ull) {
       const int slot = __popcll(m & ((1ull << lane) - 1ull));
@@ -193,48 +196,66 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
   }
 
-  // 7. U_c^T = V_c^T phi_masked and u_c, for complete chunks
+  // 7. U_c = phi_masked^T V_c and u_c, for complete chunks. Stored transposed with the
+  //    features permuted, S^T[d][pk_pos(f)], then u[pk_pos(f)]: the layout the attention
+  //    kernel feeds to MFMA straight from memory.
   if (!complete) return;  // uniform across the workgroup
-  f32x4 u[D / 16][FPW];
+  f32x4 u[FPW][D / 16];  // u[fi][db][i] = U[f = (wave*FPW + fi)*16 + 4*grp + i][d = db*16 + r16]
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
+  for (int fi = 0; fi < FPW; ++fi)
 #pragma unroll
-    for (int fi = 0; fi < FPW; ++fi) u[db][fi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < D / 16; ++db) u[fi][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    frag pb[FPW];
+    frag pa[FPW];  // A operand: row f, keys of the 32-key slice in accumulator order
 #pragma unroll
     for (int fi = 0; fi < FPW; ++fi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[fi][e] = TT::from_f(phi[2 * ks + e / 4][fi][e % 4]);
+      for (int e = 0; e < 8; ++e) pa[fi][e] = TT::from_f(phi[2 * ks + e / 4][fi][e % 4]);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      frag av;
+      frag vb;  // B operand: column d, the same keys
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = band[SW::off(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4), db * 16 + r16)];
+      for (int e = 0; e < 8; ++e) vb[e] = band[SW::off(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4), db * 16 + r16)];
 #pragma unroll
-      for (int fi = 0; fi < FPW; ++fi) TT::mma(u[db][fi], av, pb[fi]);
+      for (int fi = 0; fi < FPW; ++fi) TT::mma(u[fi][db], pa[fi], vb);
     }
   }
   float* st = a.states + (static_cast<long long>(bh) * d.nC + c) * d.R;
 #pragma unroll
   for (int fi = 0; fi < FPW; ++fi) {
-    const int f = (wave * FPW + fi) * 16 + r16;
+    const int fb = wave * FPW + fi;
+    // features fb*16 + 4*grp + 0..3 sit at 4 consecutive permuted positions
+    const int pos = fb / 2 * 32 + 8 * grp + 4 * (fb & 1);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(st + f * D + db * 16 + 4 * grp) = u[db][fi];
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(st + (db * 16 + r16) * DF + pos) = u[fi][db];
     float zs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) zs += phi[kb][fi][i];
     zs = xor_sum_groups(zs);
-    if (grp == 0) st[DF * D + f] = zs;
+    if (grp == 0) st[DF * D + pk_pos(fb * 16 + r16)] = zs;
   }
 }
 
 // Inclusive prefix sum of the chunk records over the complete chunks, in place.
-// One thread per record element; 16 chunk loads in flight per thread.
-__global__ __launch_bounds__(256) void scan_kernel(float* states, int nC, int nCc, int R) {
+// One thread per record element; 16 chunk loads in flight per thread. The last block
+// column instead reduces the per-chunk selected-key norms to one bound per compact tile
+// (tile t holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
+__global__ __launch_bounds__(256) void scan_kernel(float* states, int nC, int nCc, int R, const float* kmaxc,
+                                                   float* tilemax, int tm_stride, int topk) {
+  if (tm_stride > 0 && static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - 1) {
+    const long long bh = blockIdx.y;
+    for (int t = threadIdx.x; t < tm_stride; t += 256) {
+      const int c0 = 64 * t / topk;
+      const int c1 = min((64 * t + 63) / topk, nCc - 1);
+      float mx = 0.f;
+      for (int cc = c0; cc <= c1; ++cc) mx = fmaxf(mx, kmaxc[bh * nC + cc]);
+      tilemax[bh * tm_stride + t] = mx;
+    }
+    return;
+  }
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= R) return;
   float* p = states + static_cast<long long>(blockIdx.y) * nC * R + e;
@@ -345,10 +366,13 @@ hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float
 #undef DIMS
 }
 
-hipError_t launch_scan(const Dims& d, float* states, hipStream_t s) {
+hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* tilemax, int tm_stride,
+                       hipStream_t s) {
   if (d.nCc == 0) return hipSuccess;
-  dim3 grid((d.R + 255) / 256, d.B * d.Hkv);
-  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, s, states, d.nC, d.nCc, d.R);
+  const bool tiles = d.topk > 0 && tm_stride > 0;
+  dim3 grid((d.R + 255) / 256 + (tiles ? 1 : 0), d.B * d.Hkv);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
+                     tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
   return hipGetLastError();
 }
 
