@@ -252,10 +252,18 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   const int nt_comp = (n_comp + 63) / 64;
   const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
-  auto issue = [&](int t, int stage) {  // compact tile t -> LDS stage (asynchronous)
+  // compact tile t -> LDS stage (asynchronous); K rows [64][D] and V^T rows [D][64] of a
+  // tile are contiguous, so one resource per buffer covers every tile of this (b, h)
+  DmaTile<T, D, 64, NH> dk;
+  DmaTile<T, 64, D, NH> dv;
+  dk.init(D);
+  dv.init(64);
+  const auto krs = make_rsrc(kb_ptr, static_cast<uint32_t>(a.ntiles_sel) * C::KT * static_cast<int>(sizeof(T)));
+  const auto vrs = make_rsrc(vb_ptr, static_cast<uint32_t>(a.ntiles_sel) * C::VT * static_cast<int>(sizeof(T)));
+  auto issue = [&](int t, int stage) {
     T* st = L + C::stage_off(stage);
-    dma_tile<T, D, NH>(st, kb_ptr + static_cast<long long>(t) * 64 * D, 64, D, 64);
-    dma_tile<T, 64, NH>(st + C::KT, vb_ptr + static_cast<long long>(t) * D * 64, D, 64, D);
+    dk.issue(st, krs, t * C::KT * static_cast<int>(sizeof(T)));
+    dv.issue(st + C::KT, vrs, t * C::VT * static_cast<int>(sizeof(T)));
   };
 
   // ---- 0. every copy the fixed part needs, plus compact tile 0 -------------------------
@@ -263,17 +271,17 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     const int kvs = d.Hkv * D;  // row stride of k
     const T* kc = kk + ((b * T_ + t0) * d.Hkv + h) * D;
     if (has_prev) {
-      dma_tile<T, DF, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + t0 - kChunk) * DF, 64, DF, 64);
-      dma_tile<T, 64, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + c - 1) * D * 64, D, 64, D);
-      if (win >= 1) dma_tile<T, D, NH>(L + C::R_KP, kc - static_cast<long long>(kChunk) * kvs, 64, kvs, 64);
+      dma_tile<T, DF, 64, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + t0 - kChunk) * DF, DF, 64);
+      dma_tile<T, 64, D, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + c - 1) * D * 64, 64, D);
+      if (win >= 1) dma_tile<T, D, 64, NH>(L + C::R_KP, kc - static_cast<long long>(kChunk) * kvs, kvs, 64);
     }
-    if (la_cur) dma_tile<T, DF, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, 64, DF, nvalid);
-    dma_tile<T, 64, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, D, 64, D);
-    if (win >= 1) dma_tile<T, D, NH>(L + C::R_KC, kc, 64, kvs, nvalid);
+    if (la_cur) dma_tile<T, DF, 64, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, nvalid);
+    dma_tile<T, 64, D, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
+    if (win >= 1) dma_tile<T, D, 64, NH>(L + C::R_KC, kc, kvs, nvalid);
     if constexpr (C::STATE_LDS) {
       if (c >= 2)
-        dma_tile<float, DF, NH>(reinterpret_cast<float*>(L + C::R_ST),
-                                a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R, D, DF, D);
+        dma_tile<float, DF, D, NH>(reinterpret_cast<float*>(L + C::R_ST),
+                                   a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R, DF, D);
     }
     if (nt_comp > 0) issue(0, 0);
   }
@@ -513,14 +521,15 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
       // the running max can only move if some query's bound |q| kmax exceeds it by more
       // than the lazy threshold; otherwise the max pass would leave everything unchanged
       const int tj = t >> 6, tl = t & 63;
-      const float kt = tj == 0 ? __builtin_amdgcn_readlane(__float_as_int(tb[0]), tl)
-                     : tj == 1 ? __builtin_amdgcn_readlane(__float_as_int(tb[1]), tl)
-                     : tj == 2 ? __builtin_amdgcn_readlane(__float_as_int(tb[2]), tl)
-                     : tj == 3 ? __builtin_amdgcn_readlane(__float_as_int(tb[3]), tl)
-                               : __float_as_int(kInf);
+      const int k0 = __builtin_amdgcn_readlane(__float_as_int(tb[0]), tl);
+      const int k1 = __builtin_amdgcn_readlane(__float_as_int(tb[1]), tl);
+      const int k2 = __builtin_amdgcn_readlane(__float_as_int(tb[2]), tl);
+      const int k3 = __builtin_amdgcn_readlane(__float_as_int(tb[3]), tl);
+      const int kbits = tj == 0 ? k0 : tj == 1 ? k1 : tj == 2 ? k2 : tj == 3 ? k3 : __float_as_int(kInf);
+      const float kt = __int_as_float(kbits);
       bool far = false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) far |= qn[qb] * __int_as_float(kt) > m_run[qb] + 8.f;
+      for (int qb = 0; qb < QB; ++qb) far |= qn[qb] * kt > m_run[qb] + 8.f;
       if (__builtin_amdgcn_ballot_w64(far) != 0) sm_max<D, QB>(s_cur, o, m_run, c1);
       qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, s_next);  // after the last tile: unused
       sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o, m_run, c1);

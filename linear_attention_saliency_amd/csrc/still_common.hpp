@@ -125,37 +125,60 @@ struct Swz {
   }
 };
 
-// Asynchronous copy of a tile of `rows` rows x RL elements into the Swz<T, RL> LDS tile at
-// `lds`, straight from memory (buffer_load ... lds: no registers involved). Row r of the
-// tile is read at gbase + r * gstride; rows at or beyond `valid_rows` arrive as zeros (the
-// buffer range check). One wave instruction fills 1 KiB of LDS: lane l writes byte 16 l, so
-// the lane fetches the granule that the swizzle stores in that slot. The waves of the
-// workgroup (NW of them) share the instructions. The data is visible to the workgroup
-// after s_waitcnt vmcnt(0) and a barrier.
-template <typename T, int RL, int NW>
-__device__ __forceinline__ void dma_tile(T* lds, const T* gbase, int rows, int gstride, int valid_rows) {
-  constexpr int RB = RL * static_cast<int>(sizeof(T));  // bytes per row
-  constexpr int NGR = RB / 16;                          // 16-byte granules per row
-  constexpr int RPI = 1024 / RB;                        // rows per instruction
-  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
-  static_assert(RB >= 128 && RB <= 1024 && 1024 % RB == 0, "row size");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Asynchronous copy of a ROWS x RL tile into the Swz<T, RL> LDS tile, straight from memory
+// (buffer_load ... lds: no registers hold the data). Row r of the tile is read at byte
+// r * gstride * sizeof(T) of the buffer resource, plus a wave-uniform byte offset; reads
+// outside the resource's range arrive as zeros. One wave instruction fills 1 KiB of LDS
+// (lane l writes byte 16 l), so each lane fetches the granule the swizzle stores in its
+// slot. The NW waves of the workgroup split the instructions; the per-lane offsets are
+// fixed by the geometry, so init() runs once and issue() is a few scalar ops and the
+// copies. The data is visible to the workgroup after s_waitcnt vmcnt and a barrier.
+template <typename T, int RL, int ROWS, int NW>
+struct DmaTile {
+  static constexpr int RB = RL * static_cast<int>(sizeof(T));  // bytes per row
+  static constexpr int NGR = RB / 16;                          // 16-byte granules per row
+  static constexpr int RPI = 1024 / RB;                        // rows per instruction
+  static constexpr int EPG = 16 / static_cast<int>(sizeof(T));
+  static constexpr int NINS = ROWS / RPI;                      // instructions per tile
+  static constexpr int PER_WAVE = NINS / NW;
+  static_assert(RB >= 128 && RB <= 1024 && 1024 % RB == 0 && ROWS % RPI == 0 && NINS % NW == 0, "tile geometry");
+  int voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(int gstride) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int row = (wave + i * NW) * RPI + lane / NGR;
+      const int g = (lane % NGR) ^ (row & Swz<T, RL>::MASK);
+      voff[i] = (row * gstride + g * EPG) * static_cast<int>(sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue(T* lds, __amdgpu_buffer_rsrc_t rs, int soff) const {
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS pointers exist only in the device pass
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + (wave + i * NW) * RPI * RL), 16, voff[i], soff, 0, 0);
+#else
+      (void)lds;
+      (void)rs;
+      (void)soff;
+      (void)wave;
+#endif
+    }
+  }
+};
+
+// One-off copy of a tile whose rows at or beyond valid_rows read as zeros.
+template <typename T, int RL, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(T* lds, const T* gbase, int gstride, int valid_rows) {
   const uint32_t nrec =
       valid_rows > 0 ? static_cast<uint32_t>(((valid_rows - 1) * gstride + RL) * static_cast<int>(sizeof(T))) : 0u;
-  const auto rs = make_rsrc(gbase, nrec);
-  const int nins = rows / RPI;
-  for (int j = wave; j < nins; j += NW) {
-    const int row = j * RPI + lane / NGR;
-    const int g = (lane % NGR) ^ (row & Swz<T, RL>::MASK);
-    const int voff = (row * gstride + g * EPG) * static_cast<int>(sizeof(T));
-#if defined(__HIP_DEVICE_COMPILE__)  // LDS pointers exist only in the device pass
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(lds + j * RPI * RL), 16, voff, 0, 0, 0);
-#else
-    (void)rs;
-    (void)voff;
-#endif
-  }
+  DmaTile<T, RL, ROWS, NW> t;
+  t.init(gstride);
+  t.issue(lds, make_rsrc(gbase, nrec), 0);
 }
 
 // ---- wave64 cross-lane helpers -------------------------------------------------------
