@@ -230,6 +230,9 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   T* ring_v = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * 2 * 64 * D;
   const uint64_t prev_mask = has_prev ? a.c.sel_mask[bh * 2 + slot_prev] : 0ull;
 
+  typename Tr<T>::frag wf[DF / 64][D / 32];  // NP-Map weights, loaded early
+  np_map_load_w<T, D, DF>(wh, wf);
+
   // 0. stage the ring (and the new token) in LDS; append the token to the ring
   for (int idx = tid; idx < 129 * V8; idx += 256) {
     const int row = idx / V8, c8 = idx % V8;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
       continue;
     }
     f32x4 phi[4][FPW];
-    np_map_rows64<T, D, DF>(kt, half * 64, wh, m2part, xn2, phi);
+    np_map_rows64<T, D, DF>(kt, half * 64, wf, m2part, xn2, phi);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     }
   }
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF>(kt, 0, wh, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(kt, 0, wf, m2part, xn2, phi);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll

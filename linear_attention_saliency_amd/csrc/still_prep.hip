@@ -49,6 +49,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const bool complete = nvalid == kChunk;
   const float scale = kLog2e / sqrtf(static_cast<float>(D));  // saliency logits in log2 units
 
+  // 0. global reads issued up front so their latencies overlap the band and saliency work:
+  //    the NP-Map weights and the chunk's V rows
+  frag wf[DF / 64][D / 32];
+  np_map_load_w<T, D, DF>(w + static_cast<long long>(h) * DF * D, wf);
+  constexpr int VPT = 64 * V8 / 256;  // V pieces per thread
+  frag vpre[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * 256, row = idx / V8, c8 = idx % V8;
+    vpre[i] = row < nvalid ? TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8) : TT::zero();
+  }
+
   // 1. key band: row t <-> position t0 - 63 + t (row 127 is never in a window)
   for (int idx = tid; idx < 128 * V8; idx += 256) {
     const int row = idx / V8, c8 = idx % V8;
@@ -90,7 +102,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
   // 3. NP-Map of the chunk's keys (band rows 63..126)
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF>(band, 63, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(band, 63, wf, m2part, xn2, phi);
 
   // 4. routing of a complete chunk
   const long long nsel_rows = static_cast<long long>(d.nCc) * d.topk;
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       const long long dst =
           (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
-      if (slot < nsel) kx = TT::load8(k + ((b * T_ + t0 + selpos[slot]) * d.Hkv + h) * D + c8 * 8);
+      if (slot < nsel) kx = SW::load8(band, 63 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 63..126
       TT::store8(ks_ + dst, kx);
     }
   }
@@ -152,13 +164,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         phi[kb][fi][i] = ((smask >> row) & 1ull) ? 0.f : TT::to_f(val);
       }
 
-  // 6. V of the chunk: stage in LDS (zero past the sequence end), write the transposed,
-  //    key-permuted copy vT, and the compact transposed copy of the selected rows
-  for (int idx = tid; idx < 64 * V8; idx += 256) {
-    const int row = idx / V8, c8 = idx % V8;
-    frag x = TT::zero();
-    if (row < nvalid) x = TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8);
-    SW::store8(band, row, c8 * 8, x);
+  // 6. V of the chunk (loaded at the start; zero past the sequence end): stage in LDS over
+  //    the band once the gather is done with it, write the transposed, key-permuted copy vT,
+  //    and the compact transposed copy of the selected rows
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * 256;
+    SW::store8(band, idx / V8, (idx % V8) * 8, vpre[i]);
   }
   __syncthreads();
   {
@@ -240,14 +253,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // Inclusive prefix sum of the chunk records over the complete chunks, in place.
-// One thread per record element; 16 chunk loads in flight per thread. The last block
-// column instead reduces the per-chunk selected-key norms to one bound per compact tile
-// (tile t holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
-__global__ __launch_bounds__(256) void scan_kernel(float* states, int nC, int nCc, int R, const float* kmaxc,
-                                                   float* tilemax, int tm_stride, int topk) {
+// One thread per record element. The chain of adds is serial but the loads are not: a
+// thread keeps 64 chunk loads in flight, so a sequence of n chunks costs about n / 64
+// memory round trips. The last block column instead reduces the per-chunk selected-key
+// norms to one bound per compact tile (tile t holds compact rows 64t .. 64t+63, i.e.
+// chunks 64t/topk .. (64t+63)/topk).
+__global__ __launch_bounds__(64) void scan_kernel(float* states, int nC, int nCc, int R, const float* kmaxc,
+                                                  float* tilemax, int tm_stride, int topk) {
   if (tm_stride > 0 && static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - 1) {
     const long long bh = blockIdx.y;
-    for (int t = threadIdx.x; t < tm_stride; t += 256) {
+    for (int t = threadIdx.x; t < tm_stride; t += 64) {
       const int c0 = 64 * t / topk;
       const int c1 = min((64 * t + 63) / topk, nCc - 1);
       float mx = 0.f;
@@ -256,16 +271,17 @@ __global__ __launch_bounds__(256) void scan_kernel(float* states, int nC, int nC
     }
     return;
   }
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  constexpr int NF = 64;  // loads in flight per thread
+  const int e = blockIdx.x * 64 + threadIdx.x;
   if (e >= R) return;
   float* p = states + static_cast<long long>(blockIdx.y) * nC * R + e;
   float acc = 0.f;
-  for (int c0 = 0; c0 < nCc; c0 += 16) {
-    float x[16];
+  for (int c0 = 0; c0 < nCc; c0 += NF) {
+    float x[NF];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = c0 + j < nCc ? p[static_cast<long long>(c0 + j) * R] : 0.f;
+    for (int j = 0; j < NF; ++j) x[j] = c0 + j < nCc ? p[static_cast<long long>(c0 + j) * R] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < NF; ++j)
       if (c0 + j < nCc) {
         acc += x[j];
         p[static_cast<long long>(c0 + j) * R] = acc;
@@ -298,6 +314,8 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const long long T_ = d.T, t0 = static_cast<long long>(c) * 64;
+  typename Tr<T>::frag wf[DF / 64][D / 32];
+  np_map_load_w<T, D, DF>(w + static_cast<long long>(h) * DF * D, wf);
   for (int idx = tid; idx < 64 * V8; idx += 256) {
     const int row = idx / V8, c8 = idx % V8;
     typename TT::frag val = TT::zero();
@@ -306,7 +324,7 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
   }
   __syncthreads();
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF>(rows, 0, w + static_cast<long long>(h) * DF * D, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(rows, 0, wf, m2part, xn2, phi);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -370,8 +388,8 @@ hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* 
                        hipStream_t s) {
   if (d.nCc == 0) return hipSuccess;
   const bool tiles = d.topk > 0 && tm_stride > 0;
-  dim3 grid((d.R + 255) / 256 + (tiles ? 1 : 0), d.B * d.Hkv);
-  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
+  dim3 grid((d.R + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(64), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
                      tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
   return hipGetLastError();
 }

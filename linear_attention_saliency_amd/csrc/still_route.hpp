@@ -97,16 +97,29 @@ __device__ __forceinline__ uint64_t topk_mask(float s, int topk) {
 // NP-Map of 64 rows ([P1] section "Norm-Preserved Feature Map（NP-Map）"; [P4] section
 // Approach): phi(x) = |x| m / |m|, m = elu(W_h x) + 1.
 //
-// rows: rows row0 .. row0+63 of a Swz<T, D> LDS tile. Wh: W_h in global memory [DF][D].
-// Four waves; wave w owns feature blocks fb = w*FPW + fi (FPW = DF/64). On return
+// rows: rows row0 .. row0+63 of a Swz<T, D> LDS tile. wf: this wave's W_h fragments from
+// np_map_load_w. Four waves; wave w owns feature blocks fb = w*FPW + fi (FPW = DF/64). On return
 // phi[kb][fi][i] = phi(row kb*16 + 4*grp + i)[feature fb*16 + r16] in fp32.
 // Scratch in LDS: m2part[4*64], xn2[64]. Contains one __syncthreads(); all 256 threads
 // must call. After it returns no thread reads `rows` again.
+// The W_h fragments np_map_rows64 needs (B operand: feature column fb*16 + r16 of wave w's
+// feature blocks), loaded ahead of time so their latency can overlap other work.
 template <typename T, int D, int DF>
-__device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const T* Wh, float* m2part, float* xn2,
-                                              f32x4 (&phi)[4][DF / 64]) {
+__device__ __forceinline__ void np_map_load_w(const T* Wh, typename Tr<T>::frag (&wf)[DF / 64][D / 32]) {
   constexpr int FPW = DF / 64;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int fi = 0; fi < FPW; ++fi)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      wf[fi][ks] = Tr<T>::load8(Wh + ((wave * FPW + fi) * 16 + r16) * D + ks * 32 + grp * 8);
+}
+
+template <typename T, int D, int DF>
+__device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const typename Tr<T>::frag (&wf)[DF / 64][D / 32],
+                                              float* m2part, float* xn2, f32x4 (&phi)[4][DF / 64]) {
+  constexpr int FPW = DF / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
   if (tid < 64) {
     float s = 0.f;
     for (int d = 0; d < D; ++d) {
@@ -117,17 +130,13 @@ __device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const T* 
   }
 #pragma unroll
   for (int fi = 0; fi < FPW; ++fi) {
-    const int fb = wave * FPW + fi;
-    typename Tr<T>::frag wf[D / 32];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) wf[ks] = Tr<T>::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const typename Tr<T>::frag a = Swz<T, D>::load8(rows, row0 + kb * 16 + r16, ks * 32 + grp * 8);
-        Tr<T>::mma(acc, a, wf[ks]);
+        Tr<T>::mma(acc, a, wf[fi][ks]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
