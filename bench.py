@@ -307,7 +307,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=sorted(WORKLOAD_NAMES), default="l1b-16k")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 64 for decode)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 8 for decode)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 100 for prefill, enough for the clocks to settle; 8 for decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -326,7 +327,7 @@ def main() -> int:
     if args.steps is None:
         args.steps = 64 if decode else 50
     if args.warmup is None:
-        args.warmup = 8 if decode else 5
+        args.warmup = 8 if decode else 100
     res = (run_decode if decode else run_prefill)(wl, args, torch, still, synth)
     print(json.dumps(res), flush=True)
     return 0

@@ -99,7 +99,8 @@ typedef struct still_cache {
   int64_t max_tokens;   /* capacity per sequence */
   int64_t n_tokens;     /* tokens held per sequence = position of the next token */
   int64_t sel_capacity; /* compact rows per (batch, KV head), a multiple of 64 */
-  void* sel_k;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype */
+  void* sel_k;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype: the selected key
+                           rows times log2(e)/sqrt(head_dim), rounded to dtype */
   void* sel_v;          /* [batch, n_kv_heads, sel_capacity / 64, head_dim, 64] dtype */
   void* ring_k;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
   void* ring_v;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */

@@ -159,6 +159,87 @@ __device__ __forceinline__ void sm_exp_pv(const f32x4 (&s)[4][QB], const T* lv, 
   }
 }
 
+// Compact tiles: their K rows carry the factor log2(e)/sqrt(D), and the K Q^T product
+// starts from the accumulator value -m (the running max of each query column), so the
+// scores leave the MFMA as s = a_ij log2(e) - m and P = 2^s needs no VALU before the exp.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void qk_tile_shifted(const T* lk, const typename Tr<T>::frag (&qf)[QB][D / 32],
+                                                const f32x4 (&mneg)[QB], f32x4 (&s)[4][QB]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mneg[qb];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const typename Tr<T>::frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) Tr<T>::mma(s[kb][qb], ka, qf[qb][ks]);
+    }
+  }
+}
+
+// Running-max update for shifted scores: a column moves only if its tile max exceeds 8
+// (2^8 is the largest P the accumulators then see); the accumulators are rescaled, the
+// tile's scores and the column's -m re-based. Rare after the first tiles.
+template <int D, int QB>
+__device__ __forceinline__ void sm_max_shifted(f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB],
+                                               f32x4 (&mneg)[QB]) {
+  bool need_any = false;
+  float dm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float tm = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tm = fmaxf(tm, s[kb][qb][i]);
+    tm = xor_max_groups(tm);
+    const bool need = tm > 8.f;
+    dm[qb] = need ? tm : 0.f;
+    need_any |= need;
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float alpha = __builtin_amdgcn_exp2f(-dm[qb]);
+      m_run[qb] += dm[qb];
+      mneg[qb] -= dm[qb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb][qb] -= dm[qb];
+#pragma unroll
+      for (int db = 0; db <= D / 16; ++db) o[db][qb] *= alpha;
+    }
+  }
+}
+
+// P = 2^s (shifted scores), then O^T += V^T P^T as in sm_exp_pv.
+template <typename T, int D, int QB>
+__device__ __forceinline__ void sm_exp_pv_shifted(const f32x4 (&s)[4][QB], const T* lv, f32x4 (&o)[D / 16 + 1][QB]) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  frag one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = TT::from_f(1.0f);
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    frag pf[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[2 * hs + e / 4][qb][e % 4]));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) TT::mma(o[D / 16][qb], one, pf[qb]);
+  }
+}
+
 template <typename T, int D, int DF, int NH>
 struct AttnCfg {
   static constexpr int QW = 32;                // queries per wave
@@ -497,8 +578,11 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   //     ragged tile are copied too (they lie inside the buffer; their scores are masked and
   //     their V^T columns are zero or finite).
   if (nt_comp > 0) {
+    f32x4 mneg[QB];  // -m per query column, the starting accumulator of K Q^T
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mneg[qb] = f32x4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
     f32x4 sa[4][QB], sb[4][QB];
-    qk_tile<T, D, QB>(L + C::stage_off(0), qf, sa);  // tile 0 landed before phase 1
+    qk_tile_shifted<T, D, QB>(L + C::stage_off(0), qf, mneg, sa);  // tile 0 landed before phase 1
     __syncthreads();
 #pragma unroll
     for (int t = 1; t < 4; ++t)
@@ -530,9 +614,9 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
       bool far = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) far |= qn[qb] * kt > m_run[qb] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(far) != 0) sm_max<D, QB>(s_cur, o, m_run, c1);
-      qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, s_next);  // after the last tile: unused
-      sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o, m_run, c1);
+      if (__builtin_amdgcn_ballot_w64(far) != 0) sm_max_shifted<D, QB>(s_cur, o, m_run, mneg);
+      qk_tile_shifted<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, mneg, s_next);  // after the last tile: unused
+      sm_exp_pv_shifted<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o);
     };
     for (int t = 0; t < nt_comp; t += 2) {
       step(t, sa, sb);

@@ -62,7 +62,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / d.Hkv, h = bh % d.Hkv, G = d.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
-  const float scale = kLog2e / sqrtf(static_cast<float>(D));
   const int ntiles = (a.nsel + 63) / 64;
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(ntiles, t_begin + a.tiles_per_split);
@@ -108,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j * 16 + 4 * grp + i;
-        const float x = key < valid ? s[j][i] * scale : -kInf;
+        const float x = key < valid ? s[j][i] : -kInf;  // compact K rows carry log2(e)/sqrt(D)
         s[j][i] = x;
         mx = fmaxf(mx, x);
       }
@@ -440,7 +439,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
       const int p = idx / D, dd = idx % D;
       if ((prev_mask >> p) & 1ull) {
         const long long R = row0 + __popcll(prev_mask & ((1ull << p) - 1ull));
-        sk[R * D + dd] = kt[SW::off(p, dd)];
+        sk[R * D + dd] = TT::from_f(TT::to_f(kt[SW::off(p, dd)]) * scale);  // compact rows are pre-scaled
         sv[((R / 64) * D + dd) * 64 + pk_pos(static_cast<int>(R % 64))] = vt[p * D + dd];
       }
     }

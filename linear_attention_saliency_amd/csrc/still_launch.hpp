@@ -24,7 +24,7 @@ struct PrepArgs {
   float* sal;                 // [B,Hkv,T]
   uint64_t* selmask;          // [B,Hkv,nC]
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
-  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows
+  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows times log2(e)/sqrt(D)
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
   float* states;              // [B,Hkv,nC,R]: S^T [D][DF] with features permuted by pk_pos, then z [DF] permuted
   void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos

@@ -8,7 +8,8 @@
 //   3. NP-Map of the chunk's keys ([P1] section "Norm-Preserved Feature Map（NP-Map）");
 //   4. top-k routing of a complete chunk, ascending positions, and the gather of the
 //      selected K/V rows into the compact softmax cache ([P1] section
-//      "Chunk-Wise并行+延迟选择");
+//      "Chunk-Wise并行+延迟选择"); the K rows are stored pre-multiplied by
+//      log2(e)/sqrt(D), so their products with q are logits in log2 units;
 //   5. the chunk's linear-attention contribution U_c = sum over its unselected keys of
 //      phi(k) v^T and u_c = sum phi(k) ([P3] on the fixed-size state of linear attention).
 // scan_kernel then turns the U_c into inclusive prefix sums over chunks.
@@ -144,6 +145,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
           (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
       if (slot < nsel) kx = SW::load8(band, 63 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 63..126
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[e] = TT::from_f(TT::to_f(kx[e]) * scale);  // logits in log2 units
       TT::store8(ks_ + dst, kx);
     }
   }
