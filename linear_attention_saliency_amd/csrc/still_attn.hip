@@ -393,10 +393,13 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db <= NB; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // window = chunk takes a fast path for the masks and handles chunk c-1's linear keys
+  // together with its window tile (head_dim 64; at 128 the extra live registers spill)
+  const bool fast = D == 64 && win == kChunk;
+  frag pq[QB][DF / 32];  // phi(q): B-operand fragments (PK over f)
   // =============================== phase 1: linear attention ===========================
   {
-    // phi(q) = |q| m / |m|, m = elu(W_h q) + 1: B-operand fragments (PK over f)
-    frag pq[QB][DF / 32];
+    // phi(q) = |q| m / |m|, m = elu(W_h q) + 1
     const T* Wh = w + static_cast<long long>(h) * DF * D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -478,11 +481,12 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         }
       }
     }
-    // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w)
+    // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w);
+    // the fast path takes chunk c-1's with its window tile (chunk c has none when w = 64)
     const uint64_t selprev = has_prev ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
 #pragma unroll
     for (int cur = 0; cur < 2; ++cur) {
-      if (cur == 0 ? !has_prev : !la_cur) continue;  // uniform
+      if (fast || (cur == 0 ? !has_prev : !la_cur)) continue;  // uniform
       const T* lk = L + (cur == 0 ? C::R_PHIP : C::R_PHIC);
       const T* lv = L + (cur == 0 ? C::R_VP : C::R_VC);
       f32x4 ls[4][QB];
@@ -541,7 +545,117 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 
   // =============================== phase 2: softmax tiles ==============================
   // 2a. the window: chunk c (r - w < p <= r), chunk c-1 (p > r + 64 - w, or selected)
-  if (win >= 1) {
+  if (fast) {
+    // Masks by block: lane (r16, grp) holds keys kb*16 + 4 grp + i of query qoff + qb*16 + r16,
+    // so for key block kb and query block qb (blk = 16 (kb - qb) - qoff, uniform) key <= query
+    // holds for all lanes if blk < 0, for none if blk > 0, and where 4 grp + i <= r16 if
+    // blk = 0 (four lane masks shared by every diagonal block).
+    bool dmask[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
+    f32x4 s[4][QB];
+    // chunk c: softmax keys p <= r
+    qk_tile<T, D, QB>(L + C::R_KC, qf, s);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int blk = 16 * (kb - qb) - qoff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool keep = blk < 0 || (blk == 0 && dmask[i]);
+          s[kb][qb][i] = keep ? s[kb][qb][i] : -kInf;
+        }
+      }
+    sm_max<D, QB>(s, o, m_run, c1);
+    sm_exp_pv<T, D, QB>(s, L + C::R_VC, o, m_run, c1);
+    if (has_prev) {
+      // chunk c-1: softmax keys p > r or selected, linear keys the rest. One P holds both:
+      // 2^(a c1 - m) for softmax keys, phi(q).phi(k) 2^-m for linear keys (the shared
+      // normaliser in the running frame); the row-sum block then adds both denominators.
+      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
+      const uint32_t selw = bits_word(selprev);
+      f32x4 ls[4][QB];
+      qk_tile<T, D, QB>(L + C::R_KP, qf, s);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int fs = 0; fs < DF / 32; ++fs) {
+          const frag fa = SF::load8(L + C::R_PHIP, kb * 16 + r16, fs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+        }
+      }
+      float lmax[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lmax[qb] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool sel = (selw >> (kb * 4 + i)) & 1u;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int blk = 16 * (kb - qb) - qoff;
+            const bool sa = sel || blk > 0 || (blk == 0 && !dmask[i]);
+            s[kb][qb][i] = sa ? s[kb][qb][i] : -kInf;
+            ls[kb][qb][i] = sa ? 0.f : ls[kb][qb][i];
+            lmax[qb] = fmaxf(lmax[qb], ls[kb][qb][i]);
+          }
+        }
+      sm_max<D, QB>(s, o, m_run, c1);
+      // keep linear weights within the lazy-max bound too (2^-m times the largest weight
+      // <= 2^8); only extreme inputs (every softmax score of a query far below its linear
+      // weights) reach the rescale
+      bool lfar = false;
+      float lm[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        lm[qb] = xor_max_groups(lmax[qb]);
+        lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + 8.f);
+      }
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(lfar) != 0, 0)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float ml = __log2f(lm[qb]);
+          if (ml > m_run[qb] + 8.f) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - ml);
+#pragma unroll
+            for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha;
+            m_run[qb] = ml;
+          }
+        }
+      }
+      using TTv = Tr<T>;
+      frag one;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) one[e] = TTv::from_f(1.0f);
+      float sc2[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc2[qb] = __builtin_amdgcn_exp2f(-m_run[qb]);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        frag pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sv = s[2 * hs + e / 4][qb][e % 4], lv = ls[2 * hs + e / 4][qb][e % 4];
+            pf[qb][e] = TTv::from_f(lv * sc2[qb] + __builtin_amdgcn_exp2f(sv * c1 - m_run[qb]));
+          }
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const frag va = SV::load8(L + C::R_VP, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TTv::mma(o[db][qb], va, pf[qb]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TTv::mma(o[NB][qb], one, pf[qb]);
+      }
+    }
+  } else if (win >= 1) {
     f32x4 s[4][QB];
     uint32_t kw[QB];
     qk_tile<T, D, QB>(L + C::R_KC, qf, s);

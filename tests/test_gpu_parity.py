@@ -235,3 +235,26 @@ def test_8b_shapes_sampled(name):
     err = np.abs(got - ref).max()
     _say(wl.name, "sampled max abs err", err)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_softmax_scores_far_below_linear_weights(dt):
+    """Every query points away from every key, so all softmax scores sit tens of log2 units
+    below 0 while the NP-Map weights phi(q).phi(k) stay near |q||k|: the linear part dominates
+    the shared normaliser and the running frame must follow it (the oracle has no frame)."""
+    _say("far-scores", dt)
+    wl, (q, k, v, wp) = synth.small_case(seed=77, B=1, T=200, Hq=2, Hkv=1, D=64, F=64, window=64, chunk=64,
+                                         top_k=8, dtype=dt, qk_scale=1.0)
+    rng = np.random.default_rng(78)
+    k0 = rng.standard_normal(64).astype(np.float32)
+    k0 *= np.float32(8.0 / np.linalg.norm(k0))
+    k = np.broadcast_to(k0, k.shape).astype(np.float32) + np.float32(0.01) * rng.standard_normal(k.shape).astype(np.float32)
+    q = (-4.0 * np.broadcast_to(k0, q.shape)).astype(np.float32)
+    if dt == "bf16":
+        q, k = synth.round_bf16(q), synth.round_bf16(k)
+    out, s_gpu, idx_gpu = _run(q, k, v, wp, wl)
+    ref = O.attend(q, k, v, wp, 64, 64, 8, sel=_sel_from_idx(idx_gpu, wl.seq_len))
+    err = np.abs(out - ref).max()
+    _say("far-scores", dt, "max abs err", err)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[dt], err
