@@ -14,9 +14,10 @@ so one selection / append / fold is inside the timed window).
 
   python bench.py [--workload W] [--steps K] [--warmup W] [--no-cpu-baseline] [--calibrate-copy]
 
---calibrate-copy runs one device-to-device copy of COPY_BYTES before the steps, so that
-a rocprofv3 --pmc run of this script also records what FETCH_SIZE / WRITE_SIZE read for a
-transfer of known size (the scale applied to the attention kernel's counters).
+--calibrate-copy runs one device-to-device copy of COPY_BYTES before anything else (the
+run's first copy dispatch), so that a rocprofv3 --pmc run of this script also records what
+FETCH_SIZE / WRITE_SIZE read for a transfer of known size (the scale applied to the
+dominant kernel's counters).
 The roofline "traffic" field is read from profiles/attn_kernel_traffic.txt when that
 file was measured on the current attention-kernel source (matching SHA-1), else null.
 """
@@ -152,12 +153,6 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     sel_idx = sel.cpu().numpy()
     work = algorithmic_work(wl, sel_idx)
 
-    if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out)
     stream = torch.cuda.current_stream()
@@ -236,12 +231,6 @@ def run_decode(wl, args, torch, still, synth) -> dict:
     prefill_ms = e0.elapsed_time(e1)
     del q, k, v, out, call
     torch.cuda.empty_cache()
-    if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     # the generated tokens: step t uses [:, t]
     qs, ks, vs, _ = synth.make_inputs_device(wl, dev, seq_len=n_tok, seed_offset=1)
     toks = [(qs[:, t].contiguous(), ks[:, t].contiguous(), vs[:, t].contiguous()) for t in range(n_tok)]
@@ -322,6 +311,12 @@ def main() -> int:
 
     from linear_attention_saliency_amd import still, synth
 
+    if args.calibrate_copy:  # the run's first device-to-device copy: COPY_BYTES read and written
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = getattr(synth, WORKLOAD_NAMES[args.workload])
     decode = wl.decode_steps > 0
     if args.steps is None:
