@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         }
       m2 = xor_sum_groups(m2);
       x2 = xor_sum_groups(x2);
-      qn[qb] = sqrtf(x2) * c1 * 1.001f;  // |q| in logit units, with slack for rounding
-      const float sc = m2 > 0.f ? sqrtf(x2) / sqrtf(m2) : 0.f;
+      qn[qb] = __builtin_amdgcn_sqrtf(x2) * c1 * 1.001f;  // |q| in logit units, with slack for rounding
+      const float sc = norm_ratio(x2, m2);
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs)
 #pragma unroll

@@ -234,6 +234,12 @@ __device__ __forceinline__ uint64_t or_reduce_u64(uint64_t x) {
   return x;
 }
 
+// Norm ratio sqrt(a) / sqrt(b) with the hardware square root and reciprocal square root
+// (about 1 ulp each; the IEEE-exact library forms cost ~40 instructions), 0 if b = 0.
+__device__ __forceinline__ float norm_ratio(float a, float b) {
+  return b > 0.f ? __builtin_amdgcn_sqrtf(a) * __builtin_amdgcn_rsqf(b) : 0.f;
+}
+
 // softplus(x) = log(1 + e^x), stable for any finite x.
 __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));

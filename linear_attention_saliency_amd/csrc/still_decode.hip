@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     for (int dd = lane; dd < D; dd += 64) q2 += qs[g * D + dd] * qs[g * D + dd];
     m2 = wave_sum(m2);
     q2 = wave_sum(q2);
-    const float sc = m2 > 0.f ? sqrtf(q2) / sqrtf(m2) : 0.f;
+    const float sc = norm_ratio(q2, m2);
     for (int f = lane; f < DF; f += 64) phq[g * DF + f] *= sc;
   }
 

@@ -100,7 +100,7 @@ __device__ __forceinline__ uint64_t topk_mask(float s, int topk) {
 // rows: rows row0 .. row0+63 of a Swz<T, D> LDS tile. wf: this wave's W_h fragments from
 // np_map_load_w. Four waves; wave w owns feature blocks fb = w*FPW + fi (FPW = DF/64). On return
 // phi[kb][fi][i] = phi(row kb*16 + 4*grp + i)[feature fb*16 + r16] in fp32.
-// Scratch in LDS: m2part[4*64], xn2[64]. Contains one __syncthreads(); all 256 threads
+// Scratch in LDS: m2part[4*64], xn2[64]. Contains two __syncthreads(); all 256 threads
 // must call. After it returns no thread reads `rows` again.
 // The W_h fragments np_map_rows64 needs (B operand: feature column fb*16 + r16 of wave w's
 // feature blocks), loaded ahead of time so their latency can overlap other work.
@@ -157,13 +157,17 @@ __device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const typ
       if (r16 == 0) m2part[wave * 64 + kb * 16 + 4 * grp + i] = p;
     }
   __syncthreads();
+  // the rescale |x| / |phi(x)| of each row, once per row, left in m2part[0..63]
+  if (tid < 64) {
+    const float m2 = ((m2part[tid] + m2part[64 + tid]) + m2part[128 + tid]) + m2part[192 + tid];
+    m2part[tid] = norm_ratio(xn2[tid], m2);
+  }
+  __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = kb * 16 + 4 * grp + i;
-      const float m2 = ((m2part[row] + m2part[64 + row]) + m2part[128 + row]) + m2part[192 + row];
-      const float sc = m2 > 0.f ? sqrtf(xn2[row]) / sqrtf(m2) : 0.f;
+      const float sc = m2part[kb * 16 + 4 * grp + i];
 #pragma unroll
       for (int fi = 0; fi < FPW; ++fi) phi[kb][fi][i] *= sc;
     }
