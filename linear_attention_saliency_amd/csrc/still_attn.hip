@@ -240,6 +240,198 @@ __device__ __forceinline__ void sm_exp_pv_shifted(const f32x4 (&s)[4][QB], const
   }
 }
 
+// Window tiles when the window equals the chunk (w = 64), for a wave whose queries start at
+// QOFF within the chunk. Lane (r16, grp) holds keys kb*16 + 4 grp + i of query
+// QOFF + qb*16 + r16, so a (key block, query block) pair is of one of three kinds, known at
+// compile time: every key position below the query's (0), the diagonal (1: below where
+// 4 grp + i < r16, equal where 4 grp + i = r16) or every key position above (2).
+template <int QOFF>
+__device__ constexpr int win_kind(int kb, int qb) {
+  return 16 * (kb - qb) - QOFF < 0 ? 0 : (16 * (kb - qb) - QOFF == 0 ? 1 : 2);
+}
+
+// Chunk c: softmax keys p <= r (kinds 0 and 1; kind-2 blocks take no part).
+// Chunk c-1 (if any): softmax keys p > r or selected, linear keys the rest. One P holds both:
+// 2^(a c1 - m) for softmax keys, phi(q).phi(k) 2^-m for linear keys (the shared normaliser in
+// the running frame), and the row-sum block adds both denominators. The largest linear
+// weight is kept within the lazy-max bound too (2^-m times it <= 2^8): only extreme inputs
+// (every softmax score of a query far below its linear weights) reach that rescale.
+template <typename T, int D, int DF, int QB, int QOFF>
+__device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T* lkp, const T* lfp, const T* lvp,
+                                            bool has_prev, uint64_t selprev,
+                                            const typename Tr<T>::frag (&qf)[QB][D / 32],
+                                            const typename Tr<T>::frag (&pq)[QB][DF / 32],
+                                            f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB], float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  constexpr int NB = D / 16;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  bool dmask[4];  // key position <= query position, on a diagonal block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
+  frag one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = TT::from_f(1.0f);
+
+  // ---- chunk c
+  {
+    f32x4 s[4][QB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bool any = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) any |= win_kind<QOFF>(kb, qb) != 2;
+      if (!any) continue;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const frag ka = Swz<T, D>::load8(lkc, kb * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (win_kind<QOFF>(kb, qb) != 2) TT::mma(s[kb][qb], ka, qf[qb][ks]);
+      }
+    }
+    bool need_any = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float tm = -kInf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int kind = win_kind<QOFF>(kb, qb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kind == 1 && !dmask[i]) s[kb][qb][i] = -kInf;
+          if (kind != 2) tm = fmaxf(tm, s[kb][qb][i]);
+        }
+      }
+      tm = xor_max_groups(tm) * c1;  // finite: every query sees its own key
+      const bool need = tm > m_run[qb] + 8.f;
+      alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
+      m_run[qb] = need ? tm : m_run[qb];
+      need_any |= need;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha[qb];
+    }
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      bool live[QB], any = false;
+      frag pf[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        live[qb] = win_kind<QOFF>(2 * hs, qb) != 2 || win_kind<QOFF>(2 * hs + 1, qb) != 2;
+        any |= live[qb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kb = 2 * hs + e / 4;
+          pf[qb][e] = win_kind<QOFF>(kb, qb) == 2
+                          ? TT::from_f(0.f)
+                          : TT::from_f(__builtin_amdgcn_exp2f(s[kb][qb][e % 4] * c1 - m_run[qb]));
+        }
+      }
+      if (!any) continue;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        const frag va = Swz<T, 64>::load8(lvc, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (live[qb]) TT::mma(o[db][qb], va, pf[qb]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        if (live[qb]) TT::mma(o[NB][qb], one, pf[qb]);
+    }
+  }
+
+  // ---- chunk c-1
+  if (!has_prev) return;
+  const uint32_t selw = bits_word(selprev);
+  f32x4 s[4][QB], ls[4][QB];
+  qk_tile<T, D, QB>(lkp, qf, s);  // every block: selected keys can be anywhere
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any |= win_kind<QOFF>(kb, qb) != 2;
+    if (!any) continue;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fs = 0; fs < DF / 32; ++fs) {
+      const frag fa = Swz<T, DF>::load8(lfp, kb * 16 + r16, fs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        if (win_kind<QOFF>(kb, qb) != 2) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+    }
+  }
+  float lmax[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lmax[qb] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool sel = (selw >> (kb * 4 + i)) & 1u;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int kind = win_kind<QOFF>(kb, qb);
+        if (kind == 2) continue;  // all softmax keys
+        const bool sa = sel || (kind == 1 && !dmask[i]);
+        s[kb][qb][i] = sa ? s[kb][qb][i] : -kInf;
+        ls[kb][qb][i] = sa ? 0.f : ls[kb][qb][i];
+        lmax[qb] = fmaxf(lmax[qb], ls[kb][qb][i]);
+      }
+    }
+  sm_max<D, QB>(s, o, m_run, c1);
+  bool lfar = false;
+  float lm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    lm[qb] = xor_max_groups(lmax[qb]);
+    lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + 8.f);
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(lfar) != 0, 0)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ml = __log2f(lm[qb]);
+      if (ml > m_run[qb] + 8.f) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - ml);
+#pragma unroll
+        for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha;
+        m_run[qb] = ml;
+      }
+    }
+  }
+  float sc2[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) sc2[qb] = __builtin_amdgcn_exp2f(-m_run[qb]);
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    frag pf[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kb = 2 * hs + e / 4;
+        const float ev = __builtin_amdgcn_exp2f(s[kb][qb][e % 4] * c1 - m_run[qb]);
+        pf[qb][e] = TT::from_f(win_kind<QOFF>(kb, qb) == 2 ? ev : ls[kb][qb][e % 4] * sc2[qb] + ev);
+      }
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      const frag va = Swz<T, 64>::load8(lvp, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], one, pf[qb]);
+  }
+}
+
 template <typename T, int D, int DF, int NH>
 struct AttnCfg {
   static constexpr int QW = 32;                // queries per wave
@@ -317,7 +509,8 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   const int bhg = pi % BHG, qs = pi / BHG;
   const int gs = bhg % a.gsplit, bh = bhg / a.gsplit;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
   const int g = gs * NH + wave;
   const int qoff = qs * QW;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
@@ -347,42 +540,80 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     dv.issue(st + C::KT, vrs, t * C::VT * static_cast<int>(sizeof(T)));
   };
 
-  // ---- 0. every copy the fixed part needs, plus compact tile 0 -------------------------
+  // ---- register operands, issued ahead of the tile copies. Vector loads complete in
+  //      issue order, and every load up to phi(q) is unconditional (a range-checked
+  //      buffer load reads zeros where a condition would skip it), so the number issued
+  //      after the queries and W_h is the same on every path and phi(q) waits for those
+  //      alone while the copies are in flight ---------------------------------------------
+  // queries: B-operand fragments (SK over d); rows past the sequence end read as zeros
+  frag qf[QB][D / 32];
+  {
+    const long long q0 = t0 + qoff;  // first query row of this wave
+    const int qrow = d.Hq * D;        // elements from one position to the next
+    const long long nq = T_ - q0 < QW ? T_ - q0 : QW;
+    const auto qrs = make_rsrc(q + ((b * T_ + (nq > 0 ? q0 : 0)) * d.Hq + hq) * D,
+                               nq > 0 ? static_cast<uint32_t>(((nq - 1) * qrow + D) * static_cast<int>(sizeof(T))) : 0u);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qf[qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
+  }
+  // W_h rows fb*16 + r16 (A operand of phi(q)); held in registers only where they fit
+  const T* Wh = w + static_cast<long long>(h) * DF * D;
+  constexpr bool W_EARLY = D == 64 && DF == 64;
+  frag wq[W_EARLY ? DF / 16 : 1][D / 32];
+  if constexpr (W_EARLY) {
+#pragma unroll
+    for (int fb = 0; fb < DF / 16; ++fb)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) wq[fb][ks] = TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
+  }
+  // z of the prefix state of chunks <= c-2 (8 consecutive permuted features per lane group)
+  const float* Sg = a.states + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
+  f32x4 zr[DF / 32][2];
+  {
+    const auto zrs = make_rsrc(Sg + DF * D, c >= 2 ? DF * 4u : 0u);
+#pragma unroll
+    for (int fs = 0; fs < DF / 32; ++fs)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        zr[fs][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(zrs, (fs * 32 + grp * 8 + 4 * hf) * 4, 0, 0));
+  }
+  // the selection of chunk c-1 (0 if there is none); read out after the wait below
+  const auto selv = __builtin_amdgcn_raw_buffer_load_b64(
+      make_rsrc(a.selmask + static_cast<long long>(bh) * d.nC + (has_prev ? c - 1 : 0), has_prev ? 8u : 0u), 0, 0, 0);
+
+  // ---- 0. every copy the fixed part needs, plus compact tile 0 (a copy that is not
+  //      needed has no valid rows: it reads nothing and zero-fills its region) ----------
   {
     const int kvs = d.Hkv * D;  // row stride of k
+    const long long tp = has_prev ? t0 - kChunk : t0;  // chunk c-1 (c itself if c = 0)
+    const int cp = has_prev ? c - 1 : c;
     const T* kc = kk + ((b * T_ + t0) * d.Hkv + h) * D;
-    if (has_prev) {
-      dma_tile<T, DF, 64, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + t0 - kChunk) * DF, DF, 64);
-      dma_tile<T, 64, D, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + c - 1) * D * 64, 64, D);
-      if (win >= 1) dma_tile<T, D, 64, NH>(L + C::R_KP, kc - static_cast<long long>(kChunk) * kvs, kvs, 64);
-    }
-    if (la_cur) dma_tile<T, DF, 64, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, nvalid);
+    const T* kp = kk + ((b * T_ + tp) * d.Hkv + h) * D;
+    dma_tile<T, DF, 64, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + tp) * DF, DF, has_prev ? 64 : 0);
+    dma_tile<T, 64, D, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
+    dma_tile<T, D, 64, NH>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
+    dma_tile<T, DF, 64, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
     dma_tile<T, 64, D, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
-    if (win >= 1) dma_tile<T, D, 64, NH>(L + C::R_KC, kc, kvs, nvalid);
-    if constexpr (C::STATE_LDS) {
-      if (c >= 2)
-        dma_tile<float, DF, D, NH>(reinterpret_cast<float*>(L + C::R_ST),
-                                   a.states + (static_cast<long long>(bh) * d.nC + (c - 2)) * d.R, DF, D);
-    }
-    if (nt_comp > 0) issue(0, 0);
+    dma_tile<T, D, 64, NH>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
+    if constexpr (C::STATE_LDS)
+      dma_tile<float, DF, D, NH>(reinterpret_cast<float*>(L + C::R_ST), Sg, DF, c >= 2 ? D : 0);
+    dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
+    dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
   }
   // key-norm bounds of compact tiles 0..255 (lane l of tb[j] holds tile 64 j + l; later
   // tiles, if any, are treated as unbounded)
   float tb[4];
   {
-    const float* tmax = a.tilemax + static_cast<long long>(bh) * a.tm_stride;
+    const int ntb = nt_comp < 256 ? nt_comp : 256;
+    const auto trs = make_rsrc(a.tilemax + static_cast<long long>(bh) * a.tm_stride, static_cast<uint32_t>(ntb) * 4u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tb[j] = 64 * j + lane < nt_comp ? tmax[64 * j + lane] : kInf;
-  }
-
-  // ---- queries: B-operand fragments (SK over d) -------------------------------------
-  frag qf[QB][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const long long pos = t0 + qoff + qb * 16 + r16;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qf[qb][ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
+    for (int j = 0; j < 4; ++j) {
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, (64 * j + lane) * 4, 0, 0));
+      tb[j] = 64 * j + lane < nt_comp ? x : kInf;
+    }
   }
 
   f32x4 o[NB + 1][QB];
@@ -397,10 +628,10 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   // together with its window tile (head_dim 64; at 128 the extra live registers spill)
   const bool fast = D == 64 && win == kChunk;
   frag pq[QB][DF / 32];  // phi(q): B-operand fragments (PK over f)
+  uint64_t selprev;
   // =============================== phase 1: linear attention ===========================
   {
     // phi(q) = |q| m / |m|, m = elu(W_h q) + 1
-    const T* Wh = w + static_cast<long long>(h) * DF * D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x4 pacc[DF / 16];
@@ -408,8 +639,14 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
       for (int fb = 0; fb < DF / 16; ++fb) {
         pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-          TT::mma(pacc[fb], TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8), qf[qb][ks]);
+        for (int ks = 0; ks < D / 32; ++ks) {
+          frag wa;
+          if constexpr (W_EARLY)
+            wa = wq[fb][ks];
+          else
+            wa = TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
+          TT::mma(pacc[fb], wa, qf[qb][ks]);
+        }
       }
       float m2 = 0.f, x2 = 0.f;
 #pragma unroll
@@ -438,22 +675,13 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) pq[qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
     }
 
-    float den[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) den[qb] = 0.f;
-    // z of the prefix state (8 consecutive permuted features per lane group)
-    f32x4 zr[DF / 32][2];
-    const float* Sg = a.states + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
-    if (c >= 2) {
-#pragma unroll
-      for (int fs = 0; fs < DF / 32; ++fs) {
-        zr[fs][0] = *reinterpret_cast<const f32x4*>(Sg + DF * D + fs * 32 + grp * 8);
-        zr[fs][1] = *reinterpret_cast<const f32x4*>(Sg + DF * D + fs * 32 + grp * 8 + 4);
-      }
-    }
-
+    // phi(q) is done before the wait below (it overlaps the copies); keep the scheduler
+    // from moving it past the wait
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // every region copied at the start has landed
+    selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
+              static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
 
     // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)] (fp32): each A-operand
     // fragment (row d, the 8 features a lane group holds) is 8 consecutive floats
@@ -473,17 +701,18 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
         }
+        // the denominator phi(q).z on the row-sum block: every row of its A operand is z,
+        // so each of its entries ends up holding the whole dot product
+        const frag za = frag_of<T>(Tr<float>::join(zr[fs][0], zr[fs][1]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float zf = zr[fs][e / 4][e % 4];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) den[qb] += TT::to_f(pq[qb][fs][e]) * zf;
-        }
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], za, pq[qb][fs]);
       }
     }
     // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w);
     // the fast path takes chunk c-1's with its window tile (chunk c has none when w = 64)
-    const uint64_t selprev = has_prev ? a.selmask[static_cast<long long>(bh) * d.nC + c - 1] : 0ull;
+    frag ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = TT::from_f(1.0f);
 #pragma unroll
     for (int cur = 0; cur < 2; ++cur) {
       if (fast || (cur == 0 ? !has_prev : !la_cur)) continue;  // uniform
@@ -512,9 +741,7 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = (lw & (1u << (kb * 4 + i))) ? ls[kb][qb][i] : 0.f;
-            pv[kb][i] = x;
-            den[qb] += x;
+            pv[kb][i] = (lw & (1u << (kb * 4 + i))) ? ls[kb][qb][i] : 0.f;
           }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -529,12 +756,16 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[ks][qb]);
         }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], ones, pf[ks][qb]);  // their denominator
     }
     // the linear branch becomes one online-softmax entry: log-weight log2(D), value N / D
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float dt = xor_sum_groups(den[qb]);
-      const float inv = dt > 0.f ? 1.f / dt : 0.f;
+      const float dt = o[NB][qb][0];
+      const float inv = dt > 0.f ? __builtin_amdgcn_rcpf(dt) : 0.f;
 #pragma unroll
       for (int db = 0; db < NB; ++db) o[db][qb] *= inv;
       m_run[qb] = dt > 0.f ? __log2f(dt) : -kInf;
@@ -546,115 +777,12 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   // =============================== phase 2: softmax tiles ==============================
   // 2a. the window: chunk c (r - w < p <= r), chunk c-1 (p > r + 64 - w, or selected)
   if (fast) {
-    // Masks by block: lane (r16, grp) holds keys kb*16 + 4 grp + i of query qoff + qb*16 + r16,
-    // so for key block kb and query block qb (blk = 16 (kb - qb) - qoff, uniform) key <= query
-    // holds for all lanes if blk < 0, for none if blk > 0, and where 4 grp + i <= r16 if
-    // blk = 0 (four lane masks shared by every diagonal block).
-    bool dmask[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
-    f32x4 s[4][QB];
-    // chunk c: softmax keys p <= r
-    qk_tile<T, D, QB>(L + C::R_KC, qf, s);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int blk = 16 * (kb - qb) - qoff;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool keep = blk < 0 || (blk == 0 && dmask[i]);
-          s[kb][qb][i] = keep ? s[kb][qb][i] : -kInf;
-        }
-      }
-    sm_max<D, QB>(s, o, m_run, c1);
-    sm_exp_pv<T, D, QB>(s, L + C::R_VC, o, m_run, c1);
-    if (has_prev) {
-      // chunk c-1: softmax keys p > r or selected, linear keys the rest. One P holds both:
-      // 2^(a c1 - m) for softmax keys, phi(q).phi(k) 2^-m for linear keys (the shared
-      // normaliser in the running frame); the row-sum block then adds both denominators.
-      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
-      const uint32_t selw = bits_word(selprev);
-      f32x4 ls[4][QB];
-      qk_tile<T, D, QB>(L + C::R_KP, qf, s);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int fs = 0; fs < DF / 32; ++fs) {
-          const frag fa = SF::load8(L + C::R_PHIP, kb * 16 + r16, fs * 32 + grp * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
-        }
-      }
-      float lmax[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) lmax[qb] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool sel = (selw >> (kb * 4 + i)) & 1u;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int blk = 16 * (kb - qb) - qoff;
-            const bool sa = sel || blk > 0 || (blk == 0 && !dmask[i]);
-            s[kb][qb][i] = sa ? s[kb][qb][i] : -kInf;
-            ls[kb][qb][i] = sa ? 0.f : ls[kb][qb][i];
-            lmax[qb] = fmaxf(lmax[qb], ls[kb][qb][i]);
-          }
-        }
-      sm_max<D, QB>(s, o, m_run, c1);
-      // keep linear weights within the lazy-max bound too (2^-m times the largest weight
-      // <= 2^8); only extreme inputs (every softmax score of a query far below its linear
-      // weights) reach the rescale
-      bool lfar = false;
-      float lm[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        lm[qb] = xor_max_groups(lmax[qb]);
-        lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + 8.f);
-      }
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(lfar) != 0, 0)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float ml = __log2f(lm[qb]);
-          if (ml > m_run[qb] + 8.f) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - ml);
-#pragma unroll
-            for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha;
-            m_run[qb] = ml;
-          }
-        }
-      }
-      using TTv = Tr<T>;
-      frag one;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) one[e] = TTv::from_f(1.0f);
-      float sc2[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc2[qb] = __builtin_amdgcn_exp2f(-m_run[qb]);
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        frag pf[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float sv = s[2 * hs + e / 4][qb][e % 4], lv = ls[2 * hs + e / 4][qb][e % 4];
-            pf[qb][e] = TTv::from_f(lv * sc2[qb] + __builtin_amdgcn_exp2f(sv * c1 - m_run[qb]));
-          }
-#pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          const frag va = SV::load8(L + C::R_VP, db * 16 + r16, hs * 32 + grp * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TTv::mma(o[db][qb], va, pf[qb]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TTv::mma(o[NB][qb], one, pf[qb]);
-      }
-    }
+    if (qoff == 0)
+      window_fast<T, D, DF, QB, 0>(L + C::R_KC, L + C::R_VC, L + C::R_KP, L + C::R_PHIP, L + C::R_VP, has_prev, selprev,
+                                   qf, pq, o, m_run, c1);
+    else
+      window_fast<T, D, DF, QB, QW>(L + C::R_KC, L + C::R_VC, L + C::R_KP, L + C::R_PHIP, L + C::R_VP, has_prev,
+                                    selprev, qf, pq, o, m_run, c1);
   } else if (win >= 1) {
     f32x4 s[4][QB];
     uint32_t kw[QB];
@@ -668,7 +796,6 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     sm_max<D, QB>(s, o, m_run, c1);
     sm_exp_pv<T, D, QB>(s, L + C::R_VC, o, m_run, c1);
     if (has_prev) {
-      const uint64_t selprev = a.selmask[static_cast<long long>(bh) * d.nC + c - 1];
       const uint32_t selw = bits_word(selprev);
       qk_tile<T, D, QB>(L + C::R_KP, qf, s);
 #pragma unroll
