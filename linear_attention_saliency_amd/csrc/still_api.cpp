@@ -34,6 +34,9 @@ int check_cfg(const still_config* c, bool use_seq) {
     const int64_t nw = g < 4 ? g : 4;
     const int64_t gsplit = (g + nw - 1) / nw;
     if (n_chunks * c->batch * c->n_kv_heads * gsplit * 2 > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
+    // the chunk states of one (b, h) are addressed with 32-bit byte offsets
+    const int64_t rec = static_cast<int64_t>(c->head_dim) * c->feat_dim + c->feat_dim;
+    if (n_chunks * rec * 4 > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
   }
   return STILL_OK;
 }

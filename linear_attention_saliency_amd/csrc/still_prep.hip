@@ -256,16 +256,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // Inclusive prefix sum of the chunk records over the complete chunks, in place.
-// One thread per record element. The chain of adds is serial but the loads are not: a
-// thread keeps 64 chunk loads in flight, so a sequence of n chunks costs about n / 64
-// memory round trips. The last block column instead reduces the per-chunk selected-key
-// norms to one bound per compact tile (tile t holds compact rows 64t .. 64t+63, i.e.
-// chunks 64t/topk .. (64t+63)/topk).
-__global__ __launch_bounds__(64) void scan_kernel(float* states, int nC, int nCc, int R, const float* kmaxc,
-                                                  float* tilemax, int tm_stride, int topk) {
+// A workgroup takes 64 record elements (one per lane) of one (b, h) and 8 waves; a round
+// covers 8 x 32 chunks, wave w the 32 chunks from 32 w on: each lane loads its 32 values at
+// once (one memory round trip per round), scans them in registers, and adds the totals of
+// the earlier segments (through LDS) and of the earlier rounds (a running carry). The last
+// block column instead reduces the per-chunk selected-key norms to one bound per compact
+// tile (tile t holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
+constexpr int kScanWaves = 8, kScanSeg = 32;
+__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(float* states, int nC, int nCc, int R,
+                                                               const float* kmaxc, float* tilemax, int tm_stride,
+                                                               int topk) {
+  const long long bh = blockIdx.y;
   if (tm_stride > 0 && static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - 1) {
-    const long long bh = blockIdx.y;
-    for (int t = threadIdx.x; t < tm_stride; t += 64) {
+    for (int t = threadIdx.x; t < tm_stride; t += 64 * kScanWaves) {
       const int c0 = 64 * t / topk;
       const int c1 = min((64 * t + 63) / topk, nCc - 1);
       float mx = 0.f;
@@ -274,21 +277,39 @@ __global__ __launch_bounds__(64) void scan_kernel(float* states, int nC, int nCc
     }
     return;
   }
-  constexpr int NF = 64;  // loads in flight per thread
-  const int e = blockIdx.x * 64 + threadIdx.x;
-  if (e >= R) return;
-  float* p = states + static_cast<long long>(blockIdx.y) * nC * R + e;
-  float acc = 0.f;
-  for (int c0 = 0; c0 < nCc; c0 += NF) {
-    float x[NF];
+  __shared__ float tot[2][kScanWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int e = blockIdx.x * 64 + lane;
+  const bool ok = e < R;
+  // the complete chunks' records of this (b, h): reads past them give zeros, writes past
+  // them are dropped; lanes past the record (e >= R) read but never write
+  const auto rs = make_rsrc(states + bh * nC * R, static_cast<uint32_t>(nCc) * static_cast<uint32_t>(R) * 4u);
+  float carry = 0.f;
+  int par = 0;
+  for (int r0 = 0; r0 < nCc; r0 += kScanWaves * kScanSeg, par ^= 1) {
+    const int c0 = r0 + wave * kScanSeg;  // this wave's first chunk
+    float x[kScanSeg];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) x[j] = c0 + j < nCc ? p[static_cast<long long>(c0 + j) * R] : 0.f;
+    for (int j = 0; j < kScanSeg; ++j)
+      x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((c0 + j) * R + e) * 4, 0, 0));
 #pragma unroll
-    for (int j = 0; j < NF; ++j)
-      if (c0 + j < nCc) {
-        acc += x[j];
-        p[static_cast<long long>(c0 + j) * R] = acc;
-      }
+    for (int j = 1; j < kScanSeg; ++j) x[j] += x[j - 1];
+    tot[par][wave][lane] = x[kScanSeg - 1];
+    __syncthreads();
+    float before = carry, all = carry;
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) {
+      const float t = tot[par][w][lane];
+      before += w < wave ? t : 0.f;
+      all += t;
+    }
+    carry = all;
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < kScanSeg; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x[j] + before), rs, ((c0 + j) * R + e) * 4, 0, 0);
+    }
   }
 }
 
@@ -392,7 +413,7 @@ hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* 
   if (d.nCc == 0) return hipSuccess;
   const bool tiles = d.topk > 0 && tm_stride > 0;
   dim3 grid((d.R + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
-  hipLaunchKernelGGL(scan_kernel, grid, dim3(64), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
                      tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
   return hipGetLastError();
 }
