@@ -19,9 +19,11 @@
 // shared-normaliser output  (sum_SA e^a v + N) / (sum_SA e^a + D)  needs no offset and
 // cannot overflow whatever the magnitudes.
 // Phase 2 (softmax): the two window tiles (masked), then the compact tiles, 64 keys per
-// tile, in a three-stage LDS pipeline whose copies run straight from memory into LDS. The
-// running max is refreshed only when a tile's max exceeds it by more than 8 (log2 units);
-// a per-tile bound |q| max|k| skips even the max pass when it cannot move.
+// tile, in a four-stage LDS pipeline whose copies run straight from memory into LDS. The
+// running max is refreshed only when a tile's max exceeds it by more than kLazy = 32 (log2
+// units): P and the accumulators keep fp32's exponent range (bf16 has it too), so terms up
+// to 2^32 stay exact in relative terms and every sum stays finite. A per-tile bound
+// |q| max|k| skips even the max pass when the max cannot move that far.
 //
 // Every tile the fixed part needs (phi(K) and V of chunk c-1, K and V of the window, the
 // prefix state) is copied into its own LDS region at the start, together with the first
@@ -38,6 +40,10 @@
 #include "still_route.hpp"
 
 namespace still {
+
+// lazy running max: rescale only when a score exceeds the running max by more than this
+// (log2 units)
+constexpr float kLazy = 32.f;
 
 template <typename T> __device__ __forceinline__ typename Tr<T>::frag ones_frag() {
   typename Tr<T>::frag x;
@@ -99,7 +105,7 @@ __device__ __forceinline__ void mask_tile(f32x4 (&s)[4][QB], const uint32_t (&kw
 }
 
 // Running-max update for a tile: the max is refreshed only when the tile's max exceeds it
-// by more than 8 (log2 units); the accumulators (row-sum block included) are rescaled
+// by more than kLazy (log2 units); the accumulators (row-sum block included) are rescaled
 // then, which is rare after the first tiles.
 template <int D, int QB>
 __device__ __forceinline__ void sm_max(const f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB],
@@ -113,7 +119,7 @@ __device__ __forceinline__ void sm_max(const f32x4 (&s)[4][QB], f32x4 (&o)[D / 1
     tm = fmaxf(tm, fmaxf(fmaxf(fmaxf(s[2][qb][0], s[2][qb][1]), fmaxf(s[2][qb][2], s[2][qb][3])),
                          fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), fmaxf(s[3][qb][2], s[3][qb][3]))));
     tm = xor_max_groups(tm) * c1;
-    const bool need = tm > m_run[qb] + 8.f;
+    const bool need = tm > m_run[qb] + kLazy;
     alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
     m_run[qb] = need ? tm : m_run[qb];
     need_any |= need;
@@ -179,8 +185,8 @@ __device__ __forceinline__ void qk_tile_shifted(const T* lk, const typename Tr<T
   }
 }
 
-// Running-max update for shifted scores: a column moves only if its tile max exceeds 8
-// (2^8 is the largest P the accumulators then see); the accumulators are rescaled, the
+// Running-max update for shifted scores: a column moves only if its tile max exceeds kLazy
+// (2^kLazy is the largest P the accumulators then see); the accumulators are rescaled, the
 // tile's scores and the column's -m re-based. Rare after the first tiles.
 template <int D, int QB>
 __device__ __forceinline__ void sm_max_shifted(f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB],
@@ -195,7 +201,7 @@ __device__ __forceinline__ void sm_max_shifted(f32x4 (&s)[4][QB], f32x4 (&o)[D /
 #pragma unroll
       for (int i = 0; i < 4; ++i) tm = fmaxf(tm, s[kb][qb][i]);
     tm = xor_max_groups(tm);
-    const bool need = tm > 8.f;
+    const bool need = tm > kLazy;
     dm[qb] = need ? tm : 0.f;
     need_any |= need;
   }
@@ -254,7 +260,7 @@ __device__ constexpr int win_kind(int kb, int qb) {
 // Chunk c-1 (if any): softmax keys p > r or selected, linear keys the rest. One P holds both:
 // 2^(a c1 - m) for softmax keys, phi(q).phi(k) 2^-m for linear keys (the shared normaliser in
 // the running frame), and the row-sum block adds both denominators. The largest linear
-// weight is kept within the lazy-max bound too (2^-m times it <= 2^8): only extreme inputs
+// weight is kept within the lazy-max bound too (2^-m times it <= 2^kLazy): only extreme inputs
 // (every softmax score of a query far below its linear weights) reach that rescale.
 template <typename T, int D, int DF, int QB, int QOFF>
 __device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T* lkp, const T* lfp, const T* lvp,
@@ -307,7 +313,7 @@ __device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T*
         }
       }
       tm = xor_max_groups(tm) * c1;  // finite: every query sees its own key
-      const bool need = tm > m_run[qb] + 8.f;
+      const bool need = tm > m_run[qb] + kLazy;
       alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
       m_run[qb] = need ? tm : m_run[qb];
       need_any |= need;
@@ -393,13 +399,13 @@ __device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T*
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     lm[qb] = xor_max_groups(lmax[qb]);
-    lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + 8.f);
+    lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + kLazy);
   }
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(lfar) != 0, 0)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float ml = __log2f(lm[qb]);
-      if (ml > m_run[qb] + 8.f) {
+      if (ml > m_run[qb] + kLazy) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - ml);
 #pragma unroll
         for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha;
@@ -822,6 +828,23 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     f32x4 mneg[QB];  // -m per query column, the starting accumulator of K Q^T
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mneg[qb] = f32x4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
+    // Tiles whose key-norm bound might move the running max, one bit each: the max can only
+    // move if some query's |q| max|k| exceeds it by more than kLazy. Decided here for all
+    // tiles at once, conservatively (the wave's largest |q| against its smallest running max,
+    // which only grows), so a step tests one scalar bit; tiles from 256 on are always checked.
+    uint64_t mayfar[4];
+    {
+      float qmax = qn[0], mmin = m_run[0];
+#pragma unroll
+      for (int qb = 1; qb < QB; ++qb) {
+        qmax = fmaxf(qmax, qn[qb]);
+        mmin = fminf(mmin, m_run[qb]);
+      }
+      qmax = wave_max64(qmax);
+      mmin = -wave_max64(-mmin);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mayfar[j] = __builtin_amdgcn_ballot_w64(qmax * tb[j] > mmin + kLazy);
+    }
     f32x4 sa[4][QB], sb[4][QB];
     qk_tile_shifted<T, D, QB>(L + C::stage_off(0), qf, mneg, sa);  // tile 0 landed before phase 1
     __syncthreads();
@@ -843,19 +866,9 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
         mask_tile<QB>(s_cur, kw);
       }
-      // the running max can only move if some query's bound |q| kmax exceeds it by more
-      // than the lazy threshold; otherwise the max pass would leave everything unchanged
-      const int tj = t >> 6, tl = t & 63;
-      const int k0 = __builtin_amdgcn_readlane(__float_as_int(tb[0]), tl);
-      const int k1 = __builtin_amdgcn_readlane(__float_as_int(tb[1]), tl);
-      const int k2 = __builtin_amdgcn_readlane(__float_as_int(tb[2]), tl);
-      const int k3 = __builtin_amdgcn_readlane(__float_as_int(tb[3]), tl);
-      const int kbits = tj == 0 ? k0 : tj == 1 ? k1 : tj == 2 ? k2 : tj == 3 ? k3 : __float_as_int(kInf);
-      const float kt = __int_as_float(kbits);
-      bool far = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) far |= qn[qb] * kt > m_run[qb] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(far) != 0) sm_max_shifted<D, QB>(s_cur, o, m_run, mneg);
+      const int tj = t >> 6;
+      const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
+      if ((fw >> (t & 63)) & 1ull) sm_max_shifted<D, QB>(s_cur, o, m_run, mneg);
       qk_tile_shifted<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, mneg, s_next);  // after the last tile: unused
       sm_exp_pv_shifted<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o);
     };
