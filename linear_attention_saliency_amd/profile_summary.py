@@ -41,6 +41,8 @@ def trace(path: str, last_n: int) -> str:
             per[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     lines = [f"| kernel | dispatches | mean us over the last {last_n} | min us | max us |", "|---|---|---|---|---|"]
     for k, v in sorted(per.items(), key=lambda kv: -sum(x for _, x in kv[1])):
+        if len(v) < last_n:  # launched only outside the timed window (set-up)
+            continue
         xs = [x for _, x in sorted(v)][-last_n:]
         lines.append(f"| {k.split('(')[0][:70]} | {len(v)} | {sum(xs) / len(xs):.1f} | {min(xs):.1f} | {max(xs):.1f} |")
     return "\n".join(lines)
