@@ -168,8 +168,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       }
 
   // 6. V of the chunk (loaded at the start; zero past the sequence end): stage in LDS over
-  //    the band once the gather is done with it, write the transposed, key-permuted copy vT,
-  //    and the compact transposed copy of the selected rows
+  //    band rows 0..63 once the gather is done with the band, transpose it into band rows
+  //    64..127 as V^T [d][64] (a Swz<T, 64> tile, keys permuted: position 8*pb + e holds
+  //    key 32*(pb/4) + 16*(e/4) + 4*(pb%4) + e%4, the order MFMA operands take), then write
+  //    that tile out as vT and the compact transposed copy of the selected rows
+  using SV = Swz<T, 64>;
+  T* vtl = band + 64 * D;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -177,18 +181,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     SW::store8(band, idx / V8, (idx % V8) * 8, vpre[i]);
   }
   __syncthreads();
+  for (int idx = tid; idx < D * 8; idx += 256) {
+    const int dd = idx / 8, pb = idx % 8;  // positions 8*pb .. 8*pb+7 of row dd
+    frag x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = band[SW::off(32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4), dd)];
+    SV::store8(vtl, dd, pb * 8, x);
+  }
+  __syncthreads();
   {
     T* vt = static_cast<T*>(a.vT) + (static_cast<long long>(bh) * d.nC + c) * D * 64;
     for (int idx = tid; idx < D * 8; idx += 256) {
-      const int dd = idx / 8, pb = idx % 8;  // output positions 8*pb .. 8*pb+7 of row dd
-      frag x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // position 8*pb + e holds key 32*(pb/4) + 16*(e/4) + 4*(pb%4) + e%4
-        const int key = 32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4);
-        x[e] = band[SW::off(key, dd)];
-      }
-      TT::store8(vt + dd * 64 + pb * 8, x);
+      const int dd = idx / 8, pb = idx % 8;
+      TT::store8(vt + dd * 64 + pb * 8, SV::load8(vtl, dd, pb * 8));
     }
     if (complete && d.topk > 0) {
       T* vs = static_cast<T*>(a.vselT) + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
@@ -230,9 +235,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int e = 0; e < 8; ++e) pa[fi][e] = TT::from_f(phi[2 * ks + e / 4][fi][e % 4]);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      frag vb;  // B operand: column d, the same keys
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vb[e] = band[SW::off(ks * 32 + 16 * (e / 4) + 4 * grp + (e % 4), db * 16 + r16)];
+      // B operand: column d, the same keys (keys ks*32 + 16*(e/4) + 4*grp + e%4 sit at
+      // positions ks*32 + 8*grp + e of the permuted V^T tile)
+      const frag vb = SV::load8(vtl, db * 16 + r16, ks * 32 + grp * 8);
 #pragma unroll
       for (int fi = 0; fi < FPW; ++fi) TT::mma(u[fi][db], pa[fi], vb);
     }

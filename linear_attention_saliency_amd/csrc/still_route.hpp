@@ -120,13 +120,22 @@ __device__ __forceinline__ void np_map_rows64(const T* rows, int row0, const typ
                                               float* m2part, float* xn2, f32x4 (&phi)[4][DF / 64]) {
   constexpr int FPW = DF / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
-  if (tid < 64) {
+  {
+    // |x|^2 of each row: four lanes per row, D/4 elements each, then a sum over the four
+    const int row = tid >> 2, part = tid & 3;
     float s = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float x = Tr<T>::to_f(rows[Swz<T, D>::off(row0 + tid, d)]);
-      s += x * x;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const auto x = Swz<T, D>::load8(rows, row0 + row, part * (D / 4) + j * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = Tr<T>::to_f(x[e]);
+        s += v * v;
+      }
     }
-    xn2[tid] = s;
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) xn2[row] = s;
   }
 #pragma unroll
   for (int fi = 0; fi < FPW; ++fi) {
