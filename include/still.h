@@ -68,9 +68,9 @@ enum {
 /* Layer configuration. Supported by the kernels: chunk = 64; head_dim in {64, 128};
  * feat_dim in {64, 128}; 0 <= window <= chunk; 0 <= top_k <= chunk; top_k = 0 when
  * window = 0; n_q_heads a multiple of n_kv_heads; seq_len >= 1, with the chunk states of
- * one (batch, KV head), ceil(seq_len/64) * (head_dim*feat_dim + feat_dim) * 4 bytes, under
- * 2 GiB (about 8M tokens at 64/64, 2M at 128/128). STILL_F32 is supported with
- * head_dim = feat_dim = 64 (the reference-precision path). */
+ * one (batch, KV head), ceil(seq_len/64) * (head_dim*feat_dim + feat_dim) elements of the
+ * layer's dtype, under 2 GiB (about 16M tokens at 64/64 and 4M at 128/128 in bf16).
+ * STILL_F32 is supported with head_dim = feat_dim = 64 (the reference-precision path). */
 typedef struct still_config {
   int32_t batch;
   int32_t seq_len;

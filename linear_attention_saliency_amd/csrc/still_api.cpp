@@ -36,7 +36,7 @@ int check_cfg(const still_config* c, bool use_seq) {
     if (n_chunks * c->batch * c->n_kv_heads * gsplit * 2 > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
     // the chunk states of one (b, h) are addressed with 32-bit byte offsets
     const int64_t rec = static_cast<int64_t>(c->head_dim) * c->feat_dim + c->feat_dim;
-    if (n_chunks * rec * 4 > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
+    if (n_chunks * rec * (c->dtype == STILL_BF16 ? 2 : 4) > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
   }
   return STILL_OK;
 }
@@ -84,7 +84,7 @@ WsLayout ws_layout(const still_config* c) {
   L.vselT = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vT = take(bh * d.nC * 64 * d.D * es);
   L.phik = take(bh * d.T * d.DF * es);
-  L.states = take(bh * d.nC * d.R * sizeof(float));
+  L.states = take(bh * d.nC * d.R * (d.bf16 ? 2 : 4));
   L.kmaxc = take(bh * d.nC * sizeof(float));
   L.tilemax = take(bh * (L.ntiles_sel > 0 ? L.ntiles_sel : 1) * sizeof(float));
   L.total = off;
@@ -215,7 +215,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.sel_idx = sel_idx_out;
   pa.ksel = ws + L.ksel;
   pa.phik = ws + L.phik;
-  pa.states = reinterpret_cast<float*>(ws + L.states);
+  pa.states = ws + L.states;
   pa.vT = ws + L.vT;
   pa.vselT = ws + L.vselT;
   pa.ntiles_sel = L.ntiles_sel;

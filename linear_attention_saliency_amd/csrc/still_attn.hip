@@ -446,9 +446,9 @@ struct AttnCfg {
   static constexpr int NTHR = 64 * NH;         // threads per workgroup: one wave per head
   static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
   static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
-  // the prefix state goes through LDS when it is small (fp32 S^T [D][DF])
+  // the prefix state goes through LDS when it is small (S^T [D][DF] in the layer's dtype)
   static constexpr bool STATE_LDS = D == 64 && DF == 64;
-  static constexpr int ST = STATE_LDS ? D * DF * 4 / static_cast<int>(sizeof(T)) : 0;
+  static constexpr int ST = STATE_LDS ? D * DF : 0;
   // LDS regions of the fixed part (element offsets); compact stages 1 and 2 reuse them
   static constexpr int R_PHIP = 0, R_PHIC = FT, R_VP = 2 * FT, R_VC = 2 * FT + VT;
   static constexpr int R_KC = 2 * FT + 2 * VT, R_KP = R_KC + KT, R_ST = R_KP + KT;
@@ -489,7 +489,6 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   using SK = Swz<T, D>;    // K tile: 64 keys x D
   using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF
   using SV = Swz<T, 64>;   // V^T tile: D rows x 64 keys
-  using SS = Swz<float, DF>;  // prefix state S^T: D rows x DF (fp32)
   constexpr int NB = D / 16;  // output blocks; block NB holds the row sums
   using TT = Tr<T>;
   using frag = typename TT::frag;
@@ -575,16 +574,14 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) wq[fb][ks] = TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
   }
-  // z of the prefix state of chunks <= c-2 (8 consecutive permuted features per lane group)
-  const float* Sg = a.states + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
-  f32x4 zr[DF / 32][2];
+  // z of the prefix state of chunks <= c-2 (8 consecutive permuted features per lane group):
+  // the A operand of the denominator, the same in every row
+  const T* Sg = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
+  frag zf[DF / 32];
   {
-    const auto zrs = make_rsrc(Sg + DF * D, c >= 2 ? DF * 4u : 0u);
+    const auto zrs = make_rsrc(Sg + DF * D, c >= 2 ? DF * static_cast<uint32_t>(sizeof(T)) : 0u);
 #pragma unroll
-    for (int fs = 0; fs < DF / 32; ++fs)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        zr[fs][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(zrs, (fs * 32 + grp * 8 + 4 * hf) * 4, 0, 0));
+    for (int fs = 0; fs < DF / 32; ++fs) zf[fs] = TT::bload8(zrs, (fs * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
   }
   // the selection of chunk c-1 (0 if there is none); read out after the wait below
   const auto selv = __builtin_amdgcn_raw_buffer_load_b64(
@@ -605,7 +602,7 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     dma_tile<T, 64, D, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
     dma_tile<T, D, 64, NH>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
-      dma_tile<float, DF, D, NH>(reinterpret_cast<float*>(L + C::R_ST), Sg, DF, c >= 2 ? D : 0);
+      dma_tile<T, DF, D, NH>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
     dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
     dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
   }
@@ -689,29 +686,25 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
 
-    // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)] (fp32): each A-operand
-    // fragment (row d, the 8 features a lane group holds) is 8 consecutive floats
+    // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)]: each A-operand fragment
+    // (row d, the 8 features a lane group holds) is 8 consecutive elements
     if (c >= 2) {
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs) {
 #pragma unroll
         for (int db = 0; db < NB; ++db) {
-          f32x8 sx;
-          if constexpr (C::STATE_LDS) {
-            sx = SS::load8(reinterpret_cast<const float*>(L + C::R_ST), db * 16 + r16, fs * 32 + grp * 8);
-          } else {
-            const float* src = Sg + (db * 16 + r16) * DF + fs * 32 + grp * 8;
-            sx = Tr<float>::join(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4));
-          }
-          const frag sa = frag_of<T>(sx);
+          frag sa;
+          if constexpr (C::STATE_LDS)
+            sa = SF::load8(L + C::R_ST, db * 16 + r16, fs * 32 + grp * 8);
+          else
+            sa = TT::load8(Sg + (db * 16 + r16) * DF + fs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
         }
         // the denominator phi(q).z on the row-sum block: every row of its A operand is z,
         // so each of its entries ends up holding the whole dot product
-        const frag za = frag_of<T>(Tr<float>::join(zr[fs][0], zr[fs][1]));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], za, pq[qb][fs]);
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], zf[fs], pq[qb][fs]);
       }
     }
     // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w);

@@ -509,14 +509,14 @@ __global__ __launch_bounds__(256) void cache_export_kernel(ExportArgs a) {
   if (tid < 64)
     a.c.cur_sal[bh * 64 + tid] = (d.window >= 1 && tid < rT) ? a.sal[static_cast<long long>(bh) * T_ + cT * 64 + tid] : 0.f;
   // the prefill's records hold S^T[d][pk_pos(f)] and z[pk_pos(f)]; the cache holds S[f][d], z[f]
-  const float* src = a.states + (static_cast<long long>(bh) * d.nC + (cT >= 2 ? cT - 2 : 0)) * d.R;
+  const T* src = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (cT >= 2 ? cT - 2 : 0)) * d.R;
   for (int idx = tid; idx < d.R; idx += 256) {
     if (idx < d.DF * D) {
       const int f = idx / D, dd = idx % D;
-      a.c.state_s[static_cast<long long>(bh) * d.DF * D + idx] = cT >= 2 ? src[dd * d.DF + pk_pos(f)] : 0.f;
+      a.c.state_s[static_cast<long long>(bh) * d.DF * D + idx] = cT >= 2 ? TT::to_f(src[dd * d.DF + pk_pos(f)]) : 0.f;
     } else {
       const int f = idx - d.DF * D;
-      a.c.state_z[static_cast<long long>(bh) * d.DF + f] = cT >= 2 ? src[d.DF * D + pk_pos(f)] : 0.f;
+      a.c.state_z[static_cast<long long>(bh) * d.DF + f] = cT >= 2 ? TT::to_f(src[d.DF * D + pk_pos(f)]) : 0.f;
     }
   }
 }

@@ -10,7 +10,7 @@ struct Dims {
   int B, T, Hq, Hkv, G, D, DF, window, topk;
   int nC;   // number of chunks, ceil(T / 64)
   int nCc;  // number of complete chunks, T / 64
-  int R;    // floats per chunk state record: DF*D (S) + DF (z)
+  int R;    // elements per chunk state record: DF*D (S) + DF (z)
   int bf16; // 1 = bf16 tensors, 0 = fp32
 };
 
@@ -26,7 +26,8 @@ struct PrepArgs {
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
   void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows times log2(e)/sqrt(D)
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
-  float* states;              // [B,Hkv,nC,R]: S^T [D][DF] with features permuted by pk_pos, then z [DF] permuted
+  void* states;               // [B,Hkv,nC,R] in the layer's dtype: S^T [D][DF] with features permuted by
+                              // pk_pos, then z [DF] permuted
   void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos
   void* vselT;                // [B,Hkv,ntiles_sel,D,64]: compact V rows, same tile layout
   int ntiles_sel;             // compact tiles per (b, KV head): >= ceil(nCc*topk / 64)
@@ -43,7 +44,7 @@ struct AttnArgs {
   const void* vselT;
   const void* vT;
   const void* phik;
-  const float* states;  // inclusive prefix over complete chunks
+  const void* states;   // inclusive prefix over complete chunks (layer dtype)
   void* out;
   int ntiles_sel;
   const float* tilemax; // [B,Hkv,tm_stride]: largest |k| in each compact tile
@@ -73,7 +74,7 @@ struct ExportArgs {
   const void* v;
   const float* sal;        // [B,Hkv,T] group-summed saliency (unused if window = 0)
   const uint64_t* selmask; // [B,Hkv,nC]
-  const float* states;     // [B,Hkv,nC,R] inclusive prefix over complete chunks
+  const void* states;      // [B,Hkv,nC,R] inclusive prefix over complete chunks (layer dtype)
   CacheView c;
 };
 
@@ -95,7 +96,7 @@ struct DecodeArgs {
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 // prefix sums of the chunk records, and the per-tile key-norm bound from kmaxc
-hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* tilemax, int tm_stride,
+hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* tilemax, int tm_stride,
                        hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* sal, int32_t* sel_idx, hipStream_t s);

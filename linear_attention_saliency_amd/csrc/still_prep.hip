@@ -242,35 +242,63 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int fi = 0; fi < FPW; ++fi) TT::mma(u[fi][db], pa[fi], vb);
     }
   }
-  float* st = a.states + (static_cast<long long>(bh) * d.nC + c) * d.R;
+  T* st = static_cast<T*>(a.states) + (static_cast<long long>(bh) * d.nC + c) * d.R;
 #pragma unroll
   for (int fi = 0; fi < FPW; ++fi) {
     const int fb = wave * FPW + fi;
     // features fb*16 + 4*grp + 0..3 sit at 4 consecutive permuted positions
     const int pos = fb / 2 * 32 + 8 * grp + 4 * (fb & 1);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(st + (db * 16 + r16) * DF + pos) = u[fi][db];
+    for (int db = 0; db < D / 16; ++db) {
+      typename TT::quad qv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = TT::from_f(u[fi][db][i]);
+      *reinterpret_cast<typename TT::quad*>(st + (db * 16 + r16) * DF + pos) = qv;
+    }
     float zs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) zs += phi[kb][fi][i];
     zs = xor_sum_groups(zs);
-    if (grp == 0) st[DF * D + pk_pos(fb * 16 + r16)] = zs;
+    if (grp == 0) st[DF * D + pk_pos(fb * 16 + r16)] = TT::from_f(zs);
   }
 }
 
-// Inclusive prefix sum of the chunk records over the complete chunks, in place.
-// A workgroup takes 64 record elements (one per lane) of one (b, h) and 8 waves; a round
-// covers 8 x 32 chunks, wave w the 32 chunks from 32 w on: each lane loads its 32 values at
-// once (one memory round trip per round), scans them in registers, and adds the totals of
-// the earlier segments (through LDS) and of the earlier rounds (a running carry). The last
-// block column instead reduces the per-chunk selected-key norms to one bound per compact
-// tile (tile t holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
+// Inclusive prefix sum of the chunk records over the complete chunks, in place, summed in
+// fp32 and stored in the layer's dtype. A workgroup takes 64 32-bit words of the records
+// (one per lane: one fp32 or two bf16 elements) of one (b, h) and 8 waves; a round covers
+// 8 x 32 chunks, wave w the 32 chunks from 32 w on: each lane loads its 32 words at once (one
+// memory round trip per round), scans them in registers, and adds the totals of the earlier
+// segments (through LDS) and of the earlier rounds (a running carry). The last block column
+// instead reduces the per-chunk selected-key norms to one bound per compact tile (tile t
+// holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
 constexpr int kScanWaves = 8, kScanSeg = 32;
-__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(float* states, int nC, int nCc, int R,
+template <typename T>
+__device__ __forceinline__ void unpack_word(uint32_t u, float (&x)[4 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    x[0] = __uint_as_float(u << 16);  // bf16 -> fp32 is exact
+    x[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    x[0] = __uint_as_float(u);
+  }
+}
+template <typename T>
+__device__ __forceinline__ uint32_t pack_word(const float (&x)[4 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, Tr<T>::from_f(x[0]));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, Tr<T>::from_f(x[1]));
+    return lo | (hi << 16);
+  } else {
+    return __float_as_uint(x[0]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(void* states, int nC, int nCc, int R,
                                                                const float* kmaxc, float* tilemax, int tm_stride,
                                                                int topk) {
+  constexpr int EPW = 4 / static_cast<int>(sizeof(T));  // elements per word
   const long long bh = blockIdx.y;
   if (tm_stride > 0 && static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - 1) {
     for (int t = threadIdx.x; t < tm_stride; t += 64 * kScanWaves) {
@@ -282,38 +310,54 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(float* states, in
     }
     return;
   }
-  __shared__ float tot[2][kScanWaves][64];
+  __shared__ float tot[2][kScanWaves][64 * EPW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int e = blockIdx.x * 64 + lane;
-  const bool ok = e < R;
+  const int rw = R / EPW;  // words per record (R is even)
+  const int wd = blockIdx.x * 64 + lane;
+  const bool ok = wd < rw;
+  const int rec = R * static_cast<int>(sizeof(T));  // bytes per record
   // the complete chunks' records of this (b, h): reads past them give zeros, writes past
-  // them are dropped; lanes past the record (e >= R) read but never write
-  const auto rs = make_rsrc(states + bh * nC * R, static_cast<uint32_t>(nCc) * static_cast<uint32_t>(R) * 4u);
-  float carry = 0.f;
+  // them are dropped; lanes past the record (wd >= rw) read but never write
+  const auto rs = make_rsrc(static_cast<char*>(states) + bh * nC * rec, static_cast<uint32_t>(nCc) * static_cast<uint32_t>(rec));
+  float carry[EPW];
+#pragma unroll
+  for (int e = 0; e < EPW; ++e) carry[e] = 0.f;
   int par = 0;
   for (int r0 = 0; r0 < nCc; r0 += kScanWaves * kScanSeg, par ^= 1) {
     const int c0 = r0 + wave * kScanSeg;  // this wave's first chunk
-    float x[kScanSeg];
+    float x[kScanSeg][EPW];
 #pragma unroll
     for (int j = 0; j < kScanSeg; ++j)
-      x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((c0 + j) * R + e) * 4, 0, 0));
+      unpack_word<T>(__builtin_amdgcn_raw_buffer_load_b32(rs, (c0 + j) * rec + wd * 4, 0, 0), x[j]);
 #pragma unroll
-    for (int j = 1; j < kScanSeg; ++j) x[j] += x[j - 1];
-    tot[par][wave][lane] = x[kScanSeg - 1];
+    for (int j = 1; j < kScanSeg; ++j)
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) x[j][e] += x[j - 1][e];
+#pragma unroll
+    for (int e = 0; e < EPW; ++e) tot[par][wave][lane * EPW + e] = x[kScanSeg - 1][e];
     __syncthreads();
-    float before = carry, all = carry;
+    float before[EPW];
 #pragma unroll
-    for (int w = 0; w < kScanWaves; ++w) {
-      const float t = tot[par][w][lane];
-      before += w < wave ? t : 0.f;
-      all += t;
+    for (int e = 0; e < EPW; ++e) {
+      float bsum = carry[e], all = carry[e];
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) {
+        const float t = tot[par][w][lane * EPW + e];
+        bsum += w < wave ? t : 0.f;
+        all += t;
+      }
+      before[e] = bsum;
+      carry[e] = all;
     }
-    carry = all;
     if (ok) {
 #pragma unroll
-      for (int j = 0; j < kScanSeg; ++j)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x[j] + before), rs, ((c0 + j) * R + e) * 4, 0, 0);
+      for (int j = 0; j < kScanSeg; ++j) {
+        float y[EPW];
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) y[e] = x[j][e] + before[e];
+        __builtin_amdgcn_raw_buffer_store_b32(pack_word<T>(y), rs, (c0 + j) * rec + wd * 4, 0, 0);
+      }
     }
   }
 }
@@ -413,13 +457,18 @@ hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float
 #undef DIMS
 }
 
-hipError_t launch_scan(const Dims& d, float* states, const float* kmaxc, float* tilemax, int tm_stride,
+hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* tilemax, int tm_stride,
                        hipStream_t s) {
   if (d.nCc == 0) return hipSuccess;
   const bool tiles = d.topk > 0 && tm_stride > 0;
-  dim3 grid((d.R + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
-  hipLaunchKernelGGL(scan_kernel, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax,
-                     tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
+  const int words = d.bf16 ? d.R / 2 : d.R;
+  dim3 grid((words + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
+  if (d.bf16)
+    hipLaunchKernelGGL(scan_kernel<bf16>, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc,
+                       tilemax, tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
+  else
+    hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc,
+                       tilemax, tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def test_status_strings():
     (dict(batch=0), -1), (dict(seq_len=0), -1), (dict(n_q_heads=6, n_kv_heads=4), -1), (dict(dtype="f16"), -1),
     (dict(window=-1), -1), (dict(top_k=65), -1), (dict(window=0, top_k=1), -1), (dict(chunk=32, window=32), -2),
     (dict(window=65), -2), (dict(head_dim=96), -2), (dict(feat_dim=32), -2), (dict(dtype="f32", head_dim=128), -2),
-    (dict(seq_len=2_100_000, head_dim=128, feat_dim=128), -2),
+    (dict(seq_len=4_200_000, head_dim=128, feat_dim=128), -2),
 ])
 def test_invalid_configs_rejected_before_launch(kw, code):
     lib = still.load()
