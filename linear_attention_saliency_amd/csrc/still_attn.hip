@@ -2,9 +2,10 @@
 //
 // One workgroup per (chunk c, batch b, KV head h, head split, query split). The
 // workgroup packs up to four query heads of the group (GQA): every staged key/value tile
-// serves all of them. Wave w handles query head w of the head split, for the QW
-// consecutive queries of its query split (64 / QW query splits per chunk, so two
-// independent workgroups can share a CU and hide each other's barriers).
+// serves all of them. A wave handles one query head of the head split for QW = 32
+// consecutive queries (a query slice). Where two workgroups fit in a CU, each takes one of
+// the chunk's two slices and the pair hides each other's barriers; where one fills the
+// CU's LDS (head_dim 128, fp32), it takes both slices with twice the waves.
 //
 // Key sets for query i = 64c + r ([P1] paragraph before "STILL三大创新", sections
 // "Chunk-Wise并行+延迟选择" and NP-Map; [P2] excerpt):
@@ -440,10 +441,8 @@ __device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T*
 
 template <typename T, int D, int DF, int NH>
 struct AttnCfg {
-  static constexpr int QW = 32;                // queries per wave
+  static constexpr int QW = 32;                // queries per wave (one query slice)
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
-  static constexpr int QSPLIT = 64 / QW;       // workgroups per chunk, one per query slice
-  static constexpr int NTHR = 64 * NH;         // threads per workgroup: one wave per head
   static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
   static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
   // the prefix state goes through LDS when it is small (S^T [D][DF] in the layer's dtype)
@@ -457,10 +456,18 @@ struct AttnCfg {
   static constexpr int R_P0 = R_ST + ST > 3 * STAGE ? R_ST + ST : 3 * STAGE;
   static constexpr int LDS_BYTES = (R_P0 + STAGE) * static_cast<int>(sizeof(T));
   static __device__ __forceinline__ int stage_off(int s) { return s == 0 ? R_P0 : (s - 1) * STAGE; }
+  // Query slices per workgroup. Where two workgroups fit in a CU's LDS (two 80 KiB
+  // halves) each takes one slice, and the pair hides each other's waits. Where only one
+  // fits (head_dim 128, or fp32) it takes both slices with twice the waves, so every SIMD
+  // still runs two waves and every staged tile serves the whole chunk.
+  static constexpr int QS = LDS_BYTES > 80 * 1024 ? 2 : 1;
+  static constexpr int QSPLIT = 64 / QW / QS;  // workgroups per chunk
+  static constexpr int NWAVE = NH * QS;        // wave w: head slot w % NH, query slice w / NH
+  static constexpr int NTHR = 64 * NWAVE;
   // buffer->LDS instructions each wave issues per compact tile (1 KiB each)
   static constexpr int KINS = KT * static_cast<int>(sizeof(T)) / 1024, VINS = VT * static_cast<int>(sizeof(T)) / 1024;
-  static_assert(KINS % NH == 0 && VINS % NH == 0, "tile copies must split evenly over the waves");
-  static constexpr int NL = (KINS + VINS) / NH;
+  static_assert(KINS % NWAVE == 0 && VINS % NWAVE == 0, "tile copies must split evenly over the waves");
+  static constexpr int NL = (KINS + VINS) / NWAVE;
 };
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vector memory only, until at most n
@@ -483,9 +490,9 @@ template <typename T> __device__ __forceinline__ typename Tr<T>::frag frag_of(co
 }
 
 template <typename T, int D, int DF, int NH>
-__global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, DF, NH>::QS)) void attn_kernel(AttnArgs a) {
   using C = AttnCfg<T, D, DF, NH>;
-  constexpr int QB = C::QB, QW = C::QW, NTHR = C::NTHR;
+  constexpr int QB = C::QB, QW = C::QW, NW = C::NWAVE;
   using SK = Swz<T, D>;    // K tile: 64 keys x D
   using SF = Swz<T, DF>;   // phi(K) tile: 64 keys x DF
   using SV = Swz<T, 64>;   // V^T tile: D rows x 64 keys
@@ -511,13 +518,13 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   const int P = BHG * C::QSPLIT;
   const int c = d.nC - 1 - static_cast<int>(blockIdx.x) / P;
   const int pi = static_cast<int>(blockIdx.x) % P;
-  const int bhg = pi % BHG, qs = pi / BHG;
+  const int bhg = pi % BHG, qsb = pi / BHG;  // block of C::QS query slices
   const int gs = bhg % a.gsplit, bh = bhg / a.gsplit;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
-  const int g = gs * NH + wave;
-  const int qoff = qs * QW;  // first query of this wave within the chunk
+  const int g = gs * NH + wave % NH;
+  const int qoff = (qsb * C::QS + wave / NH) * QW;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
   const int hq = h * d.G + (head_ok ? g : d.G - 1);
   const long long T_ = d.T;
@@ -533,8 +540,8 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
   // compact tile t -> LDS stage (asynchronous); K rows [64][D] and V^T rows [D][64] of a
   // tile are contiguous, so one resource per buffer covers every tile of this (b, h)
-  DmaTile<T, D, 64, NH> dk;
-  DmaTile<T, 64, D, NH> dv;
+  DmaTile<T, D, 64, NW> dk;
+  DmaTile<T, 64, D, NW> dv;
   dk.init(D);
   dv.init(64);
   const auto krs = make_rsrc(kb_ptr, static_cast<uint32_t>(a.ntiles_sel) * C::KT * static_cast<int>(sizeof(T)));
@@ -595,14 +602,14 @@ __global__ __launch_bounds__(64 * NH, 2) void attn_kernel(AttnArgs a) {
     const int cp = has_prev ? c - 1 : c;
     const T* kc = kk + ((b * T_ + t0) * d.Hkv + h) * D;
     const T* kp = kk + ((b * T_ + tp) * d.Hkv + h) * D;
-    dma_tile<T, DF, 64, NH>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + tp) * DF, DF, has_prev ? 64 : 0);
-    dma_tile<T, 64, D, NH>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
-    dma_tile<T, D, 64, NH>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
-    dma_tile<T, DF, 64, NH>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
-    dma_tile<T, 64, D, NH>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
-    dma_tile<T, D, 64, NH>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
+    dma_tile<T, DF, 64, NW>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + tp) * DF, DF, has_prev ? 64 : 0);
+    dma_tile<T, 64, D, NW>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
+    dma_tile<T, D, 64, NW>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
+    dma_tile<T, DF, 64, NW>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
+    dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
+    dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
-      dma_tile<T, DF, D, NH>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
+      dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
     dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
     dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
   }
