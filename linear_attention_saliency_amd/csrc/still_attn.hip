@@ -445,8 +445,10 @@ struct AttnCfg {
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
   static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
   static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
-  // the prefix state goes through LDS when it is small (S^T [D][DF] in the layer's dtype)
-  static constexpr bool STATE_LDS = D == 64 && DF == 64;
+  // the prefix state (S^T [D][DF] in the layer's dtype) goes through LDS where it fits
+  // beside the tiles: at D = d_f = 64 (two workgroups per CU) and at D = 128 (one, with
+  // both query slices: 8 waves read one copy instead of 8)
+  static constexpr bool STATE_LDS = (D == 64 && DF == 64) || D == 128;
   static constexpr int ST = STATE_LDS ? D * DF : 0;
   // LDS regions of the fixed part (element offsets); compact stages 1 and 2 reuse them
   static constexpr int R_PHIP = 0, R_PHIC = FT, R_VP = 2 * FT, R_VC = 2 * FT + VT;
