@@ -573,7 +573,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int ks = 0; ks < D / 32; ++ks)
         qf[qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
   }
-  // W_h rows fb*16 + r16 (A operand of phi(q)); held in registers only where they fit
+  // W_h rows fb*16 + r16 (A operand of phi(q)): held in registers where they fit, else
+  // copied once into compact stage 0 (free until the first compact tile) for all waves
   const T* Wh = w + static_cast<long long>(h) * DF * D;
   constexpr bool W_EARLY = D == 64 && DF == 64;
   frag wq[W_EARLY ? DF / 16 : 1][D / 32];
@@ -612,8 +613,13 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
       dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
-    dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
-    dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
+    if constexpr (W_EARLY) {
+      dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
+      dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
+    } else {
+      static_assert(DF * D <= C::STAGE, "W_h must fit in one compact stage");
+      dma_tile<T, D, DF, NW>(L + C::stage_off(0), Wh, D, DF);
+    }
   }
   // key-norm bounds of compact tiles 0..255 (lane l of tb[j] holds tile 64 j + l; later
   // tiles, if any, are treated as unbounded)
@@ -643,7 +649,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   uint64_t selprev;
   // =============================== phase 1: linear attention ===========================
   {
-    // phi(q) = |q| m / |m|, m = elu(W_h q) + 1
+    // phi(q) = |q| m / |m|, m = elu(W_h q) + 1; wfrag(fb, ks) gives the W_h fragment
+    auto phi_q = [&](auto wfrag) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x4 pacc[DF / 16];
@@ -651,14 +658,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int fb = 0; fb < DF / 16; ++fb) {
         pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          frag wa;
-          if constexpr (W_EARLY)
-            wa = wq[fb][ks];
-          else
-            wa = TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
-          TT::mma(pacc[fb], wa, qf[qb][ks]);
-        }
+        for (int ks = 0; ks < D / 32; ++ks) TT::mma(pacc[fb], wfrag(fb, ks), qf[qb][ks]);
       }
       float m2 = 0.f, x2 = 0.f;
 #pragma unroll
@@ -686,12 +686,22 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 #pragma unroll
         for (int e = 0; e < 8; ++e) pq[qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
     }
-
-    // phi(q) is done before the wait below (it overlaps the copies); keep the scheduler
-    // from moving it past the wait
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // every region copied at the start has landed
+    };
+    if constexpr (W_EARLY) {
+      // phi(q) before the wait (it overlaps the copies); keep the scheduler from moving it
+      // past the wait
+      phi_q([&](int fb, int ks) { return wq[fb][ks]; });
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // every region copied at the start has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // every region copied at the start has landed, W_h among them
+      phi_q([&](int fb, int ks) { return Swz<T, D>::load8(L + C::stage_off(0), fb * 16 + r16, ks * 32 + grp * 8); });
+      __syncthreads();  // every wave is done with W_h: stage 0 takes compact tile 0
+      dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
+      dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
+    }
     selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
 
@@ -848,7 +858,11 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int j = 0; j < 4; ++j) mayfar[j] = __builtin_amdgcn_ballot_w64(qmax * tb[j] > mmin + kLazy);
     }
     f32x4 sa[4][QB], sb[4][QB];
-    qk_tile_shifted<T, D, QB>(L + C::stage_off(0), qf, mneg, sa);  // tile 0 landed before phase 1
+    if constexpr (!W_EARLY) {  // tile 0 was copied after phi(q)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    qk_tile_shifted<T, D, QB>(L + C::stage_off(0), qf, mneg, sa);  // tile 0 has landed
     __syncthreads();
 #pragma unroll
     for (int t = 1; t < 4; ++t)
