@@ -268,12 +268,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 // Inclusive prefix sum of the chunk records over the complete chunks, in place, summed in
 // fp32 and stored in the layer's dtype. A workgroup takes 64 32-bit words of the records
 // (one per lane: one fp32 or two bf16 elements) of one (b, h) and 8 waves; a round covers
-// 8 x 32 chunks, wave w the 32 chunks from 32 w on: each lane loads its 32 words at once (one
+// 8 x SEG chunks, wave w the SEG chunks from SEG w on (SEG = 8, 16 or 32, the smallest that
+// covers the sequence in one round, up to 32): each lane loads its SEG words at once (one
 // memory round trip per round), scans them in registers, and adds the totals of the earlier
 // segments (through LDS) and of the earlier rounds (a running carry). The last block column
 // instead reduces the per-chunk selected-key norms to one bound per compact tile (tile t
 // holds compact rows 64t .. 64t+63, i.e. chunks 64t/topk .. (64t+63)/topk).
-constexpr int kScanWaves = 8, kScanSeg = 32;
+constexpr int kScanWaves = 8;
 template <typename T>
 __device__ __forceinline__ void unpack_word(uint32_t u, float (&x)[4 / sizeof(T)]) {
   if constexpr (sizeof(T) == 2) {
@@ -294,7 +295,7 @@ __device__ __forceinline__ uint32_t pack_word(const float (&x)[4 / sizeof(T)]) {
   }
 }
 
-template <typename T>
+template <typename T, int kScanSeg>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(void* states, int nC, int nCc, int R,
                                                                const float* kmaxc, float* tilemax, int tm_stride,
                                                                int topk) {
@@ -463,12 +464,15 @@ hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* t
   const bool tiles = d.topk > 0 && tm_stride > 0;
   const int words = d.bf16 ? d.R / 2 : d.R;
   dim3 grid((words + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
+  const int tms = tiles ? tm_stride : 0, tk = d.topk > 0 ? d.topk : 1;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax, tms, tk);
+  };
+  const int seg = d.nCc <= 8 * kScanWaves ? 8 : d.nCc <= 16 * kScanWaves ? 16 : 32;
   if (d.bf16)
-    hipLaunchKernelGGL(scan_kernel<bf16>, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc,
-                       tilemax, tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
+    go(seg == 8 ? scan_kernel<bf16, 8> : seg == 16 ? scan_kernel<bf16, 16> : scan_kernel<bf16, 32>);
   else
-    hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc,
-                       tilemax, tiles ? tm_stride : 0, d.topk > 0 ? d.topk : 1);
+    go(seg == 8 ? scan_kernel<float, 8> : seg == 16 ? scan_kernel<float, 16> : scan_kernel<float, 32>);
   return hipGetLastError();
 }
 
