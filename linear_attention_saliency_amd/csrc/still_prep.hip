@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   using frag = typename TT::frag;
   using SW = Swz<T, D>;
 
-  __shared__ __attribute__((aligned(16))) T band[128 * D];
+  __shared__ __attribute__((aligned(16))) T band[129 * D];
   __shared__ float s_part[4][64];
   __shared__ float s_acc[64];
   __shared__ float m2part[4 * 64];
@@ -62,14 +62,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     vpre[i] = row < nvalid ? TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8) : TT::zero();
   }
 
-  // 1. key band: row t <-> position t0 - 63 + t (row 127 is never in a window)
-  for (int idx = tid; idx < 128 * V8; idx += 256) {
-    const int row = idx / V8, c8 = idx % V8;
-    const long long pos = t0 - 63 + row;
-    frag x = TT::zero();
-    if (row < 127 && pos >= 0 && pos < T_) x = TT::load8(k + ((b * T_ + pos) * d.Hkv + h) * D + c8 * 8);
-    SW::store8(band, row, c8 * 8, x);
+  // 1. key band: row t <-> position t0 - 64 + t, rows 0..63 chunk c-1 and 64..127 chunk c,
+  //    copied straight into LDS (rows outside the sequence read as zeros); row 128 (the
+  //    position after the chunk, never in a window) is zero
+  {
+    const int kvs = d.Hkv * D;
+    dma_tile<T, D, 64, 4>(band, k + ((b * T_ + (c >= 1 ? t0 - kChunk : t0)) * d.Hkv + h) * D, kvs, c >= 1 ? 64 : 0);
+    dma_tile<T, D, 64, 4>(band + 64 * D, k + ((b * T_ + t0) * d.Hkv + h) * D, kvs, nvalid);
+    if (tid < V8) SW::store8(band, 128, tid * 8, TT::zero());
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // 2. saliency, summed over the group in head order g = 0..G-1
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks)
             qf[ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
-          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale);
+          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale, 1);
           if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
         }
       }
@@ -101,9 +103,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     if (tid < nvalid) a.sal[(static_cast<long long>(bh)) * T_ + t0 + tid] = s_acc[tid];
   }
 
-  // 3. NP-Map of the chunk's keys (band rows 63..126)
+  // 3. NP-Map of the chunk's keys (band rows 64..127)
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF>(band, 63, wf, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(band, 64, wf, m2part, xn2, phi);
 
   // 4. routing of a complete chunk
   const long long nsel_rows = static_cast<long long>(d.nCc) * d.topk;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       const long long dst =
           (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
-      if (slot < nsel) kx = SW::load8(band, 63 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 63..126
+      if (slot < nsel) kx = SW::load8(band, 64 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 64..127
 #pragma unroll
       for (int e = 0; e < 8; ++e) kx[e] = TT::from_f(TT::to_f(kx[e]) * scale);  // logits in log2 units
       TT::store8(ks_ + dst, kx);
