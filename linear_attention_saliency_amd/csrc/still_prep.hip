@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
   const long long T_ = d.T;
   const long long t0 = static_cast<long long>(c) * kChunk;
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
@@ -80,13 +81,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       const int g = g0 + wave;
       if (g < d.G) {
         const int hq = h * d.G + g;
+        // queries of block qb (rows past the sequence end read as zeros), one block ahead
+        const auto qrs = make_rsrc(q + ((b * T_ + t0) * d.Hq + hq) * D,
+                                   static_cast<uint32_t>(((nvalid - 1) * d.Hq + 1) * D * static_cast<int>(sizeof(T))));
+        auto qload = [&](int qb, frag (&qf)[D / 32]) {
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks)
+            qf[ks] = TT::bload8(qrs, ((qb * 16 + r16) * d.Hq * D + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
+        };
+        frag qcur[D / 32];
+        qload(0, qcur);
 #pragma unroll 1
         for (int qb = 0; qb < 4; ++qb) {
           frag qf[D / 32];
-          const long long pos = t0 + qb * 16 + r16;
 #pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks)
-            qf[ks] = pos < T_ ? TT::load8(q + ((b * T_ + pos) * d.Hq + hq) * D + ks * 32 + grp * 8) : TT::zero();
+          for (int ks = 0; ks < D / 32; ++ks) qf[ks] = qcur[ks];
+          if (qb < 3) qload(qb + 1, qcur);
           const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale, 1);
           if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
         }
