@@ -300,6 +300,9 @@ def main() -> int:
                     help="untimed steps (default 100 for prefill, enough for the clocks to settle; 8 for decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--top-k", type=int, default=None,
+                    help="override the workload's top_k on the same kernels: 0 gives the sliding-window plus "
+                         "linear-attention baseline, 64 (= chunk) full causal softmax")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (every step is "
@@ -318,6 +321,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     wl = getattr(synth, WORKLOAD_NAMES[args.workload])
+    if args.top_k is not None and args.top_k != wl.top_k:
+        wl = wl.replace(top_k=args.top_k, name=f"{wl.name}-k{args.top_k}")
     decode = wl.decode_steps > 0
     if args.steps is None:
         args.steps = 64 if decode else 50

@@ -212,6 +212,33 @@ def test_headline_shape_sampled():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("top_k", [0, 64])
+def test_baselines_at_headline_shape(top_k):
+    """The same kernels at the 16K Llama-3.2-1B shape as the two baselines the method is
+    compared with: top_k = 0 (sliding window plus NP-Map linear attention, the positional
+    baseline) and top_k = 64 = chunk (every past token selected: full causal softmax).
+    The routing is fixed by construction (nothing or everything selected); sampled output
+    rows are checked against the per-query oracle."""
+    wl = synth.L1B_16K.replace(top_k=top_k, name=f"{synth.L1B_16K.name}-k{top_k}")
+    _say("baseline", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    out, s_gpu, idx_gpu = _run(q, k, v, wp, wl)
+    T = wl.seq_len
+    assert idx_gpu.shape == (wl.batch, wl.n_kv_heads, T // 64, top_k)
+    if top_k == 64:
+        want = np.arange(T // 64 * 64).reshape(T // 64, 64)
+        assert np.array_equal(idx_gpu, np.broadcast_to(want, idx_gpu.shape))
+    sel = _sel_from_idx(idx_gpu, T)
+    rng = np.random.default_rng(5)
+    rows = [(0, int(rng.integers(wl.n_q_heads)), int(i)) for i in
+            np.concatenate([rng.integers(0, T, 24), [0, 63, 64, 127, T - 1]])]
+    ref = O.brute_rows(q, k, v, wp, wl.window, wl.chunk, sel, rows)
+    got = np.stack([out[b, i, hq] for (b, hq, i) in rows])
+    err = np.abs(got - ref).max()
+    _say(wl.name, "sampled max abs err", err)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("name", ["L8B_4K", "L8B_64K"])
 def test_8b_shapes_sampled(name):
     """The Llama-3.1-8B-shaped layers at full size (8 x 4096 and 1 x 65536 tokens, head_dim
