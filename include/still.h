@@ -8,8 +8,13 @@
  *   [P1] "仅0.04B！哈工深首创同层混合架构STILL，极低成本线性化LLM" (PaperWeekly repost):
  *        sections "Self-Saliency Score", "Norm-Preserved Feature Map（NP-Map）",
  *        "Chunk-Wise并行+延迟选择", and the paragraph before "STILL三大创新".
+ *   [P2] "STILL: Content-Aware Intra-Layer Hybrid Attention Cuts Memory 80%, Speeds
+ *        Prefill 83%" (picx.dev), summary and the 机器之心 excerpt.
+ *   [P3] "STILL от HIT Shenzhen: гибридное внимание внутри слоя выбирает токены по
+ *        содержанию" (news piece), on the fixed-size state of linear attention.
  *   [P4] "STILL: Selecting Tokens for Intra-Layer Hybrid Attention to Linearize LLMs"
  *        (research-map summary), section Approach.
+ * The sources under linear_attention_saliency_amd/csrc cite these labels.
  *
  * The pages leave these points open; the library fixes them as follows.
  *   window      W_i = {max(0, i-w+1) .. i}, causal, contains i.

@@ -1,4 +1,5 @@
 // Fused softmax + linear attention of the STILL prefill, with the shared normaliser.
+// (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
 // One workgroup per (chunk c, batch b, KV head h, head split, query split). The
 // workgroup packs up to four query heads of the group (GQA): every staged key/value tile

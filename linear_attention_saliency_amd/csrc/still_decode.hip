@@ -1,6 +1,7 @@
 // Decode step of the STILL layer and the kernels that build its cache
 // ([P1] section "Chunk-Wise并行+延迟选择": routing decided per chunk and used one chunk later,
 // so a decoding token never waits for a per-token selection).
+// (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
 // One new token for every sequence, all at position i = 64c + r. Per (batch b, KV head h):
 //   decode_split_kernel  nsplit workgroups each read a disjoint run of 64-row tiles of the

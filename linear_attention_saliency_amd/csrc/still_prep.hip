@@ -1,5 +1,6 @@
 // Per-chunk preparation kernels of the STILL prefill, plus the standalone top-k and
 // NP-Map kernels.
+// (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
 // prep_kernel, one workgroup per (chunk c, batch b, KV head h), four waves:
 //   1. stage the 128-row key band around chunk c in LDS;

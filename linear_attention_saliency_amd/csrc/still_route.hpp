@@ -1,4 +1,5 @@
 // Saliency, per-chunk top-k and NP-Map device routines.
+// (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
 // The prefill kernels and the decode kernel call exactly these functions, so a token's
 // saliency (and hence every routing decision) is bit-identical whichever path computed it.
