@@ -20,10 +20,12 @@
 
 namespace still {
 
-// At head_dim 64 in bf16 the kernel fits in 76 registers, so six workgroups share a CU
-// (LDS allows eight): the 2048 workgroups of a 16K layer then need few waves of dispatch.
+// Workgroups per CU the registers are sized for: at D = d_f = 64 in bf16 the kernel fits
+// in 76 registers, so six share a CU (LDS allows eight) and the 2048 workgroups of a 16K
+// layer need few waves of dispatch; at head_dim 128 three (LDS allows four).
 template <typename T, int D, int DF>
-__global__ __launch_bounds__(256, (D == 64 && sizeof(T) == 2) ? 6 : 1) void prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, (D == 64 && DF == 64 && sizeof(T) == 2) ? 6 : (D == 128 ? 3 : 1))
+void prep_kernel(PrepArgs a) {
   constexpr int FPW = DF / 64;
   constexpr int V8 = D / 8;
   using TT = Tr<T>;
