@@ -76,14 +76,15 @@ PEAK_BF16_MFMA = 2.5e15   # dense, FLOP/s
 PEAK_HBM = 8.0e12         # bytes/s
 
 
-def algorithmic_work(wl, sel_idx: np.ndarray) -> dict:
+def algorithmic_work(wl, sel_idx: np.ndarray, score: str = "saliency") -> dict:
     """Algorithmic flops and bytes of the layer, from the routing the device chose.
 
     Softmax: 4*D flops per (query head, softmax key) pair, the keys being the window
     plus every selected key outside it. Linear attention: the recurrent minimum, 2*F*D+2*F
     per query-head token (read-out) plus the same per KV-head token (state update).
     NP-Map: 2*D*F per query-head and per KV-head row. Saliency: 2*D per (query head,
-    window key). Bytes: Q, K, V and O once each (bf16), plus the NP-Map weights.
+    window key); routed by the diagonal logit, 2*D per query head. Bytes: Q, K, V and O once
+    each (bf16), plus the NP-Map weights.
     """
     B, T, Hq, Hkv, D, F = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.feat_dim
     w, C = wl.window, wl.chunk
@@ -103,7 +104,7 @@ def algorithmic_work(wl, sel_idx: np.ndarray) -> dict:
     la_k = (2.0 * F * D + 2.0 * F) * Hkv * B * T
     np_q = 2.0 * D * F * Hq * B * T
     np_k = 2.0 * D * F * Hkv * B * T
-    sal = 2.0 * D * float(np.sum(win)) * Hq * B
+    sal = 2.0 * D * (float(np.sum(win)) if score == "saliency" else float(T)) * Hq * B
     esz = 2 if wl.dtype == "bf16" else 4
     bytes_ = esz * (B * T * (2 * Hq + 2 * Hkv) * D + Hkv * F * D)
     return {"flops": sa + la_q + la_k + np_q + np_k + sal, "bytes": float(bytes_),
@@ -145,13 +146,13 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     if not (wl is synth.L1B_16K and not args.no_cpu_baseline):
         del q, k, v, w
     out = torch.empty_like(tq)
-    call = still.Prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, chunk=wl.chunk)
+    call = still.Prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, chunk=wl.chunk, score=args.score)
     sel = torch.empty((wl.batch, wl.n_kv_heads, wl.seq_len // wl.chunk, wl.top_k), dtype=torch.int32, device=dev)
     torch.cuda.reset_peak_memory_stats()
     call(tq, tk, tv, tw, out, sel_idx=sel)
     torch.cuda.synchronize()
     sel_idx = sel.cpu().numpy()
-    work = algorithmic_work(wl, sel_idx)
+    work = algorithmic_work(wl, sel_idx, args.score)
 
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out)
@@ -194,7 +195,7 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
         "data": "synthetic: seeded N(0,1)/sqrt(D) Q/K/V, 1% planted keys x4, W_phi N(0,1/D); bf16",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len, "n_q_heads": wl.n_q_heads,
                    "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "feat_dim": wl.feat_dim,
-                   "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k},
+                   "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k, "score": args.score},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
                      "traffic": measured_traffic(wl.name)},
@@ -218,11 +219,12 @@ def run_decode(wl, args, torch, still, synth) -> dict:
     T0, C = wl.seq_len, wl.chunk
     n_tok = args.warmup + args.steps
     cache = still.DecodeCache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, feat_dim=F, window=wl.window,
-                              top_k=wl.top_k, max_tokens=T0 + n_tok, dtype=torch.bfloat16, device=dev)
+                              top_k=wl.top_k, max_tokens=T0 + n_tok, dtype=torch.bfloat16, device=dev,
+                              score=args.score)
     # the 64K-token prefix of all sequences goes into the cache through one prefill
     q, k, v, w = synth.make_inputs_device(wl, dev)
     out = torch.empty_like(q)
-    call = still.Prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, chunk=C)
+    call = still.Prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, chunk=C, score=args.score)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     call(q, k, v, w, out, cache=cache)
@@ -275,7 +277,8 @@ def run_decode(wl, args, torch, still, synth) -> dict:
         "dtype": "bf16",
         "data": "synthetic: seeded (torch generator on the device) N(0,1)/sqrt(D) Q/K/V, W_phi N(0,1/D); bf16",
         "config": {"workload": wl.name, "batch": B, "context": T0, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "head_dim": D, "feat_dim": F, "window": wl.window, "chunk": C, "top_k": wl.top_k},
+                   "head_dim": D, "feat_dim": F, "window": wl.window, "chunk": C, "top_k": wl.top_k,
+                   "score": args.score},
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": ach / 1e9,
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach / PEAK_HBM,
                      "traffic": measured_traffic(wl.name, DECODE_TRAFFIC_FILE, DECODE_SRCS)},
@@ -303,6 +306,8 @@ def main() -> int:
     ap.add_argument("--top-k", type=int, default=None,
                     help="override the workload's top_k on the same kernels: 0 gives the sliding-window plus "
                          "linear-attention baseline, 64 (= chunk) full causal softmax")
+    ap.add_argument("--score", choices=["saliency", "diag"], default="saliency",
+                    help="routing score: the Self-Saliency Score, or the diagonal logit alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (every step is "
@@ -323,6 +328,8 @@ def main() -> int:
     wl = getattr(synth, WORKLOAD_NAMES[args.workload])
     if args.top_k is not None and args.top_k != wl.top_k:
         wl = wl.replace(top_k=args.top_k, name=f"{wl.name}-k{args.top_k}")
+    if args.score != "saliency":
+        wl = wl.replace(name=f"{wl.name}-{args.score}")
     decode = wl.decode_steps > 0
     if args.steps is None:
         args.steps = 64 if decode else 50

@@ -13,7 +13,7 @@
  *   [P3] "STILL от HIT Shenzhen: гибридное внимание внутри слоя выбирает токены по
  *        содержанию" (news piece), on the fixed-size state of linear attention.
  *   [P4] "STILL: Selecting Tokens for Intra-Layer Hybrid Attention to Linearize LLMs"
- *        (research-map summary), section Approach.
+ *        (research-map summary), sections Approach and "Surprising findings".
  * The sources under linear_attention_saliency_amd/csrc cite these labels.
  *
  * The pages leave these points open; the library fixes them as follows.
@@ -59,6 +59,16 @@ extern "C" {
 /* Element type of q, k, v, w_phi and out. */
 typedef enum still_dtype { STILL_F32 = 0, STILL_BF16 = 1 } still_dtype;
 
+/* Routing score of a token (the value each chunk's top_k is taken on):
+ *   STILL_SCORE_SALIENCY  the Self-Saliency Score above ([P1] section "Self-Saliency Score");
+ *   STILL_SCORE_DIAG      the diagonal logit alone, s_i = sum_g q_{g,i} . k_i / sqrt(head_dim):
+ *                         the pages' ablation that routes by the diagonal attention without
+ *                         the rest of the window ([P4] section "Surprising findings"). Routing by the diagonal
+ *                         softmax weight p_ii itself would select exactly the saliency's
+ *                         tokens, since -log(1 - p_ii) grows with p_ii; the raw logit is the
+ *                         reading that differs. */
+typedef enum still_score { STILL_SCORE_SALIENCY = 0, STILL_SCORE_DIAG = 1 } still_score;
+
 /* Status codes (0 = success). */
 enum {
   STILL_OK = 0,
@@ -87,6 +97,7 @@ typedef struct still_config {
   int32_t chunk;
   int32_t top_k;
   int32_t dtype; /* still_dtype */
+  int32_t score; /* still_score; 0 = the Self-Saliency Score */
 } still_config;
 
 /* Decode state for batched token-by-token generation with chunk-delayed selection

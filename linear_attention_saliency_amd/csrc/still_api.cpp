@@ -22,6 +22,7 @@ int check_cfg(const still_config* c, bool use_seq) {
   if (use_seq && c->seq_len < 1) return STILL_ERR_INVALID_ARG;
   if (c->n_q_heads % c->n_kv_heads != 0) return STILL_ERR_INVALID_ARG;
   if (c->dtype != STILL_F32 && c->dtype != STILL_BF16) return STILL_ERR_INVALID_ARG;
+  if (c->score != STILL_SCORE_SALIENCY && c->score != STILL_SCORE_DIAG) return STILL_ERR_INVALID_ARG;
   if (c->head_dim < 1 || c->feat_dim < 1 || c->chunk < 1) return STILL_ERR_INVALID_ARG;
   if (c->window < 0 || c->top_k < 0 || c->top_k > c->chunk) return STILL_ERR_INVALID_ARG;
   if (c->window == 0 && c->top_k != 0) return STILL_ERR_INVALID_ARG;
@@ -52,6 +53,7 @@ Dims dims_of(const still_config* c) {
   d.DF = c->feat_dim;
   d.window = c->window;
   d.topk = c->top_k;
+  d.score = c->score;
   d.nC = (c->seq_len + 63) / 64;
   d.nCc = c->seq_len / 64;
   d.R = c->feat_dim * c->head_dim + c->feat_dim;
@@ -135,7 +137,7 @@ int check_cache_cfg(const still_config* c, int64_t max_tokens) {
 bool same_layer(const still_config* a, const still_config* b) {
   return a->batch == b->batch && a->n_q_heads == b->n_q_heads && a->n_kv_heads == b->n_kv_heads &&
          a->head_dim == b->head_dim && a->feat_dim == b->feat_dim && a->window == b->window &&
-         a->chunk == b->chunk && a->top_k == b->top_k && a->dtype == b->dtype;
+         a->chunk == b->chunk && a->top_k == b->top_k && a->dtype == b->dtype && a->score == b->score;
 }
 
 still::CacheView view_of(const still_cache* c) {

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
           qf[ks] = r16 == (r & 15) ? TT::load8(q + g * D + ks * 32 + grp * 8) : TT::zero();
-        const float sv = saliency_qblock<T, D>(kt, qf, r >> 4, w, 64 * c - 63, scale, 1);
+        const float sv = saliency_qblock<T, D>(kt, qf, r >> 4, w, 64 * c - 63, scale, 1, d.score);
         if (lane == (r & 15)) gsal[g] = sv;
       }
     }

@@ -12,6 +12,7 @@ struct Dims {
   int nCc;  // number of complete chunks, T / 64
   int R;    // elements per chunk state record: DF*D (S) + DF (z)
   int bf16; // 1 = bf16 tensors, 0 = fp32
+  int score; // routing score: 0 = Self-Saliency Score, 1 = diagonal logit
 };
 
 struct PrepArgs {

@@ -102,7 +102,7 @@ void prep_kernel(PrepArgs a) {
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) qf[ks] = qcur[ks];
           if (qb < 3) qload(qb + 1, qcur);
-          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale, 1);
+          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale, 1, d.score);
           if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
         }
       }

@@ -27,10 +27,12 @@ constexpr int kChunk = 64;
 // without i, Z' = sum over the window without i of
 // e^{a - M'}, and s_i = LSE(W_i) - LSE(W_i \ i) = softplus(a_ii - M' - log Z'), which is
 // +inf when i is alone in its window. Returned in every lane of the query's column.
+// With score = 1 the routing score is the diagonal logit alone, q_i . k_i / sqrt(D) in
+// natural units ([P4] section "Surprising findings": routing by the diagonal attention).
 template <typename T, int D>
 __device__ __forceinline__ float saliency_qblock(const T* band, const typename Tr<T>::frag (&qf)[D / 32],
                                                  int qb, int window, long long band_pos0, float scale,
-                                                 int row_base = 0) {
+                                                 int row_base = 0, int score = 0) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   f32x4 acc[5];
 #pragma unroll
@@ -42,9 +44,18 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
       Tr<T>::mma(acc[j], a, qf[ks]);
     }
   }
-  // logits in log2 units: scale = log2(e) / sqrt(D)
   const int r = qb * 16 + r16;
   const int diag = r + 63;
+  if (score == 1) {
+    float dr = -kInf;
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((qb + j) * 16 + 4 * grp + i == diag) dr = acc[j][i];
+    return xor_max_groups(dr) * (1.0f / sqrtf(static_cast<float>(D)));
+  }
+  // logits in log2 units: scale = log2(e) / sqrt(D)
   const int lo = max(r + 64 - window, static_cast<int>(-band_pos0));  // first window row inside the sequence
   float mx = -kInf, dg = -kInf;
 #pragma unroll
@@ -74,14 +85,17 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
   return sp * 0.69314718055994531f;
 }
 
-// Top-k of one chunk ([P1] section "Chunk-Wise并行+延迟选择"): lane p holds the
-// saliency of chunk position p (a non-negative float or +inf). A bitonic sort of the
-// 64-bit keys (saliency bits, 63 - p) in descending order leaves rank j in lane j; the
-// first topk ranks are returned as a position bit mask. Equal saliency sorts the lower
-// position first. Every lane of the wave must call.
+// Top-k of one chunk ([P1] section "Chunk-Wise并行+延迟选择"): lane p holds the routing
+// score of chunk position p (any float but NaN; +inf sorts first). A bitonic sort of the
+// 64-bit keys (order-preserving score bits, 63 - p) in descending order leaves rank j in
+// lane j; the first topk ranks are returned as a position bit mask. Equal scores sort the
+// lower position first. Every lane of the wave must call.
 __device__ __forceinline__ uint64_t topk_mask(float s, int topk) {
   const int lane = threadIdx.x & 63;
-  uint64_t key = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | static_cast<uint32_t>(63 - lane);
+  // fp32 bits ordered as unsigned integers: negative values flipped, the sign bit set on the rest
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint64_t key = (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(63 - lane);
 #pragma unroll
   for (int kk = 2; kk <= 64; kk <<= 1)
 #pragma unroll

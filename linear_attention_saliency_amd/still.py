@@ -34,7 +34,7 @@ class StillError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "seq_len", "n_q_heads", "n_kv_heads", "head_dim",
-                                               "feat_dim", "window", "chunk", "top_k", "dtype")]
+                                               "feat_dim", "window", "chunk", "top_k", "dtype", "score")]
 
 
 class Cache(ctypes.Structure):
@@ -85,10 +85,14 @@ def load():
     return lib
 
 
+SCORES = {"saliency": 0, "diag": 1}  # still_score: the routing score
+
+
 def make_config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k,
-                dtype) -> Config:
+                dtype, score: str = "saliency") -> Config:
     dt = STILL_BF16 if dtype in (torch.bfloat16, "bf16") else STILL_F32 if dtype in (torch.float32, "f32") else -1
-    return Config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dt)
+    return Config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dt,
+                  SCORES.get(score, -1))
 
 
 def _ptr(t):
@@ -105,12 +109,12 @@ def _check(rc: int, what: str):
         raise StillError(rc, what)
 
 
-def _tensor_cfg(q, k, w_phi, window, chunk, top_k):
+def _tensor_cfg(q, k, w_phi, window, chunk, top_k, score="saliency"):
     if q.dim() != 4 or k.dim() != 4 or w_phi.dim() != 3:
         raise ValueError("q/k must be [B,T,H,D] and w_phi [Hkv,d_f,D]")
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    return make_config(B, T, Hq, Hkv, D, w_phi.shape[1], window, chunk, top_k, q.dtype)
+    return make_config(B, T, Hq, Hkv, D, w_phi.shape[1], window, chunk, top_k, q.dtype, score)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -120,8 +124,8 @@ def workspace_bytes(cfg: Config) -> int:
 class Prefill:
     """A prepared prefill call: the config and a reusable workspace for fixed shapes."""
 
-    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64):
-        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k)
+    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, score: str = "saliency"):
+        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k, score)
         nbytes = workspace_bytes(self.cfg)
         if nbytes == 0:
             rc = load().still_prefill(ctypes.byref(self.cfg), None, None, None, None, None, None, None, None,
@@ -146,16 +150,17 @@ class Prefill:
 
 
 def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing=None,
-            return_saliency: bool = False, return_routing: bool = False, cache=None):
+            return_saliency: bool = False, return_routing: bool = False, cache=None, score: str = "saliency"):
     """One STILL layer over whole sequences.
 
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
     GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection.
     cache: optional empty DecodeCache, left ready to decode token T.
-    Returns out (and saliency [B,Hkv,T] fp32, sel_idx [B,Hkv,T//chunk,top_k] int32 on
-    request).
+    score: "saliency" (the Self-Saliency Score) or "diag" (the diagonal logit alone).
+    Returns out (and the routing score [B,Hkv,T] fp32, sel_idx [B,Hkv,T//chunk,top_k] int32
+    on request).
     """
-    call = Prefill(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk)
+    call = Prefill(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk, score=score)
     B, T, _, _ = q.shape
     Hkv = k.shape[2]
     out = torch.empty_like(q)
@@ -203,9 +208,10 @@ class DecodeCache:
 
     def __init__(self, *, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, feat_dim: int,
                  window: int, top_k: int, max_tokens: int, dtype=torch.bfloat16, chunk: int = 64,
-                 device="cuda"):
+                 device="cuda", score: str = "saliency"):
         lib = load()
-        self.cfg = make_config(batch, 0, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dtype)
+        self.cfg = make_config(batch, 0, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dtype,
+                               score)
         nbytes = int(lib.still_cache_bytes(ctypes.byref(self.cfg), max_tokens))
         if nbytes == 0:
             raise StillError(-2, "still_cache_bytes")

@@ -113,6 +113,24 @@ def saliency(q, k, window: int):
     return s_kv, s_q
 
 
+def diagonal_score(q, k):
+    """Routing score of the pages' ablation that routes by the diagonal attention alone
+    ([P4] section "Surprising findings"): the raw diagonal logit q_i . k_i / sqrt(D) per
+    query head, summed over each KV head's group as for the saliency. (The diagonal softmax
+    weight p_ii itself would route exactly like the saliency, which grows with it.)
+
+    q [B,T,Hq,D], k [B,T,Hkv,D] -> (s_kv [B,Hkv,T], s_q [B,Hq,T]).
+    """
+    q, k = _f64(q), _f64(k)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = _check_group(Hq, Hkv)
+    kq = np.repeat(k, G, axis=2)  # query head hq reads KV head hq // G
+    s_q = np.einsum("bthd,bthd->bht", q, kq) / np.sqrt(D)
+    s_kv = s_q.reshape(B, Hkv, G, T).sum(axis=2)
+    return s_kv, s_q
+
+
 # --------------------------------------------------------------------------------------
 # Chunk-wise routing  ([P1] section "Chunk-Wise并行+延迟选择"; [P4] section Approach)
 # --------------------------------------------------------------------------------------

@@ -46,11 +46,11 @@ def _mask_bits(m):
     return ((u[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
 
 
-def _new_cache(wl, max_tokens):
+def _new_cache(wl, max_tokens, score="saliency"):
     return still.DecodeCache(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
                              head_dim=wl.head_dim, feat_dim=wl.feat_dim, window=wl.window, top_k=wl.top_k,
                              max_tokens=max_tokens,
-                             dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32)
+                             dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, score=score)
 
 
 def _decode_steps(cache, tq, tk, tv, tw, t0, t1):
@@ -80,12 +80,16 @@ PREFILL_THEN_DECODE = [
     ("bf16-g6", 1, 64, 200, 6, 1, 64, 64, 64, 8, "bf16", 1.0),
     ("bf16-d64-f128-from-1", 2, 1, 141, 4, 2, 64, 128, 64, 4, "bf16", None),
     ("bf16-d128-f64-k64", 1, 190, 330, 4, 1, 128, 64, 64, 64, "bf16", 1.0),
+    # routed by the diagonal logit instead of the Self-Saliency Score
+    ("bf16-diag-score", 2, 100, 270, 4, 1, 64, 64, 64, 8, "bf16", 1.0, "diag"),
+    ("bf16-d128-diag-score", 1, 64, 200, 4, 2, 128, 128, 64, 16, "bf16", None, "diag"),
 ]
 
 
 @pytest.mark.parametrize("case", PREFILL_THEN_DECODE, ids=[c[0] for c in PREFILL_THEN_DECODE])
 def test_prefill_then_decode_equals_prefill(case):
-    name, B, T0, T, Hq, Hkv, D, F, w, k, dt, sc = case
+    name, B, T0, T, Hq, Hkv, D, F, w, k, dt, sc, *rest = case
+    score = rest[0] if rest else "saliency"
     _say(name)
     wl, (q, kk, v, wp) = synth.small_case(seed=zlib.crc32(name.encode()) % 1000, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D,
                                            F=F, window=w, chunk=64, top_k=k, dtype=dt, qk_scale=sc,
@@ -93,18 +97,18 @@ def test_prefill_then_decode_equals_prefill(case):
     tq, tk, tv, tw = (_dev(a, dt) for a in (q, kk, v, wp))
 
     # reference: one prefill of all T tokens, into a cache as well
-    full_cache = _new_cache(wl, T + 16)
+    full_cache = _new_cache(wl, T + 16, score)
     if w >= 1:
         out_full, sal_full, idx_full = still.prefill(tq, tk, tv, tw, window=w, top_k=k, return_saliency=True,
-                                                     return_routing=True, cache=full_cache)
+                                                     return_routing=True, cache=full_cache, score=score)
     else:
         out_full, idx_full = still.prefill(tq, tk, tv, tw, window=w, top_k=k, return_routing=True,
                                            cache=full_cache)
         sal_full = None
 
-    cache = _new_cache(wl, T + 16)
+    cache = _new_cache(wl, T + 16, score)
     still.prefill(tq[:, :T0].contiguous(), tk[:, :T0].contiguous(), tv[:, :T0].contiguous(), tw, window=w,
-                  top_k=k, cache=cache)
+                  top_k=k, cache=cache, score=score)
     out_dec, sal_dec, masks = _decode_steps(cache, tq, tk, tv, tw, T0, T)
     assert cache.n_tokens == T
 

@@ -31,13 +31,13 @@ def _dev(x, dtype):
     return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32).contiguous()
 
 
-def _run(q, k, v, w, wl, routing=None):
+def _run(q, k, v, w, wl, routing=None, score="saliency"):
     dt = wl.dtype
     tq, tk, tv, tw = (_dev(a, dt) for a in (q, k, v, w))
     r = None if routing is None else torch.from_numpy(routing.astype(np.int32)).cuda()
     if wl.window >= 1:
         out, sal, sel = still.prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, routing=r,
-                                      return_saliency=True, return_routing=True)
+                                      return_saliency=True, return_routing=True, score=score)
     else:
         out, sel = still.prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, routing=r, return_routing=True)
         sal = None
@@ -209,6 +209,44 @@ def test_headline_shape_sampled():
     got = np.stack([out[b, i, hq] for (b, hq, i) in rows])
     err = np.abs(got - ref).max()
     _say("headline sampled max abs err", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dt,D,F,G", [("f32", 64, 64, 1), ("bf16", 64, 64, 4), ("bf16", 128, 128, 4)])
+def test_diagonal_score_routing(dt, D, F, G):
+    """Routing by the diagonal logit alone: the device's scores against the oracle's, the
+    selection of every decided chunk, and the output under the device's routing."""
+    _say("diag-score", dt, D, F, G)
+    wl, (q, kk, v, wp) = synth.small_case(seed=91 + D + G, B=1, T=330, Hq=G, Hkv=1, D=D, F=F, window=64,
+                                           chunk=64, top_k=8, dtype=dt, qk_scale=1.0, n_planted=6)
+    out, s_gpu, idx_gpu = _run(q, kk, v, wp, wl, score="diag")
+    s_ref, _ = O.diagonal_score(q, kk)
+    decided, flips = _check_routing(s_gpu, idx_gpu, s_ref, wl)
+    _say("diag-score decided", decided, "flips", flips)
+    ref = O.attend(q, kk, v, wp, wl.window, wl.chunk, wl.top_k, sel=_sel_from_idx(idx_gpu, wl.seq_len))
+    err = np.abs(out - ref).max()
+    _say("diag-score max abs err", err)
+    assert decided > 0 and err <= TOL[dt]
+
+
+def test_diagonal_score_at_headline_shape():
+    """The 16K Llama-3.2-1B-shaped layer routed by the diagonal logit: routing over every
+    chunk against the oracle's, and sampled output rows against the per-query oracle."""
+    wl = synth.L1B_16K
+    _say("diag-score headline", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    out, s_gpu, idx_gpu = _run(q, k, v, wp, wl, score="diag")
+    s_ref, _ = O.diagonal_score(q, k)
+    decided, flips = _check_routing(s_gpu, idx_gpu, s_ref, wl)
+    _say("diag-score headline decided", decided, "flips", flips)
+    sel = _sel_from_idx(idx_gpu, wl.seq_len)
+    rng = np.random.default_rng(6)
+    rows = [(0, int(rng.integers(wl.n_q_heads)), int(i)) for i in
+            np.concatenate([rng.integers(0, wl.seq_len, 24), [0, 63, 64, 127, wl.seq_len - 1]])]
+    ref = O.brute_rows(q, k, v, wp, wl.window, wl.chunk, sel, rows)
+    got = np.stack([out[b, i, hq] for (b, hq, i) in rows])
+    err = np.abs(got - ref).max()
+    _say("diag-score headline sampled max abs err", err)
     assert err <= TOL["bf16"]
 
 

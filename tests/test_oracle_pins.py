@@ -95,6 +95,43 @@ def test_saliency_group_sum_and_identical_heads():
     assert np.array_equal(a, b)
 
 
+def test_diagonal_score_brute_force_and_group_sum():
+    """The diagonal-logit routing score: an explicit per-token dot product (math.fsum over
+    the head dimension), and the sum over identical heads of a group."""
+    B, T, Hq, Hkv, D = 1, 9, 4, 2, 5
+    q = _rand(B, T, Hq, D)
+    k = _rand(B, T, Hkv, D)
+    s_kv, s_q = O.diagonal_score(q, k)
+    G = Hq // Hkv
+    for hq in range(Hq):
+        for i in range(T):
+            want = math.fsum(q[0, i, hq, d] * k[0, i, hq // G, d] for d in range(D)) / math.sqrt(D)
+            assert abs(s_q[0, hq, i] - want) < 1e-14
+    q1 = _rand(B, T, 1, D)
+    s_rep, _ = O.diagonal_score(np.repeat(q1, 3, axis=2), k[:, :, :1])
+    s_one, _ = O.diagonal_score(q1, k[:, :, :1])
+    np.testing.assert_allclose(s_rep, 3 * s_one, rtol=1e-14, atol=0)
+
+
+def test_diagonal_score_against_saliency_closed_form():
+    """With a window of two tokens and every query orthogonal to the previous key, the
+    saliency is -log(1 - p_ii) = softplus(a_ii - 0): a monotone function of the diagonal
+    logit, so the two scores agree through that closed form (and route alike)."""
+    T, D = 65, 2
+    x, y = _rand(T), _rand(T)
+    q = np.zeros((1, T, 1, D))
+    k = np.zeros((1, T, 1, D))
+    for i in range(T):  # token i lives in dimension i % 2 only
+        q[0, i, 0, i % 2] = 3.0 * x[i]
+        k[0, i, 0, i % 2] = y[i]
+    s, _ = O.saliency(q, k, 2)
+    d, _ = O.diagonal_score(q, k)
+    np.testing.assert_allclose(s[0, 0, 1:], np.logaddexp(0.0, d[0, 0, 1:]), rtol=1e-12, atol=1e-15)
+    assert math.isinf(s[0, 0, 0])  # a one-token window
+    # positions 1..64 as one chunk: both scores pick the same five
+    assert np.array_equal(O.route(s[:, :, 1:], 64, 5)[0], O.route(d[:, :, 1:], 64, 5)[0])
+
+
 # ----------------------------------------------------------------------------- routing
 
 def _brute_topk(seg, k):
