@@ -36,7 +36,10 @@ Readings taken where the pages are silent (each is exercised by a test):
     M = max over the softmax set (0 when that set is empty); o_i = 0 if the denominator is 0.
 
 Parity pins: every function here is pinned in tests/test_oracle_pins.py against closed
-forms, library routines (torch SDPA / ELU in fp64) and hand-derived cases.
+forms, library routines (torch SDPA / ELU in fp64) and hand-derived cases. The backward
+pass (attend_backward) is pinned against central finite differences of attend, against
+an exact identity of the gradients, and against torch SDPA's gradients where the layer
+reduces to causal softmax attention.
 """
 
 from __future__ import annotations
@@ -47,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "lse", "saliency", "route", "route_margins", "np_map", "sa_mask_row", "brute",
-    "brute_rows", "attend", "DecodeOracle",
+    "brute_rows", "attend", "attend_backward", "DecodeOracle",
 ]
 
 
@@ -361,6 +364,62 @@ def attend(q, k, v, w_phi, window: int, chunk: int, top_k: int, sel=None,
     if return_routing:
         return out, s_kv, sel
     return out
+
+
+# --------------------------------------------------------------------------------------
+# Backward pass with the routing held fixed  ([P1] section "Chunk-Wise并行+延迟选择" and
+# [P4] section Approach: the same chunked layer is used for training)
+# --------------------------------------------------------------------------------------
+
+def _np_map_t(x, w):
+    """NP-Map in torch fp64 (the same definition as np_map), for automatic differentiation."""
+    import torch
+    z = x @ w.T
+    m = torch.where(z > 0.0, z + 1.0, torch.exp(torch.clamp(z, max=0.0)))
+    return torch.linalg.vector_norm(x, dim=-1, keepdim=True) * m / torch.linalg.vector_norm(m, dim=-1, keepdim=True)
+
+
+def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
+    """Gradients of sum(out * dout) with respect to q, k, v and w_phi, for a fixed routing.
+
+    The routing sel [B,Hkv,T] (bool) is an input: it is piecewise constant in q and k, so
+    it contributes no gradient. The layer is written in its dense form (the SA and LA masks
+    of every (i, j) pair, as in brute) with plain torch fp64 ops, and torch's reverse-mode
+    differentiation takes the chain rule through the shared normaliser, both branches and
+    the NP-Map. Rows whose normaliser is 0 have out = 0 and contribute nothing.
+    Returns (dq, dk, dv, dw_phi) as fp64 arrays shaped like q, k, v and w_phi.
+    """
+    import torch
+    _check_cfg(window, chunk, 0)
+    qt, kt, vt, wt = (torch.tensor(_f64(x), requires_grad=True) for x in (q, k, v, w_phi))
+    do = torch.tensor(_f64(dout))
+    B, T, Hq, D = qt.shape
+    G = _check_group(Hq, kt.shape[2])
+    sel = torch.tensor(np.asarray(sel, dtype=bool))
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    causal = j <= i
+    in_window = j > i - window
+    earlier_chunk = (j // chunk) < (i // chunk)
+    loss = torch.zeros((), dtype=torch.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            sa = causal & (in_window | (earlier_chunk & sel[b, h][None, :]))
+            la = causal & ~sa
+            qq, kk, vv = qt[b, :, hq], kt[b, :, h], vt[b, :, h]
+            a = torch.where(sa, qq @ kk.T / math.sqrt(D), -math.inf)
+            M = a.detach().amax(dim=1, keepdim=True)
+            M = torch.where(torch.isfinite(M), M, torch.zeros_like(M))
+            e_sa = torch.exp(a - M)
+            lw = torch.where(la, _np_map_t(qq, wt[h]) @ _np_map_t(kk, wt[h]).T, 0.0) * torch.exp(-M)
+            wgt = e_sa + lw
+            den = wgt.sum(dim=1, keepdim=True)
+            safe = den > 0.0
+            o = torch.where(safe, (wgt @ vv) / torch.where(safe, den, torch.ones_like(den)), 0.0)
+            loss = loss + (o * do[b, :, hq]).sum()
+    loss.backward()
+    return tuple(t.grad.numpy() for t in (qt, kt, vt, wt))
 
 
 # --------------------------------------------------------------------------------------

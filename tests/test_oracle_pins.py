@@ -355,3 +355,75 @@ def test_decode_replay_equals_prefill(T, w, C, k, G):
         got_idx = np.stack(dec.sel_idx, axis=2) if dec.sel_idx else np.zeros((2, 1, 0, k))
         want_idx = O.route(s_kv, C, k)[0]
         assert np.array_equal(got_idx, want_idx)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _fixed_routing(q, k, w, C, top_k, B, Hkv, T):
+    if top_k == 0:
+        return np.zeros((B, Hkv, T), dtype=bool)
+    s_kv, _ = O.saliency(q, k, w)
+    return O.route(s_kv, C, top_k)[1]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,w,C,k", [(37, 2, 1, 8, 8, 2), (20, 2, 2, 0, 8, 0), (30, 4, 2, 3, 8, 3),
+                                            (26, 2, 1, 8, 8, 8)])
+def test_backward_matches_finite_differences(T, Hq, Hkv, w, C, k):
+    """attend_backward (torch reverse mode over the dense form) against central differences
+    of attend (the chunked NumPy form) at random coordinates of every input."""
+    q, k_, v, wp = _case(1, T, Hq, Hkv, 8, 6, seed=T + w, scale=1.5)
+    sel = _fixed_routing(q, k_, w, C, k, 1, Hkv, T)
+    dout = np.random.default_rng(T).standard_normal(q.shape)
+    grads = O.attend_backward(q, k_, v, wp, w, C, sel, dout)
+    inputs = [q, k_, v, wp]
+    rng = np.random.default_rng(w + 100 * k)
+    h = 1e-5
+
+    def loss(xs):
+        return float(np.sum(O.attend(*xs, w, C, k, sel=sel) * dout))
+
+    for t, (x, g) in enumerate(zip(inputs, grads)):
+        assert g.shape == x.shape
+        for _ in range(6):
+            idx = tuple(int(rng.integers(n)) for n in x.shape)
+            plus = [a.copy() for a in inputs]
+            minus = [a.copy() for a in inputs]
+            plus[t][idx] += h
+            minus[t][idx] -= h
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-7 * (1.0 + abs(fd)), (t, idx, fd, g[idx])
+
+
+def test_backward_value_gradients_sum_to_output_gradients():
+    """Every row's weights sum to 1, so the value gradients of a KV head sum (over
+    positions) to the output gradients of its query heads, exactly."""
+    T, Hq, Hkv, w, C, k = 45, 4, 2, 8, 8, 2
+    q, k_, v, wp = _case(2, T, Hq, Hkv, 8, 6, seed=5, scale=1.5)
+    sel = _fixed_routing(q, k_, w, C, k, 2, Hkv, T)
+    dout = np.random.default_rng(1).standard_normal(q.shape)
+    _, _, dv, _ = O.attend_backward(q, k_, v, wp, w, C, sel, dout)
+    G = Hq // Hkv
+    want = dout.reshape(2, T, Hkv, G, 8).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), want, rtol=0, atol=1e-10)
+
+
+def test_backward_reduces_to_causal_softmax_gradients():
+    """With window = chunk = top_k every past token is in the softmax set: the gradients are
+    those of causal softmax attention (torch SDPA, fp64), and the NP-Map gets none."""
+    T, Hq, Hkv, C = 29, 4, 2, 8
+    q, k_, v, wp = _case(1, T, Hq, Hkv, 8, 6, seed=8, scale=1.5)
+    sel = np.ones((1, Hkv, T), dtype=bool)
+    dout = np.random.default_rng(2).standard_normal(q.shape)
+    dq, dk, dv, dw = O.attend_backward(q, k_, v, wp, C, C, sel, dout)
+    G = Hq // Hkv
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k_, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.repeat_interleave(G, dim=2).permute(0, 2, 1, 3),
+        tv.repeat_interleave(G, dim=2).permute(0, 2, 1, 3), is_causal=True)
+    (o.permute(0, 2, 1, 3) * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.all(dw == 0.0)
