@@ -212,6 +212,39 @@ int still_decode_step_timed(const still_config* cfg, still_cache* cache, const v
                             void* workspace, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t* events);
 
+/* Bytes of scratch still_backward needs for `cfg` (0 if cfg is invalid or unsupported). */
+size_t still_backward_workspace_bytes(const still_config* cfg);
+
+/* Backward pass of one layer with the routing held fixed: the gradients of sum(out * dout)
+ * ([P1] section "Chunk-Wise并行+延迟选择" and [P4] section Approach: the chunked layer is
+ * also the training form). The routing is piecewise constant in q and k, so it carries no
+ * gradient; it is passed in as the selection the forward pass made.
+ *   q, k, v, w_phi  as still_prefill (dtype)
+ *   out      [batch, seq_len, n_q_heads, head_dim] dtype: the forward output for these inputs
+ *            and this routing (it gives Delta_i = dout_i . out_i)
+ *   dout     [batch, seq_len, n_q_heads, head_dim] dtype
+ *   sel_idx  [batch, n_kv_heads, seq_len/chunk, top_k] int32, ascending positions inside their
+ *            chunk, as still_prefill's sel_idx_out writes them (may be null if top_k = 0 or
+ *            seq_len < chunk)
+ *   dq       like q; dk, dv like k (dtype, written)
+ *   dw_phi   [n_kv_heads, feat_dim, head_dim] fp32 (written, not accumulated)
+ *   workspace  device scratch of at least still_backward_workspace_bytes(cfg) bytes.
+ * Supported for head_dim = feat_dim = 64 (STILL_ERR_UNSUPPORTED otherwise). Every sum runs in
+ * a fixed order, so repeated calls give identical bits. Rows whose normaliser is 0 (output
+ * 0) get no gradient. Returns STILL_OK or a negative status. */
+int still_backward(const still_config* cfg, const void* q, const void* k, const void* v,
+                   const void* w_phi, const void* out, const void* dout, const int32_t* sel_idx,
+                   void* dq, void* dk, void* dv, float* dw_phi, void* workspace, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* still_backward with timing events: if `events` is non-null it must hold 8 events created by
+ * the caller, recorded before each of the seven stages (key preparation, linear-attention state
+ * scan, dq, reverse state scan, selected keys, local keys, dW reduction) and after the last. */
+int still_backward_timed(const still_config* cfg, const void* q, const void* k, const void* v,
+                         const void* w_phi, const void* out, const void* dout, const int32_t* sel_idx,
+                         void* dq, void* dk, void* dv, float* dw_phi, void* workspace, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/still.h"
 #include "still_launch.hpp"
 
@@ -157,6 +159,58 @@ still::CacheView view_of(const still_cache* c) {
 size_t decode_ws_bytes(const still_config* c) {
   const size_t recs = static_cast<size_t>(c->batch) * c->n_kv_heads * kMaxSplit * (c->n_q_heads / c->n_kv_heads);
   return align_up(recs * 2 * sizeof(float)) + align_up(recs * c->head_dim * sizeof(float));
+}
+
+// ---- backward workspace
+struct BwdLayout {
+  size_t kt, phik, phikt, ustate, ksel, vsel, kselt, qt, dot, phiq, phiqt, ld, apart, rstate, dwq, dwk, dkvsel,
+      dwpart, total;
+  int ntiles, nsplit, dw_parts;
+};
+
+int check_bwd_cfg(const still_config* c) {
+  const int st = check_cfg(c, true);
+  if (st != STILL_OK) return st;
+  if (c->head_dim != 64 || c->feat_dim != 64) return STILL_ERR_UNSUPPORTED;
+  return STILL_OK;
+}
+
+BwdLayout bwd_layout(const still_config* c) {
+  const Dims d = dims_of(c);
+  const size_t bh = static_cast<size_t>(d.B) * d.Hkv, bhq = static_cast<size_t>(d.B) * d.Hq;
+  const size_t es = elem_bytes(c), nC = d.nC, D = d.D, F = d.DF, R = d.R;
+  BwdLayout L;
+  L.ntiles = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
+  const int64_t far_wgs = static_cast<int64_t>(L.ntiles) * d.B * d.Hkv;
+  L.nsplit = far_wgs > 0 ? static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, (2048 + far_wgs - 1) / far_wgs))) : 1;
+  const int64_t items = static_cast<int64_t>(d.B) * (d.G + 1) * d.nC;
+  L.dw_parts = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, items / 16)));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.kt = take(bh * nC * 64 * D * es);
+  L.phik = take(bh * nC * 64 * F * es);
+  L.phikt = take(bh * nC * 64 * F * es);
+  L.ustate = take(bh * nC * R * 4);
+  L.ksel = take(bh * L.ntiles * 64 * D * es);
+  L.vsel = take(bh * L.ntiles * 64 * D * es);
+  L.kselt = take(bh * L.ntiles * 64 * D * es);
+  L.qt = take(bhq * nC * 64 * D * es);
+  L.dot = take(bhq * nC * 64 * D * es);
+  L.phiq = take(bhq * nC * 64 * F * es);
+  L.phiqt = take(bhq * nC * 64 * F * es);
+  L.ld = take(bhq * nC * 64 * 2 * 4);
+  L.apart = take(bhq * nC * R * 4);
+  L.rstate = take(bh * nC * R * 4);
+  L.dwq = take(bhq * nC * F * D * 4);
+  L.dwk = take(bh * nC * F * D * 4);
+  L.dkvsel = take(static_cast<size_t>(L.nsplit) * bh * L.ntiles * 64 * 2 * D * 4);
+  L.dwpart = take(static_cast<size_t>(L.dw_parts) * d.Hkv * F * D * 4);
+  L.total = off;
+  return L;
 }
 
 }  // namespace
@@ -383,6 +437,71 @@ int still_decode_step(const still_config* cfg, still_cache* cache, const void* q
                       const void* v, const void* w_phi, void* out, void* workspace,
                       size_t ws_bytes, hipStream_t stream) {
   return still_decode_step_timed(cfg, cache, q, k, v, w_phi, out, workspace, ws_bytes, stream, nullptr);
+}
+
+size_t still_backward_workspace_bytes(const still_config* cfg) {
+  if (check_bwd_cfg(cfg) != STILL_OK) return 0;
+  return bwd_layout(cfg).total;
+}
+
+int still_backward_timed(const still_config* cfg, const void* q, const void* k, const void* v,
+                         const void* w_phi, const void* out, const void* dout, const int32_t* sel_idx,
+                         void* dq, void* dk, void* dv, float* dw_phi, void* workspace, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t* events) {
+  const int st = check_bwd_cfg(cfg);
+  if (st != STILL_OK) return st;
+  if (!q || !k || !v || !w_phi || !out || !dout || !dq || !dk || !dv || !dw_phi || !workspace)
+    return STILL_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, w_phi, out, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv), static_cast<const void*>(dw_phi),
+                        static_cast<const void*>(workspace)})
+    if (!aligned(p, 16)) return STILL_ERR_INVALID_ARG;
+  if (cfg->top_k > 0 && cfg->seq_len >= 64 && (!sel_idx || !aligned(sel_idx, 4))) return STILL_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(cfg);
+  if (ws_bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  still::BwdArgs a;
+  a.d = dims_of(cfg);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.w = w_phi;
+  a.out = out;
+  a.dout = dout;
+  a.sel_idx = sel_idx;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = dw_phi;
+  a.kt = ws + L.kt;
+  a.phik = ws + L.phik;
+  a.phikt = ws + L.phikt;
+  a.ustate = reinterpret_cast<float*>(ws + L.ustate);
+  a.ksel = ws + L.ksel;
+  a.vsel = ws + L.vsel;
+  a.kselt = ws + L.kselt;
+  a.qt = ws + L.qt;
+  a.dot = ws + L.dot;
+  a.phiq = ws + L.phiq;
+  a.phiqt = ws + L.phiqt;
+  a.ld = reinterpret_cast<float*>(ws + L.ld);
+  a.apart = reinterpret_cast<float*>(ws + L.apart);
+  a.rstate = reinterpret_cast<float*>(ws + L.rstate);
+  a.dwq = reinterpret_cast<float*>(ws + L.dwq);
+  a.dwk = reinterpret_cast<float*>(ws + L.dwk);
+  a.dkvsel = reinterpret_cast<float*>(ws + L.dkvsel);
+  a.dwpart = reinterpret_cast<float*>(ws + L.dwpart);
+  a.ntiles = L.ntiles;
+  a.nsplit = L.nsplit;
+  a.dw_parts = L.dw_parts;
+  return still::launch_bwd(a, stream, events) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+}
+
+int still_backward(const still_config* cfg, const void* q, const void* k, const void* v, const void* w_phi,
+                   const void* out, const void* dout, const int32_t* sel_idx, void* dq, void* dk, void* dv,
+                   float* dw_phi, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return still_backward_timed(cfg, q, k, v, w_phi, out, dout, sel_idx, dq, dk, dv, dw_phi, workspace, ws_bytes,
+                              stream, nullptr);
 }
 
 }  // extern "C"

@@ -1,0 +1,940 @@
+// Backward pass of the STILL layer with the routing held fixed: the gradients of
+// sum(out * dout) with respect to q, k, v and the NP-Map weights.
+// (Page labels [P1]..[P4]: the pages listed at the top of include/still.h. [P1] section
+// "Chunk-Wise并行+延迟选择" and [P4] section Approach use the same chunked layer for
+// training, which is what these kernels differentiate.)
+//
+// With den_i the shared normaliser of query i (softmax terms e^{a_ij} of its SA keys plus
+// the linear-attention weights phi(q_i).phi(k_j) of its LA keys), L_i = log den_i, and
+// Delta_i = dout_i . out_i:
+//   SA pair:  P_ij = e^{a_ij - L_i};  dS_ij = P_ij (dout_i.v_j - Delta_i)
+//             dq_i += dS_ij k_j / sqrt(D),  dk_j += dS_ij q_i / sqrt(D),  dv_j += P_ij dout_i
+//   LA pair:  g_ij = (dout_i.v_j - Delta_i) e^{-L_i}
+//             dphi(q_i) += g_ij phi(k_j),  dphi(k_j) += g_ij phi(q_i),
+//             dv_j += e^{-L_i} (phi(q_i).phi(k_j)) dout_i
+// LA keys of chunks <= c-2 enter through states: S_c = sum phi(k) v^T and z_c = sum phi(k)
+// over their unselected keys for the queries of chunk c, and, for the keys of chunk c,
+// R_c = sum e^{-L} phi(q) dout^T and r_c = sum e^{-L} Delta phi(q) over the queries of
+// chunks >= c+2. NP-Map phi(x) = |x| m / |m|, m = elu(W x) + 1, is differentiated row by
+// row: with m^ = m / |m| and dr = dphi . m^, dm = |x| (dphi - m^ dr) / |m|,
+// dz = dm * elu'(Wx), dx = W^T dz + dr x / |x|, dW += dz x^T.
+//
+// Launch order (one stream):
+//   bwd_kprep_kernel     per (chunk, KV head, batch): phi(k), K^T, U_c / u_c, compact rows
+//   bwd_scan_fwd_kernel  U_c -> S_c (sum over chunks <= c-2), in place
+//   bwd_dq_kernel        per (chunk, query head, batch): L_i (first pass over the keys),
+//                        dq (second pass), the per-chunk sums behind R, the q side of dW
+//   bwd_scan_rev_kernel  R_c = sum over chunks >= c+2 and over the query group
+//   bwd_dkv_far_kernel   per (compact tile, query split, KV head): the selected keys
+//                        against the queries of chunks >= their chunk + 2
+//   bwd_dkv_local_kernel per (chunk, KV head, batch): keys against the queries of their
+//                        own chunk and the next; R_c; the NP-Map backward; dk, dv
+//   bwd_dw_part_kernel / bwd_dw_sum_kernel: dW summed over chunks, heads and batch
+//
+// Supported: head_dim = feat_dim = 64, chunk 64, fp32 or bf16. Matrix products run on
+// MFMA in the layer's dtype with fp32 accumulation; every sum that crosses workgroups
+// goes through fp32 buffers in a fixed order, so the result is deterministic.
+#include "still_launch.hpp"
+#include "still_layout.hpp"
+#include "still_route.hpp"
+
+namespace still {
+
+namespace {
+
+constexpr int BD = 64;   // head_dim
+constexpr int BF = 64;   // feat_dim
+constexpr int BR = BF * BD + BF;
+
+// index k (0..63) stored at position p = pk_pos(k) of a pk-permuted 64-vector
+__device__ __forceinline__ int pk_index(int p) {
+  const int s = p & ~31, q = p & 31, g = q >> 3, e = q & 7;
+  return s + 16 * (e >> 2) + 4 * g + (e & 3);
+}
+
+// Operand fragment from two accumulators (the PK assignment of still_common.hpp): the
+// elements 0..3 come from the block of rows 32s..32s+15, 4..7 from rows 32s+16..32s+31.
+template <typename T>
+__device__ __forceinline__ typename Tr<T>::frag pk_frag(const f32x4& lo, const f32x4& hi) {
+  typename Tr<T>::frag f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = Tr<T>::from_f(lo[e]);
+    f[4 + e] = Tr<T>::from_f(hi[e]);
+  }
+  return f;
+}
+
+// eight consecutive fp32 values as an operand fragment of dtype T
+template <typename T>
+__device__ __forceinline__ typename Tr<T>::frag f32_frag(const float* p) {
+  return pk_frag<T>(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4));
+}
+
+// 64 rows of 64 elements from memory (row stride `stride` elements) into a Swz<T, 64> LDS
+// tile; rows at or beyond nvalid are zero. All 256 threads call.
+template <typename T>
+__device__ __forceinline__ void tile_load(T* lds, const T* g, long long stride, int nvalid) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = static_cast<int>(threadIdx.x) + it * 256;
+    const int row = idx >> 3, col = (idx & 7) * 8;
+    const typename Tr<T>::frag x = row < nvalid ? Tr<T>::load8(g + row * stride + col) : Tr<T>::zero();
+    Swz<T, 64>::store8(lds, row, col, x);
+  }
+}
+
+// acc[blk] = tile rows blk*16 + r16 (k = the 64 columns, straight) times the B fragments
+template <typename T>
+__device__ __forceinline__ void rows_x_frag(f32x4 (&acc)[4], const T* tile, const typename Tr<T>::frag (&bf)[2]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, ks * 32 + grp * 8), bf[ks]);
+  }
+}
+
+// acc[blk] += tile rows blk*16 + r16 (k = 64 pk-permuted positions) times the PK operand
+// built from the accumulators v[0..3] (rows 0..63 of a previous product)
+template <typename T>
+__device__ __forceinline__ void rows_x_acc(f32x4 (&acc)[4], const T* tile, const f32x4 (&v)[4]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const typename Tr<T>::frag b0 = pk_frag<T>(v[0], v[1]);
+  const typename Tr<T>::frag b1 = pk_frag<T>(v[2], v[3]);
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, grp * 8), b0);
+    Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, 32 + grp * 8), b1);
+  }
+}
+
+// acc[blk] += rows blk*16 + r16 of a row-major fp32 [64][64] matrix in memory (k = the 64
+// columns, straight) times the B fragments
+template <typename T>
+__device__ __forceinline__ void f32rows_x_frag(f32x4 (&acc)[4], const float* m, const typename Tr<T>::frag (&bf)[2]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(acc[blk], f32_frag<T>(m + (blk * 16 + r16) * 64 + ks * 32 + grp * 8), bf[ks]);
+}
+
+// One 64x64 output of a workgroup-wide product over 64 pk-permuted positions:
+// out[row][col] = sum_p A[row][p] B[col][p], A and B Swz<T, 64> tiles. Wave w computes rows
+// 16w..16w+15; returns acc[cb][i] = out[16w + 4grp + i][16cb + r16].
+template <typename T>
+__device__ __forceinline__ void tile_x_tile(f32x4 (&acc)[4], const T* A, const T* B) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      Tr<T>::mma(acc[cb], Swz<T, 64>::load8(A, wave * 16 + r16, ks * 32 + grp * 8),
+                 Swz<T, 64>::load8(B, cb * 16 + r16, ks * 32 + grp * 8));
+  }
+}
+
+// NP-Map forward of one row per lane column, for the row held as B fragments xf (SK):
+// z[blk][i] = (W x)[16 blk + 4 grp + i]; also m = elu(z) + 1, |x| and 1/|m|.
+struct NpRow {
+  f32x4 z[4];
+  f32x4 m[4];
+  float r, inv_nm;
+};
+
+template <typename T>
+__device__ __forceinline__ void np_forward(NpRow& n, const T* W, const typename Tr<T>::frag (&xf)[2]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    n.z[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(n.z[fb], Tr<T>::load8(W + (fb * 16 + r16) * BD + ks * 32 + grp * 8), xf[ks]);
+  }
+  float nm2 = 0.f, xn2 = 0.f;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float zv = n.z[fb][i];
+      const float mv = zv > 0.f ? zv + 1.f : exp2f(zv * kLog2e);
+      n.m[fb][i] = mv;
+      nm2 += mv * mv;
+    }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = Tr<T>::to_f(xf[ks][e]);
+      xn2 += x * x;
+    }
+  nm2 = xor_sum_groups(nm2);
+  xn2 = xor_sum_groups(xn2);
+  n.r = sqrtf(xn2);
+  n.inv_nm = 1.0f / sqrtf(nm2);
+}
+
+// NP-Map backward for the same row: dphi[blk][i] (feature 16 blk + 4 grp + i) -> dz (in
+// place) and dr = dphi . m^. dx = W^T dz + dr x / |x| is formed by the caller.
+__device__ __forceinline__ float np_backward(const NpRow& n, f32x4 (&dphi)[4]) {
+  float dr = 0.f;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dr += dphi[fb][i] * n.m[fb][i];
+  dr = xor_sum_groups(dr) * n.inv_nm;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mh = n.m[fb][i] * n.inv_nm;
+      const float dm = n.r * (dphi[fb][i] - mh * dr) * n.inv_nm;
+      dphi[fb][i] = dm * (n.z[fb][i] > 0.f ? 1.f : n.m[fb][i]);
+    }
+  return dr;
+}
+
+// W^T with the features pk-permuted, [dim][pk_pos(f)], into an LDS tile
+template <typename T>
+__device__ __forceinline__ void load_wt(T* lds, const T* W) {
+  for (int e = threadIdx.x; e < BF * BD; e += 256) {
+    const int f = e >> 6, dd = e & 63;
+    lds[Swz<T, 64>::off(dd, pk_pos(f))] = W[e];
+  }
+}
+
+// selection bit mask of complete chunk c from the ascending positions (entries outside
+// the chunk are ignored); wave-uniform
+__device__ __forceinline__ uint64_t chunk_sel(const int32_t* sel_idx, long long bh, int c, const Dims& d) {
+  if (d.topk == 0 || c < 0 || c >= d.nCc) return 0ull;
+  const int32_t* p = sel_idx + (bh * d.nCc + c) * d.topk;
+  uint64_t m = 0;
+  for (int r = 0; r < d.topk; ++r) {
+    const int pos = p[r] - 64 * c;
+    if (pos >= 0 && pos < 64) m |= 1ull << pos;
+  }
+  return m;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
+  using TT = Tr<T>;
+  __shared__ __attribute__((aligned(16))) T t_k[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_v[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_vt[64 * 64];
+  __shared__ float m2part[4 * 64];
+  __shared__ float xn2[64];
+  const Dims& d = a.d;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long long bh = static_cast<long long>(b) * d.Hkv + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int nvalid = min(64, d.T - 64 * c);
+  const long long rs = static_cast<long long>(d.Hkv) * BD;
+  const long long row0 = (static_cast<long long>(b) * d.T + 64LL * c) * d.Hkv + h;
+  tile_load<T>(t_k, static_cast<const T*>(a.k) + row0 * BD, rs, nvalid);
+  tile_load<T>(t_v, static_cast<const T*>(a.v) + row0 * BD, rs, nvalid);
+  const uint64_t selm = chunk_sel(a.sel_idx, bh, c, d);
+  typename TT::frag wf[1][2];
+  np_map_load_w<T, 64, 64>(static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD, wf);
+  __syncthreads();
+  // V^T (keys pk-permuted) into LDS, K^T into memory
+  T* ktg = static_cast<T*>(a.kt) + (bh * d.nC + c) * (BD * 64);
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int dd = e >> 6, p = e & 63, row = pk_index(p);
+    t_vt[Swz<T, 64>::off(dd, p)] = t_v[Swz<T, 64>::off(row, dd)];
+    ktg[e] = t_k[Swz<T, 64>::off(row, dd)];
+  }
+  f32x4 phi[4][1];
+  np_map_rows64<T, 64, 64>(t_k, 0, wf, m2part, xn2, phi);  // synchronises the workgroup
+  const int f = wave * 16 + r16;
+  T* phk = static_cast<T*>(a.phik) + (bh * d.nC * 64 + 64LL * c) * BF;
+  T* phkt = static_cast<T*>(a.phikt) + (bh * d.nC + c) * (BF * 64);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) phk[(kb * 16 + 4 * grp + i) * BF + pk_pos(f)] = TT::from_f(phi[kb][0][i]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) TT::store8(phkt + f * 64 + 32 * s + 8 * grp, pk_frag<T>(phi[2 * s][0], phi[2 * s + 1][0]));
+  // U_c = sum over unselected keys of phi(k) v^T, u_c = sum phi(k)
+  f32x4 ph[4];
+  float zs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = kb * 16 + 4 * grp + i;
+      const bool la = row < nvalid && !((selm >> row) & 1ull);
+      ph[kb][i] = la ? phi[kb][0][i] : 0.f;
+      zs += ph[kb][i];
+    }
+  zs = xor_sum_groups(zs);
+  f32x4 u[4] = {};
+  rows_x_acc<T>(u, t_vt, ph);  // u[db][i] = U[f][16 db + 4 grp + i]
+  float* ust = a.ustate + (bh * d.nC + c) * BR;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4*>(ust + f * BD + db * 16 + 4 * grp) = u[db];
+  if (grp == 0) ust[BF * BD + f] = zs;
+  // the selected rows, in chunk order, into the compact buffers
+  if (c < d.nCc && d.topk > 0) {
+    const int32_t* sp = a.sel_idx + (bh * d.nCc + c) * d.topk;
+    T* ks = static_cast<T*>(a.ksel) + bh * a.ntiles * 64 * BD;
+    T* vs = static_cast<T*>(a.vsel) + bh * a.ntiles * 64 * BD;
+    T* kst = static_cast<T*>(a.kselt) + bh * a.ntiles * (BD * 64);
+    for (int e = tid; e < d.topk * 64; e += 256) {
+      const int r = e >> 6, dd = e & 63;
+      const int pos = sp[r] - 64 * c;
+      const bool ok = pos >= 0 && pos < 64;
+      const T kv = ok ? t_k[Swz<T, 64>::off(pos, dd)] : TT::from_f(0.f);
+      const T vv = ok ? t_v[Swz<T, 64>::off(pos, dd)] : TT::from_f(0.f);
+      const int n = c * d.topk + r;
+      ks[static_cast<long long>(n) * BD + dd] = kv;
+      vs[static_cast<long long>(n) * BD + dd] = vv;
+      kst[(static_cast<long long>(n >> 6) * BD + dd) * 64 + pk_pos(n & 63)] = kv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// U_c -> S_c = sum over chunks <= c-2, in place; one thread per (b, KV head, element)
+__global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, long long n_elems) {
+  const long long gid = blockIdx.x * 256LL + threadIdx.x;
+  if (gid >= n_elems) return;
+  const long long bh = gid / BR, e = gid % BR;
+  float* p = ust + bh * nC * BR + e;
+  float acc = 0.f, p1 = 0.f, p2 = 0.f;
+  for (int c = 0; c < nC; ++c) {
+    const float cur = p[static_cast<long long>(c) * BR];
+    acc += p2;
+    p[static_cast<long long>(c) * BR] = acc;
+    p2 = p1;
+    p1 = cur;
+  }
+}
+
+// R_c = sum over chunks >= c+2 of the group's per-chunk sums; one thread per (b, KV head, element)
+__global__ __launch_bounds__(256) void bwd_scan_rev_kernel(const float* apart, float* rst, int nC, int G, int Hkv,
+                                                           long long n_elems) {
+  const long long gid = blockIdx.x * 256LL + threadIdx.x;
+  if (gid >= n_elems) return;
+  const long long bh = gid / BR, e = gid % BR;
+  const long long b = bh / Hkv, h = bh % Hkv;
+  const long long hq0 = b * Hkv * G + h * G;
+  float acc = 0.f;
+  for (int c = nC - 1; c >= 0; --c) {
+    if (c + 2 <= nC - 1) {
+      float s = 0.f;
+      for (int g = 0; g < G; ++g) s += apart[((hq0 + g) * nC + c + 2) * BR + e];
+      acc += s;
+    }
+    rst[(bh * nC + c) * BR + e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  using SW = Swz<T, 64>;
+  __shared__ __attribute__((aligned(16))) T t_k[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_v[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_kt[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_pk[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_pkt[64 * 64];
+  __shared__ float s_red[4][64];
+
+  const Dims& d = a.d;
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int h = hq / d.G;
+  const long long bh = static_cast<long long>(b) * d.Hkv + h;
+  const long long bhq = static_cast<long long>(b) * d.Hq + hq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int qrow = wave * 16 + r16;
+  const long long i = 64LL * c + qrow;  // this lane column's query
+  const bool qvalid = i < d.T;
+  const float scale2 = kLog2e * 0.125f;  // log2(e) / sqrt(64)
+  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD;
+
+  // the query row, dout row and Delta = dout . out
+  const long long qoff = ((static_cast<long long>(b) * d.T + i) * d.Hq + hq) * BD;
+  frag qf[2], dof[2];
+  float delta = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    qf[ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qoff + ks * 32 + grp * 8) : TT::zero();
+    dof[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
+    const frag of = qvalid ? TT::load8(static_cast<const T*>(a.out) + qoff + ks * 32 + grp * 8) : TT::zero();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) delta += TT::to_f(dof[ks][e]) * TT::to_f(of[e]);
+  }
+  delta = xor_sum_groups(delta);
+
+  NpRow nq;
+  np_forward<T>(nq, W, qf);
+  f32x4 phq[4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+  const frag phf[2] = {pk_frag<T>(phq[0], phq[1]), pk_frag<T>(phq[2], phq[3])};
+
+  const uint64_t sel_prev = chunk_sel(a.sel_idx, bh, c - 1, d);
+  const int nsel_c = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
+  const T* ksel = static_cast<const T*>(a.ksel) + bh * a.ntiles * 64 * BD;
+  const T* vsel = static_cast<const T*>(a.vsel) + bh * a.ntiles * 64 * BD;
+  const T* kselt = static_cast<const T*>(a.kselt) + bh * a.ntiles * (BD * 64);
+  const float* st = a.ustate + (bh * d.nC + c) * BR;  // S_c, z_c
+  const long long krs = static_cast<long long>(d.Hkv) * BD;
+
+  // linear-attention state part of the normaliser
+  float dla = 0.f;
+  if (c >= 2) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dla += phq[fb][e] * st[BF * BD + fb * 16 + 4 * grp + e];
+  }
+
+  // ---- pass 1: L = log2 of the normaliser
+  float mx2 = -kInf, l = 0.f;
+  auto online = [&](const f32x4 (&a2)[4], const bool (&sa)[4][4]) {
+    float tm = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (sa[kb][e]) tm = fmaxf(tm, a2[kb][e]);
+    tm = xor_max_groups(tm);
+    const float mn = fmaxf(mx2, tm);
+    const bool any = mn != -kInf;  // the same in the four lanes of a query
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (sa[kb][e]) ps += exp2f(a2[kb][e] - mn);
+    ps = xor_sum_groups(ps);
+    l = any ? l * exp2f(mx2 - mn) + ps : l;
+    mx2 = mn;
+  };
+  for (int t = 0; t * 64 < nsel_c; ++t) {
+    __syncthreads();
+    tile_load<T>(t_k, ksel + static_cast<long long>(t) * 64 * BD, BD, min(64, nsel_c - t * 64));
+    __syncthreads();
+    f32x4 s[4];
+    rows_x_frag<T>(s, t_k, qf);
+    bool sa[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[kb][e] = t * 64 + kb * 16 + 4 * grp + e < nsel_c;
+        s[kb][e] *= scale2;
+      }
+    online(s, sa);
+  }
+  for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
+    __syncthreads();
+    const long long r0 = (static_cast<long long>(b) * d.T + 64LL * cc) * d.Hkv + h;
+    tile_load<T>(t_k, static_cast<const T*>(a.k) + r0 * BD, krs, min(64, d.T - 64 * cc));
+    tile_load<T>(t_pk, static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, BF, 64);
+    __syncthreads();
+    f32x4 s[4], lw[4];
+    rows_x_frag<T>(s, t_k, qf);
+    rows_x_frag<T>(lw, t_pk, phf);
+    bool sa[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jr = kb * 16 + 4 * grp + e;
+        const long long j = 64LL * cc + jr;
+        const bool vis = j <= i;
+        const bool inwin = i - j < d.window;
+        const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
+        sa[kb][e] = vis && (inwin || sel);
+        if (vis && !(inwin || sel)) dla += lw[kb][e];
+        s[kb][e] *= scale2;
+      }
+    online(s, sa);
+  }
+  dla = xor_sum_groups(dla);
+  float L2;
+  if (!qvalid) {
+    L2 = kInf;
+  } else if (l > 0.f && dla > 0.f) {
+    const float ld = log2f(dla);
+    const float M = fmaxf(mx2, ld);
+    L2 = M + log2f(l * exp2f(mx2 - M) + exp2f(ld - M));
+  } else if (l > 0.f) {
+    L2 = mx2 + log2f(l);
+  } else {
+    L2 = dla > 0.f ? log2f(dla) : kInf;  // an empty normaliser: out = 0, no gradient
+  }
+  const float einv = exp2f(-L2);
+
+  // ---- pass 2: dq (softmax part) and dphi(q)
+  f32x4 dqt[4] = {}, dpt[4] = {};
+  for (int t = 0; t * 64 < nsel_c; ++t) {
+    __syncthreads();
+    const int nv = min(64, nsel_c - t * 64);
+    tile_load<T>(t_k, ksel + static_cast<long long>(t) * 64 * BD, BD, nv);
+    tile_load<T>(t_v, vsel + static_cast<long long>(t) * 64 * BD, BD, nv);
+    tile_load<T>(t_kt, kselt + static_cast<long long>(t) * BD * 64, 64, 64);
+    __syncthreads();
+    f32x4 s[4], dp[4];
+    rows_x_frag<T>(s, t_k, qf);
+    rows_x_frag<T>(dp, t_v, dof);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = kb * 16 + 4 * grp + e < nv;
+        const float p = ok ? exp2f(s[kb][e] * scale2 - L2) : 0.f;
+        s[kb][e] = p * (dp[kb][e] - delta);
+      }
+    rows_x_acc<T>(dqt, t_kt, s);
+  }
+  for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
+    __syncthreads();
+    const long long r0 = (static_cast<long long>(b) * d.T + 64LL * cc) * d.Hkv + h;
+    const int nv = min(64, d.T - 64 * cc);
+    tile_load<T>(t_k, static_cast<const T*>(a.k) + r0 * BD, krs, nv);
+    tile_load<T>(t_v, static_cast<const T*>(a.v) + r0 * BD, krs, nv);
+    tile_load<T>(t_kt, static_cast<const T*>(a.kt) + (bh * d.nC + cc) * BD * 64, 64, 64);
+    tile_load<T>(t_pk, static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, BF, 64);
+    tile_load<T>(t_pkt, static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * BF * 64, 64, 64);
+    __syncthreads();
+    f32x4 s[4], dp[4], lw[4];
+    rows_x_frag<T>(s, t_k, qf);
+    rows_x_frag<T>(dp, t_v, dof);
+    rows_x_frag<T>(lw, t_pk, phf);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jr = kb * 16 + 4 * grp + e;
+        const long long j = 64LL * cc + jr;
+        const bool vis = j <= i;
+        const bool inwin = i - j < d.window;
+        const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
+        const bool sa = vis && (inwin || sel);
+        const bool la = vis && !(inwin || sel);
+        const float p = sa ? exp2f(s[kb][e] * scale2 - L2) : 0.f;
+        const float g = dp[kb][e] - delta;
+        s[kb][e] = p * g;
+        lw[kb][e] = la ? g * einv : 0.f;
+      }
+    rows_x_acc<T>(dqt, t_kt, s);
+    rows_x_acc<T>(dpt, t_pkt, lw);
+  }
+  if (c >= 2) {
+    // dphi(q) += e^{-L} (S_c dout - Delta z_c)
+    f32x4 sdo[4] = {};
+    f32rows_x_frag<T>(sdo, st, dof);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dpt[fb][e] += einv * (sdo[fb][e] - delta * st[BF * BD + fb * 16 + 4 * grp + e]);
+  }
+
+  // ---- NP-Map backward and dq
+  const float dr = np_backward(nq, dpt);  // dpt now holds dz
+  __syncthreads();
+  load_wt<T>(t_k, W);
+  __syncthreads();
+  f32x4 dxt[4] = {};
+  rows_x_acc<T>(dxt, t_k, dpt);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
+  if (qvalid) {
+    T* dq = static_cast<T*>(a.dq) + qoff;
+    const T* xq = static_cast<const T*>(a.q) + qoff;
+    const float xs = nq.r > 0.f ? dr / nq.r : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const typename TT::quad x4 = TT::load4(xq + db * 16 + 4 * grp);
+      typename TT::quad o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = TT::from_f(dqt[db][e] * 0.125f + dxt[db][e] + xs * TT::to_f(x4[e]));
+      *reinterpret_cast<typename TT::quad*>(dq + db * 16 + 4 * grp) = o4;
+    }
+  }
+
+  // ---- what the key side needs: (L, Delta), phi(q) rows and transposed, q^T, dout^T
+  const long long qc = bhq * d.nC + c;
+  if (grp == 0) {
+    a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2] = L2;
+    a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta : 0.f;
+  }
+  T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * BF;
+  TT::store8(phqr + 8 * grp, phf[0]);
+  TT::store8(phqr + 32 + 8 * grp, phf[1]);
+  T* phqt = static_cast<T*>(a.phiqt) + qc * BF * 64;
+  T* qt = static_cast<T*>(a.qt) + qc * BD * 64;
+  T* dot = static_cast<T*>(a.dot) + qc * BD * 64;
+  const int pq = pk_pos(qrow);
+  __syncthreads();  // t_k (W^T) is reused below
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = fb * 16 + 4 * grp + e;
+      phqt[f * 64 + pq] = TT::from_f(phq[fb][e]);
+      t_k[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);  // e^{-L} phi(q)^T
+      t_pk[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);        // dz^T
+    }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dd = ks * 32 + grp * 8 + e;
+      qt[dd * 64 + pq] = qf[ks][e];
+      dot[dd * 64 + pq] = dof[ks][e];
+      t_v[SW::off(dd, pq)] = dof[ks][e];
+      t_kt[SW::off(dd, pq)] = qf[ks][e];
+    }
+  // a_c partial: sum over the workgroup's queries of e^{-L} Delta phi(q)
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta : 0.f));
+      if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
+    }
+  __syncthreads();
+  float* ap = a.apart + qc * BR;
+  if (tid < 64) ap[BF * BD + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+  f32x4 acc[4];
+  tile_x_tile<T>(acc, t_k, t_v);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ap[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+  tile_x_tile<T>(acc, t_pk, t_kt);  // dW[f][d] = sum_q dz[f] q[d]
+  float* wp = a.dwq + qc * (BF * BD);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wp[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+}
+
+// ---------------------------------------------------------------------------------------
+// Selected keys of compact tile `tile` against the queries of chunks >= their chunk + 2,
+// split over blockIdx.y; writes fp32 partial dk, dv (softmax part, before the 1/sqrt(D) of dk).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dkv_far_kernel(BwdArgs a) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  __shared__ __attribute__((aligned(16))) T t_q[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_do[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_qt[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_dot[64 * 64];
+  __shared__ float s_ld[64 * 2];
+  const Dims& d = a.d;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const long long bh = blockIdx.z;
+  const int b = static_cast<int>(bh / d.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const float scale2 = kLog2e * 0.125f;
+  const int nsel = d.nCc * d.topk;
+  const int n = tile * 64 + wave * 16 + r16;  // this lane column's compact row
+  const bool kvalid = n < nsel;
+  const int ckey = kvalid ? n / d.topk : 0x3fffffff;
+  frag kf[2], vf[2];
+  const T* ksel = static_cast<const T*>(a.ksel) + (bh * a.ntiles * 64 + n) * BD;
+  const T* vsel = static_cast<const T*>(a.vsel) + (bh * a.ntiles * 64 + n) * BD;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    kf[ks] = TT::load8(ksel + ks * 32 + grp * 8);
+    vf[ks] = TT::load8(vsel + ks * 32 + grp * 8);
+  }
+  // query chunks [c_lo, nC) split evenly over gridDim.y
+  const int c_lo = (tile * 64) / d.topk + 2;
+  const int span = max(0, d.nC - c_lo);
+  const int per = (span + gridDim.y - 1) / gridDim.y;
+  const int cb0 = c_lo + split * per, cb1 = min(d.nC, cb0 + per);
+  f32x4 dkt[4] = {}, dvt[4] = {};
+  for (int cq = cb0; cq < cb1; ++cq) {
+    for (int g = 0; g < d.G; ++g) {
+      const long long hq = static_cast<long long>(b) * d.Hq + (bh % d.Hkv) * d.G + g;  // b*Hq + hq
+      const long long qc = hq * d.nC + cq;
+      const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (hq - static_cast<long long>(b) * d.Hq)) * BD;
+      const int nv = min(64, d.T - 64 * cq);
+      __syncthreads();
+      tile_load<T>(t_q, static_cast<const T*>(a.q) + r0, static_cast<long long>(d.Hq) * BD, nv);
+      tile_load<T>(t_do, static_cast<const T*>(a.dout) + r0, static_cast<long long>(d.Hq) * BD, nv);
+      tile_load<T>(t_qt, static_cast<const T*>(a.qt) + qc * BD * 64, 64, 64);
+      tile_load<T>(t_dot, static_cast<const T*>(a.dot) + qc * BD * 64, 64, 64);
+      if (tid < 128) s_ld[tid] = a.ld[(hq * d.nC * 64 + 64LL * cq) * 2 + tid];
+      __syncthreads();
+      f32x4 s[4], dp[4];
+      rows_x_frag<T>(s, t_q, kf);   // s[qb][e] = q[16 qb + 4 grp + e] . k
+      rows_x_frag<T>(dp, t_do, vf);
+      const bool on = cq >= ckey + 2;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qr = qb * 16 + 4 * grp + e;
+          const float p = on ? exp2f(s[qb][e] * scale2 - s_ld[2 * qr]) : 0.f;
+          s[qb][e] = p * (dp[qb][e] - s_ld[2 * qr + 1]);
+          dp[qb][e] = p;
+        }
+      rows_x_acc<T>(dvt, t_dot, dp);
+      rows_x_acc<T>(dkt, t_qt, s);
+    }
+  }
+  float* out = a.dkvsel + ((static_cast<long long>(split) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    *reinterpret_cast<f32x4*>(out + db * 16 + 4 * grp) = dkt[db];
+    *reinterpret_cast<f32x4*>(out + BD + db * 16 + 4 * grp) = dvt[db];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  using SW = Swz<T, 64>;
+  __shared__ __attribute__((aligned(16))) T t_q[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_do[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_qt[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_dot[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_pq[64 * 64];
+  __shared__ __attribute__((aligned(16))) T t_pqt[64 * 64];
+  __shared__ float s_ld[64 * 2];
+  const Dims& d = a.d;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long long bh = static_cast<long long>(b) * d.Hkv + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const float scale2 = kLog2e * 0.125f;
+  const int jr = wave * 16 + r16;
+  const long long j = 64LL * c + jr;  // this lane column's key
+  const bool kvalid = j < d.T;
+  const uint64_t selm = chunk_sel(a.sel_idx, bh, c, d);
+  const bool selj = (selm >> jr) & 1ull;
+  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD;
+  const long long koff = ((static_cast<long long>(b) * d.T + j) * d.Hkv + h) * BD;
+  frag kf[2], vf[2], phk[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    kf[ks] = kvalid ? TT::load8(static_cast<const T*>(a.k) + koff + ks * 32 + grp * 8) : TT::zero();
+    vf[ks] = kvalid ? TT::load8(static_cast<const T*>(a.v) + koff + ks * 32 + grp * 8) : TT::zero();
+    phk[ks] = TT::load8(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + j) * BF + ks * 32 + grp * 8);
+  }
+  f32x4 dkt[4] = {}, dvt[4] = {}, dpk[4] = {};
+  for (int g = 0; g < d.G; ++g) {
+    const long long hq = static_cast<long long>(b) * d.Hq + h * d.G + g;  // b*Hq + query head
+    for (int cq = c; cq <= c + 1 && cq < d.nC; ++cq) {
+      const long long qc = hq * d.nC + cq;
+      const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (h * d.G + g)) * BD;
+      const int nv = min(64, d.T - 64 * cq);
+      __syncthreads();
+      tile_load<T>(t_q, static_cast<const T*>(a.q) + r0, static_cast<long long>(d.Hq) * BD, nv);
+      tile_load<T>(t_do, static_cast<const T*>(a.dout) + r0, static_cast<long long>(d.Hq) * BD, nv);
+      tile_load<T>(t_qt, static_cast<const T*>(a.qt) + qc * BD * 64, 64, 64);
+      tile_load<T>(t_dot, static_cast<const T*>(a.dot) + qc * BD * 64, 64, 64);
+      tile_load<T>(t_pq, static_cast<const T*>(a.phiq) + (hq * d.nC * 64 + 64LL * cq) * BF, BF, 64);
+      tile_load<T>(t_pqt, static_cast<const T*>(a.phiqt) + qc * BF * 64, 64, 64);
+      if (tid < 128) s_ld[tid] = a.ld[(hq * d.nC * 64 + 64LL * cq) * 2 + tid];
+      __syncthreads();
+      f32x4 s[4], dp[4], lw[4];
+      rows_x_frag<T>(s, t_q, kf);
+      rows_x_frag<T>(dp, t_do, vf);
+      rows_x_frag<T>(lw, t_pq, phk);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qr = qb * 16 + 4 * grp + e;
+          const long long i = 64LL * cq + qr;
+          const bool vis = j <= i;
+          const bool inwin = i - j < d.window;
+          const bool sel = cq > c && selj;
+          const bool sa = vis && (inwin || sel);
+          const bool la = vis && !(inwin || sel);
+          const float L2 = s_ld[2 * qr], dl = s_ld[2 * qr + 1];
+          const float einv = exp2f(-L2);
+          const float p = sa ? exp2f(s[qb][e] * scale2 - L2) : 0.f;
+          const float gg = dp[qb][e] - dl;
+          s[qb][e] = p * gg;                           // dS
+          dp[qb][e] = p + (la ? lw[qb][e] * einv : 0.f);  // weight of v_j in out_i
+          lw[qb][e] = la ? gg * einv : 0.f;            // g
+        }
+      rows_x_acc<T>(dvt, t_dot, dp);
+      rows_x_acc<T>(dkt, t_qt, s);
+      rows_x_acc<T>(dpk, t_pqt, lw);
+    }
+  }
+  // queries of chunks >= c+2 through R_c, r_c (unselected keys only)
+  if (c + 2 < d.nC) {
+    const float* rs = a.rstate + (bh * d.nC + c) * BR;
+    f32x4 rv[4] = {};
+    f32rows_x_frag<T>(rv, rs, vf);  // (R v)[16 fb + 4 grp + e]
+    __syncthreads();
+    for (int e = tid; e < BF * BD; e += 256) {  // R^T, features pk-permuted
+      const int f = e >> 6, dd = e & 63;
+      t_q[SW::off(dd, pk_pos(f))] = TT::from_f(rs[e]);
+    }
+    __syncthreads();
+    const float on = (kvalid && !selj) ? 1.f : 0.f;
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dpk[fb][e] += on * (rv[fb][e] - rs[BF * BD + fb * 16 + 4 * grp + e]);
+    frag pm[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pm[ks][e] = TT::from_f(on * TT::to_f(phk[ks][e]));
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) TT::mma(dvt[db], SW::load8(t_q, db * 16 + r16, ks * 32 + grp * 8), pm[ks]);
+  }
+  // selected keys: the later chunks' softmax part from the compact partials
+  if (selj && kvalid) {
+    const int32_t* sp = a.sel_idx + (bh * d.nCc + c) * d.topk;
+    int rank = 0;
+    for (int r = 0; r < d.topk; ++r) rank += (sp[r] - 64 * c) < jr ? 1 : 0;
+    const int n = c * d.topk + rank;
+    for (int sidx = 0; sidx < a.nsplit; ++sidx) {
+      const float* p = a.dkvsel + ((static_cast<long long>(sidx) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dkt[db] += *reinterpret_cast<const f32x4*>(p + db * 16 + 4 * grp);
+        dvt[db] += *reinterpret_cast<const f32x4*>(p + BD + db * 16 + 4 * grp);
+      }
+    }
+  }
+  // NP-Map backward and dk, dv
+  NpRow nk;
+  np_forward<T>(nk, W, kf);
+  const float dr = np_backward(nk, dpk);  // dpk now holds dz
+  __syncthreads();
+  load_wt<T>(t_q, W);
+  __syncthreads();
+  f32x4 dxt[4] = {};
+  rows_x_acc<T>(dxt, t_q, dpk);
+  if (kvalid) {
+    T* dk = static_cast<T*>(a.dk) + koff;
+    T* dv = static_cast<T*>(a.dv) + koff;
+    const T* xk = static_cast<const T*>(a.k) + koff;
+    const float xs = nk.r > 0.f ? dr / nk.r : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const typename TT::quad x4 = TT::load4(xk + db * 16 + 4 * grp);
+      typename TT::quad o4, v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o4[e] = TT::from_f(dkt[db][e] * 0.125f + dxt[db][e] + xs * TT::to_f(x4[e]));
+        v4[e] = TT::from_f(dvt[db][e]);
+      }
+      *reinterpret_cast<typename TT::quad*>(dk + db * 16 + 4 * grp) = o4;
+      *reinterpret_cast<typename TT::quad*>(dv + db * 16 + 4 * grp) = v4;
+    }
+  }
+  // dW (k side) of the chunk: sum over its keys of dz k^T
+  __syncthreads();
+  const int pj = pk_pos(jr);
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t_do[SW::off(fb * 16 + 4 * grp + e, pj)] = TT::from_f(kvalid ? dpk[fb][e] : 0.f);
+  tile_load<T>(t_qt, static_cast<const T*>(a.kt) + (bh * d.nC + c) * BD * 64, 64, 64);
+  __syncthreads();
+  f32x4 acc[4];
+  tile_x_tile<T>(acc, t_do, t_qt);
+  float* wp = a.dwk + (bh * d.nC + c) * (BF * BD);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wp[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+}
+
+// ---------------------------------------------------------------------------------------
+// dW = sum over batch, chunks and the group's query heads (q side) plus keys (k side):
+// gridDim.y slices of the item list, then a fixed-order sum of the slices.
+__global__ __launch_bounds__(256) void bwd_dw_part_kernel(const float* dwq, const float* dwk, float* part, int B,
+                                                          int Hkv, int G, int nC) {
+  const int e = blockIdx.x * 256 + threadIdx.x;  // over Hkv * F * D
+  const int h = e / (BF * BD), fd = e % (BF * BD);
+  const int nq = B * G * nC, nitems = nq + B * nC;
+  const int per = (nitems + gridDim.y - 1) / gridDim.y;
+  const int i0 = blockIdx.y * per, i1 = min(nitems, i0 + per);
+  float acc = 0.f;
+  for (int it = i0; it < i1; ++it) {
+    long long src;
+    if (it < nq) {
+      const int b = it / (G * nC), g = (it / nC) % G, c = it % nC;
+      src = ((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * (BF * BD) + fd;
+      acc += dwq[src];
+    } else {
+      const int it2 = it - nq, b = it2 / nC, c = it2 % nC;
+      src = ((static_cast<long long>(b) * Hkv + h) * nC + c) * (BF * BD) + fd;
+      acc += dwk[src];
+    }
+  }
+  part[static_cast<long long>(blockIdx.y) * Hkv * BF * BD + e] = acc;
+}
+
+__global__ __launch_bounds__(256) void bwd_dw_sum_kernel(const float* part, float* dw, int n, int nparts) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float acc = 0.f;
+  for (int p = 0; p < nparts; ++p) acc += part[static_cast<long long>(p) * n + e];
+  dw[e] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const Dims& d = a.d;
+  hipError_t e;
+  auto mark = [&](int k) { return ev ? hipEventRecord(ev[k], s) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return e;
+  if (a.ntiles > 0) {
+    const size_t tb = static_cast<size_t>(d.B) * d.Hkv * a.ntiles * 64 * BD * sizeof(T);
+    if ((e = launch_fill_zero(a.kselt, tb, s)) != hipSuccess) return e;
+    if ((e = launch_fill_zero(a.ksel, tb, s)) != hipSuccess) return e;
+    if ((e = launch_fill_zero(a.vsel, tb, s)) != hipSuccess) return e;
+  }
+  const dim3 gk(d.nC, d.Hkv, d.B), gq(d.nC, d.Hq, d.B);
+  hipLaunchKernelGGL(bwd_kprep_kernel<T>, gk, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  const long long ne = static_cast<long long>(d.B) * d.Hkv * BR;
+  const dim3 gs(static_cast<unsigned>((ne + 255) / 256));
+  hipLaunchKernelGGL(bwd_scan_fwd_kernel, gs, dim3(256), 0, s, a.ustate, d.nC, ne);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel<T>, gq, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scan_rev_kernel, gs, dim3(256), 0, s, a.apart, a.rstate, d.nC, d.G, d.Hkv, ne);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
+  if (a.ntiles > 0) {
+    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3(a.ntiles, a.nsplit, d.B * d.Hkv), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = mark(5)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkv_local_kernel<T>, gk, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
+  const int nw = d.Hkv * BF * BD;
+  hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 256, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
+                     d.Hkv, d.G, d.nC);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((nw + 255) / 256), dim3(256), 0, s, a.dwpart, a.dw, nw, a.dw_parts);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(7);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events) {
+  return a.d.bf16 ? launch_bwd_t<bf16>(a, s, events) : launch_bwd_t<float>(a, s, events);
+}
+
+}  // namespace still

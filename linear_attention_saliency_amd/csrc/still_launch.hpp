@@ -95,6 +95,47 @@ struct DecodeArgs {
   CacheView c;
 };
 
+// Backward pass with the routing held fixed (head_dim = feat_dim = 64). Workspace buffers,
+// per (b, KV head) or per (b, query head); "pk" marks 64-vectors stored pk-permuted.
+struct BwdArgs {
+  Dims d;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* w;
+  const void* out;
+  const void* dout;
+  const int32_t* sel_idx;  // [B,Hkv,nCc,topk] ascending positions
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw;               // [Hkv,DF,D]
+  void* kt;                // [B,Hkv,nC,D,64 pk]: K^T of each chunk
+  void* phik;              // [B,Hkv,nC*64,DF pk]: phi(k) rows
+  void* phikt;             // [B,Hkv,nC,DF,64 pk]
+  float* ustate;           // [B,Hkv,nC,R]: U_c, then S_c = sum over chunks <= c-2
+  void* ksel;              // [B,Hkv,ntiles*64,D]: selected K rows in chunk order
+  void* vsel;              // [B,Hkv,ntiles*64,D]
+  void* kselt;             // [B,Hkv,ntiles,D,64 pk]
+  void* qt;                // [B,Hq,nC,D,64 pk]
+  void* dot;               // [B,Hq,nC,D,64 pk]
+  void* phiq;              // [B,Hq,nC*64,DF pk]
+  void* phiqt;             // [B,Hq,nC,DF,64 pk]
+  float* ld;               // [B,Hq,nC*64,2]: (log2 of the normaliser, Delta)
+  float* apart;            // [B,Hq,nC,R]: per-chunk sum of e^{-L} phi(q) dout^T, e^{-L} Delta phi(q)
+  float* rstate;           // [B,Hkv,nC,R]: R_c, r_c (chunks >= c+2)
+  float* dwq;              // [B,Hq,nC,DF*D]
+  float* dwk;              // [B,Hkv,nC,DF*D]
+  float* dkvsel;           // [nsplit,B,Hkv,ntiles*64,2,D]
+  float* dwpart;           // [dw_parts,Hkv,DF*D]
+  int ntiles;              // compact tiles per (b, KV head)
+  int nsplit;              // query splits of the compact-key kernel
+  int dw_parts;
+};
+
+// events: optional, 8 events recorded before each of the seven stages and after the last
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events);
+
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 // prefix sums of the chunk records, and the per-tile key-norm bound from kmaxc
 hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* tilemax, int tm_stride,

@@ -23,7 +23,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: 
 EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefill", "still_prefill_timed",
            "still_select_topk",
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
-           "still_decode_step", "still_decode_step_timed")
+           "still_decode_step", "still_decode_step_timed", "still_backward_workspace_bytes", "still_backward",
+           "still_backward_timed")
 
 
 class StillError(RuntimeError):
@@ -81,6 +82,12 @@ def load():
     lib.still_decode_step.restype = I
     lib.still_decode_step_timed.argtypes = [CP, KP, P, P, P, P, P, P, S, V, P]
     lib.still_decode_step_timed.restype = I
+    lib.still_backward_workspace_bytes.argtypes = [CP]
+    lib.still_backward_workspace_bytes.restype = S
+    lib.still_backward.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, P, S, V]
+    lib.still_backward.restype = I
+    lib.still_backward_timed.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, P, S, V, P]
+    lib.still_backward_timed.restype = I
     _lib = lib
     return lib
 
@@ -175,6 +182,45 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
     if return_routing:
         res.append(sel)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+class Backward:
+    """A prepared backward call (routing held fixed): the config and a reusable workspace."""
+
+    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64):
+        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k)
+        nbytes = int(load().still_backward_workspace_bytes(ctypes.byref(self.cfg)))
+        if nbytes == 0:
+            raise StillError(-2, "still_backward_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+    def __call__(self, q, k, v, w_phi, out, dout, sel_idx, dq, dk, dv, dw_phi, *, stream=None, events=None):
+        """events: optional array of 8 hipEvent_t handles (ctypes c_void_p * 8)."""
+        for t in (q, k, v, w_phi, out, dout, dq, dk, dv, dw_phi):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("tensors must be contiguous device tensors")
+        if sel_idx is not None and not (sel_idx.is_cuda and sel_idx.is_contiguous() and sel_idx.dtype == torch.int32):
+            raise ValueError("sel_idx must be a contiguous int32 device tensor")
+        rc = load().still_backward_timed(ctypes.byref(self.cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w_phi), _ptr(out),
+                                         _ptr(dout), _ptr(sel_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw_phi),
+                                         _ptr(self.workspace), self.workspace.numel(), _stream(stream), events)
+        _check(rc, "still_backward")
+        return dq, dk, dv, dw_phi
+
+
+def backward(q, k, v, w_phi, out, dout, sel_idx, *, window: int, top_k: int, chunk: int = 64):
+    """Gradients of sum(out * dout) for one STILL layer with the routing sel_idx held fixed.
+
+    q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D], out and dout like q (one dtype, on the
+    GPU); sel_idx int32 [B,Hkv,T//chunk,top_k] as prefill(return_routing=True) gives it.
+    Returns (dq, dk, dv) in the inputs' dtype and dw_phi in float32.
+    """
+    call = Backward(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dw = torch.empty(w_phi.shape, dtype=torch.float32, device=q.device)
+    if sel_idx is not None:
+        sel_idx = sel_idx.to(device=q.device, dtype=torch.int32).contiguous()
+    return call(q, k, v, w_phi, out, dout, sel_idx, dq, dk, dv, dw)
 
 
 def select_topk(saliency, *, chunk: int, top_k: int, n_q_heads: int = 1, head_dim: int = 64, feat_dim: int = 64,

@@ -113,6 +113,16 @@ def make_inputs(wl: Workload, seq_len: int | None = None, batch: int | None = No
     return q, k, v, w
 
 
+def make_grad_out(wl: Workload, seq_len: int | None = None, batch: int | None = None) -> np.ndarray:
+    """The gradient of a scalar loss with respect to the layer output, for backward-pass
+    cases: N(0, 1/D) entries [B,T,Hq,D] (seed wl.seed + 7919), exact in wl.dtype."""
+    B = wl.batch if batch is None else batch
+    T = wl.seq_len if seq_len is None else seq_len
+    rng = np.random.default_rng(wl.seed + 7919)
+    g = rng.standard_normal((B, T, wl.n_q_heads, wl.head_dim), dtype=np.float32) * np.float32(1.0 / math.sqrt(wl.head_dim))
+    return round_bf16(g) if wl.dtype == "bf16" else g
+
+
 def small_case(seed: int, B: int, T: int, Hq: int, Hkv: int, D: int, F: int, window: int,
                chunk: int, top_k: int, dtype: str = "f32", qk_scale: float | None = None,
                n_planted: int = 0) -> tuple[Workload, tuple]:

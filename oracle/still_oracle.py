@@ -379,7 +379,7 @@ def _np_map_t(x, w):
     return torch.linalg.vector_norm(x, dim=-1, keepdim=True) * m / torch.linalg.vector_norm(m, dim=-1, keepdim=True)
 
 
-def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
+def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: int = 0):
     """Gradients of sum(out * dout) with respect to q, k, v and w_phi, for a fixed routing.
 
     The routing sel [B,Hkv,T] (bool) is an input: it is piecewise constant in q and k, so
@@ -387,6 +387,10 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
     of every (i, j) pair, as in brute) with plain torch fp64 ops, and torch's reverse-mode
     differentiation takes the chain rule through the shared normaliser, both branches and
     the NP-Map. Rows whose normaliser is 0 have out = 0 and contribute nothing.
+    q_from: only query rows i >= q_from enter the sum. Query row i affects out_i alone and key
+    j only the rows i >= j, so the gradients of q rows and of k, v rows at positions >= q_from
+    are then the full ones (the others are partial): a long sequence can be checked at its
+    tail for the cost of its last rows.
     Returns (dq, dk, dv, dw_phi) as fp64 arrays shaped like q, k, v and w_phi.
     """
     import torch
@@ -396,7 +400,7 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
     B, T, Hq, D = qt.shape
     G = _check_group(Hq, kt.shape[2])
     sel = torch.tensor(np.asarray(sel, dtype=bool))
-    i = torch.arange(T)[:, None]
+    i = torch.arange(q_from, T)[:, None]
     j = torch.arange(T)[None, :]
     causal = j <= i
     in_window = j > i - window
@@ -407,7 +411,7 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
             h = hq // G
             sa = causal & (in_window | (earlier_chunk & sel[b, h][None, :]))
             la = causal & ~sa
-            qq, kk, vv = qt[b, :, hq], kt[b, :, h], vt[b, :, h]
+            qq, kk, vv = qt[b, q_from:, hq], kt[b, :, h], vt[b, :, h]
             a = torch.where(sa, qq @ kk.T / math.sqrt(D), -math.inf)
             M = a.detach().amax(dim=1, keepdim=True)
             M = torch.where(torch.isfinite(M), M, torch.zeros_like(M))
@@ -417,7 +421,7 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout):
             den = wgt.sum(dim=1, keepdim=True)
             safe = den > 0.0
             o = torch.where(safe, (wgt @ vv) / torch.where(safe, den, torch.ones_like(den)), 0.0)
-            loss = loss + (o * do[b, :, hq]).sum()
+            loss = loss + (o * do[b, q_from:, hq]).sum()
     loss.backward()
     return tuple(t.grad.numpy() for t in (qt, kt, vt, wt))
 

@@ -1,0 +1,133 @@
+"""Parity of the backward pass (through the C ABI) with the fp64 oracle's gradients.
+
+The routing is the one the device's forward pass chose; the oracle differentiates the
+dense form of the layer under that routing. Bars, as max-abs error over a tensor relative
+to that tensor's largest oracle entry (at least 1e-3): 1e-4 in fp32 (fp32 MFMA sums, the fp32 output in
+Delta) and 3e-2 in bf16 (every MFMA operand, including the probabilities and the scores'
+gradients, is rounded to bf16, and Delta uses the bf16-rounded output).
+"""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_saliency_amd import still, synth
+from oracle import still_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = {"f32": 1e-4, "bf16": 3e-2}
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32).contiguous()
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _sel_from_idx(idx, T):
+    B, H, nc, k = idx.shape
+    sel = np.zeros((B, H, T), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            sel[b, h, idx[b, h].reshape(-1)] = True
+    return sel
+
+
+def _forward_backward(wl, q, k, v, w, dout):
+    dt = wl.dtype
+    tq, tk, tv, tw, tdo = (_dev(a, dt) for a in (q, k, v, w, dout))
+    out, idx = still.prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, return_routing=True)
+    dq, dk, dv, dw = still.backward(tq, tk, tv, tw, out, tdo, idx, window=wl.window, top_k=wl.top_k)
+    torch.cuda.synchronize()
+    return out, idx, (dq, dk, dv, dw)
+
+
+def _rel_err(got, ref):
+    # a floor of 1e-3 (gradients here are of order 0.1 to 1): where the exact gradient is 0,
+    # as dq of a token whose only softmax key is itself, rounding noise is not divided by 0
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-3))
+
+
+CASES = [
+    # name, B, T, Hq, Hkv, w, k, dtype, qk_scale
+    ("f32-ragged", 1, 200, 2, 1, 64, 8, "f32", 1.0),
+    ("f32-gqa2-b2", 2, 150, 4, 2, 64, 4, "f32", None),
+    ("bf16-gqa4-ragged", 1, 333, 8, 2, 64, 8, "bf16", 1.0),
+    ("bf16-window16", 1, 260, 4, 1, 16, 8, "bf16", 1.0),
+    ("bf16-window1", 1, 200, 2, 1, 1, 8, "bf16", None),
+    ("f32-window0-k0", 1, 170, 2, 1, 0, 0, "f32", 1.0),
+    ("bf16-k64-full-softmax", 1, 200, 4, 1, 64, 64, "bf16", 1.0),
+    ("bf16-g6", 1, 150, 6, 1, 64, 8, "bf16", 1.0),
+    ("bf16-short", 1, 37, 4, 1, 64, 8, "bf16", 1.0),
+    ("f32-one-token", 2, 1, 2, 1, 64, 8, "f32", None),
+    ("f32-two-chunks", 1, 128, 2, 1, 64, 16, "f32", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case):
+    name, B, T, Hq, Hkv, w, k, dt, sc = case
+    _say(name)
+    wl, (q, kk, v, wp) = synth.small_case(seed=zlib.crc32(name.encode()) % 1000, B=B, T=T, Hq=Hq, Hkv=Hkv, D=64,
+                                           F=64, window=w, chunk=64, top_k=k, dtype=dt, qk_scale=sc,
+                                           n_planted=max(1, T // 50))
+    dout = synth.make_grad_out(wl)
+    out, idx, grads = _forward_backward(wl, q, kk, v, wp, dout)
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    ref = O.attend_backward(q, kk, v, wp, w, 64, sel, dout)
+    for nm, g, r in zip(("dq", "dk", "dv", "dw"), grads, ref):
+        assert np.all(np.isfinite(_np(g))), nm
+        e = _rel_err(_np(g), r)
+        _say(name, nm, "rel max err", e)
+        assert e <= REL_TOL[dt], (nm, e)
+
+
+def test_backward_is_deterministic():
+    wl, (q, kk, v, wp) = synth.small_case(seed=5, B=1, T=300, Hq=8, Hkv=2, D=64, F=64, window=64, chunk=64,
+                                           top_k=8, dtype="bf16", qk_scale=1.0, n_planted=6)
+    dout = synth.make_grad_out(wl)
+    _say("deterministic")
+    _, _, g1 = _forward_backward(wl, q, kk, v, wp, dout)
+    _, _, g2 = _forward_backward(wl, q, kk, v, wp, dout)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_at_headline_shape():
+    """The 16K Llama-3.2-1B-shaped layer: gradients of the last four chunks' q, k and v rows
+    against the oracle (exact there: later rows get no gradient from earlier queries), and
+    the identity that the value gradients of a KV head sum to its query heads' dout."""
+    wl = synth.L1B_16K
+    _say("backward headline", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    dout = synth.make_grad_out(wl)
+    out, idx, (dq, dk, dv, dw) = _forward_backward(wl, q, k, v, wp, dout)
+    T, G = wl.seq_len, wl.n_q_heads // wl.n_kv_heads
+    t0 = T - 4 * wl.chunk
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    ref = O.attend_backward(q, k, v, wp, wl.window, wl.chunk, sel, dout, q_from=t0)
+    for nm, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        gn = _np(g)
+        assert np.all(np.isfinite(gn)), nm
+        e = _rel_err(gn[:, t0:], r[:, t0:])
+        _say("headline", nm, "rel max err over the last 256 rows", e)
+        assert e <= REL_TOL["bf16"], (nm, e)
+    dvn = _np(dv)
+    want = dout.astype(np.float64).reshape(1, T, wl.n_kv_heads, G, wl.head_dim).sum(axis=(1, 3))
+    got = dvn.sum(axis=1)
+    e = float(np.abs(got - want).max() / np.abs(want).max())
+    _say("headline sum of dv rel err", e)
+    assert e <= 1e-2
+    assert np.all(np.isfinite(_np(dw)))

@@ -427,3 +427,16 @@ def test_backward_reduces_to_causal_softmax_gradients():
     np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
     assert np.all(dw == 0.0)
+
+
+def test_backward_tail_rows_equal_full_gradients():
+    """attend_backward(q_from=t0) gives the full gradients of q, k and v rows at t0 and after."""
+    T, Hq, Hkv, w, C, k = 40, 2, 1, 8, 8, 2
+    q, k_, v, wp = _case(1, T, Hq, Hkv, 8, 6, seed=12, scale=1.5)
+    sel = _fixed_routing(q, k_, w, C, k, 1, Hkv, T)
+    dout = np.random.default_rng(3).standard_normal(q.shape)
+    full = O.attend_backward(q, k_, v, wp, w, C, sel, dout)
+    tail = O.attend_backward(q, k_, v, wp, w, C, sel, dout, q_from=27)
+    for a, b in zip(full[:3], tail[:3]):
+        np.testing.assert_allclose(b[:, 27:], a[:, 27:], rtol=0, atol=1e-12)
+    assert np.abs(tail[1][:, :27]).max() > 0  # earlier keys get only part of their gradient
