@@ -213,6 +213,83 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     return res
 
 
+BWD_STAGES = ("kprep", "scan_fwd", "dq", "scan_rev", "dkv_far", "dkv_local", "dw")
+
+
+def backward_work(wl, sel_idx) -> dict:
+    """Algorithmic flops of the backward pass, from the routing.
+
+    Softmax pairs (query head, softmax key) as in the forward count: 10*D flops each (the
+    scores recomputed, dout.v, and the dq, dk and dv products). Linear attention: 4*F*D per
+    query-head token (S_c dout and its share of R) and 4*F*D per KV-head token (R v and
+    R^T phi(k)). NP-Map: 6*F*D per query-head and per KV-head row (W x recomputed, W^T dz and
+    dz x^T).
+    """
+    fw = algorithmic_work(wl, sel_idx)
+    B, T, Hq, Hkv, D, F = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.feat_dim
+    sa = 10.0 * D * fw["sa_pairs"]
+    la = 4.0 * F * D * (Hq + Hkv) * B * T
+    npm = 6.0 * F * D * (Hq + Hkv) * B * T
+    return {"flops": sa + la + npm, "sa_flops": sa}
+
+
+def run_backward(wl, args, torch, still, synth) -> dict:
+    dev = torch.device("cuda:0")
+    q, k, v, w = synth.make_inputs(wl)
+    dout = synth.make_grad_out(wl)
+    tq, tk, tv, tw, tdo = (torch.from_numpy(a).to(dev, torch.bfloat16).contiguous() for a in (q, k, v, w, dout))
+    del q, k, v, w, dout
+    out, sel = still.prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, return_routing=True)
+    call = still.Backward(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    dw = torch.empty(tw.shape, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    work = backward_work(wl, sel.cpu().numpy())
+    for _ in range(args.warmup):
+        call(tq, tk, tv, tw, out, tdo, sel, dq, dk, dv, dw)
+    stream = torch.cuda.current_stream()
+    evs, handles = _events(torch, args.steps, 8)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s_ in range(args.steps):
+        call(tq, tk, tv, tw, out, tdo, sel, dq, dk, dv, dw, events=handles[s_])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = np.array([[step[j].elapsed_time(step[j + 1]) for j in range(7)] for step in evs]).mean(axis=0)
+    stage_ms = {n: float(x) for n, x in zip(BWD_STAGES, k_ms)}
+    tflops = work["flops"] / (ms_step * 1e-3)
+    dom = max(("dq", "dkv_far", "dkv_local"), key=lambda n: stage_ms[n])
+    return {
+        "metric": f"backward tokens/s per layer ({wl.name}, bf16, routing fixed); % of MFMA roofline",
+        "value": wl.batch * wl.seq_len / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1)/sqrt(D) Q/K/V and dout, 1% planted keys x4, W_phi N(0,1/D); bf16",
+        "config": {"workload": wl.name + "-backward", "batch": wl.batch, "seq_len": wl.seq_len,
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "feat_dim": wl.feat_dim, "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k},
+        "roofline": {"bound": "mfma", "kernel": "whole backward pass", "achieved": tflops / 1e12,
+                     "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_MFMA,
+                     "traffic": None},
+        "dominant_stage": dom,
+        "kernel_ms": stage_ms,
+        "flops": work["flops"],
+        "memory": {"workspace_bytes": int(call.workspace.numel())},
+        "wall_s": wall,
+    }
+
+
 def run_decode(wl, args, torch, still, synth) -> dict:
     dev = torch.device("cuda:0")
     B, Hq, Hkv, D, F = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.feat_dim
@@ -306,6 +383,8 @@ def main() -> int:
     ap.add_argument("--top-k", type=int, default=None,
                     help="override the workload's top_k on the same kernels: 0 gives the sliding-window plus "
                          "linear-attention baseline, 64 (= chunk) full causal softmax")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (routing fixed) instead of the forward")
     ap.add_argument("--score", choices=["saliency", "diag"], default="saliency",
                     help="routing score: the Self-Saliency Score, or the diagonal logit alone")
     args = ap.parse_args()
@@ -335,7 +414,13 @@ def main() -> int:
         args.steps = 64 if decode else 50
     if args.warmup is None:
         args.warmup = 8 if decode else 100
-    res = (run_decode if decode else run_prefill)(wl, args, torch, still, synth)
+    if args.backward:
+        if decode or wl.head_dim != 64:
+            print("--backward covers prefill workloads with head_dim 64", file=sys.stderr)
+            return 2
+        res = run_backward(wl, args, torch, still, synth)
+    else:
+        res = (run_decode if decode else run_prefill)(wl, args, torch, still, synth)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -206,6 +206,20 @@ __device__ __forceinline__ void load_wt(T* lds, const T* W) {
   }
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vector memory only, until at most n
+// operations of this wave are outstanding
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// s_waitcnt immediate that waits for LDS (and scalar memory) only
+constexpr int kLgkmWait0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// workgroup barrier; the waits for memory are the caller's, and no LDS access moves across it
+__device__ __forceinline__ void lds_sync() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // selection bit mask of complete chunk c from the ascending positions (entries outside
 // the chunk are ignored); wave-uniform
 __device__ __forceinline__ uint64_t chunk_sel(const int32_t* sel_idx, long long bh, int c, const Dims& d) {
@@ -338,16 +352,18 @@ __global__ __launch_bounds__(256) void bwd_scan_rev_kernel(const float* apart, f
 
 // ---------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
-  __shared__ __attribute__((aligned(16))) T t_k[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_v[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_kt[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_pk[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_pkt[64 * 64];
+  // six tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5
+  __shared__ __attribute__((aligned(16))) T lds[6][64 * 64];
   __shared__ float s_red[4][64];
+  T* const t_k = lds[0];
+  T* const t_v = lds[1];
+  T* const t_kt = lds[2];
+  T* const t_pk = lds[3];
+  T* const t_pkt = lds[4];
 
   const Dims& d = a.d;
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -375,14 +391,28 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
   delta = xor_sum_groups(delta);
 
-  NpRow nq;
-  np_forward<T>(nq, W, qf);
-  f32x4 phq[4];
+  // phi(q): kept as operand fragments through the key loops (the NP-Map forward is
+  // recomputed for its backward at the end, which keeps the loops' registers low)
+  frag phf[2];
+  float dla = 0.f;  // the linear-attention part of the normaliser
+  {
+    NpRow nq;
+    np_forward<T>(nq, W, qf);
+    f32x4 phq[4];
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+    for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
-  const frag phf[2] = {pk_frag<T>(phq[0], phq[1]), pk_frag<T>(phq[2], phq[3])};
+      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+    phf[0] = pk_frag<T>(phq[0], phq[1]);
+    phf[1] = pk_frag<T>(phq[2], phq[3]);
+    if (c >= 2) {  // state part: phi(q) . z_c
+      const float* zc = a.ustate + (bh * d.nC + c) * BR + BF * BD;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dla += phq[fb][e] * zc[fb * 16 + 4 * grp + e];
+    }
+  }
 
   const uint64_t sel_prev = chunk_sel(a.sel_idx, bh, c - 1, d);
   const int nsel_c = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
@@ -392,14 +422,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const float* st = a.ustate + (bh * d.nC + c) * BR;  // S_c, z_c
   const long long krs = static_cast<long long>(d.Hkv) * BD;
 
-  // linear-attention state part of the normaliser
-  float dla = 0.f;
-  if (c >= 2) {
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dla += phq[fb][e] * st[BF * BD + fb * 16 + 4 * grp + e];
-  }
 
   // ---- pass 1: L = log2 of the normaliser
   float mx2 = -kInf, l = 0.f;
@@ -423,12 +445,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     l = any ? l * exp2f(mx2 - mn) + ps : l;
     mx2 = mn;
   };
-  for (int t = 0; t * 64 < nsel_c; ++t) {
-    __syncthreads();
-    tile_load<T>(t_k, ksel + static_cast<long long>(t) * 64 * BD, BD, min(64, nsel_c - t * 64));
-    __syncthreads();
+  // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
+  // nsel_c read as zeros (the copies' range ends there)
+  using Dma = DmaTile<T, 64, 64, 4>;
+  Dma dma;
+  dma.init(64);
+  constexpr int ES = static_cast<int>(sizeof(T));
+  const int ntc = (nsel_c + 63) / 64;
+  const auto rs_k = make_rsrc(ksel, static_cast<uint32_t>(nsel_c * BD * ES));
+  const auto rs_v = make_rsrc(vsel, static_cast<uint32_t>(nsel_c * BD * ES));
+  const auto rs_kt = make_rsrc(kselt, static_cast<uint32_t>(ntc * BD * 64 * ES));
+  if (ntc > 0) dma.issue(lds[0], rs_k, 0);
+  for (int t = 0; t < ntc; ++t) {
+    if (t + 1 < ntc) {
+      dma.issue(lds[((t + 1) & 1) * 3], rs_k, (t + 1) * 64 * BD * ES);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(Dma::PER_WAVE));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    }
+    lds_sync();
     f32x4 s[4];
-    rows_x_frag<T>(s, t_k, qf);
+    rows_x_frag<T>(s, lds[(t & 1) * 3], qf);
     bool sa[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -438,6 +475,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         s[kb][e] *= scale2;
       }
     online(s, sa);
+    lds_sync();
   }
   for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
     __syncthreads();
@@ -481,16 +519,26 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
   // ---- pass 2: dq (softmax part) and dphi(q)
   f32x4 dqt[4] = {}, dpt[4] = {};
-  for (int t = 0; t * 64 < nsel_c; ++t) {
-    __syncthreads();
+  auto issue3 = [&](int t) {
+    const int sl = (t & 1) * 3;
+    dma.issue(lds[sl], rs_k, t * 64 * BD * ES);
+    dma.issue(lds[sl + 1], rs_v, t * 64 * BD * ES);
+    dma.issue(lds[sl + 2], rs_kt, t * BD * 64 * ES);
+  };
+  if (ntc > 0) issue3(0);
+  for (int t = 0; t < ntc; ++t) {
+    if (t + 1 < ntc) {
+      issue3(t + 1);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * Dma::PER_WAVE));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    }
+    lds_sync();
     const int nv = min(64, nsel_c - t * 64);
-    tile_load<T>(t_k, ksel + static_cast<long long>(t) * 64 * BD, BD, nv);
-    tile_load<T>(t_v, vsel + static_cast<long long>(t) * 64 * BD, BD, nv);
-    tile_load<T>(t_kt, kselt + static_cast<long long>(t) * BD * 64, 64, 64);
-    __syncthreads();
+    const int sl = (t & 1) * 3;
     f32x4 s[4], dp[4];
-    rows_x_frag<T>(s, t_k, qf);
-    rows_x_frag<T>(dp, t_v, dof);
+    rows_x_frag<T>(s, lds[sl], qf);
+    rows_x_frag<T>(dp, lds[sl + 1], dof);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -499,7 +547,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         const float p = ok ? exp2f(s[kb][e] * scale2 - L2) : 0.f;
         s[kb][e] = p * (dp[kb][e] - delta);
       }
-    rows_x_acc<T>(dqt, t_kt, s);
+    rows_x_acc<T>(dqt, lds[sl + 2], s);
+    lds_sync();
   }
   for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
     __syncthreads();
@@ -545,6 +594,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // ---- NP-Map backward and dq
+  NpRow nq;
+  np_forward<T>(nq, W, qf);
+  f32x4 phq[4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
   const float dr = np_backward(nq, dpt);  // dpt now holds dz
   __syncthreads();
   load_wt<T>(t_k, W);
@@ -624,76 +680,122 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Selected keys of compact tile `tile` against the queries of chunks >= their chunk + 2,
-// split over blockIdx.y; writes fp32 partial dk, dv (softmax part, before the 1/sqrt(D) of dk).
+// Selected keys against the queries of chunks >= their chunk + 2. A workgroup of eight
+// waves takes 128 compact rows (16 per wave) and one of gridDim.y slices of the query
+// chunks; it writes fp32 partial dk, dv (softmax part, before the 1/sqrt(D) of dk). The
+// query-side tiles (q rows, dout rows, q^T, dout^T) arrive by buffer -> LDS copies one
+// (chunk, head) step ahead, with that step's (L, Delta) prefetched into registers.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dkv_far_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
-  __shared__ __attribute__((aligned(16))) T t_q[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_do[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_qt[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_dot[64 * 64];
-  __shared__ float s_ld[64 * 2];
+  using Dma = DmaTile<T, 64, 64, 8>;
+  constexpr int ES = static_cast<int>(sizeof(T));
+  __shared__ __attribute__((aligned(16))) T lds[2][4][64 * 64];  // [buffer][q, dout, q^T, dout^T]
+  __shared__ float s_ld[2][128];
   const Dims& d = a.d;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int split = blockIdx.y;
   const long long bh = blockIdx.z;
-  const int b = static_cast<int>(bh / d.Hkv);
+  const int b = static_cast<int>(bh / d.Hkv), h = static_cast<int>(bh % d.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const float scale2 = kLog2e * 0.125f;
   const int nsel = d.nCc * d.topk;
-  const int n = tile * 64 + wave * 16 + r16;  // this lane column's compact row
-  const bool kvalid = n < nsel;
-  const int ckey = kvalid ? n / d.topk : 0x3fffffff;
+  const int row0 = blockIdx.x * 128;
+  const int n = row0 + wave * 16 + r16;  // this lane column's compact row
+  const bool nin = n < a.ntiles * 64;     // inside the buffers (rows past nsel are zeros)
+  const int ckey = n < nsel ? n / d.topk : 0x3fffffff;
   frag kf[2], vf[2];
-  const T* ksel = static_cast<const T*>(a.ksel) + (bh * a.ntiles * 64 + n) * BD;
-  const T* vsel = static_cast<const T*>(a.vsel) + (bh * a.ntiles * 64 + n) * BD;
+  {
+    const T* kr = static_cast<const T*>(a.ksel) + (bh * a.ntiles * 64 + n) * BD;
+    const T* vr = static_cast<const T*>(a.vsel) + (bh * a.ntiles * 64 + n) * BD;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    kf[ks] = TT::load8(ksel + ks * 32 + grp * 8);
-    vf[ks] = TT::load8(vsel + ks * 32 + grp * 8);
+    for (int ks = 0; ks < 2; ++ks) {
+      kf[ks] = nin ? TT::load8(kr + ks * 32 + grp * 8) : TT::zero();
+      vf[ks] = nin ? TT::load8(vr + ks * 32 + grp * 8) : TT::zero();
+    }
   }
-  // query chunks [c_lo, nC) split evenly over gridDim.y
-  const int c_lo = (tile * 64) / d.topk + 2;
+  // query chunks [c_lo, nC) split evenly over gridDim.y; steps run over (chunk, head)
+  const int c_lo = row0 / d.topk + 2;
   const int span = max(0, d.nC - c_lo);
   const int per = (span + gridDim.y - 1) / gridDim.y;
   const int cb0 = c_lo + split * per, cb1 = min(d.nC, cb0 + per);
+  const int nsteps = max(0, cb1 - cb0) * d.G;
+  Dma dma;
+  dma.init(64);
+  Dma dmq;
+  dmq.init(d.Hq * BD);
+  const long long hq0 = static_cast<long long>(b) * d.Hq + static_cast<long long>(h) * d.G;  // b*Hq + first head
+  auto step_ptrs = [&](int st, long long& qc, long long& r0, int& nv) {
+    const int cq = cb0 + st / d.G, g = st % d.G;
+    qc = (hq0 + g) * d.nC + cq;
+    r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + h * d.G + g) * BD;
+    nv = min(64, d.T - 64 * cq);
+  };
+  auto issue = [&](int st) {
+    long long qc, r0;
+    int nv;
+    step_ptrs(st, qc, r0, nv);
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * BD + BD) * ES);
+    T* dst = lds[st & 1][0];
+    dmq.issue(dst, make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
+    dmq.issue(dst + 64 * 64, make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
+    dma.issue(dst + 2 * 64 * 64, make_rsrc(static_cast<const T*>(a.qt) + qc * BD * 64, BD * 64 * ES), 0);
+    dma.issue(dst + 3 * 64 * 64, make_rsrc(static_cast<const T*>(a.dot) + qc * BD * 64, BD * 64 * ES), 0);
+  };
+  auto ld_of = [&](int st) {  // this thread's (L, Delta) entry of step st
+    long long qc, r0;
+    int nv;
+    step_ptrs(st, qc, r0, nv);
+    return a.ld[qc * 128 + (tid & 127)];
+  };
   f32x4 dkt[4] = {}, dvt[4] = {};
-  for (int cq = cb0; cq < cb1; ++cq) {
-    for (int g = 0; g < d.G; ++g) {
-      const long long hq = static_cast<long long>(b) * d.Hq + (bh % d.Hkv) * d.G + g;  // b*Hq + hq
-      const long long qc = hq * d.nC + cq;
-      const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (hq - static_cast<long long>(b) * d.Hq)) * BD;
-      const int nv = min(64, d.T - 64 * cq);
-      __syncthreads();
-      tile_load<T>(t_q, static_cast<const T*>(a.q) + r0, static_cast<long long>(d.Hq) * BD, nv);
-      tile_load<T>(t_do, static_cast<const T*>(a.dout) + r0, static_cast<long long>(d.Hq) * BD, nv);
-      tile_load<T>(t_qt, static_cast<const T*>(a.qt) + qc * BD * 64, 64, 64);
-      tile_load<T>(t_dot, static_cast<const T*>(a.dot) + qc * BD * 64, 64, 64);
-      if (tid < 128) s_ld[tid] = a.ld[(hq * d.nC * 64 + 64LL * cq) * 2 + tid];
-      __syncthreads();
-      f32x4 s[4], dp[4];
-      rows_x_frag<T>(s, t_q, kf);   // s[qb][e] = q[16 qb + 4 grp + e] . k
-      rows_x_frag<T>(dp, t_do, vf);
-      const bool on = cq >= ckey + 2;
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qr = qb * 16 + 4 * grp + e;
-          const float p = on ? exp2f(s[qb][e] * scale2 - s_ld[2 * qr]) : 0.f;
-          s[qb][e] = p * (dp[qb][e] - s_ld[2 * qr + 1]);
-          dp[qb][e] = p;
-        }
-      rows_x_acc<T>(dvt, t_dot, dp);
-      rows_x_acc<T>(dkt, t_qt, s);
-    }
+  float ldn = 0.f;
+  if (nsteps > 0) {
+    ldn = ld_of(0);
+    issue(0);
   }
-  float* out = a.dkvsel + ((static_cast<long long>(split) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+  for (int st = 0; st < nsteps; ++st) {
+    const float ldc = ldn;
+    if (st + 1 < nsteps) {
+      ldn = ld_of(st + 1);
+      issue(st + 1);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * Dma::PER_WAVE + 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    }
+    if (tid < 128) s_ld[st & 1][tid] = ldc;
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);  // the copies of the next step stay in flight
+    lds_sync();
+    const int cq = cb0 + st / d.G;
+    const T* tq = lds[st & 1][0];
+    const T* tdo = lds[st & 1][1];
+    const T* tqt = lds[st & 1][2];
+    const T* tdot = lds[st & 1][3];
+    const float* sl = s_ld[st & 1];
+    f32x4 s[4], dp[4];
+    rows_x_frag<T>(s, tq, kf);  // s[qb][e] = q[16 qb + 4 grp + e] . k
+    rows_x_frag<T>(dp, tdo, vf);
+    const bool on = cq >= ckey + 2;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    *reinterpret_cast<f32x4*>(out + db * 16 + 4 * grp) = dkt[db];
-    *reinterpret_cast<f32x4*>(out + BD + db * 16 + 4 * grp) = dvt[db];
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qr = qb * 16 + 4 * grp + e;
+        const float p = on ? exp2f(s[qb][e] * scale2 - sl[2 * qr]) : 0.f;
+        s[qb][e] = p * (dp[qb][e] - sl[2 * qr + 1]);
+        dp[qb][e] = p;
+      }
+    rows_x_acc<T>(dvt, tdot, dp);
+    rows_x_acc<T>(dkt, tqt, s);
+    lds_sync();
+  }
+  if (nin) {
+    float* out = a.dkvsel + ((static_cast<long long>(split) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      *reinterpret_cast<f32x4*>(out + db * 16 + 4 * grp) = dkt[db];
+      *reinterpret_cast<f32x4*>(out + BD + db * 16 + 4 * grp) = dvt[db];
+    }
   }
 }
 
@@ -918,7 +1020,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   hipLaunchKernelGGL(bwd_scan_rev_kernel, gs, dim3(256), 0, s, a.apart, a.rstate, d.nC, d.G, d.Hkv, ne);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
   if (a.ntiles > 0) {
-    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3(a.ntiles, a.nsplit, d.B * d.Hkv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3((a.ntiles + 1) / 2, a.nsplit, d.B * d.Hkv), dim3(512), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(5)) != hipSuccess) return e;
