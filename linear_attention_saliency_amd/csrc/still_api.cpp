@@ -163,8 +163,8 @@ size_t decode_ws_bytes(const still_config* c) {
 
 // ---- backward workspace
 struct BwdLayout {
-  size_t kt, phik, phikt, ustate, ksel, vsel, kselt, qt, dot, phiq, phiqt, ld, apart, rstate, dwq, dwk, dkvsel,
-      dwpart, total;
+  size_t kt, phik, phikt, ustate, ksel, vsel, kselt, qt, dot, phiq, phiqt, ld, apart, rstate, segsum, dwq, dwk,
+      dkvsel, dwpart, total;
   int ntiles, nsplit, dw_parts;
 };
 
@@ -205,6 +205,7 @@ BwdLayout bwd_layout(const still_config* c) {
   L.ld = take(bhq * nC * 64 * 2 * 4);
   L.apart = take(bhq * nC * R * 4);
   L.rstate = take(bh * nC * R * 4);
+  L.segsum = take(bh * ((nC + 15) / 16) * R * 4);
   L.dwq = take(bhq * nC * F * D * 4);
   L.dwk = take(bh * nC * F * D * 4);
   L.dkvsel = take(static_cast<size_t>(L.nsplit) * bh * L.ntiles * 64 * 2 * D * 4);
@@ -487,6 +488,7 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
   a.ld = reinterpret_cast<float*>(ws + L.ld);
   a.apart = reinterpret_cast<float*>(ws + L.apart);
   a.rstate = reinterpret_cast<float*>(ws + L.rstate);
+  a.segsum = reinterpret_cast<float*>(ws + L.segsum);
   a.dwq = reinterpret_cast<float*>(ws + L.dwq);
   a.dwk = reinterpret_cast<float*>(ws + L.dwk);
   a.dkvsel = reinterpret_cast<float*>(ws + L.dkvsel);

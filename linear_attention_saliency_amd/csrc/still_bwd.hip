@@ -24,7 +24,8 @@
 //   bwd_scan_fwd_kernel  U_c -> S_c (sum over chunks <= c-2), in place
 //   bwd_dq_kernel        per (chunk, query head, batch): L_i (first pass over the keys),
 //                        dq (second pass), the per-chunk sums behind R, the q side of dW
-//   bwd_scan_rev_kernel  R_c = sum over chunks >= c+2 and over the query group
+//   bwd_rev_seg_kernel / bwd_rev_scan_kernel: R_c = sum over chunks >= c+2 and over the
+//                        query group (a segmented scan)
 //   bwd_dkv_far_kernel   per (compact tile, query split, KV head): the selected keys
 //                        against the queries of chunks >= their chunk + 2
 //   bwd_dkv_local_kernel per (chunk, KV head, batch): keys against the queries of their
@@ -72,12 +73,10 @@ __device__ __forceinline__ typename Tr<T>::frag f32_frag(const float* p) {
 }
 
 // 64 rows of 64 elements from memory (row stride `stride` elements) into a Swz<T, 64> LDS
-// tile; rows at or beyond nvalid are zero. All 256 threads call.
+// tile; rows at or beyond nvalid are zero. All threads of the workgroup call.
 template <typename T>
 __device__ __forceinline__ void tile_load(T* lds, const T* g, long long stride, int nvalid) {
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = static_cast<int>(threadIdx.x) + it * 256;
+  for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
     const int row = idx >> 3, col = (idx & 7) * 8;
     const typename Tr<T>::frag x = row < nvalid ? Tr<T>::load8(g + row * stride + col) : Tr<T>::zero();
     Swz<T, 64>::store8(lds, row, col, x);
@@ -123,10 +122,10 @@ __device__ __forceinline__ void f32rows_x_frag(f32x4 (&acc)[4], const float* m, 
 
 // One 64x64 output of a workgroup-wide product over 64 pk-permuted positions:
 // out[row][col] = sum_p A[row][p] B[col][p], A and B Swz<T, 64> tiles. Wave w computes rows
-// 16w..16w+15; returns acc[cb][i] = out[16w + 4grp + i][16cb + r16].
+// 16w..16w+15 (w = wave % 4); returns acc[cb][i] = out[16w + 4grp + i][16cb + r16].
 template <typename T>
 __device__ __forceinline__ void tile_x_tile(f32x4 (&acc)[4], const T* A, const T* B) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4, wave = (threadIdx.x >> 6) & 3;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -160,7 +159,7 @@ __device__ __forceinline__ void np_forward(NpRow& n, const T* W, const typename 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float zv = n.z[fb][i];
-      const float mv = zv > 0.f ? zv + 1.f : exp2f(zv * kLog2e);
+      const float mv = zv > 0.f ? zv + 1.f : __builtin_amdgcn_exp2f(zv * kLog2e);
       n.m[fb][i] = mv;
       nm2 += mv * mv;
     }
@@ -200,7 +199,7 @@ __device__ __forceinline__ float np_backward(const NpRow& n, f32x4 (&dphi)[4]) {
 // W^T with the features pk-permuted, [dim][pk_pos(f)], into an LDS tile
 template <typename T>
 __device__ __forceinline__ void load_wt(T* lds, const T* W) {
-  for (int e = threadIdx.x; e < BF * BD; e += 256) {
+  for (int e = threadIdx.x; e < BF * BD; e += blockDim.x) {
     const int f = e >> 6, dd = e & 63;
     lds[Swz<T, 64>::off(dd, pk_pos(f))] = W[e];
   }
@@ -210,6 +209,12 @@ __device__ __forceinline__ void load_wt(T* lds, const T* W) {
 // operations of this wave are outstanding
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// buffers of the local-key kernel's step tiles in bf16 (2: the next step's copies overlap
+// this one's work; 1 leaves room for more workgroups per CU)
+constexpr int kLocalBuffers = 1;
+// query heads per dq workgroup in bf16 when the group size is even (1 or 2)
+constexpr int kDqHeads = 1;
+
 // s_waitcnt immediate that waits for LDS (and scalar memory) only
 constexpr int kLgkmWait0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 
@@ -218,6 +223,14 @@ __device__ __forceinline__ void lds_sync() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
+}
+
+// Work index of workgroup L out of n: the hardware deals workgroups to the eight XCDs in
+// turn (L on XCD L % 8), so consecutive work indices, which share data, are given to
+// workgroups of one XCD and meet in its L2.
+__device__ __forceinline__ int xcd_work(int L, int n) {
+  const int per = n >> 3, rem = n & 7, x = L & 7, slot = L >> 3;
+  return x * per + min(x, rem) + slot;
 }
 
 // selection bit mask of complete chunk c from the ascending positions (entries outside
@@ -322,43 +335,96 @@ __global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, l
   const long long bh = gid / BR, e = gid % BR;
   float* p = ust + bh * nC * BR + e;
   float acc = 0.f, p1 = 0.f, p2 = 0.f;
-  for (int c = 0; c < nC; ++c) {
-    const float cur = p[static_cast<long long>(c) * BR];
-    acc += p2;
-    p[static_cast<long long>(c) * BR] = acc;
-    p2 = p1;
-    p1 = cur;
+  constexpr int U = 8;  // loads of U chunks in flight together
+  for (int c0 = 0; c0 < nC; c0 += U) {
+    float cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = c0 + u < nC ? p[static_cast<long long>(c0 + u) * BR] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nC) {
+        acc += p2;
+        p[static_cast<long long>(c0 + u) * BR] = acc;
+      }
+      p2 = p1;
+      p1 = cur[u];
+    }
   }
 }
 
-// R_c = sum over chunks >= c+2 of the group's per-chunk sums; one thread per (b, KV head, element)
-__global__ __launch_bounds__(256) void bwd_scan_rev_kernel(const float* apart, float* rst, int nC, int G, int Hkv,
-                                                           long long n_elems) {
+// R_c = sum over chunks >= c+2 of the group's per-chunk sums, as a segmented scan over
+// chunks: bwd_rev_seg_kernel sums each segment of kRevSeg chunks (and the group's heads),
+// bwd_rev_scan_kernel starts from the later segments' total and scans its own segment down.
+// One thread per (b, KV head, segment, element) in both.
+constexpr int kRevSeg = 16;
+
+__global__ __launch_bounds__(256) void bwd_rev_seg_kernel(const float* apart, float* segsum, int nC, int G,
+                                                          int Hkv, int nseg, long long n_elems) {
   const long long gid = blockIdx.x * 256LL + threadIdx.x;
   if (gid >= n_elems) return;
-  const long long bh = gid / BR, e = gid % BR;
+  const long long e = gid % BR, seg = (gid / BR) % nseg, bh = gid / (BR * nseg);
   const long long b = bh / Hkv, h = bh % Hkv;
   const long long hq0 = b * Hkv * G + h * G;
+  const int c0 = static_cast<int>(seg) * kRevSeg, c1 = min(nC, c0 + kRevSeg);
   float acc = 0.f;
-  for (int c = nC - 1; c >= 0; --c) {
-    if (c + 2 <= nC - 1) {
-      float s = 0.f;
-      for (int g = 0; g < G; ++g) s += apart[((hq0 + g) * nC + c + 2) * BR + e];
-      acc += s;
+  for (int g = 0; g < G; ++g) {
+    const float* p = apart + (hq0 + g) * nC * BR + e;
+    float x[kRevSeg];
+#pragma unroll
+    for (int u = 0; u < kRevSeg; ++u) x[u] = c0 + u < c1 ? p[static_cast<long long>(c0 + u) * BR] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kRevSeg; ++u) acc += x[u];
+  }
+  segsum[gid] = acc;
+}
+
+__global__ __launch_bounds__(256) void bwd_rev_scan_kernel(const float* apart, const float* segsum, float* rst,
+                                                           int nC, int G, int Hkv, int nseg, long long n_elems) {
+  const long long gid = blockIdx.x * 256LL + threadIdx.x;
+  if (gid >= n_elems) return;
+  const long long e = gid % BR, seg = (gid / BR) % nseg, bh = gid / (BR * nseg);
+  const long long b = bh / Hkv, h = bh % Hkv;
+  const long long hq0 = b * Hkv * G + h * G;
+  const int c0 = static_cast<int>(seg) * kRevSeg, c1 = min(nC, c0 + kRevSeg);
+  float acc = 0.f;  // sum over the chunks of later segments
+  for (long long s2 = nseg - 1; s2 > seg; --s2) acc += segsum[(bh * nseg + s2) * BR + e];
+  float x[kRevSeg];
+#pragma unroll
+  for (int u = 0; u < kRevSeg; ++u) x[u] = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const float* p = apart + (hq0 + g) * nC * BR + e;
+#pragma unroll
+    for (int u = 0; u < kRevSeg; ++u)
+      if (c0 + u < c1) x[u] += p[static_cast<long long>(c0 + u) * BR];
+  }
+  float* r = rst + bh * nC * BR + e;
+#pragma unroll
+  for (int u = kRevSeg - 1; u >= 0; --u) {
+    const int c = c0 + u;
+    if (c < c1) {
+      acc += x[u];  // acc = sum over chunks >= c
+      if (c >= 2) r[static_cast<long long>(c - 2) * BR] = acc;
     }
-    rst[(bh * nC + c) * BR + e] = acc;
+  }
+  if (seg == nseg - 1) {  // no chunk lies two or more after the last two
+    r[static_cast<long long>(nC - 1) * BR] = 0.f;
+    if (nC >= 2) r[static_cast<long long>(nC - 2) * BR] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
+// NH query heads of one KV head per workgroup (four waves each, 16 queries per wave): the
+// key tiles each copy brings serve NH x 64 queries.
+template <typename T, int NH>
+__global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
-  // six tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5
-  __shared__ __attribute__((aligned(16))) T lds[6][64 * 64];
-  __shared__ float s_red[4][64];
+  constexpr int NSLOT = 4 * NH > 6 ? 4 * NH : 6;
+  // tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5; the
+  // closing products use slots 4 hs .. 4 hs + 3 for head hs
+  __shared__ __attribute__((aligned(16))) T lds[NSLOT][64 * 64];
+  __shared__ float s_red[NH][4][64];
   T* const t_k = lds[0];
   T* const t_v = lds[1];
   T* const t_kt = lds[2];
@@ -366,12 +432,17 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   T* const t_pkt = lds[4];
 
   const Dims& d = a.d;
-  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  // work index: chunk fastest, then head group, then batch (the heads of one KV head
+  // share its compact tiles)
+  const int ngrp = d.Hq / NH;
+  const int w = xcd_work(blockIdx.x, gridDim.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int hs = wave >> 2, wl = wave & 3;  // head slot, wave within the head
+  const int c = w % d.nC, hq = ((w / d.nC) % ngrp) * NH + hs, b = w / (d.nC * ngrp);
   const int h = hq / d.G;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const long long bhq = static_cast<long long>(b) * d.Hq + hq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
-  const int qrow = wave * 16 + r16;
+  const int qrow = wl * 16 + r16;
   const long long i = 64LL * c + qrow;  // this lane column's query
   const bool qvalid = i < d.T;
   const float scale2 = kLog2e * 0.125f;  // log2(e) / sqrt(64)
@@ -440,14 +511,14 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (sa[kb][e]) ps += exp2f(a2[kb][e] - mn);
+        if (sa[kb][e]) ps += __builtin_amdgcn_exp2f(a2[kb][e] - mn);
     ps = xor_sum_groups(ps);
-    l = any ? l * exp2f(mx2 - mn) + ps : l;
+    l = any ? l * __builtin_amdgcn_exp2f(mx2 - mn) + ps : l;
     mx2 = mn;
   };
   // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
   // nsel_c read as zeros (the copies' range ends there)
-  using Dma = DmaTile<T, 64, 64, 4>;
+  using Dma = DmaTile<T, 64, 64, 4 * NH>;
   Dma dma;
   dma.init(64);
   constexpr int ES = static_cast<int>(sizeof(T));
@@ -544,7 +615,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool ok = kb * 16 + 4 * grp + e < nv;
-        const float p = ok ? exp2f(s[kb][e] * scale2 - L2) : 0.f;
+        const float p = ok ? __builtin_amdgcn_exp2f(s[kb][e] * scale2 - L2) : 0.f;
         s[kb][e] = p * (dp[kb][e] - delta);
       }
     rows_x_acc<T>(dqt, lds[sl + 2], s);
@@ -575,7 +646,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
         const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
         const bool sa = vis && (inwin || sel);
         const bool la = vis && !(inwin || sel);
-        const float p = sa ? exp2f(s[kb][e] * scale2 - L2) : 0.f;
+        const float p = sa ? __builtin_amdgcn_exp2f(s[kb][e] * scale2 - L2) : 0.f;
         const float g = dp[kb][e] - delta;
         s[kb][e] = p * g;
         lw[kb][e] = la ? g * einv : 0.f;
@@ -634,15 +705,19 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
   T* qt = static_cast<T*>(a.qt) + qc * BD * 64;
   T* dot = static_cast<T*>(a.dot) + qc * BD * 64;
   const int pq = pk_pos(qrow);
-  __syncthreads();  // t_k (W^T) is reused below
+  T* const e_phq = lds[4 * hs];      // e^{-L} phi(q)^T of this head
+  T* const e_do = lds[4 * hs + 1];   // dout^T
+  T* const e_dz = lds[4 * hs + 2];   // dz^T
+  T* const e_q = lds[4 * hs + 3];    // q^T
+  __syncthreads();  // slot 0 (W^T) is reused below
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int f = fb * 16 + 4 * grp + e;
       phqt[f * 64 + pq] = TT::from_f(phq[fb][e]);
-      t_k[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);  // e^{-L} phi(q)^T
-      t_pk[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);        // dz^T
+      e_phq[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);
+      e_dz[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);
     }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
@@ -651,32 +726,33 @@ __global__ __launch_bounds__(256, 3) void bwd_dq_kernel(BwdArgs a) {
       const int dd = ks * 32 + grp * 8 + e;
       qt[dd * 64 + pq] = qf[ks][e];
       dot[dd * 64 + pq] = dof[ks][e];
-      t_v[SW::off(dd, pq)] = dof[ks][e];
-      t_kt[SW::off(dd, pq)] = qf[ks][e];
+      e_do[SW::off(dd, pq)] = dof[ks][e];
+      e_q[SW::off(dd, pq)] = qf[ks][e];
     }
-  // a_c partial: sum over the workgroup's queries of e^{-L} Delta phi(q)
+  // a_c partial: sum over the head's 64 queries of e^{-L} Delta phi(q)
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta : 0.f));
-      if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
+      if (r16 == 0) s_red[hs][wl][fb * 16 + 4 * grp + e] = v;
     }
   __syncthreads();
   float* ap = a.apart + qc * BR;
-  if (tid < 64) ap[BF * BD + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+  if (wl == 0)
+    ap[BF * BD + lane] = ((s_red[hs][0][lane] + s_red[hs][1][lane]) + s_red[hs][2][lane]) + s_red[hs][3][lane];
   f32x4 acc[4];
-  tile_x_tile<T>(acc, t_k, t_v);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
+  tile_x_tile<T>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ap[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
-  tile_x_tile<T>(acc, t_pk, t_kt);  // dW[f][d] = sum_q dz[f] q[d]
+    for (int e = 0; e < 4; ++e) ap[(wl * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+  tile_x_tile<T>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
   float* wp = a.dwq + qc * (BF * BD);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wp[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+    for (int e = 0; e < 4; ++e) wp[(wl * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -694,13 +770,17 @@ __global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * 64];  // [buffer][q, dout, q^T, dout^T]
   __shared__ float s_ld[2][128];
   const Dims& d = a.d;
-  const int split = blockIdx.y;
-  const long long bh = blockIdx.z;
+  // work index: row group fastest, then query slice, then (batch, KV head): the row groups
+  // of one slice read the same query tiles
+  const int ngroups = (a.ntiles + 1) / 2;
+  const int w = xcd_work(blockIdx.x, gridDim.x);
+  const int grp_id = w % ngroups, split = (w / ngroups) % a.nsplit;
+  const long long bh = w / (ngroups * a.nsplit);
   const int b = static_cast<int>(bh / d.Hkv), h = static_cast<int>(bh % d.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const float scale2 = kLog2e * 0.125f;
   const int nsel = d.nCc * d.topk;
-  const int row0 = blockIdx.x * 128;
+  const int row0 = grp_id * 128;
   const int n = row0 + wave * 16 + r16;  // this lane column's compact row
   const bool nin = n < a.ntiles * 64;     // inside the buffers (rows past nsel are zeros)
   const int ckey = n < nsel ? n / d.topk : 0x3fffffff;
@@ -714,11 +794,11 @@ __global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
       vf[ks] = nin ? TT::load8(vr + ks * 32 + grp * 8) : TT::zero();
     }
   }
-  // query chunks [c_lo, nC) split evenly over gridDim.y; steps run over (chunk, head)
+  // query chunks: slice `split` of [0, nC) (the same slices for every row group), from the
+  // group's first chunk + 2 on; steps run over (chunk, head)
   const int c_lo = row0 / d.topk + 2;
-  const int span = max(0, d.nC - c_lo);
-  const int per = (span + gridDim.y - 1) / gridDim.y;
-  const int cb0 = c_lo + split * per, cb1 = min(d.nC, cb0 + per);
+  const int per = (d.nC + a.nsplit - 1) / a.nsplit;
+  const int cb0 = max(c_lo, split * per), cb1 = min(d.nC, (split + 1) * per);
   const int nsteps = max(0, cb1 - cb0) * d.G;
   Dma dma;
   dma.init(64);
@@ -781,7 +861,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int qr = qb * 16 + 4 * grp + e;
-        const float p = on ? exp2f(s[qb][e] * scale2 - sl[2 * qr]) : 0.f;
+        const float p = on ? __builtin_amdgcn_exp2f(s[qb][e] * scale2 - sl[2 * qr]) : 0.f;
         s[qb][e] = p * (dp[qb][e] - sl[2 * qr + 1]);
         dp[qb][e] = p;
       }
@@ -805,13 +885,15 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
-  __shared__ __attribute__((aligned(16))) T t_q[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_do[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_qt[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_dot[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_pq[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_pqt[64 * 64];
-  __shared__ float s_ld[64 * 2];
+  using Dma = DmaTile<T, 64, 64, 4>;
+  constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr int NBUF = sizeof(T) == 2 ? kLocalBuffers : 1;
+  // per step: q rows, dout rows, q^T, dout^T, phi(q) rows, phi(q)^T of one (head, chunk)
+  __shared__ __attribute__((aligned(16))) T lds[NBUF][6][64 * 64];
+  __shared__ float s_ld[NBUF][128];
+  T* const t_q = lds[0][0];
+  T* const t_do = lds[0][1];
+  T* const t_qt = lds[0][2];
   const Dims& d = a.d;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
@@ -832,25 +914,69 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
     phk[ks] = TT::load8(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + j) * BF + ks * 32 + grp * 8);
   }
   f32x4 dkt[4] = {}, dvt[4] = {}, dpk[4] = {};
-  for (int g = 0; g < d.G; ++g) {
-    const long long hq = static_cast<long long>(b) * d.Hq + h * d.G + g;  // b*Hq + query head
-    for (int cq = c; cq <= c + 1 && cq < d.nC; ++cq) {
-      const long long qc = hq * d.nC + cq;
-      const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (h * d.G + g)) * BD;
-      const int nv = min(64, d.T - 64 * cq);
-      __syncthreads();
-      tile_load<T>(t_q, static_cast<const T*>(a.q) + r0, static_cast<long long>(d.Hq) * BD, nv);
-      tile_load<T>(t_do, static_cast<const T*>(a.dout) + r0, static_cast<long long>(d.Hq) * BD, nv);
-      tile_load<T>(t_qt, static_cast<const T*>(a.qt) + qc * BD * 64, 64, 64);
-      tile_load<T>(t_dot, static_cast<const T*>(a.dot) + qc * BD * 64, 64, 64);
-      tile_load<T>(t_pq, static_cast<const T*>(a.phiq) + (hq * d.nC * 64 + 64LL * cq) * BF, BF, 64);
-      tile_load<T>(t_pqt, static_cast<const T*>(a.phiqt) + qc * BF * 64, 64, 64);
-      if (tid < 128) s_ld[tid] = a.ld[(hq * d.nC * 64 + 64LL * cq) * 2 + tid];
-      __syncthreads();
+  // steps over (query head g, query chunk cq in {c, c+1}); the tiles arrive by
+  // buffer -> LDS copies, one step ahead when two buffers fit
+  const int ncq = c + 1 < d.nC ? 2 : 1;
+  const int nsteps = d.G * ncq;
+  Dma dma, dmq;
+  dma.init(64);
+  dmq.init(d.Hq * BD);
+  auto step_of = [&](int st, long long& hq, int& cq) {
+    hq = static_cast<long long>(b) * d.Hq + h * d.G + st / ncq;  // b*Hq + query head
+    cq = c + st % ncq;
+  };
+  auto issue = [&](int st) {
+    long long hq;
+    int cq;
+    step_of(st, hq, cq);
+    const long long qc = hq * d.nC + cq;
+    const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (hq - static_cast<long long>(b) * d.Hq)) * BD;
+    const int nv = min(64, d.T - 64 * cq);
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * BD + BD) * ES);
+    T(*dst)[64 * 64] = lds[st % NBUF];
+    dmq.issue(dst[0], make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
+    dmq.issue(dst[1], make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
+    dma.issue(dst[2], make_rsrc(static_cast<const T*>(a.qt) + qc * BD * 64, BD * 64 * ES), 0);
+    dma.issue(dst[3], make_rsrc(static_cast<const T*>(a.dot) + qc * BD * 64, BD * 64 * ES), 0);
+    dma.issue(dst[4], make_rsrc(static_cast<const T*>(a.phiq) + qc * 64 * BF, 64 * BF * ES), 0);
+    dma.issue(dst[5], make_rsrc(static_cast<const T*>(a.phiqt) + qc * BF * 64, BF * 64 * ES), 0);
+  };
+  auto ld_of = [&](int st) {
+    long long hq;
+    int cq;
+    step_of(st, hq, cq);
+    return a.ld[(hq * d.nC + cq) * 128 + (tid & 127)];
+  };
+  float ldn = ld_of(0);
+  if (NBUF == 2) issue(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const float ldc = ldn;
+    if (NBUF == 2) {
+      if (st + 1 < nsteps) {
+        ldn = ld_of(st + 1);
+        issue(st + 1);
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(6 * Dma::PER_WAVE + 1));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      }
+    } else {
+      issue(st);
+      if (st + 1 < nsteps) ldn = ld_of(st + 1);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    }
+    if (tid < 128) s_ld[st % NBUF][tid] = ldc;
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+    lds_sync();
+    long long hq;
+    int cq;
+    step_of(st, hq, cq);
+    T(*cur)[64 * 64] = lds[st % NBUF];
+    const float* sl = s_ld[st % NBUF];
+    {
       f32x4 s[4], dp[4], lw[4];
-      rows_x_frag<T>(s, t_q, kf);
-      rows_x_frag<T>(dp, t_do, vf);
-      rows_x_frag<T>(lw, t_pq, phk);
+      rows_x_frag<T>(s, cur[0], kf);
+      rows_x_frag<T>(dp, cur[1], vf);
+      rows_x_frag<T>(lw, cur[4], phk);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -862,18 +988,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
           const bool sel = cq > c && selj;
           const bool sa = vis && (inwin || sel);
           const bool la = vis && !(inwin || sel);
-          const float L2 = s_ld[2 * qr], dl = s_ld[2 * qr + 1];
-          const float einv = exp2f(-L2);
-          const float p = sa ? exp2f(s[qb][e] * scale2 - L2) : 0.f;
+          const float L2 = sl[2 * qr], dl = sl[2 * qr + 1];
+          const float einv = __builtin_amdgcn_exp2f(-L2);
+          const float p = sa ? __builtin_amdgcn_exp2f(s[qb][e] * scale2 - L2) : 0.f;
           const float gg = dp[qb][e] - dl;
           s[qb][e] = p * gg;                           // dS
           dp[qb][e] = p + (la ? lw[qb][e] * einv : 0.f);  // weight of v_j in out_i
           lw[qb][e] = la ? gg * einv : 0.f;            // g
         }
-      rows_x_acc<T>(dvt, t_dot, dp);
-      rows_x_acc<T>(dkt, t_qt, s);
-      rows_x_acc<T>(dpk, t_pqt, lw);
+      rows_x_acc<T>(dvt, cur[3], dp);
+      rows_x_acc<T>(dkt, cur[2], s);
+      rows_x_acc<T>(dpk, cur[5], lw);
     }
+    lds_sync();
   }
   // queries of chunks >= c+2 through R_c, r_c (unselected keys only)
   if (c + 2 < d.nC) {
@@ -972,17 +1099,25 @@ __global__ __launch_bounds__(256) void bwd_dw_part_kernel(const float* dwq, cons
   const int per = (nitems + gridDim.y - 1) / gridDim.y;
   const int i0 = blockIdx.y * per, i1 = min(nitems, i0 + per);
   float acc = 0.f;
-  for (int it = i0; it < i1; ++it) {
-    long long src;
-    if (it < nq) {
-      const int b = it / (G * nC), g = (it / nC) % G, c = it % nC;
-      src = ((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * (BF * BD) + fd;
-      acc += dwq[src];
-    } else {
-      const int it2 = it - nq, b = it2 / nC, c = it2 % nC;
-      src = ((static_cast<long long>(b) * Hkv + h) * nC + c) * (BF * BD) + fd;
-      acc += dwk[src];
+  constexpr int U = 8;  // loads of U items in flight together
+  for (int it0 = i0; it0 < i1; it0 += U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u;
+      x[u] = 0.f;
+      if (it < i1) {
+        if (it < nq) {
+          const int b = it / (G * nC), g = (it / nC) % G, c = it % nC;
+          x[u] = dwq[((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * (BF * BD) + fd];
+        } else {
+          const int it2 = it - nq, b = it2 / nC, c = it2 % nC;
+          x[u] = dwk[((static_cast<long long>(b) * Hkv + h) * nC + c) * (BF * BD) + fd];
+        }
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += x[u];
   }
   part[static_cast<long long>(blockIdx.y) * Hkv * BF * BD + e] = acc;
 }
@@ -1008,19 +1143,30 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
     if ((e = launch_fill_zero(a.ksel, tb, s)) != hipSuccess) return e;
     if ((e = launch_fill_zero(a.vsel, tb, s)) != hipSuccess) return e;
   }
-  const dim3 gk(d.nC, d.Hkv, d.B), gq(d.nC, d.Hq, d.B);
+  const dim3 gk(d.nC, d.Hkv, d.B);
   hipLaunchKernelGGL(bwd_kprep_kernel<T>, gk, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
   const long long ne = static_cast<long long>(d.B) * d.Hkv * BR;
   const dim3 gs(static_cast<unsigned>((ne + 255) / 256));
   hipLaunchKernelGGL(bwd_scan_fwd_kernel, gs, dim3(256), 0, s, a.ustate, d.nC, ne);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel<T>, gq, dim3(256), 0, s, a);
+  if (kDqHeads == 2 && sizeof(T) == 2 && d.G % 2 == 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 1>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scan_rev_kernel, gs, dim3(256), 0, s, a.apart, a.rstate, d.nC, d.G, d.Hkv, ne);
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
+  {
+    const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;
+    const long long nr = ne * nseg;
+    const dim3 gr(static_cast<unsigned>((nr + 255) / 256));
+    hipLaunchKernelGGL(bwd_rev_seg_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, d.nC, d.G, d.Hkv, nseg, nr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_rev_scan_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, a.rstate, d.nC, d.G, d.Hkv, nseg,
+                       nr);
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
+  }
   if (a.ntiles > 0) {
-    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3((a.ntiles + 1) / 2, a.nsplit, d.B * d.Hkv), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3((a.ntiles + 1) / 2 * a.nsplit * d.B * d.Hkv), dim3(512), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(5)) != hipSuccess) return e;

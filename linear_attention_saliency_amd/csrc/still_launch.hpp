@@ -124,6 +124,7 @@ struct BwdArgs {
   float* ld;               // [B,Hq,nC*64,2]: (log2 of the normaliser, Delta)
   float* apart;            // [B,Hq,nC,R]: per-chunk sum of e^{-L} phi(q) dout^T, e^{-L} Delta phi(q)
   float* rstate;           // [B,Hkv,nC,R]: R_c, r_c (chunks >= c+2)
+  float* segsum;           // [B,Hkv,ceil(nC/16),R]: per-segment sums of the scan behind R
   float* dwq;              // [B,Hq,nC,DF*D]
   float* dwk;              // [B,Hkv,nC,DF*D]
   float* dkvsel;           // [nsplit,B,Hkv,ntiles*64,2,D]
