@@ -438,7 +438,11 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   const int w = xcd_work(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const int hs = wave >> 2, wl = wave & 3;  // head slot, wave within the head
-  const int c = w % d.nC, hq = ((w / d.nC) % ngrp) * NH + hs, b = w / (d.nC * ngrp);
+  // (divisions by run-time sizes leave the compiler unsure that these are uniform; telling
+  // it keeps the buffer descriptors in scalar registers)
+  const int c = __builtin_amdgcn_readfirstlane(w % d.nC);
+  const int hq = __builtin_amdgcn_readfirstlane(((w / d.nC) % ngrp) * NH + hs);
+  const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * ngrp));
   const int h = hq / d.G;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const long long bhq = static_cast<long long>(b) * d.Hq + hq;
@@ -495,23 +499,26 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
 
 
   // ---- pass 1: L = log2 of the normaliser
+  // online softmax sums over raw scores s = q.k: the running max mx2 and the exponents
+  // are in log2 units (s * scale2), the scale folded into one fma per score
   float mx2 = -kInf, l = 0.f;
-  auto online = [&](const f32x4 (&a2)[4], const bool (&sa)[4][4]) {
+  auto online = [&](const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
     float tm = -kInf;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (sa[kb][e]) tm = fmaxf(tm, a2[kb][e]);
-    tm = xor_max_groups(tm);
+      for (int e = 0; e < 4; ++e) tm = (!masked || sa[kb][e]) ? fmaxf(tm, sc[kb][e]) : tm;
+    tm = xor_max_groups(tm) * scale2;
     const float mn = fmaxf(mx2, tm);
     const bool any = mn != -kInf;  // the same in the four lanes of a query
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (sa[kb][e]) ps += __builtin_amdgcn_exp2f(a2[kb][e] - mn);
+      for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], scale2, -mn));
+        ps += (!masked || sa[kb][e]) ? pe : 0.f;
+      }
     ps = xor_sum_groups(ps);
     l = any ? l * __builtin_amdgcn_exp2f(mx2 - mn) + ps : l;
     mx2 = mn;
@@ -538,14 +545,15 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     f32x4 s[4];
     rows_x_frag<T>(s, lds[(t & 1) * 3], qf);
     bool sa[4][4];
+    if (nsel_c - t * 64 >= 64) {  // a full tile
+      online(s, sa, false);
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sa[kb][e] = t * 64 + kb * 16 + 4 * grp + e < nsel_c;
-        s[kb][e] *= scale2;
-      }
-    online(s, sa);
+        for (int e = 0; e < 4; ++e) sa[kb][e] = t * 64 + kb * 16 + 4 * grp + e < nsel_c;
+      online(s, sa, true);
+    }
     lds_sync();
   }
   for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
@@ -569,9 +577,8 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
         const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
         sa[kb][e] = vis && (inwin || sel);
         if (vis && !(inwin || sel)) dla += lw[kb][e];
-        s[kb][e] *= scale2;
       }
-    online(s, sa);
+    online(s, sa, true);
   }
   dla = xor_sum_groups(dla);
   float L2;
@@ -610,14 +617,21 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     f32x4 s[4], dp[4];
     rows_x_frag<T>(s, lds[sl], qf);
     rows_x_frag<T>(dp, lds[sl + 1], dof);
+    if (nv == 64) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = kb * 16 + 4 * grp + e < nv;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[kb][e] * scale2 - L2) : 0.f;
-        s[kb][e] = p * (dp[kb][e] - delta);
-      }
+        for (int e = 0; e < 4; ++e) s[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) * (dp[kb][e] - delta);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = kb * 16 + 4 * grp + e < nv;
+          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) : 0.f;
+          s[kb][e] = p * (dp[kb][e] - delta);
+        }
+    }
     rows_x_acc<T>(dqt, lds[sl + 2], s);
     lds_sync();
   }
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
         const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
         const bool sa = vis && (inwin || sel);
         const bool la = vis && !(inwin || sel);
-        const float p = sa ? __builtin_amdgcn_exp2f(s[kb][e] * scale2 - L2) : 0.f;
+        const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) : 0.f;
         const float g = dp[kb][e] - delta;
         s[kb][e] = p * g;
         lw[kb][e] = la ? g * einv : 0.f;
@@ -762,21 +776,23 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
 // query-side tiles (q rows, dout rows, q^T, dout^T) arrive by buffer -> LDS copies one
 // (chunk, head) step ahead, with that step's (L, Delta) prefetched into registers.
 template <typename T>
-__global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using Dma = DmaTile<T, 64, 64, 8>;
   constexpr int ES = static_cast<int>(sizeof(T));
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * 64];  // [buffer][q, dout, q^T, dout^T]
-  __shared__ float s_ld[2][128];
+  __shared__ __attribute__((aligned(16))) float s_ld[2][2][64];  // [buffer][L, Delta][query]
   const Dims& d = a.d;
   // work index: row group fastest, then query slice, then (batch, KV head): the row groups
   // of one slice read the same query tiles
   const int ngroups = (a.ntiles + 1) / 2;
   const int w = xcd_work(blockIdx.x, gridDim.x);
-  const int grp_id = w % ngroups, split = (w / ngroups) % a.nsplit;
-  const long long bh = w / (ngroups * a.nsplit);
-  const int b = static_cast<int>(bh / d.Hkv), h = static_cast<int>(bh % d.Hkv);
+  const int grp_id = __builtin_amdgcn_readfirstlane(w % ngroups);
+  const int split = __builtin_amdgcn_readfirstlane((w / ngroups) % a.nsplit);
+  const long long bh = __builtin_amdgcn_readfirstlane(w / (ngroups * a.nsplit));
+  const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(bh / d.Hkv));
+  const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % d.Hkv));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const float scale2 = kLog2e * 0.125f;
   const int nsel = d.nCc * d.topk;
@@ -806,7 +822,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
   dmq.init(d.Hq * BD);
   const long long hq0 = static_cast<long long>(b) * d.Hq + static_cast<long long>(h) * d.G;  // b*Hq + first head
   auto step_ptrs = [&](int st, long long& qc, long long& r0, int& nv) {
-    const int cq = cb0 + st / d.G, g = st % d.G;
+    const int cq = __builtin_amdgcn_readfirstlane(cb0 + st / d.G), g = __builtin_amdgcn_readfirstlane(st % d.G);
     qc = (hq0 + g) * d.nC + cq;
     r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + h * d.G + g) * BD;
     nv = min(64, d.T - 64 * cq);
@@ -843,28 +859,29 @@ __global__ __launch_bounds__(512) void bwd_dkv_far_kernel(BwdArgs a) {
     } else {
       __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     }
-    if (tid < 128) s_ld[st & 1][tid] = ldc;
+    if (tid < 128) s_ld[st & 1][tid & 1][tid >> 1] = ldc;
     __builtin_amdgcn_s_waitcnt(kLgkmWait0);  // the copies of the next step stay in flight
     lds_sync();
-    const int cq = cb0 + st / d.G;
+    const int cq = __builtin_amdgcn_readfirstlane(cb0 + st / d.G);
     const T* tq = lds[st & 1][0];
     const T* tdo = lds[st & 1][1];
     const T* tqt = lds[st & 1][2];
     const T* tdot = lds[st & 1][3];
-    const float* sl = s_ld[st & 1];
     f32x4 s[4], dp[4];
     rows_x_frag<T>(s, tq, kf);  // s[qb][e] = q[16 qb + 4 grp + e] . k
     rows_x_frag<T>(dp, tdo, vf);
     const bool on = cq >= ckey + 2;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4 lq = *reinterpret_cast<const f32x4*>(&s_ld[st & 1][0][qb * 16 + 4 * grp]);
+      const f32x4 dq4 = *reinterpret_cast<const f32x4*>(&s_ld[st & 1][1][qb * 16 + 4 * grp]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int qr = qb * 16 + 4 * grp + e;
-        const float p = on ? __builtin_amdgcn_exp2f(s[qb][e] * scale2 - sl[2 * qr]) : 0.f;
-        s[qb][e] = p * (dp[qb][e] - sl[2 * qr + 1]);
+        const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], scale2, -lq[e])) : 0.f;
+        s[qb][e] = p * (dp[qb][e] - dq4[e]);
         dp[qb][e] = p;
       }
+    }
     rows_x_acc<T>(dvt, tdot, dp);
     rows_x_acc<T>(dkt, tqt, s);
     lds_sync();
@@ -890,7 +907,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   constexpr int NBUF = sizeof(T) == 2 ? kLocalBuffers : 1;
   // per step: q rows, dout rows, q^T, dout^T, phi(q) rows, phi(q)^T of one (head, chunk)
   __shared__ __attribute__((aligned(16))) T lds[NBUF][6][64 * 64];
-  __shared__ float s_ld[NBUF][128];
+  __shared__ __attribute__((aligned(16))) float s_ld[NBUF][2][64];  // [buffer][L, Delta][query]
   T* const t_q = lds[0][0];
   T* const t_do = lds[0][1];
   T* const t_qt = lds[0][2];
@@ -922,8 +939,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   dma.init(64);
   dmq.init(d.Hq * BD);
   auto step_of = [&](int st, long long& hq, int& cq) {
-    hq = static_cast<long long>(b) * d.Hq + h * d.G + st / ncq;  // b*Hq + query head
-    cq = c + st % ncq;
+    hq = static_cast<long long>(b) * d.Hq + h * d.G + __builtin_amdgcn_readfirstlane(st / ncq);  // b*Hq + query head
+    cq = c + __builtin_amdgcn_readfirstlane(st % ncq);
   };
   auto issue = [&](int st) {
     long long hq;
@@ -964,21 +981,22 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
       if (st + 1 < nsteps) ldn = ld_of(st + 1);
       __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     }
-    if (tid < 128) s_ld[st % NBUF][tid] = ldc;
+    if (tid < 128) s_ld[st % NBUF][tid & 1][tid >> 1] = ldc;
     __builtin_amdgcn_s_waitcnt(kLgkmWait0);
     lds_sync();
     long long hq;
     int cq;
     step_of(st, hq, cq);
     T(*cur)[64 * 64] = lds[st % NBUF];
-    const float* sl = s_ld[st % NBUF];
     {
       f32x4 s[4], dp[4], lw[4];
       rows_x_frag<T>(s, cur[0], kf);
       rows_x_frag<T>(dp, cur[1], vf);
       rows_x_frag<T>(lw, cur[4], phk);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < 4; ++qb) {
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(&s_ld[st % NBUF][0][qb * 16 + 4 * grp]);
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(&s_ld[st % NBUF][1][qb * 16 + 4 * grp]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qr = qb * 16 + 4 * grp + e;
@@ -988,14 +1006,15 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
           const bool sel = cq > c && selj;
           const bool sa = vis && (inwin || sel);
           const bool la = vis && !(inwin || sel);
-          const float L2 = sl[2 * qr], dl = sl[2 * qr + 1];
+          const float L2 = lq[e], dl = dq4[e];
           const float einv = __builtin_amdgcn_exp2f(-L2);
-          const float p = sa ? __builtin_amdgcn_exp2f(s[qb][e] * scale2 - L2) : 0.f;
+          const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], scale2, -L2)) : 0.f;
           const float gg = dp[qb][e] - dl;
           s[qb][e] = p * gg;                           // dS
           dp[qb][e] = p + (la ? lw[qb][e] * einv : 0.f);  // weight of v_j in out_i
           lw[qb][e] = la ? gg * einv : 0.f;            // g
         }
+      }
       rows_x_acc<T>(dvt, cur[3], dp);
       rows_x_acc<T>(dkt, cur[2], s);
       rows_x_acc<T>(dpk, cur[5], lw);
