@@ -50,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "lse", "saliency", "route", "route_margins", "np_map", "sa_mask_row", "brute",
-    "brute_rows", "attend", "attend_backward", "DecodeOracle",
+    "brute_rows", "attend", "attend_backward", "future_attention_mass", "selection_overlap", "DecodeOracle",
 ]
 
 
@@ -363,6 +363,49 @@ def attend(q, k, v, w_phi, window: int, chunk: int, top_k: int, sel=None,
                 out[b, i0:i1, hq] = np.where(safe, num / np.where(safe, den, 1.0), 0.0)
     if return_routing:
         return out, s_kv, sel
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Local-global consistency of the saliency  ([P2] excerpt: the local score is meant to
+# predict whether a token will still be attended once it is far history, with a reported
+# overlap; [P1] section "Self-Saliency Score": selection accuracy close to global attention)
+# --------------------------------------------------------------------------------------
+
+def future_attention_mass(q, k, window: int, q_from: int = 0):
+    """Attention each key receives from far-future queries under full causal softmax.
+
+    For KV head h and key j: F_j = sum over the group's query heads g and over queries
+    i >= j + max(window, 0) (j is outside i's window, i.e. far history for i) of
+    p_ij = e^{a_ij} / sum_{l <= i} e^{a_il}, a_ij = q_i . k_j / sqrt(D).
+    q_from: only queries i >= q_from are summed (the values of keys j >= q_from - window
+    are then exact). Returns F [B, Hkv, T] fp64.
+    """
+    q, k = _f64(q), _f64(k)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = _check_group(Hq, Hkv)
+    w = max(window, 0)
+    F = np.zeros((B, Hkv, T))
+    i = np.arange(q_from, T)[:, None]
+    j = np.arange(T)[None, :]
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            a = q[b, q_from:, hq] @ k[b, :, h].T / math.sqrt(D)
+            a = np.where(j <= i, a, -np.inf)
+            p = np.exp(a - lse(a, axis=1)[:, None])
+            F[b, h] += np.where(i >= j + w, p, 0.0).sum(axis=0)
+    return F
+
+
+def selection_overlap(sel_a, sel_b) -> np.ndarray:
+    """Tokens two per-chunk selections have in common: sel_a, sel_b [B, Hkv, nC, k]
+    -> counts [B, Hkv, nC]."""
+    sel_a, sel_b = np.asarray(sel_a), np.asarray(sel_b)
+    out = np.zeros(sel_a.shape[:3], dtype=np.int64)
+    for idx in np.ndindex(*sel_a.shape[:3]):
+        out[idx] = len(set(sel_a[idx].tolist()) & set(sel_b[idx].tolist()))
     return out
 
 

@@ -440,3 +440,48 @@ def test_backward_tail_rows_equal_full_gradients():
     for a, b in zip(full[:3], tail[:3]):
         np.testing.assert_allclose(b[:, 27:], a[:, 27:], rtol=0, atol=1e-12)
     assert np.abs(tail[1][:, :27]).max() > 0  # earlier keys get only part of their gradient
+
+
+# ----------------------------------------------------------------------------- local-global consistency
+
+def test_future_attention_mass_brute_force():
+    """Double loop over (query, key) with explicit softmax rows."""
+    T, Hq, Hkv, D, w = 11, 4, 2, 8, 3
+    q, k, _, _ = _case(1, T, Hq, Hkv, D, 4, seed=21, scale=1.3)
+    got = O.future_attention_mass(q, k, w)
+    want = np.zeros((1, Hkv, T))
+    for hq in range(Hq):
+        h = hq // (Hq // Hkv)
+        for i in range(T):
+            logits = [float(np.dot(q[0, i, hq], k[0, j, h])) / math.sqrt(D) for j in range(i + 1)]
+            zs = sum(math.exp(x) for x in logits)
+            for j in range(i + 1):
+                if i - j >= w:
+                    want[0, h, j] += math.exp(logits[j]) / zs
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+def test_future_attention_mass_uniform_closed_form():
+    """q = 0 makes every causal row uniform, p_ij = 1/(i+1), so F_j = G (H_T - H_{j+w}) with
+    H_n the harmonic numbers."""
+    T, Hq, Hkv, w = 40, 3, 1, 5
+    _, k, _, _ = _case(1, T, Hq, Hkv, 8, 4, seed=2)
+    q = np.zeros((1, T, Hq, 8))
+    got = O.future_attention_mass(q, k, w)[0, 0]
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1))])
+    want = np.array([Hq * (H[T] - H[min(j + w, T)]) for j in range(T)])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_future_attention_mass_tail_rows():
+    T, w = 30, 4
+    q, k, _, _ = _case(1, T, 2, 1, 8, 4, seed=6, scale=1.5)
+    full = O.future_attention_mass(q, k, w)
+    tail = O.future_attention_mass(q, k, w, q_from=20)
+    np.testing.assert_allclose(tail[..., 20 - w:], full[..., 20 - w:], rtol=0, atol=1e-13)
+
+
+def test_selection_overlap_counts():
+    a = np.array([[[[0, 1, 2], [64, 70, 80]]]])
+    b = np.array([[[[1, 2, 5], [64, 70, 80]]]])
+    assert O.selection_overlap(a, b).tolist() == [[[2, 3]]]
