@@ -245,6 +245,27 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
                          void* dq, void* dk, void* dv, float* dw_phi, void* workspace, size_t ws_bytes,
                          hipStream_t stream, hipEvent_t* events);
 
+/* Bytes of scratch still_future_attention_mass needs (0 if cfg is invalid or unsupported). */
+size_t still_future_attention_mass_workspace_bytes(const still_config* cfg);
+
+/* Attention each key receives from far-future queries under full causal softmax, the global
+ * reference for the routing's local-global consistency ([P2]: the local score is meant to
+ * predict whether a token is still attended once it is far history; [P1] section
+ * "Self-Saliency Score"). For KV head h and key j:
+ *   mass_out[b, h, j] = sum over the group's query heads and over queries i >= j + window of
+ *                       softmax_{l <= i}(q_i . k_l / sqrt(head_dim))_j
+ *   q [batch, seq_len, n_q_heads, head_dim], k [batch, seq_len, n_kv_heads, head_dim] (dtype);
+ *   mass_out [batch, n_kv_heads, seq_len] fp32 (written).
+ * Supported for head_dim = 64 (feat_dim and top_k are not used). Sums run in a fixed order. */
+int still_future_attention_mass(const still_config* cfg, const void* q, const void* k, float* mass_out,
+                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Tokens two per-chunk selections share: sel_a, sel_b [batch, n_kv_heads, seq_len/chunk,
+ * top_k] int32 -> common_out [batch, n_kv_heads, seq_len/chunk] int32 (with still_select_topk
+ * on the mass above, the overlap of the routing with the global choice). */
+int still_selection_overlap(const still_config* cfg, const int32_t* sel_a, const int32_t* sel_b,
+                            int32_t* common_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,6 +214,38 @@ BwdLayout bwd_layout(const still_config* c) {
   return L;
 }
 
+// ---- future attention mass workspace
+constexpr int kMassChunksPerSlice = 16;
+
+struct MassLayout {
+  size_t lse, part, total;
+  int nsplit, per;
+};
+
+MassLayout mass_layout(const still_config* c) {
+  const Dims d = dims_of(c);
+  MassLayout L;
+  L.per = kMassChunksPerSlice;
+  L.nsplit = (d.nC + L.per - 1) / L.per;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.lse = take(static_cast<size_t>(d.B) * d.Hq * d.nC * 64 * sizeof(float));
+  L.part = take(static_cast<size_t>(L.nsplit) * d.B * d.Hkv * d.T * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+int check_mass_cfg(const still_config* c) {
+  const int st = check_cfg(c, true);
+  if (st != STILL_OK) return st;
+  if (c->head_dim != 64) return STILL_ERR_UNSUPPORTED;
+  return STILL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,6 +536,44 @@ int still_backward(const still_config* cfg, const void* q, const void* k, const 
                    float* dw_phi, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return still_backward_timed(cfg, q, k, v, w_phi, out, dout, sel_idx, dq, dk, dv, dw_phi, workspace, ws_bytes,
                               stream, nullptr);
+}
+
+size_t still_future_attention_mass_workspace_bytes(const still_config* cfg) {
+  if (check_mass_cfg(cfg) != STILL_OK) return 0;
+  return mass_layout(cfg).total;
+}
+
+int still_future_attention_mass(const still_config* cfg, const void* q, const void* k, float* mass_out,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_mass_cfg(cfg);
+  if (st != STILL_OK) return st;
+  if (!q || !k || !mass_out || !workspace) return STILL_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(mass_out, 4) || !aligned(workspace, 16))
+    return STILL_ERR_INVALID_ARG;
+  const MassLayout L = mass_layout(cfg);
+  if (ws_bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  still::MassArgs a;
+  a.d = dims_of(cfg);
+  a.q = q;
+  a.k = k;
+  a.lse = reinterpret_cast<float*>(ws + L.lse);
+  a.part = reinterpret_cast<float*>(ws + L.part);
+  a.mass = mass_out;
+  a.nsplit = L.nsplit;
+  a.per = L.per;
+  return still::launch_mass(a, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+}
+
+int still_selection_overlap(const still_config* cfg, const int32_t* sel_a, const int32_t* sel_b,
+                            int32_t* common_out, hipStream_t stream) {
+  const int st = check_cfg(cfg, true);
+  if (st != STILL_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.nCc == 0 || d.topk == 0) return STILL_OK;
+  if (!sel_a || !sel_b || !common_out || !aligned(sel_a, 4) || !aligned(sel_b, 4) || !aligned(common_out, 4))
+    return STILL_ERR_INVALID_ARG;
+  return still::launch_overlap(d, sel_a, sel_b, common_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
 }
 
 }  // extern "C"

@@ -137,6 +137,21 @@ struct BwdArgs {
 // events: optional, 8 events recorded before each of the seven stages and after the last
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events);
 
+// Attention from far-future queries under full causal softmax (head_dim 64).
+struct MassArgs {
+  Dims d;
+  const void* q;
+  const void* k;
+  float* lse;   // [B,Hq,nC*64]: log2 of each row's causal normaliser (inf past T)
+  float* part;  // [nsplit,B,Hkv,T]: per query slice column sums
+  float* mass;  // [B,Hkv,T]
+  int nsplit;   // query slices
+  int per;      // chunks per slice
+};
+
+hipError_t launch_mass(const MassArgs& a, hipStream_t s);
+hipError_t launch_overlap(const Dims& d, const int32_t* sa, const int32_t* sb, int32_t* out, hipStream_t s);
+
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 // prefix sums of the chunk records, and the per-tile key-norm bound from kmaxc
 hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* tilemax, int tm_stride,

@@ -24,7 +24,8 @@ EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefil
            "still_select_topk",
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
            "still_decode_step", "still_decode_step_timed", "still_backward_workspace_bytes", "still_backward",
-           "still_backward_timed")
+           "still_backward_timed", "still_future_attention_mass_workspace_bytes", "still_future_attention_mass",
+           "still_selection_overlap")
 
 
 class StillError(RuntimeError):
@@ -88,6 +89,12 @@ def load():
     lib.still_backward.restype = I
     lib.still_backward_timed.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, P, P, S, V, P]
     lib.still_backward_timed.restype = I
+    lib.still_future_attention_mass_workspace_bytes.argtypes = [CP]
+    lib.still_future_attention_mass_workspace_bytes.restype = S
+    lib.still_future_attention_mass.argtypes = [CP, P, P, P, P, S, V]
+    lib.still_future_attention_mass.restype = I
+    lib.still_selection_overlap.argtypes = [CP, P, P, P, V]
+    lib.still_selection_overlap.restype = I
     _lib = lib
     return lib
 
@@ -221,6 +228,67 @@ def backward(q, k, v, w_phi, out, dout, sel_idx, *, window: int, top_k: int, chu
     if sel_idx is not None:
         sel_idx = sel_idx.to(device=q.device, dtype=torch.int32).contiguous()
     return call(q, k, v, w_phi, out, dout, sel_idx, dq, dk, dv, dw)
+
+
+class FutureAttentionMass:
+    """A prepared call of still_future_attention_mass (fixed shapes, reusable workspace)."""
+
+    def __init__(self, q, k, *, window: int):
+        B, T, Hq, D = q.shape
+        self.cfg = make_config(B, T, Hq, k.shape[2], D, 64, window, 64, 0, q.dtype)
+        nbytes = int(load().still_future_attention_mass_workspace_bytes(ctypes.byref(self.cfg)))
+        if nbytes == 0:
+            raise StillError(-2, "still_future_attention_mass_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+    def __call__(self, q, k, mass, *, stream=None):
+        for t in (q, k, mass):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("tensors must be contiguous device tensors")
+        rc = load().still_future_attention_mass(ctypes.byref(self.cfg), _ptr(q), _ptr(k), _ptr(mass),
+                                                _ptr(self.workspace), self.workspace.numel(), _stream(stream))
+        _check(rc, "still_future_attention_mass")
+        return mass
+
+
+def future_attention_mass(q, k, *, window: int):
+    """Attention each key receives from queries at distance >= window under full causal
+    softmax, summed over the query heads of its KV head: fp32 [B,Hkv,T]."""
+    B, T, _, _ = q.shape
+    mass = torch.empty((B, k.shape[2], T), dtype=torch.float32, device=q.device)
+    return FutureAttentionMass(q, k, window=window)(q, k, mass)
+
+
+def selection_overlap(sel_a, sel_b):
+    """Tokens two per-chunk selections [B,Hkv,nC,k] (int32, device) share: int32 [B,Hkv,nC]."""
+    B, Hkv, nC, k = sel_a.shape
+    cfg = make_config(B, nC * 64, Hkv, Hkv, 64, 64, 64, 64, k, torch.bfloat16)
+    out = torch.zeros((B, Hkv, nC), dtype=torch.int32, device=sel_a.device)
+    rc = load().still_selection_overlap(ctypes.byref(cfg), _ptr(sel_a.contiguous()), _ptr(sel_b.contiguous()),
+                                        _ptr(out), _stream())
+    _check(rc, "still_selection_overlap")
+    return out
+
+
+def saliency_fidelity(q, k, w_phi, *, window: int, top_k: int, score: str = "saliency"):
+    """Local-global consistency of the routing on these inputs: the layer's own per-chunk
+    selection (from the local routing score) against the top_k of each chunk by attention
+    from far-future queries under full causal softmax.
+
+    Returns a dict of device tensors: sel_local and sel_global [B,Hkv,T//64,top_k], common
+    [B,Hkv,T//64] (tokens both selections hold), mass [B,Hkv,T]; and `overlap`, the mean of
+    common / top_k over the chunks whose every token has at least one far-future query.
+    """
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _, sel_local = prefill(q, k, k, w_phi, window=window, top_k=top_k, return_routing=True, score=score)
+    mass = future_attention_mass(q, k, window=window)
+    sel_global = select_topk(mass, chunk=64, top_k=top_k, n_q_heads=Hq // Hkv, head_dim=D,
+                             feat_dim=w_phi.shape[1], dtype=q.dtype)
+    common = selection_overlap(sel_local, sel_global)
+    n_ok = max(0, min(T // 64, (T - window) // 64))  # chunks c with 64 c + 63 + window <= T - 1
+    overlap = float(common[:, :, :n_ok].double().mean() / top_k) if n_ok > 0 else float("nan")
+    return {"sel_local": sel_local, "sel_global": sel_global, "common": common, "mass": mass, "overlap": overlap}
 
 
 def select_topk(saliency, *, chunk: int, top_k: int, n_q_heads: int = 1, head_dim: int = 64, feat_dim: int = 64,
