@@ -290,6 +290,57 @@ def run_backward(wl, args, torch, still, synth) -> dict:
     }
 
 
+def run_fidelity(wl, args, torch, still, synth) -> dict:
+    """The local-global consistency diagnostic on the workload: attention from far-future
+    queries under full causal softmax (timed), its per-chunk top-k, and the overlap with the
+    layer's own routing."""
+    dev = torch.device("cuda:0")
+    q, k, v, w = synth.make_inputs(wl)
+    tq, tk, tw = (torch.from_numpy(a).to(dev, torch.bfloat16).contiguous() for a in (q, k, w))
+    del q, k, v, w
+    B, T, Hq, D = tq.shape
+    Hkv = tk.shape[2]
+    call = still.FutureAttentionMass(tq, tk, window=wl.window)
+    mass = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        call(tq, tk, mass)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        call(tq, tk, mass)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    fid = still.saliency_fidelity(tq, tk, tw, window=wl.window, top_k=wl.top_k)
+    wd = wl.window
+    pairs = T * (T + 1) / 2.0 + (T - wd) * (T - wd + 1) / 2.0  # both passes, per query head
+    flops = 2.0 * D * pairs * Hq * B
+    ach = flops / (ms * 1e-3)
+    return {
+        "metric": f"far-future attention mass, tokens/s per layer ({wl.name}, bf16); % of MFMA roofline",
+        "value": B * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1)/sqrt(D) Q/K, 1% planted keys x4; bf16",
+        "config": {"workload": wl.name + "-fidelity", "batch": B, "seq_len": T, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k},
+        "roofline": {"bound": "mfma", "kernel": "mass_lse_kernel + mass_col_kernel", "achieved": ach / 1e12,
+                     "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_MFMA, "traffic": None},
+        "overlap": fid["overlap"],
+        "wall_s": wall,
+    }
+
+
 def run_decode(wl, args, torch, still, synth) -> dict:
     dev = torch.device("cuda:0")
     B, Hq, Hkv, D, F = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.feat_dim
@@ -385,6 +436,8 @@ def main() -> int:
                          "linear-attention baseline, 64 (= chunk) full causal softmax")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (routing fixed) instead of the forward")
+    ap.add_argument("--fidelity", action="store_true",
+                    help="time the local-global consistency diagnostic (far-future attention mass)")
     ap.add_argument("--score", choices=["saliency", "diag"], default="saliency",
                     help="routing score: the Self-Saliency Score, or the diagonal logit alone")
     args = ap.parse_args()
@@ -414,7 +467,12 @@ def main() -> int:
         args.steps = 64 if decode else 50
     if args.warmup is None:
         args.warmup = 8 if decode else 100
-    if args.backward:
+    if args.fidelity:
+        if decode or wl.head_dim != 64:
+            print("--fidelity covers prefill workloads with head_dim 64", file=sys.stderr)
+            return 2
+        res = run_fidelity(wl, args, torch, still, synth)
+    elif args.backward:
         if decode or wl.head_dim != 64:
             print("--backward covers prefill workloads with head_dim 64", file=sys.stderr)
             return 2

@@ -4,7 +4,8 @@ The attention each key receives from far-future queries (full causal softmax) is
 with the oracle's as max-abs error relative to the largest oracle value: 1e-4 in fp32 and
 2e-4 in bf16 (the inputs are exact in both; every product and sum runs in fp32). The
 per-chunk top-k of that mass is bit-exact wherever the oracle's k-th/(k+1)-th gap exceeds
-1e-3 of the largest value, and the overlap counts are exact integers.
+both 1e-5 of the largest value and 50 times the measured error, and the overlap counts are
+exact integers.
 """
 
 import sys
@@ -55,7 +56,8 @@ def test_fidelity_matches_oracle(case):
     torch.cuda.synchronize()
     got = mass.cpu().numpy().astype(np.float64)
     ref = O.future_attention_mass(q, kk, w)
-    e = float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+    abs_err = float(np.abs(got - ref).max())
+    e = abs_err / max(np.abs(ref).max(), 1e-30)
     _say(name, "mass rel max err", e)
     assert e <= REL_TOL[dt]
     if k == 0 or T < 64:
@@ -64,7 +66,7 @@ def test_fidelity_matches_oracle(case):
     sel_g = fid["sel_global"].cpu().numpy()
     ref_idx, _ = O.route(ref, 64, k)
     margins = O.route_margins(ref, 64, k)
-    decided = margins > 1e-3 * np.abs(ref).max()
+    decided = margins > max(1e-5 * np.abs(ref).max(), 50 * abs_err)
     same = np.all(sel_g == ref_idx, axis=-1)
     assert np.all(same[decided]), f"global top-k differs in {int((~same[decided]).sum())} decided chunks"
     common = fid["common"].cpu().numpy()
