@@ -22,8 +22,10 @@
 // Launch order (one stream):
 //   bwd_kprep_kernel     per (chunk, KV head, batch): phi(k), K^T, U_c / u_c, compact rows
 //   bwd_scan_fwd_kernel  U_c -> S_c (sum over chunks <= c-2), in place
-//   bwd_dq_kernel        per (chunk, query head, batch): L_i (first pass over the keys),
-//                        dq (second pass), the per-chunk sums behind R, the q side of dW
+//   bwd_dq_kernel        per (chunk, query head, batch): one pass over the keys gives dq and
+//                        L_i together (the softmax part against a running reference,
+//                        divided by the normaliser at the end), the per-chunk sums behind
+//                        R, the q side of dW
 //   bwd_rev_seg_kernel / bwd_rev_scan_kernel: R_c = sum over chunks >= c+2 and over the
 //                        query group (a segmented scan)
 //   bwd_dkv_far_kernel   per (compact tile, query split, KV head): the selected keys
@@ -389,30 +391,30 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   const long long krs = static_cast<long long>(d.Hkv) * BD;
 
 
-  // ---- pass 1: L = log2 of the normaliser
-  // online softmax sums over raw scores s = q.k: the running max mx2 and the exponents
-  // are in log2 units (s * scale2), the scale folded into one fma per score
-  float mx2 = -kInf, l = 0.f;
-  auto online = [&](const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
+  // ---- one pass over the keys. The softmax part of dq accumulates sum 2^{a - m} (dP - Delta) k
+  // against a running reference m (log2 units; moved up only when a score passes it by more
+  // than kLazy2, the accumulator rescaled then), the linear-attention part of dphi(q)
+  // accumulates sum (dP - Delta) phi(k) unscaled, and both are divided by the normaliser
+  // once it is known, at the end. Scores are raw q.k, the scale folded into the exponent's fma.
+  constexpr float kLazy2 = 8.f;
+  float m2 = -kInf, l_lane = 0.f;  // this lane's share of the softmax part of the normaliser / 2^m
+  f32x4 dqt[4] = {}, dpt[4] = {};
+  auto rebase = [&](const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
     float tm = -kInf;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tm = (!masked || sa[kb][e]) ? fmaxf(tm, sc[kb][e]) : tm;
     tm = xor_max_groups(tm) * scale2;
-    const float mn = fmaxf(mx2, tm);
-    const bool any = mn != -kInf;  // the same in the four lanes of a query
-    float ps = 0.f;
+    const bool move = tm > m2 + kLazy2;  // the same in the four lanes of a query
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float mn = move ? tm : m2;
+      const float alpha = mn == m2 ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
+      l_lane *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], scale2, -mn));
-        ps += (!masked || sa[kb][e]) ? pe : 0.f;
-      }
-    ps = xor_sum_groups(ps);
-    l = any ? l * __builtin_amdgcn_exp2f(mx2 - mn) + ps : l;
-    mx2 = mn;
+      for (int db = 0; db < 4; ++db) dqt[db] *= alpha;
+      m2 = mn;
+    }
   };
   // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
   // nsel_c read as zeros (the copies' range ends there)
@@ -424,70 +426,6 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   const auto rs_k = make_rsrc(ksel, static_cast<uint32_t>(nsel_c * BD * ES));
   const auto rs_v = make_rsrc(vsel, static_cast<uint32_t>(nsel_c * BD * ES));
   const auto rs_kt = make_rsrc(kselt, static_cast<uint32_t>(ntc * BD * 64 * ES));
-  if (ntc > 0) dma.issue(lds[0], rs_k, 0);
-  for (int t = 0; t < ntc; ++t) {
-    if (t + 1 < ntc) {
-      dma.issue(lds[((t + 1) & 1) * 3], rs_k, (t + 1) * 64 * BD * ES);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(Dma::PER_WAVE));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    }
-    lds_sync();
-    f32x4 s[4];
-    rows_x_frag<T>(s, lds[(t & 1) * 3], qf);
-    bool sa[4][4];
-    if (nsel_c - t * 64 >= 64) {  // a full tile
-      online(s, sa, false);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sa[kb][e] = t * 64 + kb * 16 + 4 * grp + e < nsel_c;
-      online(s, sa, true);
-    }
-    lds_sync();
-  }
-  for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
-    __syncthreads();
-    const long long r0 = (static_cast<long long>(b) * d.T + 64LL * cc) * d.Hkv + h;
-    tile_load<T>(t_k, static_cast<const T*>(a.k) + r0 * BD, krs, min(64, d.T - 64 * cc));
-    tile_load<T>(t_pk, static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, BF, 64);
-    __syncthreads();
-    f32x4 s[4], lw[4];
-    rows_x_frag<T>(s, t_k, qf);
-    rows_x_frag<T>(lw, t_pk, phf);
-    bool sa[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jr = kb * 16 + 4 * grp + e;
-        const long long j = 64LL * cc + jr;
-        const bool vis = j <= i;
-        const bool inwin = i - j < d.window;
-        const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
-        sa[kb][e] = vis && (inwin || sel);
-        if (vis && !(inwin || sel)) dla += lw[kb][e];
-      }
-    online(s, sa, true);
-  }
-  dla = xor_sum_groups(dla);
-  float L2;
-  if (!qvalid) {
-    L2 = kInf;
-  } else if (l > 0.f && dla > 0.f) {
-    const float ld = log2f(dla);
-    const float M = fmaxf(mx2, ld);
-    L2 = M + log2f(l * exp2f(mx2 - M) + exp2f(ld - M));
-  } else if (l > 0.f) {
-    L2 = mx2 + log2f(l);
-  } else {
-    L2 = dla > 0.f ? log2f(dla) : kInf;  // an empty normaliser: out = 0, no gradient
-  }
-  const float einv = exp2f(-L2);
-
-  // ---- pass 2: dq (softmax part) and dphi(q)
-  f32x4 dqt[4] = {}, dpt[4] = {};
   auto issue3 = [&](int t) {
     const int sl = (t & 1) * 3;
     dma.issue(lds[sl], rs_k, t * 64 * BD * ES);
@@ -508,57 +446,103 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     f32x4 s[4], dp[4];
     rows_x_frag<T>(s, lds[sl], qf);
     rows_x_frag<T>(dp, lds[sl + 1], dof);
-    if (nv == 64) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) * (dp[kb][e] - delta);
-    } else {
+    bool sa[4][4];
+    if (nv == 64) {  // a full tile
+      rebase(s, sa, false);
+      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = kb * 16 + 4 * grp + e < nv;
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) : 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2));
+          ps += p;
+          s[kb][e] = p * (dp[kb][e] - delta);
+        }
+      l_lane += ps;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sa[kb][e] = kb * 16 + 4 * grp + e < nv;
+      rebase(s, sa, true);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2)) : 0.f;
+          l_lane += p;
           s[kb][e] = p * (dp[kb][e] - delta);
         }
     }
     rows_x_acc<T>(dqt, lds[sl + 2], s);
     lds_sync();
   }
+  Dma dkv;  // key and value rows of the input, row stride Hkv * D
+  dkv.init(static_cast<int>(krs));
   for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
     __syncthreads();
     const long long r0 = (static_cast<long long>(b) * d.T + 64LL * cc) * d.Hkv + h;
     const int nv = min(64, d.T - 64 * cc);
-    tile_load<T>(t_k, static_cast<const T*>(a.k) + r0 * BD, krs, nv);
-    tile_load<T>(t_v, static_cast<const T*>(a.v) + r0 * BD, krs, nv);
-    tile_load<T>(t_kt, static_cast<const T*>(a.kt) + (bh * d.nC + cc) * BD * 64, 64, 64);
-    tile_load<T>(t_pk, static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, BF, 64);
-    tile_load<T>(t_pkt, static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * BF * 64, 64, 64);
-    __syncthreads();
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * krs + BD) * ES);
+    dkv.issue(t_k, make_rsrc(static_cast<const T*>(a.k) + r0 * BD, rows_b), 0);
+    dkv.issue(t_v, make_rsrc(static_cast<const T*>(a.v) + r0 * BD, rows_b), 0);
+    dma.issue(t_kt, make_rsrc(static_cast<const T*>(a.kt) + (bh * d.nC + cc) * BD * 64, BD * 64 * ES), 0);
+    dma.issue(t_pk, make_rsrc(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, 64 * BF * ES), 0);
+    dma.issue(t_pkt, make_rsrc(static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * BF * 64, BF * 64 * ES), 0);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    lds_sync();
     f32x4 s[4], dp[4], lw[4];
     rows_x_frag<T>(s, t_k, qf);
     rows_x_frag<T>(dp, t_v, dof);
     rows_x_frag<T>(lw, t_pk, phf);
+    bool sa[4][4], la[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jr = kb * 16 + 4 * grp + e;
-        const long long j = 64LL * cc + jr;
-        const bool vis = j <= i;
-        const bool inwin = i - j < d.window;
+        const int dist = 64 * (c - cc) + qrow - jr;  // i - j
+        const bool vis = dist >= 0;
+        const bool inwin = dist < d.window;
         const bool sel = cc < c && ((sel_prev >> jr) & 1ull);
-        const bool sa = vis && (inwin || sel);
-        const bool la = vis && !(inwin || sel);
-        const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -L2)) : 0.f;
+        sa[kb][e] = vis && (inwin || sel);
+        la[kb][e] = vis && !(inwin || sel);
+      }
+    rebase(s, sa, true);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2)) : 0.f;
         const float g = dp[kb][e] - delta;
+        l_lane += p;
+        dla += la[kb][e] ? lw[kb][e] : 0.f;
         s[kb][e] = p * g;
-        lw[kb][e] = la ? g * einv : 0.f;
+        lw[kb][e] = la[kb][e] ? g : 0.f;
       }
     rows_x_acc<T>(dqt, t_kt, s);
     rows_x_acc<T>(dpt, t_pkt, lw);
   }
+  const float l = xor_sum_groups(l_lane);
+  dla = xor_sum_groups(dla);
+  float L2;
+  if (!qvalid) {
+    L2 = kInf;
+  } else if (l > 0.f && dla > 0.f) {
+    const float ld = log2f(dla);
+    const float M = fmaxf(m2, ld);
+    L2 = M + log2f(l * exp2f(m2 - M) + exp2f(ld - M));
+  } else if (l > 0.f) {
+    L2 = m2 + log2f(l);
+  } else {
+    L2 = dla > 0.f ? log2f(dla) : kInf;  // an empty normaliser: out = 0, no gradient
+  }
+  const float einv = exp2f(-L2);
+  const float sa_scale = l > 0.f ? exp2f(m2 - L2) : 0.f;  // 2^m / normaliser
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dqt[db] *= sa_scale;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) dpt[fb] *= einv;
   if (c >= 2) {
     // dphi(q) += e^{-L} (S_c dout - Delta z_c)
     f32x4 sdo[4] = {};
@@ -603,9 +587,15 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2] = L2;
     a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta : 0.f;
   }
+  // phi(q) rows and phi(q)^T are stored times e^{-L}, the factor every key-side use takes
   T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * BF;
-  TT::store8(phqr + 8 * grp, phf[0]);
-  TT::store8(phqr + 32 + 8 * grp, phf[1]);
+  {
+    f32x4 ps4[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) ps4[fb] = phq[fb] * einv;
+    TT::store8(phqr + 8 * grp, pk_frag<T>(ps4[0], ps4[1]));
+    TT::store8(phqr + 32 + 8 * grp, pk_frag<T>(ps4[2], ps4[3]));
+  }
   T* phqt = static_cast<T*>(a.phiqt) + qc * BF * 64;
   T* qt = static_cast<T*>(a.qt) + qc * BD * 64;
   T* dot = static_cast<T*>(a.dot) + qc * BD * 64;
@@ -620,7 +610,6 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int f = fb * 16 + 4 * grp + e;
-      phqt[f * 64 + pq] = TT::from_f(phq[fb][e]);
       e_phq[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);
       e_dz[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);
     }
@@ -629,8 +618,6 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int dd = ks * 32 + grp * 8 + e;
-      qt[dd * 64 + pq] = qf[ks][e];
-      dot[dd * 64 + pq] = dof[ks][e];
       e_do[SW::off(dd, pq)] = dof[ks][e];
       e_q[SW::off(dd, pq)] = qf[ks][e];
     }
@@ -643,6 +630,13 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
       if (r16 == 0) s_red[hs][wl][fb * 16 + 4 * grp + e] = v;
     }
   __syncthreads();
+  // the transposed tiles to memory in 16-byte pieces
+  for (int idx = tid & 255; idx < 512; idx += 256) {
+    const int row = idx >> 3, col = (idx & 7) * 8;
+    TT::store8(phqt + row * 64 + col, SW::load8(e_phq, row, col));
+    TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
+    TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
+  }
   float* ap = a.apart + qc * BR;
   if (wl == 0)
     ap[BF * BD + lane] = ((s_red[hs][0][lane] + s_red[hs][1][lane]) + s_red[hs][2][lane]) + s_red[hs][3][lane];
@@ -891,19 +885,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qr = qb * 16 + 4 * grp + e;
-          const long long i = 64LL * cq + qr;
-          const bool vis = j <= i;
-          const bool inwin = i - j < d.window;
+          const int dist = 64 * (cq - c) + qr - jr;  // i - j
+          const bool vis = dist >= 0;
+          const bool inwin = dist < d.window;
           const bool sel = cq > c && selj;
           const bool sa = vis && (inwin || sel);
           const bool la = vis && !(inwin || sel);
           const float L2 = lq[e], dl = dq4[e];
-          const float einv = __builtin_amdgcn_exp2f(-L2);
           const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], scale2, -L2)) : 0.f;
           const float gg = dp[qb][e] - dl;
-          s[qb][e] = p * gg;                           // dS
-          dp[qb][e] = p + (la ? lw[qb][e] * einv : 0.f);  // weight of v_j in out_i
-          lw[qb][e] = la ? gg * einv : 0.f;            // g
+          s[qb][e] = p * gg;                    // dS
+          dp[qb][e] = p + (la ? lw[qb][e] : 0.f);  // weight of v_j in out_i (phi(q) carries e^{-L})
+          lw[qb][e] = la ? gg : 0.f;            // g / e^{-L}
         }
       }
       rows_x_acc<T>(dvt, cur[3], dp);

@@ -119,8 +119,8 @@ struct BwdArgs {
   void* kselt;             // [B,Hkv,ntiles,D,64 pk]
   void* qt;                // [B,Hq,nC,D,64 pk]
   void* dot;               // [B,Hq,nC,D,64 pk]
-  void* phiq;              // [B,Hq,nC*64,DF pk]
-  void* phiqt;             // [B,Hq,nC,DF,64 pk]
+  void* phiq;              // [B,Hq,nC*64,DF pk]: e^{-L} phi(q) rows
+  void* phiqt;             // [B,Hq,nC,DF,64 pk]: e^{-L} phi(q)^T
   float* ld;               // [B,Hq,nC*64,2]: (log2 of the normaliser, Delta)
   float* apart;            // [B,Hq,nC,R]: per-chunk sum of e^{-L} phi(q) dout^T, e^{-L} Delta phi(q)
   float* rstate;           // [B,Hkv,nC,R]: R_c, r_c (chunks >= c+2)
