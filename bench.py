@@ -146,13 +146,15 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     if not (wl is synth.L1B_16K and not args.no_cpu_baseline):
         del q, k, v, w
     out = torch.empty_like(tq)
-    call = still.Prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, chunk=wl.chunk, score=args.score)
-    sel = torch.empty((wl.batch, wl.n_kv_heads, wl.seq_len // wl.chunk, wl.top_k), dtype=torch.int32, device=dev)
+    call = still.Prefill(tq, tk, tv, tw, window=wl.window, top_k=wl.top_k, chunk=wl.chunk, score=args.score,
+                         scope=args.scope)
+    n_sel_heads = wl.n_q_heads if args.scope == "query_head" else wl.n_kv_heads
+    sel = torch.empty((wl.batch, n_sel_heads, wl.seq_len // wl.chunk, wl.top_k), dtype=torch.int32, device=dev)
     torch.cuda.reset_peak_memory_stats()
     call(tq, tk, tv, tw, out, sel_idx=sel)
     torch.cuda.synchronize()
     sel_idx = sel.cpu().numpy()
-    work = algorithmic_work(wl, sel_idx, args.score)
+    work = algorithmic_work(wl if args.scope == "kv_head" else wl.replace(n_kv_heads=wl.n_q_heads), sel_idx, args.score)
 
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out)
@@ -195,7 +197,8 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
         "data": "synthetic: seeded N(0,1)/sqrt(D) Q/K/V, 1% planted keys x4, W_phi N(0,1/D); bf16",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len, "n_q_heads": wl.n_q_heads,
                    "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "feat_dim": wl.feat_dim,
-                   "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k, "score": args.score},
+                   "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k, "score": args.score,
+                   "routing_scope": args.scope},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
                      "traffic": measured_traffic(wl.name)},
@@ -438,6 +441,8 @@ def main() -> int:
                     help="time the backward pass (routing fixed) instead of the forward")
     ap.add_argument("--fidelity", action="store_true",
                     help="time the local-global consistency diagnostic (far-future attention mass)")
+    ap.add_argument("--scope", choices=["kv_head", "query_head"], default="kv_head",
+                    help="who selects: each KV head for its group, or each query head for itself (prefill)")
     ap.add_argument("--score", choices=["saliency", "diag"], default="saliency",
                     help="routing score: the Self-Saliency Score, or the diagonal logit alone")
     args = ap.parse_args()
@@ -462,11 +467,16 @@ def main() -> int:
         wl = wl.replace(top_k=args.top_k, name=f"{wl.name}-k{args.top_k}")
     if args.score != "saliency":
         wl = wl.replace(name=f"{wl.name}-{args.score}")
+    if args.scope != "kv_head":
+        wl = wl.replace(name=f"{wl.name}-per-query-head")
     decode = wl.decode_steps > 0
     if args.steps is None:
         args.steps = 64 if decode else 50
     if args.warmup is None:
         args.warmup = 8 if decode else 100
+    if args.scope != "kv_head" and (decode or args.backward or args.fidelity):
+        print("--scope query_head is timed for prefill only", file=sys.stderr)
+        return 2
     if args.fidelity:
         if decode or wl.head_dim != 64:
             print("--fidelity covers prefill workloads with head_dim 64", file=sys.stderr)

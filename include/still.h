@@ -69,6 +69,19 @@ typedef enum still_dtype { STILL_F32 = 0, STILL_BF16 = 1 } still_dtype;
  *                         reading that differs. */
 typedef enum still_score { STILL_SCORE_SALIENCY = 0, STILL_SCORE_DIAG = 1 } still_score;
 
+/* Who selects ([P1] section "Chunk-Wise并行+延迟选择" selects per chunk; the pages do not say
+ * per which head):
+ *   STILL_ROUTE_PER_KV_HEAD     every KV head selects once, on the sum of its query heads'
+ *                               scores; the selection is shared by the group (default);
+ *   STILL_ROUTE_PER_QUERY_HEAD  every query head selects on its own score and has its own
+ *                               softmax cache and linear-attention state. The library runs
+ *                               the layer on keys, values and NP-Map weights expanded to one
+ *                               copy per query head (in the workspace) and, in the backward
+ *                               pass, sums the copies' gradients over each group. Prefill and
+ *                               backward only (no decode cache); saliency_out and sel_idx are
+ *                               then per query head ([batch, n_q_heads, ...]). */
+typedef enum still_routing_scope { STILL_ROUTE_PER_KV_HEAD = 0, STILL_ROUTE_PER_QUERY_HEAD = 1 } still_routing_scope;
+
 /* Status codes (0 = success). */
 enum {
   STILL_OK = 0,
@@ -98,6 +111,7 @@ typedef struct still_config {
   int32_t top_k;
   int32_t dtype; /* still_dtype */
   int32_t score; /* still_score; 0 = the Self-Saliency Score */
+  int32_t routing_scope; /* still_routing_scope; 0 = per KV head */
 } still_config;
 
 /* Decode state for batched token-by-token generation with chunk-delayed selection

@@ -25,6 +25,8 @@ int check_cfg(const still_config* c, bool use_seq) {
   if (c->n_q_heads % c->n_kv_heads != 0) return STILL_ERR_INVALID_ARG;
   if (c->dtype != STILL_F32 && c->dtype != STILL_BF16) return STILL_ERR_INVALID_ARG;
   if (c->score != STILL_SCORE_SALIENCY && c->score != STILL_SCORE_DIAG) return STILL_ERR_INVALID_ARG;
+  if (c->routing_scope != STILL_ROUTE_PER_KV_HEAD && c->routing_scope != STILL_ROUTE_PER_QUERY_HEAD)
+    return STILL_ERR_INVALID_ARG;
   if (c->head_dim < 1 || c->feat_dim < 1 || c->chunk < 1) return STILL_ERR_INVALID_ARG;
   if (c->window < 0 || c->top_k < 0 || c->top_k > c->chunk) return STILL_ERR_INVALID_ARG;
   if (c->window == 0 && c->top_k != 0) return STILL_ERR_INVALID_ARG;
@@ -133,13 +135,15 @@ int check_cache_cfg(const still_config* c, int64_t max_tokens) {
   if (st != STILL_OK) return st;
   if (max_tokens < 1 || max_tokens > 0x7fffffffLL) return STILL_ERR_INVALID_ARG;
   if (c->n_q_heads / c->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
+  if (c->routing_scope != STILL_ROUTE_PER_KV_HEAD) return STILL_ERR_UNSUPPORTED;
   return STILL_OK;
 }
 
 bool same_layer(const still_config* a, const still_config* b) {
   return a->batch == b->batch && a->n_q_heads == b->n_q_heads && a->n_kv_heads == b->n_kv_heads &&
          a->head_dim == b->head_dim && a->feat_dim == b->feat_dim && a->window == b->window &&
-         a->chunk == b->chunk && a->top_k == b->top_k && a->dtype == b->dtype && a->score == b->score;
+         a->chunk == b->chunk && a->top_k == b->top_k && a->dtype == b->dtype && a->score == b->score &&
+         a->routing_scope == b->routing_scope;
 }
 
 still::CacheView view_of(const still_cache* c) {
@@ -159,6 +163,49 @@ still::CacheView view_of(const still_cache* c) {
 size_t decode_ws_bytes(const still_config* c) {
   const size_t recs = static_cast<size_t>(c->batch) * c->n_kv_heads * kMaxSplit * (c->n_q_heads / c->n_kv_heads);
   return align_up(recs * 2 * sizeof(float)) + align_up(recs * c->head_dim * sizeof(float));
+}
+
+// ---- per-query-head routing: the layer on K, V and W_h expanded to one copy per query head
+still_config expanded_cfg(const still_config* c) {
+  still_config e = *c;
+  e.n_kv_heads = c->n_q_heads;
+  e.routing_scope = STILL_ROUTE_PER_KV_HEAD;
+  return e;
+}
+
+struct ExpLayout {
+  size_t ek, ev, ew, total;  // expanded K, V, W_h; the inner call's workspace starts at total
+};
+
+ExpLayout exp_layout(const still_config* c) {
+  const size_t es = c->dtype == STILL_BF16 ? 2 : 4;
+  const size_t rows = static_cast<size_t>(c->batch) * c->seq_len;
+  ExpLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.ek = take(rows * c->n_q_heads * c->head_dim * es);
+  L.ev = take(rows * c->n_q_heads * c->head_dim * es);
+  L.ew = take(static_cast<size_t>(c->n_q_heads) * c->feat_dim * c->head_dim * es);
+  L.total = off;
+  return L;
+}
+
+hipError_t expand_kvw(const still_config* c, const void* k, const void* v, const void* w, char* ws, const ExpLayout& L,
+                      hipStream_t stream) {
+  const long long rows = static_cast<long long>(c->batch) * c->seq_len;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  const long long es = c->dtype == STILL_BF16 ? 2 : 4;
+  hipError_t e;
+  if ((e = still::launch_expand_heads(k, ws + L.ek, rows, c->n_kv_heads, G, c->head_dim * es, stream)) != hipSuccess)
+    return e;
+  if ((e = still::launch_expand_heads(v, ws + L.ev, rows, c->n_kv_heads, G, c->head_dim * es, stream)) != hipSuccess)
+    return e;
+  return still::launch_expand_heads(w, ws + L.ew, 1, c->n_kv_heads, G,
+                                    static_cast<long long>(c->feat_dim) * c->head_dim * es, stream);
 }
 
 // ---- backward workspace
@@ -242,7 +289,7 @@ MassLayout mass_layout(const still_config* c) {
 int check_mass_cfg(const still_config* c) {
   const int st = check_cfg(c, true);
   if (st != STILL_OK) return st;
-  if (c->head_dim != 64) return STILL_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 || c->routing_scope != STILL_ROUTE_PER_KV_HEAD) return STILL_ERR_UNSUPPORTED;
   return STILL_OK;
 }
 
@@ -265,6 +312,11 @@ const char* still_status_string(int status) {
 
 size_t still_prefill_workspace_bytes(const still_config* cfg) {
   if (check_cfg(cfg, true) != STILL_OK) return 0;
+  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
+    const still_config e = expanded_cfg(cfg);
+    if (check_cfg(&e, true) != STILL_OK) return 0;
+    return exp_layout(cfg).total + ws_layout(&e).total;
+  }
   return ws_layout(cfg).total;
 }
 
@@ -282,6 +334,18 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
                         static_cast<const void*>(sel_idx_out)})
     if (p && !aligned(p, 4)) return STILL_ERR_INVALID_ARG;
   if (saliency_out && cfg->window < 1) return STILL_ERR_INVALID_ARG;
+  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
+    if (cache) return STILL_ERR_UNSUPPORTED;
+    const still_config e = expanded_cfg(cfg);
+    const int se = check_cfg(&e, true);
+    if (se != STILL_OK) return se;
+    const ExpLayout X = exp_layout(cfg);
+    if (ws_bytes < X.total + ws_layout(&e).total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+    char* ws = static_cast<char*>(workspace);
+    if (expand_kvw(cfg, k, v, w_phi, ws, X, stream) != hipSuccess) return STILL_ERR_HIP;
+    return still_prefill_timed(&e, q, ws + X.ek, ws + X.ev, ws + X.ew, out, routing_in, saliency_out,
+                               sel_idx_out, nullptr, ws + X.total, ws_bytes - X.total, stream, events);
+  }
   if (cache) {
     if (!same_layer(&cache->cfg, cfg)) return STILL_ERR_CACHE_MISMATCH;
     if (cache->n_tokens != 0) return STILL_ERR_INVALID_ARG;
@@ -472,8 +536,37 @@ int still_decode_step(const still_config* cfg, still_cache* cache, const void* q
   return still_decode_step_timed(cfg, cache, q, k, v, w_phi, out, workspace, ws_bytes, stream, nullptr);
 }
 
+// per-query-head backward: after the expanded K, V, W_h, the copies' dk, dv, dW
+struct ExpBwdLayout {
+  ExpLayout x;
+  size_t dk, dv, dw, total;
+};
+
+ExpBwdLayout exp_bwd_layout(const still_config* c) {
+  ExpBwdLayout L;
+  L.x = exp_layout(c);
+  const size_t es = c->dtype == STILL_BF16 ? 2 : 4;
+  const size_t kv = static_cast<size_t>(c->batch) * c->seq_len * c->n_q_heads * c->head_dim * es;
+  size_t off = L.x.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.dk = take(kv);
+  L.dv = take(kv);
+  L.dw = take(static_cast<size_t>(c->n_q_heads) * c->feat_dim * c->head_dim * sizeof(float));
+  L.total = off;
+  return L;
+}
+
 size_t still_backward_workspace_bytes(const still_config* cfg) {
   if (check_bwd_cfg(cfg) != STILL_OK) return 0;
+  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
+    const still_config e = expanded_cfg(cfg);
+    if (check_bwd_cfg(&e) != STILL_OK) return 0;
+    return exp_bwd_layout(cfg).total + bwd_layout(&e).total;
+  }
   return bwd_layout(cfg).total;
 }
 
@@ -490,6 +583,28 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
                         static_cast<const void*>(workspace)})
     if (!aligned(p, 16)) return STILL_ERR_INVALID_ARG;
   if (cfg->top_k > 0 && cfg->seq_len >= 64 && (!sel_idx || !aligned(sel_idx, 4))) return STILL_ERR_INVALID_ARG;
+  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
+    const still_config e = expanded_cfg(cfg);
+    const int se = check_bwd_cfg(&e);
+    if (se != STILL_OK) return se;
+    const ExpBwdLayout X = exp_bwd_layout(cfg);
+    if (ws_bytes < X.total + bwd_layout(&e).total) return STILL_ERR_WORKSPACE_TOO_SMALL;
+    char* ws = static_cast<char*>(workspace);
+    if (expand_kvw(cfg, k, v, w_phi, ws, X.x, stream) != hipSuccess) return STILL_ERR_HIP;
+    const int rc = still_backward_timed(&e, q, ws + X.x.ek, ws + X.x.ev, ws + X.x.ew, out, dout, sel_idx, dq, ws + X.dk,
+                                        ws + X.dv, reinterpret_cast<float*>(ws + X.dw), ws + X.total,
+                                        ws_bytes - X.total, stream, events);
+    if (rc != STILL_OK) return rc;
+    const long long rows = static_cast<long long>(cfg->batch) * cfg->seq_len;
+    const int G = cfg->n_q_heads / cfg->n_kv_heads;
+    const int es = cfg->dtype == STILL_BF16 ? 2 : 4;
+    if (still::launch_reduce_heads(ws + X.dk, dk, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream) != hipSuccess ||
+        still::launch_reduce_heads(ws + X.dv, dv, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream) != hipSuccess ||
+        still::launch_reduce_heads(ws + X.dw, dw_phi, 1, cfg->n_kv_heads, G, cfg->feat_dim * cfg->head_dim, 4,
+                                   stream) != hipSuccess)
+      return STILL_ERR_HIP;
+    return STILL_OK;
+  }
   const BwdLayout L = bwd_layout(cfg);
   if (ws_bytes < L.total) return STILL_ERR_WORKSPACE_TOO_SMALL;
   char* ws = static_cast<char*>(workspace);

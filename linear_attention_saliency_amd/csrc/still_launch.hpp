@@ -152,6 +152,13 @@ struct MassArgs {
 hipError_t launch_mass(const MassArgs& a, hipStream_t s);
 hipError_t launch_overlap(const Dims& d, const int32_t* sa, const int32_t* sb, int32_t* out, hipStream_t s);
 
+// Per-query-head routing: dst[r][h*G+g][:] = src[r][h][:] (inner_bytes a multiple of 16),
+// and dst[r][h][:] = sum_g src[r][h*G+g][:] (elem 2: bf16, 4: fp32).
+hipError_t launch_expand_heads(const void* src, void* dst, long long rows, int Hkv, int G, long long inner_bytes,
+                               hipStream_t s);
+hipError_t launch_reduce_heads(const void* src, void* dst, long long rows, int Hkv, int G, int inner, int elem,
+                               hipStream_t s);
+
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 // prefix sums of the chunk records, and the per-tile key-norm bound from kmaxc
 hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* tilemax, int tm_stride,

@@ -36,7 +36,8 @@ class StillError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "seq_len", "n_q_heads", "n_kv_heads", "head_dim",
-                                               "feat_dim", "window", "chunk", "top_k", "dtype", "score")]
+                                               "feat_dim", "window", "chunk", "top_k", "dtype", "score",
+                                               "routing_scope")]
 
 
 class Cache(ctypes.Structure):
@@ -100,13 +101,14 @@ def load():
 
 
 SCORES = {"saliency": 0, "diag": 1}  # still_score: the routing score
+SCOPES = {"kv_head": 0, "query_head": 1}  # still_routing_scope: who selects
 
 
 def make_config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k,
-                dtype, score: str = "saliency") -> Config:
+                dtype, score: str = "saliency", scope: str = "kv_head") -> Config:
     dt = STILL_BF16 if dtype in (torch.bfloat16, "bf16") else STILL_F32 if dtype in (torch.float32, "f32") else -1
     return Config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dt,
-                  SCORES.get(score, -1))
+                  SCORES.get(score, -1), SCOPES.get(scope, -1))
 
 
 def _ptr(t):
@@ -123,12 +125,12 @@ def _check(rc: int, what: str):
         raise StillError(rc, what)
 
 
-def _tensor_cfg(q, k, w_phi, window, chunk, top_k, score="saliency"):
+def _tensor_cfg(q, k, w_phi, window, chunk, top_k, score="saliency", scope="kv_head"):
     if q.dim() != 4 or k.dim() != 4 or w_phi.dim() != 3:
         raise ValueError("q/k must be [B,T,H,D] and w_phi [Hkv,d_f,D]")
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
-    return make_config(B, T, Hq, Hkv, D, w_phi.shape[1], window, chunk, top_k, q.dtype, score)
+    return make_config(B, T, Hq, Hkv, D, w_phi.shape[1], window, chunk, top_k, q.dtype, score, scope)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -138,8 +140,9 @@ def workspace_bytes(cfg: Config) -> int:
 class Prefill:
     """A prepared prefill call: the config and a reusable workspace for fixed shapes."""
 
-    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, score: str = "saliency"):
-        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k, score)
+    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, score: str = "saliency",
+                 scope: str = "kv_head"):
+        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k, score, scope)
         nbytes = workspace_bytes(self.cfg)
         if nbytes == 0:
             rc = load().still_prefill(ctypes.byref(self.cfg), None, None, None, None, None, None, None, None,
@@ -164,19 +167,22 @@ class Prefill:
 
 
 def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing=None,
-            return_saliency: bool = False, return_routing: bool = False, cache=None, score: str = "saliency"):
+            return_saliency: bool = False, return_routing: bool = False, cache=None, score: str = "saliency",
+            scope: str = "kv_head"):
     """One STILL layer over whole sequences.
 
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
     GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection.
     cache: optional empty DecodeCache, left ready to decode token T.
     score: "saliency" (the Self-Saliency Score) or "diag" (the diagonal logit alone).
+    scope: "kv_head" (each KV head selects for its group) or "query_head" (each query head
+    selects for itself; the score and routing are then [B,Hq,...]).
     Returns out (and the routing score [B,Hkv,T] fp32, sel_idx [B,Hkv,T//chunk,top_k] int32
     on request).
     """
-    call = Prefill(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk, score=score)
-    B, T, _, _ = q.shape
-    Hkv = k.shape[2]
+    call = Prefill(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk, score=score, scope=scope)
+    B, T, Hq, _ = q.shape
+    Hkv = Hq if scope == "query_head" else k.shape[2]  # heads that select
     out = torch.empty_like(q)
     sal = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device) if return_saliency else None
     sel = torch.empty((B, Hkv, T // chunk, top_k), dtype=torch.int32, device=q.device) if return_routing else None
@@ -194,8 +200,8 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
 class Backward:
     """A prepared backward call (routing held fixed): the config and a reusable workspace."""
 
-    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64):
-        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k)
+    def __init__(self, q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, scope: str = "kv_head"):
+        self.cfg = _tensor_cfg(q, k, w_phi, window, chunk, top_k, scope=scope)
         nbytes = int(load().still_backward_workspace_bytes(ctypes.byref(self.cfg)))
         if nbytes == 0:
             raise StillError(-2, "still_backward_workspace_bytes")
@@ -215,14 +221,14 @@ class Backward:
         return dq, dk, dv, dw_phi
 
 
-def backward(q, k, v, w_phi, out, dout, sel_idx, *, window: int, top_k: int, chunk: int = 64):
+def backward(q, k, v, w_phi, out, dout, sel_idx, *, window: int, top_k: int, chunk: int = 64, scope: str = "kv_head"):
     """Gradients of sum(out * dout) for one STILL layer with the routing sel_idx held fixed.
 
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D], out and dout like q (one dtype, on the
     GPU); sel_idx int32 [B,Hkv,T//chunk,top_k] as prefill(return_routing=True) gives it.
     Returns (dq, dk, dv) in the inputs' dtype and dw_phi in float32.
     """
-    call = Backward(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk)
+    call = Backward(q, k, v, w_phi, window=window, top_k=top_k, chunk=chunk, scope=scope)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dw = torch.empty(w_phi.shape, dtype=torch.float32, device=q.device)
     if sel_idx is not None:

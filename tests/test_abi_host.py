@@ -138,3 +138,17 @@ def test_decode_step_validation():
                         (_fake_cache(cfg, max_tokens=100), -4)):
         assert lib.still_prefill(ctypes.byref(cfg), p, p, p, p, p, None, None, None, ctypes.byref(cache), p, need,
                                  None) == code
+
+
+def test_routing_scope_checks():
+    """Per-query-head routing: a bad scope is rejected, a decode cache refuses it, and the
+    prefill and backward workspaces include the expanded copies."""
+    lib = still.load()
+    assert lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(scope="bogus"))) == 0
+    q1 = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(scope="query_head")))
+    kv = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg()))
+    assert q1 > kv > 0
+    assert lib.still_cache_bytes(ctypes.byref(_cfg(scope="query_head")), 1024) == 0
+    assert lib.still_backward_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) > \
+        lib.still_backward_workspace_bytes(ctypes.byref(_cfg())) > 0
+    assert lib.still_future_attention_mass_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) == 0

@@ -94,6 +94,31 @@ def test_backward_matches_oracle(case):
         assert e <= REL_TOL[dt], (nm, e)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_per_query_head_routing(dt):
+    """Per-query-head routing: the gradients of K, V and W_h are the sums over each group of
+    the oracle's gradients for the copies repeated per query head."""
+    B, T, Hq, Hkv, w, k = 1, 260, 4, 1, 64, 8
+    _say("per-query-head backward", dt)
+    wl, (q, kk, v, wp) = synth.small_case(seed=23, B=B, T=T, Hq=Hq, Hkv=Hkv, D=64, F=64, window=w, chunk=64,
+                                           top_k=k, dtype=dt, qk_scale=1.0, n_planted=5)
+    dout = synth.make_grad_out(wl)
+    tq, tk, tv, tw, tdo = (_dev(a, dt) for a in (q, kk, v, wp, dout))
+    out, idx = still.prefill(tq, tk, tv, tw, window=w, top_k=k, return_routing=True, scope="query_head")
+    grads = still.backward(tq, tk, tv, tw, out, tdo, idx, window=w, top_k=k, scope="query_head")
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    k_e, v_e, w_e = np.repeat(kk, G, axis=2), np.repeat(v, G, axis=2), np.repeat(wp, G, axis=0)
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    dq_r, dk_e, dv_e, dw_e = O.attend_backward(q, k_e, v_e, w_e, w, 64, sel, dout)
+    ref = (dq_r, dk_e.reshape(B, T, Hkv, G, 64).sum(axis=3), dv_e.reshape(B, T, Hkv, G, 64).sum(axis=3),
+           dw_e.reshape(Hkv, G, 64, 64).sum(axis=1))
+    for nm, g, r in zip(("dq", "dk", "dv", "dw"), grads, ref):
+        e = _rel_err(_np(g), r)
+        _say("per-query-head", dt, nm, "rel max err", e)
+        assert e <= REL_TOL[dt], (nm, e)
+
+
 def test_backward_is_deterministic():
     wl, (q, kk, v, wp) = synth.small_case(seed=5, B=1, T=300, Hq=8, Hkv=2, D=64, F=64, window=64, chunk=64,
                                            top_k=8, dtype="bf16", qk_scale=1.0, n_planted=6)
