@@ -156,3 +156,28 @@ def test_backward_at_headline_shape():
     _say("headline sum of dv rel err", e)
     assert e <= 1e-2
     assert np.all(np.isfinite(_np(dw)))
+
+
+def test_backward_long_sequence():
+    """65536 tokens of the 1B-shaped layer (bf16): 4x the headline's chunks and compact tiles,
+    the same checks as at the headline shape."""
+    wl = synth.L1B_16K.replace(seq_len=65536, name="llama3.2-1b-layer-T65536")
+    _say("backward long", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    dout = synth.make_grad_out(wl)
+    out, idx, (dq, dk, dv, dw) = _forward_backward(wl, q, k, v, wp, dout)
+    T, G = wl.seq_len, wl.n_q_heads // wl.n_kv_heads
+    t0 = T - 2 * wl.chunk
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    ref = O.attend_backward(q, k, v, wp, wl.window, wl.chunk, sel, dout, q_from=t0)
+    for nm, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        gn = _np(g)
+        assert np.all(np.isfinite(gn)), nm
+        e = _rel_err(gn[:, t0:], r[:, t0:])
+        _say("long", nm, "rel max err over the last 128 rows", e)
+        assert e <= REL_TOL["bf16"], (nm, e)
+    want = dout.astype(np.float64).reshape(1, T, wl.n_kv_heads, G, wl.head_dim).sum(axis=(1, 3))
+    e = float(np.abs(_np(dv).sum(axis=1) - want).max() / np.abs(want).max())
+    _say("long sum of dv rel err", e)
+    assert e <= 1e-2
+    assert np.all(np.isfinite(_np(dw)))
