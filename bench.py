@@ -483,8 +483,8 @@ def main() -> int:
             return 2
         res = run_fidelity(wl, args, torch, still, synth)
     elif args.backward:
-        if decode or wl.head_dim != 64:
-            print("--backward covers prefill workloads with head_dim 64", file=sys.stderr)
+        if decode or wl.head_dim != wl.feat_dim or wl.head_dim not in (64, 128):
+            print("--backward covers prefill workloads with head_dim = feat_dim = 64 or 128", file=sys.stderr)
             return 2
         res = run_backward(wl, args, torch, still, synth)
     else:

@@ -243,8 +243,9 @@ size_t still_backward_workspace_bytes(const still_config* cfg);
  *   dq       like q; dk, dv like k (dtype, written)
  *   dw_phi   [n_kv_heads, feat_dim, head_dim] fp32 (written, not accumulated)
  *   workspace  device scratch of at least still_backward_workspace_bytes(cfg) bytes.
- * Supported for head_dim = feat_dim = 64 (STILL_ERR_UNSUPPORTED otherwise). Every sum runs in
- * a fixed order, so repeated calls give identical bits. Rows whose normaliser is 0 (output
+ * Supported for head_dim = feat_dim = 64 (both dtypes) and head_dim = feat_dim = 128 (bf16);
+ * STILL_ERR_UNSUPPORTED otherwise. Every sum runs in a fixed order, so repeated calls give
+ * identical bits. Rows whose normaliser is 0 (output
  * 0) get no gradient. Returns STILL_OK or a negative status. */
 int still_backward(const still_config* cfg, const void* q, const void* k, const void* v,
                    const void* w_phi, const void* out, const void* dout, const int32_t* sel_idx,

@@ -218,7 +218,7 @@ struct BwdLayout {
 int check_bwd_cfg(const still_config* c) {
   const int st = check_cfg(c, true);
   if (st != STILL_OK) return st;
-  if (c->head_dim != 64 || c->feat_dim != 64) return STILL_ERR_UNSUPPORTED;
+  if (!still::bwd_shape_supported(c->dtype == STILL_BF16, c->head_dim, c->feat_dim)) return STILL_ERR_UNSUPPORTED;
   return STILL_OK;
 }
 

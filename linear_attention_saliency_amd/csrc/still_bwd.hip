@@ -28,15 +28,16 @@
 //                        R, the q side of dW
 //   bwd_rev_seg_kernel / bwd_rev_scan_kernel: R_c = sum over chunks >= c+2 and over the
 //                        query group (a segmented scan)
-//   bwd_dkv_far_kernel   per (compact tile, query split, KV head): the selected keys
+//   bwd_dkv_far_kernel   per (compact rows, query slice, KV head): the selected keys
 //                        against the queries of chunks >= their chunk + 2
 //   bwd_dkv_local_kernel per (chunk, KV head, batch): keys against the queries of their
 //                        own chunk and the next; R_c; the NP-Map backward; dk, dv
 //   bwd_dw_part_kernel / bwd_dw_sum_kernel: dW summed over chunks, heads and batch
 //
-// Supported: head_dim = feat_dim = 64, chunk 64, fp32 or bf16. Matrix products run on
-// MFMA in the layer's dtype with fp32 accumulation; every sum that crosses workgroups
-// goes through fp32 buffers in a fixed order, so the result is deterministic.
+// Instantiated for (head_dim, feat_dim) = (64, 64) in fp32 and bf16 and (128, 128) in bf16,
+// chunk 64. Matrix products run on MFMA in the layer's dtype with fp32 accumulation; every
+// sum that crosses workgroups goes through fp32 buffers in a fixed order, so the result is
+// deterministic.
 #include "still_launch.hpp"
 #include "still_layout.hpp"
 #include "still_route.hpp"
@@ -46,30 +47,28 @@ namespace still {
 
 namespace {
 
-constexpr int BD = 64;   // head_dim
-constexpr int BF = 64;   // feat_dim
-constexpr int BR = BF * BD + BF;
-
 // NP-Map forward of one row per lane column, for the row held as B fragments xf (SK):
 // z[blk][i] = (W x)[16 blk + 4 grp + i]; also m = elu(z) + 1, |x| and 1/|m|.
+template <int F>
 struct NpRow {
-  f32x4 z[4];
-  f32x4 m[4];
+  f32x4 z[F / 16];
+  f32x4 m[F / 16];
   float r, inv_nm;
 };
 
-template <typename T>
-__device__ __forceinline__ void np_forward(NpRow& n, const T* W, const typename Tr<T>::frag (&xf)[2]) {
+template <typename T, int D, int F>
+__device__ __forceinline__ void np_forward(NpRow<F>& n, const T* W, const typename Tr<T>::frag (&xf)[D / 32]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
+  for (int fb = 0; fb < F / 16; ++fb) {
     n.z[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(n.z[fb], Tr<T>::load8(W + (fb * 16 + r16) * BD + ks * 32 + grp * 8), xf[ks]);
+    for (int ks = 0; ks < D / 32; ++ks)
+      Tr<T>::mma(n.z[fb], Tr<T>::load8(W + (fb * 16 + r16) * D + ks * 32 + grp * 8), xf[ks]);
   }
   float nm2 = 0.f, xn2 = 0.f;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < F / 16; ++fb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float zv = n.z[fb][i];
@@ -78,7 +77,7 @@ __device__ __forceinline__ void np_forward(NpRow& n, const T* W, const typename 
       nm2 += mv * mv;
     }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = Tr<T>::to_f(xf[ks][e]);
@@ -92,15 +91,16 @@ __device__ __forceinline__ void np_forward(NpRow& n, const T* W, const typename 
 
 // NP-Map backward for the same row: dphi[blk][i] (feature 16 blk + 4 grp + i) -> dz (in
 // place) and dr = dphi . m^. dx = W^T dz + dr x / |x| is formed by the caller.
-__device__ __forceinline__ float np_backward(const NpRow& n, f32x4 (&dphi)[4]) {
+template <int F>
+__device__ __forceinline__ float np_backward(const NpRow<F>& n, f32x4 (&dphi)[F / 16]) {
   float dr = 0.f;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < F / 16; ++fb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dr += dphi[fb][i] * n.m[fb][i];
   dr = xor_sum_groups(dr) * n.inv_nm;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < F / 16; ++fb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float mh = n.m[fb][i] * n.inv_nm;
@@ -110,21 +110,14 @@ __device__ __forceinline__ float np_backward(const NpRow& n, f32x4 (&dphi)[4]) {
   return dr;
 }
 
-// W^T with the features pk-permuted, [dim][pk_pos(f)], into an LDS tile
-template <typename T>
+// W^T with the features pk-permuted, [dim][pk_pos(f)], into a Swz<T, F> LDS tile of D rows
+template <typename T, int D, int F>
 __device__ __forceinline__ void load_wt(T* lds, const T* W) {
-  for (int e = threadIdx.x; e < BF * BD; e += blockDim.x) {
-    const int f = e >> 6, dd = e & 63;
-    lds[Swz<T, 64>::off(dd, pk_pos(f))] = W[e];
+  for (int e = threadIdx.x; e < F * D; e += blockDim.x) {
+    const int f = e / D, dd = e % D;
+    lds[Swz<T, F>::off(dd, pk_pos(f))] = W[e];
   }
 }
-
-
-// buffers of the local-key kernel's step tiles in bf16 (2: the next step's copies overlap
-// this one's work; 1 leaves room for more workgroups per CU)
-constexpr int kLocalBuffers = 1;
-// query heads per dq workgroup in bf16 when the group size is even (1 or 2)
-constexpr int kDqHeads = 1;
 
 // selection bit mask of complete chunk c from the ascending positions (entries outside
 // the chunk are ignored); wave-uniform
@@ -139,15 +132,20 @@ __device__ __forceinline__ uint64_t chunk_sel(const int32_t* sel_idx, long long 
   return m;
 }
 
+// 1 / sqrt(head_dim)
+template <int D>
+constexpr float inv_sqrt_d() { return D == 64 ? 0.125f : 0.08838834764831845f; }
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D, int F>
 __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   using TT = Tr<T>;
-  __shared__ __attribute__((aligned(16))) T t_k[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_v[64 * 64];
-  __shared__ __attribute__((aligned(16))) T t_vt[64 * 64];
+  constexpr int FPW = F / 64, R = F * D + F;
+  __shared__ __attribute__((aligned(16))) T t_k[64 * D];
+  __shared__ __attribute__((aligned(16))) T t_v[64 * D];
+  __shared__ __attribute__((aligned(16))) T t_vt[D * 64];
   __shared__ float m2part[4 * 64];
   __shared__ float xn2[64];
   const Dims& d = a.d;
@@ -155,89 +153,93 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const int nvalid = min(64, d.T - 64 * c);
-  const long long rs = static_cast<long long>(d.Hkv) * BD;
+  const long long rs = static_cast<long long>(d.Hkv) * D;
   const long long row0 = (static_cast<long long>(b) * d.T + 64LL * c) * d.Hkv + h;
-  tile_load<T>(t_k, static_cast<const T*>(a.k) + row0 * BD, rs, nvalid);
-  tile_load<T>(t_v, static_cast<const T*>(a.v) + row0 * BD, rs, nvalid);
+  tile_load<T, D>(t_k, static_cast<const T*>(a.k) + row0 * D, rs, nvalid);
+  tile_load<T, D>(t_v, static_cast<const T*>(a.v) + row0 * D, rs, nvalid);
   const uint64_t selm = chunk_sel(a.sel_idx, bh, c, d);
-  typename TT::frag wf[1][2];
-  np_map_load_w<T, 64, 64>(static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD, wf);
+  typename TT::frag wf[FPW][D / 32];
+  np_map_load_w<T, D, F>(static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D, wf);
   __syncthreads();
   // V^T (keys pk-permuted) into LDS, K^T into memory
-  T* ktg = static_cast<T*>(a.kt) + (bh * d.nC + c) * (BD * 64);
-  for (int e = tid; e < 64 * 64; e += 256) {
+  T* ktg = static_cast<T*>(a.kt) + (bh * d.nC + c) * (D * 64);
+  for (int e = tid; e < D * 64; e += 256) {
     const int dd = e >> 6, p = e & 63, row = pk_index(p);
-    t_vt[Swz<T, 64>::off(dd, p)] = t_v[Swz<T, 64>::off(row, dd)];
-    ktg[e] = t_k[Swz<T, 64>::off(row, dd)];
+    t_vt[Swz<T, 64>::off(dd, p)] = t_v[Swz<T, D>::off(row, dd)];
+    ktg[e] = t_k[Swz<T, D>::off(row, dd)];
   }
-  f32x4 phi[4][1];
-  np_map_rows64<T, 64, 64>(t_k, 0, wf, m2part, xn2, phi);  // synchronises the workgroup
-  const int f = wave * 16 + r16;
-  T* phk = static_cast<T*>(a.phik) + (bh * d.nC * 64 + 64LL * c) * BF;
-  T* phkt = static_cast<T*>(a.phikt) + (bh * d.nC + c) * (BF * 64);
+  f32x4 phi[4][FPW];
+  np_map_rows64<T, D, F>(t_k, 0, wf, m2part, xn2, phi);  // synchronises the workgroup
+  T* phk = static_cast<T*>(a.phik) + (bh * d.nC * 64 + 64LL * c) * F;
+  T* phkt = static_cast<T*>(a.phikt) + (bh * d.nC + c) * (F * 64);
+  float* ust = a.ustate + (bh * d.nC + c) * R;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int fi = 0; fi < FPW; ++fi) {
+    const int f = (wave * FPW + fi) * 16 + r16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) phk[(kb * 16 + 4 * grp + i) * BF + pk_pos(f)] = TT::from_f(phi[kb][0][i]);
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-  for (int s = 0; s < 2; ++s) TT::store8(phkt + f * 64 + 32 * s + 8 * grp, pk_frag<T>(phi[2 * s][0], phi[2 * s + 1][0]));
-  // U_c = sum over unselected keys of phi(k) v^T, u_c = sum phi(k)
-  f32x4 ph[4];
-  float zs = 0.f;
+      for (int i = 0; i < 4; ++i) phk[(kb * 16 + 4 * grp + i) * F + pk_pos(f)] = TT::from_f(phi[kb][fi][i]);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+    for (int s = 0; s < 2; ++s)
+      TT::store8(phkt + f * 64 + 32 * s + 8 * grp, pk_frag<T>(phi[2 * s][fi], phi[2 * s + 1][fi]));
+    // U_c = sum over unselected keys of phi(k) v^T, u_c = sum phi(k)
+    f32x4 ph[4];
+    float zs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = kb * 16 + 4 * grp + i;
-      const bool la = row < nvalid && !((selm >> row) & 1ull);
-      ph[kb][i] = la ? phi[kb][0][i] : 0.f;
-      zs += ph[kb][i];
-    }
-  zs = xor_sum_groups(zs);
-  f32x4 u[4] = {};
-  rows_x_acc<T>(u, t_vt, ph);  // u[db][i] = U[f][16 db + 4 grp + i]
-  float* ust = a.ustate + (bh * d.nC + c) * BR;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-  for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4*>(ust + f * BD + db * 16 + 4 * grp) = u[db];
-  if (grp == 0) ust[BF * BD + f] = zs;
+      for (int i = 0; i < 4; ++i) {
+        const int row = kb * 16 + 4 * grp + i;
+        const bool la = row < nvalid && !((selm >> row) & 1ull);
+        ph[kb][i] = la ? phi[kb][fi][i] : 0.f;
+        zs += ph[kb][i];
+      }
+    zs = xor_sum_groups(zs);
+    f32x4 u[D / 16] = {};
+    rows_x_acc<T, D / 16>(u, t_vt, ph);  // u[db][i] = U[f][16 db + 4 grp + i]
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(ust + f * D + db * 16 + 4 * grp) = u[db];
+    if (grp == 0) ust[F * D + f] = zs;
+  }
   // the selected rows, in chunk order, into the compact buffers
   if (c < d.nCc && d.topk > 0) {
     const int32_t* sp = a.sel_idx + (bh * d.nCc + c) * d.topk;
-    T* ks = static_cast<T*>(a.ksel) + bh * a.ntiles * 64 * BD;
-    T* vs = static_cast<T*>(a.vsel) + bh * a.ntiles * 64 * BD;
-    T* kst = static_cast<T*>(a.kselt) + bh * a.ntiles * (BD * 64);
-    for (int e = tid; e < d.topk * 64; e += 256) {
-      const int r = e >> 6, dd = e & 63;
+    T* ks = static_cast<T*>(a.ksel) + bh * a.ntiles * 64 * D;
+    T* vs = static_cast<T*>(a.vsel) + bh * a.ntiles * 64 * D;
+    T* kst = static_cast<T*>(a.kselt) + bh * a.ntiles * (D * 64);
+    for (int e = tid; e < d.topk * D; e += 256) {
+      const int r = e / D, dd = e % D;
       const int pos = sp[r] - 64 * c;
       const bool ok = pos >= 0 && pos < 64;
-      const T kv = ok ? t_k[Swz<T, 64>::off(pos, dd)] : TT::from_f(0.f);
-      const T vv = ok ? t_v[Swz<T, 64>::off(pos, dd)] : TT::from_f(0.f);
+      const T kv = ok ? t_k[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
+      const T vv = ok ? t_v[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
       const int n = c * d.topk + r;
-      ks[static_cast<long long>(n) * BD + dd] = kv;
-      vs[static_cast<long long>(n) * BD + dd] = vv;
-      kst[(static_cast<long long>(n >> 6) * BD + dd) * 64 + pk_pos(n & 63)] = kv;
+      ks[static_cast<long long>(n) * D + dd] = kv;
+      vs[static_cast<long long>(n) * D + dd] = vv;
+      kst[(static_cast<long long>(n >> 6) * D + dd) * 64 + pk_pos(n & 63)] = kv;
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// U_c -> S_c = sum over chunks <= c-2, in place; one thread per (b, KV head, element)
-__global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, long long n_elems) {
+// U_c -> S_c = sum over chunks <= c-2, in place; one thread per (b, KV head, element of R)
+__global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, int R, long long n_elems) {
   const long long gid = blockIdx.x * 256LL + threadIdx.x;
   if (gid >= n_elems) return;
-  const long long bh = gid / BR, e = gid % BR;
-  float* p = ust + bh * nC * BR + e;
+  const long long bh = gid / R, e = gid % R;
+  float* p = ust + bh * nC * R + e;
   float acc = 0.f, p1 = 0.f, p2 = 0.f;
   constexpr int U = 8;  // loads of U chunks in flight together
   for (int c0 = 0; c0 < nC; c0 += U) {
     float cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = c0 + u < nC ? p[static_cast<long long>(c0 + u) * BR] : 0.f;
+    for (int u = 0; u < U; ++u) cur[u] = c0 + u < nC ? p[static_cast<long long>(c0 + u) * R] : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + u < nC) {
         acc += p2;
-        p[static_cast<long long>(c0 + u) * BR] = acc;
+        p[static_cast<long long>(c0 + u) * R] = acc;
       }
       p2 = p1;
       p1 = cur[u];
@@ -248,23 +250,23 @@ __global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, l
 // R_c = sum over chunks >= c+2 of the group's per-chunk sums, as a segmented scan over
 // chunks: bwd_rev_seg_kernel sums each segment of kRevSeg chunks (and the group's heads),
 // bwd_rev_scan_kernel starts from the later segments' total and scans its own segment down.
-// One thread per (b, KV head, segment, element) in both.
+// One thread per (b, KV head, segment, element of R) in both.
 constexpr int kRevSeg = 16;
 
 __global__ __launch_bounds__(256) void bwd_rev_seg_kernel(const float* apart, float* segsum, int nC, int G,
-                                                          int Hkv, int nseg, long long n_elems) {
+                                                          int Hkv, int nseg, int R, long long n_elems) {
   const long long gid = blockIdx.x * 256LL + threadIdx.x;
   if (gid >= n_elems) return;
-  const long long e = gid % BR, seg = (gid / BR) % nseg, bh = gid / (BR * nseg);
+  const long long e = gid % R, seg = (gid / R) % nseg, bh = gid / (static_cast<long long>(R) * nseg);
   const long long b = bh / Hkv, h = bh % Hkv;
   const long long hq0 = b * Hkv * G + h * G;
   const int c0 = static_cast<int>(seg) * kRevSeg, c1 = min(nC, c0 + kRevSeg);
   float acc = 0.f;
   for (int g = 0; g < G; ++g) {
-    const float* p = apart + (hq0 + g) * nC * BR + e;
+    const float* p = apart + (hq0 + g) * nC * R + e;
     float x[kRevSeg];
 #pragma unroll
-    for (int u = 0; u < kRevSeg; ++u) x[u] = c0 + u < c1 ? p[static_cast<long long>(c0 + u) * BR] : 0.f;
+    for (int u = 0; u < kRevSeg; ++u) x[u] = c0 + u < c1 ? p[static_cast<long long>(c0 + u) * R] : 0.f;
 #pragma unroll
     for (int u = 0; u < kRevSeg; ++u) acc += x[u];
   }
@@ -272,85 +274,85 @@ __global__ __launch_bounds__(256) void bwd_rev_seg_kernel(const float* apart, fl
 }
 
 __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(const float* apart, const float* segsum, float* rst,
-                                                           int nC, int G, int Hkv, int nseg, long long n_elems) {
+                                                           int nC, int G, int Hkv, int nseg, int R,
+                                                           long long n_elems) {
   const long long gid = blockIdx.x * 256LL + threadIdx.x;
   if (gid >= n_elems) return;
-  const long long e = gid % BR, seg = (gid / BR) % nseg, bh = gid / (BR * nseg);
+  const long long e = gid % R, seg = (gid / R) % nseg, bh = gid / (static_cast<long long>(R) * nseg);
   const long long b = bh / Hkv, h = bh % Hkv;
   const long long hq0 = b * Hkv * G + h * G;
   const int c0 = static_cast<int>(seg) * kRevSeg, c1 = min(nC, c0 + kRevSeg);
   float acc = 0.f;  // sum over the chunks of later segments
-  for (long long s2 = nseg - 1; s2 > seg; --s2) acc += segsum[(bh * nseg + s2) * BR + e];
+  for (long long s2 = nseg - 1; s2 > seg; --s2) acc += segsum[(bh * nseg + s2) * R + e];
   float x[kRevSeg];
 #pragma unroll
   for (int u = 0; u < kRevSeg; ++u) x[u] = 0.f;
   for (int g = 0; g < G; ++g) {
-    const float* p = apart + (hq0 + g) * nC * BR + e;
+    const float* p = apart + (hq0 + g) * nC * R + e;
 #pragma unroll
     for (int u = 0; u < kRevSeg; ++u)
-      if (c0 + u < c1) x[u] += p[static_cast<long long>(c0 + u) * BR];
+      if (c0 + u < c1) x[u] += p[static_cast<long long>(c0 + u) * R];
   }
-  float* r = rst + bh * nC * BR + e;
+  float* r = rst + bh * nC * R + e;
 #pragma unroll
   for (int u = kRevSeg - 1; u >= 0; --u) {
     const int c = c0 + u;
     if (c < c1) {
       acc += x[u];  // acc = sum over chunks >= c
-      if (c >= 2) r[static_cast<long long>(c - 2) * BR] = acc;
+      if (c >= 2) r[static_cast<long long>(c - 2) * R] = acc;
     }
   }
   if (seg == nseg - 1) {  // no chunk lies two or more after the last two
-    r[static_cast<long long>(nC - 1) * BR] = 0.f;
-    if (nC >= 2) r[static_cast<long long>(nC - 2) * BR] = 0.f;
+    r[static_cast<long long>(nC - 1) * R] = 0.f;
+    if (nC >= 2) r[static_cast<long long>(nC - 2) * R] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// NH query heads of one KV head per workgroup (four waves each, 16 queries per wave): the
-// key tiles each copy brings serve NH x 64 queries.
-template <typename T, int NH>
-__global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdArgs a) {
+// One query head of one KV head per workgroup: four waves, 16 queries per wave.
+template <typename T, int D, int F>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
-  constexpr int NSLOT = 4 * NH > 6 ? 4 * NH : 6;
+  constexpr int ND = D / 16, NF = F / 16, R = F * D + F;
+  constexpr int SLOT = (D > F ? D : F) * 64;  // elements per tile slot
   // tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5; the
-  // closing products use slots 4 hs .. 4 hs + 3 for head hs
-  __shared__ __attribute__((aligned(16))) T lds[NSLOT][64 * 64];
-  __shared__ float s_red[NH][4][64];
-  T* const t_k = lds[0];
-  T* const t_v = lds[1];
-  T* const t_kt = lds[2];
-  T* const t_pk = lds[3];
-  T* const t_pkt = lds[4];
+  // near chunks use K, V, K^T, phi(K), phi(K)^T in slots 0-4; W^T takes slots 0-1 (D x F);
+  // the closing products use slots 2-5
+  __shared__ __attribute__((aligned(16))) T lds[6 * SLOT];
+  __shared__ float s_red[4][F];
+  T* const t_k = lds;
+  T* const t_v = lds + SLOT;
+  T* const t_kt = lds + 2 * SLOT;
+  T* const t_pk = lds + 3 * SLOT;
+  T* const t_pkt = lds + 4 * SLOT;
 
   const Dims& d = a.d;
-  // work index: chunk fastest, then head group, then batch (the heads of one KV head
-  // share its compact tiles)
-  const int ngrp = d.Hq / NH;
+  // work index: chunk fastest, then query head, then batch (the heads of one KV head share
+  // its compact tiles). Divisions by run-time sizes leave the compiler unsure that these
+  // are uniform; telling it keeps the buffer descriptors in scalar registers.
   const int w = xcd_work(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
-  const int hs = wave >> 2, wl = wave & 3;  // head slot, wave within the head
-  // (divisions by run-time sizes leave the compiler unsure that these are uniform; telling
-  // it keeps the buffer descriptors in scalar registers)
   const int c = __builtin_amdgcn_readfirstlane(w % d.nC);
-  const int hq = __builtin_amdgcn_readfirstlane(((w / d.nC) % ngrp) * NH + hs);
-  const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * ngrp));
+  const int hq = __builtin_amdgcn_readfirstlane((w / d.nC) % d.Hq);
+  const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * d.Hq));
   const int h = hq / d.G;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const long long bhq = static_cast<long long>(b) * d.Hq + hq;
-  const int qrow = wl * 16 + r16;
+  const int qrow = wave * 16 + r16;
   const long long i = 64LL * c + qrow;  // this lane column's query
   const bool qvalid = i < d.T;
-  const float scale2 = kLog2e * 0.125f;  // log2(e) / sqrt(64)
-  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD;
+  constexpr float isd = inv_sqrt_d<D>();
+  const float scale2 = kLog2e * isd;
+  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D;
 
   // the query row, dout row and Delta = dout . out
-  const long long qoff = ((static_cast<long long>(b) * d.T + i) * d.Hq + hq) * BD;
-  frag qf[2], dof[2];
+  const long long qoff = ((static_cast<long long>(b) * d.T + i) * d.Hq + hq) * D;
+  frag qf[D / 32], dof[D / 32];
   float delta = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < D / 32; ++ks) {
     qf[ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qoff + ks * 32 + grp * 8) : TT::zero();
     dof[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
     const frag of = qvalid ? TT::load8(static_cast<const T*>(a.out) + qoff + ks * 32 + grp * 8) : TT::zero();
@@ -359,37 +361,35 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   }
   delta = xor_sum_groups(delta);
 
-  // phi(q): kept as operand fragments through the key loops (the NP-Map forward is
-  // recomputed for its backward at the end, which keeps the loops' registers low)
-  frag phf[2];
-  float dla = 0.f;  // the linear-attention part of the normaliser
-  {
-    NpRow nq;
-    np_forward<T>(nq, W, qf);
-    f32x4 phq[4];
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
-    phf[0] = pk_frag<T>(phq[0], phq[1]);
-    phf[1] = pk_frag<T>(phq[2], phq[3]);
-    if (c >= 2) {  // state part: phi(q) . z_c
-      const float* zc = a.ustate + (bh * d.nC + c) * BR + BF * BD;
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dla += phq[fb][e] * zc[fb * 16 + 4 * grp + e];
-    }
-  }
-
   const uint64_t sel_prev = chunk_sel(a.sel_idx, bh, c - 1, d);
   const int nsel_c = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
-  const T* ksel = static_cast<const T*>(a.ksel) + bh * a.ntiles * 64 * BD;
-  const T* vsel = static_cast<const T*>(a.vsel) + bh * a.ntiles * 64 * BD;
-  const T* kselt = static_cast<const T*>(a.kselt) + bh * a.ntiles * (BD * 64);
-  const float* st = a.ustate + (bh * d.nC + c) * BR;  // S_c, z_c
-  const long long krs = static_cast<long long>(d.Hkv) * BD;
+  const T* ksel = static_cast<const T*>(a.ksel) + bh * a.ntiles * 64 * D;
+  const T* vsel = static_cast<const T*>(a.vsel) + bh * a.ntiles * 64 * D;
+  const T* kselt = static_cast<const T*>(a.kselt) + bh * a.ntiles * (D * 64);
+  const float* st = a.ustate + (bh * d.nC + c) * R;  // S_c, z_c
+  const long long krs = static_cast<long long>(d.Hkv) * D;
 
+  // phi(q): kept as operand fragments through the key loops (the NP-Map forward is
+  // recomputed for its backward at the end, which keeps the loops' registers low)
+  frag phf[F / 32];
+  float dla = 0.f;  // the linear-attention part of the normaliser
+  {
+    NpRow<F> nq;
+    np_forward<T, D, F>(nq, W, qf);
+    f32x4 phq[NF];
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+#pragma unroll
+    for (int s2 = 0; s2 < F / 32; ++s2) phf[s2] = pk_frag<T>(phq[2 * s2], phq[2 * s2 + 1]);
+    if (c >= 2) {  // state part: phi(q) . z_c
+#pragma unroll
+      for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dla += phq[fb][e] * st[F * D + fb * 16 + 4 * grp + e];
+    }
+  }
 
   // ---- one pass over the keys. The softmax part of dq accumulates sum 2^{a - m} (dP - Delta) k
   // against a running reference m (log2 units; moved up only when a score passes it by more
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   // once it is known, at the end. Scores are raw q.k, the scale folded into the exponent's fma.
   constexpr float kLazy2 = 8.f;
   float m2 = -kInf, l_lane = 0.f;  // this lane's share of the softmax part of the normaliser / 2^m
-  f32x4 dqt[4] = {}, dpt[4] = {};
+  f32x4 dqt[ND] = {}, dpt[NF] = {};
   auto rebase = [&](const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
     float tm = -kInf;
 #pragma unroll
@@ -412,40 +412,45 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
       const float alpha = mn == m2 ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
       l_lane *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dqt[db] *= alpha;
+      for (int db = 0; db < ND; ++db) dqt[db] *= alpha;
       m2 = mn;
     }
   };
   // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
   // nsel_c read as zeros (the copies' range ends there)
-  using Dma = DmaTile<T, 64, 64, 4 * NH>;
-  Dma dma;
-  dma.init(64);
+  using DmaR = DmaTile<T, D, 64, 4>;   // 64 rows of D
+  using DmaT = DmaTile<T, 64, D, 4>;   // D rows of 64 (K^T)
+  using DmaF = DmaTile<T, F, 64, 4>;   // 64 rows of F (phi(K))
+  using DmaFT = DmaTile<T, 64, F, 4>;  // F rows of 64 (phi(K)^T)
+  DmaR dmr;
+  dmr.init(D);
+  DmaT dmt;
+  dmt.init(64);
   constexpr int ES = static_cast<int>(sizeof(T));
   const int ntc = (nsel_c + 63) / 64;
-  const auto rs_k = make_rsrc(ksel, static_cast<uint32_t>(nsel_c * BD * ES));
-  const auto rs_v = make_rsrc(vsel, static_cast<uint32_t>(nsel_c * BD * ES));
-  const auto rs_kt = make_rsrc(kselt, static_cast<uint32_t>(ntc * BD * 64 * ES));
+  const auto rs_k = make_rsrc(ksel, static_cast<uint32_t>(nsel_c * D * ES));
+  const auto rs_v = make_rsrc(vsel, static_cast<uint32_t>(nsel_c * D * ES));
+  const auto rs_kt = make_rsrc(kselt, static_cast<uint32_t>(ntc * D * 64 * ES));
   auto issue3 = [&](int t) {
-    const int sl = (t & 1) * 3;
-    dma.issue(lds[sl], rs_k, t * 64 * BD * ES);
-    dma.issue(lds[sl + 1], rs_v, t * 64 * BD * ES);
-    dma.issue(lds[sl + 2], rs_kt, t * BD * 64 * ES);
+    T* const sl = lds + (t & 1) * 3 * SLOT;
+    dmr.issue(sl, rs_k, t * 64 * D * ES);
+    dmr.issue(sl + SLOT, rs_v, t * 64 * D * ES);
+    dmt.issue(sl + 2 * SLOT, rs_kt, t * D * 64 * ES);
   };
   if (ntc > 0) issue3(0);
   for (int t = 0; t < ntc; ++t) {
     if (t + 1 < ntc) {
       issue3(t + 1);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * Dma::PER_WAVE));
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DmaR::PER_WAVE + DmaT::PER_WAVE));
     } else {
       __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     }
     lds_sync();
     const int nv = min(64, nsel_c - t * 64);
-    const int sl = (t & 1) * 3;
+    const T* const sl = lds + (t & 1) * 3 * SLOT;
     f32x4 s[4], dp[4];
-    rows_x_frag<T>(s, lds[sl], qf);
-    rows_x_frag<T>(dp, lds[sl + 1], dof);
+    rows_x_frag<T, D>(s, sl, qf);
+    rows_x_frag<T, D>(dp, sl + SLOT, dof);
     bool sa[4][4];
     if (nv == 64) {  // a full tile
       rebase(s, sa, false);
@@ -474,27 +479,31 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
           s[kb][e] = p * (dp[kb][e] - delta);
         }
     }
-    rows_x_acc<T>(dqt, lds[sl + 2], s);
+    rows_x_acc<T, ND>(dqt, sl + 2 * SLOT, s);
     lds_sync();
   }
-  Dma dkv;  // key and value rows of the input, row stride Hkv * D
+  DmaR dkv;  // key and value rows of the input, row stride Hkv * D
   dkv.init(static_cast<int>(krs));
+  DmaF dmf;
+  dmf.init(F);
+  DmaFT dmft;
+  dmft.init(64);
   for (int cc = c >= 1 ? c - 1 : 0; cc <= c; ++cc) {
     __syncthreads();
     const long long r0 = (static_cast<long long>(b) * d.T + 64LL * cc) * d.Hkv + h;
     const int nv = min(64, d.T - 64 * cc);
-    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * krs + BD) * ES);
-    dkv.issue(t_k, make_rsrc(static_cast<const T*>(a.k) + r0 * BD, rows_b), 0);
-    dkv.issue(t_v, make_rsrc(static_cast<const T*>(a.v) + r0 * BD, rows_b), 0);
-    dma.issue(t_kt, make_rsrc(static_cast<const T*>(a.kt) + (bh * d.nC + cc) * BD * 64, BD * 64 * ES), 0);
-    dma.issue(t_pk, make_rsrc(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * BF, 64 * BF * ES), 0);
-    dma.issue(t_pkt, make_rsrc(static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * BF * 64, BF * 64 * ES), 0);
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * krs + D) * ES);
+    dkv.issue(t_k, make_rsrc(static_cast<const T*>(a.k) + r0 * D, rows_b), 0);
+    dkv.issue(t_v, make_rsrc(static_cast<const T*>(a.v) + r0 * D, rows_b), 0);
+    dmt.issue(t_kt, make_rsrc(static_cast<const T*>(a.kt) + (bh * d.nC + cc) * D * 64, D * 64 * ES), 0);
+    dmf.issue(t_pk, make_rsrc(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + 64LL * cc) * F, 64 * F * ES), 0);
+    dmft.issue(t_pkt, make_rsrc(static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * F * 64, F * 64 * ES), 0);
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_sync();
     f32x4 s[4], dp[4], lw[4];
-    rows_x_frag<T>(s, t_k, qf);
-    rows_x_frag<T>(dp, t_v, dof);
-    rows_x_frag<T>(lw, t_pk, phf);
+    rows_x_frag<T, D>(s, t_k, qf);
+    rows_x_frag<T, D>(dp, t_v, dof);
+    rows_x_frag<T, F>(lw, t_pk, phf);
     bool sa[4][4], la[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -520,8 +529,8 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
         s[kb][e] = p * g;
         lw[kb][e] = la[kb][e] ? g : 0.f;
       }
-    rows_x_acc<T>(dqt, t_kt, s);
-    rows_x_acc<T>(dpt, t_pkt, lw);
+    rows_x_acc<T, ND>(dqt, t_kt, s);
+    rows_x_acc<T, NF>(dpt, t_pkt, lw);
   }
   const float l = xor_sum_groups(l_lane);
   dla = xor_sum_groups(dla);
@@ -540,43 +549,44 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
   const float einv = exp2f(-L2);
   const float sa_scale = l > 0.f ? exp2f(m2 - L2) : 0.f;  // 2^m / normaliser
 #pragma unroll
-  for (int db = 0; db < 4; ++db) dqt[db] *= sa_scale;
+  for (int db = 0; db < ND; ++db) dqt[db] *= sa_scale;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) dpt[fb] *= einv;
+  for (int fb = 0; fb < NF; ++fb) dpt[fb] *= einv;
   if (c >= 2) {
     // dphi(q) += e^{-L} (S_c dout - Delta z_c)
-    f32x4 sdo[4] = {};
-    f32rows_x_frag<T>(sdo, st, dof);
+    f32x4 sdo[NF] = {};
+    f32rows_x_frag<T, NF, D>(sdo, st, dof);
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
+    for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dpt[fb][e] += einv * (sdo[fb][e] - delta * st[BF * BD + fb * 16 + 4 * grp + e]);
+      for (int e = 0; e < 4; ++e) dpt[fb][e] += einv * (sdo[fb][e] - delta * st[F * D + fb * 16 + 4 * grp + e]);
   }
 
   // ---- NP-Map backward and dq
-  NpRow nq;
-  np_forward<T>(nq, W, qf);
-  f32x4 phq[4];
+  NpRow<F> nq;
+  np_forward<T, D, F>(nq, W, qf);
+  f32x4 phq[NF];
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
-  const float dr = np_backward(nq, dpt);  // dpt now holds dz
+  const float dr = np_backward<F>(nq, dpt);  // dpt now holds dz
   __syncthreads();
-  load_wt<T>(t_k, W);
+  T* const t_wt = lds;  // D x F, slots 0-1
+  load_wt<T, D, F>(t_wt, W);
   __syncthreads();
-  f32x4 dxt[4] = {};
-  rows_x_acc<T>(dxt, t_k, dpt);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
+  f32x4 dxt[ND] = {};
+  rows_x_acc<T, ND, F>(dxt, t_wt, dpt);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
   if (qvalid) {
     T* dq = static_cast<T*>(a.dq) + qoff;
     const T* xq = static_cast<const T*>(a.q) + qoff;
     const float xs = nq.r > 0.f ? dr / nq.r : 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < ND; ++db) {
       const typename TT::quad x4 = TT::load4(xq + db * 16 + 4 * grp);
       typename TT::quad o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = TT::from_f(dqt[db][e] * 0.125f + dxt[db][e] + xs * TT::to_f(x4[e]));
+      for (int e = 0; e < 4; ++e) o4[e] = TT::from_f(dqt[db][e] * isd + dxt[db][e] + xs * TT::to_f(x4[e]));
       *reinterpret_cast<typename TT::quad*>(dq + db * 16 + 4 * grp) = o4;
     }
   }
@@ -588,25 +598,25 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta : 0.f;
   }
   // phi(q) rows and phi(q)^T are stored times e^{-L}, the factor every key-side use takes
-  T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * BF;
+  T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * F;
   {
-    f32x4 ps4[4];
+    f32x4 ps4[NF];
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) ps4[fb] = phq[fb] * einv;
-    TT::store8(phqr + 8 * grp, pk_frag<T>(ps4[0], ps4[1]));
-    TT::store8(phqr + 32 + 8 * grp, pk_frag<T>(ps4[2], ps4[3]));
+    for (int fb = 0; fb < NF; ++fb) ps4[fb] = phq[fb] * einv;
+#pragma unroll
+    for (int s2 = 0; s2 < F / 32; ++s2) TT::store8(phqr + 32 * s2 + 8 * grp, pk_frag<T>(ps4[2 * s2], ps4[2 * s2 + 1]));
   }
-  T* phqt = static_cast<T*>(a.phiqt) + qc * BF * 64;
-  T* qt = static_cast<T*>(a.qt) + qc * BD * 64;
-  T* dot = static_cast<T*>(a.dot) + qc * BD * 64;
+  T* phqt = static_cast<T*>(a.phiqt) + qc * F * 64;
+  T* qt = static_cast<T*>(a.qt) + qc * D * 64;
+  T* dot = static_cast<T*>(a.dot) + qc * D * 64;
   const int pq = pk_pos(qrow);
-  T* const e_phq = lds[4 * hs];      // e^{-L} phi(q)^T of this head
-  T* const e_do = lds[4 * hs + 1];   // dout^T
-  T* const e_dz = lds[4 * hs + 2];   // dz^T
-  T* const e_q = lds[4 * hs + 3];    // q^T
-  __syncthreads();  // slot 0 (W^T) is reused below
+  T* const e_phq = lds + 2 * SLOT;  // e^{-L} phi(q)^T, F rows
+  T* const e_do = lds + 3 * SLOT;   // dout^T, D rows
+  T* const e_dz = lds + 4 * SLOT;   // dz^T, F rows
+  T* const e_q = lds + 5 * SLOT;    // q^T, D rows
+  __syncthreads();  // W^T is no longer read
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int f = fb * 16 + 4 * grp + e;
@@ -614,7 +624,7 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
       e_dz[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);
     }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int dd = ks * 32 + grp * 8 + e;
@@ -623,50 +633,60 @@ __global__ __launch_bounds__(256 * NH, NH == 1 ? 3 : 1) void bwd_dq_kernel(BwdAr
     }
   // a_c partial: sum over the head's 64 queries of e^{-L} Delta phi(q)
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta : 0.f));
-      if (r16 == 0) s_red[hs][wl][fb * 16 + 4 * grp + e] = v;
+      if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
     }
   __syncthreads();
   // the transposed tiles to memory in 16-byte pieces
-  for (int idx = tid & 255; idx < 512; idx += 256) {
+  for (int idx = tid; idx < F * 8; idx += 256) {
     const int row = idx >> 3, col = (idx & 7) * 8;
     TT::store8(phqt + row * 64 + col, SW::load8(e_phq, row, col));
+  }
+  for (int idx = tid; idx < D * 8; idx += 256) {
+    const int row = idx >> 3, col = (idx & 7) * 8;
     TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
     TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
   }
-  float* ap = a.apart + qc * BR;
-  if (wl == 0)
-    ap[BF * BD + lane] = ((s_red[hs][0][lane] + s_red[hs][1][lane]) + s_red[hs][2][lane]) + s_red[hs][3][lane];
-  f32x4 acc[4];
-  tile_x_tile<T>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
+  float* ap = a.apart + qc * R;
+  for (int f = tid; f < F; f += 256) ap[F * D + f] = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
+  {
+    f32x4 acc[F / 64][D / 16];
+    tile_x_tile<T, F, D>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+    for (int rb = 0; rb < F / 64; ++rb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ap[(wl * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
-  tile_x_tile<T>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
-  float* wp = a.dwq + qc * (BF * BD);
+      for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+        for (int e = 0; e < 4; ++e) ap[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+    tile_x_tile<T, F, D>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
+    float* wp = a.dwq + qc * (F * D);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wp[(wl * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+    for (int rb = 0; rb < F / 64; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wp[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // Selected keys against the queries of chunks >= their chunk + 2. A workgroup of eight
-// waves takes 128 compact rows (16 per wave) and one of gridDim.y slices of the query
-// chunks; it writes fp32 partial dk, dv (softmax part, before the 1/sqrt(D) of dk). The
-// query-side tiles (q rows, dout rows, q^T, dout^T) arrive by buffer -> LDS copies one
-// (chunk, head) step ahead, with that step's (L, Delta) prefetched into registers.
-template <typename T>
-__global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
+// waves takes 128 compact rows (16 per wave) and one of the query slices; it writes fp32
+// partial dk, dv (softmax part, before the 1/sqrt(D) of dk). The query-side tiles (q rows,
+// dout rows, q^T, dout^T) arrive by buffer -> LDS copies one (chunk, head) step ahead, with
+// that step's (L, Delta) prefetched into registers.
+template <typename T, int D>
+__global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkv_far_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
-  using Dma = DmaTile<T, 64, 64, 8>;
+  using DmaR = DmaTile<T, D, 64, 8>;  // 64 rows of D
+  using DmaT = DmaTile<T, 64, D, 8>;  // D rows of 64
   constexpr int ES = static_cast<int>(sizeof(T));
-  __shared__ __attribute__((aligned(16))) T lds[2][4][64 * 64];  // [buffer][q, dout, q^T, dout^T]
+  constexpr int ND = D / 16;
+  __shared__ __attribute__((aligned(16))) T lds[2][4][D * 64];  // [buffer][q, dout, q^T, dout^T]
   __shared__ __attribute__((aligned(16))) float s_ld[2][2][64];  // [buffer][L, Delta][query]
   const Dims& d = a.d;
   // work index: row group fastest, then query slice, then (batch, KV head): the row groups
@@ -679,18 +699,18 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
   const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(bh / d.Hkv));
   const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % d.Hkv));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
-  const float scale2 = kLog2e * 0.125f;
+  const float scale2 = kLog2e * inv_sqrt_d<D>();
   const int nsel = d.nCc * d.topk;
   const int row0 = grp_id * 128;
   const int n = row0 + wave * 16 + r16;  // this lane column's compact row
   const bool nin = n < a.ntiles * 64;     // inside the buffers (rows past nsel are zeros)
   const int ckey = n < nsel ? n / d.topk : 0x3fffffff;
-  frag kf[2], vf[2];
+  frag kf[D / 32], vf[D / 32];
   {
-    const T* kr = static_cast<const T*>(a.ksel) + (bh * a.ntiles * 64 + n) * BD;
-    const T* vr = static_cast<const T*>(a.vsel) + (bh * a.ntiles * 64 + n) * BD;
+    const T* kr = static_cast<const T*>(a.ksel) + (bh * a.ntiles * 64 + n) * D;
+    const T* vr = static_cast<const T*>(a.vsel) + (bh * a.ntiles * 64 + n) * D;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < D / 32; ++ks) {
       kf[ks] = nin ? TT::load8(kr + ks * 32 + grp * 8) : TT::zero();
       vf[ks] = nin ? TT::load8(vr + ks * 32 + grp * 8) : TT::zero();
     }
@@ -701,27 +721,27 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
   const int per = (d.nC + a.nsplit - 1) / a.nsplit;
   const int cb0 = max(c_lo, split * per), cb1 = min(d.nC, (split + 1) * per);
   const int nsteps = max(0, cb1 - cb0) * d.G;
-  Dma dma;
+  DmaT dma;
   dma.init(64);
-  Dma dmq;
-  dmq.init(d.Hq * BD);
+  DmaR dmq;
+  dmq.init(d.Hq * D);
   const long long hq0 = static_cast<long long>(b) * d.Hq + static_cast<long long>(h) * d.G;  // b*Hq + first head
   auto step_ptrs = [&](int st, long long& qc, long long& r0, int& nv) {
     const int cq = __builtin_amdgcn_readfirstlane(cb0 + st / d.G), g = __builtin_amdgcn_readfirstlane(st % d.G);
     qc = (hq0 + g) * d.nC + cq;
-    r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + h * d.G + g) * BD;
+    r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + h * d.G + g) * D;
     nv = min(64, d.T - 64 * cq);
   };
   auto issue = [&](int st) {
     long long qc, r0;
     int nv;
     step_ptrs(st, qc, r0, nv);
-    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * BD + BD) * ES);
-    T* dst = lds[st & 1][0];
-    dmq.issue(dst, make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
-    dmq.issue(dst + 64 * 64, make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
-    dma.issue(dst + 2 * 64 * 64, make_rsrc(static_cast<const T*>(a.qt) + qc * BD * 64, BD * 64 * ES), 0);
-    dma.issue(dst + 3 * 64 * 64, make_rsrc(static_cast<const T*>(a.dot) + qc * BD * 64, BD * 64 * ES), 0);
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * D + D) * ES);
+    T(*dst)[D * 64] = lds[st & 1];
+    dmq.issue(dst[0], make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
+    dmq.issue(dst[1], make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
+    dma.issue(dst[2], make_rsrc(static_cast<const T*>(a.qt) + qc * D * 64, D * 64 * ES), 0);
+    dma.issue(dst[3], make_rsrc(static_cast<const T*>(a.dot) + qc * D * 64, D * 64 * ES), 0);
   };
   auto ld_of = [&](int st) {  // this thread's (L, Delta) entry of step st
     long long qc, r0;
@@ -729,7 +749,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
     step_ptrs(st, qc, r0, nv);
     return a.ld[qc * 128 + (tid & 127)];
   };
-  f32x4 dkt[4] = {}, dvt[4] = {};
+  f32x4 dkt[ND] = {}, dvt[ND] = {};
   float ldn = 0.f;
   if (nsteps > 0) {
     ldn = ld_of(0);
@@ -740,7 +760,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
     if (st + 1 < nsteps) {
       ldn = ld_of(st + 1);
       issue(st + 1);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * Dma::PER_WAVE + 1));
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DmaR::PER_WAVE + 2 * DmaT::PER_WAVE + 1));
     } else {
       __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     }
@@ -753,8 +773,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
     const T* tqt = lds[st & 1][2];
     const T* tdot = lds[st & 1][3];
     f32x4 s[4], dp[4];
-    rows_x_frag<T>(s, tq, kf);  // s[qb][e] = q[16 qb + 4 grp + e] . k
-    rows_x_frag<T>(dp, tdo, vf);
+    rows_x_frag<T, D>(s, tq, kf);  // s[qb][e] = q[16 qb + 4 grp + e] . k
+    rows_x_frag<T, D>(dp, tdo, vf);
     const bool on = cq >= ckey + 2;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -767,121 +787,99 @@ __global__ __launch_bounds__(512, 2) void bwd_dkv_far_kernel(BwdArgs a) {
         dp[qb][e] = p;
       }
     }
-    rows_x_acc<T>(dvt, tdot, dp);
-    rows_x_acc<T>(dkt, tqt, s);
+    rows_x_acc<T, ND>(dvt, tdot, dp);
+    rows_x_acc<T, ND>(dkt, tqt, s);
     lds_sync();
   }
   if (nin) {
-    float* out = a.dkvsel + ((static_cast<long long>(split) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+    float* out = a.dkvsel + ((static_cast<long long>(split) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * D);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < ND; ++db) {
       *reinterpret_cast<f32x4*>(out + db * 16 + 4 * grp) = dkt[db];
-      *reinterpret_cast<f32x4*>(out + BD + db * 16 + 4 * grp) = dvt[db];
+      *reinterpret_cast<f32x4*>(out + D + db * 16 + 4 * grp) = dvt[db];
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D, int F>
 __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
-  using Dma = DmaTile<T, 64, 64, 4>;
+  using DmaR = DmaTile<T, D, 64, 4>;   // 64 rows of D
+  using DmaT = DmaTile<T, 64, D, 4>;   // D rows of 64
+  using DmaF = DmaTile<T, F, 64, 4>;   // 64 rows of F
+  using DmaFT = DmaTile<T, 64, F, 4>;  // F rows of 64
   constexpr int ES = static_cast<int>(sizeof(T));
-  constexpr int NBUF = sizeof(T) == 2 ? kLocalBuffers : 1;
+  constexpr int ND = D / 16, NF = F / 16, R = F * D + F;
+  constexpr int SLOT = (D > F ? D : F) * 64;
   // per step: q rows, dout rows, q^T, dout^T, phi(q) rows, phi(q)^T of one (head, chunk)
-  __shared__ __attribute__((aligned(16))) T lds[NBUF][6][64 * 64];
-  __shared__ __attribute__((aligned(16))) float s_ld[NBUF][2][64];  // [buffer][L, Delta][query]
-  T* const t_q = lds[0][0];
-  T* const t_do = lds[0][1];
-  T* const t_qt = lds[0][2];
+  __shared__ __attribute__((aligned(16))) T lds[6 * SLOT];
+  __shared__ __attribute__((aligned(16))) float s_ld[2][64];  // [L, Delta][query]
   const Dims& d = a.d;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
-  const float scale2 = kLog2e * 0.125f;
+  constexpr float isd = inv_sqrt_d<D>();
+  const float scale2 = kLog2e * isd;
   const int jr = wave * 16 + r16;
   const long long j = 64LL * c + jr;  // this lane column's key
   const bool kvalid = j < d.T;
   const uint64_t selm = chunk_sel(a.sel_idx, bh, c, d);
   const bool selj = (selm >> jr) & 1ull;
-  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * BF * BD;
-  const long long koff = ((static_cast<long long>(b) * d.T + j) * d.Hkv + h) * BD;
-  frag kf[2], vf[2], phk[2];
+  const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D;
+  const long long koff = ((static_cast<long long>(b) * d.T + j) * d.Hkv + h) * D;
+  frag kf[D / 32], vf[D / 32], phk[F / 32];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < D / 32; ++ks) {
     kf[ks] = kvalid ? TT::load8(static_cast<const T*>(a.k) + koff + ks * 32 + grp * 8) : TT::zero();
     vf[ks] = kvalid ? TT::load8(static_cast<const T*>(a.v) + koff + ks * 32 + grp * 8) : TT::zero();
-    phk[ks] = TT::load8(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + j) * BF + ks * 32 + grp * 8);
   }
-  f32x4 dkt[4] = {}, dvt[4] = {}, dpk[4] = {};
+#pragma unroll
+  for (int s2 = 0; s2 < F / 32; ++s2)
+    phk[s2] = TT::load8(static_cast<const T*>(a.phik) + (bh * d.nC * 64 + j) * F + s2 * 32 + grp * 8);
+  f32x4 dkt[ND] = {}, dvt[ND] = {}, dpk[NF] = {};
   // steps over (query head g, query chunk cq in {c, c+1}); the tiles arrive by
-  // buffer -> LDS copies, one step ahead when two buffers fit
+  // buffer -> LDS copies
   const int ncq = c + 1 < d.nC ? 2 : 1;
   const int nsteps = d.G * ncq;
-  Dma dma, dmq;
-  dma.init(64);
-  dmq.init(d.Hq * BD);
-  auto step_of = [&](int st, long long& hq, int& cq) {
-    hq = static_cast<long long>(b) * d.Hq + h * d.G + __builtin_amdgcn_readfirstlane(st / ncq);  // b*Hq + query head
-    cq = c + __builtin_amdgcn_readfirstlane(st % ncq);
-  };
-  auto issue = [&](int st) {
-    long long hq;
-    int cq;
-    step_of(st, hq, cq);
-    const long long qc = hq * d.nC + cq;
-    const long long r0 = ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (hq - static_cast<long long>(b) * d.Hq)) * BD;
-    const int nv = min(64, d.T - 64 * cq);
-    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * BD + BD) * ES);
-    T(*dst)[64 * 64] = lds[st % NBUF];
-    dmq.issue(dst[0], make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
-    dmq.issue(dst[1], make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
-    dma.issue(dst[2], make_rsrc(static_cast<const T*>(a.qt) + qc * BD * 64, BD * 64 * ES), 0);
-    dma.issue(dst[3], make_rsrc(static_cast<const T*>(a.dot) + qc * BD * 64, BD * 64 * ES), 0);
-    dma.issue(dst[4], make_rsrc(static_cast<const T*>(a.phiq) + qc * 64 * BF, 64 * BF * ES), 0);
-    dma.issue(dst[5], make_rsrc(static_cast<const T*>(a.phiqt) + qc * BF * 64, BF * 64 * ES), 0);
-  };
-  auto ld_of = [&](int st) {
-    long long hq;
-    int cq;
-    step_of(st, hq, cq);
-    return a.ld[(hq * d.nC + cq) * 128 + (tid & 127)];
-  };
-  float ldn = ld_of(0);
-  if (NBUF == 2) issue(0);
+  DmaR dmq;
+  dmq.init(d.Hq * D);
+  DmaT dmt;
+  dmt.init(64);
+  DmaF dmf;
+  dmf.init(F);
+  DmaFT dmft;
+  dmft.init(64);
   for (int st = 0; st < nsteps; ++st) {
-    const float ldc = ldn;
-    if (NBUF == 2) {
-      if (st + 1 < nsteps) {
-        ldn = ld_of(st + 1);
-        issue(st + 1);
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(6 * Dma::PER_WAVE + 1));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-      }
-    } else {
-      issue(st);
-      if (st + 1 < nsteps) ldn = ld_of(st + 1);
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    }
-    if (tid < 128) s_ld[st % NBUF][tid & 1][tid >> 1] = ldc;
+    const long long hq = static_cast<long long>(b) * d.Hq + h * d.G + __builtin_amdgcn_readfirstlane(st / ncq);
+    const int cq = c + __builtin_amdgcn_readfirstlane(st % ncq);
+    const long long qc = hq * d.nC + cq;
+    const long long r0 =
+        ((static_cast<long long>(b) * d.T + 64LL * cq) * d.Hq + (hq - static_cast<long long>(b) * d.Hq)) * D;
+    const int nv = min(64, d.T - 64 * cq);
+    const uint32_t rows_b = static_cast<uint32_t>(((nv - 1) * d.Hq * D + D) * ES);
+    const float ldc = a.ld[qc * 128 + (tid & 127)];
+    dmq.issue(lds, make_rsrc(static_cast<const T*>(a.q) + r0, rows_b), 0);
+    dmq.issue(lds + SLOT, make_rsrc(static_cast<const T*>(a.dout) + r0, rows_b), 0);
+    dmt.issue(lds + 2 * SLOT, make_rsrc(static_cast<const T*>(a.qt) + qc * D * 64, D * 64 * ES), 0);
+    dmt.issue(lds + 3 * SLOT, make_rsrc(static_cast<const T*>(a.dot) + qc * D * 64, D * 64 * ES), 0);
+    dmf.issue(lds + 4 * SLOT, make_rsrc(static_cast<const T*>(a.phiq) + qc * 64 * F, 64 * F * ES), 0);
+    dmft.issue(lds + 5 * SLOT, make_rsrc(static_cast<const T*>(a.phiqt) + qc * F * 64, F * 64 * ES), 0);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    if (tid < 128) s_ld[tid & 1][tid >> 1] = ldc;
     __builtin_amdgcn_s_waitcnt(kLgkmWait0);
     lds_sync();
-    long long hq;
-    int cq;
-    step_of(st, hq, cq);
-    T(*cur)[64 * 64] = lds[st % NBUF];
     {
       f32x4 s[4], dp[4], lw[4];
-      rows_x_frag<T>(s, cur[0], kf);
-      rows_x_frag<T>(dp, cur[1], vf);
-      rows_x_frag<T>(lw, cur[4], phk);
+      rows_x_frag<T, D>(s, lds, kf);
+      rows_x_frag<T, D>(dp, lds + SLOT, vf);
+      rows_x_frag<T, F>(lw, lds + 4 * SLOT, phk);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const f32x4 lq = *reinterpret_cast<const f32x4*>(&s_ld[st % NBUF][0][qb * 16 + 4 * grp]);
-        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(&s_ld[st % NBUF][1][qb * 16 + 4 * grp]);
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(&s_ld[0][qb * 16 + 4 * grp]);
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(&s_ld[1][qb * 16 + 4 * grp]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qr = qb * 16 + 4 * grp + e;
@@ -891,45 +889,46 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
           const bool sel = cq > c && selj;
           const bool sa = vis && (inwin || sel);
           const bool la = vis && !(inwin || sel);
-          const float L2 = lq[e], dl = dq4[e];
-          const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], scale2, -L2)) : 0.f;
-          const float gg = dp[qb][e] - dl;
-          s[qb][e] = p * gg;                    // dS
+          const float p = sa ? __builtin_amdgcn_exp2f(fmaf(s[qb][e], scale2, -lq[e])) : 0.f;
+          const float gg = dp[qb][e] - dq4[e];
+          s[qb][e] = p * gg;                       // dS
           dp[qb][e] = p + (la ? lw[qb][e] : 0.f);  // weight of v_j in out_i (phi(q) carries e^{-L})
-          lw[qb][e] = la ? gg : 0.f;            // g / e^{-L}
+          lw[qb][e] = la ? gg : 0.f;               // g / e^{-L}
         }
       }
-      rows_x_acc<T>(dvt, cur[3], dp);
-      rows_x_acc<T>(dkt, cur[2], s);
-      rows_x_acc<T>(dpk, cur[5], lw);
+      rows_x_acc<T, ND>(dvt, lds + 3 * SLOT, dp);
+      rows_x_acc<T, ND>(dkt, lds + 2 * SLOT, s);
+      rows_x_acc<T, NF>(dpk, lds + 5 * SLOT, lw);
     }
     lds_sync();
   }
   // queries of chunks >= c+2 through R_c, r_c (unselected keys only)
   if (c + 2 < d.nC) {
-    const float* rs = a.rstate + (bh * d.nC + c) * BR;
-    f32x4 rv[4] = {};
-    f32rows_x_frag<T>(rv, rs, vf);  // (R v)[16 fb + 4 grp + e]
+    const float* rs = a.rstate + (bh * d.nC + c) * R;
+    f32x4 rv[NF] = {};
+    f32rows_x_frag<T, NF, D>(rv, rs, vf);  // (R v)[16 fb + 4 grp + e]
+    T* const t_rt = lds;                   // R^T, D rows of F (features pk-permuted)
     __syncthreads();
-    for (int e = tid; e < BF * BD; e += 256) {  // R^T, features pk-permuted
-      const int f = e >> 6, dd = e & 63;
-      t_q[SW::off(dd, pk_pos(f))] = TT::from_f(rs[e]);
+    for (int e = tid; e < F * D; e += 256) {
+      const int f = e / D, dd = e % D;
+      t_rt[Swz<T, F>::off(dd, pk_pos(f))] = TT::from_f(rs[e]);
     }
     __syncthreads();
     const float on = (kvalid && !selj) ? 1.f : 0.f;
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
+    for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dpk[fb][e] += on * (rv[fb][e] - rs[BF * BD + fb * 16 + 4 * grp + e]);
-    frag pm[2];
+      for (int e = 0; e < 4; ++e) dpk[fb][e] += on * (rv[fb][e] - rs[F * D + fb * 16 + 4 * grp + e]);
+    frag pm[F / 32];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int s2 = 0; s2 < F / 32; ++s2)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pm[ks][e] = TT::from_f(on * TT::to_f(phk[ks][e]));
+      for (int e = 0; e < 8; ++e) pm[s2][e] = TT::from_f(on * TT::to_f(phk[s2][e]));
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) TT::mma(dvt[db], SW::load8(t_q, db * 16 + r16, ks * 32 + grp * 8), pm[ks]);
+      for (int s2 = 0; s2 < F / 32; ++s2)
+        TT::mma(dvt[db], Swz<T, F>::load8(t_rt, db * 16 + r16, s2 * 32 + grp * 8), pm[s2]);
   }
   // selected keys: the later chunks' softmax part from the compact partials
   if (selj && kvalid) {
@@ -938,35 +937,36 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
     for (int r = 0; r < d.topk; ++r) rank += (sp[r] - 64 * c) < jr ? 1 : 0;
     const int n = c * d.topk + rank;
     for (int sidx = 0; sidx < a.nsplit; ++sidx) {
-      const float* p = a.dkvsel + ((static_cast<long long>(sidx) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * BD);
+      const float* p = a.dkvsel + ((static_cast<long long>(sidx) * d.B * d.Hkv + bh) * a.ntiles * 64 + n) * (2 * D);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < ND; ++db) {
         dkt[db] += *reinterpret_cast<const f32x4*>(p + db * 16 + 4 * grp);
-        dvt[db] += *reinterpret_cast<const f32x4*>(p + BD + db * 16 + 4 * grp);
+        dvt[db] += *reinterpret_cast<const f32x4*>(p + D + db * 16 + 4 * grp);
       }
     }
   }
   // NP-Map backward and dk, dv
-  NpRow nk;
-  np_forward<T>(nk, W, kf);
-  const float dr = np_backward(nk, dpk);  // dpk now holds dz
+  NpRow<F> nk;
+  np_forward<T, D, F>(nk, W, kf);
+  const float dr = np_backward<F>(nk, dpk);  // dpk now holds dz
   __syncthreads();
-  load_wt<T>(t_q, W);
+  T* const t_wt = lds;  // W^T, D rows of F
+  load_wt<T, D, F>(t_wt, W);
   __syncthreads();
-  f32x4 dxt[4] = {};
-  rows_x_acc<T>(dxt, t_q, dpk);
+  f32x4 dxt[ND] = {};
+  rows_x_acc<T, ND, F>(dxt, t_wt, dpk);
   if (kvalid) {
     T* dk = static_cast<T*>(a.dk) + koff;
     T* dv = static_cast<T*>(a.dv) + koff;
     const T* xk = static_cast<const T*>(a.k) + koff;
     const float xs = nk.r > 0.f ? dr / nk.r : 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < ND; ++db) {
       const typename TT::quad x4 = TT::load4(xk + db * 16 + 4 * grp);
       typename TT::quad o4, v4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o4[e] = TT::from_f(dkt[db][e] * 0.125f + dxt[db][e] + xs * TT::to_f(x4[e]));
+        o4[e] = TT::from_f(dkt[db][e] * isd + dxt[db][e] + xs * TT::to_f(x4[e]));
         v4[e] = TT::from_f(dvt[db][e]);
       }
       *reinterpret_cast<typename TT::quad*>(dk + db * 16 + 4 * grp) = o4;
@@ -975,29 +975,33 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   }
   // dW (k side) of the chunk: sum over its keys of dz k^T
   __syncthreads();
+  T* const t_dz = lds + 2 * SLOT;  // dz^T, F rows of 64 keys
+  T* const t_kt = lds + 4 * SLOT;  // K^T, D rows of 64 keys
   const int pj = pk_pos(jr);
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t_do[SW::off(fb * 16 + 4 * grp + e, pj)] = TT::from_f(kvalid ? dpk[fb][e] : 0.f);
-  tile_load<T>(t_qt, static_cast<const T*>(a.kt) + (bh * d.nC + c) * BD * 64, 64, 64);
+    for (int e = 0; e < 4; ++e) t_dz[SW::off(fb * 16 + 4 * grp + e, pj)] = TT::from_f(kvalid ? dpk[fb][e] : 0.f);
+  tile_load<T, 64, D>(t_kt, static_cast<const T*>(a.kt) + (bh * d.nC + c) * D * 64, 64, D);
   __syncthreads();
-  f32x4 acc[4];
-  tile_x_tile<T>(acc, t_do, t_qt);
-  float* wp = a.dwk + (bh * d.nC + c) * (BF * BD);
+  f32x4 acc[F / 64][D / 16];
+  tile_x_tile<T, F, D>(acc, t_dz, t_kt);
+  float* wp = a.dwk + (bh * d.nC + c) * (F * D);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int rb = 0; rb < F / 64; ++rb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wp[(wave * 16 + 4 * grp + e) * BD + cb * 16 + r16] = acc[cb][e];
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wp[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
 }
 
 // ---------------------------------------------------------------------------------------
 // dW = sum over batch, chunks and the group's query heads (q side) plus keys (k side):
 // gridDim.y slices of the item list, then a fixed-order sum of the slices.
 __global__ __launch_bounds__(256) void bwd_dw_part_kernel(const float* dwq, const float* dwk, float* part, int B,
-                                                          int Hkv, int G, int nC) {
+                                                          int Hkv, int G, int nC, int FD) {
   const int e = blockIdx.x * 256 + threadIdx.x;  // over Hkv * F * D
-  const int h = e / (BF * BD), fd = e % (BF * BD);
+  const int h = e / FD, fd = e % FD;
   const int nq = B * G * nC, nitems = nq + B * nC;
   const int per = (nitems + gridDim.y - 1) / gridDim.y;
   const int i0 = blockIdx.y * per, i1 = min(nitems, i0 + per);
@@ -1012,17 +1016,17 @@ __global__ __launch_bounds__(256) void bwd_dw_part_kernel(const float* dwq, cons
       if (it < i1) {
         if (it < nq) {
           const int b = it / (G * nC), g = (it / nC) % G, c = it % nC;
-          x[u] = dwq[((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * (BF * BD) + fd];
+          x[u] = dwq[((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * FD + fd];
         } else {
           const int it2 = it - nq, b = it2 / nC, c = it2 % nC;
-          x[u] = dwk[((static_cast<long long>(b) * Hkv + h) * nC + c) * (BF * BD) + fd];
+          x[u] = dwk[((static_cast<long long>(b) * Hkv + h) * nC + c) * FD + fd];
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc += x[u];
   }
-  part[static_cast<long long>(blockIdx.y) * Hkv * BF * BD + e] = acc;
+  part[static_cast<long long>(blockIdx.y) * Hkv * FD + e] = acc;
 }
 
 __global__ __launch_bounds__(256) void bwd_dw_sum_kernel(const float* part, float* dw, int n, int nparts) {
@@ -1034,58 +1038,65 @@ __global__ __launch_bounds__(256) void bwd_dw_sum_kernel(const float* part, floa
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D, int F>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   const Dims& d = a.d;
+  constexpr int R = F * D + F;
   hipError_t e;
   auto mark = [&](int k) { return ev ? hipEventRecord(ev[k], s) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
   if (a.ntiles > 0) {
-    const size_t tb = static_cast<size_t>(d.B) * d.Hkv * a.ntiles * 64 * BD * sizeof(T);
+    const size_t tb = static_cast<size_t>(d.B) * d.Hkv * a.ntiles * 64 * D * sizeof(T);
     if ((e = launch_fill_zero(a.kselt, tb, s)) != hipSuccess) return e;
     if ((e = launch_fill_zero(a.ksel, tb, s)) != hipSuccess) return e;
     if ((e = launch_fill_zero(a.vsel, tb, s)) != hipSuccess) return e;
   }
   const dim3 gk(d.nC, d.Hkv, d.B);
-  hipLaunchKernelGGL(bwd_kprep_kernel<T>, gk, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_kprep_kernel<T, D, F>), gk, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
-  const long long ne = static_cast<long long>(d.B) * d.Hkv * BR;
+  const long long ne = static_cast<long long>(d.B) * d.Hkv * R;
   const dim3 gs(static_cast<unsigned>((ne + 255) / 256));
-  hipLaunchKernelGGL(bwd_scan_fwd_kernel, gs, dim3(256), 0, s, a.ustate, d.nC, ne);
+  hipLaunchKernelGGL(bwd_scan_fwd_kernel, gs, dim3(256), 0, s, a.ustate, d.nC, R, ne);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  if (kDqHeads == 2 && sizeof(T) == 2 && d.G % 2 == 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 1>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, F>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   {
     const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;
     const long long nr = ne * nseg;
     const dim3 gr(static_cast<unsigned>((nr + 255) / 256));
-    hipLaunchKernelGGL(bwd_rev_seg_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, d.nC, d.G, d.Hkv, nseg, nr);
+    hipLaunchKernelGGL(bwd_rev_seg_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, d.nC, d.G, d.Hkv, nseg, R, nr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_rev_scan_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, a.rstate, d.nC, d.G, d.Hkv, nseg,
-                       nr);
+                       R, nr);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
   }
   if (a.ntiles > 0) {
-    hipLaunchKernelGGL(bwd_dkv_far_kernel<T>, dim3((a.ntiles + 1) / 2 * a.nsplit * d.B * d.Hkv), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkv_far_kernel<T, D>), dim3((a.ntiles + 1) / 2 * a.nsplit * d.B * d.Hkv), dim3(512), 0, s,
+                       a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(5)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_local_kernel<T>, gk, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkv_local_kernel<T, D, F>), gk, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
-  const int nw = d.Hkv * BF * BD;
+  const int nw = d.Hkv * F * D;
   hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 256, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
-                     d.Hkv, d.G, d.nC);
+                     d.Hkv, d.G, d.nC, F * D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((nw + 255) / 256), dim3(256), 0, s, a.dwpart, a.dw, nw, a.dw_parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(7);
 }
 
+bool bwd_shape_supported(int bf16, int D, int F) {
+  return (D == 64 && F == 64) || (bf16 && D == 128 && F == 128);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events) {
-  return a.d.bf16 ? launch_bwd_t<bf16>(a, s, events) : launch_bwd_t<float>(a, s, events);
+  const Dims& d = a.d;
+  if (d.bf16 && d.D == 64 && d.DF == 64) return launch_bwd_t<bf16, 64, 64>(a, s, events);
+  if (d.bf16 && d.D == 128 && d.DF == 128) return launch_bwd_t<bf16, 128, 128>(a, s, events);
+  if (!d.bf16 && d.D == 64 && d.DF == 64) return launch_bwd_t<float, 64, 64>(a, s, events);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace still

@@ -136,6 +136,8 @@ struct BwdArgs {
 
 // events: optional, 8 events recorded before each of the seven stages and after the last
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events);
+// (bf16, head_dim, feat_dim) triples the backward kernels are instantiated for
+bool bwd_shape_supported(int bf16, int D, int F);
 
 // Attention from far-future queries under full causal softmax (head_dim 64).
 struct MassArgs {

@@ -32,68 +32,77 @@ __device__ __forceinline__ typename Tr<T>::frag f32_frag(const float* p) {
   return pk_frag<T>(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4));
 }
 
-// 64 rows of 64 elements from memory (row stride `stride` elements) into a Swz<T, 64> LDS
+// ROWS rows of RL elements from memory (row stride `stride` elements) into a Swz<T, RL> LDS
 // tile; rows at or beyond nvalid are zero. All threads of the workgroup call.
-template <typename T>
+template <typename T, int RL = 64, int ROWS = 64>
 __device__ __forceinline__ void tile_load(T* lds, const T* g, long long stride, int nvalid) {
-  for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
-    const int row = idx >> 3, col = (idx & 7) * 8;
+  constexpr int PPR = RL / 8;  // 8-element pieces per row
+  for (int idx = threadIdx.x; idx < ROWS * PPR; idx += blockDim.x) {
+    const int row = idx / PPR, col = (idx % PPR) * 8;
     const typename Tr<T>::frag x = row < nvalid ? Tr<T>::load8(g + row * stride + col) : Tr<T>::zero();
-    Swz<T, 64>::store8(lds, row, col, x);
+    Swz<T, RL>::store8(lds, row, col, x);
   }
 }
 
-// acc[blk] = tile rows blk*16 + r16 (k = the 64 columns, straight) times the B fragments
-template <typename T>
-__device__ __forceinline__ void rows_x_frag(f32x4 (&acc)[4], const T* tile, const typename Tr<T>::frag (&bf)[2]) {
+// acc[blk] = rows blk*16 + r16 of a 64-row Swz<T, RL> tile (k = its RL columns, straight)
+// times the B fragments bf[RL / 32]
+template <typename T, int RL = 64>
+__device__ __forceinline__ void rows_x_frag(f32x4 (&acc)[4], const T* tile, const typename Tr<T>::frag (&bf)[RL / 32]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, ks * 32 + grp * 8), bf[ks]);
+    for (int ks = 0; ks < RL / 32; ++ks)
+      Tr<T>::mma(acc[blk], Swz<T, RL>::load8(tile, blk * 16 + r16, ks * 32 + grp * 8), bf[ks]);
   }
 }
 
-// acc[blk] += tile rows blk*16 + r16 (k = 64 pk-permuted positions) times the PK operand
-// built from the accumulators v[0..3] (rows 0..63 of a previous product)
-template <typename T>
-__device__ __forceinline__ void rows_x_acc(f32x4 (&acc)[4], const T* tile, const f32x4 (&v)[4]) {
+// acc[blk] += rows blk*16 + r16 of an NB*16-row Swz<T, NPOS> tile (k = its NPOS pk-permuted
+// positions) times the PK operands built from the accumulators v[NPOS / 16] (rows 0..NPOS-1
+// of a previous product)
+template <typename T, int NB = 4, int NPOS = 64>
+__device__ __forceinline__ void rows_x_acc(f32x4 (&acc)[NB], const T* tile, const f32x4 (&v)[NPOS / 16]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
-  const typename Tr<T>::frag b0 = pk_frag<T>(v[0], v[1]);
-  const typename Tr<T>::frag b1 = pk_frag<T>(v[2], v[3]);
+  typename Tr<T>::frag b[NPOS / 32];
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, grp * 8), b0);
-    Tr<T>::mma(acc[blk], Swz<T, 64>::load8(tile, blk * 16 + r16, 32 + grp * 8), b1);
-  }
+  for (int s2 = 0; s2 < NPOS / 32; ++s2) b[s2] = pk_frag<T>(v[2 * s2], v[2 * s2 + 1]);
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int s2 = 0; s2 < NPOS / 32; ++s2)
+      Tr<T>::mma(acc[blk], Swz<T, NPOS>::load8(tile, blk * 16 + r16, s2 * 32 + grp * 8), b[s2]);
 }
 
-// acc[blk] += rows blk*16 + r16 of a row-major fp32 [64][64] matrix in memory (k = the 64
-// columns, straight) times the B fragments
-template <typename T>
-__device__ __forceinline__ void f32rows_x_frag(f32x4 (&acc)[4], const float* m, const typename Tr<T>::frag (&bf)[2]) {
+// acc[blk] += rows blk*16 + r16 of a row-major fp32 [NB*16][KC] matrix in memory (k = its KC
+// columns, straight) times the B fragments bf[KC / 32]
+template <typename T, int NB = 4, int KC = 64>
+__device__ __forceinline__ void f32rows_x_frag(f32x4 (&acc)[NB], const float* m, const typename Tr<T>::frag (&bf)[KC / 32]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
+  for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Tr<T>::mma(acc[blk], f32_frag<T>(m + (blk * 16 + r16) * 64 + ks * 32 + grp * 8), bf[ks]);
+    for (int ks = 0; ks < KC / 32; ++ks)
+      Tr<T>::mma(acc[blk], f32_frag<T>(m + (blk * 16 + r16) * KC + ks * 32 + grp * 8), bf[ks]);
 }
 
-// One 64x64 output of a workgroup-wide product over 64 pk-permuted positions:
-// out[row][col] = sum_p A[row][p] B[col][p], A and B Swz<T, 64> tiles. Wave w computes rows
-// 16w..16w+15 (w = wave % 4); returns acc[cb][i] = out[16w + 4grp + i][16cb + r16].
-template <typename T>
-__device__ __forceinline__ void tile_x_tile(f32x4 (&acc)[4], const T* A, const T* B) {
+// An NR x NC output of a workgroup-wide product over 64 pk-permuted positions:
+// out[row][col] = sum_p A[row][p] B[col][p], A (NR rows) and B (NC rows) Swz<T, 64> tiles.
+// Wave w (w = wave % 4) computes the row blocks w + 4 rb; returns
+// acc[rb][cb][i] = out[16 (w + 4 rb) + 4 grp + i][16 cb + r16].
+template <typename T, int NR = 64, int NC = 64>
+__device__ __forceinline__ void tile_x_tile(f32x4 (&acc)[NR / 64][NC / 16], const T* A, const T* B) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4, wave = (threadIdx.x >> 6) & 3;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < NR / 64; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      Tr<T>::mma(acc[cb], Swz<T, 64>::load8(A, wave * 16 + r16, ks * 32 + grp * 8),
-                 Swz<T, 64>::load8(B, cb * 16 + r16, ks * 32 + grp * 8));
-  }
+    for (int cb = 0; cb < NC / 16; ++cb) {
+      acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        Tr<T>::mma(acc[rb][cb], Swz<T, 64>::load8(A, (wave + 4 * rb) * 16 + r16, ks * 32 + grp * 8),
+                   Swz<T, 64>::load8(B, cb * 16 + r16, ks * 32 + grp * 8));
+    }
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vector memory only, until at most n

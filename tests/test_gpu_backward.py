@@ -94,6 +94,32 @@ def test_backward_matches_oracle(case):
         assert e <= REL_TOL[dt], (nm, e)
 
 
+CASES_128 = [
+    # name, B, T, Hq, Hkv, w, k (bf16, head_dim = feat_dim = 128)
+    ("d128-gqa4-ragged", 1, 333, 8, 2, 64, 16),
+    ("d128-b2-window16", 2, 200, 4, 1, 16, 8),
+    ("d128-k64", 1, 190, 4, 1, 64, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES_128, ids=[c[0] for c in CASES_128])
+def test_backward_head_dim_128(case):
+    name, B, T, Hq, Hkv, w, k = case
+    _say(name)
+    wl, (q, kk, v, wp) = synth.small_case(seed=zlib.crc32(name.encode()) % 1000, B=B, T=T, Hq=Hq, Hkv=Hkv, D=128,
+                                           F=128, window=w, chunk=64, top_k=k, dtype="bf16", qk_scale=1.0,
+                                           n_planted=max(1, T // 50))
+    dout = synth.make_grad_out(wl)
+    out, idx, grads = _forward_backward(wl, q, kk, v, wp, dout)
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    ref = O.attend_backward(q, kk, v, wp, w, 64, sel, dout)
+    for nm, g, r in zip(("dq", "dk", "dv", "dw"), grads, ref):
+        assert np.all(np.isfinite(_np(g))), nm
+        e = _rel_err(_np(g), r)
+        _say(name, nm, "rel max err", e)
+        assert e <= REL_TOL["bf16"], (nm, e)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_backward_per_query_head_routing(dt):
     """Per-query-head routing: the gradients of K, V and W_h are the sums over each group of
@@ -179,5 +205,34 @@ def test_backward_long_sequence():
     want = dout.astype(np.float64).reshape(1, T, wl.n_kv_heads, G, wl.head_dim).sum(axis=(1, 3))
     e = float(np.abs(_np(dv).sum(axis=1) - want).max() / np.abs(want).max())
     _say("long sum of dv rel err", e)
+    assert e <= 1e-2
+    assert np.all(np.isfinite(_np(dw)))
+
+
+def test_backward_llama8b_shape():
+    """The Llama-3.1-8B-shaped layer (head_dim = feat_dim = 128, bf16), 8 sequences of 4096
+    tokens: the last two chunks' q, k and v gradients of the first and the last sequence
+    against the oracle (sequences are independent), and the value-gradient identity."""
+    wl = synth.L8B_4K
+    _say("backward 8B", wl.name)
+    q, k, v, wp = synth.make_inputs(wl)
+    dout = synth.make_grad_out(wl)
+    out, idx, (dq, dk, dv, dw) = _forward_backward(wl, q, k, v, wp, dout)
+    B, T, G = wl.batch, wl.seq_len, wl.n_q_heads // wl.n_kv_heads
+    t0 = T - 2 * wl.chunk
+    sel = _sel_from_idx(idx.cpu().numpy().astype(np.int64), T)
+    for b in (0, B - 1):
+        s_ = slice(b, b + 1)
+        ref = O.attend_backward(q[s_], k[s_], v[s_], wp, wl.window, wl.chunk, sel[s_], dout[s_], q_from=t0)
+        for nm, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            gn = _np(g[s_])
+            assert np.all(np.isfinite(gn)), nm
+            e = _rel_err(gn[:, t0:], r[:, t0:])
+            _say("8B sequence", b, nm, "rel max err over the last 128 rows", e)
+            assert e <= REL_TOL["bf16"], (nm, e)
+    assert np.all(np.isfinite(_np(dq))) and np.all(np.isfinite(_np(dk)))
+    want = dout.astype(np.float64).reshape(B, T, wl.n_kv_heads, G, wl.head_dim).sum(axis=(1, 3))
+    e = float(np.abs(_np(dv).sum(axis=1) - want).max() / np.abs(want).max())
+    _say("8B sum of dv rel err", e)
     assert e <= 1e-2
     assert np.all(np.isfinite(_np(dw)))
