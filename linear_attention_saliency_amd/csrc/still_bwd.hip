@@ -22,8 +22,8 @@
 // Launch order (one stream):
 //   bwd_kprep_kernel     per (chunk, KV head, batch): phi(k), K^T, U_c / u_c, compact rows
 //   bwd_scan_fwd_kernel  U_c -> S_c (sum over chunks <= c-2), in place
-//   bwd_dq_kernel        per (chunk, query head, batch): one pass over the keys gives dq and
-//                        L_i together (the softmax part against a running reference,
+//   bwd_dq_kernel        per (chunk, one or two query heads, batch): one pass over the keys
+//                        gives dq and L_i together (the softmax part against a running reference,
 //                        divided by the normaliser at the end), the per-chunk sums behind
 //                        R, the q side of dW
 //   bwd_rev_seg_kernel / bwd_rev_scan_kernel: R_c = sum over chunks >= c+2 and over the
@@ -56,15 +56,19 @@ struct NpRow {
   float r, inv_nm;
 };
 
-template <typename T, int D, int F>
+// W is [F][D] row-major in memory, or with TILE a Swz<T, D> LDS tile of F rows.
+template <typename T, int D, int F, bool TILE = false>
 __device__ __forceinline__ void np_forward(NpRow<F>& n, const T* W, const typename Tr<T>::frag (&xf)[D / 32]) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int fb = 0; fb < F / 16; ++fb) {
     n.z[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      Tr<T>::mma(n.z[fb], Tr<T>::load8(W + (fb * 16 + r16) * D + ks * 32 + grp * 8), xf[ks]);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const typename Tr<T>::frag wf = TILE ? Swz<T, D>::load8(W, fb * 16 + r16, ks * 32 + grp * 8)
+                                           : Tr<T>::load8(W + (fb * 16 + r16) * D + ks * 32 + grp * 8);
+      Tr<T>::mma(n.z[fb], wf, xf[ks]);
+    }
   }
   float nm2 = 0.f, xn2 = 0.f;
 #pragma unroll
@@ -111,11 +115,15 @@ __device__ __forceinline__ float np_backward(const NpRow<F>& n, f32x4 (&dphi)[F 
 }
 
 // W^T with the features pk-permuted, [dim][pk_pos(f)], into a Swz<T, F> LDS tile of D rows
+// (16-byte pieces of W's rows, a few in flight at a time)
 template <typename T, int D, int F>
 __device__ __forceinline__ void load_wt(T* lds, const T* W) {
-  for (int e = threadIdx.x; e < F * D; e += blockDim.x) {
-    const int f = e / D, dd = e % D;
-    lds[Swz<T, F>::off(dd, pk_pos(f))] = W[e];
+#pragma unroll 2
+  for (int e8 = threadIdx.x; e8 < F * D / 8; e8 += blockDim.x) {
+    const int f = e8 / (D / 8), dd = (e8 % (D / 8)) * 8, pf = pk_pos(f);
+    const typename Tr<T>::frag x = Tr<T>::load8(W + f * D + dd);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds[Swz<T, F>::off(dd + j, pf)] = x[j];
   }
 }
 
@@ -309,18 +317,22 @@ __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(const float* apart, c
 }
 
 // ---------------------------------------------------------------------------------------
-// One query head of one KV head per workgroup: four waves, 16 queries per wave.
-template <typename T, int D, int F>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a) {
+// QH query heads of one KV head per workgroup: four waves, 16 queries per wave, the wave
+// taking the same 16 rows of each of its QH heads, so that every K, V and K^T fragment it
+// reads from LDS serves QH products.
+template <typename T, int D, int F, int QH>
+__global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_kernel(BwdArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
   constexpr int ND = D / 16, NF = F / 16, R = F * D + F;
   constexpr int SLOT = (D > F ? D : F) * 64;  // elements per tile slot
-  // tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5; the
-  // near chunks use K, V, K^T, phi(K), phi(K)^T in slots 0-4; W^T takes slots 0-1 (D x F);
-  // the closing products use slots 2-5
+  // tile slots: the compact-key loops double-buffer (K, V, K^T) in slots 0-2 and 3-5; S_c
+  // takes slots 0-1 (F x D) after them; the near chunks use K, V, K^T, phi(K), phi(K)^T in
+  // slots 0-4; W^T takes slots 0-1 (D x F); the closing products use slots 2-5. W (F x D)
+  // stays in a region of its own for the NP-Map forward of every head.
   __shared__ __attribute__((aligned(16))) T lds[6 * SLOT];
+  __shared__ __attribute__((aligned(16))) T t_w[F * D];
   __shared__ float s_red[4][F];
   T* const t_k = lds;
   T* const t_v = lds + SLOT;
@@ -329,17 +341,17 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
   T* const t_pkt = lds + 4 * SLOT;
 
   const Dims& d = a.d;
-  // work index: chunk fastest, then query head, then batch (the heads of one KV head share
-  // its compact tiles). Divisions by run-time sizes leave the compiler unsure that these
-  // are uniform; telling it keeps the buffer descriptors in scalar registers.
+  // work index: chunk fastest, then the group of QH query heads, then batch (the heads of one
+  // KV head share its compact tiles). Divisions by run-time sizes leave the compiler unsure
+  // that these are uniform; telling it keeps the buffer descriptors in scalar registers.
+  const int nhg = d.Hq / QH;
   const int w = xcd_work(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const int c = __builtin_amdgcn_readfirstlane(w % d.nC);
-  const int hq = __builtin_amdgcn_readfirstlane((w / d.nC) % d.Hq);
-  const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * d.Hq));
-  const int h = hq / d.G;
+  const int hq0 = __builtin_amdgcn_readfirstlane((w / d.nC) % nhg) * QH;
+  const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * nhg));
+  const int h = hq0 / d.G;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
-  const long long bhq = static_cast<long long>(b) * d.Hq + hq;
   const int qrow = wave * 16 + r16;
   const long long i = 64LL * c + qrow;  // this lane column's query
   const bool qvalid = i < d.T;
@@ -347,19 +359,24 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
   const float scale2 = kLog2e * isd;
   const T* W = static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D;
 
-  // the query row, dout row and Delta = dout . out
-  const long long qoff = ((static_cast<long long>(b) * d.T + i) * d.Hq + hq) * D;
-  frag qf[D / 32], dof[D / 32];
-  float delta = 0.f;
+  // the query rows, dout rows and Delta = dout . out of each head (head g at qoff0 + g D)
+  const long long qoff0 = ((static_cast<long long>(b) * d.T + i) * d.Hq + hq0) * D;
+  frag qf[QH][D / 32], dof[QH][D / 32];
+  float delta[QH];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    qf[ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qoff + ks * 32 + grp * 8) : TT::zero();
-    dof[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
-    const frag of = qvalid ? TT::load8(static_cast<const T*>(a.out) + qoff + ks * 32 + grp * 8) : TT::zero();
+  for (int g = 0; g < QH; ++g) {
+    const long long qo = qoff0 + g * D;
+    delta[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) delta += TT::to_f(dof[ks][e]) * TT::to_f(of[e]);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qf[g][ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qo + ks * 32 + grp * 8) : TT::zero();
+      dof[g][ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qo + ks * 32 + grp * 8) : TT::zero();
+      const frag of = qvalid ? TT::load8(static_cast<const T*>(a.out) + qo + ks * 32 + grp * 8) : TT::zero();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) delta[g] += TT::to_f(dof[g][ks][e]) * TT::to_f(of[e]);
+    }
+    delta[g] = xor_sum_groups(delta[g]);
   }
-  delta = xor_sum_groups(delta);
 
   const uint64_t sel_prev = chunk_sel(a.sel_idx, bh, c - 1, d);
   const int nsel_c = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
@@ -369,51 +386,36 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
   const float* st = a.ustate + (bh * d.nC + c) * R;  // S_c, z_c
   const long long krs = static_cast<long long>(d.Hkv) * D;
 
-  // phi(q): kept as operand fragments through the key loops (the NP-Map forward is
-  // recomputed for its backward at the end, which keeps the loops' registers low)
-  frag phf[F / 32];
-  float dla = 0.f;  // the linear-attention part of the normaliser
-  {
-    NpRow<F> nq;
-    np_forward<T, D, F>(nq, W, qf);
-    f32x4 phq[NF];
-#pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
-#pragma unroll
-    for (int s2 = 0; s2 < F / 32; ++s2) phf[s2] = pk_frag<T>(phq[2 * s2], phq[2 * s2 + 1]);
-    if (c >= 2) {  // state part: phi(q) . z_c
-#pragma unroll
-      for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dla += phq[fb][e] * st[F * D + fb * 16 + 4 * grp + e];
-    }
-  }
-
   // ---- one pass over the keys. The softmax part of dq accumulates sum 2^{a - m} (dP - Delta) k
   // against a running reference m (log2 units; moved up only when a score passes it by more
   // than kLazy2, the accumulator rescaled then), the linear-attention part of dphi(q)
   // accumulates sum (dP - Delta) phi(k) unscaled, and both are divided by the normaliser
   // once it is known, at the end. Scores are raw q.k, the scale folded into the exponent's fma.
   constexpr float kLazy2 = 8.f;
-  float m2 = -kInf, l_lane = 0.f;  // this lane's share of the softmax part of the normaliser / 2^m
-  f32x4 dqt[ND] = {}, dpt[NF] = {};
-  auto rebase = [&](const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
+  float m2[QH], l_lane[QH];  // running reference; this lane's share of the softmax part / 2^m
+  f32x4 dqt[QH][ND];
+#pragma unroll
+  for (int g = 0; g < QH; ++g) {
+    m2[g] = -kInf;
+    l_lane[g] = 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dqt[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto rebase = [&](int g, const f32x4 (&sc)[4], const bool (&sa)[4][4], bool masked) {
     float tm = -kInf;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tm = (!masked || sa[kb][e]) ? fmaxf(tm, sc[kb][e]) : tm;
     tm = xor_max_groups(tm) * scale2;
-    const bool move = tm > m2 + kLazy2;  // the same in the four lanes of a query
+    const bool move = tm > m2[g] + kLazy2;  // the same in the four lanes of a query
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
-      const float mn = move ? tm : m2;
-      const float alpha = mn == m2 ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
-      l_lane *= alpha;
+      const float mn = move ? tm : m2[g];
+      const float alpha = mn == m2[g] ? 1.f : __builtin_amdgcn_exp2f(m2[g] - mn);
+      l_lane[g] *= alpha;
 #pragma unroll
-      for (int db = 0; db < ND; ++db) dqt[db] *= alpha;
-      m2 = mn;
+      for (int db = 0; db < ND; ++db) dqt[g][db] *= alpha;
+      m2[g] = mn;
     }
   };
   // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
@@ -437,6 +439,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
     dmr.issue(sl + SLOT, rs_v, t * 64 * D * ES);
     dmt.issue(sl + 2 * SLOT, rs_kt, t * D * 64 * ES);
   };
+  {  // W into its own region, ahead of the first compact tile (copies complete in order)
+    DmaTile<T, D, F, 4> dmw;
+    dmw.init(D);
+    dmw.issue(t_w, make_rsrc(W, static_cast<uint32_t>(F * D * ES)), 0);
+  }
   if (ntc > 0) issue3(0);
   for (int t = 0; t < ntc; ++t) {
     if (t + 1 < ntc) {
@@ -448,39 +455,101 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
     lds_sync();
     const int nv = min(64, nsel_c - t * 64);
     const T* const sl = lds + (t & 1) * 3 * SLOT;
-    f32x4 s[4], dp[4];
-    rows_x_frag<T, D>(s, sl, qf);
-    rows_x_frag<T, D>(dp, sl + SLOT, dof);
+    f32x4 s[QH][4], dp[QH][4];
+    rows_x_frags<T, D, QH>(s, sl, qf);
+    rows_x_frags<T, D, QH>(dp, sl + SLOT, dof);
     bool sa[4][4];
     if (nv == 64) {  // a full tile
-      rebase(s, sa, false);
-      float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int g = 0; g < QH; ++g) {
+        rebase(g, s[g], sa, false);
+        float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2));
-          ps += p;
-          s[kb][e] = p * (dp[kb][e] - delta);
-        }
-      l_lane += ps;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[g][kb][e], scale2, -m2[g]));
+            ps += p;
+            s[g][kb][e] = p * (dp[g][kb][e] - delta[g]);
+          }
+        l_lane[g] += ps;
+      }
     } else {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sa[kb][e] = kb * 16 + 4 * grp + e < nv;
-      rebase(s, sa, true);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int g = 0; g < QH; ++g) {
+        rebase(g, s[g], sa, true);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2)) : 0.f;
-          l_lane += p;
-          s[kb][e] = p * (dp[kb][e] - delta);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[g][kb][e], scale2, -m2[g])) : 0.f;
+            l_lane[g] += p;
+            s[g][kb][e] = p * (dp[g][kb][e] - delta[g]);
+          }
+      }
     }
-    rows_x_acc<T, ND>(dqt, sl + 2 * SLOT, s);
+    rows_x_accs<T, ND, 64, QH>(dqt, sl + 2 * SLOT, s);
     lds_sync();
+  }
+
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  lds_sync();  // W is in place, the compact tiles are no longer read
+
+  // dphi(q) starts with the state part S_c dout - Delta z_c (its factor e^{-L}, like that of
+  // the near chunks' part, is applied once L is known); S_c is staged in LDS in the operand
+  // dtype, which is the rounding its MFMA operands take, and serves every head
+  f32x4 dpt[QH][NF];
+#pragma unroll
+  for (int g = 0; g < QH; ++g)
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb) dpt[g][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c >= 2) {
+    T* const t_s = lds;  // F rows of D, slots 0-1
+    for (int e8 = tid; e8 < F * D / 8; e8 += 256) {
+      const int f = e8 / (D / 8), dd = (e8 % (D / 8)) * 8;
+      Swz<T, D>::store8(t_s, f, dd, f32_frag<T>(st + f * D + dd));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < F / 64; ++rb) {
+      f32x4 sdo[QH][4];
+      rows_x_frags<T, D, QH>(sdo, t_s + rb * 64 * D, dof);
+#pragma unroll
+      for (int g = 0; g < QH; ++g)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dpt[g][rb * 4 + blk][e] = sdo[g][blk][e] - delta[g] * st[F * D + (rb * 4 + blk) * 16 + 4 * grp + e];
+    }
+  }
+
+  // phi(q) of each head as operand fragments for the near chunks (the NP-Map forward is
+  // recomputed for its backward at the end, which keeps the loops' registers low)
+  frag phf[QH][F / 32];
+  float dla[QH];  // the linear-attention part of the normaliser
+#pragma unroll
+  for (int g = 0; g < QH; ++g) {
+    NpRow<F> nq;
+    np_forward<T, D, F, true>(nq, t_w, qf[g]);
+    f32x4 phq[NF];
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+#pragma unroll
+    for (int s2 = 0; s2 < F / 32; ++s2) phf[g][s2] = pk_frag<T>(phq[2 * s2], phq[2 * s2 + 1]);
+    dla[g] = 0.f;
+    if (c >= 2) {  // state part: phi(q) . z_c
+#pragma unroll
+      for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dla[g] += phq[fb][e] * st[F * D + fb * 16 + 4 * grp + e];
+    }
   }
   DmaR dkv;  // key and value rows of the input, row stride Hkv * D
   dkv.init(static_cast<int>(krs));
@@ -500,10 +569,6 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
     dmft.issue(t_pkt, make_rsrc(static_cast<const T*>(a.phikt) + (bh * d.nC + cc) * F * 64, F * 64 * ES), 0);
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_sync();
-    f32x4 s[4], dp[4], lw[4];
-    rows_x_frag<T, D>(s, t_k, qf);
-    rows_x_frag<T, D>(dp, t_v, dof);
-    rows_x_frag<T, F>(lw, t_pk, phf);
     bool sa[4][4], la[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -517,158 +582,177 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
         sa[kb][e] = vis && (inwin || sel);
         la[kb][e] = vis && !(inwin || sel);
       }
-    rebase(s, sa, true);
+    // the heads one after the other here (two chunks against the compact loop's many tiles;
+    // holding both heads' scores at once would not fit the registers at D = 128)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int g = 0; g < QH; ++g) {
+      f32x4 s[4], dp[4], lw[4];
+      rows_x_frag<T, D>(s, t_k, qf[g]);
+      rows_x_frag<T, D>(dp, t_v, dof[g]);
+      rows_x_frag<T, F>(lw, t_pk, phf[g]);
+      rebase(g, s, sa, true);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2)) : 0.f;
-        const float g = dp[kb][e] - delta;
-        l_lane += p;
-        dla += la[kb][e] ? lw[kb][e] : 0.f;
-        s[kb][e] = p * g;
-        lw[kb][e] = la[kb][e] ? g : 0.f;
-      }
-    rows_x_acc<T, ND>(dqt, t_kt, s);
-    rows_x_acc<T, NF>(dpt, t_pkt, lw);
-  }
-  const float l = xor_sum_groups(l_lane);
-  dla = xor_sum_groups(dla);
-  float L2;
-  if (!qvalid) {
-    L2 = kInf;
-  } else if (l > 0.f && dla > 0.f) {
-    const float ld = log2f(dla);
-    const float M = fmaxf(m2, ld);
-    L2 = M + log2f(l * exp2f(m2 - M) + exp2f(ld - M));
-  } else if (l > 0.f) {
-    L2 = m2 + log2f(l);
-  } else {
-    L2 = dla > 0.f ? log2f(dla) : kInf;  // an empty normaliser: out = 0, no gradient
-  }
-  const float einv = exp2f(-L2);
-  const float sa_scale = l > 0.f ? exp2f(m2 - L2) : 0.f;  // 2^m / normaliser
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-  for (int db = 0; db < ND; ++db) dqt[db] *= sa_scale;
-#pragma unroll
-  for (int fb = 0; fb < NF; ++fb) dpt[fb] *= einv;
-  if (c >= 2) {
-    // dphi(q) += e^{-L} (S_c dout - Delta z_c)
-    f32x4 sdo[NF] = {};
-    f32rows_x_frag<T, NF, D>(sdo, st, dof);
-#pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dpt[fb][e] += einv * (sdo[fb][e] - delta * st[F * D + fb * 16 + 4 * grp + e]);
-  }
-
-  // ---- NP-Map backward and dq
-  NpRow<F> nq;
-  np_forward<T, D, F>(nq, W, qf);
-  f32x4 phq[NF];
-#pragma unroll
-  for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
-  const float dr = np_backward<F>(nq, dpt);  // dpt now holds dz
-  __syncthreads();
-  T* const t_wt = lds;  // D x F, slots 0-1
-  load_wt<T, D, F>(t_wt, W);
-  __syncthreads();
-  f32x4 dxt[ND] = {};
-  rows_x_acc<T, ND, F>(dxt, t_wt, dpt);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
-  if (qvalid) {
-    T* dq = static_cast<T*>(a.dq) + qoff;
-    const T* xq = static_cast<const T*>(a.q) + qoff;
-    const float xs = nq.r > 0.f ? dr / nq.r : 0.f;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const typename TT::quad x4 = TT::load4(xq + db * 16 + 4 * grp);
-      typename TT::quad o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = TT::from_f(dqt[db][e] * isd + dxt[db][e] + xs * TT::to_f(x4[e]));
-      *reinterpret_cast<typename TT::quad*>(dq + db * 16 + 4 * grp) = o4;
+        for (int e = 0; e < 4; ++e) {
+          const float p = sa[kb][e] ? __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale2, -m2[g])) : 0.f;
+          const float gr = dp[kb][e] - delta[g];
+          l_lane[g] += p;
+          dla[g] += la[kb][e] ? lw[kb][e] : 0.f;
+          s[kb][e] = p * gr;
+          lw[kb][e] = la[kb][e] ? gr : 0.f;
+        }
+      rows_x_acc<T, ND>(dqt[g], t_kt, s);
+      rows_x_acc<T, NF>(dpt[g], t_pkt, lw);
+      __builtin_amdgcn_sched_barrier(0);  // keeps the heads' live ranges apart
     }
   }
 
-  // ---- what the key side needs: (L, Delta), phi(q) rows and transposed, q^T, dout^T
-  const long long qc = bhq * d.nC + c;
-  if (grp == 0) {
-    a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2] = L2;
-    a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta : 0.f;
-  }
-  // phi(q) rows and phi(q)^T are stored times e^{-L}, the factor every key-side use takes
-  T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * F;
-  {
-    f32x4 ps4[NF];
-#pragma unroll
-    for (int fb = 0; fb < NF; ++fb) ps4[fb] = phq[fb] * einv;
-#pragma unroll
-    for (int s2 = 0; s2 < F / 32; ++s2) TT::store8(phqr + 32 * s2 + 8 * grp, pk_frag<T>(ps4[2 * s2], ps4[2 * s2 + 1]));
-  }
-  T* phqt = static_cast<T*>(a.phiqt) + qc * F * 64;
-  T* qt = static_cast<T*>(a.qt) + qc * D * 64;
-  T* dot = static_cast<T*>(a.dot) + qc * D * 64;
-  const int pq = pk_pos(qrow);
+  // ---- per head: the normaliser, the NP-Map backward and dq, then what the key side needs:
+  // (L, Delta), phi(q) rows and transposed, q^T, dout^T, the per-chunk sums behind R and the
+  // q side of dW
+  __syncthreads();  // the near tiles are no longer read
+  T* const t_wt = lds;  // D x F, slots 0-1
+  load_wt<T, D, F>(t_wt, W);
+  __syncthreads();
   T* const e_phq = lds + 2 * SLOT;  // e^{-L} phi(q)^T, F rows
   T* const e_do = lds + 3 * SLOT;   // dout^T, D rows
   T* const e_dz = lds + 4 * SLOT;   // dz^T, F rows
   T* const e_q = lds + 5 * SLOT;    // q^T, D rows
-  __syncthreads();  // W^T is no longer read
+  const int pq = pk_pos(qrow);
 #pragma unroll
-  for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int f = fb * 16 + 4 * grp + e;
-      e_phq[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);
-      e_dz[SW::off(f, pq)] = TT::from_f(dpt[fb][e]);
+  for (int g = 0; g < QH; ++g) {
+    const int hq = hq0 + g;
+    const long long bhq = static_cast<long long>(b) * d.Hq + hq;
+    const long long qoff = qoff0 + g * D;
+    const float l = xor_sum_groups(l_lane[g]);
+    const float dl = xor_sum_groups(dla[g]);
+    float L2;
+    if (!qvalid) {
+      L2 = kInf;
+    } else if (l > 0.f && dl > 0.f) {
+      const float ld = log2f(dl);
+      const float M = fmaxf(m2[g], ld);
+      L2 = M + log2f(l * exp2f(m2[g] - M) + exp2f(ld - M));
+    } else if (l > 0.f) {
+      L2 = m2[g] + log2f(l);
+    } else {
+      L2 = dl > 0.f ? log2f(dl) : kInf;  // an empty normaliser: out = 0, no gradient
     }
+    const float einv = exp2f(-L2);
+    const float sa_scale = l > 0.f ? exp2f(m2[g] - L2) : 0.f;  // 2^m / normaliser
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+    for (int db = 0; db < ND; ++db) dqt[g][db] *= sa_scale;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dd = ks * 32 + grp * 8 + e;
-      e_do[SW::off(dd, pq)] = dof[ks][e];
-      e_q[SW::off(dd, pq)] = qf[ks][e];
+    for (int fb = 0; fb < NF; ++fb) dpt[g][fb] *= einv;
+
+    // the head's q and dout rows read again: the loops' copies end there, rather than living
+    // on (unpacked for the element stores below) through the loops
+    frag xq8[D / 32], do8[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      xq8[ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qoff + ks * 32 + grp * 8) : TT::zero();
+      do8[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
     }
-  // a_c partial: sum over the head's 64 queries of e^{-L} Delta phi(q)
+
+    // NP-Map backward and dq
+    NpRow<F> nq;
+    np_forward<T, D, F, true>(nq, t_w, xq8);
+    f32x4 phq[NF];
 #pragma unroll
-  for (int fb = 0; fb < NF; ++fb)
+    for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta : 0.f));
-      if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
+      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+    const float dr = np_backward<F>(nq, dpt[g]);  // dpt[g] now holds dz
+    f32x4 dxt[ND] = {};
+    rows_x_acc<T, ND, F>(dxt, t_wt, dpt[g]);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
+    if (qvalid) {
+      T* dq = static_cast<T*>(a.dq) + qoff;
+      const T* xq = static_cast<const T*>(a.q) + qoff;
+      const float xs = nq.r > 0.f ? dr / nq.r : 0.f;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const typename TT::quad x4 = TT::load4(xq + db * 16 + 4 * grp);
+        typename TT::quad o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = TT::from_f(dqt[g][db][e] * isd + dxt[db][e] + xs * TT::to_f(x4[e]));
+        *reinterpret_cast<typename TT::quad*>(dq + db * 16 + 4 * grp) = o4;
+      }
     }
-  __syncthreads();
-  // the transposed tiles to memory in 16-byte pieces
-  for (int idx = tid; idx < F * 8; idx += 256) {
-    const int row = idx >> 3, col = (idx & 7) * 8;
-    TT::store8(phqt + row * 64 + col, SW::load8(e_phq, row, col));
-  }
-  for (int idx = tid; idx < D * 8; idx += 256) {
-    const int row = idx >> 3, col = (idx & 7) * 8;
-    TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
-    TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
-  }
-  float* ap = a.apart + qc * R;
-  for (int f = tid; f < F; f += 256) ap[F * D + f] = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
-  {
-    f32x4 acc[F / 64][D / 16];
-    tile_x_tile<T, F, D>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
+
+    const long long qc = bhq * d.nC + c;
+    if (grp == 0) {
+      a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2] = L2;
+      a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta[g] : 0.f;
+    }
+    // phi(q) rows and phi(q)^T are stored times e^{-L}, the factor every key-side use takes
+    T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * F;
+    {
+      f32x4 ps4[NF];
 #pragma unroll
-    for (int rb = 0; rb < F / 64; ++rb)
+      for (int fb = 0; fb < NF; ++fb) ps4[fb] = phq[fb] * einv;
 #pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb)
+      for (int s2 = 0; s2 < F / 32; ++s2) TT::store8(phqr + 32 * s2 + 8 * grp, pk_frag<T>(ps4[2 * s2], ps4[2 * s2 + 1]));
+    }
+    T* phqt = static_cast<T*>(a.phiqt) + qc * F * 64;
+    T* qt = static_cast<T*>(a.qt) + qc * D * 64;
+    T* dot = static_cast<T*>(a.dot) + qc * D * 64;
+    if (g > 0) __syncthreads();  // the previous head's tiles and sums are no longer read
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ap[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
-    tile_x_tile<T, F, D>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
-    float* wp = a.dwq + qc * (F * D);
+    for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-    for (int rb = 0; rb < F / 64; ++rb)
+      for (int e = 0; e < 4; ++e) {
+        const int f = fb * 16 + 4 * grp + e;
+        e_phq[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);
+        e_dz[SW::off(f, pq)] = TT::from_f(dpt[g][fb][e]);
+      }
 #pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb)
+    for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wp[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+      for (int e = 0; e < 8; ++e) {
+        const int dd = ks * 32 + grp * 8 + e;
+        e_do[SW::off(dd, pq)] = do8[ks][e];
+        e_q[SW::off(dd, pq)] = xq8[ks][e];
+      }
+    // a_c partial: sum over the head's 64 queries of e^{-L} Delta phi(q)
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta[g] : 0.f));
+        if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
+      }
+    __syncthreads();
+    // the transposed tiles to memory in 16-byte pieces
+    for (int idx = tid; idx < F * 8; idx += 256) {
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      TT::store8(phqt + row * 64 + col, SW::load8(e_phq, row, col));
+    }
+    for (int idx = tid; idx < D * 8; idx += 256) {
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
+      TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
+    }
+    float* ap = a.apart + qc * R;
+    for (int f = tid; f < F; f += 256) ap[F * D + f] = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
+    {
+      f32x4 acc[F / 64][D / 16];
+      tile_x_tile<T, F, D>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
+#pragma unroll
+      for (int rb = 0; rb < F / 64; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ap[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+      tile_x_tile<T, F, D>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
+      float* wp = a.dwq + qc * (F * D);
+#pragma unroll
+      for (int rb = 0; rb < F / 64; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wp[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+    }
   }
 }
 
@@ -1058,7 +1142,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   const dim3 gs(static_cast<unsigned>((ne + 255) / 256));
   hipLaunchKernelGGL(bwd_scan_fwd_kernel, gs, dim3(256), 0, s, a.ustate, d.nC, R, ne);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, F>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
+  // two query heads per wave where the group splits evenly (bf16: the fp32 operands would
+  // double the registers)
+  bool two = false;
+  if constexpr (sizeof(T) == 2) {
+    two = d.G % 2 == 0;
+    if (two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(256), 0, s, a);
+  }
+  if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   {
     const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;

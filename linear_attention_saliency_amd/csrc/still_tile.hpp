@@ -74,6 +74,45 @@ __device__ __forceinline__ void rows_x_acc(f32x4 (&acc)[NB], const T* tile, cons
       Tr<T>::mma(acc[blk], Swz<T, NPOS>::load8(tile, blk * 16 + r16, s2 * 32 + grp * 8), b[s2]);
 }
 
+// rows_x_frag for NG sets of B fragments at once: acc[g][blk] = rows blk*16 + r16 of the tile
+// times bf[g]; every A fragment is read from LDS once and serves all NG sets
+template <typename T, int RL, int NG>
+__device__ __forceinline__ void rows_x_frags(f32x4 (&acc)[NG][4], const T* tile,
+                                             const typename Tr<T>::frag (&bf)[NG][RL / 32]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < RL / 32; ++ks) {
+      const typename Tr<T>::frag af = Swz<T, RL>::load8(tile, blk * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) Tr<T>::mma(acc[g][blk], af, bf[g][ks]);
+    }
+  }
+}
+
+// rows_x_acc for NG sets of accumulators at once: acc[g][blk] += rows blk*16 + r16 of the
+// tile times the PK operands built from v[g]; one LDS read of each A fragment serves all sets
+template <typename T, int NB, int NPOS, int NG>
+__device__ __forceinline__ void rows_x_accs(f32x4 (&acc)[NG][NB], const T* tile, const f32x4 (&v)[NG][NPOS / 16]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  typename Tr<T>::frag b[NG][NPOS / 32];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int s2 = 0; s2 < NPOS / 32; ++s2) b[g][s2] = pk_frag<T>(v[g][2 * s2], v[g][2 * s2 + 1]);
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int s2 = 0; s2 < NPOS / 32; ++s2) {
+      const typename Tr<T>::frag af = Swz<T, NPOS>::load8(tile, blk * 16 + r16, s2 * 32 + grp * 8);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) Tr<T>::mma(acc[g][blk], af, b[g][s2]);
+    }
+}
+
 // acc[blk] += rows blk*16 + r16 of a row-major fp32 [NB*16][KC] matrix in memory (k = its KC
 // columns, straight) times the B fragments bf[KC / 32]
 template <typename T, int NB = 4, int KC = 64>
