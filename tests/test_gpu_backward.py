@@ -70,6 +70,8 @@ CASES = [
     ("f32-window0-k0", 1, 170, 2, 1, 0, 0, "f32", 1.0),
     ("bf16-k64-full-softmax", 1, 200, 4, 1, 64, 64, "bf16", 1.0),
     ("bf16-g6", 1, 150, 6, 1, 64, 8, "bf16", 1.0),
+    ("bf16-g3-odd-group", 1, 210, 6, 2, 64, 8, "bf16", 1.0),
+    ("bf16-g8-b2", 2, 300, 16, 2, 64, 16, "bf16", 1.0),
     ("bf16-short", 1, 37, 4, 1, 64, 8, "bf16", 1.0),
     ("f32-one-token", 2, 1, 2, 1, 64, 8, "f32", None),
     ("f32-two-chunks", 1, 128, 2, 1, 64, 16, "f32", 1.0),
