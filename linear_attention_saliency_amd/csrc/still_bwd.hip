@@ -256,7 +256,8 @@ __global__ __launch_bounds__(256) void bwd_scan_fwd_kernel(float* ust, int nC, i
 }
 
 // R_c = sum over chunks >= c+2 of the group's per-chunk sums, as a segmented scan over
-// chunks: bwd_rev_seg_kernel sums each segment of kRevSeg chunks (and the group's heads),
+// chunks: bwd_rev_seg_kernel sums each segment of kRevSeg chunks (and the group's G records:
+// one per query head, or per pair of heads when dq runs two heads per wave),
 // bwd_rev_scan_kernel starts from the later segments' total and scans its own segment down.
 // One thread per (b, KV head, segment, element of R) in both.
 constexpr int kRevSeg = 16;
@@ -620,6 +621,10 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
   T* const e_dz = lds + 4 * SLOT;   // dz^T, F rows
   T* const e_q = lds + 5 * SLOT;    // q^T, D rows
   const int pq = pk_pos(qrow);
+  // the shares of R and of dW are kept per group of QH heads: the second head adds its share
+  // onto the first's (the same thread writes the same elements for both), so the reductions
+  // over the query heads read half as much
+  const long long gc = (static_cast<long long>(b) * nhg + hq0 / QH) * d.nC + c;
 #pragma unroll
   for (int g = 0; g < QH; ++g) {
     const int hq = hq0 + g;
@@ -733,8 +738,11 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
       TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
       TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
     }
-    float* ap = a.apart + qc * R;
-    for (int f = tid; f < F; f += 256) ap[F * D + f] = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
+    float* ap = a.apart + gc * R;
+    for (int f = tid; f < F; f += 256) {
+      const float v = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
+      ap[F * D + f] = g > 0 ? ap[F * D + f] + v : v;
+    }
     {
       f32x4 acc[F / 64][D / 16];
       tile_x_tile<T, F, D>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
@@ -743,15 +751,21 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ap[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+          for (int e = 0; e < 4; ++e) {
+            float* o = ap + ((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16;
+            *o = g > 0 ? *o + acc[rb][cb][e] : acc[rb][cb][e];
+          }
       tile_x_tile<T, F, D>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
-      float* wp = a.dwq + qc * (F * D);
+      float* wp = a.dwq + gc * (F * D);
 #pragma unroll
       for (int rb = 0; rb < F / 64; ++rb)
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wp[((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16] = acc[rb][cb][e];
+          for (int e = 0; e < 4; ++e) {
+            float* o = wp + ((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16;
+            *o = g > 0 ? *o + acc[rb][cb][e] : acc[rb][cb][e];
+          }
     }
   }
 }
@@ -1144,9 +1158,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   // two query heads per wave where the group splits evenly (bf16: the fp32 operands would
   // double the registers)
-  bool two = false;
+  const bool two = sizeof(T) == 2 && d.G % 2 == 0;
+  const int Gp = two ? d.G / 2 : d.G;  // records of R and dW shares per KV head and chunk
   if constexpr (sizeof(T) == 2) {
-    two = d.G % 2 == 0;
     if (two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(256), 0, s, a);
   }
   if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
@@ -1155,9 +1169,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
     const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;
     const long long nr = ne * nseg;
     const dim3 gr(static_cast<unsigned>((nr + 255) / 256));
-    hipLaunchKernelGGL(bwd_rev_seg_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, d.nC, d.G, d.Hkv, nseg, R, nr);
+    hipLaunchKernelGGL(bwd_rev_seg_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, d.nC, Gp, d.Hkv, nseg, R, nr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_rev_scan_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, a.rstate, d.nC, d.G, d.Hkv, nseg,
+    hipLaunchKernelGGL(bwd_rev_scan_kernel, gr, dim3(256), 0, s, a.apart, a.segsum, a.rstate, d.nC, Gp, d.Hkv, nseg,
                        R, nr);
     if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
   }
@@ -1171,7 +1185,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
   const int nw = d.Hkv * F * D;
   hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 256, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
-                     d.Hkv, d.G, d.nC, F * D);
+                     d.Hkv, Gp, d.nC, F * D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((nw + 255) / 256), dim3(256), 0, s, a.dwpart, a.dw, nw, a.dw_parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
