@@ -250,10 +250,12 @@ BwdLayout bwd_layout(const still_config* c) {
   L.phiq = take(bhq * nC * 64 * F * es);
   L.phiqt = take(bhq * nC * 64 * F * es);
   L.ld = take(bhq * nC * 64 * 2 * 4);
-  L.apart = take(bhq * nC * R * 4);
+  // the shares of R and dW: one record per group of query heads that a dq wave takes
+  const size_t bgq = bhq / static_cast<size_t>(still::bwd_heads_per_wave(c->dtype == STILL_BF16, d.G));
+  L.apart = take(bgq * nC * R * 4);
   L.rstate = take(bh * nC * R * 4);
   L.segsum = take(bh * ((nC + 15) / 16) * R * 4);
-  L.dwq = take(bhq * nC * F * D * 4);
+  L.dwq = take(bgq * nC * F * D * 4);
   L.dwk = take(bh * nC * F * D * 4);
   L.dkvsel = take(static_cast<size_t>(L.nsplit) * bh * L.ntiles * 64 * 2 * D * 4);
   L.dwpart = take(static_cast<size_t>(L.dw_parts) * d.Hkv * F * D * 4);

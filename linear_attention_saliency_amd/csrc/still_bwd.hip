@@ -1158,7 +1158,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   // two query heads per wave where the group splits evenly (bf16: the fp32 operands would
   // double the registers)
-  const bool two = sizeof(T) == 2 && d.G % 2 == 0;
+  const bool two = bwd_heads_per_wave(sizeof(T) == 2, d.G) == 2;
   const int Gp = two ? d.G / 2 : d.G;  // records of R and dW shares per KV head and chunk
   if constexpr (sizeof(T) == 2) {
     if (two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(256), 0, s, a);
@@ -1191,6 +1191,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(7);
 }
+
+int bwd_heads_per_wave(int bf16, int G) { return bf16 && G % 2 == 0 ? 2 : 1; }
 
 bool bwd_shape_supported(int bf16, int D, int F) {
   return (D == 64 && F == 64) || (bf16 && D == 128 && F == 128);

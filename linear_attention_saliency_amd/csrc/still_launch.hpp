@@ -138,6 +138,9 @@ struct BwdArgs {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t* events);
 // (bf16, head_dim, feat_dim) triples the backward kernels are instantiated for
 bool bwd_shape_supported(int bf16, int D, int F);
+// Query heads per wave in the backward's dq kernel (1 or 2); its shares of R and dW are kept
+// per group of that many heads of a KV head.
+int bwd_heads_per_wave(int bf16, int G);
 
 // Attention from far-future queries under full causal softmax (head_dim 64).
 struct MassArgs {
