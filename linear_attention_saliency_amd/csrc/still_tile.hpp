@@ -1,5 +1,7 @@
-// 64 x 64 tile helpers shared by the backward and the attention-mass kernels (gfx950,
-// wave64, 16x16x32 MFMA with the operand conventions of still_common.hpp).
+// Tile helpers shared by the backward and the attention-mass kernels (gfx950, wave64,
+// 16x16x32 MFMA with the operand conventions of still_common.hpp): 64-row tiles whose row
+// length (head or feature width) is a template parameter, products that read each LDS
+// fragment once for several operand sets, and the copy-wait and barrier primitives.
 #pragma once
 
 #include "still_common.hpp"
