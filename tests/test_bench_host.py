@@ -83,3 +83,30 @@ def test_traffic_needs_the_same_workload_and_source(tmp_path):
     p.write_text("hbm_bytes_per_launch: 12345\nworkload: wl-a\nsource_sha1: 0000\n")
     assert bench.measured_traffic("wl-a", str(p)) is None
     assert bench.measured_traffic("wl-a", str(tmp_path / "missing.txt")) is None
+
+
+def test_counter_summary_names_and_shares(tmp_path):
+    from linear_attention_saliency_amd import profile_summary as PS
+
+    assert PS._short_name("_ZN5still13bwd_dq_kernelIDF16bLi128ELi128ELi2EEEvNS_7BwdArgsE") == "bwd_dq_kernel<bf16,128,128,2>"
+    assert PS._short_name("_ZN5still11scan_kernelIDF16bLi32EEEvPviiiPKfPfii") == "scan_kernel<bf16,32>"
+    assert PS._short_name("_ZN5still11attn_kernelIfLi64ELi64ELi4EEEvNS_8AttnArgsE") == "attn_kernel<f32,64,64,4>"
+    assert PS._short_name("still::bwd_dw_sum_kernel(float const*, float*, int, int)") == "bwd_dw_sum_kernel"
+    # one kernel over two passes: 4 waves, 16 VALU and 8 MFMA instructions in all; 102400 MFMA
+    # busy cycles summed over the SIMDs against 1024 SIMDs x 8000 / 8 active cycles is 10%
+    k = "_ZN5still11attn_kernelIDF16bLi64ELi64ELi4EEEvNS_8AttnArgsE"
+    hdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    (tmp_path / "p1").mkdir()
+    (tmp_path / "p2").mkdir()
+    (tmp_path / "p1" / "run_counter_collection.csv").write_text(
+        hdr + f"1,{k},SQ_WAVES,4\n1,{k},SQ_VALU_MFMA_BUSY_CYCLES,102400\n1,{k},SQ_WAVE_CYCLES,1000\n1,{k},SQ_WAIT_ANY,250\n")
+    (tmp_path / "p2" / "run_counter_collection.csv").write_text(
+        hdr + f"1,{k},SQ_INSTS_VALU,16\n1,{k},SQ_INSTS_MFMA,8\n1,{k},GRBM_GUI_ACTIVE,8000\n")
+    rows = PS.counters([str(tmp_path / "p1"), str(tmp_path / "p2")]).splitlines()
+    assert len(rows) == 3
+    cells = [c.strip() for c in rows[2].strip("|").split("|")]
+    assert cells[0] == "attn_kernel<bf16,64,64,4>"
+    assert cells[2].startswith("4 / 2 / ")  # per wave
+    assert cells[3] == "2.0"                 # VALU per MFMA
+    assert cells[4] == "10.0%"               # 102400 / (1024 SIMDs * 8000 / 8)
+    assert cells[6] == "25% of wave time"
