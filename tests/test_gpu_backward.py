@@ -72,6 +72,9 @@ CASES = [
     ("bf16-g6", 1, 150, 6, 1, 64, 8, "bf16", 1.0),
     ("bf16-g3-odd-group", 1, 210, 6, 2, 64, 8, "bf16", 1.0),
     ("bf16-g8-b2", 2, 300, 16, 2, 64, 16, "bf16", 1.0),
+    ("bf16-w33-k3", 1, 290, 4, 1, 33, 3, "bf16", 1.0),
+    ("bf16-k63", 1, 330, 4, 2, 64, 63, "bf16", 1.0),
+    ("f32-k1", 1, 300, 2, 1, 64, 1, "f32", 1.0),
     ("bf16-short", 1, 37, 4, 1, 64, 8, "bf16", 1.0),
     ("f32-one-token", 2, 1, 2, 1, 64, 8, "f32", None),
     ("f32-two-chunks", 1, 128, 2, 1, 64, 16, "f32", 1.0),

@@ -80,6 +80,8 @@ PREFILL_THEN_DECODE = [
     ("bf16-g6", 1, 64, 200, 6, 1, 64, 64, 64, 8, "bf16", 1.0),
     ("bf16-d64-f128-from-1", 2, 1, 141, 4, 2, 64, 128, 64, 4, "bf16", None),
     ("bf16-d128-f64-k64", 1, 190, 330, 4, 1, 128, 64, 64, 64, "bf16", 1.0),
+    ("bf16-w33-k3", 1, 100, 300, 4, 1, 64, 64, 33, 3, "bf16", 1.0),
+    ("bf16-d128-k63", 1, 120, 280, 4, 2, 128, 128, 64, 63, "bf16", 1.0),
     # routed by the diagonal logit instead of the Self-Saliency Score
     ("bf16-diag-score", 2, 100, 270, 4, 1, 64, 64, 64, 8, "bf16", 1.0, "diag"),
     ("bf16-d128-diag-score", 1, 64, 200, 4, 2, 128, 128, 64, 16, "bf16", None, "diag"),

@@ -88,6 +88,10 @@ CASES = [
     ("bf16-one-token", 2, 1, 4, 2, 64, 64, 64, 8, "bf16", None),
     ("f32-window-only-k0", 1, 200, 1, 1, 64, 64, 64, 0, "f32", 1.0),
     ("bf16-full-softmax", 1, 256, 4, 1, 64, 64, 64, 64, "bf16", 1.0),
+    # top-k values whose compact rows straddle the 64-row tiles at odd offsets, an odd window
+    ("bf16-k1", 1, 300, 4, 1, 64, 64, 64, 1, "bf16", 1.0),
+    ("bf16-d128-k63", 1, 330, 4, 2, 128, 128, 64, 63, "bf16", 1.0),
+    ("bf16-w33-k3", 2, 290, 4, 1, 64, 64, 33, 3, "bf16", 1.0),
 ]
 
 
