@@ -229,7 +229,10 @@ BwdLayout bwd_layout(const still_config* c) {
   BwdLayout L;
   L.ntiles = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
   const int64_t far_wgs = static_cast<int64_t>(L.ntiles) * d.B * d.Hkv;
-  L.nsplit = far_wgs > 0 ? static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, (2048 + far_wgs - 1) / far_wgs))) : 1;
+  // query slices per row group of the selected-key kernel: about 4096 workgroups in all, so
+  // that the long row groups (the early compact rows see every later chunk) are split up,
+  // and at most 16 partials for the local-key kernel to add
+  L.nsplit = far_wgs > 0 ? static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, (4096 + far_wgs - 1) / far_wgs))) : 1;
   const int64_t items = static_cast<int64_t>(d.B) * (d.G + 1) * d.nC;
   L.dw_parts = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, items / 16)));
   size_t off = 0;
