@@ -67,6 +67,13 @@ Dims dims_of(const still_config* c) {
 
 size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4; }
 
+// Compact tiles per (b, KV head), rounded up to an odd count. The tiles of all (b, KV head)
+// pairs sit at this stride, and the workgroups of different pairs read the same tile index
+// at about the same time; with an even count (a power of two at the usual sizes) those
+// reads meet in the same HBM channels. Measured on the 32 x 64K decode: 258 tiles per pair
+// read the compact rows 34% slower than 257.
+inline int64_t odd_tiles(int64_t n) { return n > 0 ? (n | 1) : 0; }
+
 struct WsLayout {
   size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, tilemax, total;
   int ntiles_sel;
@@ -85,7 +92,7 @@ WsLayout ws_layout(const still_config* c) {
   };
   L.sal = take(bh * d.T * sizeof(float));
   L.selmask = take(bh * d.nC * sizeof(uint64_t));
-  L.ntiles_sel = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
+  L.ntiles_sel = static_cast<int>(odd_tiles((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64));
   L.ksel = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vselT = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vT = take(bh * d.nC * 64 * d.D * es);
@@ -111,7 +118,7 @@ CacheLayout cache_layout(const still_config* c, int64_t max_tokens) {
   const size_t es = elem_bytes(c);
   const size_t D = c->head_dim, F = c->feat_dim;
   CacheLayout L;
-  L.sel_capacity = ((max_tokens / 64) * c->top_k + 63) / 64 * 64;
+  L.sel_capacity = odd_tiles(((max_tokens / 64) * c->top_k + 63) / 64) * 64;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
