@@ -234,7 +234,9 @@ BwdLayout bwd_layout(const still_config* c) {
   const size_t bh = static_cast<size_t>(d.B) * d.Hkv, bhq = static_cast<size_t>(d.B) * d.Hq;
   const size_t es = elem_bytes(c), nC = d.nC, D = d.D, F = d.DF, R = d.R;
   BwdLayout L;
-  L.ntiles = static_cast<int>((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64);
+  // compact tiles per (b, KV head), odd like the prefill's (the padding tile's row group of
+  // the selected-key kernel starts past the last chunk and does no steps)
+  L.ntiles = static_cast<int>(odd_tiles((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64));
   const int64_t far_wgs = static_cast<int64_t>(L.ntiles) * d.B * d.Hkv;
   // query slices per row group of the selected-key kernel: about 4096 workgroups in all, so
   // that the long row groups (the early compact rows see every later chunk) are split up,
