@@ -40,9 +40,11 @@
  *   - The library never allocates device memory and never synchronises: all work is
  *     enqueued on `stream`, so results are ready when the stream reaches them.
  *   - Validation errors are returned before anything is enqueued, and no output is
- *     touched. STILL_ERR_HIP means a launch failed; outputs are then undefined.
- *   - There is no global state: calls on distinct streams with distinct workspaces and
- *     caches may run concurrently. Calls sharing a workspace or cache must be ordered.
+ *     touched. STILL_ERR_HIP means a HIP call or launch failed; outputs are then undefined,
+ *     and still_last_hip_error() names the hipError_t.
+ *   - There is no shared mutable state (only the per-thread record of the last HIP error):
+ *     calls on distinct streams with distinct workspaces and caches may run concurrently.
+ *     Calls sharing a workspace or cache must be ordered.
  */
 #ifndef STILL_H
 #define STILL_H
@@ -132,7 +134,7 @@ typedef struct still_cache {
   int64_t n_tokens;     /* tokens held per sequence = position of the next token */
   int64_t sel_capacity; /* compact rows per (batch, KV head), a multiple of 64 */
   void* sel_k;          /* [batch, n_kv_heads, sel_capacity, head_dim] dtype: the selected key
-                           rows times log2(e)/sqrt(head_dim), rounded to dtype */
+                           rows as given */
   void* sel_v;          /* [batch, n_kv_heads, sel_capacity / 64, head_dim, 64] dtype */
   void* ring_k;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
   void* ring_v;         /* [batch, n_kv_heads, 2, chunk, head_dim] dtype */
@@ -145,6 +147,11 @@ typedef struct still_cache {
 /* Human-readable name of a status code (static storage). */
 const char* still_status_string(int status);
 
+/* The hipError_t (as an int) of the HIP call or launch behind the last STILL_ERR_HIP that any
+ * entry point returned on the calling thread; 0 (hipSuccess) if none has. Not cleared by
+ * later successful calls. */
+int still_last_hip_error(void);
+
 /* Bytes of scratch still_prefill needs for `cfg` (0 if cfg is invalid). */
 size_t still_prefill_workspace_bytes(const still_config* cfg);
 
@@ -153,10 +160,14 @@ size_t still_prefill_workspace_bytes(const still_config* cfg);
  *   k, v   [batch, seq_len, n_kv_heads, head_dim]  dtype   (post-RoPE keys/values)
  *   w_phi  [n_kv_heads, feat_dim, head_dim]        dtype   (NP-Map weight per KV head)
  *   out    [batch, seq_len, n_q_heads, head_dim]   dtype   (written, RNE for bf16)
- *   routing_in    optional [batch, n_kv_heads, seq_len/chunk, top_k] int32: if non-null,
- *                 these ascending, distinct in-chunk positions replace the saliency
- *                 selection (an override for testing the attention alone; entries outside
- *                 their chunk are ignored, which leaves that slot's softmax row undefined).
+ *   routing_in    optional HOST memory, [batch, n_kv_heads, seq_len/chunk, top_k] int32
+ *                 ([batch, n_q_heads, ...] with per-query-head routing): if non-null, these
+ *                 positions replace the score's selection (an override for testing the
+ *                 attention alone). Every chunk c's top_k entries must be strictly ascending
+ *                 and lie in [64 c, 64 c + 63]; otherwise STILL_ERR_INVALID_ARG, before
+ *                 anything is enqueued. The array is read during the call and copied into the
+ *                 workspace on `stream` (from pageable memory that copy may wait for the
+ *                 stream's earlier work); it is not retained.
  *   saliency_out  optional [batch, n_kv_heads, seq_len] fp32: the group-summed saliency
  *                 (requires window >= 1).
  *   sel_idx_out   optional [batch, n_kv_heads, seq_len/chunk, top_k] int32: the selected
@@ -237,9 +248,11 @@ size_t still_backward_workspace_bytes(const still_config* cfg);
  *   out      [batch, seq_len, n_q_heads, head_dim] dtype: the forward output for these inputs
  *            and this routing (it gives Delta_i = dout_i . out_i)
  *   dout     [batch, seq_len, n_q_heads, head_dim] dtype
- *   sel_idx  [batch, n_kv_heads, seq_len/chunk, top_k] int32, ascending positions inside their
- *            chunk, as still_prefill's sel_idx_out writes them (may be null if top_k = 0 or
- *            seq_len < chunk)
+ *   sel_idx  [batch, n_kv_heads, seq_len/chunk, top_k] int32 device memory: for every complete
+ *            chunk, top_k distinct positions inside that chunk, in any order, as still_prefill's
+ *            sel_idx_out writes them (may be null if top_k = 0 or seq_len < chunk). The entries
+ *            are not checked (they live on the device); repeated or out-of-chunk entries give
+ *            undefined gradients.
  *   dq       like q; dk, dv like k (dtype, written)
  *   dw_phi   [n_kv_heads, feat_dim, head_dim] fp32 (written, not accumulated)
  *   workspace  device scratch of at least still_backward_workspace_bytes(cfg) bytes.

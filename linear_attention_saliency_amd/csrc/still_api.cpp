@@ -12,6 +12,21 @@ using still::Dims;
 
 namespace {
 
+// The hipError_t behind the last STILL_ERR_HIP this thread returned (hipSuccess if none).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+int fail_hip(hipError_t e) {
+  t_last_hip = e;
+  return STILL_ERR_HIP;
+}
+
+// evaluate a HIP call or launch; on failure keep its error and return STILL_ERR_HIP
+#define STILL_HIP(expr)                          \
+  do {                                           \
+    const hipError_t still_e_ = (expr);          \
+    if (still_e_ != hipSuccess) return fail_hip(still_e_); \
+  } while (0)
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -75,7 +90,7 @@ size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4
 inline int64_t odd_tiles(int64_t n) { return n > 0 ? (n | 1) : 0; }
 
 struct WsLayout {
-  size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, tilemax, total;
+  size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, tilemax, routing, total;
   int ntiles_sel;
 };
 
@@ -100,8 +115,25 @@ WsLayout ws_layout(const still_config* c) {
   L.states = take(bh * d.nC * d.R * (d.bf16 ? 2 : 4));
   L.kmaxc = take(bh * d.nC * sizeof(float));
   L.tilemax = take(bh * (L.ntiles_sel > 0 ? L.ntiles_sel : 1) * sizeof(float));
+  L.routing = take(bh * d.nCc * d.topk * sizeof(int32_t));  // a copy of routing_in, if given
   L.total = off;
   return L;
+}
+
+// routing_in (host memory): for every (b, selecting head, complete chunk c), top_k positions
+// strictly ascending inside [64 c, 64 c + 63]
+bool routing_valid(const still_config* c, const int32_t* r) {
+  const int64_t heads = c->routing_scope == STILL_ROUTE_PER_QUERY_HEAD ? c->n_q_heads : c->n_kv_heads;
+  const int64_t nCc = c->seq_len / 64, k = c->top_k;
+  for (int64_t rec = 0; rec < static_cast<int64_t>(c->batch) * heads * nCc; ++rec) {
+    const int64_t lo = (rec % nCc) * 64;
+    const int32_t* e = r + rec * k;
+    for (int64_t i = 0; i < k; ++i) {
+      if (e[i] < lo || e[i] > lo + 63) return false;
+      if (i > 0 && e[i] <= e[i - 1]) return false;
+    }
+  }
+  return true;
 }
 
 constexpr int kMaxDecodeGroup = 16;  // query heads per KV head the decode kernels handle
@@ -324,6 +356,8 @@ const char* still_status_string(int status) {
   }
 }
 
+int still_last_hip_error(void) { return static_cast<int>(t_last_hip); }
+
 size_t still_prefill_workspace_bytes(const still_config* cfg) {
   if (check_cfg(cfg, true) != STILL_OK) return 0;
   if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
@@ -348,6 +382,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
                         static_cast<const void*>(sel_idx_out)})
     if (p && !aligned(p, 4)) return STILL_ERR_INVALID_ARG;
   if (saliency_out && cfg->window < 1) return STILL_ERR_INVALID_ARG;
+  if (routing_in && cfg->top_k > 0 && !routing_valid(cfg, routing_in)) return STILL_ERR_INVALID_ARG;
   if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
     if (cache) return STILL_ERR_UNSUPPORTED;
     const still_config e = expanded_cfg(cfg);
@@ -356,7 +391,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
     const ExpLayout X = exp_layout(cfg);
     if (ws_bytes < X.total + ws_layout(&e).total) return STILL_ERR_WORKSPACE_TOO_SMALL;
     char* ws = static_cast<char*>(workspace);
-    if (expand_kvw(cfg, k, v, w_phi, ws, X, stream) != hipSuccess) return STILL_ERR_HIP;
+    STILL_HIP(expand_kvw(cfg, k, v, w_phi, ws, X, stream));
     return still_prefill_timed(&e, q, ws + X.ek, ws + X.ev, ws + X.ew, out, routing_in, saliency_out,
                                sel_idx_out, nullptr, ws + X.total, ws_bytes - X.total, stream, events);
   }
@@ -376,7 +411,13 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.k = k;
   pa.v = v;
   pa.w = w_phi;
-  pa.routing_in = cfg->top_k > 0 ? routing_in : nullptr;
+  pa.routing_in = nullptr;
+  if (routing_in && cfg->top_k > 0 && d.nCc > 0) {  // validated above; the prep kernel reads a device copy
+    pa.routing_in = reinterpret_cast<const int32_t*>(ws + L.routing);
+    STILL_HIP(hipMemcpyAsync(ws + L.routing, routing_in,
+                             static_cast<size_t>(d.B) * d.Hkv * d.nCc * d.topk * sizeof(int32_t),
+                             hipMemcpyHostToDevice, stream));
+  }
   pa.sal = saliency_out ? saliency_out : reinterpret_cast<float*>(ws + L.sal);
   pa.selmask = reinterpret_cast<uint64_t*>(ws + L.selmask);
   pa.sel_idx = sel_idx_out;
@@ -392,12 +433,12 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
     pa.vselT = cache->sel_v;
     pa.ntiles_sel = static_cast<int>(cache->sel_capacity / 64);
   }
-  if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
-  if (still::launch_prep(pa, stream) != hipSuccess) return STILL_ERR_HIP;
-  if (events && hipEventRecord(events[1], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (events) STILL_HIP(hipEventRecord(events[0], stream));
+  STILL_HIP(still::launch_prep(pa, stream));
+  if (events) STILL_HIP(hipEventRecord(events[1], stream));
   float* tilemax = reinterpret_cast<float*>(ws + L.tilemax);
-  if (still::launch_scan(d, pa.states, pa.kmaxc, tilemax, L.ntiles_sel, stream) != hipSuccess) return STILL_ERR_HIP;
-  if (events && hipEventRecord(events[2], stream) != hipSuccess) return STILL_ERR_HIP;
+  STILL_HIP(still::launch_scan(d, pa.states, pa.kmaxc, tilemax, L.ntiles_sel, stream));
+  if (events) STILL_HIP(hipEventRecord(events[2], stream));
 
   still::AttnArgs aa;
   aa.d = d;
@@ -416,8 +457,8 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.tm_stride = L.ntiles_sel;
   aa.nw = d.G >= 4 ? 4 : (d.G == 3 ? 4 : d.G);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
-  if (still::launch_attn(aa, stream) != hipSuccess) return STILL_ERR_HIP;
-  if (events && hipEventRecord(events[3], stream) != hipSuccess) return STILL_ERR_HIP;
+  STILL_HIP(still::launch_attn(aa, stream));
+  if (events) STILL_HIP(hipEventRecord(events[3], stream));
   if (cache) {
     still::ExportArgs ea;
     ea.d = d;
@@ -427,7 +468,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
     ea.selmask = pa.selmask;
     ea.states = pa.states;
     ea.c = view_of(cache);
-    if (still::launch_cache_export(ea, stream) != hipSuccess) return STILL_ERR_HIP;
+    STILL_HIP(still::launch_cache_export(ea, stream));
     cache->n_tokens = cfg->seq_len;
   }
   return STILL_OK;
@@ -447,7 +488,8 @@ int still_select_topk(const still_config* cfg, const float* saliency, int32_t* s
   if (st != STILL_OK) return st;
   if (!saliency || !sel_idx_out || !aligned(saliency, 4) || !aligned(sel_idx_out, 4)) return STILL_ERR_INVALID_ARG;
   const Dims d = dims_of(cfg);
-  return still::launch_topk(d, saliency, sel_idx_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+  STILL_HIP(still::launch_topk(d, saliency, sel_idx_out, stream));
+  return STILL_OK;
 }
 
 int still_feature_map(const still_config* cfg, const void* x, const void* w_phi, float* phi_out,
@@ -457,7 +499,8 @@ int still_feature_map(const still_config* cfg, const void* x, const void* w_phi,
   if (!x || !w_phi || !phi_out || !aligned(x, 16) || !aligned(w_phi, 16) || !aligned(phi_out, 4))
     return STILL_ERR_INVALID_ARG;
   const Dims d = dims_of(cfg);
-  return still::launch_feature_map(d, x, w_phi, phi_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+  STILL_HIP(still::launch_feature_map(d, x, w_phi, phi_out, stream));
+  return STILL_OK;
 }
 
 size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens) {
@@ -488,7 +531,7 @@ int still_cache_init(const still_config* cfg, int64_t max_tokens, void* dev_buf,
   c.state_z = reinterpret_cast<float*>(base + L.state_z);
   c.sel_mask = reinterpret_cast<uint64_t*>(base + L.sel_mask);
   c.cur_saliency = reinterpret_cast<float*>(base + L.cur_sal);
-  if (still::launch_fill_zero(dev_buf, L.total, stream) != hipSuccess) return STILL_ERR_HIP;
+  STILL_HIP(still::launch_fill_zero(dev_buf, L.total, stream));
   *out = c;
   return STILL_OK;
 }
@@ -498,22 +541,23 @@ size_t still_decode_workspace_bytes(const still_config* cfg, int64_t max_tokens)
   return decode_ws_bytes(cfg);
 }
 
-int still_decode_step_timed(const still_config* cfg, still_cache* cache, const void* q, const void* k,
-                            const void* v, const void* w_phi, void* out, void* workspace,
-                            size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+}  // extern "C"
+
+namespace {
+
+// Checks of one decode step and its split plan (everything but the scratch of the partials).
+int decode_plan(const still_config* cfg, const still_cache* cache, const void* q, const void* k, const void* v,
+                const void* w_phi, void* out, still::DecodeArgs& a) {
   const int st = check_cfg(cfg, false);
   if (st != STILL_OK) return st;
-  if (!cache || !q || !k || !v || !w_phi || !out || !workspace) return STILL_ERR_INVALID_ARG;
-  for (const void* p : {q, k, v, w_phi, static_cast<const void*>(out), static_cast<const void*>(workspace)})
+  if (!cache || !q || !k || !v || !w_phi || !out) return STILL_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, w_phi, static_cast<const void*>(out)})
     if (!aligned(p, 16)) return STILL_ERR_INVALID_ARG;
   if (!same_layer(&cache->cfg, cfg)) return STILL_ERR_CACHE_MISMATCH;
   if (cfg->n_q_heads / cfg->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
   if (cache->n_tokens < 0 || cache->n_tokens >= cache->max_tokens) return STILL_ERR_CACHE_FULL;
-  if (ws_bytes < decode_ws_bytes(cfg)) return STILL_ERR_WORKSPACE_TOO_SMALL;
-
   still_config c1 = *cfg;
   c1.seq_len = 1;
-  still::DecodeArgs a;
   a.d = dims_of(&c1);
   a.pos = cache->n_tokens;
   const int64_t chunk = cache->n_tokens / 64;
@@ -533,13 +577,28 @@ int still_decode_step_timed(const still_config* cfg, still_cache* cache, const v
   a.v = v;
   a.w = w_phi;
   a.out = out;
-  const size_t recs = static_cast<size_t>(bhn) * kMaxSplit * a.d.G;
+  a.c = view_of(cache);
+  return STILL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int still_decode_step_timed(const still_config* cfg, still_cache* cache, const void* q, const void* k,
+                            const void* v, const void* w_phi, void* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  still::DecodeArgs a;
+  const int st = decode_plan(cfg, cache, q, k, v, w_phi, out, a);
+  if (st != STILL_OK) return st;
+  if (!workspace || !aligned(workspace, 16)) return STILL_ERR_INVALID_ARG;
+  if (ws_bytes < decode_ws_bytes(cfg)) return STILL_ERR_WORKSPACE_TOO_SMALL;
+  const size_t recs = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * kMaxSplit * a.d.G;
   a.part_ml = static_cast<float*>(workspace);
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(recs * 2 * sizeof(float)));
-  a.c = view_of(cache);
-  if (events && hipEventRecord(events[0], stream) != hipSuccess) return STILL_ERR_HIP;
-  if (still::launch_decode(a, stream, events ? events[1] : nullptr) != hipSuccess) return STILL_ERR_HIP;
-  if (events && hipEventRecord(events[2], stream) != hipSuccess) return STILL_ERR_HIP;
+  if (events) STILL_HIP(hipEventRecord(events[0], stream));
+  STILL_HIP(still::launch_decode(a, stream, events ? events[1] : nullptr));
+  if (events) STILL_HIP(hipEventRecord(events[2], stream));
   cache->n_tokens += 1;
   return STILL_OK;
 }
@@ -604,7 +663,7 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
     const ExpBwdLayout X = exp_bwd_layout(cfg);
     if (ws_bytes < X.total + bwd_layout(&e).total) return STILL_ERR_WORKSPACE_TOO_SMALL;
     char* ws = static_cast<char*>(workspace);
-    if (expand_kvw(cfg, k, v, w_phi, ws, X.x, stream) != hipSuccess) return STILL_ERR_HIP;
+    STILL_HIP(expand_kvw(cfg, k, v, w_phi, ws, X.x, stream));
     const int rc = still_backward_timed(&e, q, ws + X.x.ek, ws + X.x.ev, ws + X.x.ew, out, dout, sel_idx, dq, ws + X.dk,
                                         ws + X.dv, reinterpret_cast<float*>(ws + X.dw), ws + X.total,
                                         ws_bytes - X.total, stream, events);
@@ -612,11 +671,10 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
     const long long rows = static_cast<long long>(cfg->batch) * cfg->seq_len;
     const int G = cfg->n_q_heads / cfg->n_kv_heads;
     const int es = cfg->dtype == STILL_BF16 ? 2 : 4;
-    if (still::launch_reduce_heads(ws + X.dk, dk, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream) != hipSuccess ||
-        still::launch_reduce_heads(ws + X.dv, dv, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream) != hipSuccess ||
-        still::launch_reduce_heads(ws + X.dw, dw_phi, 1, cfg->n_kv_heads, G, cfg->feat_dim * cfg->head_dim, 4,
-                                   stream) != hipSuccess)
-      return STILL_ERR_HIP;
+    STILL_HIP(still::launch_reduce_heads(ws + X.dk, dk, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream));
+    STILL_HIP(still::launch_reduce_heads(ws + X.dv, dv, rows, cfg->n_kv_heads, G, cfg->head_dim, es, stream));
+    STILL_HIP(still::launch_reduce_heads(ws + X.dw, dw_phi, 1, cfg->n_kv_heads, G, cfg->feat_dim * cfg->head_dim, 4,
+                                         stream));
     return STILL_OK;
   }
   const BwdLayout L = bwd_layout(cfg);
@@ -657,7 +715,8 @@ int still_backward_timed(const still_config* cfg, const void* q, const void* k, 
   a.ntiles = L.ntiles;
   a.nsplit = L.nsplit;
   a.dw_parts = L.dw_parts;
-  return still::launch_bwd(a, stream, events) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+  STILL_HIP(still::launch_bwd(a, stream, events));
+  return STILL_OK;
 }
 
 int still_backward(const still_config* cfg, const void* q, const void* k, const void* v, const void* w_phi,
@@ -691,7 +750,8 @@ int still_future_attention_mass(const still_config* cfg, const void* q, const vo
   a.mass = mass_out;
   a.nsplit = L.nsplit;
   a.per = L.per;
-  return still::launch_mass(a, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+  STILL_HIP(still::launch_mass(a, stream));
+  return STILL_OK;
 }
 
 int still_selection_overlap(const still_config* cfg, const int32_t* sel_a, const int32_t* sel_b,
@@ -702,7 +762,8 @@ int still_selection_overlap(const still_config* cfg, const int32_t* sel_a, const
   if (d.nCc == 0 || d.topk == 0) return STILL_OK;
   if (!sel_a || !sel_b || !common_out || !aligned(sel_a, 4) || !aligned(sel_b, 4) || !aligned(common_out, 4))
     return STILL_ERR_INVALID_ARG;
-  return still::launch_overlap(d, sel_a, sel_b, common_out, stream) == hipSuccess ? STILL_OK : STILL_ERR_HIP;
+  STILL_HIP(still::launch_overlap(d, sel_a, sel_b, common_out, stream));
+  return STILL_OK;
 }
 
 }  // extern "C"

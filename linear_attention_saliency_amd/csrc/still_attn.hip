@@ -21,7 +21,11 @@
 // shared-normaliser output  (sum_SA e^a v + N) / (sum_SA e^a + D)  needs no offset and
 // cannot overflow whatever the magnitudes.
 // Phase 2 (softmax): the two window tiles (masked), then the compact tiles, 64 keys per
-// tile, in a four-stage LDS pipeline whose copies run straight from memory into LDS. The
+// tile, in a four-stage LDS pipeline whose copies run straight from memory into LDS. Every
+// score is the exact fp32 sum of bf16 products of the stored q and k; the logit scale
+// log2(e)/sqrt(D) and the running max enter in fp32, in the fma that feeds the exp (a key
+// pre-multiplied by the scale and rounded to bf16 would carry a logit error growing with
+// the logit, 2^-9 of it per element). The
 // running max is refreshed only when a tile's max exceeds it by more than kLazy = 32 (log2
 // units): P and the accumulators keep fp32's exponent range (bf16 has it too), so terms up
 // to 2^32 stay exact in relative terms and every sum stays finite. A per-tile bound
@@ -156,87 +160,6 @@ __device__ __forceinline__ void sm_exp_pv(const f32x4 (&s)[4][QB], const T* lv, 
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pf[qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[2 * hs + e / 4][qb][e % 4] * c1 - mq[qb]));
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) TT::mma(o[D / 16][qb], one, pf[qb]);
-  }
-}
-
-// Compact tiles: their K rows carry the factor log2(e)/sqrt(D), and the K Q^T product
-// starts from the accumulator value -m (the running max of each query column), so the
-// scores leave the MFMA as s = a_ij log2(e) - m and P = 2^s needs no VALU before the exp.
-template <typename T, int D, int QB>
-__device__ __forceinline__ void qk_tile_shifted(const T* lk, const typename Tr<T>::frag (&qf)[QB][D / 32],
-                                                const f32x4 (&mneg)[QB], f32x4 (&s)[4][QB]) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mneg[qb];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const typename Tr<T>::frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) Tr<T>::mma(s[kb][qb], ka, qf[qb][ks]);
-    }
-  }
-}
-
-// Running-max update for shifted scores: a column moves only if its tile max exceeds kLazy
-// (2^kLazy is the largest P the accumulators then see); the accumulators are rescaled, the
-// tile's scores and the column's -m re-based. Rare after the first tiles.
-template <int D, int QB>
-__device__ __forceinline__ void sm_max_shifted(f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB],
-                                               f32x4 (&mneg)[QB]) {
-  bool need_any = false;
-  float dm[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float tm = -kInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tm = fmaxf(tm, s[kb][qb][i]);
-    tm = xor_max_groups(tm);
-    const bool need = tm > kLazy;
-    dm[qb] = need ? tm : 0.f;
-    need_any |= need;
-  }
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float alpha = __builtin_amdgcn_exp2f(-dm[qb]);
-      m_run[qb] += dm[qb];
-      mneg[qb] -= dm[qb];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb][qb] -= dm[qb];
-#pragma unroll
-      for (int db = 0; db <= D / 16; ++db) o[db][qb] *= alpha;
-    }
-  }
-}
-
-// P = 2^s (shifted scores), then O^T += V^T P^T as in sm_exp_pv.
-template <typename T, int D, int QB>
-__device__ __forceinline__ void sm_exp_pv_shifted(const f32x4 (&s)[4][QB], const T* lv, f32x4 (&o)[D / 16 + 1][QB]) {
-  using TT = Tr<T>;
-  using frag = typename TT::frag;
-  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
-  frag one;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) one[e] = TT::from_f(1.0f);
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    frag pf[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[2 * hs + e / 4][qb][e % 4]));
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
@@ -542,13 +465,15 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
   // compact tile t -> LDS stage (asynchronous); K rows [64][D] and V^T rows [D][64] of a
-  // tile are contiguous, so one resource per buffer covers every tile of this (b, h)
+  // tile are contiguous, so one resource per buffer covers the nt_comp tiles this chunk
+  // reads (bounded by the sequence's own compact rows, so the 32-bit range holds whatever
+  // the capacity of a decode cache the rows are written into)
   DmaTile<T, D, 64, NW> dk;
   DmaTile<T, 64, D, NW> dv;
   dk.init(D);
   dv.init(64);
-  const auto krs = make_rsrc(kb_ptr, static_cast<uint32_t>(a.ntiles_sel) * C::KT * static_cast<int>(sizeof(T)));
-  const auto vrs = make_rsrc(vb_ptr, static_cast<uint32_t>(a.ntiles_sel) * C::VT * static_cast<int>(sizeof(T)));
+  const auto krs = make_rsrc(kb_ptr, static_cast<uint32_t>(nt_comp) * C::KT * static_cast<int>(sizeof(T)));
+  const auto vrs = make_rsrc(vb_ptr, static_cast<uint32_t>(nt_comp) * C::VT * static_cast<int>(sizeof(T)));
   auto issue = [&](int t, int stage) {
     T* st = L + C::stage_off(stage);
     dk.issue(st, krs, t * C::KT * static_cast<int>(sizeof(T)));
@@ -838,9 +763,6 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   //     ragged tile are copied too (they lie inside the buffer; their scores are masked and
   //     their V^T columns are zero or finite).
   if (nt_comp > 0) {
-    f32x4 mneg[QB];  // -m per query column, the starting accumulator of K Q^T
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mneg[qb] = f32x4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
     // Tiles whose key-norm bound might move the running max, one bit each: the max can only
     // move if some query's |q| max|k| exceeds it by more than kLazy. Decided here for all
     // tiles at once, conservatively (the wave's largest |q| against its smallest running max,
@@ -863,7 +785,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    qk_tile_shifted<T, D, QB>(L + C::stage_off(0), qf, mneg, sa);  // tile 0 has landed
+    qk_tile<T, D, QB>(L + C::stage_off(0), qf, sa);  // tile 0 has landed
     __syncthreads();
 #pragma unroll
     for (int t = 1; t < 4; ++t)
@@ -885,9 +807,9 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       }
       const int tj = t >> 6;
       const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-      if ((fw >> (t & 63)) & 1ull) sm_max_shifted<D, QB>(s_cur, o, m_run, mneg);
-      qk_tile_shifted<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, mneg, s_next);  // after the last tile: unused
-      sm_exp_pv_shifted<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o);
+      if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(s_cur, o, m_run, c1);
+      qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, s_next);  // after the last tile: unused
+      sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o, m_run, c1);
     };
     for (int t = 0; t < nt_comp; t += 2) {
       step(t, sa, sb);

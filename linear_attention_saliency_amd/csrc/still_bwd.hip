@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T t_vt[D * 64];
   __shared__ float m2part[4 * 64];
   __shared__ float xn2[64];
+  __shared__ int selpos[64];  // position of the chunk's selected key of each rank
   const Dims& d = a.d;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
@@ -166,6 +167,7 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   tile_load<T, D>(t_k, static_cast<const T*>(a.k) + row0 * D, rs, nvalid);
   tile_load<T, D>(t_v, static_cast<const T*>(a.v) + row0 * D, rs, nvalid);
   const uint64_t selm = chunk_sel(a.sel_idx, bh, c, d);
+  if (tid < 64 && ((selm >> tid) & 1ull)) selpos[__popcll(selm & ((1ull << tid) - 1ull))] = tid;
   typename TT::frag wf[FPW][D / 32];
   np_map_load_w<T, D, F>(static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D, wf);
   __syncthreads();
@@ -210,16 +212,17 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
     for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(ust + f * D + db * 16 + 4 * grp) = u[db];
     if (grp == 0) ust[F * D + f] = zs;
   }
-  // the selected rows, in chunk order, into the compact buffers
+  // the selected rows, in position order (compact row c * top_k + rank, as the local-key
+  // kernel looks them up), into the compact buffers
   if (c < d.nCc && d.topk > 0) {
-    const int32_t* sp = a.sel_idx + (bh * d.nCc + c) * d.topk;
+    const int nsel = __popcll(selm);
     T* ks = static_cast<T*>(a.ksel) + bh * a.ntiles * 64 * D;
     T* vs = static_cast<T*>(a.vsel) + bh * a.ntiles * 64 * D;
     T* kst = static_cast<T*>(a.kselt) + bh * a.ntiles * (D * 64);
     for (int e = tid; e < d.topk * D; e += 256) {
       const int r = e / D, dd = e % D;
-      const int pos = sp[r] - 64 * c;
-      const bool ok = pos >= 0 && pos < 64;
+      const bool ok = r < nsel;
+      const int pos = ok ? selpos[r] : 0;
       const T kv = ok ? t_k[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
       const T vv = ok ? t_v[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
       const int n = c * d.topk + r;

@@ -25,7 +25,7 @@ struct PrepArgs {
   float* sal;                 // [B,Hkv,T]
   uint64_t* selmask;          // [B,Hkv,nC]
   int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
-  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows times log2(e)/sqrt(D)
+  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows (the selected keys)
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
   void* states;               // [B,Hkv,nC,R] in the layer's dtype: S^T [D][DF] with features permuted by
                               // pk_pos, then z [DF] permuted

@@ -9,8 +9,8 @@
 //   3. NP-Map of the chunk's keys ([P1] section "Norm-Preserved Feature Map（NP-Map）");
 //   4. top-k routing of a complete chunk, ascending positions, and the gather of the
 //      selected K/V rows into the compact softmax cache ([P1] section
-//      "Chunk-Wise并行+延迟选择"); the K rows are stored pre-multiplied by
-//      log2(e)/sqrt(D), so their products with q are logits in log2 units;
+//      "Chunk-Wise并行+延迟选择"), stored as they are (the consumers scale the
+//      fp32 scores);
 //   5. the chunk's linear-attention contribution U_c = sum over its unselected keys of
 //      phi(k) v^T and u_c = sum phi(k) ([P3] on the fixed-size state of linear attention).
 // scan_kernel then turns the U_c into inclusive prefix sums over chunks.
@@ -162,9 +162,7 @@ void prep_kernel(PrepArgs a) {
           (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
       if (slot < nsel) kx = SW::load8(band, 64 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 64..127
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kx[e] = TT::from_f(TT::to_f(kx[e]) * scale);  // logits in log2 units
-      TT::store8(ks_ + dst, kx);
+      TT::store8(ks_ + dst, kx);  // raw rows: the logit scale is applied to the fp32 scores
     }
   }
 

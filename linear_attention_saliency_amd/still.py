@@ -25,13 +25,17 @@ EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefil
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
            "still_decode_step", "still_decode_step_timed", "still_backward_workspace_bytes", "still_backward",
            "still_backward_timed", "still_future_attention_mass_workspace_bytes", "still_future_attention_mass",
-           "still_selection_overlap")
+           "still_selection_overlap", "still_last_hip_error")
 
 
 class StillError(RuntimeError):
-    def __init__(self, code: int, what: str = ""):
-        super().__init__(f"{what}: status {code} ({STATUS.get(code, 'unknown')})")
+    def __init__(self, code: int, what: str = "", hip_error: int = 0):
+        msg = f"{what}: status {code} ({STATUS.get(code, 'unknown')})"
+        if hip_error:
+            msg += f", hipError_t {hip_error}"
+        super().__init__(msg)
         self.code = code
+        self.hip_error = hip_error
 
 
 class Config(ctypes.Structure):
@@ -96,6 +100,8 @@ def load():
     lib.still_future_attention_mass.restype = I
     lib.still_selection_overlap.argtypes = [CP, P, P, P, V]
     lib.still_selection_overlap.restype = I
+    lib.still_last_hip_error.argtypes = []
+    lib.still_last_hip_error.restype = I
     _lib = lib
     return lib
 
@@ -122,7 +128,18 @@ def _stream(stream=None):
 
 def _check(rc: int, what: str):
     if rc != 0:
-        raise StillError(rc, what)
+        raise StillError(rc, what, load().still_last_hip_error() if rc == -6 else 0)
+
+
+def _host_i32(t):
+    """A C-contiguous int32 host copy of a tensor or array (kept alive by the caller)."""
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        t = t.detach().to("cpu", torch.int32).numpy()
+    import numpy as np
+
+    return np.ascontiguousarray(t, dtype=np.int32)
 
 
 def _tensor_cfg(q, k, w_phi, window, chunk, top_k, score="saliency", scope="kv_head"):
@@ -153,12 +170,16 @@ class Prefill:
     def __call__(self, q, k, v, w_phi, out, *, routing=None, saliency=None, sel_idx=None, cache=None,
                  stream=None, events=None):
         """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4).
-        cache: optional DecodeCache with no tokens; it is left holding the sequence."""
+        cache: optional DecodeCache with no tokens; it is left holding the sequence.
+        routing: optional selection override (host or device tensor, or array), passed to the
+        library as host memory."""
         for t in (q, k, v, w_phi, out):
             if not (t.is_cuda and t.is_contiguous()):
                 raise ValueError("tensors must be contiguous device tensors")
+        r = _host_i32(routing)
+        rptr = None if r is None else ctypes.c_void_p(r.ctypes.data)
         rc = load().still_prefill_timed(ctypes.byref(self.cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w_phi),
-                                        _ptr(out), _ptr(routing), _ptr(saliency), _ptr(sel_idx),
+                                        _ptr(out), rptr, _ptr(saliency), _ptr(sel_idx),
                                         None if cache is None else ctypes.byref(cache.c),
                                         _ptr(self.workspace), self.workspace.numel(), _stream(stream),
                                         events)
@@ -172,7 +193,8 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
     """One STILL layer over whole sequences.
 
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
-    GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection.
+    GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection (ascending
+    positions inside each chunk; anything else raises StillError with status -1).
     cache: optional empty DecodeCache, left ready to decode token T.
     score: "saliency" (the Self-Saliency Score) or "diag" (the diagonal logit alone).
     scope: "kv_head" (each KV head selects for its group) or "query_head" (each query head
@@ -186,8 +208,6 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
     out = torch.empty_like(q)
     sal = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device) if return_saliency else None
     sel = torch.empty((B, Hkv, T // chunk, top_k), dtype=torch.int32, device=q.device) if return_routing else None
-    if routing is not None:
-        routing = routing.to(device=q.device, dtype=torch.int32).contiguous()
     call(q, k, v, w_phi, out, routing=routing, saliency=sal, sel_idx=sel, cache=cache)
     res = [out]
     if return_saliency:
