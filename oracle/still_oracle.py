@@ -422,7 +422,7 @@ def _np_map_t(x, w):
     return torch.linalg.vector_norm(x, dim=-1, keepdim=True) * m / torch.linalg.vector_norm(m, dim=-1, keepdim=True)
 
 
-def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: int = 0):
+def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: int = 0, rows=None):
     """Gradients of sum(out * dout) with respect to q, k, v and w_phi, for a fixed routing.
 
     The routing sel [B,Hkv,T] (bool) is an input: it is piecewise constant in q and k, so
@@ -434,6 +434,9 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: 
     j only the rows i >= j, so the gradients of q rows and of k, v rows at positions >= q_from
     are then the full ones (the others are partial): a long sequence can be checked at its
     tail for the cost of its last rows.
+    rows: alternatively, the query positions (distinct) whose rows enter the sum, in place of
+    q_from. Where dout is zero on every other row, these are the whole loss, and every
+    gradient returned (dq, dk, dv and dw_phi at every position) is the full one.
     Returns (dq, dk, dv, dw_phi) as fp64 arrays shaped like q, k, v and w_phi.
     """
     import torch
@@ -443,7 +446,13 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: 
     B, T, Hq, D = qt.shape
     G = _check_group(Hq, kt.shape[2])
     sel = torch.tensor(np.asarray(sel, dtype=bool))
-    i = torch.arange(q_from, T)[:, None]
+    if rows is None:
+        ridx = torch.arange(q_from, T)
+    else:
+        ridx = torch.tensor(np.asarray(rows, dtype=np.int64).reshape(-1))
+        if ridx.numel() and (int(ridx.min()) < 0 or int(ridx.max()) >= T or ridx.unique().numel() != ridx.numel()):
+            raise ValueError("rows must be distinct positions in [0, seq_len)")
+    i = ridx[:, None]
     j = torch.arange(T)[None, :]
     causal = j <= i
     in_window = j > i - window
@@ -454,7 +463,7 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: 
             h = hq // G
             sa = causal & (in_window | (earlier_chunk & sel[b, h][None, :]))
             la = causal & ~sa
-            qq, kk, vv = qt[b, q_from:, hq], kt[b, :, h], vt[b, :, h]
+            qq, kk, vv = qt[b, ridx, hq], kt[b, :, h], vt[b, :, h]
             a = torch.where(sa, qq @ kk.T / math.sqrt(D), -math.inf)
             M = a.detach().amax(dim=1, keepdim=True)
             M = torch.where(torch.isfinite(M), M, torch.zeros_like(M))
@@ -464,7 +473,7 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: 
             den = wgt.sum(dim=1, keepdim=True)
             safe = den > 0.0
             o = torch.where(safe, (wgt @ vv) / torch.where(safe, den, torch.ones_like(den)), 0.0)
-            loss = loss + (o * do[b, q_from:, hq]).sum()
+            loss = loss + (o * do[b, ridx, hq]).sum()
     loss.backward()
     return tuple(t.grad.numpy() for t in (qt, kt, vt, wt))
 

@@ -152,3 +152,36 @@ def test_routing_scope_checks():
     assert lib.still_backward_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) > \
         lib.still_backward_workspace_bytes(ctypes.byref(_cfg())) > 0
     assert lib.still_future_attention_mass_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) == 0
+
+
+def test_routing_override_is_validated_on_the_host():
+    """routing_in is host memory, checked before anything is enqueued: each chunk's top_k
+    entries strictly ascending inside the chunk, else INVALID_ARG."""
+    import numpy as np
+
+    lib = still.load()
+    cfg = _cfg(seq_len=200, top_k=4)  # 3 complete chunks
+    need = lib.still_prefill_workspace_bytes(ctypes.byref(cfg))
+    p = ctypes.c_void_p(1 << 20)
+    good = np.array([[[[1, 5, 9, 63], [64, 65, 66, 127], [130, 140, 150, 191]]]], dtype=np.int32)
+    bad_cases = []
+    for (c, i, val) in ((0, 3, 64), (1, 0, 63), (2, 1, 130), (2, 2, 139), (0, 0, -1)):
+        r = good.copy()
+        r[0, 0, c, i] = val  # out of its chunk, repeated, or descending
+        bad_cases.append(r)
+    for r in bad_cases:
+        rc = lib.still_prefill(ctypes.byref(cfg), p, p, p, p, p, ctypes.c_void_p(r.ctypes.data), None, None, None,
+                               p, need, None)
+        assert rc == -1
+    # per-query-head routing validates [batch, n_q_heads, ...] records
+    cfgq = _cfg(seq_len=200, top_k=4, scope="query_head")
+    needq = lib.still_prefill_workspace_bytes(ctypes.byref(cfgq))
+    rq = np.broadcast_to(good, (1, 4, 3, 4)).copy()
+    rq[0, 3, 1, 2] = 200
+    assert lib.still_prefill(ctypes.byref(cfgq), p, p, p, p, p, ctypes.c_void_p(rq.ctypes.data), None, None, None,
+                             p, needq, None) == -1
+
+
+def test_last_hip_error_starts_clear():
+    lib = still.load()
+    assert lib.still_last_hip_error() == 0

@@ -209,39 +209,30 @@ def test_decode_from_empty_matches_oracle(case):
     assert err <= TOL[dt], err
 
 
-def test_decode_full_size_sampled():
-    """The batched decode workload at full size (32 sequences, 65536-token prefix put into
-    the cache by one prefill, head_dim 128, top_k 16), in the launch configuration the
-    benchmark times: two decode steps, sampled (sequence, KV head) groups against the
-    per-query oracle on the extended sequences under the device's routing."""
-    wl = synth.L8B_DECODE
-    _say("decode-full", wl.name)
-    dev = torch.device("cuda")
-    B, Hq, Hkv, D, T0, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.seq_len, wl.chunk
-    G = Hq // Hkv
-    n_new = 2
-    cache = _new_cache(wl, T0 + n_new)
-    q, k, v, w = synth.make_inputs_device(wl, dev)
-    out, idx = still.prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, return_routing=True, cache=cache)
-    del q, out
-    qn, kn, vn, _ = synth.make_inputs_device(wl, dev, seq_len=n_new, seed_offset=1)
-    outs = [cache.step(qn[:, t].contiguous(), kn[:, t].contiguous(), vn[:, t].contiguous(), w)
-            for t in range(n_new)]
+def test_prefill_into_cache_beyond_4gib():
+    """A decode cache sized for 2^24 tokens at head_dim 128 and top_k 64 holds 2^18 + 1
+    compact tiles per (batch, KV head): 4 GiB + 16 KiB of compact K rows, past a 32-bit byte
+    range. A prefill into it reads its compact rows back from the cache, and must give the
+    same output bits as the same prefill without a cache; two decode steps then match the
+    prefill of the extended sequence within the bf16 bar."""
+    name = "cache-beyond-4gib"
+    _say(name)
+    wl, (q, kk, v, wp) = synth.small_case(seed=404, B=1, T=302, Hq=4, Hkv=1, D=128, F=128, window=64, chunk=64,
+                                           top_k=64, dtype="bf16", qk_scale=1.0, n_planted=3)
+    tq, tk, tv, tw = (_dev(a, "bf16") for a in (q, kk, v, wp))
+    T0 = 300
+    cache = _new_cache(wl, 1 << 24)
+    assert cache.c.sel_capacity * 128 * 2 > (1 << 32)
+    ref_out = still.prefill(tq[:, :T0].contiguous(), tk[:, :T0].contiguous(), tv[:, :T0].contiguous(), tw,
+                            window=64, top_k=64)
+    out = still.prefill(tq[:, :T0].contiguous(), tk[:, :T0].contiguous(), tv[:, :T0].contiguous(), tw, window=64,
+                        top_k=64, cache=cache)
+    dec, _, _ = _decode_steps(cache, tq, tk, tv, tw, T0, 302)
     torch.cuda.synchronize()
-    idx = idx.cpu().numpy()
-    wh = w.float().cpu().numpy()
-    worst = 0.0
-    for (b, h) in ((0, 0), (13, 5), (31, 7)):
-        kb = torch.cat([k[b, :, h], kn[b, :, h]]).float().cpu().numpy()[None, :, None, :]
-        vb = torch.cat([v[b, :, h], vn[b, :, h]]).float().cpu().numpy()[None, :, None, :]
-        qb = np.zeros((1, T0 + n_new, G, D), dtype=np.float32)
-        qb[0, T0:] = qn[b, :, h * G:(h + 1) * G].float().cpu().numpy()
-        selb = np.zeros((1, 1, T0 + n_new), dtype=bool)
-        selb[0, 0, idx[b, h].reshape(-1)] = True
-        rows = [(0, g, T0 + t) for t in range(n_new) for g in range(G)]
-        ref = O.brute_rows(qb, kb, vb, wh[h:h + 1], wl.window, C, selb, rows)
-        got = np.stack([_np(outs[t][b, h * G + g]) for (_, g, i) in rows for t in [i - T0]])
-        err = float(np.abs(got - ref).max())
-        worst = max(worst, err)
-        _say("decode-full", (b, h), "max abs err", err)
-    assert worst <= TOL["bf16"], worst
+    assert torch.equal(out, ref_out)
+    full = _np(still.prefill(tq, tk, tv, tw, window=64, top_k=64))
+    err = float(np.abs(dec - full[:, T0:]).max())
+    _say(name, "decode against prefill max abs err", err)
+    assert err <= TOL["bf16"], err
+    del cache
+    torch.cuda.empty_cache()

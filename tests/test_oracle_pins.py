@@ -442,6 +442,27 @@ def test_backward_tail_rows_equal_full_gradients():
     assert np.abs(tail[1][:, :27]).max() > 0  # earlier keys get only part of their gradient
 
 
+def test_backward_row_list_equals_masked_output_gradient():
+    """attend_backward(rows=R) equals the full-loss gradients when dout is zero outside the
+    rows R (rows unsorted, with gaps, the first and the last among them): every gradient is
+    then exact at every position, dW included."""
+    T, Hq, Hkv, w, C, k = 43, 4, 2, 8, 8, 3
+    q, k_, v, wp = _case(1, T, Hq, Hkv, 8, 6, seed=14, scale=1.5)
+    sel = _fixed_routing(q, k_, w, C, k, 1, Hkv, T)
+    rows = np.array([30, 0, 17, 42, 9, 8, 25])
+    dout = np.random.default_rng(4).standard_normal(q.shape)
+    masked = np.zeros_like(dout)
+    masked[:, rows] = dout[:, rows]
+    full = O.attend_backward(q, k_, v, wp, w, C, sel, masked)
+    part = O.attend_backward(q, k_, v, wp, w, C, sel, dout, rows=rows)
+    for a, b in zip(full, part):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    assert np.all(part[0][:, np.setdiff1d(np.arange(T), rows)] == 0.0)
+    assert np.abs(part[1]).max() > 0 and np.abs(part[3]).max() > 0
+    with pytest.raises(ValueError):
+        O.attend_backward(q, k_, v, wp, w, C, sel, dout, rows=[3, 3])
+
+
 # ----------------------------------------------------------------------------- local-global consistency
 
 def test_future_attention_mass_brute_force():
