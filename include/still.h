@@ -237,6 +237,25 @@ int still_decode_step_timed(const still_config* cfg, still_cache* cache, const v
                             void* workspace, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t* events);
 
+/* Size of the library's own decode scratch (bytes), the limit of still_decode_step_noalloc. */
+#define STILL_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* still_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same step, with no
+ * workspace argument. The split partials go to a scratch array the library holds in device
+ * memory, one copy per GPU, from the first call on that GPU until the process ends; no HIP
+ * allocating routine is called. A call needs 8 * n + 4 * head_dim * n bytes of it (n =
+ * batch * n_kv_heads * n_q_heads/n_kv_heads * splits, splits <= 64, chosen as in
+ * still_decode_step), at most STILL_DECODE_NOALLOC_SCRATCH_BYTES; a larger step returns
+ * STILL_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the 32 x 64K Llama-3.1-8B-shaped
+ * decode needs 4.3 MB). Every call on one GPU shares the one scratch: calls that overlap on
+ * one GPU (different streams or threads) race, and must be ordered by the caller. Nothing in
+ * the scratch has to start at zero (each call writes its partials before reading them).
+ * Results are those of still_decode_step. */
+int still_decode_step_noalloc(const still_config* cfg, still_cache* cache, const void* q,
+                              const void* k, const void* v, const void* w_phi, void* out,
+                              hipStream_t stream);
+
 /* Bytes of scratch still_backward needs for `cfg` (0 if cfg is invalid or unsupported). */
 size_t still_backward_workspace_bytes(const still_config* cfg);
 

@@ -137,6 +137,8 @@ bool routing_valid(const still_config* c, const int32_t* r) {
 }
 
 constexpr int kMaxDecodeGroup = 16;  // query heads per KV head the decode kernels handle
+static_assert(STILL_DECODE_NOALLOC_SCRATCH_BYTES == still::kDecodeScratchBytes, "the header states the scratch size");
+
 constexpr int kMaxSplit = 64;        // workgroups per (b, KV head) over the compact cache
 constexpr int kSplitTarget = 2048;   // aim for this many split workgroups per decode step
 
@@ -599,6 +601,25 @@ int still_decode_step_timed(const still_config* cfg, still_cache* cache, const v
   if (events) STILL_HIP(hipEventRecord(events[0], stream));
   STILL_HIP(still::launch_decode(a, stream, events ? events[1] : nullptr));
   if (events) STILL_HIP(hipEventRecord(events[2], stream));
+  cache->n_tokens += 1;
+  return STILL_OK;
+}
+
+int still_decode_step_noalloc(const still_config* cfg, still_cache* cache, const void* q, const void* k,
+                              const void* v, const void* w_phi, void* out, hipStream_t stream) {
+  still::DecodeArgs a;
+  const int st = decode_plan(cfg, cache, q, k, v, w_phi, out, a);
+  if (st != STILL_OK) return st;
+  // the partials of this call's splits only, at the front of the library's scratch
+  const size_t recs = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * a.nsplit * a.d.G;
+  const size_t ml_bytes = align_up(recs * 2 * sizeof(float));
+  if (ml_bytes + recs * cfg->head_dim * sizeof(float) > still::kDecodeScratchBytes)
+    return STILL_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  STILL_HIP(still::decode_scratch(&scratch));
+  a.part_ml = static_cast<float*>(scratch);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(scratch) + ml_bytes);
+  STILL_HIP(still::launch_decode(a, stream, nullptr));
   cache->n_tokens += 1;
   return STILL_OK;
 }

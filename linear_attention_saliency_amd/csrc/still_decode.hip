@@ -20,11 +20,39 @@
 //                        rows are appended to the compact cache, the others are added to the
 //                        state (sum phi(k) v^T, sum phi(k)).
 // cache_export_kernel leaves a cache as these kernels expect it after a prefill of T tokens.
+#include <mutex>
+
 #include "still_launch.hpp"
 #include "still_layout.hpp"
 #include "still_route.hpp"
 
+// Scratch of still_decode_step_noalloc: the split partials, for callers that cannot
+// allocate. One copy per GPU, held until the process ends; calls on one GPU share it. In
+// host code this name is not a device address: decode_scratch() below looks the address
+// up once per device, and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[still::kDecodeScratchBytes];
+
 namespace still {
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -175,6 +175,11 @@ hipError_t launch_feature_map(const Dims& d, const void* x, const void* w, float
 hipError_t launch_cache_export(const ExportArgs& a, hipStream_t s);
 // mid: optional event recorded between the compact-cache kernel and the token kernel
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t mid);
+// Bytes of the decode step's file-scope device scratch (the entry point that allocates
+// nothing keeps its split partials there), and that scratch's device address on the
+// current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // true if the (dtype, D, DF) triple has kernel instantiations

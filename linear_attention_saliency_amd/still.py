@@ -25,7 +25,7 @@ EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefil
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
            "still_decode_step", "still_decode_step_timed", "still_backward_workspace_bytes", "still_backward",
            "still_backward_timed", "still_future_attention_mass_workspace_bytes", "still_future_attention_mass",
-           "still_selection_overlap", "still_last_hip_error")
+           "still_selection_overlap", "still_last_hip_error", "still_decode_step_noalloc")
 
 
 class StillError(RuntimeError):
@@ -100,6 +100,8 @@ def load():
     lib.still_future_attention_mass.restype = I
     lib.still_selection_overlap.argtypes = [CP, P, P, P, V]
     lib.still_selection_overlap.restype = I
+    lib.still_decode_step_noalloc.argtypes = [CP, KP, P, P, P, P, P, V]
+    lib.still_decode_step_noalloc.restype = I
     lib.still_last_hip_error.argtypes = []
     lib.still_last_hip_error.restype = I
     _lib = lib
@@ -404,4 +406,15 @@ class DecodeCache:
                                             _ptr(v), _ptr(w_phi), _ptr(out), _ptr(self.workspace),
                                             self.workspace.numel(), _stream(stream), events)
         _check(rc, "still_decode_step")
+        return out
+
+    def step_noalloc(self, q, k, v, w_phi, out, *, stream=None):
+        """As step(), through still_decode_step_noalloc: no workspace, the library's own
+        device scratch (out must be given: nothing is allocated)."""
+        for t in (q, k, v, w_phi, out):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("tensors must be contiguous device tensors")
+        rc = load().still_decode_step_noalloc(ctypes.byref(self.cfg), ctypes.byref(self.c), _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(w_phi), _ptr(out), _stream(stream))
+        _check(rc, "still_decode_step_noalloc")
         return out
