@@ -369,19 +369,37 @@ struct AttnCfg {
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
   static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
   static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
+  // Sequential plan, where the usual one (every fixed tile, the prefix state and a compact
+  // stage resident at once) would pass the CU's 160 KiB (fp32 at head_dim 128: six 32 KiB
+  // tiles and a 64 KiB state): the linear-attention tiles first, the window's K tiles
+  // then over the phi(K) regions, W_h and the state read from memory, and the compact
+  // tiles in two stages over the same regions.
+  static constexpr int ST_FULL = D * DF;
+  static constexpr bool SEQ = (2 * FT + 2 * VT + 2 * KT + ST_FULL + STAGE) * static_cast<int>(sizeof(T)) > 160 * 1024;
   // the prefix state (S^T [D][DF] in the layer's dtype) goes through LDS where it fits
   // beside the tiles: at D = d_f = 64 (two workgroups per CU) and at D = 128 (one, with
   // both query slices: 8 waves read one copy instead of 8)
-  static constexpr bool STATE_LDS = (D == 64 && DF == 64) || D == 128;
+  static constexpr bool STATE_LDS = !SEQ && ((D == 64 && DF == 64) || D == 128);
   static constexpr int ST = STATE_LDS ? D * DF : 0;
-  // LDS regions of the fixed part (element offsets); compact stages 1 and 2 reuse them
-  static constexpr int R_PHIP = 0, R_PHIC = FT, R_VP = 2 * FT, R_VC = 2 * FT + VT;
-  static constexpr int R_KC = 2 * FT + 2 * VT, R_KP = R_KC + KT, R_ST = R_KP + KT;
-  // compact pipeline: 4 stages; stage 0 after the fixed regions, stages 1..3 over them
-  static constexpr int NSTAGE = 4;
-  static constexpr int R_P0 = R_ST + ST > 3 * STAGE ? R_ST + ST : 3 * STAGE;
-  static constexpr int LDS_BYTES = (R_P0 + STAGE) * static_cast<int>(sizeof(T));
-  static __device__ __forceinline__ int stage_off(int s) { return s == 0 ? R_P0 : (s - 1) * STAGE; }
+  // LDS regions of the fixed part (element offsets); compact stages 1 and 2 reuse them. In
+  // the sequential plan the V^T tiles come first and K of chunks c and c-1 go over the
+  // phi(K) regions once phase 1 is done with them (and past them where K is the wider).
+  static constexpr int R_PHIP = SEQ ? 2 * VT : 0, R_PHIC = R_PHIP + FT;
+  static constexpr int R_VP = SEQ ? 0 : 2 * FT, R_VC = R_VP + VT;
+  static constexpr int R_KC = SEQ ? 2 * VT : 2 * FT + 2 * VT, R_KP = R_KC + KT;
+  static constexpr int R_ST = SEQ ? 2 * FT + 2 * VT : R_KP + KT;
+  // compact pipeline: 4 stages (2 in the sequential plan); stage 0 after the fixed regions,
+  // stages 1..3 over them
+  static constexpr int NSTAGE = SEQ ? 2 : 4;
+  static constexpr int R_P0 = SEQ ? 0 : (R_ST + ST > 3 * STAGE ? R_ST + ST : 3 * STAGE);
+  static constexpr int SEQ_FIXED = 2 * VT + (FT > KT ? 2 * FT : 2 * KT);
+  static constexpr int LDS_ELEMS = SEQ ? (SEQ_FIXED > 2 * STAGE ? SEQ_FIXED : 2 * STAGE) : R_P0 + STAGE;
+  static constexpr int LDS_BYTES = LDS_ELEMS * static_cast<int>(sizeof(T));
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS plan must fit a CU");
+  static __device__ __forceinline__ int stage_off(int s) {
+    if constexpr (SEQ) return s * STAGE;
+    return s == 0 ? R_P0 : (s - 1) * STAGE;
+  }
   // Query slices per workgroup. Where two workgroups fit in a CU's LDS (two 80 KiB
   // halves) each takes one slice, and the pair hides each other's waits. Where only one
   // fits (head_dim 128, or fp32) it takes both slices with twice the waves, so every SIMD
@@ -502,7 +520,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   // W_h rows fb*16 + r16 (A operand of phi(q)): held in registers where they fit, else
   // copied once into compact stage 0 (free until the first compact tile) for all waves
   const T* Wh = w + static_cast<long long>(h) * DF * D;
-  constexpr bool W_EARLY = D == 64 && DF == 64;
+  constexpr bool W_EARLY = D == 64 && DF == 64 && !C::SEQ;
+  constexpr bool W_GLOBAL = C::SEQ;  // W_h fragments straight from memory (no LDS room)
   frag wq[W_EARLY ? DF / 16 : 1][D / 32];
   if constexpr (W_EARLY) {
 #pragma unroll
@@ -533,13 +552,15 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     const T* kp = kk + ((b * T_ + tp) * d.Hkv + h) * D;
     dma_tile<T, DF, 64, NW>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + tp) * DF, DF, has_prev ? 64 : 0);
     dma_tile<T, 64, D, NW>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
-    dma_tile<T, D, 64, NW>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
+    if constexpr (!C::SEQ) dma_tile<T, D, 64, NW>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
     dma_tile<T, DF, 64, NW>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
     dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
-    dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
+    if constexpr (!C::SEQ) dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
       dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
-    if constexpr (W_EARLY) {
+    if constexpr (C::SEQ) {
+      // the window's K tiles come after phase 1, over the phi(K) regions
+    } else if constexpr (W_EARLY) {
       dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
       dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
     } else {
@@ -570,7 +591,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 
   // window = chunk takes a fast path for the masks and handles chunk c-1's linear keys
   // together with its window tile (head_dim 64; at 128 the extra live registers spill)
-  const bool fast = D == 64 && win == kChunk;
+  const bool fast = D == 64 && win == kChunk && !C::SEQ;
   frag pq[QB][DF / 32];  // phi(q): B-operand fragments (PK over f)
   uint64_t selprev;
   // =============================== phase 1: linear attention ===========================
@@ -620,6 +641,10 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every region copied at the start has landed
+    } else if constexpr (W_GLOBAL) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // the linear-attention tiles have landed
+      phi_q([&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8); });
     } else {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every region copied at the start has landed, W_h among them
@@ -719,6 +744,15 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   }
 
   // =============================== phase 2: softmax tiles ==============================
+  if constexpr (C::SEQ) {  // K of chunks c and c-1 over the phi(K) regions phase 1 is done with
+    __syncthreads();
+    const int kvs = d.Hkv * D;
+    const long long tp = has_prev ? t0 - kChunk : t0;
+    dma_tile<T, D, 64, NW>(L + C::R_KP, kk + ((b * T_ + tp) * d.Hkv + h) * D, kvs, has_prev && win >= 1 ? 64 : 0);
+    dma_tile<T, D, 64, NW>(L + C::R_KC, kk + ((b * T_ + t0) * d.Hkv + h) * D, kvs, win >= 1 ? nvalid : 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   // 2a. the window: chunk c (r - w < p <= r), chunk c-1 (p > r + 64 - w, or selected)
   if (fast) {
     if (qoff == 0)
@@ -780,6 +814,37 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 #pragma unroll
       for (int j = 0; j < 4; ++j) mayfar[j] = __builtin_amdgcn_ballot_w64(qmax * tb[j] > mmin + kLazy);
     }
+    if constexpr (C::SEQ) {
+      // two stages over the fixed regions: tile t in stage t % 2, tile t + 2 issued once
+      // every wave is done with tile t
+      __syncthreads();  // every wave is done with the window tiles
+      issue(0, 0);
+      if (nt_comp > 1) issue(1, 1);
+      for (int t = 0; t < nt_comp; ++t) {
+        if (t + 1 < nt_comp)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();
+        f32x4 sc[4][QB];
+        qk_tile<T, D, QB>(L + C::stage_off(t & 1), qf, sc);
+        const int nk = n_comp - t * 64;
+        if (nk < 64) {
+          uint32_t kw[QB];
+          const uint32_t rw = range_word(0, nk - 1);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
+          mask_tile<QB>(sc, kw);
+        }
+        const int tj = t >> 6;
+        const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
+        if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(sc, o, m_run, c1);
+        sm_exp_pv<T, D, QB>(sc, L + C::stage_off(t & 1) + C::KT, o, m_run, c1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's reads of the stage are done (and no copy is in flight)
+        lds_barrier();
+        if (t + 2 < nt_comp) issue(t + 2, t & 1);
+      }
+    } else {
     f32x4 sa[4][QB], sb[4][QB];
     if constexpr (!W_EARLY) {  // tile 0 was copied after phi(q)
       __builtin_amdgcn_s_waitcnt(0);
@@ -814,6 +879,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     for (int t = 0; t < nt_comp; t += 2) {
       step(t, sa, sb);
       if (t + 1 < nt_comp) step(t + 1, sb, sa);
+    }
     }
   }
 
@@ -864,8 +930,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     if (dd.D == 64 && dd.DF == 128) return attn_t<bf16, 64, 128>(a, s);
     if (dd.D == 128 && dd.DF == 64) return attn_t<bf16, 128, 64>(a, s);
     if (dd.D == 128 && dd.DF == 128) return attn_t<bf16, 128, 128>(a, s);
-  } else if (dd.D == 64 && dd.DF == 64) {
-    return attn_t<float, 64, 64>(a, s);
+  } else {
+    if (dd.D == 64 && dd.DF == 64) return attn_t<float, 64, 64>(a, s);
+    if (dd.D == 64 && dd.DF == 128) return attn_t<float, 64, 128>(a, s);
+    if (dd.D == 128 && dd.DF == 64) return attn_t<float, 128, 64>(a, s);
+    if (dd.D == 128 && dd.DF == 128) return attn_t<float, 128, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

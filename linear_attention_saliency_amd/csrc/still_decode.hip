@@ -201,9 +201,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 template <typename T, int D, int DF>
 struct TokLds {
   static constexpr int KP = DF + 1;  // padded phi row (conflict-free column reads)
+  // the ring's V rows are staged in LDS where the whole plan fits the CU's 160 KiB, else
+  // read from the ring in memory (fp32 at head_dim = feat_dim = 128)
+  static constexpr size_t fixed = 129 * D * sizeof(T) + kMaxGroup * (D + DF) * 4 + 64 * KP * 4 + 2 * kMaxGroup * 128 * 4 +
+                                  (256 + 64 + 5 * kMaxGroup) * 4;
+  static constexpr bool VT_LDS = fixed + 128 * D * sizeof(T) <= 160 * 1024;
   static constexpr size_t kt = 0;                                     // Swz<T,D>, 129 rows
-  static constexpr size_t vt = kt + 129 * D * sizeof(T);              // [128][D] T
-  static constexpr size_t qs = vt + 128 * D * sizeof(T);              // [16][D] f32
+  static constexpr size_t vt = kt + 129 * D * sizeof(T);              // [128][D] T (VT_LDS)
+  static constexpr size_t qs = vt + (VT_LDS ? 128 * D * sizeof(T) : 0);  // [16][D] f32
   static constexpr size_t phq = qs + kMaxGroup * D * 4;               // [16][DF]
   static constexpr size_t phk = phq + kMaxGroup * DF * 4;             // [64][KP]
   static constexpr size_t wla = phk + 64 * KP * 4;                    // [16][128]
@@ -212,6 +217,8 @@ struct TokLds {
   static constexpr size_t xn2 = m2part + 256 * 4;                     // [64]
   static constexpr size_t gstat = xn2 + 64 * 4;                       // [5][16]
   static constexpr size_t bytes = gstat + 5 * kMaxGroup * 4;
+  static_assert(bytes == fixed + (VT_LDS ? 128 * D * sizeof(T) : 0), "layout and budget agree");
+  static_assert(bytes <= 160 * 1024, "the token kernel's LDS must fit a CU");
 };
 
 // One workgroup per (b, KV head). LDS tile row t holds the key at position 64(c-1) + t:
@@ -258,6 +265,17 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   T* ring_k = static_cast<T*>(a.c.ring_k) + static_cast<long long>(bh) * 2 * 64 * D;
   T* ring_v = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * 2 * 64 * D;
   const uint64_t prev_mask = has_prev ? a.c.sel_mask[bh * 2 + slot_prev] : 0ull;
+  // element dd of ring row `row` (rows 0..63 chunk c-1, 64..127 chunk c; the new token at
+  // row 64 + r, later rows zero), from LDS or from the ring in memory
+  auto vring = [&](int row, int dd) -> float {
+    if constexpr (L::VT_LDS) {
+      return TT::to_f(vt[row * D + dd]);
+    } else {
+      if (row < 64) return has_prev ? TT::to_f(ring_v[(slot_prev * 64 + row) * D + dd]) : 0.f;
+      if (row < 64 + r) return TT::to_f(ring_v[(slot_cur * 64 + row - 64) * D + dd]);
+      return row == 64 + r ? TT::to_f(vnew[dd]) : 0.f;
+    }
+  };
 
   typename Tr<T>::frag wf[DF / 64][D / 32];  // NP-Map weights, loaded early
   np_map_load_w<T, D, DF>(wh, wf);
@@ -281,7 +299,8 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
       TT::store8(ring_v + (slot_cur * 64 + r) * D + c8 * 8, xv);
     }
     SW::store8(kt, row, c8 * 8, xk);
-    if (row < 128) TT::store8(vt + row * D + c8 * 8, xv);
+    if constexpr (L::VT_LDS)
+      if (row < 128) TT::store8(vt + row * D + c8 * 8, xv);
   }
   for (int idx = tid; idx < G * D; idx += 256) qs[idx] = TT::to_f(q[idx]);
   __syncthreads();
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     float osa = 0.f, ola = 0.f;
 #pragma unroll 8
     for (int row = 0; row < 128; ++row) {
-      const float vv = TT::to_f(vt[row * D + dd]);
+      const float vv = vring(row, dd);
       osa += ex[g * 128 + row] * vv;
       ola += wla[g * 128 + row] * vv;
     }
@@ -470,7 +489,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
       if ((prev_mask >> p) & 1ull) {
         const long long R = row0 + __popcll(prev_mask & ((1ull << p) - 1ull));
         sk[R * D + dd] = kt[SW::off(p, dd)];  // compact rows are the raw keys
-        sv[((R / 64) * D + dd) * 64 + pk_pos(static_cast<int>(R % 64))] = vt[p * D + dd];
+        sv[((R / 64) * D + dd) * 64 + pk_pos(static_cast<int>(R % 64))] = TT::from_f(vring(p, dd));
       }
     }
   }
@@ -492,7 +511,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     const int f = idx / D, dd = idx % D;
     float acc = 0.f;
 #pragma unroll 8
-    for (int p = 0; p < 64; ++p) acc += phk[p * KP + f] * TT::to_f(vt[p * D + dd]);
+    for (int p = 0; p < 64; ++p) acc += phk[p * KP + f] * vring(p, dd);
     Sw[idx] += acc;
   }
   for (int f = tid; f < DF; f += 256) {
@@ -594,8 +613,11 @@ static hipError_t export_t(const ExportArgs& a, hipStream_t s) {
       if (dd_.D == 64 && dd_.DF == 128) return FN<bf16, 64, 128>(__VA_ARGS__);    \
       if (dd_.D == 128 && dd_.DF == 64) return FN<bf16, 128, 64>(__VA_ARGS__);    \
       if (dd_.D == 128 && dd_.DF == 128) return FN<bf16, 128, 128>(__VA_ARGS__);  \
-    } else if (dd_.D == 64 && dd_.DF == 64) {                                     \
-      return FN<float, 64, 64>(__VA_ARGS__);                                      \
+    } else {                                                                      \
+      if (dd_.D == 64 && dd_.DF == 64) return FN<float, 64, 64>(__VA_ARGS__);     \
+      if (dd_.D == 64 && dd_.DF == 128) return FN<float, 64, 128>(__VA_ARGS__);   \
+      if (dd_.D == 128 && dd_.DF == 64) return FN<float, 128, 64>(__VA_ARGS__);   \
+      if (dd_.D == 128 && dd_.DF == 128) return FN<float, 128, 128>(__VA_ARGS__); \
     }                                                                             \
     return hipErrorInvalidValue;                                                  \
   } while (0)

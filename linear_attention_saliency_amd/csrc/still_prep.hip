@@ -442,10 +442,7 @@ static hipError_t fmap_t(const Dims& d, const void* x, const void* w, float* phi
   return hipGetLastError();
 }
 
-bool shape_supported(int bf16, int D, int DF) {
-  if (bf16) return (D == 64 || D == 128) && (DF == 64 || DF == 128);
-  return D == 64 && DF == 64;
-}
+bool shape_supported(int, int D, int DF) { return (D == 64 || D == 128) && (DF == 64 || DF == 128); }
 
 #define STILL_DISPATCH(FN, ...)                                                   \
   do {                                                                            \
@@ -455,8 +452,11 @@ bool shape_supported(int bf16, int D, int DF) {
       if (dd_.D == 64 && dd_.DF == 128) return FN<bf16, 64, 128>(__VA_ARGS__);    \
       if (dd_.D == 128 && dd_.DF == 64) return FN<bf16, 128, 64>(__VA_ARGS__);    \
       if (dd_.D == 128 && dd_.DF == 128) return FN<bf16, 128, 128>(__VA_ARGS__);  \
-    } else if (dd_.D == 64 && dd_.DF == 64) {                                     \
-      return FN<float, 64, 64>(__VA_ARGS__);                                      \
+    } else {                                                                      \
+      if (dd_.D == 64 && dd_.DF == 64) return FN<float, 64, 64>(__VA_ARGS__);     \
+      if (dd_.D == 64 && dd_.DF == 128) return FN<float, 64, 128>(__VA_ARGS__);   \
+      if (dd_.D == 128 && dd_.DF == 64) return FN<float, 128, 64>(__VA_ARGS__);   \
+      if (dd_.D == 128 && dd_.DF == 128) return FN<float, 128, 128>(__VA_ARGS__); \
     }                                                                             \
     return hipErrorInvalidValue;                                                  \
   } while (0)

@@ -486,36 +486,37 @@ def attend_backward(q, k, v, w_phi, window: int, chunk: int, sel, dout, q_from: 
 class DecodeOracle:
     """Token-by-token replay of the layer with an explicit decode state.
 
-    State per (batch, KV head): a compact list of selected tokens from chunks <= c-2 (the
-    softmax cache), the raw keys/values of chunks c-1 and c (the ring), the selection of
-    chunk c-1, the running saliency of chunk c, and the linear-attention state (S, z) of
-    every unselected token of chunks <= c-2. When a chunk completes, its top_k tokens are
-    chosen, and the chunk before it is folded: selected rows join the cache, the rest join
-    (S, z). Needs 1 <= window <= chunk (or window = 0 with top_k = 0).
+    With L = max(1, ceil((window - 1) / chunk)) earlier chunks kept raw (every key of a
+    token's window lies in them or in its own chunk), the state per (batch, KV head) for a
+    token of chunk c is: a compact list of the selected tokens of chunks <= c-L-1 (the
+    softmax cache), the raw keys/values of chunks c-L .. c (the ring), the selections of
+    chunks c-L .. c-1, the running saliency of chunk c, and the linear-attention state
+    (S, z) of every unselected token of chunks <= c-L-1. When chunk c completes, its top_k
+    tokens are chosen, and chunk c-L is folded: its selected rows join the cache, the rest
+    join (S, z). Needs window >= 1 (or window = 0 with top_k = 0).
     """
 
     def __init__(self, w_phi, n_q_heads: int, window: int, chunk: int, top_k: int):
         _check_cfg(window, chunk, top_k)
-        if window > chunk:
-            raise ValueError("the decode state holds two chunks, so window <= chunk")
         self.w = _f64(w_phi)
         self.Hkv, self.F, self.D = self.w.shape
         self.Hq = n_q_heads
         self.G = _check_group(n_q_heads, self.Hkv)
         self.window, self.chunk, self.top_k = window, chunk, top_k
+        self.L = max(1, -(-(window - 1) // chunk)) if window >= 1 else 1
         self.B = None
         self.t = 0
 
     def _init(self, B):
-        H, D, F, C = self.Hkv, self.D, self.F, self.chunk
+        H, D, F, C, L = self.Hkv, self.D, self.F, self.chunk, self.L
         self.B = B
         self.cache_k = [[np.zeros((0, D)) for _ in range(H)] for _ in range(B)]
         self.cache_v = [[np.zeros((0, D)) for _ in range(H)] for _ in range(B)]
         self.S = np.zeros((B, H, F, D))
         self.z = np.zeros((B, H, F))
-        self.ring_k = np.zeros((B, H, 2, C, D))  # [.., 0] = chunk c-1, [.., 1] = chunk c
-        self.ring_v = np.zeros((B, H, 2, C, D))
-        self.prev_sel = np.zeros((B, H, C), dtype=bool)
+        self.ring_k = np.zeros((B, H, L + 1, C, D))  # slot l holds chunk c - L + l
+        self.ring_v = np.zeros((B, H, L + 1, C, D))
+        self.ring_sel = np.zeros((B, H, L, C), dtype=bool)  # selections of chunks c-L .. c-1
         self.cur_s = np.zeros((B, H, C))
         self.sel_idx = []  # per completed chunk: [B,H,top_k] absolute positions
 
@@ -525,41 +526,39 @@ class DecodeOracle:
         B = q_t.shape[0]
         if self.B is None:
             self._init(B)
-        C, w, D, G = self.chunk, self.window, self.D, self.G
+        C, w, D, G, L = self.chunk, self.window, self.D, self.G, self.L
         i = self.t
         c, r = divmod(i, C)
-        self.ring_k[:, :, 1, r] = k_t
-        self.ring_v[:, :, 1, r] = v_t
+        self.ring_k[:, :, L, r] = k_t
+        self.ring_v[:, :, L, r] = v_t
         out = np.zeros((B, self.Hq, D))
         inv = 1.0 / math.sqrt(D)
+        # ring keys in position order (chunks that exist, the current one up to i), their
+        # positions, and which are selected tokens of earlier chunks
+        slots = [l for l in range(L + 1) if c - L + l >= 0]
+        pos = np.concatenate([(c - L + l) * C + np.arange(C if l < L else r + 1) for l in slots])
         for b in range(B):
             for h in range(self.Hkv):
                 W = self.w[h]
-                # keys of chunk c-1 (only if it exists) and chunk c up to i
-                prev_k = self.ring_k[b, h, 0] if c > 0 else np.zeros((0, D))
-                prev_v = self.ring_v[b, h, 0] if c > 0 else np.zeros((0, D))
-                cur_k = self.ring_k[b, h, 1, : r + 1]
-                cur_v = self.ring_v[b, h, 1, : r + 1]
-                p_prev = np.arange(prev_k.shape[0])
-                sa_prev = (p_prev > r + C - w) | self.prev_sel[b, h, : prev_k.shape[0]]
-                p_cur = np.arange(r + 1)
-                sa_cur = p_cur > r - w
+                rk = np.concatenate([self.ring_k[b, h, l, : (C if l < L else r + 1)] for l in slots])
+                rv = np.concatenate([self.ring_v[b, h, l, : (C if l < L else r + 1)] for l in slots])
+                rsel = np.concatenate([self.ring_sel[b, h, l] if l < L else np.zeros(r + 1, dtype=bool)
+                                       for l in slots])
+                in_window = pos > i - w
+                sa = in_window | rsel
                 ck, cv = self.cache_k[b][h], self.cache_v[b][h]
                 s_sum = 0.0
                 for g in range(G):
                     qv = q_t[b, h * G + g]
                     # saliency of token i over its window (all inside the ring)
                     if w >= 1:
-                        win_prev = prev_k[p_prev > r + C - w]
-                        win_cur = cur_k[p_cur > r - w]
-                        logits = np.concatenate([win_prev @ qv, win_cur @ qv]) * inv
-                        rest = logits[:-1]  # the window without the diagonal (last entry)
+                        logits = rk[in_window] @ qv * inv  # the last entry is token i itself
+                        rest = logits[:-1]
                         s_sum += lse(logits) - (lse(rest) if rest.size else -np.inf)
                     phiq = np_map(qv, W)
-                    keys_sa = np.concatenate([ck, prev_k[sa_prev], cur_k[sa_cur]])
-                    vals_sa = np.concatenate([cv, prev_v[sa_prev], cur_v[sa_cur]])
-                    keys_la = np.concatenate([prev_k[~sa_prev], cur_k[~sa_cur]])
-                    vals_la = np.concatenate([prev_v[~sa_prev], cur_v[~sa_cur]])
+                    keys_sa = np.concatenate([ck, rk[sa]])
+                    vals_sa = np.concatenate([cv, rv[sa]])
+                    keys_la, vals_la = rk[~sa], rv[~sa]
                     a = keys_sa @ qv * inv
                     M = a.max() if a.size else 0.0
                     e = np.exp(a - M)
@@ -574,13 +573,13 @@ class DecodeOracle:
         return out
 
     def _complete_chunk(self, c: int):
-        C, k = self.chunk, self.top_k
+        C, k, L = self.chunk, self.top_k, self.L
         B, H = self.B, self.Hkv
-        # fold chunk c-1: selected rows -> softmax cache, the rest -> (S, z)
-        if c > 0:
+        # fold chunk c-L: selected rows -> softmax cache, the rest -> (S, z)
+        if c - L >= 0:
             for b in range(B):
                 for h in range(H):
-                    sel = self.prev_sel[b, h]
+                    sel = self.ring_sel[b, h, 0]
                     pk, pv = self.ring_k[b, h, 0], self.ring_v[b, h, 0]
                     self.cache_k[b][h] = np.concatenate([self.cache_k[b][h], pk[sel]])
                     self.cache_v[b][h] = np.concatenate([self.cache_v[b][h], pv[sel]])
@@ -598,9 +597,11 @@ class DecodeOracle:
                 new_sel[b, h, pick] = True
                 picks[b, h] = pick + c * C
         self.sel_idx.append(picks)
-        self.prev_sel = new_sel
-        self.ring_k[:, :, 0] = self.ring_k[:, :, 1]
-        self.ring_v[:, :, 0] = self.ring_v[:, :, 1]
-        self.ring_k[:, :, 1] = 0.0
-        self.ring_v[:, :, 1] = 0.0
+        # rotate: chunk c - L + l + 1 moves to slot l; slot L takes the next chunk
+        self.ring_k[:, :, :L] = self.ring_k[:, :, 1:].copy()
+        self.ring_v[:, :, :L] = self.ring_v[:, :, 1:].copy()
+        self.ring_k[:, :, L] = 0.0
+        self.ring_v[:, :, L] = 0.0
+        self.ring_sel[:, :, : L - 1] = self.ring_sel[:, :, 1:].copy()
+        self.ring_sel[:, :, L - 1] = new_sel
         self.cur_s[:] = 0.0

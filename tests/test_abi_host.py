@@ -44,7 +44,7 @@ def test_status_strings():
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -1), (dict(seq_len=0), -1), (dict(n_q_heads=6, n_kv_heads=4), -1), (dict(dtype="f16"), -1),
     (dict(window=-1), -1), (dict(top_k=65), -1), (dict(window=0, top_k=1), -1), (dict(chunk=32, window=32), -2),
-    (dict(window=65), -2), (dict(head_dim=96), -2), (dict(feat_dim=32), -2), (dict(dtype="f32", head_dim=128), -2),
+    (dict(window=65), -2), (dict(head_dim=96), -2), (dict(feat_dim=32), -2), (dict(dtype="f32", head_dim=96), -2),
     (dict(seq_len=4_200_000, head_dim=128, feat_dim=128), -2),
 ])
 def test_invalid_configs_rejected_before_launch(kw, code):
@@ -71,6 +71,14 @@ def test_pointer_and_workspace_checks():
     sal = ctypes.c_void_p(1 << 21)
     need0 = lib.still_prefill_workspace_bytes(ctypes.byref(cfg0))
     assert lib.still_prefill(ctypes.byref(cfg0), p, p, p, p, p, None, sal, None, None, p, need0, None) == -1
+
+
+def test_f32_covers_every_head_and_feature_width():
+    lib = still.load()
+    for D in (64, 128):
+        for F in (64, 128):
+            assert lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(dtype="f32", head_dim=D, feat_dim=F))) > 0
+            assert lib.still_cache_bytes(ctypes.byref(_cfg(dtype="f32", head_dim=D, feat_dim=F)), 1024) > 0
 
 
 def test_workspace_scales_with_sequence():

@@ -82,6 +82,8 @@ PREFILL_THEN_DECODE = [
     ("bf16-d128-f64-k64", 1, 190, 330, 4, 1, 128, 64, 64, 64, "bf16", 1.0),
     ("bf16-w33-k3", 1, 100, 300, 4, 1, 64, 64, 33, 3, "bf16", 1.0),
     ("bf16-d128-k63", 1, 120, 280, 4, 2, 128, 128, 64, 63, "bf16", 1.0),
+    ("f32-d128-at-boundary", 2, 128, 268, 8, 2, 128, 128, 64, 16, "f32", 1.0),
+    ("f32-d128-f64-w16", 1, 70, 200, 4, 1, 128, 64, 16, 8, "f32", 1.0),
     # routed by the diagonal logit instead of the Self-Saliency Score
     ("bf16-diag-score", 2, 100, 270, 4, 1, 64, 64, 64, 8, "bf16", 1.0, "diag"),
     ("bf16-d128-diag-score", 1, 64, 200, 4, 2, 128, 128, 64, 16, "bf16", None, "diag"),
@@ -167,6 +169,7 @@ FROM_EMPTY = [
     # name, B, T, Hq, Hkv, D, F, w, k, dtype, qk_scale
     ("f32-from-empty", 2, 200, 2, 1, 64, 64, 64, 8, "f32", 1.0),
     ("bf16-from-empty-gqa4", 1, 210, 8, 2, 128, 128, 64, 16, "bf16", 1.0),
+    ("f32-d128-from-empty", 1, 200, 4, 1, 128, 128, 64, 16, "f32", 1.0),
 ]
 
 

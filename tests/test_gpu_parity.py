@@ -93,6 +93,11 @@ CASES = [
     ("bf16-k1", 1, 300, 4, 1, 64, 64, 64, 1, "bf16", 1.0),
     ("bf16-d128-k63", 1, 330, 4, 2, 128, 128, 64, 63, "bf16", 1.0),
     ("bf16-w33-k3", 2, 290, 4, 1, 64, 64, 33, 3, "bf16", 1.0),
+    # fp32 at head_dim / feat_dim 128 (the sequential LDS plan of the attention kernel)
+    ("f32-d128", 2, 200, 8, 2, 128, 128, 64, 16, "f32", 1.0),
+    ("f32-d128-f64-w16", 1, 330, 4, 1, 128, 64, 16, 8, "f32", 1.0),
+    ("f32-d64-f128", 1, 290, 4, 1, 64, 128, 64, 4, "f32", 1.0),
+    ("f32-d128-k63", 1, 260, 2, 1, 128, 128, 64, 63, "f32", 1.0),
 ]
 
 
@@ -171,7 +176,7 @@ def test_topk_alone_is_bit_exact():
 
 
 @pytest.mark.parametrize("dt,D,F", [("f32", 64, 64), ("bf16", 64, 64), ("bf16", 128, 128), ("bf16", 64, 128),
-                                    ("bf16", 128, 64)])
+                                    ("bf16", 128, 64), ("f32", 128, 128)])
 def test_feature_map_matches_oracle(dt, D, F):
     _say("np-map", dt, D, F)
     wl, (q, k, v, wp) = synth.small_case(seed=D + F, B=2, T=100, Hq=2, Hkv=2, D=D, F=F, window=64, chunk=64,
@@ -280,16 +285,18 @@ def test_tiny_f32_workload(stress):
     assert ok, (ea, er, nbad)
 
 
-@pytest.mark.parametrize("T", [4352, 16448])
-def test_f32_many_compact_tiles(T):
-    """fp32 at the reference precision with many compact tiles (GQA 4, top_k 8, stress draw):
-    T = 4352 (68 chunks: the 16-chunk scan segment, 9 compact tiles for the last chunk),
-    every output against the chunked oracle; T = 16448 (257 chunks: a second scan round,
-    32 compact tiles), about 70 sampled rows against the per-query oracle. Routing bit-exact
-    on every decided chunk; outputs within 1e-4 and 1e-3 of each row's size."""
-    wl, (q, k, v, wp) = synth.small_case(seed=T % 997, B=1, T=T, Hq=8, Hkv=2, D=64, F=64, window=64, chunk=64,
-                                         top_k=8, dtype="f32", qk_scale=1.0, n_planted=T // 100)
-    _say("f32-many-tiles", T)
+@pytest.mark.parametrize("T,D,k", [(4352, 64, 8), (16448, 64, 8), (4352, 128, 16)])
+def test_f32_many_compact_tiles(T, D, k):
+    """fp32 at the reference precision with many compact tiles (GQA 4, stress draw):
+    T = 4352 (68 chunks: the 16-chunk scan segment; 9 compact tiles for the last chunk at
+    top_k 8, 17 at head_dim 128 and top_k 16), every output against the chunked oracle;
+    T = 16448 (257 chunks: a second scan round, 32 compact tiles), about 70 sampled rows
+    against the per-query oracle. Routing bit-exact on every decided chunk; outputs within
+    1e-4 and 1e-3 of each row's size."""
+    topk = k
+    wl, (q, k, v, wp) = synth.small_case(seed=T % 997 + D, B=1, T=T, Hq=8, Hkv=2, D=D, F=D, window=64, chunk=64,
+                                         top_k=topk, dtype="f32", qk_scale=1.0, n_planted=T // 100)
+    _say("f32-many-tiles", T, D, topk)
     out, s_gpu, idx_gpu = _run(q, k, v, wp, wl)
     s_ref, _ = O.saliency(q, k, wl.window)
     decided, flips = _check_routing(s_gpu, idx_gpu, s_ref, wl)
@@ -297,8 +304,8 @@ def test_f32_many_compact_tiles(T):
     assert decided >= s_ref.shape[1] * (T // 64) // 2
     sel = _sel_from_idx(idx_gpu, T)
     if T <= 4352:
-        ref = O.attend(q, k, v, wp, 64, 64, 8, sel=sel)
-        got, ref = out.reshape(-1, 64), ref.reshape(-1, 64)
+        ref = O.attend(q, k, v, wp, 64, 64, topk, sel=sel)
+        got, ref = out.reshape(-1, D), ref.reshape(-1, D)
     else:
         rows = PC.sample_rows(np.random.default_rng(T), 1, T, 8, 64)
         ref = O.brute_rows(q, k, v, wp, 64, 64, sel, rows)

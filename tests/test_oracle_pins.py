@@ -344,7 +344,8 @@ def test_brute_rows_match_brute():
         np.testing.assert_allclose(got[r], full[b, i, hq], atol=1e-14)
 
 
-@pytest.mark.parametrize("T,w,C,k,G", [(70, 8, 8, 2, 2), (33, 4, 8, 3, 1), (24, 8, 8, 8, 1), (20, 0, 8, 0, 2)])
+@pytest.mark.parametrize("T,w,C,k,G", [(70, 8, 8, 2, 2), (33, 4, 8, 3, 1), (24, 8, 8, 8, 1), (20, 0, 8, 0, 2),
+                                       (61, 12, 8, 2, 2), (50, 16, 8, 3, 1), (45, 9, 8, 8, 1), (40, 20, 8, 2, 1)])
 def test_decode_replay_equals_prefill(T, w, C, k, G):
     q, k_, v, wp = _case(2, T, G, 1, 8, 6, seed=11, scale=1.5)
     want, s_kv, sel = O.attend(q, k_, v, wp, w, C, k, return_routing=True)
