@@ -171,6 +171,113 @@ __device__ __forceinline__ void sm_exp_pv(const f32x4 (&s)[4][QB], const T* lv, 
   }
 }
 
+// x + the sum of the 8 probabilities of a fragment (bf16: four dot2 with (1, 1); fp32: adds)
+template <typename F> __device__ __forceinline__ float row_sum_add(const F& p, float x) {
+  if constexpr (sizeof(p[0]) == 2) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{p[2 * j], p[2 * j + 1]}, one2, x, false);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x += p[j];
+  }
+  return x;
+}
+
+// sm_max with the row sums held as per-lane partials lp (sm_exp_pv_hv) instead of the
+// accumulators' ones block: the same lazy refresh, rescaling o's value blocks and lp.
+template <int D, int QB>
+__device__ __forceinline__ void sm_max_lp(const f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&lp)[QB],
+                                          float (&m_run)[QB], float c1) {
+  bool need_any = false;
+  float alpha[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float tm = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tm = fmaxf(tm, s[kb][qb][i]);
+    tm = xor_max_groups(tm) * c1;
+    const bool need = tm > m_run[qb] + kLazy;
+    alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
+    m_run[qb] = need ? tm : m_run[qb];
+    need_any |= need;
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha[qb];
+      lp[qb] *= alpha[qb];
+    }
+  }
+}
+
+// Scores of one 64-key tile for HV query groups of a wave: every K fragment read from LDS
+// feeds the products of all of them (qk_tile with HV groups).
+template <typename T, int D, int QB, int HV>
+__device__ __forceinline__ void qk_tile_hv(const T* lk, const typename Tr<T>::frag (&qf)[HV][QB][D / 32],
+                                           f32x4 (&s)[HV][4][QB]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[hv][kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const typename Tr<T>::frag ka = Swz<T, D>::load8(lk, kb * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) Tr<T>::mma(s[hv][kb][qb], ka, qf[hv][qb][ks]);
+    }
+  }
+}
+
+// sm_exp_pv for HV query groups: every V^T fragment read from LDS feeds all of them. The
+// row sums are not a ones block of the product here but per-lane partials lp (each lane
+// adds the probabilities it holds, already rounded as the product uses them, by bf16 dot2;
+// the four lane groups are summed once at the end), which frees that block's registers.
+template <typename T, int D, int QB, int HV>
+__device__ __forceinline__ void sm_exp_pv_hv(const f32x4 (&s)[HV][4][QB], const T* lv, f32x4 (&o)[HV][D / 16 + 1][QB],
+                                             float (&lp)[HV][QB], const float (&m_run)[HV][QB], float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  float mq[HV][QB];
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mq[hv][qb] = m_run[hv][qb] == -kInf ? 0.f : m_run[hv][qb];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    frag pf[HV][QB];
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[hv][qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[hv][2 * hs + e / 4][qb][e % 4] * c1 - mq[hv][qb]));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[hv][qb]);
+    }
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = row_sum_add(pf[hv][qb], lp[hv][qb]);
+  }
+}
+
 // Window tiles when the window equals the chunk (w = 64), for a wave whose queries start at
 // QOFF within the chunk. Lane (r16, grp) holds keys kb*16 + 4 grp + i of query
 // QOFF + qb*16 + r16, so a (key block, query block) pair is of one of three kinds, known at
@@ -405,7 +512,12 @@ struct AttnCfg {
   // fits (head_dim 128, or fp32) it takes both slices with twice the waves, so every SIMD
   // still runs two waves and every staged tile serves the whole chunk.
   static constexpr int QS = LDS_BYTES > 80 * 1024 ? 2 : 1;
-  static constexpr int QSPLIT = 64 / QW / QS;  // workgroups per chunk
+  // Query halves per wave. At head_dim 64, where two workgroups share a CU, a wave takes
+  // both 32-query halves of the chunk: every compact K and V^T fragment it reads from LDS
+  // then feeds twice the MFMAs, and the step's fixed costs (copy issue and wait, barrier,
+  // scalar control, LDS latency) are spread over twice the work.
+  static constexpr int HV = (!SEQ && QS == 1 && D == 64) ? 2 : 1;
+  static constexpr int QSPLIT = 64 / QW / QS / HV;  // workgroups per chunk
   static constexpr int NWAVE = NH * QS;        // wave w: head slot w % NH, query slice w / NH
   static constexpr int NTHR = 64 * NWAVE;
   // buffer->LDS instructions each wave issues per compact tile (1 KiB each)
@@ -468,7 +580,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
   const int g = gs * NH + wave % NH;
-  const int qoff = (qsb * C::QS + wave / NH) * QW;  // first query of this wave within the chunk
+  constexpr int HV = C::HV;
+  const int qoff0 = (qsb * C::QS + wave / NH) * QW * HV;  // first query of this wave within the chunk
   const bool head_ok = g < d.G;
   const int hq = h * d.G + (head_ok ? g : d.G - 1);
   const long long T_ = d.T;
@@ -504,10 +617,11 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   //      after the queries and W_h is the same on every path and phi(q) waits for those
   //      alone while the copies are in flight ---------------------------------------------
   // queries: B-operand fragments (SK over d); rows past the sequence end read as zeros
-  frag qf[QB][D / 32];
-  {
-    const long long q0 = t0 + qoff;  // first query row of this wave
-    const int qrow = d.Hq * D;        // elements from one position to the next
+  frag qf[HV][QB][D / 32];  // [query half][16-query block][k slice]
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv) {
+    const long long q0 = t0 + qoff0 + hv * QW;  // first query row of this half
+    const int qrow = d.Hq * D;                   // elements from one position to the next
     const long long nq = T_ - q0 < QW ? T_ - q0 : QW;
     const auto qrs = make_rsrc(q + ((b * T_ + (nq > 0 ? q0 : 0)) * d.Hq + hq) * D,
                                nq > 0 ? static_cast<uint32_t>(((nq - 1) * qrow + D) * static_cast<int>(sizeof(T))) : 0u);
@@ -515,7 +629,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        qf[qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
+        qf[hv][qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
   }
   // W_h rows fb*16 + r16 (A operand of phi(q)): held in registers where they fit, else
   // copied once into compact stage 0 (free until the first compact tile) for all waves
@@ -581,23 +695,25 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     }
   }
 
-  f32x4 o[NB + 1][QB];
-  float m_run[QB];
-  float qn[QB];  // |q| c1: with |k| <= kmax, every logit of a tile is <= qn kmax
+  f32x4 o[HV][NB + 1][QB];
+  float m_run[HV][QB];
+  float qn[HV][QB];  // |q| c1: with |k| <= kmax, every logit of a tile is <= qn kmax
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
-    for (int db = 0; db <= NB; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db <= NB; ++db) o[hv][db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // window = chunk takes a fast path for the masks and handles chunk c-1's linear keys
   // together with its window tile (head_dim 64; at 128 the extra live registers spill)
   const bool fast = D == 64 && win == kChunk && !C::SEQ;
-  frag pq[QB][DF / 32];  // phi(q): B-operand fragments (PK over f)
+  frag pq[HV][QB][DF / 32];  // phi(q): B-operand fragments (PK over f)
   uint64_t selprev;
   // =============================== phase 1: linear attention ===========================
   {
     // phi(q) = |q| m / |m|, m = elu(W_h q) + 1; wfrag(fb, ks) gives the W_h fragment
-    auto phi_q = [&](auto wfrag) {
+    auto phi_q = [&](int hv, auto wfrag) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x4 pacc[DF / 16];
@@ -605,7 +721,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int fb = 0; fb < DF / 16; ++fb) {
         pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) TT::mma(pacc[fb], wfrag(fb, ks), qf[qb][ks]);
+        for (int ks = 0; ks < D / 32; ++ks) TT::mma(pacc[fb], wfrag(fb, ks), qf[hv][qb][ks]);
       }
       float m2 = 0.f, x2 = 0.f;
 #pragma unroll
@@ -621,34 +737,39 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xv = TT::to_f(qf[qb][ks][e]);
+          const float xv = TT::to_f(qf[hv][qb][ks][e]);
           x2 += xv * xv;
         }
       m2 = xor_sum_groups(m2);
       x2 = xor_sum_groups(x2);
-      qn[qb] = __builtin_amdgcn_sqrtf(x2) * c1 * 1.001f;  // |q| in logit units, with slack for rounding
+      qn[hv][qb] = __builtin_amdgcn_sqrtf(x2) * c1 * 1.001f;  // |q| in logit units, with slack for rounding
       const float sc = norm_ratio(x2, m2);
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pq[qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
+        for (int e = 0; e < 8; ++e) pq[hv][qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
     }
     };
     if constexpr (W_EARLY) {
       // phi(q) before the wait (it overlaps the copies); keep the scheduler from moving it
       // past the wait
-      phi_q([&](int fb, int ks) { return wq[fb][ks]; });
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv) phi_q(hv, [&](int fb, int ks) { return wq[fb][ks]; });
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every region copied at the start has landed
     } else if constexpr (W_GLOBAL) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // the linear-attention tiles have landed
-      phi_q([&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8); });
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+        phi_q(hv, [&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8); });
     } else {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // every region copied at the start has landed, W_h among them
-      phi_q([&](int fb, int ks) { return Swz<T, D>::load8(L + C::stage_off(0), fb * 16 + r16, ks * 32 + grp * 8); });
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+        phi_q(hv, [&](int fb, int ks) { return Swz<T, D>::load8(L + C::stage_off(0), fb * 16 + r16, ks * 32 + grp * 8); });
       __syncthreads();  // every wave is done with W_h: stage 0 takes compact tile 0
       dk.issue(L + C::stage_off(0), make_rsrc(kb_ptr, nt_comp > 0 ? C::KT * static_cast<int>(sizeof(T)) : 0u), 0);
       dv.issue(L + C::stage_off(0) + C::KT, make_rsrc(vb_ptr, nt_comp > 0 ? C::VT * static_cast<int>(sizeof(T)) : 0u), 0);
@@ -656,6 +777,14 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
 
+  }
+
+  // ===================== per query half: phase 1 (linear attention), phase 2a (window) ==
+  // Each half runs its prefix read-out, its linear keys and its window tiles before the
+  // next one starts, so only one half's window scores are live at a time.
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv) {
+  {
     // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)]: each A-operand fragment
     // (row d, the 8 features a lane group holds) is 8 consecutive elements
     if (c >= 2) {
@@ -669,12 +798,12 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
           else
             sa = TT::load8(Sg + (db * 16 + r16) * DF + fs * 32 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], sa, pq[qb][fs]);
+          for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], sa, pq[hv][qb][fs]);
         }
         // the denominator phi(q).z on the row-sum block: every row of its A operand is z,
         // so each of its entries ends up holding the whole dot product
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], zf[fs], pq[qb][fs]);
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][NB][qb], zf[fs], pq[hv][qb][fs]);
       }
     }
     // linear keys of chunk c-1 (p <= r + 64 - w, unselected) and of chunk c (p <= r - w);
@@ -685,6 +814,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 #pragma unroll
     for (int cur = 0; cur < 2; ++cur) {
       if (fast || (cur == 0 ? !has_prev : !la_cur)) continue;  // uniform
+      const int qoff = qoff0 + hv * QW;
       const T* lk = L + (cur == 0 ? C::R_PHIP : C::R_PHIC);
       const T* lv = L + (cur == 0 ? C::R_VP : C::R_VC);
       f32x4 ls[4][QB];
@@ -696,7 +826,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
         for (int fs = 0; fs < DF / 32; ++fs) {
           const frag fa = SF::load8(lk, kb * 16 + r16, fs * 32 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+          for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[hv][qb][fs]);
         }
       }
       const uint32_t selw = cur ? 0u : bits_word(selprev);
@@ -723,28 +853,27 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
         for (int ks = 0; ks < 2; ++ks) {
           const frag va = SV::load8(lv, db * 16 + r16, ks * 32 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[ks][qb]);
+          for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[ks][qb]);
         }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], ones, pf[ks][qb]);  // their denominator
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][NB][qb], ones, pf[ks][qb]);  // their denominator
     }
     // the linear branch becomes one online-softmax entry: log-weight log2(D), value N / D
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float dt = o[NB][qb][0];
+      const float dt = o[hv][NB][qb][0];
       const float inv = dt > 0.f ? __builtin_amdgcn_rcpf(dt) : 0.f;
 #pragma unroll
-      for (int db = 0; db < NB; ++db) o[db][qb] *= inv;
-      m_run[qb] = dt > 0.f ? __log2f(dt) : -kInf;
+      for (int db = 0; db < NB; ++db) o[hv][db][qb] *= inv;
+      m_run[hv][qb] = dt > 0.f ? __log2f(dt) : -kInf;
       const float l0 = dt > 0.f ? 1.f : 0.f;
-      o[NB][qb] = f32x4{l0, l0, l0, l0};
+      o[hv][NB][qb] = f32x4{l0, l0, l0, l0};
     }
   }
-
   // =============================== phase 2: softmax tiles ==============================
-  if constexpr (C::SEQ) {  // K of chunks c and c-1 over the phi(K) regions phase 1 is done with
+  if constexpr (C::SEQ) {  // (one query half in this plan)  // K of chunks c and c-1 over the phi(K) regions phase 1 is done with
     __syncthreads();
     const int kvs = d.Hkv * D;
     const long long tp = has_prev ? t0 - kChunk : t0;
@@ -754,37 +883,42 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     __syncthreads();
   }
   // 2a. the window: chunk c (r - w < p <= r), chunk c-1 (p > r + 64 - w, or selected)
+  {
+  const int qoff = qoff0 + hv * QW;
   if (fast) {
     if (qoff == 0)
       window_fast<T, D, DF, QB, 0>(L + C::R_KC, L + C::R_VC, L + C::R_KP, L + C::R_PHIP, L + C::R_VP, has_prev, selprev,
-                                   qf, pq, o, m_run, c1);
+                                   qf[hv], pq[hv], o[hv], m_run[hv], c1);
     else
       window_fast<T, D, DF, QB, QW>(L + C::R_KC, L + C::R_VC, L + C::R_KP, L + C::R_PHIP, L + C::R_VP, has_prev,
-                                    selprev, qf, pq, o, m_run, c1);
+                                    selprev, qf[hv], pq[hv], o[hv], m_run[hv], c1);
   } else if (win >= 1) {
     f32x4 s[4][QB];
     uint32_t kw[QB];
-    qk_tile<T, D, QB>(L + C::R_KC, qf, s);
+    qk_tile<T, D, QB>(L + C::R_KC, qf[hv], s);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int r = qoff + qb * 16 + r16;
       kw[qb] = range_word(r - win + 1, r);
     }
     mask_tile<QB>(s, kw);
-    sm_max<D, QB>(s, o, m_run, c1);
-    sm_exp_pv<T, D, QB>(s, L + C::R_VC, o, m_run, c1);
+    sm_max<D, QB>(s, o[hv], m_run[hv], c1);
+    sm_exp_pv<T, D, QB>(s, L + C::R_VC, o[hv], m_run[hv], c1);
     if (has_prev) {
       const uint32_t selw = bits_word(selprev);
-      qk_tile<T, D, QB>(L + C::R_KP, qf, s);
+      qk_tile<T, D, QB>(L + C::R_KP, qf[hv], s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int r = qoff + qb * 16 + r16;
         kw[qb] = range_word(r + 65 - win, 63) | selw;
       }
       mask_tile<QB>(s, kw);
-      sm_max<D, QB>(s, o, m_run, c1);
-      sm_exp_pv<T, D, QB>(s, L + C::R_VP, o, m_run, c1);
+      sm_max<D, QB>(s, o[hv], m_run[hv], c1);
+      sm_exp_pv<T, D, QB>(s, L + C::R_VP, o[hv], m_run[hv], c1);
     }
+  }
+  }
+
   }
 
   // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
@@ -803,12 +937,14 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     // which only grows), so a step tests one scalar bit; tiles from 256 on are always checked.
     uint64_t mayfar[4];
     {
-      float qmax = qn[0], mmin = m_run[0];
+      float qmax = qn[0][0], mmin = m_run[0][0];
 #pragma unroll
-      for (int qb = 1; qb < QB; ++qb) {
-        qmax = fmaxf(qmax, qn[qb]);
-        mmin = fminf(mmin, m_run[qb]);
-      }
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          qmax = fmaxf(qmax, qn[hv][qb]);
+          mmin = fminf(mmin, m_run[hv][qb]);
+        }
       qmax = wave_max64(qmax);
       mmin = -wave_max64(-mmin);
 #pragma unroll
@@ -827,7 +963,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
         f32x4 sc[4][QB];
-        qk_tile<T, D, QB>(L + C::stage_off(t & 1), qf, sc);
+        qk_tile<T, D, QB>(L + C::stage_off(t & 1), qf[0], sc);
         const int nk = n_comp - t * 64;
         if (nk < 64) {
           uint32_t kw[QB];
@@ -838,19 +974,72 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
         }
         const int tj = t >> 6;
         const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-        if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(sc, o, m_run, c1);
-        sm_exp_pv<T, D, QB>(sc, L + C::stage_off(t & 1) + C::KT, o, m_run, c1);
+        if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(sc, o[0], m_run[0], c1);
+        sm_exp_pv<T, D, QB>(sc, L + C::stage_off(t & 1) + C::KT, o[0], m_run[0], c1);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's reads of the stage are done (and no copy is in flight)
         lds_barrier();
         if (t + 2 < nt_comp) issue(t + 2, t & 1);
       }
+    } else if constexpr (HV == 2) {
+      // Both query halves per step, each K and V^T fragment read once for both. Tile t in
+      // stage t % 4; tile 0 landed with the fixed part, tiles 1 and 2 are issued once every
+      // wave is done with the fixed regions, tile t + 3 in step t (into the stage of tile
+      // t - 1, free after the step's barrier). Step t waits for its own copies of tile t
+      // (those of tiles t + 1 and t + 2 may still be in flight).
+      if constexpr (!W_EARLY) {  // tile 0 was copied after phi(q)
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __syncthreads();
+      if (1 < nt_comp) issue(1, 1);
+      if (2 < nt_comp) issue(2, 2);
+      // the row sums as per-lane partials: lane group 0 starts from the whole sum so far
+      float lp[HV][QB];
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = grp == 0 ? o[hv][NB][qb][0] : 0.f;
+      for (int t = 0; t < nt_comp; ++t) {
+        if (t + 2 < nt_comp)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::NL));
+        else if (t + 1 < nt_comp)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();
+        if (t + 3 < nt_comp) issue(t + 3, (t + 3) & 3);
+        f32x4 sc[HV][4][QB];
+        qk_tile_hv<T, D, QB, HV>(L + C::stage_off(t & 3), qf, sc);
+        const int nk = n_comp - t * 64;
+        if (nk < 64) {
+          uint32_t kw[QB];
+          const uint32_t rw = range_word(0, nk - 1);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
+#pragma unroll
+          for (int hv = 0; hv < HV; ++hv) mask_tile<QB>(sc[hv], kw);
+        }
+        const int tj = t >> 6;
+        const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
+        if ((fw >> (t & 63)) & 1ull) {
+#pragma unroll
+          for (int hv = 0; hv < HV; ++hv) sm_max_lp<D, QB>(sc[hv], o[hv], lp[hv], m_run[hv], c1);
+        }
+        sm_exp_pv_hv<T, D, QB, HV>(sc, L + C::stage_off(t & 3) + C::KT, o, lp, m_run, c1);
+      }
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float l = xor_sum_groups(lp[hv][qb]);
+          o[hv][NB][qb] = f32x4{l, l, l, l};
+        }
     } else {
     f32x4 sa[4][QB], sb[4][QB];
     if constexpr (!W_EARLY) {  // tile 0 was copied after phi(q)
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    qk_tile<T, D, QB>(L + C::stage_off(0), qf, sa);  // tile 0 has landed
+    qk_tile<T, D, QB>(L + C::stage_off(0), qf[0], sa);  // tile 0 has landed
     __syncthreads();
 #pragma unroll
     for (int t = 1; t < 4; ++t)
@@ -872,9 +1061,9 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       }
       const int tj = t >> 6;
       const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-      if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(s_cur, o, m_run, c1);
-      qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf, s_next);  // after the last tile: unused
-      sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o, m_run, c1);
+      if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(s_cur, o[0], m_run[0], c1);
+      qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf[0], s_next);  // after the last tile: unused
+      sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o[0], m_run[0], c1);
     };
     for (int t = 0; t < nt_comp; t += 2) {
       step(t, sa, sb);
@@ -886,17 +1075,19 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   // ---- epilogue: divide by the shared normaliser, write [B,T,Hq,D] ------------------
   T* out = static_cast<T*>(a.out);
 #pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = o[NB][qb][0];
+    const float lt = o[hv][NB][qb][0];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int r = qoff + qb * 16 + r16;
+    const int r = qoff0 + hv * QW + qb * 16 + r16;
     if (head_ok && r < nvalid) {
       T* dst = out + ((b * T_ + t0 + r) * d.Hq + hq) * D + 4 * grp;
 #pragma unroll
       for (int db = 0; db < NB; ++db) {
         typename TT::quad ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = TT::from_f(o[db][qb][i] * inv);
+        for (int i = 0; i < 4; ++i) ov[i] = TT::from_f(o[hv][db][qb][i] * inv);
         *reinterpret_cast<typename TT::quad*>(dst + db * 16) = ov;
       }
     }
