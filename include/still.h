@@ -96,7 +96,9 @@ enum {
 };
 
 /* Layer configuration. Supported by the kernels: chunk = 64; head_dim in {64, 128};
- * feat_dim in {64, 128}; 0 <= window <= chunk; 0 <= top_k <= chunk; top_k = 0 when
+ * feat_dim in {64, 128}; 0 <= window <= 2 * chunk (a window longer than a chunk reaches into
+ * L = ceil(window / chunk) earlier chunks, which the kernels take with per-query masks; a
+ * decode cache then holds L + 1 chunks of raw rows); 0 <= top_k <= chunk; top_k = 0 when
  * window = 0; n_q_heads a multiple of n_kv_heads; seq_len >= 1, with the chunk states of
  * one (batch, KV head), ceil(seq_len/64) * (head_dim*feat_dim + feat_dim) elements of the
  * layer's dtype, under 2 GiB (about 16M tokens at 64/64 and 4M at 128/128 in bf16).
@@ -275,8 +277,8 @@ size_t still_backward_workspace_bytes(const still_config* cfg);
  *   dq       like q; dk, dv like k (dtype, written)
  *   dw_phi   [n_kv_heads, feat_dim, head_dim] fp32 (written, not accumulated)
  *   workspace  device scratch of at least still_backward_workspace_bytes(cfg) bytes.
- * Supported for head_dim = feat_dim = 64 (both dtypes) and head_dim = feat_dim = 128 (bf16);
- * STILL_ERR_UNSUPPORTED otherwise. Every sum runs in a fixed order, so repeated calls give
+ * Supported for head_dim = feat_dim = 64 (both dtypes) and head_dim = feat_dim = 128 (bf16),
+ * window <= chunk; STILL_ERR_UNSUPPORTED otherwise. Every sum runs in a fixed order, so repeated calls give
  * identical bits. Rows whose normaliser is 0 (output
  * 0) get no gradient. Returns STILL_OK or a negative status. */
 int still_backward(const still_config* cfg, const void* q, const void* k, const void* v,

@@ -45,7 +45,7 @@ int check_cfg(const still_config* c, bool use_seq) {
   if (c->head_dim < 1 || c->feat_dim < 1 || c->chunk < 1) return STILL_ERR_INVALID_ARG;
   if (c->window < 0 || c->top_k < 0 || c->top_k > c->chunk) return STILL_ERR_INVALID_ARG;
   if (c->window == 0 && c->top_k != 0) return STILL_ERR_INVALID_ARG;
-  if (c->chunk != 64 || c->window > c->chunk) return STILL_ERR_UNSUPPORTED;
+  if (c->chunk != 64 || c->window > still::kMaxWindow) return STILL_ERR_UNSUPPORTED;
   if (!still::shape_supported(c->dtype == STILL_BF16, c->head_dim, c->feat_dim)) return STILL_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(c->batch) * c->n_kv_heads > 65535) return STILL_ERR_UNSUPPORTED;
   if (use_seq) {
@@ -161,11 +161,12 @@ CacheLayout cache_layout(const still_config* c, int64_t max_tokens) {
   };
   L.sel_k = take(bh * L.sel_capacity * D * es);
   L.sel_v = take(bh * L.sel_capacity * D * es);
-  L.ring_k = take(bh * 2 * 64 * D * es);
-  L.ring_v = take(bh * 2 * 64 * D * es);
+  const size_t nr = still::band_chunks(c->window) + 1;  // ring slots: chunks c-L .. c
+  L.ring_k = take(bh * nr * 64 * D * es);
+  L.ring_v = take(bh * nr * 64 * D * es);
   L.state_s = take(bh * F * D * sizeof(float));
   L.state_z = take(bh * F * sizeof(float));
-  L.sel_mask = take(bh * 2 * sizeof(uint64_t));
+  L.sel_mask = take(bh * nr * sizeof(uint64_t));
   L.cur_sal = take(bh * 64 * sizeof(float));
   L.total = off;
   return L;
@@ -260,6 +261,7 @@ int check_bwd_cfg(const still_config* c) {
   const int st = check_cfg(c, true);
   if (st != STILL_OK) return st;
   if (!still::bwd_shape_supported(c->dtype == STILL_BF16, c->head_dim, c->feat_dim)) return STILL_ERR_UNSUPPORTED;
+  if (c->window > c->chunk) return STILL_ERR_UNSUPPORTED;  // the backward's band is chunks c-1 and c
   return STILL_OK;
 }
 
@@ -563,7 +565,8 @@ int decode_plan(const still_config* cfg, const still_cache* cache, const void* q
   a.d = dims_of(&c1);
   a.pos = cache->n_tokens;
   const int64_t chunk = cache->n_tokens / 64;
-  a.nsel = static_cast<int>((chunk >= 1 ? chunk - 1 : 0) * cfg->top_k);
+  const int bl = still::band_chunks(cfg->window);  // compact rows: chunks <= chunk - bl - 1
+  a.nsel = static_cast<int>((chunk >= bl ? chunk - bl : 0) * cfg->top_k);
   const int ntiles = (a.nsel + 63) / 64;
   const int bhn = cfg->batch * cfg->n_kv_heads;
   int nsplit = (kSplitTarget + bhn - 1) / bhn;

@@ -470,6 +470,97 @@ __device__ __forceinline__ void window_fast(const T* lkc, const T* lvc, const T*
   }
 }
 
+// One band chunk c-l (l >= 2, windows longer than a chunk) for 16-query blocks starting at
+// qoff: key p of the chunk is in query r's window when p > r + lim (lim = 64 l - w); it is a
+// softmax key when in the window or selected (bit p of sel), a linear key otherwise. As for
+// chunk c-1 in window_fast, one P carries both kinds: 2^(a c1 - m) for softmax keys and
+// phi(q).phi(k) 2^-m for linear keys, with the row-sum block adding both denominators. The
+// masks are runtime values here. lk, lf, lv: K, phi(K) and V^T tiles of the chunk.
+template <typename T, int D, int DF, int QB>
+__device__ __forceinline__ void band_tile(const T* lk, const T* lf, const T* lv, int qoff, int lim, uint64_t sel,
+                                          const typename Tr<T>::frag (&qf)[QB][D / 32],
+                                          const typename Tr<T>::frag (&pq)[QB][DF / 32],
+                                          f32x4 (&o)[D / 16 + 1][QB], float (&m_run)[QB], float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  constexpr int NB = D / 16;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  f32x4 s[4][QB], ls[4][QB];
+  qk_tile<T, D, QB>(lk, qf, s);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fs = 0; fs < DF / 32; ++fs) {
+      const frag fa = Swz<T, DF>::load8(lf, kb * 16 + r16, fs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+    }
+  }
+  const uint32_t selw = bits_word(sel);
+  float lmax[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint32_t kw = range_word(qoff + qb * 16 + r16 + lim + 1, 63) | selw;  // softmax keys
+    lmax[qb] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool sa = (kw >> (kb * 4 + i)) & 1u;
+        s[kb][qb][i] = sa ? s[kb][qb][i] : -kInf;
+        ls[kb][qb][i] = sa ? 0.f : ls[kb][qb][i];
+        lmax[qb] = fmaxf(lmax[qb], ls[kb][qb][i]);
+      }
+  }
+  sm_max<D, QB>(s, o, m_run, c1);
+  bool lfar = false;
+  float lm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    lm[qb] = xor_max_groups(lmax[qb]);
+    lfar |= lm[qb] > __builtin_amdgcn_exp2f(m_run[qb] + kLazy);
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(lfar) != 0, 0)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ml = __log2f(lm[qb]);
+      if (ml > m_run[qb] + kLazy) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - ml);
+#pragma unroll
+        for (int db = 0; db <= NB; ++db) o[db][qb] *= alpha;
+        m_run[qb] = ml;
+      }
+    }
+  }
+  float sc2[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) sc2[qb] = __builtin_amdgcn_exp2f(-m_run[qb]);
+  frag one;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) one[e] = TT::from_f(1.0f);
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    frag pf[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kb = 2 * hs + e / 4;
+        pf[qb][e] = TT::from_f(ls[kb][qb][e % 4] * sc2[qb] + __builtin_amdgcn_exp2f(s[kb][qb][e % 4] * c1 - m_run[qb]));
+      }
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(o[db][qb], va, pf[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) TT::mma(o[NB][qb], one, pf[qb]);
+  }
+}
+
 template <typename T, int D, int DF, int NH>
 struct AttnCfg {
   static constexpr int QW = 32;                // queries per wave (one query slice)
@@ -502,6 +593,10 @@ struct AttnCfg {
   static constexpr int SEQ_FIXED = 2 * VT + (FT > KT ? 2 * FT : 2 * KT);
   static constexpr int LDS_ELEMS = SEQ ? (SEQ_FIXED > 2 * STAGE ? SEQ_FIXED : 2 * STAGE) : R_P0 + STAGE;
   static constexpr int LDS_BYTES = LDS_ELEMS * static_cast<int>(sizeof(T));
+  // band chunks c-2 .. c-BL (windows longer than a chunk) staged one at a time once the
+  // fixed part is done with its regions, before any compact tile but tile 0 is issued
+  static constexpr int R_BV = 0, R_BK = VT, R_BF = VT + KT;
+  static_assert(VT + KT + FT <= (SEQ ? LDS_ELEMS : R_ST), "band tiles stay inside the fixed regions");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS plan must fit a CU");
   static __device__ __forceinline__ int stage_off(int s) {
     if constexpr (SEQ) return s * STAGE;
@@ -545,7 +640,9 @@ template <typename T> __device__ __forceinline__ typename Tr<T>::frag frag_of(co
   return y;
 }
 
-template <typename T, int D, int DF, int NH>
+// BAND: windows longer than a chunk (band chunks c-2 .. c-BL); a separate instantiation, so the
+// kernels for windows up to a chunk keep their register plan
+template <typename T, int D, int DF, int NH, bool BAND>
 __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, DF, NH>::QS)) void attn_kernel(AttnArgs a) {
   using C = AttnCfg<T, D, DF, NH>;
   constexpr int QB = C::QB, QW = C::QW, NW = C::NWAVE;
@@ -591,7 +688,10 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   const int win = d.window;
   const bool has_prev = c >= 1;
   const bool la_cur = win < kChunk;  // chunk c holds linear keys (p <= r - w)
-  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;  // compact rows of chunks <= c-2
+  // chunks c-BL .. c-1 are handled with per-query masks; the compact rows and the prefix
+  // state cover chunks <= c-BL-1
+  const int BL = BAND ? band_chunks(win) : 1;
+  const int n_comp = c >= BL + 1 ? (c - BL) * d.topk : 0;  // compact rows of chunks <= c-BL-1
   const int nt_comp = (n_comp + 63) / 64;
   const T* kb_ptr = ksel + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
   const T* vb_ptr = vselT + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
@@ -643,12 +743,13 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) wq[fb][ks] = TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8);
   }
-  // z of the prefix state of chunks <= c-2 (8 consecutive permuted features per lane group):
-  // the A operand of the denominator, the same in every row
-  const T* Sg = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (c >= 2 ? c - 2 : 0)) * d.R;
+  // z of the prefix state of chunks <= c-BL-1 (8 consecutive permuted features per lane
+  // group): the A operand of the denominator, the same in every row
+  const bool has_state = c >= BL + 1;
+  const T* Sg = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (has_state ? c - BL - 1 : 0)) * d.R;
   frag zf[DF / 32];
   {
-    const auto zrs = make_rsrc(Sg + DF * D, c >= 2 ? DF * static_cast<uint32_t>(sizeof(T)) : 0u);
+    const auto zrs = make_rsrc(Sg + DF * D, has_state ? DF * static_cast<uint32_t>(sizeof(T)) : 0u);
 #pragma unroll
     for (int fs = 0; fs < DF / 32; ++fs) zf[fs] = TT::bload8(zrs, (fs * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
   }
@@ -671,7 +772,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
     if constexpr (!C::SEQ) dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
-      dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, c >= 2 ? D : 0);
+      dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, has_state ? D : 0);
     if constexpr (C::SEQ) {
       // the window's K tiles come after phase 1, over the phi(K) regions
     } else if constexpr (W_EARLY) {
@@ -785,9 +886,9 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 #pragma unroll
   for (int hv = 0; hv < HV; ++hv) {
   {
-    // prefix state of chunks <= c-2, stored as S^T[d][pk_pos(f)]: each A-operand fragment
+    // prefix state of chunks <= c-BL-1, stored as S^T[d][pk_pos(f)]: each A-operand fragment
     // (row d, the 8 features a lane group holds) is 8 consecutive elements
-    if (c >= 2) {
+    if (has_state) {
 #pragma unroll
       for (int fs = 0; fs < DF / 32; ++fs) {
 #pragma unroll
@@ -921,7 +1022,25 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 
   }
 
-  // 2b. the compact cache: selected rows of chunks <= c-2, unmasked except a ragged end.
+  // 2c. band chunks c-2 .. c-BL (windows longer than a chunk): each staged into the fixed
+  //     regions, then both kinds of keys for every query half
+  if constexpr (BAND)
+  for (int l = 2; l <= BL && l <= c; ++l) {  // uniform
+    __syncthreads();  // every wave is done with the fixed regions (or the previous band chunk)
+    const long long tb = t0 - static_cast<long long>(l) * kChunk;
+    dma_tile<T, D, 64, NW>(L + C::R_BK, kk + ((b * T_ + tb) * d.Hkv + h) * D, d.Hkv * D, 64);
+    dma_tile<T, DF, 64, NW>(L + C::R_BF, phik + (static_cast<long long>(bh) * T_ + tb) * DF, DF, 64);
+    dma_tile<T, 64, D, NW>(L + C::R_BV, vT + (static_cast<long long>(bh) * d.nC + (c - l)) * D * 64, 64, D);
+    const uint64_t sel = a.selmask[static_cast<long long>(bh) * d.nC + (c - l)];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+      band_tile<T, D, DF, QB>(L + C::R_BK, L + C::R_BF, L + C::R_BV, qoff0 + hv * QW, l * kChunk - win, sel, qf[hv],
+                              pq[hv], o[hv], m_run[hv], c1);
+  }
+
+  // 2b. the compact cache: selected rows of chunks <= c-BL-1, unmasked except a ragged end.
   //     Tile t lives in stage t % 4. Tile 0 was copied at the start; tiles 1..3 go into
   //     the fixed regions once every wave is done with them, and tile t+3 is issued in step
   //     t, two steps ahead of its first use. In step t each wave waits for its own copies of
@@ -1094,16 +1213,21 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   }
 }
 
-template <typename T, int D, int DF, int NH>
-static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
+template <typename T, int D, int DF, int NH, bool BAND>
+static hipError_t attn_nhb(const AttnArgs& a, hipStream_t s) {
   using C = AttnCfg<T, D, DF, NH>;
   const int P = a.d.B * a.d.Hkv * a.gsplit * C::QSPLIT;
   dim3 grid(a.d.nC * P);
   if (C::LDS_BYTES > 65536)  // opt in to more than 64 KiB of LDS (gfx950 has 160 KiB per CU)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, NH>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, NH, BAND>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  hipLaunchKernelGGL((attn_kernel<T, D, DF, NH>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
+  hipLaunchKernelGGL((attn_kernel<T, D, DF, NH, BAND>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int DF, int NH>
+static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
+  return band_chunks(a.d.window) >= 2 ? attn_nhb<T, D, DF, NH, true>(a, s) : attn_nhb<T, D, DF, NH, false>(a, s);
 }
 
 template <typename T, int D, int DF>

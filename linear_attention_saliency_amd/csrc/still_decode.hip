@@ -10,13 +10,13 @@
 //                        for each of the G query heads of the group. This is the only part
 //                        whose bytes grow with the context; it is HBM-bound.
 //   decode_token_kernel  one workgroup: writes the token into the ring of raw rows (chunks
-//                        c-1 and c), computes its Self-Saliency Score with the prefill's
+//                        c-L .. c, L = band_chunks(w)), computes its Self-Saliency Score with the prefill's
 //                        routine (so routing is bit-identical to a prefill of the same
 //                        tokens), the softmax over the ring keys in the softmax set, the
 //                        NP-Map linear-attention term (prefix state plus the ring keys
 //                        outside the softmax set), merges all of it with the split partials
 //                        under one normaliser and writes the outputs. When the token completes
-//                        chunk c it picks that chunk's top_k and folds chunk c-1: the selected
+//                        chunk c it picks that chunk's top_k and folds chunk c-L: the selected
 //                        rows are appended to the compact cache, the others are added to the
 //                        state (sum phi(k) v^T, sum phi(k)).
 // cache_export_kernel leaves a cache as these kernels expect it after a prefill of T tokens.
@@ -198,38 +198,45 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------------ token kernel
 
-template <typename T, int D, int DF>
+// LDS plan of the token kernel for a ring of NR = BL + 1 chunks (RW = 64 NR ring rows). The
+// softmax logits (ex) reuse the phi(K) rows' space: phi(K) is done with before the logits
+// are written, and written again only after the last read of the logits.
+template <typename T, int D, int DF, int BL>
 struct TokLds {
   static constexpr int KP = DF + 1;  // padded phi row (conflict-free column reads)
+  static constexpr int RW = 64 * (BL + 1);
+  static_assert(kMaxGroup * RW <= 64 * KP, "the logits fit in the phi(K) rows' space");
   // the ring's V rows are staged in LDS where the whole plan fits the CU's 160 KiB, else
-  // read from the ring in memory (fp32 at head_dim = feat_dim = 128)
-  static constexpr size_t fixed = 129 * D * sizeof(T) + kMaxGroup * (D + DF) * 4 + 64 * KP * 4 + 2 * kMaxGroup * 128 * 4 +
-                                  (256 + 64 + 5 * kMaxGroup) * 4;
-  static constexpr bool VT_LDS = fixed + 128 * D * sizeof(T) <= 160 * 1024;
-  static constexpr size_t kt = 0;                                     // Swz<T,D>, 129 rows
-  static constexpr size_t vt = kt + 129 * D * sizeof(T);              // [128][D] T (VT_LDS)
-  static constexpr size_t qs = vt + (VT_LDS ? 128 * D * sizeof(T) : 0);  // [16][D] f32
+  // read from the ring in memory
+  static constexpr size_t fixed = (RW + 1) * D * sizeof(T) + kMaxGroup * (D + DF) * 4 + 64 * KP * 4 +
+                                  kMaxGroup * RW * 4 + (256 + 64 + 5 * kMaxGroup) * 4;
+  static constexpr bool VT_LDS = fixed + RW * D * sizeof(T) <= 160 * 1024;
+  static constexpr size_t kt = 0;                                     // Swz<T,D>, RW + 1 rows
+  static constexpr size_t vt = kt + (RW + 1) * D * sizeof(T);         // [RW][D] T (VT_LDS)
+  static constexpr size_t qs = vt + (VT_LDS ? RW * D * sizeof(T) : 0);  // [16][D] f32
   static constexpr size_t phq = qs + kMaxGroup * D * 4;               // [16][DF]
   static constexpr size_t phk = phq + kMaxGroup * DF * 4;             // [64][KP]
-  static constexpr size_t wla = phk + 64 * KP * 4;                    // [16][128]
-  static constexpr size_t ex = wla + kMaxGroup * 128 * 4;             // [16][128]
-  static constexpr size_t m2part = ex + kMaxGroup * 128 * 4;          // [256]
+  static constexpr size_t ex = phk;                                   // [16][RW] over phk
+  static constexpr size_t wla = phk + 64 * KP * 4;                    // [16][RW]
+  static constexpr size_t m2part = wla + kMaxGroup * RW * 4;          // [256]
   static constexpr size_t xn2 = m2part + 256 * 4;                     // [64]
   static constexpr size_t gstat = xn2 + 64 * 4;                       // [5][16]
   static constexpr size_t bytes = gstat + 5 * kMaxGroup * 4;
-  static_assert(bytes == fixed + (VT_LDS ? 128 * D * sizeof(T) : 0), "layout and budget agree");
+  static_assert(bytes == fixed + (VT_LDS ? RW * D * sizeof(T) : 0), "layout and budget agree");
   static_assert(bytes <= 160 * 1024, "the token kernel's LDS must fit a CU");
 };
 
-// One workgroup per (b, KV head). LDS tile row t holds the key at position 64(c-1) + t:
-// rows 0..63 are chunk c-1 (zero when c = 0), rows 64..64+r chunk c up to the new token,
-// the rest zero. Query head g of the group is h*G + g.
-template <typename T, int D, int DF>
+// One workgroup per (b, KV head). LDS tile row t holds the key at position 64(c-BL) + t:
+// rows 64(BL-l) .. 64(BL-l)+63 are chunk c-l (zero when c < l), rows 64 BL .. 64 BL + r
+// chunk c up to the new token, the rest zero. Chunk x lives in ring slot x mod (BL + 1).
+// Query head g of the group is h*G + g.
+template <typename T, int D, int DF, int BL>
 __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, D>;
-  using L = TokLds<T, D, DF>;
+  using L = TokLds<T, D, DF, BL>;
+  constexpr int NR = BL + 1, RW = L::RW;
   constexpr int V8 = D / 8;
   constexpr int FPW = DF / 64;
   constexpr int KP = L::KP;
@@ -254,26 +261,31 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const long long pos = a.pos, c = pos / 64;
   const int r = static_cast<int>(pos % 64);
-  const int slot_cur = static_cast<int>(c & 1), slot_prev = slot_cur ^ 1;
-  const bool has_prev = c >= 1;
+  auto slot_of = [&](long long ch) { return static_cast<int>(ch % NR); };  // ch >= 0
+  const int slot_cur = slot_of(c);
   const float scale = kLog2e / sqrtf(static_cast<float>(D));
 
   const T* q = static_cast<const T*>(a.q) + static_cast<long long>(b * d.Hq + h * G) * D;
   const T* knew = static_cast<const T*>(a.k) + static_cast<long long>(b * d.Hkv + h) * D;
   const T* vnew = static_cast<const T*>(a.v) + static_cast<long long>(b * d.Hkv + h) * D;
   const T* wh = static_cast<const T*>(a.w) + static_cast<long long>(h) * DF * D;
-  T* ring_k = static_cast<T*>(a.c.ring_k) + static_cast<long long>(bh) * 2 * 64 * D;
-  T* ring_v = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * 2 * 64 * D;
-  const uint64_t prev_mask = has_prev ? a.c.sel_mask[bh * 2 + slot_prev] : 0ull;
-  // element dd of ring row `row` (rows 0..63 chunk c-1, 64..127 chunk c; the new token at
-  // row 64 + r, later rows zero), from LDS or from the ring in memory
+  T* ring_k = static_cast<T*>(a.c.ring_k) + static_cast<long long>(bh) * NR * 64 * D;
+  T* ring_v = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * NR * 64 * D;
+  // selection of band chunk c-l (l = 1 .. BL; none before the sequence)
+  uint64_t band_mask[BL + 1];
+#pragma unroll
+  for (int l = 1; l <= BL; ++l) band_mask[l] = c >= l ? a.c.sel_mask[bh * NR + slot_of(c - l)] : 0ull;
+  // element dd of ring row `row` (rows 64(BL-l).. chunk c-l, 64 BL.. chunk c; the new token at
+  // row 64 BL + r, later rows zero), from LDS or from the ring in memory
   auto vring = [&](int row, int dd) -> float {
     if constexpr (L::VT_LDS) {
       return TT::to_f(vt[row * D + dd]);
     } else {
-      if (row < 64) return has_prev ? TT::to_f(ring_v[(slot_prev * 64 + row) * D + dd]) : 0.f;
-      if (row < 64 + r) return TT::to_f(ring_v[(slot_cur * 64 + row - 64) * D + dd]);
-      return row == 64 + r ? TT::to_f(vnew[dd]) : 0.f;
+      const long long ch = c - BL + row / 64;
+      const int p = row % 64;
+      if (row < 64 * BL) return ch >= 0 ? TT::to_f(ring_v[(slot_of(ch) * 64 + p) * D + dd]) : 0.f;
+      if (p < r) return TT::to_f(ring_v[(slot_cur * 64 + p) * D + dd]);
+      return p == r ? TT::to_f(vnew[dd]) : 0.f;
     }
   };
 
@@ -281,18 +293,20 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   np_map_load_w<T, D, DF>(wh, wf);
 
   // 0. stage the ring (and the new token) in LDS; append the token to the ring
-  for (int idx = tid; idx < 129 * V8; idx += 256) {
+  for (int idx = tid; idx < (RW + 1) * V8; idx += 256) {
     const int row = idx / V8, c8 = idx % V8;
+    const long long ch = c - BL + row / 64;
+    const int p = row % 64;
     frag xk = TT::zero(), xv = TT::zero();
-    if (row < 64) {
-      if (has_prev) {
-        xk = TT::load8(ring_k + (slot_prev * 64 + row) * D + c8 * 8);
-        xv = TT::load8(ring_v + (slot_prev * 64 + row) * D + c8 * 8);
+    if (row < 64 * BL) {
+      if (ch >= 0) {
+        xk = TT::load8(ring_k + (slot_of(ch) * 64 + p) * D + c8 * 8);
+        xv = TT::load8(ring_v + (slot_of(ch) * 64 + p) * D + c8 * 8);
       }
-    } else if (row < 64 + r) {
-      xk = TT::load8(ring_k + (slot_cur * 64 + row - 64) * D + c8 * 8);
-      xv = TT::load8(ring_v + (slot_cur * 64 + row - 64) * D + c8 * 8);
-    } else if (row == 64 + r) {
+    } else if (row < RW && p < r) {
+      xk = TT::load8(ring_k + (slot_cur * 64 + p) * D + c8 * 8);
+      xv = TT::load8(ring_v + (slot_cur * 64 + p) * D + c8 * 8);
+    } else if (row < RW && p == r) {
       xk = TT::load8(knew + c8 * 8);
       xv = TT::load8(vnew + c8 * 8);
       TT::store8(ring_k + (slot_cur * 64 + r) * D + c8 * 8, xk);
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     }
     SW::store8(kt, row, c8 * 8, xk);
     if constexpr (L::VT_LDS)
-      if (row < 128) TT::store8(vt + row * D + c8 * 8, xv);
+      if (row < RW) TT::store8(vt + row * D + c8 * 8, xv);
   }
   for (int idx = tid; idx < G * D; idx += 256) qs[idx] = TT::to_f(q[idx]);
   __syncthreads();
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
           qf[ks] = r16 == (r & 15) ? TT::load8(q + g * D + ks * 32 + grp * 8) : TT::zero();
-        const float sv = saliency_qblock<T, D>(kt, qf, r >> 4, w, 64 * c - 63, scale, 1, d.score);
+        const float sv = saliency_qblock<T, D, BL>(kt, qf, r >> 4, w, 64 * c - 64 * BL + 1, scale, 1, d.score);
         if (lane == (r & 15)) gsal[g] = sv;
       }
     }
@@ -351,15 +365,17 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   }
 
   // 3. linear-attention weights phi(q_g).phi(k_p) of the ring keys outside the softmax set:
-  //    chunk c-1 position p: p <= r + 64 - w and not selected; chunk c position p: p <= r - w
-  for (int half = 0; half < 2; ++half) {
-    const bool any = half == 0 ? has_prev : (r - w >= 0);
+  //    chunk c-l (l >= 1) position p: p <= r + 64 l - w and not selected; chunk c position p:
+  //    p <= r - w
+  for (int part = 0; part <= BL; ++part) {  // ring chunk c - BL + part
+    const int l = BL - part;
+    const bool any = l >= 1 ? c >= l : (r - w >= 0);
     if (!any) {
-      for (int idx = tid; idx < G * 64; idx += 256) wla[(idx / 64) * 128 + half * 64 + idx % 64] = 0.f;
+      for (int idx = tid; idx < G * 64; idx += 256) wla[(idx / 64) * RW + part * 64 + idx % 64] = 0.f;
       continue;
     }
     f32x4 phi[4][FPW];
-    np_map_rows64<T, D, DF>(kt, half * 64, wf, m2part, xn2, phi);
+    np_map_rows64<T, D, DF>(kt, part * 64, wf, m2part, xn2, phi);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -367,26 +383,27 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) phk[(kb * 16 + 4 * grp + i) * KP + (wave * FPW + fi) * 16 + r16] = phi[kb][fi][i];
     __syncthreads();
+    const uint64_t lmask = l >= 1 ? band_mask[l] : 0ull;
     for (int idx = tid; idx < G * 64; idx += 256) {
       const int g = idx / 64, p = idx % 64;
-      const bool la = half == 0 ? (p <= r + 64 - w && !((prev_mask >> p) & 1ull)) : (p <= r - w);
+      const bool la = l >= 1 ? (p <= r + 64 * l - w && !((lmask >> p) & 1ull)) : (p <= r - w);
       float s = 0.f;
       if (la)
         for (int f = 0; f < DF; ++f) s += phk[p * KP + f] * phq[g * DF + f];
-      wla[g * 128 + half * 64 + p] = s;
+      wla[g * RW + part * 64 + p] = s;
     }
     __syncthreads();
   }
 
   // 4. softmax logits (log2 units) of the ring keys in the softmax set:
-  //    chunk c-1 position p: p > r + 64 - w or selected; chunk c position p: r - w < p <= r
-  for (int idx = tid; idx < G * 128; idx += 256) {
-    const int g = idx / 128, row = idx % 128;
+  //    chunk c-l position p: p > r + 64 l - w or selected; chunk c position p: r - w < p <= r
+  for (int idx = tid; idx < G * RW; idx += 256) {
+    const int g = idx / RW, row = idx % RW;
+    const int l = BL - row / 64, p = row % 64;
     bool sa;
-    if (row < 64) {
-      sa = has_prev && (row > r + 64 - w || ((prev_mask >> row) & 1ull));
+    if (l >= 1) {
+      sa = c >= l && (p > r + 64 * l - w || ((band_mask[l] >> p) & 1ull));
     } else {
-      const int p = row - 64;
       sa = p <= r && p > r - w;
     }
     float x = -kInf;
@@ -404,14 +421,24 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   }
   __syncthreads();
   for (int g = wave; g < G; g += 4) {
-    const float x0 = ex[g * 128 + lane], x1 = ex[g * 128 + 64 + lane];
-    const float mx = wave_max(fmaxf(x0, x1));
-    const float e0 = mx > -kInf ? __builtin_amdgcn_exp2f(x0 - mx) : 0.f;
-    const float e1 = mx > -kInf ? __builtin_amdgcn_exp2f(x1 - mx) : 0.f;
-    ex[g * 128 + lane] = e0;
-    ex[g * 128 + 64 + lane] = e1;
-    const float l = wave_sum(e0 + e1);
-    const float dl = wave_sum(wla[g * 128 + lane] + wla[g * 128 + 64 + lane]);
+    float xs[NR];
+    float mx = -kInf;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      xs[j] = ex[g * RW + 64 * j + lane];
+      mx = fmaxf(mx, xs[j]);
+    }
+    mx = wave_max(mx);
+    float es = 0.f, ws = 0.f;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const float e = mx > -kInf ? __builtin_amdgcn_exp2f(xs[j] - mx) : 0.f;
+      ex[g * RW + 64 * j + lane] = e;
+      es += e;
+      ws += wla[g * RW + 64 * j + lane];
+    }
+    const float l = wave_sum(es);
+    const float dl = wave_sum(ws);
     if (lane == 0) {
       gmax[g] = mx;
       gsum[g] = l;
@@ -431,10 +458,10 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     const int g = idx / D, dd = idx % D;
     float osa = 0.f, ola = 0.f;
 #pragma unroll 8
-    for (int row = 0; row < 128; ++row) {
+    for (int row = 0; row < RW; ++row) {
       const float vv = vring(row, dd);
-      osa += ex[g * 128 + row] * vv;
-      ola += wla[g * 128 + row] * vv;
+      osa += ex[g * RW + row] * vv;
+      ola += wla[g * RW + row] * vv;
     }
     float dla = gden[g];
 #pragma unroll 16
@@ -470,20 +497,22 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     out[idx] = TT::from_f(Lsum > 0.f ? O / Lsum : 0.f);
   }
 
-  // 6. chunk completion: top_k of chunk c; fold chunk c-1
+  // 6. chunk completion: top_k of chunk c; fold chunk c-BL (ring rows 0..63), whose slot
+  //    the next chunk takes
   if (r != 63) return;  // uniform across the workgroup
   __syncthreads();
   if (wave == 0) {
     uint64_t nm = 0;
     if (d.topk > 0) nm = topk_mask(lane < 63 ? a.c.cur_sal[bh * 64 + lane] : gmisc[0], d.topk);
-    if (lane == 0) a.c.sel_mask[bh * 2 + slot_cur] = nm;
+    if (lane == 0) a.c.sel_mask[bh * NR + slot_cur] = nm;
   }
-  if (!has_prev) return;
+  if (c < BL) return;
+  const uint64_t prev_mask = band_mask[BL];
   {
     const long long tiles = a.c.sel_tiles;
     T* sk = static_cast<T*>(a.c.sel_k) + static_cast<long long>(bh) * tiles * 64 * D;
     T* sv = static_cast<T*>(a.c.sel_v) + static_cast<long long>(bh) * tiles * D * 64;
-    const long long row0 = (c - 1) * d.topk;
+    const long long row0 = (c - BL) * d.topk;
     for (int idx = tid; idx < 64 * D; idx += 256) {
       const int p = idx / D, dd = idx % D;
       if ((prev_mask >> p) & 1ull) {
@@ -524,9 +553,9 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------- cache export
 
 // One workgroup per (b, KV head): after a prefill of T tokens (chunk cT = T/64 holds the
-// next token), put chunks cT-1 and cT into the ring, chunk cT-1's selection and chunk
-// cT's saliencies in place, and the state of the unselected tokens of chunks <= cT-2.
-// The compact rows were written by the prefill itself.
+// next token), put chunks cT-L .. cT into the ring (chunk x in slot x mod (L + 1)), their
+// selections and chunk cT's saliencies in place, and the state of the unselected tokens of
+// chunks <= cT-L-1 (L = band_chunks(w)). The compact rows were written by the prefill itself.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void cache_export_kernel(ExportArgs a) {
   using TT = Tr<T>;
@@ -535,13 +564,16 @@ __global__ __launch_bounds__(256) void cache_export_kernel(ExportArgs a) {
   const int bh = blockIdx.x, b = bh / d.Hkv, h = bh % d.Hkv, tid = threadIdx.x;
   const long long T_ = d.T, cT = T_ / 64;
   const int rT = static_cast<int>(T_ % 64);
+  const int BL = band_chunks(d.window), NR = BL + 1;
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
-  T* rk = static_cast<T*>(a.c.ring_k) + static_cast<long long>(bh) * 2 * 64 * D;
-  T* rv = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * 2 * 64 * D;
-  for (int idx = tid; idx < 2 * 64 * V8; idx += 256) {
+  T* rk = static_cast<T*>(a.c.ring_k) + static_cast<long long>(bh) * NR * 64 * D;
+  T* rv = static_cast<T*>(a.c.ring_v) + static_cast<long long>(bh) * NR * 64 * D;
+  // the chunk in slot s: the one of cT-L .. cT congruent to s (mod L + 1)
+  auto chunk_in = [&](int slot) { return cT - ((cT - slot) % NR + NR) % NR; };
+  for (int idx = tid; idx < NR * 64 * V8; idx += 256) {
     const int slot = idx / (64 * V8), row = (idx / V8) % 64, c8 = idx % V8;
-    const long long ch = (cT & 1) == slot ? cT : cT - 1;
+    const long long ch = chunk_in(slot);
     const long long p = ch * 64 + row;
     typename TT::frag xk = TT::zero(), xv = TT::zero();
     if (ch >= 0 && p < T_) {
@@ -551,21 +583,22 @@ __global__ __launch_bounds__(256) void cache_export_kernel(ExportArgs a) {
     TT::store8(rk + (slot * 64 + row) * D + c8 * 8, xk);
     TT::store8(rv + (slot * 64 + row) * D + c8 * 8, xv);
   }
-  if (tid < 2) {
-    const long long ch = (cT & 1) == tid ? cT : cT - 1;
-    a.c.sel_mask[bh * 2 + tid] = (ch >= 0 && ch < d.nCc) ? a.selmask[static_cast<long long>(bh) * d.nC + ch] : 0ull;
+  if (tid < NR) {
+    const long long ch = chunk_in(tid);
+    a.c.sel_mask[bh * NR + tid] = (ch >= 0 && ch < d.nCc) ? a.selmask[static_cast<long long>(bh) * d.nC + ch] : 0ull;
   }
   if (tid < 64)
     a.c.cur_sal[bh * 64 + tid] = (d.window >= 1 && tid < rT) ? a.sal[static_cast<long long>(bh) * T_ + cT * 64 + tid] : 0.f;
   // the prefill's records hold S^T[d][pk_pos(f)] and z[pk_pos(f)]; the cache holds S[f][d], z[f]
-  const T* src = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (cT >= 2 ? cT - 2 : 0)) * d.R;
+  const bool has_state = cT >= BL + 1;
+  const T* src = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (has_state ? cT - BL - 1 : 0)) * d.R;
   for (int idx = tid; idx < d.R; idx += 256) {
     if (idx < d.DF * D) {
       const int f = idx / D, dd = idx % D;
-      a.c.state_s[static_cast<long long>(bh) * d.DF * D + idx] = cT >= 2 ? TT::to_f(src[dd * d.DF + pk_pos(f)]) : 0.f;
+      a.c.state_s[static_cast<long long>(bh) * d.DF * D + idx] = has_state ? TT::to_f(src[dd * d.DF + pk_pos(f)]) : 0.f;
     } else {
       const int f = idx - d.DF * D;
-      a.c.state_z[static_cast<long long>(bh) * d.DF + f] = cT >= 2 ? TT::to_f(src[d.DF * D + pk_pos(f)]) : 0.f;
+      a.c.state_z[static_cast<long long>(bh) * d.DF + f] = has_state ? TT::to_f(src[d.DF * D + pk_pos(f)]) : 0.f;
     }
   }
 }
@@ -591,12 +624,16 @@ static hipError_t decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t mid) {
     const hipError_t e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
   }
-  constexpr size_t lds = TokLds<T, D, DF>::bytes;  // above 64 KiB: opt in (gfx950 has 160 KiB per CU)
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_token_kernel<T, D, DF>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_token_kernel<T, D, DF>), dim3(bhn), dim3(256), lds, s, a);
-  return hipGetLastError();
+  static_assert(kMaxBand == 2, "one token kernel per band length");
+  auto go = [&](auto kern, size_t lds) {  // above 64 KiB: opt in (gfx950 has 160 KiB per CU)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(bhn), dim3(256), lds, s, a);
+    return hipGetLastError();
+  };
+  if (band_chunks(a.d.window) == 1) return go(decode_token_kernel<T, D, DF, 1>, TokLds<T, D, DF, 1>::bytes);
+  return go(decode_token_kernel<T, D, DF, 2>, TokLds<T, D, DF, 2>::bytes);
 }
 
 template <typename T, int D, int DF>

@@ -179,6 +179,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t mid);
 // nothing keeps its split partials there), and that scratch's device address on the
 // current device (looked up once per device).
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// Earlier chunks taken with per-query masks: L = ceil(w / 64), at least 1 (the chunk before
+// is always one of them, since its selection is the latest one a query sees). A band of L
+// chunks before the query's chunk holds the whole window of every query in it, with the
+// window's first key at or after the band's second row, which the saliency's 16-row key
+// blocks need. Windows up to kMaxWindow = 2 * 64 (L <= 2) are built.
+constexpr int kMaxBand = 2;
+constexpr int kMaxWindow = kMaxBand * 64;
+__host__ __device__ constexpr int band_chunks(int window) { return window <= 64 ? 1 : (window + 63) / 64; }
+static_assert(band_chunks(64) == 1 && band_chunks(65) == 2 && band_chunks(kMaxWindow) == 2, "band length");
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 

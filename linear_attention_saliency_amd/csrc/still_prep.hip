@@ -3,7 +3,7 @@
 // (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
 // prep_kernel, one workgroup per (chunk c, batch b, KV head h), four waves:
-//   1. stage the 128-row key band around chunk c in LDS;
+//   1. stage the key band of chunks c-L .. c in LDS (L = band_chunks(window));
 //   2. Self-Saliency Score of the chunk's 64 tokens for each query head of the group,
 //      summed over the group in head order ([P1] section "Self-Saliency Score");
 //   3. NP-Map of the chunk's keys ([P1] section "Norm-Preserved Feature Map（NP-Map）");
@@ -23,7 +23,7 @@ namespace still {
 // Workgroups per CU the registers are sized for: at D = d_f = 64 in bf16 the kernel fits
 // in 76 registers, so six share a CU (LDS allows eight) and the 2048 workgroups of a 16K
 // layer need few waves of dispatch; at head_dim 128 three (LDS allows four).
-template <typename T, int D, int DF>
+template <typename T, int D, int DF, int L>
 __global__ __launch_bounds__(256, (D == 64 && DF == 64 && sizeof(T) == 2) ? 6 : (D == 128 ? 3 : 1))
 void prep_kernel(PrepArgs a) {
   constexpr int FPW = DF / 64;
@@ -32,7 +32,10 @@ void prep_kernel(PrepArgs a) {
   using frag = typename TT::frag;
   using SW = Swz<T, D>;
 
-  __shared__ __attribute__((aligned(16))) T band[129 * D];
+  // key band: chunks c-L .. c and one zero row; bandc (chunks c-1 and c, then the zero row)
+  // is also where the gather, the NP-Map of the chunk and the V staging work
+  __shared__ __attribute__((aligned(16))) T band[(64 * L + 65) * D];
+  T* const bandc = band + 64 * (L - 1) * D;
   __shared__ float s_part[4][64];
   __shared__ float s_acc[64];
   __shared__ float m2part[4 * 64];
@@ -68,14 +71,18 @@ void prep_kernel(PrepArgs a) {
     vpre[i] = row < nvalid ? TT::load8(v + ((b * T_ + t0 + row) * d.Hkv + h) * D + c8 * 8) : TT::zero();
   }
 
-  // 1. key band: row t <-> position t0 - 64 + t, rows 0..63 chunk c-1 and 64..127 chunk c,
-  //    copied straight into LDS (rows outside the sequence read as zeros); row 128 (the
-  //    position after the chunk, never in a window) is zero
+  // 1. key band: row t <-> position t0 - 64 L + t, rows 64 (L - l) .. 64 (L - l) + 63 chunk
+  //    c-l, rows 64 L .. 64 L + 63 chunk c, copied straight into LDS (rows outside the
+  //    sequence read as zeros); row 64 L + 64 (the position after the chunk, never in a
+  //    window) is zero
   {
     const int kvs = d.Hkv * D;
-    dma_tile<T, D, 64, 4>(band, k + ((b * T_ + (c >= 1 ? t0 - kChunk : t0)) * d.Hkv + h) * D, kvs, c >= 1 ? 64 : 0);
-    dma_tile<T, D, 64, 4>(band + 64 * D, k + ((b * T_ + t0) * d.Hkv + h) * D, kvs, nvalid);
-    if (tid < V8) SW::store8(band, 128, tid * 8, TT::zero());
+#pragma unroll
+    for (int l = L; l >= 1; --l)
+      dma_tile<T, D, 64, 4>(band + 64 * (L - l) * D, k + ((b * T_ + (c >= l ? t0 - l * kChunk : t0)) * d.Hkv + h) * D,
+                            kvs, c >= l ? 64 : 0);
+    dma_tile<T, D, 64, 4>(band + 64 * L * D, k + ((b * T_ + t0) * d.Hkv + h) * D, kvs, nvalid);
+    if (tid < V8) SW::store8(band, 64 * L + 64, tid * 8, TT::zero());
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -102,7 +109,7 @@ void prep_kernel(PrepArgs a) {
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) qf[ks] = qcur[ks];
           if (qb < 3) qload(qb + 1, qcur);
-          const float sv = saliency_qblock<T, D>(band, qf, qb, d.window, t0 - 63, scale, 1, d.score);
+          const float sv = saliency_qblock<T, D, L>(band, qf, qb, d.window, t0 - 64 * L + 1, scale, 1, d.score);
           if (grp == 0) s_part[wave][qb * 16 + r16] = sv;
         }
       }
@@ -118,9 +125,9 @@ void prep_kernel(PrepArgs a) {
     if (tid < nvalid) a.sal[(static_cast<long long>(bh)) * T_ + t0 + tid] = s_acc[tid];
   }
 
-  // 3. NP-Map of the chunk's keys (band rows 64..127)
+  // 3. NP-Map of the chunk's keys (bandc rows 64..127)
   f32x4 phi[4][FPW];
-  np_map_rows64<T, D, DF>(band, 64, wf, m2part, xn2, phi);
+  np_map_rows64<T, D, DF>(bandc, 64, wf, m2part, xn2, phi);
 
   // 4. routing of a complete chunk
   const long long nsel_rows = static_cast<long long>(d.nCc) * d.topk;
@@ -161,7 +168,7 @@ void prep_kernel(PrepArgs a) {
       const long long dst =
           (static_cast<long long>(bh) * a.ntiles_sel * 64 + static_cast<long long>(c) * d.topk + slot) * D + c8 * 8;
       frag kx = TT::zero();
-      if (slot < nsel) kx = SW::load8(band, 64 + selpos[slot], c8 * 8);  // the chunk's rows are band rows 64..127
+      if (slot < nsel) kx = SW::load8(bandc, 64 + selpos[slot], c8 * 8);  // the chunk's rows are bandc rows 64..127
       TT::store8(ks_ + dst, kx);  // raw rows: the logit scale is applied to the fp32 scores
     }
   }
@@ -183,24 +190,24 @@ void prep_kernel(PrepArgs a) {
       }
 
   // 6. V of the chunk (loaded at the start; zero past the sequence end): stage in LDS over
-  //    band rows 0..63 once the gather is done with the band, transpose it into band rows
+  //    bandc rows 0..63 once the gather is done with the band, transpose it into bandc rows
   //    64..127 as V^T [d][64] (a Swz<T, 64> tile, keys permuted: position 8*pb + e holds
   //    key 32*(pb/4) + 16*(e/4) + 4*(pb%4) + e%4, the order MFMA operands take), then write
   //    that tile out as vT and the compact transposed copy of the selected rows
   using SV = Swz<T, 64>;
-  T* vtl = band + 64 * D;
+  T* vtl = bandc + 64 * D;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int idx = tid + i * 256;
-    SW::store8(band, idx / V8, (idx % V8) * 8, vpre[i]);
+    SW::store8(bandc, idx / V8, (idx % V8) * 8, vpre[i]);
   }
   __syncthreads();
   for (int idx = tid; idx < D * 8; idx += 256) {
     const int dd = idx / 8, pb = idx % 8;  // positions 8*pb .. 8*pb+7 of row dd
     frag x;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = band[SW::off(32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4), dd)];
+    for (int e = 0; e < 8; ++e) x[e] = bandc[SW::off(32 * (pb / 4) + 16 * (e / 4) + 4 * (pb % 4) + (e % 4), dd)];
     SV::store8(vtl, dd, pb * 8, x);
   }
   __syncthreads();
@@ -216,7 +223,7 @@ void prep_kernel(PrepArgs a) {
       for (int idx = tid; idx < d.topk * D; idx += 256) {
         const int slot = idx / D, dd = idx % D;
         const long long r = static_cast<long long>(c) * d.topk + slot;  // compact row
-        const T x = slot < nsel ? band[SW::off(selpos[slot], dd)] : TT::from_f(0.f);
+        const T x = slot < nsel ? bandc[SW::off(selpos[slot], dd)] : TT::from_f(0.f);
         vs[((r / 64) * D + dd) * 64 + pk_pos(static_cast<int>(r % 64))] = x;
       }
       // the last compact tile's unused columns are zero (they meet zero weights)
@@ -431,7 +438,11 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
 template <typename T, int D, int DF>
 static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
   dim3 grid(a.d.nC, a.d.B * a.d.Hkv);
-  hipLaunchKernelGGL((prep_kernel<T, D, DF>), grid, dim3(256), 0, s, a);
+  static_assert(kMaxBand == 2, "one prep instantiation per band length");
+  if (band_chunks(a.d.window) == 1)
+    hipLaunchKernelGGL((prep_kernel<T, D, DF, 1>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prep_kernel<T, D, DF, 2>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,13 +15,15 @@ constexpr int kChunk = 64;
 // Self-Saliency Score of 16 queries of one query head
 // ([P1] section "Self-Saliency Score"; [P4] section Approach).
 //
-// `band` holds 128 key rows (a Swz<T, D> tile): band row t is the key at position band_pos0 + t,
-// with band_pos0 = chunk_start - 63 (rows outside the sequence are zero and masked here); it is
-// stored at LDS tile row t + row_base (row_base 0 or 1, so a tile that starts one position
-// earlier can be used as is).
-// Query r of the chunk (its position is chunk_start + r) sits at band row r + 63, so its
-// window is band rows [r + 64 - w, r + 63]. qf holds the B-operand (SK) fragments of the
-// queries qb*16 .. qb*16+15 (lane r16 <-> query qb*16 + r16).
+// `band` holds 64 (L + 1) key rows (a Swz<T, D> tile), L = band_chunks(window): band row t is
+// the key at position band_pos0 + t, with band_pos0 = chunk_start - 64 L + 1 (rows outside the
+// sequence are zero and masked here); it is stored at LDS tile row t + row_base (row_base 0
+// or 1, so a tile that starts one position earlier can be used as is).
+// Query r of the chunk (its position is chunk_start + r) sits at band row r + 64 L - 1, so
+// its window is band rows [r + 64 L - w, r + 64 L - 1]. qf holds the B-operand (SK) fragments
+// of the queries qb*16 .. qb*16+15 (lane r16 <-> query qb*16 + r16). The result does not
+// depend on L beyond the window's reach (rows outside the window add nothing, and a lane
+// holds the same positions whatever L), so every caller gets the same bits.
 //
 // For query i (logits in log2 units, scale = log2(e)/sqrt(D)): M' = max over the window
 // without i, Z' = sum over the window without i of
@@ -29,14 +31,15 @@ constexpr int kChunk = 64;
 // +inf when i is alone in its window. Returned in every lane of the query's column.
 // With score = 1 the routing score is the diagonal logit alone, q_i . k_i / sqrt(D) in
 // natural units ([P4] section "Surprising findings": routing by the diagonal attention).
-template <typename T, int D>
+template <typename T, int D, int L = 1>
 __device__ __forceinline__ float saliency_qblock(const T* band, const typename Tr<T>::frag (&qf)[D / 32],
                                                  int qb, int window, long long band_pos0, float scale,
                                                  int row_base = 0, int score = 0) {
+  constexpr int NJ = 4 * L + 1;  // 16-row key blocks from the query block's window start to its diagonal
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
-  f32x4 acc[5];
+  f32x4 acc[NJ];
 #pragma unroll
-  for (int j = 0; j < 5; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -45,21 +48,21 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
     }
   }
   const int r = qb * 16 + r16;
-  const int diag = r + 63;
+  const int diag = r + 64 * L - 1;
   if (score == 1) {
     float dr = -kInf;
 #pragma unroll
-    for (int j = 0; j < 5; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if ((qb + j) * 16 + 4 * grp + i == diag) dr = acc[j][i];
     return xor_max_groups(dr) * (1.0f / sqrtf(static_cast<float>(D)));
   }
   // logits in log2 units: scale = log2(e) / sqrt(D)
-  const int lo = max(r + 64 - window, static_cast<int>(-band_pos0));  // first window row inside the sequence
+  const int lo = max(r + 64 * L - window, static_cast<int>(-band_pos0));  // first window row inside the sequence
   float mx = -kInf, dg = -kInf;
 #pragma unroll
-  for (int j = 0; j < 5; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (qb + j) * 16 + 4 * grp + i;
@@ -71,7 +74,7 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
   dg = xor_max_groups(dg);
   float z = 0.f;
 #pragma unroll
-  for (int j = 0; j < 5; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (qb + j) * 16 + 4 * grp + i;

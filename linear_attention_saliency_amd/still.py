@@ -112,6 +112,13 @@ SCORES = {"saliency": 0, "diag": 1}  # still_score: the routing score
 SCOPES = {"kv_head": 0, "query_head": 1}  # still_routing_scope: who selects
 
 
+def band_chunks(window: int) -> int:
+    """Earlier chunks a query's window can reach, at least 1 (the library's band length): a
+    decode cache holds band_chunks(window) + 1 chunks of raw rows, chunk x in slot
+    x % (band_chunks(window) + 1)."""
+    return 1 if window <= 64 else (window + 63) // 64
+
+
 def make_config(batch, seq_len, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k,
                 dtype, score: str = "saliency", scope: str = "kv_head") -> Config:
     dt = STILL_BF16 if dtype in (torch.bfloat16, "bf16") else STILL_F32 if dtype in (torch.float32, "f32") else -1
@@ -384,14 +391,15 @@ class DecodeCache:
             return self.buffer[off:off + n * esize].view(dtype).view(*shape)
 
         cap = int(c.sel_capacity)
+        nr = band_chunks(cfg.window) + 1  # ring slots
         return {
             "sel_k": view(c.sel_k, (B, H, cap, D), dt, es),
             "sel_v": view(c.sel_v, (B, H, cap // 64, D, 64), dt, es),
-            "ring_k": view(c.ring_k, (B, H, 2, 64, D), dt, es),
-            "ring_v": view(c.ring_v, (B, H, 2, 64, D), dt, es),
+            "ring_k": view(c.ring_k, (B, H, nr, 64, D), dt, es),
+            "ring_v": view(c.ring_v, (B, H, nr, 64, D), dt, es),
             "state_s": view(c.state_s, (B, H, F, D), torch.float32, 4),
             "state_z": view(c.state_z, (B, H, F), torch.float32, 4),
-            "sel_mask": view(c.sel_mask, (B, H, 2), torch.int64, 8),
+            "sel_mask": view(c.sel_mask, (B, H, nr), torch.int64, 8),
             "cur_saliency": view(c.cur_saliency, (B, H, 64), torch.float32, 4),
         }
 

@@ -44,7 +44,7 @@ def test_status_strings():
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -1), (dict(seq_len=0), -1), (dict(n_q_heads=6, n_kv_heads=4), -1), (dict(dtype="f16"), -1),
     (dict(window=-1), -1), (dict(top_k=65), -1), (dict(window=0, top_k=1), -1), (dict(chunk=32, window=32), -2),
-    (dict(window=65), -2), (dict(head_dim=96), -2), (dict(feat_dim=32), -2), (dict(dtype="f32", head_dim=96), -2),
+    (dict(window=129), -2), (dict(head_dim=96), -2), (dict(feat_dim=32), -2), (dict(dtype="f32", head_dim=96), -2),
     (dict(seq_len=4_200_000, head_dim=128, feat_dim=128), -2),
 ])
 def test_invalid_configs_rejected_before_launch(kw, code):
@@ -55,6 +55,23 @@ def test_invalid_configs_rejected_before_launch(kw, code):
     rc = lib.still_prefill(ctypes.byref(cfg), dummy, dummy, dummy, dummy, dummy, None, None, None, None, dummy,
                            1 << 40, None)
     assert rc == code
+
+
+def test_windows_longer_than_a_chunk():
+    """Windows up to 2 chunks are built for the forward and decode paths: the decode cache then
+    holds one more chunk of raw rows (and its selection mask); the backward refuses them."""
+    lib = still.load()
+    for w in (65, 96, 128):
+        cfg = _cfg(window=w)
+        assert lib.still_prefill_workspace_bytes(ctypes.byref(cfg)) > 0, w
+        assert lib.still_backward_workspace_bytes(ctypes.byref(cfg)) == 0, w
+    assert lib.still_backward_workspace_bytes(ctypes.byref(_cfg(window=64))) > 0
+    b1, b64, b65, b128 = (lib.still_cache_bytes(ctypes.byref(_cfg(window=w)), 4096) for w in (1, 64, 65, 128))
+    assert b1 == b64 and b65 == b128 and b65 > b64
+    cfg = _cfg()
+    ring_row = cfg.batch * cfg.n_kv_heads * 64 * cfg.head_dim * 2  # one chunk of K (or V) rows, bf16
+    assert b65 - b64 >= 2 * ring_row
+    assert [still.band_chunks(w) for w in (0, 1, 64, 65, 128)] == [1, 1, 1, 2, 2]
 
 
 def test_pointer_and_workspace_checks():

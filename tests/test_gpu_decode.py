@@ -64,7 +64,7 @@ def _decode_steps(cache, tq, tk, tv, tw, t0, t1):
         st = cache.tensors()
         sals.append(st["cur_saliency"][:, :, t % 64].clone())
         if t % 64 == 63:
-            masks[t // 64] = _mask_bits(st["sel_mask"][:, :, (t // 64) & 1])
+            masks[t // 64] = _mask_bits(st["sel_mask"][:, :, (t // 64) % st["sel_mask"].shape[2]])
     torch.cuda.synchronize()
     out = np.stack([_np(o) for o in outs], axis=1)
     sal = np.stack([s.cpu().numpy() for s in sals], axis=-1)
@@ -87,6 +87,11 @@ PREFILL_THEN_DECODE = [
     # routed by the diagonal logit instead of the Self-Saliency Score
     ("bf16-diag-score", 2, 100, 270, 4, 1, 64, 64, 64, 8, "bf16", 1.0, "diag"),
     ("bf16-d128-diag-score", 1, 64, 200, 4, 2, 128, 128, 64, 16, "bf16", None, "diag"),
+    # windows longer than a chunk: a ring of three chunks, chunk c-2 folded at completion
+    ("f32-w96-mid-chunk", 1, 150, 400, 4, 1, 64, 64, 96, 8, "f32", 1.0),
+    ("bf16-w128-d128-at-boundary", 2, 192, 330, 8, 2, 128, 128, 128, 16, "bf16", 1.0),
+    ("f32-w127-d128-f128", 1, 70, 300, 2, 1, 128, 128, 127, 8, "f32", 1.0),
+    ("bf16-w65", 1, 100, 260, 4, 1, 64, 64, 65, 8, "bf16", 1.0),
 ]
 
 
@@ -144,18 +149,21 @@ def test_prefill_then_decode_equals_prefill(case):
     # the cache after decoding holds what the prefill of T tokens leaves
     a, bb = cache.tensors(), full_cache.tensors()
     c_next, r_next = T // 64, T % 64
-    nsel = max(0, c_next - 1) * k
+    bl = still.band_chunks(w)
+    nr = bl + 1
+    nsel = max(0, c_next - bl) * k
     assert torch.equal(a["sel_k"][:, :, :nsel], bb["sel_k"][:, :, :nsel])
     sv_a = a["sel_v"].reshape(B, Hkv, -1, D, 64)
     sv_b = bb["sel_v"].reshape(B, Hkv, -1, D, 64)
     full_tiles = nsel // 64
     assert torch.equal(sv_a[:, :, :full_tiles], sv_b[:, :, :full_tiles])
-    if c_next >= 1:
-        sp = (c_next - 1) & 1
-        assert torch.equal(a["ring_k"][:, :, sp], bb["ring_k"][:, :, sp])
-        assert torch.equal(a["ring_v"][:, :, sp], bb["ring_v"][:, :, sp])
-        assert torch.equal(a["sel_mask"][:, :, sp], bb["sel_mask"][:, :, sp])
-    sc_ = c_next & 1
+    for l in range(1, bl + 1):  # the band chunks c_next - l
+        if c_next >= l:
+            sp = (c_next - l) % nr
+            assert torch.equal(a["ring_k"][:, :, sp], bb["ring_k"][:, :, sp])
+            assert torch.equal(a["ring_v"][:, :, sp], bb["ring_v"][:, :, sp])
+            assert torch.equal(a["sel_mask"][:, :, sp], bb["sel_mask"][:, :, sp])
+    sc_ = c_next % nr
     assert torch.equal(a["ring_k"][:, :, sc_, :r_next], bb["ring_k"][:, :, sc_, :r_next])
     if w >= 1:
         assert torch.equal(a["cur_saliency"][:, :, :r_next], bb["cur_saliency"][:, :, :r_next])
@@ -170,6 +178,8 @@ FROM_EMPTY = [
     ("f32-from-empty", 2, 200, 2, 1, 64, 64, 64, 8, "f32", 1.0),
     ("bf16-from-empty-gqa4", 1, 210, 8, 2, 128, 128, 64, 16, "bf16", 1.0),
     ("f32-d128-from-empty", 1, 200, 4, 1, 128, 128, 64, 16, "f32", 1.0),
+    ("bf16-w100-from-empty", 1, 330, 4, 1, 64, 64, 100, 8, "bf16", 1.0),
+    ("f32-w65-from-empty", 1, 270, 2, 1, 64, 64, 65, 8, "f32", 1.0),
 ]
 
 

@@ -98,6 +98,17 @@ CASES = [
     ("f32-d128-f64-w16", 1, 330, 4, 1, 128, 64, 16, 8, "f32", 1.0),
     ("f32-d64-f128", 1, 290, 4, 1, 64, 128, 64, 4, "f32", 1.0),
     ("f32-d128-k63", 1, 260, 2, 1, 128, 128, 64, 63, "f32", 1.0),
+    # windows longer than a chunk (two band chunks), each dtype and head / feature width,
+    # several compact tiles
+    ("bf16-w65", 1, 300, 4, 1, 64, 64, 65, 8, "bf16", 1.0),
+    ("f32-w66-f128", 1, 260, 4, 1, 64, 128, 66, 8, "f32", 1.0),
+    ("f32-w96", 1, 420, 2, 1, 64, 64, 96, 8, "f32", 1.0),
+    ("bf16-w96-gqa4", 1, 600, 8, 2, 64, 64, 96, 8, "bf16", 1.0),
+    ("bf16-w96-many-tiles", 1, 1300, 4, 1, 64, 64, 96, 16, "bf16", 1.0),
+    ("f32-w128-d128", 1, 390, 4, 1, 128, 128, 128, 16, "f32", 1.0),
+    ("bf16-w128-d128", 2, 333, 8, 2, 128, 128, 128, 16, "bf16", 1.0),
+    ("bf16-w127-f128-k3", 1, 450, 4, 1, 64, 128, 127, 3, "bf16", 1.0),
+    ("f32-w100-d128-f64", 1, 300, 2, 1, 128, 64, 100, 8, "f32", None),
 ]
 
 

@@ -325,6 +325,8 @@ def test_empty_softmax_set_zero_query():
 @pytest.mark.parametrize("T,Hq,Hkv,w,C,k", [
     (64, 2, 1, 8, 8, 2), (61, 4, 2, 8, 8, 3), (50, 2, 2, 3, 8, 1), (40, 1, 1, 1, 8, 4),
     (45, 3, 1, 12, 8, 2), (30, 2, 1, 8, 8, 8), (7, 2, 1, 8, 8, 2), (1, 2, 1, 4, 4, 1),
+    # windows longer than a chunk: one key past it, two chunks, past two chunks
+    (40, 2, 1, 9, 8, 1), (52, 2, 1, 16, 8, 2), (60, 2, 1, 17, 8, 3),
 ])
 def test_chunked_equals_brute(T, Hq, Hkv, w, C, k):
     q, k_, v, wp = _case(2, T, Hq, Hkv, 8, 6, seed=T + k, scale=1.7)
