@@ -67,6 +67,9 @@ Dims dims_of(const still_config* c) {
   d.T = c->seq_len;
   d.Hq = c->n_q_heads;
   d.Hkv = c->n_kv_heads;
+  const bool per_q = c->routing_scope == STILL_ROUTE_PER_QUERY_HEAD;
+  d.Hr = per_q ? c->n_q_heads : c->n_kv_heads;
+  d.Gr = per_q ? 1 : c->n_q_heads / c->n_kv_heads;
   d.G = c->n_q_heads / c->n_kv_heads;
   d.D = c->head_dim;
   d.DF = c->feat_dim;
@@ -96,7 +99,8 @@ struct WsLayout {
 
 WsLayout ws_layout(const still_config* c) {
   const Dims d = dims_of(c);
-  const size_t bh = static_cast<size_t>(d.B) * d.Hkv;
+  const size_t bh = static_cast<size_t>(d.B) * d.Hr;   // routing-head records
+  const size_t bkv = static_cast<size_t>(d.B) * d.Hkv;  // KV-head records (V^T and phi(K) tiles)
   const size_t es = elem_bytes(c);
   WsLayout L;
   size_t off = 0;
@@ -110,8 +114,8 @@ WsLayout ws_layout(const still_config* c) {
   L.ntiles_sel = static_cast<int>(odd_tiles((static_cast<int64_t>(d.nCc) * d.topk + 63) / 64));
   L.ksel = take(bh * L.ntiles_sel * 64 * d.D * es);
   L.vselT = take(bh * L.ntiles_sel * 64 * d.D * es);
-  L.vT = take(bh * d.nC * 64 * d.D * es);
-  L.phik = take(bh * d.T * d.DF * es);
+  L.vT = take(bkv * d.nC * 64 * d.D * es);
+  L.phik = take(bkv * d.T * d.DF * es);
   L.states = take(bh * d.nC * d.R * (d.bf16 ? 2 : 4));
   L.kmaxc = take(bh * d.nC * sizeof(float));
   L.tilemax = take(bh * (L.ntiles_sel > 0 ? L.ntiles_sel : 1) * sizeof(float));
@@ -148,7 +152,8 @@ struct CacheLayout {
 };
 
 CacheLayout cache_layout(const still_config* c, int64_t max_tokens) {
-  const size_t bh = static_cast<size_t>(c->batch) * c->n_kv_heads;
+  const Dims d = dims_of(c);
+  const size_t bh = static_cast<size_t>(c->batch) * d.Hr;  // routing-head records
   const size_t es = elem_bytes(c);
   const size_t D = c->head_dim, F = c->feat_dim;
   CacheLayout L;
@@ -177,7 +182,6 @@ int check_cache_cfg(const still_config* c, int64_t max_tokens) {
   if (st != STILL_OK) return st;
   if (max_tokens < 1 || max_tokens > 0x7fffffffLL) return STILL_ERR_INVALID_ARG;
   if (c->n_q_heads / c->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
-  if (c->routing_scope != STILL_ROUTE_PER_KV_HEAD) return STILL_ERR_UNSUPPORTED;
   return STILL_OK;
 }
 
@@ -364,11 +368,6 @@ int still_last_hip_error(void) { return static_cast<int>(t_last_hip); }
 
 size_t still_prefill_workspace_bytes(const still_config* cfg) {
   if (check_cfg(cfg, true) != STILL_OK) return 0;
-  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
-    const still_config e = expanded_cfg(cfg);
-    if (check_cfg(&e, true) != STILL_OK) return 0;
-    return exp_layout(cfg).total + ws_layout(&e).total;
-  }
   return ws_layout(cfg).total;
 }
 
@@ -387,18 +386,6 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
     if (p && !aligned(p, 4)) return STILL_ERR_INVALID_ARG;
   if (saliency_out && cfg->window < 1) return STILL_ERR_INVALID_ARG;
   if (routing_in && cfg->top_k > 0 && !routing_valid(cfg, routing_in)) return STILL_ERR_INVALID_ARG;
-  if (cfg->routing_scope == STILL_ROUTE_PER_QUERY_HEAD) {
-    if (cache) return STILL_ERR_UNSUPPORTED;
-    const still_config e = expanded_cfg(cfg);
-    const int se = check_cfg(&e, true);
-    if (se != STILL_OK) return se;
-    const ExpLayout X = exp_layout(cfg);
-    if (ws_bytes < X.total + ws_layout(&e).total) return STILL_ERR_WORKSPACE_TOO_SMALL;
-    char* ws = static_cast<char*>(workspace);
-    STILL_HIP(expand_kvw(cfg, k, v, w_phi, ws, X, stream));
-    return still_prefill_timed(&e, q, ws + X.ek, ws + X.ev, ws + X.ew, out, routing_in, saliency_out,
-                               sel_idx_out, nullptr, ws + X.total, ws_bytes - X.total, stream, events);
-  }
   if (cache) {
     if (!same_layer(&cache->cfg, cfg)) return STILL_ERR_CACHE_MISMATCH;
     if (cache->n_tokens != 0) return STILL_ERR_INVALID_ARG;
@@ -419,7 +406,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   if (routing_in && cfg->top_k > 0 && d.nCc > 0) {  // validated above; the prep kernel reads a device copy
     pa.routing_in = reinterpret_cast<const int32_t*>(ws + L.routing);
     STILL_HIP(hipMemcpyAsync(ws + L.routing, routing_in,
-                             static_cast<size_t>(d.B) * d.Hkv * d.nCc * d.topk * sizeof(int32_t),
+                             static_cast<size_t>(d.B) * d.Hr * d.nCc * d.topk * sizeof(int32_t),
                              hipMemcpyHostToDevice, stream));
   }
   pa.sal = saliency_out ? saliency_out : reinterpret_cast<float*>(ws + L.sal);
@@ -459,8 +446,8 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.ntiles_sel = pa.ntiles_sel;
   aa.tilemax = tilemax;
   aa.tm_stride = L.ntiles_sel;
-  aa.nw = d.G >= 4 ? 4 : (d.G == 3 ? 4 : d.G);  // query heads per workgroup: 1, 2 or 4
-  aa.gsplit = (d.G + aa.nw - 1) / aa.nw;
+  aa.nw = d.Gr >= 4 ? 4 : (d.Gr == 3 ? 4 : d.Gr);  // query heads per workgroup: 1, 2 or 4
+  aa.gsplit = (d.Gr + aa.nw - 1) / aa.nw;
   STILL_HIP(still::launch_attn(aa, stream));
   if (events) STILL_HIP(hipEventRecord(events[3], stream));
   if (cache) {
@@ -568,7 +555,7 @@ int decode_plan(const still_config* cfg, const still_cache* cache, const void* q
   const int bl = still::band_chunks(cfg->window);  // compact rows: chunks <= chunk - bl - 1
   a.nsel = static_cast<int>((chunk >= bl ? chunk - bl : 0) * cfg->top_k);
   const int ntiles = (a.nsel + 63) / 64;
-  const int bhn = cfg->batch * cfg->n_kv_heads;
+  const int bhn = cfg->batch * a.d.Hr;
   int nsplit = (kSplitTarget + bhn - 1) / bhn;
   if (nsplit > kMaxSplit) nsplit = kMaxSplit;
   if (nsplit > ntiles) nsplit = ntiles;

@@ -667,20 +667,23 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   // workgroup order: heaviest chunks first; within a chunk, consecutive workgroups take
   // consecutive (b, h, head split) so that, with 8 XCDs dispatched round-robin, one
   // XCD's L2 serves a fixed set of KV heads
-  const int BHG = d.B * d.Hkv * a.gsplit;
+  const int BHG = d.B * d.Hr * a.gsplit;
   const int P = BHG * C::QSPLIT;
   const int c = d.nC - 1 - static_cast<int>(blockIdx.x) / P;
   const int pi = static_cast<int>(blockIdx.x) % P;
   const int bhg = pi % BHG, qsb = pi / BHG;  // block of C::QS query slices
   const int gs = bhg % a.gsplit, bh = bhg / a.gsplit;
-  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  // bh: the (b, routing head) record (compact rows, state, selection); bkv: the KV head's
+  // (keys, values, phi(K), V^T tiles)
+  const int b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G;
+  const long long bkv = static_cast<long long>(b) * d.Hkv + h;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
   const int g = gs * NH + wave % NH;
   constexpr int HV = C::HV;
   const int qoff0 = (qsb * C::QS + wave / NH) * QW * HV;  // first query of this wave within the chunk
-  const bool head_ok = g < d.G;
-  const int hq = h * d.G + (head_ok ? g : d.G - 1);
+  const bool head_ok = g < d.Gr;
+  const int hq = rh * d.Gr + (head_ok ? g : d.Gr - 1);
   const long long T_ = d.T;
   const long long t0 = static_cast<long long>(c) * kChunk;
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
@@ -765,11 +768,11 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     const int cp = has_prev ? c - 1 : c;
     const T* kc = kk + ((b * T_ + t0) * d.Hkv + h) * D;
     const T* kp = kk + ((b * T_ + tp) * d.Hkv + h) * D;
-    dma_tile<T, DF, 64, NW>(L + C::R_PHIP, phik + (static_cast<long long>(bh) * T_ + tp) * DF, DF, has_prev ? 64 : 0);
-    dma_tile<T, 64, D, NW>(L + C::R_VP, vT + (static_cast<long long>(bh) * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
+    dma_tile<T, DF, 64, NW>(L + C::R_PHIP, phik + (bkv * T_ + tp) * DF, DF, has_prev ? 64 : 0);
+    dma_tile<T, 64, D, NW>(L + C::R_VP, vT + (bkv * d.nC + cp) * D * 64, 64, has_prev ? D : 0);
     if constexpr (!C::SEQ) dma_tile<T, D, 64, NW>(L + C::R_KP, kp, kvs, has_prev && win >= 1 ? 64 : 0);
-    dma_tile<T, DF, 64, NW>(L + C::R_PHIC, phik + (static_cast<long long>(bh) * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
-    dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (static_cast<long long>(bh) * d.nC + c) * D * 64, 64, D);
+    dma_tile<T, DF, 64, NW>(L + C::R_PHIC, phik + (bkv * T_ + t0) * DF, DF, la_cur ? nvalid : 0);
+    dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (bkv * d.nC + c) * D * 64, 64, D);
     if constexpr (!C::SEQ) dma_tile<T, D, 64, NW>(L + C::R_KC, kc, kvs, win >= 1 ? nvalid : 0);
     if constexpr (C::STATE_LDS)
       dma_tile<T, DF, D, NW>(L + C::R_ST, Sg, DF, has_state ? D : 0);
@@ -1029,8 +1032,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
     __syncthreads();  // every wave is done with the fixed regions (or the previous band chunk)
     const long long tb = t0 - static_cast<long long>(l) * kChunk;
     dma_tile<T, D, 64, NW>(L + C::R_BK, kk + ((b * T_ + tb) * d.Hkv + h) * D, d.Hkv * D, 64);
-    dma_tile<T, DF, 64, NW>(L + C::R_BF, phik + (static_cast<long long>(bh) * T_ + tb) * DF, DF, 64);
-    dma_tile<T, 64, D, NW>(L + C::R_BV, vT + (static_cast<long long>(bh) * d.nC + (c - l)) * D * 64, 64, D);
+    dma_tile<T, DF, 64, NW>(L + C::R_BF, phik + (bkv * T_ + tb) * DF, DF, 64);
+    dma_tile<T, 64, D, NW>(L + C::R_BV, vT + (bkv * d.nC + (c - l)) * D * 64, 64, D);
     const uint64_t sel = a.selmask[static_cast<long long>(bh) * d.nC + (c - l)];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1216,7 +1219,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 template <typename T, int D, int DF, int NH, bool BAND>
 static hipError_t attn_nhb(const AttnArgs& a, hipStream_t s) {
   using C = AttnCfg<T, D, DF, NH>;
-  const int P = a.d.B * a.d.Hkv * a.gsplit * C::QSPLIT;
+  const int P = a.d.B * a.d.Hr * a.gsplit * C::QSPLIT;
   dim3 grid(a.d.nC * P);
   if (C::LDS_BYTES > 65536)  // opt in to more than 64 KiB of LDS (gfx950 has 160 KiB per CU)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<T, D, DF, NH, BAND>),

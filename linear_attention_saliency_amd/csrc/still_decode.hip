@@ -3,11 +3,12 @@
 // so a decoding token never waits for a per-token selection).
 // (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
-// One new token for every sequence, all at position i = 64c + r. Per (batch b, KV head h):
+// One new token for every sequence, all at position i = 64c + r. Per (batch b, routing
+// head rh: the KV head, or a query head when each query head selects for itself):
 //   decode_split_kernel  nsplit workgroups each read a disjoint run of 64-row tiles of the
-//                        compact softmax cache (the selected rows of chunks <= c-2) and leave
+//                        compact softmax cache (the selected rows of chunks <= c-L-1) and leave
 //                        an online-softmax partial (max, sum, unnormalised output, log2 units)
-//                        for each of the G query heads of the group. This is the only part
+//                        for each of the Gr query heads the routing head serves. This is the only part
 //                        whose bytes grow with the context; it is HBM-bound.
 //   decode_token_kernel  one workgroup: writes the token into the ring of raw rows (chunks
 //                        c-L .. c, L = band_chunks(w)), computes its Self-Saliency Score with the prefill's
@@ -89,14 +90,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   const Dims& d = a.d;
   const float c1 = kLog2e / sqrtf(static_cast<float>(D));  // logit scale in log2 units
-  const int split = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / d.Hkv, h = bh % d.Hkv, G = d.G;
+  const int split = blockIdx.x, bh = blockIdx.y;  // bh: the (b, routing head) record
+  const int b = bh / d.Hr, rh = bh % d.Hr, G = d.Gr;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int ntiles = (a.nsel + 63) / 64;
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(ntiles, t_begin + a.tiles_per_split);
 
-  const T* q = static_cast<const T*>(a.q) + static_cast<long long>(b * d.Hq + h * G) * D;
+  const T* q = static_cast<const T*>(a.q) + static_cast<long long>(b * d.Hq + rh * G) * D;
   frag qf[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) qf[ks] = r16 < G ? TT::load8(q + r16 * D + ks * 32 + grp * 8) : TT::zero();
@@ -226,10 +227,11 @@ struct TokLds {
   static_assert(bytes <= 160 * 1024, "the token kernel's LDS must fit a CU");
 };
 
-// One workgroup per (b, KV head). LDS tile row t holds the key at position 64(c-BL) + t:
+// One workgroup per (b, routing head) (a KV head, or a query head when each query head
+// selects for itself: then every query head keeps its own ring, compact rows and state). LDS tile row t holds the key at position 64(c-BL) + t:
 // rows 64(BL-l) .. 64(BL-l)+63 are chunk c-l (zero when c < l), rows 64 BL .. 64 BL + r
 // chunk c up to the new token, the rest zero. Chunk x lives in ring slot x mod (BL + 1).
-// Query head g of the group is h*G + g.
+// Query head g of the routing head is rh*Gr + g.
 template <typename T, int D, int DF, int BL>
 __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   using TT = Tr<T>;
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   float* gmisc = gsal + kMaxGroup;  // [0] = group-summed saliency of the new token
 
   const Dims& d = a.d;
-  const int bh = blockIdx.x, b = bh / d.Hkv, h = bh % d.Hkv, G = d.G, w = d.window;
+  // bh: the (b, routing head) record; h: its KV head; G: the query heads it serves
+  const int bh = blockIdx.x, b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G, G = d.Gr, w = d.window;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const long long pos = a.pos, c = pos / 64;
   const int r = static_cast<int>(pos % 64);
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   const int slot_cur = slot_of(c);
   const float scale = kLog2e / sqrtf(static_cast<float>(D));
 
-  const T* q = static_cast<const T*>(a.q) + static_cast<long long>(b * d.Hq + h * G) * D;
+  const T* q = static_cast<const T*>(a.q) + static_cast<long long>(b * d.Hq + rh * G) * D;
   const T* knew = static_cast<const T*>(a.k) + static_cast<long long>(b * d.Hkv + h) * D;
   const T* vnew = static_cast<const T*>(a.v) + static_cast<long long>(b * d.Hkv + h) * D;
   const T* wh = static_cast<const T*>(a.w) + static_cast<long long>(h) * DF * D;
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   //    and the compact-cache partials, one shared normaliser
   const float* S = a.c.state_s + static_cast<long long>(bh) * DF * D;
   const float* z = a.c.state_z + static_cast<long long>(bh) * DF;
-  T* out = static_cast<T*>(a.out) + static_cast<long long>(b * d.Hq + h * G) * D;
+  T* out = static_cast<T*>(a.out) + static_cast<long long>(b * d.Hq + rh * G) * D;
   const long long rec0 = static_cast<long long>(bh) * a.nsplit * G;
   const int nsplit = a.nsel > 0 ? a.nsplit : 0;
   for (int idx = tid; idx < G * D; idx += 256) {
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------- cache export
 
-// One workgroup per (b, KV head): after a prefill of T tokens (chunk cT = T/64 holds the
+// One workgroup per (b, routing head): after a prefill of T tokens (chunk cT = T/64 holds the
 // next token), put chunks cT-L .. cT into the ring (chunk x in slot x mod (L + 1)), their
 // selections and chunk cT's saliencies in place, and the state of the unselected tokens of
 // chunks <= cT-L-1 (L = band_chunks(w)). The compact rows were written by the prefill itself.
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(256) void cache_export_kernel(ExportArgs a) {
   using TT = Tr<T>;
   constexpr int V8 = D / 8;
   const Dims& d = a.d;
-  const int bh = blockIdx.x, b = bh / d.Hkv, h = bh % d.Hkv, tid = threadIdx.x;
+  const int bh = blockIdx.x, b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G, tid = threadIdx.x;
   const long long T_ = d.T, cT = T_ / 64;
   const int rT = static_cast<int>(T_ % 64);
   const int BL = band_chunks(d.window), NR = BL + 1;
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, long long n16)
 
 template <typename T, int D, int DF>
 static hipError_t decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t mid) {
-  const int bhn = a.d.B * a.d.Hkv;
+  const int bhn = a.d.B * a.d.Hr;
   if (a.nsel > 0) {
     hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.nsplit, bhn), dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
@@ -638,7 +641,7 @@ static hipError_t decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t mid) {
 
 template <typename T, int D, int DF>
 static hipError_t export_t(const ExportArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((cache_export_kernel<T, D>), dim3(a.d.B * a.d.Hkv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((cache_export_kernel<T, D>), dim3(a.d.B * a.d.Hr), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

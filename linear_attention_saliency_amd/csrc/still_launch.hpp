@@ -8,6 +8,11 @@ namespace still {
 
 struct Dims {
   int B, T, Hq, Hkv, G, D, DF, window, topk;
+  // Routing heads: who selects. Per KV head: Hr = Hkv, Gr = G; per query head: Hr = Hq,
+  // Gr = 1. Saliency, selection, the compact softmax rows and the linear-attention state are
+  // kept per (b, routing head); routing head rh reads KV head rh * Gr / G and serves query
+  // heads rh * Gr .. rh * Gr + Gr - 1.
+  int Hr, Gr;
   int nC;   // number of chunks, ceil(T / 64)
   int nCc;  // number of complete chunks, T / 64
   int R;    // elements per chunk state record: DF*D (S) + DF (z)
@@ -22,17 +27,17 @@ struct PrepArgs {
   const void* v;
   const void* w;
   const int32_t* routing_in;  // optional
-  float* sal;                 // [B,Hkv,T]
-  uint64_t* selmask;          // [B,Hkv,nC]
-  int32_t* sel_idx;           // optional [B,Hkv,nCc,topk]
-  void* ksel;                 // [B,Hkv,ntiles_sel*64,D]: compact K rows (the selected keys)
+  float* sal;                 // [B,Hr,T]
+  uint64_t* selmask;          // [B,Hr,nC]
+  int32_t* sel_idx;           // optional [B,Hr,nCc,topk]
+  void* ksel;                 // [B,Hr,ntiles_sel*64,D]: compact K rows (the selected keys)
   void* phik;                // [B,Hkv,T,DF], features permuted by pk_pos
-  void* states;               // [B,Hkv,nC,R] in the layer's dtype: S^T [D][DF] with features permuted by
+  void* states;               // [B,Hr,nC,R] in the layer's dtype: S^T [D][DF] with features permuted by
                               // pk_pos, then z [DF] permuted
   void* vT;                   // [B,Hkv,nC,D,64]: V of each chunk transposed, keys permuted by pk_pos
-  void* vselT;                // [B,Hkv,ntiles_sel,D,64]: compact V rows, same tile layout
+  void* vselT;                // [B,Hr,ntiles_sel,D,64]: compact V rows, same tile layout
   int ntiles_sel;             // compact tiles per (b, KV head): >= ceil(nCc*topk / 64)
-  float* kmaxc;               // [B,Hkv,nC]: largest |k| among each chunk's selected keys
+  float* kmaxc;               // [B,Hr,nC]: largest |k| among each chunk's selected keys
 };
 
 struct AttnArgs {

@@ -2,10 +2,12 @@
 // NP-Map kernels.
 // (Page labels [P1]..[P4]: the pages listed at the top of include/still.h.)
 //
-// prep_kernel, one workgroup per (chunk c, batch b, KV head h), four waves:
+// prep_kernel, one workgroup per (chunk c, batch b, routing head rh), four waves; the routing
+// head is the KV head (selection per KV head) or a query head (selection per query head), and
+// its keys and values are those of KV head h = rh * Gr / G:
 //   1. stage the key band of chunks c-L .. c in LDS (L = band_chunks(window));
-//   2. Self-Saliency Score of the chunk's 64 tokens for each query head of the group,
-//      summed over the group in head order ([P1] section "Self-Saliency Score");
+//   2. Self-Saliency Score of the chunk's 64 tokens for each query head the routing head
+//      serves, summed over them in head order ([P1] section "Self-Saliency Score");
 //   3. NP-Map of the chunk's keys ([P1] section "Norm-Preserved Feature Map（NP-Map）");
 //   4. top-k routing of a complete chunk, ascending positions, and the gather of the
 //      selected K/V rows into the compact softmax cache ([P1] section
@@ -49,8 +51,11 @@ void prep_kernel(PrepArgs a) {
   const T* v = static_cast<const T*>(a.v);
   const T* w = static_cast<const T*>(a.w);
   const int c = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  const int bh = blockIdx.y;  // (b, routing head) record
+  const int b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G;
+  // phi(K) and V^T depend on the KV head alone: the first routing head of each KV head writes them
+  const long long bkv = static_cast<long long>(b) * d.Hkv + h;
+  const bool kv_writer = (rh * d.Gr) % d.G == 0;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses stay scalar
   const long long T_ = d.T;
@@ -89,10 +94,10 @@ void prep_kernel(PrepArgs a) {
 
   // 2. saliency, summed over the group in head order g = 0..G-1
   if (d.window >= 1) {
-    for (int g0 = 0; g0 < d.G; g0 += 4) {
+    for (int g0 = 0; g0 < d.Gr; g0 += 4) {
       const int g = g0 + wave;
-      if (g < d.G) {
-        const int hq = h * d.G + g;
+      if (g < d.Gr) {
+        const int hq = rh * d.Gr + g;
         // queries of block qb (rows past the sequence end read as zeros), one block ahead
         const auto qrs = make_rsrc(q + ((b * T_ + t0) * d.Hq + hq) * D,
                                    static_cast<uint32_t>(((nvalid - 1) * d.Hq + 1) * D * static_cast<int>(sizeof(T))));
@@ -116,7 +121,7 @@ void prep_kernel(PrepArgs a) {
       __syncthreads();
       if (wave == 0) {
         float acc = g0 == 0 ? 0.f : s_acc[lane];
-        const int nw = d.G - g0 < 4 ? d.G - g0 : 4;
+        const int nw = d.Gr - g0 < 4 ? d.Gr - g0 : 4;
         for (int w2 = 0; w2 < nw; ++w2) acc += s_part[w2][lane];
         s_acc[lane] = acc;
       }
@@ -185,7 +190,7 @@ void prep_kernel(PrepArgs a) {
         const int row = kb * 16 + 4 * grp + i;
         const int f = (wave * FPW + fi) * 16 + r16;
         const T val = TT::from_f(phi[kb][fi][i]);
-        if (row < nvalid) phik[(static_cast<long long>(bh) * T_ + t0 + row) * DF + pk_pos(f)] = val;
+        if (row < nvalid && kv_writer) phik[(bkv * T_ + t0 + row) * DF + pk_pos(f)] = val;
         phi[kb][fi][i] = ((smask >> row) & 1ull) ? 0.f : TT::to_f(val);
       }
 
@@ -212,11 +217,12 @@ void prep_kernel(PrepArgs a) {
   }
   __syncthreads();
   {
-    T* vt = static_cast<T*>(a.vT) + (static_cast<long long>(bh) * d.nC + c) * D * 64;
-    for (int idx = tid; idx < D * 8; idx += 256) {
-      const int dd = idx / 8, pb = idx % 8;
-      TT::store8(vt + dd * 64 + pb * 8, SV::load8(vtl, dd, pb * 8));
-    }
+    T* vt = static_cast<T*>(a.vT) + (bkv * d.nC + c) * D * 64;
+    if (kv_writer)
+      for (int idx = tid; idx < D * 8; idx += 256) {
+        const int dd = idx / 8, pb = idx % 8;
+        TT::store8(vt + dd * 64 + pb * 8, SV::load8(vtl, dd, pb * 8));
+      }
     if (complete && d.topk > 0) {
       T* vs = static_cast<T*>(a.vselT) + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
       const int nsel = __popcll(smask);
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
 
 template <typename T, int D, int DF>
 static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
-  dim3 grid(a.d.nC, a.d.B * a.d.Hkv);
+  dim3 grid(a.d.nC, a.d.B * a.d.Hr);
   static_assert(kMaxBand == 2, "one prep instantiation per band length");
   if (band_chunks(a.d.window) == 1)
     hipLaunchKernelGGL((prep_kernel<T, D, DF, 1>), grid, dim3(256), 0, s, a);
@@ -489,7 +495,7 @@ hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* t
   if (d.nCc == 0) return hipSuccess;
   const bool tiles = d.topk > 0 && tm_stride > 0;
   const int words = d.bf16 ? d.R / 2 : d.R;
-  dim3 grid((words + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hkv);
+  dim3 grid((words + 63) / 64 + (tiles ? 1 : 0), d.B * d.Hr);
   const int tms = tiles ? tm_stride : 0, tk = d.topk > 0 ? d.topk : 1;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), 0, s, states, d.nC, d.nCc, d.R, kmaxc, tilemax, tms, tk);
@@ -504,7 +510,7 @@ hipError_t launch_scan(const Dims& d, void* states, const float* kmaxc, float* t
 
 hipError_t launch_topk(const Dims& d, const float* sal, int32_t* sel_idx, hipStream_t s) {
   if (d.nCc == 0 || d.topk == 0) return hipSuccess;
-  dim3 grid(d.nCc, d.B * d.Hkv);
+  dim3 grid(d.nCc, d.B * d.Hr);
   hipLaunchKernelGGL(topk_kernel, grid, dim3(64), 0, s, sal, sel_idx, d.T, d.nCc, d.topk);
   return hipGetLastError();
 }

@@ -204,7 +204,7 @@ def prefill(q, k, v, w_phi, *, window: int, top_k: int, chunk: int = 64, routing
     q [B,T,Hq,D], k/v [B,T,Hkv,D], w_phi [Hkv,d_f,D] (all float32 or all bfloat16, on the
     GPU). routing: optional int32 [B,Hkv,T//chunk,top_k] override of the selection (ascending
     positions inside each chunk; anything else raises StillError with status -1).
-    cache: optional empty DecodeCache, left ready to decode token T.
+    cache: optional empty DecodeCache (of the same scope), left ready to decode token T.
     score: "saliency" (the Self-Saliency Score) or "diag" (the diagonal logit alone).
     scope: "kv_head" (each KV head selects for its group) or "query_head" (each query head
     selects for itself; the score and routing are then [B,Hq,...]).
@@ -357,10 +357,10 @@ class DecodeCache:
 
     def __init__(self, *, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, feat_dim: int,
                  window: int, top_k: int, max_tokens: int, dtype=torch.bfloat16, chunk: int = 64,
-                 device="cuda", score: str = "saliency"):
+                 device="cuda", score: str = "saliency", scope: str = "kv_head"):
         lib = load()
         self.cfg = make_config(batch, 0, n_q_heads, n_kv_heads, head_dim, feat_dim, window, chunk, top_k, dtype,
-                               score)
+                               score, scope)
         nbytes = int(lib.still_cache_bytes(ctypes.byref(self.cfg), max_tokens))
         if nbytes == 0:
             raise StillError(-2, "still_cache_bytes")
@@ -378,7 +378,8 @@ class DecodeCache:
     def tensors(self):
         """Views of the device state (for inspection): dict of torch tensors."""
         c, cfg = self.c, self.cfg
-        B, H, D, F = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.feat_dim
+        B, D, F = cfg.batch, cfg.head_dim, cfg.feat_dim
+        H = cfg.n_q_heads if cfg.routing_scope == SCOPES["query_head"] else cfg.n_kv_heads  # heads that select
         dt = torch.bfloat16 if cfg.dtype == STILL_BF16 else torch.float32
         es = 2 if dt == torch.bfloat16 else 4
         base = self.buffer.data_ptr()

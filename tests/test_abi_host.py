@@ -166,14 +166,18 @@ def test_decode_step_validation():
 
 
 def test_routing_scope_checks():
-    """Per-query-head routing: a bad scope is rejected, a decode cache refuses it, and the
-    prefill and backward workspaces include the expanded copies."""
+    """Per-query-head routing: a bad scope is rejected; the prefill keeps per-query-head
+    records (scores, selections, compact rows, states) but no copy of K or V; the decode
+    cache holds per-query-head records; the backward workspace includes expanded copies."""
     lib = still.load()
     assert lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(scope="bogus"))) == 0
-    q1 = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg(scope="query_head")))
-    kv = lib.still_prefill_workspace_bytes(ctypes.byref(_cfg()))
+    cq, ckv = _cfg(scope="query_head"), _cfg()
+    q1 = lib.still_prefill_workspace_bytes(ctypes.byref(cq))
+    kv = lib.still_prefill_workspace_bytes(ctypes.byref(ckv))
     assert q1 > kv > 0
-    assert lib.still_cache_bytes(ctypes.byref(_cfg(scope="query_head")), 1024) == 0
+    kv_copies = 2 * ckv.batch * ckv.seq_len * ckv.n_q_heads * ckv.head_dim * 2  # K and V per query head, bf16
+    assert q1 - kv < kv_copies
+    assert lib.still_cache_bytes(ctypes.byref(cq), 1024) > lib.still_cache_bytes(ctypes.byref(ckv), 1024) > 0
     assert lib.still_backward_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) > \
         lib.still_backward_workspace_bytes(ctypes.byref(_cfg())) > 0
     assert lib.still_future_attention_mass_workspace_bytes(ctypes.byref(_cfg(scope="query_head"))) == 0

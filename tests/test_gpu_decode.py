@@ -46,11 +46,12 @@ def _mask_bits(m):
     return ((u[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
 
 
-def _new_cache(wl, max_tokens, score="saliency"):
+def _new_cache(wl, max_tokens, score="saliency", scope="kv_head"):
     return still.DecodeCache(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
                              head_dim=wl.head_dim, feat_dim=wl.feat_dim, window=wl.window, top_k=wl.top_k,
                              max_tokens=max_tokens,
-                             dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, score=score)
+                             dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, score=score,
+                             scope=scope)
 
 
 def _decode_steps(cache, tq, tk, tv, tw, t0, t1):
@@ -92,6 +93,11 @@ PREFILL_THEN_DECODE = [
     ("bf16-w128-d128-at-boundary", 2, 192, 330, 8, 2, 128, 128, 128, 16, "bf16", 1.0),
     ("f32-w127-d128-f128", 1, 70, 300, 2, 1, 128, 128, 127, 8, "f32", 1.0),
     ("bf16-w65", 1, 100, 260, 4, 1, 64, 64, 65, 8, "bf16", 1.0),
+    # each query head selects for itself: per-query-head rings, compact rows and states over
+    # shared K and V (the oracle runs on K, V and W_h repeated per query head)
+    ("bf16-query-head-gqa4", 1, 100, 300, 8, 2, 64, 64, 64, 8, "bf16", 1.0, "saliency", "query_head"),
+    ("f32-query-head-w96-d128", 1, 130, 330, 4, 1, 128, 128, 96, 16, "f32", 1.0, "saliency", "query_head"),
+    ("bf16-query-head-diag", 2, 64, 200, 4, 2, 128, 64, 64, 8, "bf16", None, "diag", "query_head"),
 ]
 
 
@@ -99,6 +105,8 @@ PREFILL_THEN_DECODE = [
 def test_prefill_then_decode_equals_prefill(case):
     name, B, T0, T, Hq, Hkv, D, F, w, k, dt, sc, *rest = case
     score = rest[0] if rest else "saliency"
+    scope = rest[1] if len(rest) > 1 else "kv_head"
+    Hr = Hq if scope == "query_head" else Hkv  # heads that select
     _say(name)
     wl, (q, kk, v, wp) = synth.small_case(seed=zlib.crc32(name.encode()) % 1000, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D,
                                            F=F, window=w, chunk=64, top_k=k, dtype=dt, qk_scale=sc,
@@ -106,18 +114,18 @@ def test_prefill_then_decode_equals_prefill(case):
     tq, tk, tv, tw = (_dev(a, dt) for a in (q, kk, v, wp))
 
     # reference: one prefill of all T tokens, into a cache as well
-    full_cache = _new_cache(wl, T + 16, score)
+    full_cache = _new_cache(wl, T + 16, score, scope)
     if w >= 1:
         out_full, sal_full, idx_full = still.prefill(tq, tk, tv, tw, window=w, top_k=k, return_saliency=True,
-                                                     return_routing=True, cache=full_cache, score=score)
+                                                     return_routing=True, cache=full_cache, score=score, scope=scope)
     else:
         out_full, idx_full = still.prefill(tq, tk, tv, tw, window=w, top_k=k, return_routing=True,
-                                           cache=full_cache)
+                                           cache=full_cache, scope=scope)
         sal_full = None
 
-    cache = _new_cache(wl, T + 16, score)
+    cache = _new_cache(wl, T + 16, score, scope)
     still.prefill(tq[:, :T0].contiguous(), tk[:, :T0].contiguous(), tv[:, :T0].contiguous(), tw, window=w,
-                  top_k=k, cache=cache, score=score)
+                  top_k=k, cache=cache, score=score, scope=scope)
     out_dec, sal_dec, masks = _decode_steps(cache, tq, tk, tv, tw, T0, T)
     assert cache.n_tokens == T
 
@@ -127,18 +135,21 @@ def test_prefill_then_decode_equals_prefill(case):
         assert np.array_equal(sal_dec.view(np.uint32), s_full[:, :, T0:T].view(np.uint32)), "saliency bits differ"
     idx = idx_full.cpu().numpy()
     for c, m in masks.items():
-        ref = np.zeros((B, Hkv, 64), dtype=bool)
+        ref = np.zeros((B, Hr, 64), dtype=bool)
         for b in range(B):
-            for h in range(Hkv):
+            for h in range(Hr):
                 ref[b, h, idx[b, h, c] - 64 * c] = k > 0
         assert np.array_equal(m, ref), f"selection of chunk {c} differs"
     _say(name, "chunks completed while decoding", sorted(masks))
 
     # outputs against the oracle under that routing
-    sel = np.zeros((B, Hkv, T), dtype=bool)
+    sel = np.zeros((B, Hr, T), dtype=bool)
     for b in range(B):
-        for h in range(Hkv):
+        for h in range(Hr):
             sel[b, h, idx[b, h].reshape(-1)] = k > 0
+    if scope == "query_head":  # the same layer with every query head its own KV head
+        G = Hq // Hkv
+        kk, v, wp = np.repeat(kk, G, axis=2), np.repeat(v, G, axis=2), np.repeat(wp, G, axis=0)
     ref = O.attend(q, kk, v, wp, w, 64, k, sel=sel)
     err = np.abs(out_dec - ref[:, T0:T]).max()
     err_full = np.abs(_np(out_full) - ref).max()
@@ -153,8 +164,8 @@ def test_prefill_then_decode_equals_prefill(case):
     nr = bl + 1
     nsel = max(0, c_next - bl) * k
     assert torch.equal(a["sel_k"][:, :, :nsel], bb["sel_k"][:, :, :nsel])
-    sv_a = a["sel_v"].reshape(B, Hkv, -1, D, 64)
-    sv_b = bb["sel_v"].reshape(B, Hkv, -1, D, 64)
+    sv_a = a["sel_v"].reshape(B, Hr, -1, D, 64)
+    sv_b = bb["sel_v"].reshape(B, Hr, -1, D, 64)
     full_tiles = nsel // 64
     assert torch.equal(sv_a[:, :, :full_tiles], sv_b[:, :, :full_tiles])
     for l in range(1, bl + 1):  # the band chunks c_next - l

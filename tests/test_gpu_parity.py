@@ -229,26 +229,28 @@ def test_diagonal_score_routing(dt, D, F, G):
     assert decided > 0 and err <= TOL[dt]
 
 
-@pytest.mark.parametrize("dt,D,F,Hq,Hkv", [("f32", 64, 64, 2, 1), ("bf16", 64, 64, 8, 2), ("bf16", 128, 128, 4, 1)])
-def test_per_query_head_routing(dt, D, F, Hq, Hkv):
+@pytest.mark.parametrize("dt,D,F,Hq,Hkv,T,w", [("f32", 64, 64, 2, 1, 300, 64), ("bf16", 64, 64, 8, 2, 300, 64),
+                                               ("bf16", 128, 128, 4, 1, 300, 64), ("bf16", 64, 64, 4, 1, 1100, 64),
+                                               ("f32", 64, 128, 4, 2, 420, 96), ("bf16", 128, 64, 6, 2, 333, 33)])
+def test_per_query_head_routing(dt, D, F, Hq, Hkv, T, w):
     """Each query head selects on its own saliency: the score and routing per query head
     against the oracle on K, V and W_h repeated per query head (the same layer with
     n_kv_heads = n_q_heads), and the output under the device's routing."""
-    _say("per-query-head", dt, D, F, Hq, Hkv)
-    wl, (q, kk, v, wp) = synth.small_case(seed=17 + D + Hq, B=1, T=300, Hq=Hq, Hkv=Hkv, D=D, F=F, window=64,
+    _say("per-query-head", dt, D, F, Hq, Hkv, T, w)
+    wl, (q, kk, v, wp) = synth.small_case(seed=17 + D + Hq + T, B=1, T=T, Hq=Hq, Hkv=Hkv, D=D, F=F, window=w,
                                            chunk=64, top_k=8, dtype=dt, qk_scale=1.0, n_planted=6)
     G = Hq // Hkv
     tq, tk, tv, tw = (_dev(a, dt) for a in (q, kk, v, wp))
-    out, sal, idx = still.prefill(tq, tk, tv, tw, window=64, top_k=8, return_saliency=True, return_routing=True,
+    out, sal, idx = still.prefill(tq, tk, tv, tw, window=w, top_k=8, return_saliency=True, return_routing=True,
                                   scope="query_head")
     torch.cuda.synchronize()
-    assert tuple(sal.shape) == (1, Hq, 300) and tuple(idx.shape) == (1, Hq, 4, 8)
+    assert tuple(sal.shape) == (1, Hq, T) and tuple(idx.shape) == (1, Hq, T // 64, 8)
     k_e, v_e, w_e = np.repeat(kk, G, axis=2), np.repeat(v, G, axis=2), np.repeat(wp, G, axis=0)
     wl_e = wl.replace(n_kv_heads=Hq)
-    s_ref, _ = O.saliency(q, k_e, 64)
+    s_ref, _ = O.saliency(q, k_e, w)
     idx_np = idx.cpu().numpy().astype(np.int64)
     decided, flips = _check_routing(sal.cpu().numpy().astype(np.float64), idx_np, s_ref, wl_e)
-    ref = O.attend(q, k_e, v_e, w_e, 64, 64, 8, sel=_sel_from_idx(idx_np, 300))
+    ref = O.attend(q, k_e, v_e, w_e, w, 64, 8, sel=_sel_from_idx(idx_np, T))
     err = np.abs(out.float().cpu().numpy().astype(np.float64) - ref).max()
     _say("per-query-head decided", decided, "flips", flips, "max abs err", err)
     assert decided > 0 and err <= TOL[dt]
