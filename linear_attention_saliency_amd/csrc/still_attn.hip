@@ -606,7 +606,9 @@ struct AttnCfg {
   // halves) each takes one slice, and the pair hides each other's waits. Where only one
   // fits (head_dim 128, or fp32) it takes both slices with twice the waves, so every SIMD
   // still runs two waves and every staged tile serves the whole chunk.
-  static constexpr int QS = LDS_BYTES > 80 * 1024 ? 2 : 1;
+  // A workgroup of one query head (each query head selecting for itself, or one query head
+  // per KV head) takes both slices too: the LDS per workgroup is the same, the waves double.
+  static constexpr int QS = (LDS_BYTES > 80 * 1024 || NH == 1) ? 2 : 1;
   // Query halves per wave. At head_dim 64, where two workgroups share a CU, a wave takes
   // both 32-query halves of the chunk: every compact K and V^T fragment it reads from LDS
   // then feeds twice the MFMAs, and the step's fixed costs (copy issue and wait, barrier,
