@@ -567,13 +567,17 @@ struct AttnCfg {
   static constexpr int QB = QW / 16;           // 16-query blocks per wave
   static constexpr int KT = 64 * D, FT = 64 * DF, VT = D * 64;  // elements of a K, phi(K), V^T tile
   static constexpr int STAGE = KT + VT;        // one compact tile (K then V^T)
-  // Sequential plan, where the usual one (every fixed tile, the prefix state and a compact
-  // stage resident at once) would pass the CU's 160 KiB (fp32 at head_dim 128: six 32 KiB
-  // tiles and a 64 KiB state): the linear-attention tiles first, the window's K tiles
-  // then over the phi(K) regions, W_h and the state read from memory, and the compact
-  // tiles in two stages over the same regions.
+  // Sequential plan: the linear-attention tiles first, the window's K tiles then over the
+  // phi(K) regions, W_h and the state read from memory, and the compact tiles in two stages
+  // over the same regions. Taken where the usual plan (every fixed tile, the prefix state
+  // and a compact stage resident at once) would pass the CU's 160 KiB (fp32 at head_dim
+  // 128: six 32 KiB tiles and a 64 KiB state), and for bf16 at head_dim 128, where the usual
+  // plan fills a CU with one workgroup (160 KiB) and this one lets two share it (64 KiB
+  // each): their waits then overlap (Llama-3.1-8B-shaped layer: 7% less time at 8 x 4K
+  // tokens, 22% less at 64K, for the shorter compact pipeline).
   static constexpr int ST_FULL = D * DF;
-  static constexpr bool SEQ = (2 * FT + 2 * VT + 2 * KT + ST_FULL + STAGE) * static_cast<int>(sizeof(T)) > 160 * 1024;
+  static constexpr bool SEQ = (2 * FT + 2 * VT + 2 * KT + ST_FULL + STAGE) * static_cast<int>(sizeof(T)) > 160 * 1024 ||
+                              (sizeof(T) == 2 && D == 128);
   // the prefix state (S^T [D][DF] in the layer's dtype) goes through LDS where it fits
   // beside the tiles: at D = d_f = 64 (two workgroups per CU) and at D = 128 (one, with
   // both query slices: 8 waves read one copy instead of 8)
