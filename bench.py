@@ -18,8 +18,9 @@ so one selection / append / fold is inside the timed window).
 run's first copy dispatch), so that a rocprofv3 --pmc run of this script also records what
 FETCH_SIZE / WRITE_SIZE read for a transfer of known size (the scale applied to the
 dominant kernel's counters).
-The roofline "traffic" field is read from profiles/attn_kernel_traffic.txt when that
-file was measured on the current attention-kernel source (matching SHA-1), else null.
+The roofline "traffic" field is read from profiles/attn_kernel_traffic_<workload>.txt when
+that file was measured on this workload and the current attention-kernel source (matching
+SHA-1), else null.
 """
 
 from __future__ import annotations
@@ -43,7 +44,9 @@ _CSRC = os.path.join(ROOT, "linear_attention_saliency_amd", "csrc")
 # the attention kernel's source and every header it includes
 ATTN_SRCS = [os.path.join(_CSRC, f) for f in ("still_attn.hip", "still_common.hpp", "still_layout.hpp",
                                               "still_launch.hpp", "still_route.hpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
+def traffic_file(workload_key: str) -> str:
+    """The committed HBM-traffic summary of the attention kernel on one prefill workload."""
+    return os.path.join(ROOT, "profiles", f"attn_kernel_traffic_{workload_key}.txt")
 # the decode compact-cache kernel's source and the headers it includes
 DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("still_decode.hip", "still_common.hpp", "still_layout.hpp",
                                                 "still_launch.hpp", "still_route.hpp")]
@@ -60,7 +63,7 @@ def source_sha1(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, path: str = TRAFFIC_FILE, srcs=ATTN_SRCS):
+def measured_traffic(workload: str, path: str, srcs=ATTN_SRCS):
     """HBM bytes per launch of the bench's dominant kernel from a committed counter
     summary, if it was taken on this workload and the current kernel source; else None."""
     try:
@@ -201,7 +204,7 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
                    "routing_scope": args.scope},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
-                     "traffic": measured_traffic(wl.name)},
+                     "traffic": measured_traffic(wl.name, traffic_file(args.workload))},
         "layer_roofline": {"flops": work["flops"], "bytes": work["bytes"],
                            "mfma_frac": layer_tflops / PEAK_BF16_MFMA, "hbm_frac": layer_gbs / PEAK_HBM,
                            "frac": max(layer_tflops / PEAK_BF16_MFMA, layer_gbs / PEAK_HBM)},

@@ -65,9 +65,12 @@ def _per_kernel(dirpath: str, counter: str):
     return out
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn_kernel") -> str:
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn_kernel", others=()) -> str:
+    """HBM bytes per launch of `kernel` (the machine-read line), then of each kernel in
+    `others` (name substrings) as comment lines."""
     lines = []
     total = 0.0
+    extra = collections.defaultdict(float)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _per_kernel(d, counter)
         copies = [k for k in per if "copyBuffer" in k]
@@ -82,7 +85,14 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn
         total += val
         lines.append(f"{counter}: copy kernel {ck[:60]} read {per[ck][0]:.0f} for {copy_bytes} bytes "
                      f"(scale {scale:.2f} B/unit); {kernel} mean {val / 1e6:.2f} MB per launch")
+        for o in others:
+            for k in per:
+                if o in k and "still" in k:
+                    extra[(_short_name(k), counter)] = sum(per[k]) / len(per[k]) * scale
     lines.append(f"hbm_bytes_per_launch: {total:.0f}")
+    for name in sorted({n for n, _ in extra}):
+        f, w = extra.get((name, "FETCH_SIZE"), 0.0), extra.get((name, "WRITE_SIZE"), 0.0)
+        lines.append(f"# {name}: {f / 1e6:.2f} MB read + {w / 1e6:.2f} MB written = {(f + w) / 1e6:.2f} MB per launch")
     return "\n".join(lines)
 
 
@@ -153,7 +163,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "trace":
         print(trace(sys.argv[2], int(sys.argv[3])))
     elif sys.argv[1] == "traffic":
-        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), *sys.argv[5:6]))
+        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), *sys.argv[5:6], others=sys.argv[6:]))
     elif sys.argv[1] == "counters":
         opts = [a for a in sys.argv[2:] if a.startswith("--match=")]
         print(counters([a for a in sys.argv[2:] if not a.startswith("--match=")],
