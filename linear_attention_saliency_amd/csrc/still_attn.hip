@@ -28,8 +28,10 @@
 // the logit, 2^-9 of it per element). The
 // running max is refreshed only when a tile's max exceeds it by more than kLazy = 32 (log2
 // units): P and the accumulators keep fp32's exponent range (bf16 has it too), so terms up
-// to 2^32 stay exact in relative terms and every sum stays finite. A per-tile bound
-// |q| max|k| skips even the max pass when the max cannot move that far.
+// to 2^32 stay exact in relative terms and every sum stays finite. Before the compact
+// tiles the max is set once, from the bound |q| max|k| of their logits (or, where that bound
+// is far above every score so far, from their exact largest logit), so the compact loop
+// itself has no max pass.
 //
 // Every tile the fixed part needs (phi(K) and V of chunk c-1, K and V of the window, the
 // prefix state) is copied into its own LDS region at the start, together with the first
@@ -41,6 +43,8 @@
 // in the PV product as one extra 16-row block whose A operand is all ones. V tiles arrive
 // transposed and key-permuted from the prep kernel, phi(K) rows feature-permuted, so
 // every LDS operand fragment is a single 16-byte read.
+#include <type_traits>
+
 #include "still_launch.hpp"
 #include "still_layout.hpp"
 #include "still_route.hpp"
@@ -50,6 +54,9 @@ namespace still {
 // lazy running max: rescale only when a score exceeds the running max by more than this
 // (log2 units)
 constexpr float kLazy = 32.f;
+// how far (log2 units) the running max may be raised above every score seen so far to a
+// bound of the compact logits, before the exact largest compact logit is taken instead
+constexpr float kRaise = 64.f;
 
 template <typename T> __device__ __forceinline__ typename Tr<T>::frag ones_frag() {
   typename Tr<T>::frag x;
@@ -185,36 +192,6 @@ template <typename F> __device__ __forceinline__ float row_sum_add(const F& p, f
   return x;
 }
 
-// sm_max with the row sums held as per-lane partials lp (sm_exp_pv_hv) instead of the
-// accumulators' ones block: the same lazy refresh, rescaling o's value blocks and lp.
-template <int D, int QB>
-__device__ __forceinline__ void sm_max_lp(const f32x4 (&s)[4][QB], f32x4 (&o)[D / 16 + 1][QB], float (&lp)[QB],
-                                          float (&m_run)[QB], float c1) {
-  bool need_any = false;
-  float alpha[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float tm = -kInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tm = fmaxf(tm, s[kb][qb][i]);
-    tm = xor_max_groups(tm) * c1;
-    const bool need = tm > m_run[qb] + kLazy;
-    alpha[qb] = need ? (m_run[qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - tm)) : 1.f;
-    m_run[qb] = need ? tm : m_run[qb];
-    need_any |= need;
-  }
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need_any) != 0, 0)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha[qb];
-      lp[qb] *= alpha[qb];
-    }
-  }
-}
-
 // Scores of one 64-key tile for HV query groups of a wave: every K fragment read from LDS
 // feeds the products of all of them (qk_tile with HV groups).
 template <typename T, int D, int QB, int HV>
@@ -276,6 +253,42 @@ __device__ __forceinline__ void sm_exp_pv_hv(const f32x4 (&s)[HV][4][QB], const 
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = row_sum_add(pf[hv][qb], lp[hv][qb]);
   }
+}
+
+// The largest compact logit of each query of a wave (log2 units: the fp32 score times c1),
+// over the n_comp compact keys: K rows (D elements each, rsrc kr) straight from memory, no
+// LDS and no barrier, so the other waves of the workgroup are not held up.
+template <typename T, int D, int QB, int HV>
+__device__ __forceinline__ void compact_max(__amdgpu_buffer_rsrc_t kr, int n_comp,
+                                            const typename Tr<T>::frag (&qf)[HV][QB][D / 32], float (&mx)[HV][QB],
+                                            float c1) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  float m[HV][QB];
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m[hv][qb] = -kInf;
+  for (int k0 = 0; k0 < n_comp; k0 += 16) {  // 16-key blocks: lane r16 loads key k0 + r16
+    typename Tr<T>::frag ka[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      ka[ks] = Tr<T>::bload8(kr, ((k0 + r16) * D + ks * 32 + grp * 8) * static_cast<int>(sizeof(T)), 0);
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) Tr<T>::mma(sv, ka[ks], qf[hv][qb][ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // element i: key k0 + 4 grp + i
+          if (k0 + 4 * grp + i < n_comp) m[hv][qb] = fmaxf(m[hv][qb], sv[i]);
+      }
+  }
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[hv][qb] = xor_max_groups(m[hv][qb]) * c1;
 }
 
 // Window tiles when the window equals the chunk (w = 64), for a wave whose queries start at
@@ -1059,24 +1072,51 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   //     ragged tile are copied too (they lie inside the buffer; their scores are masked and
   //     their V^T columns are zero or finite).
   if (nt_comp > 0) {
-    // Tiles whose key-norm bound might move the running max, one bit each: the max can only
-    // move if some query's |q| max|k| exceeds it by more than kLazy. Decided here for all
-    // tiles at once, conservatively (the wave's largest |q| against its smallest running max,
-    // which only grows), so a step tests one scalar bit; tiles from 256 on are always checked.
-    uint64_t mayfar[4];
+    // The running max is fixed for the whole compact loop, so its steps have no max pass
+    // and no branch rewrites the accumulators. A compact logit of a query is at most
+    // U = |q| max|k|, the largest key-norm bound of the chunk's compact tiles (prep and
+    // scan). Where U - kLazy exceeds the running max by at most kRaise, the max is raised to
+    // U - kLazy: what is accumulated so far keeps a weight of at least 2^-kRaise, and a
+    // compact weight small enough to underflow (below 2^-126) is negligible next to it.
+    // Otherwise (very large norms, or tiles past the bounds' reach) a pre-pass takes the
+    // exact largest compact logit.
     {
-      float qmax = qn[0][0], mmin = m_run[0][0];
+      float tmax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, 64 * j + lane < nt_comp ? tb[j] : 0.f);
+      tmax = wave_max64(tmax);
+      float m0[HV][QB];
+      bool exact = nt_comp > 256;
 #pragma unroll
       for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          qmax = fmaxf(qmax, qn[hv][qb]);
-          mmin = fminf(mmin, m_run[hv][qb]);
+          m0[hv][qb] = fmaxf(m_run[hv][qb], qn[hv][qb] * tmax - kLazy);
+          exact |= m_run[hv][qb] == -kInf || m0[hv][qb] - m_run[hv][qb] > kRaise;
         }
-      qmax = wave_max64(qmax);
-      mmin = -wave_max64(-mmin);
+      if (__builtin_amdgcn_ballot_w64(exact) != 0) {
+        compact_max<T, D, QB, HV>(krs, n_comp, qf, m0, c1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mayfar[j] = __builtin_amdgcn_ballot_w64(qmax * tb[j] > mmin + kLazy);
+        for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) m0[hv][qb] = fmaxf(m_run[hv][qb], m0[hv][qb]);
+      }
+      bool moved = false;
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) moved |= m0[hv][qb] > m_run[hv][qb];
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float alpha = m_run[hv][qb] == -kInf ? 0.f : __builtin_amdgcn_exp2f(m_run[hv][qb] - m0[hv][qb]);
+#pragma unroll
+            for (int db = 0; db <= NB; ++db) o[hv][db][qb] *= alpha;
+            m_run[hv][qb] = m0[hv][qb];
+          }
+      }
     }
     if constexpr (C::SEQ) {
       // two stages over the fixed regions: tile t in stage t % 2, tile t + 2 issued once
@@ -1100,9 +1140,6 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
           for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
           mask_tile<QB>(sc, kw);
         }
-        const int tj = t >> 6;
-        const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-        if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(sc, o[0], m_run[0], c1);
         sm_exp_pv<T, D, QB>(sc, L + C::stage_off(t & 1) + C::KT, o[0], m_run[0], c1);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's reads of the stage are done (and no copy is in flight)
         lds_barrier();
@@ -1126,7 +1163,9 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
       for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = grp == 0 ? o[hv][NB][qb][0] : 0.f;
-      for (int t = 0; t < nt_comp; ++t) {
+      // One step; RAGGED: the last tile, keys past n_comp masked.
+      auto step = [&](int t, auto ragged) {
+        constexpr bool RAGGED = decltype(ragged)::value;
         if (t + 2 < nt_comp)
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::NL));
         else if (t + 1 < nt_comp)
@@ -1137,23 +1176,19 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
         if (t + 3 < nt_comp) issue(t + 3, (t + 3) & 3);
         f32x4 sc[HV][4][QB];
         qk_tile_hv<T, D, QB, HV>(L + C::stage_off(t & 3), qf, sc);
-        const int nk = n_comp - t * 64;
-        if (nk < 64) {
+        if constexpr (RAGGED) {
           uint32_t kw[QB];
-          const uint32_t rw = range_word(0, nk - 1);
+          const uint32_t rw = range_word(0, n_comp - t * 64 - 1);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
 #pragma unroll
           for (int hv = 0; hv < HV; ++hv) mask_tile<QB>(sc[hv], kw);
         }
-        const int tj = t >> 6;
-        const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-        if ((fw >> (t & 63)) & 1ull) {
-#pragma unroll
-          for (int hv = 0; hv < HV; ++hv) sm_max_lp<D, QB>(sc[hv], o[hv], lp[hv], m_run[hv], c1);
-        }
         sm_exp_pv_hv<T, D, QB, HV>(sc, L + C::stage_off(t & 3) + C::KT, o, lp, m_run, c1);
-      }
+      };
+      const int nt_full = n_comp / 64;  // tiles of 64 keys; a ragged one, if any, follows
+      for (int t = 0; t < nt_full; ++t) step(t, std::false_type{});
+      if (nt_full < nt_comp) step(nt_full, std::true_type{});
 #pragma unroll
       for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
@@ -1187,9 +1222,6 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
         for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
         mask_tile<QB>(s_cur, kw);
       }
-      const int tj = t >> 6;
-      const uint64_t fw = tj == 0 ? mayfar[0] : tj == 1 ? mayfar[1] : tj == 2 ? mayfar[2] : tj == 3 ? mayfar[3] : ~0ull;
-      if ((fw >> (t & 63)) & 1ull) sm_max<D, QB>(s_cur, o[0], m_run[0], c1);
       qk_tile<T, D, QB>(L + C::stage_off((t + 1) & 3), qf[0], s_next);  // after the last tile: unused
       sm_exp_pv<T, D, QB>(s_cur, L + C::stage_off(t & 3) + C::KT, o[0], m_run[0], c1);
     };

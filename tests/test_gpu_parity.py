@@ -109,6 +109,13 @@ CASES = [
     ("bf16-w128-d128", 2, 333, 8, 2, 128, 128, 128, 16, "bf16", 1.0),
     ("bf16-w127-f128-k3", 1, 450, 4, 1, 64, 128, 127, 3, "bf16", 1.0),
     ("f32-w100-d128-f64", 1, 300, 2, 1, 128, 64, 100, 8, "f32", None),
+    # logits of hundreds of log2 units (|q|, |k| ~ 32, planted keys ~ 128): the key-norm
+    # bound of the compact logits is far above every score of the window, so the attention
+    # kernel takes the exact largest compact logit in a pre-pass before the compact tiles
+    ("f32-huge-logits", 1, 400, 4, 1, 64, 64, 64, 8, "f32", 4.0),
+    ("bf16-huge-logits-gqa4", 1, 700, 8, 2, 64, 64, 64, 8, "bf16", 4.0),
+    ("bf16-huge-logits-d128", 1, 500, 4, 1, 128, 128, 64, 16, "bf16", 4.0),
+    ("f32-huge-logits-d128-w96", 1, 450, 2, 1, 128, 128, 96, 16, "f32", 4.0),
 ]
 
 
