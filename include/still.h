@@ -185,10 +185,11 @@ int still_prefill(const still_config* cfg, const void* q, const void* k, const v
                   float* saliency_out, int32_t* sel_idx_out, still_cache* cache,
                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* still_prefill with timing events: if `events` is non-null it must hold 4 events created
- * by the caller; they are recorded on `stream` before the per-chunk preparation kernel,
- * before the chunk-state scan, before the fused attention kernel and after it, so
- * hipEventElapsedTime between consecutive events gives each kernel's duration. */
+/* still_prefill with timing events: if `events` is non-null it must hold 4 entries, each an
+ * event created by the caller or null (not recorded); they are recorded on `stream` before
+ * the per-chunk preparation kernel, before the chunk-state scan, before the fused attention
+ * kernel and after it, so hipEventElapsedTime between consecutive events gives each kernel's
+ * duration. */
 int still_prefill_timed(const still_config* cfg, const void* q, const void* k, const void* v,
                         const void* w_phi, void* out, const int32_t* routing_in,
                         float* saliency_out, int32_t* sel_idx_out, still_cache* cache,

@@ -424,12 +424,12 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
     pa.vselT = cache->sel_v;
     pa.ntiles_sel = static_cast<int>(cache->sel_capacity / 64);
   }
-  if (events) STILL_HIP(hipEventRecord(events[0], stream));
+  if (events && events[0]) STILL_HIP(hipEventRecord(events[0], stream));
   STILL_HIP(still::launch_prep(pa, stream));
-  if (events) STILL_HIP(hipEventRecord(events[1], stream));
+  if (events && events[1]) STILL_HIP(hipEventRecord(events[1], stream));
   float* tilemax = reinterpret_cast<float*>(ws + L.tilemax);
   STILL_HIP(still::launch_scan(d, pa.states, pa.kmaxc, tilemax, L.ntiles_sel, stream));
-  if (events) STILL_HIP(hipEventRecord(events[2], stream));
+  if (events && events[2]) STILL_HIP(hipEventRecord(events[2], stream));
 
   still::AttnArgs aa;
   aa.d = d;
@@ -449,7 +449,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.nw = d.Gr >= 4 ? 4 : (d.Gr == 3 ? 4 : d.Gr);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.Gr + aa.nw - 1) / aa.nw;
   STILL_HIP(still::launch_attn(aa, stream));
-  if (events) STILL_HIP(hipEventRecord(events[3], stream));
+  if (events && events[3]) STILL_HIP(hipEventRecord(events[3], stream));
   if (cache) {
     still::ExportArgs ea;
     ea.d = d;

@@ -59,6 +59,39 @@ __device__ __forceinline__ float saliency_qblock(const T* band, const typename T
     return xor_max_groups(dr) * (1.0f / sqrtf(static_cast<float>(D)));
   }
   // logits in log2 units: scale = log2(e) / sqrt(D)
+  if (L == 1 && window == 64 && band_pos0 >= 0) {
+    // The window is the 63 rows before the diagonal, all inside the sequence: element (j, i)
+    // of the lane's query sits at offset 16 j + e_i from the window's first row, with
+    // e_i = 4 grp + i - r16 in [-15, 15]. Blocks 1 and 2 lie inside the window; block 0 holds
+    // rows before it (e_i < 0), block 3 the diagonal (e_i = 15) and block 4 the diagonal
+    // (e_i = -1) and rows after it (e_i >= 0). Rows outside the window become -inf, so the
+    // max and the sum need no further masks (the same values and order as the general path).
+    float dr = -kInf, mr = -kInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * grp + i - r16;
+      if (e == 15) dr = acc[3][i];
+      if (e == -1) dr = acc[4][i];
+      if (e < 0) acc[0][i] = -kInf;
+      if (e == 15) acc[3][i] = -kInf;
+      if (e >= -1) acc[4][i] = -kInf;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mr = fmaxf(mr, acc[j][i]);
+    const float mx = xor_max_groups(mr) * scale;  // max of the scaled logits (scale > 0)
+    const float dg = xor_max_groups(dr) * scale;
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z += __builtin_amdgcn_exp2f(acc[j][i] * scale - mx);
+    z = xor_sum_groups(z);
+    const float x = dg - mx - __builtin_amdgcn_logf(z);
+    const float sp = fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x)));
+    return sp * 0.69314718055994531f;
+  }
   const int lo = max(r + 64 * L - window, static_cast<int>(-band_pos0));  // first window row inside the sequence
   float mx = -kInf, dg = -kInf;
 #pragma unroll

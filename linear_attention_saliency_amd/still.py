@@ -178,7 +178,7 @@ class Prefill:
 
     def __call__(self, q, k, v, w_phi, out, *, routing=None, saliency=None, sel_idx=None, cache=None,
                  stream=None, events=None):
-        """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4).
+        """events: optional array of 4 hipEvent_t handles (ctypes c_void_p * 4); a None entry is not recorded.
         cache: optional DecodeCache with no tokens; it is left holding the sequence.
         routing: optional selection override (host or device tensor, or array), passed to the
         library as host memory."""
