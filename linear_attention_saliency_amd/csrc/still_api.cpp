@@ -93,7 +93,7 @@ size_t elem_bytes(const still_config* c) { return c->dtype == STILL_BF16 ? 2 : 4
 inline int64_t odd_tiles(int64_t n) { return n > 0 ? (n | 1) : 0; }
 
 struct WsLayout {
-  size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, tilemax, routing, total;
+  size_t sal, selmask, ksel, vselT, vT, phik, states, kmaxc, kall, tilemax, routing, total;
   int ntiles_sel;
 };
 
@@ -118,6 +118,7 @@ WsLayout ws_layout(const still_config* c) {
   L.phik = take(bkv * d.T * d.DF * es);
   L.states = take(bh * d.nC * d.R * (d.bf16 ? 2 : 4));
   L.kmaxc = take(bh * d.nC * sizeof(float));
+  L.kall = take(bh * d.nC * sizeof(float));
   L.tilemax = take(bh * (L.ntiles_sel > 0 ? L.ntiles_sel : 1) * sizeof(float));
   L.routing = take(bh * d.nCc * d.topk * sizeof(int32_t));  // a copy of routing_in, if given
   L.total = off;
@@ -419,6 +420,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   pa.vselT = ws + L.vselT;
   pa.ntiles_sel = L.ntiles_sel;
   pa.kmaxc = reinterpret_cast<float*>(ws + L.kmaxc);
+  pa.kall = reinterpret_cast<float*>(ws + L.kall);
   if (cache && cfg->top_k > 0) {  // the compact rows go straight into the cache
     pa.ksel = cache->sel_k;
     pa.vselT = cache->sel_v;
@@ -445,6 +447,7 @@ int still_prefill_timed(const still_config* cfg, const void* q, const void* k, c
   aa.out = out;
   aa.ntiles_sel = pa.ntiles_sel;
   aa.tilemax = tilemax;
+  aa.kall = pa.kall;
   aa.tm_stride = L.ntiles_sel;
   aa.nw = d.Gr >= 4 ? 4 : (d.Gr == 3 ? 4 : d.Gr);  // query heads per workgroup: 1, 2 or 4
   aa.gsplit = (d.Gr + aa.nw - 1) / aa.nw;

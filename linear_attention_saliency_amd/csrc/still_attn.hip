@@ -219,8 +219,8 @@ __device__ __forceinline__ void qk_tile_hv(const T* lk, const typename Tr<T>::fr
 // row sums are not a ones block of the product here but per-lane partials lp (each lane
 // adds the probabilities it holds, already rounded as the product uses them, by bf16 dot2;
 // the four lane groups are summed once at the end), which frees that block's registers.
-template <typename T, int D, int QB, int HV>
-__device__ __forceinline__ void sm_exp_pv_hv(const f32x4 (&s)[HV][4][QB], const T* lv, f32x4 (&o)[HV][D / 16 + 1][QB],
+template <typename T, int D, int QB, int HV, int NO>
+__device__ __forceinline__ void sm_exp_pv_hv(const f32x4 (&s)[HV][4][QB], const T* lv, f32x4 (&o)[HV][NO][QB],
                                              float (&lp)[HV][QB], const float (&m_run)[HV][QB], float c1) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
@@ -1254,6 +1254,505 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
   }
 }
 
+// ======================================================================================
+// Window = chunk at bf16, head_dim = feat_dim = 64, four query heads per workgroup (the
+// Llama-3.2-1B-shaped layer), under a softmax frame fixed up front.
+//
+// A wave takes one query head and all 64 queries of chunk c (two 32-query halves). Before
+// any tile, each query's frame m0 (log2 units) is set so that no weight can pass 2^32 and
+// nothing is ever rescaled: a softmax logit is at most |q| Kmax c1 and a linear weight
+// phi(q).phi(k) at most |q| Kmax (the NP-Map preserves norms), where Kmax is the largest key
+// norm of the window chunks (kall) and of the compact tiles (tilemax). So
+//   m0 = max(a_ii c1, |q| Kmax c1 - kLazy, log2(|q| Kmax) - kLazy),
+// with a_ii c1 the query's own logit, which is always a softmax term. Where m0 is more than
+// kRaise above a_ii c1, the wave takes the exact largest log-weight over all of its terms
+// instead (global loads only: no LDS, no barrier). Then, with no max pass anywhere:
+//   1. per query half: phi(q) (W_h from LDS), the prefix read-out (one entry of weight
+//      D 2^-m0 and value N / D), chunk c (causal) and chunk c-1 (softmax keys p > r or
+//      selected, linear keys the rest, one P for both);
+//   2. the compact tiles through a four-stage LDS ring (stage 0 of its own, stages 1..3 over
+//      the window regions once the window is done), copies issued three tiles ahead;
+//   3. the normalised output through LDS, so every position's four heads leave as one
+//      contiguous 512-byte row.
+// Every P is 2^(a c1 - m0) or phi(q).phi(k) 2^-m0; the row sums are per-lane dot2 partials.
+struct W64 {
+  static constexpr int D = 64, QB = 2, HV = 2, NW = 4, NB = 4;
+  static constexpr int KT = 64 * 64, STAGE = 2 * KT;  // a 64 x 64 tile; a compact stage (K, V^T)
+  // window regions (three compact stages' worth), then compact stage 0 and W_h
+  static constexpr int R_PHIP = 0, R_VP = R_PHIP + KT, R_VC = R_VP + KT, R_KC = R_VC + KT, R_KP = R_KC + KT,
+                       R_ST = R_KP + KT, R_S0 = R_ST + KT, R_W = R_S0 + STAGE, LDS_ELEMS = R_W + KT;
+  static constexpr int LDS_BYTES = LDS_ELEMS * 2;  // 72 KiB: two workgroups per CU
+  static constexpr int NL = 4;                     // copy instructions per wave for one compact tile
+  static constexpr int NFIX = 14;                  // ... for the six window / state tiles and W_h
+  static __device__ __forceinline__ int stage_off(int s) { return s == 0 ? R_S0 : (s - 1) * STAGE; }
+};
+static_assert(W64::LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+
+// acc + the dot product of two fragments (bf16: four dot2; fp32: fmas)
+template <typename F> __device__ __forceinline__ float frag_dot(const F& x, const F& y, float acc) {
+  if constexpr (sizeof(x[0]) == 2) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{x[2 * j], x[2 * j + 1]}, bf16x2_t{y[2 * j], y[2 * j + 1]}, acc, false);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += x[j] * y[j];
+  }
+  return acc;
+}
+
+// phi(q) = |q| m / |m|, m = elu(W_h q) + 1, for the 16-query blocks of qf (B-operand, SK
+// over d); W_h fragments from wfrag(fb, ks). Leaves PK-ordered B fragments over f.
+template <typename T, int D, int DF, int QB, typename WF>
+__device__ __forceinline__ void phi_q_frags(const typename Tr<T>::frag (&qf)[QB][D / 32], WF wfrag,
+                                            typename Tr<T>::frag (&pq)[QB][DF / 32]) {
+  using TT = Tr<T>;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    f32x4 pacc[DF / 16];
+#pragma unroll
+    for (int fb = 0; fb < DF / 16; ++fb) {
+      pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) TT::mma(pacc[fb], wfrag(fb, ks), qf[qb][ks]);
+    }
+    float m2 = 0.f, x2 = 0.f;
+#pragma unroll
+    for (int fb = 0; fb < DF / 16; ++fb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zv = pacc[fb][i];
+        const float mv = zv > 0.f ? zv + 1.f : __builtin_amdgcn_exp2f(zv * kLog2e);
+        pacc[fb][i] = mv;
+        m2 += mv * mv;
+      }
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) x2 = frag_dot(qf[qb][ks], qf[qb][ks], x2);
+    const float sc = norm_ratio(xor_sum_groups(x2), xor_sum_groups(m2));
+#pragma unroll
+    for (int fs = 0; fs < DF / 32; ++fs)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pq[qb][fs][e] = TT::from_f(pacc[2 * fs + e / 4][e % 4] * sc);
+  }
+}
+
+// The exact frame of W64's queries (one wave, both halves): the largest of the softmax logits
+// (compact keys, chunk c up to the query, chunk c-1 past the query or selected; times c1) and
+// of log2 of the whole linear weight (prefix state plus chunk c-1's other keys). Global loads
+// only, so the other waves are not held up.
+template <typename T>
+__device__ __forceinline__ void w64_exact_frame(
+    const typename Tr<T>::frag (&qf)[W64::HV][W64::QB][2], float (&m0)[W64::HV][W64::QB],
+    __amdgpu_buffer_rsrc_t krs, int n_comp, __amdgpu_buffer_rsrc_t kc_rs, __amdgpu_buffer_rsrc_t kp_rs, int kst,
+    __amdgpu_buffer_rsrc_t fp_rs, uint64_t selprev, const T* Wh, __amdgpu_buffer_rsrc_t z_rs, bool has_prev,
+    float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  constexpr int QB = W64::QB, HV = W64::HV;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  float cm[HV][QB];
+  compact_max<T, 64, QB, HV>(krs, n_comp, qf, cm, c1);
+  const uint32_t selw = bits_word(selprev);
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv) {
+    frag pq[QB][2];
+    phi_q_frags<T, 64, 64, QB>(qf[hv], [&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * 64 + ks * 32 + grp * 8); },
+                               pq);
+    float smax[QB], lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      smax[qb] = cm[hv][qb];
+      lsum[qb] = 0.f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      frag ka[2], kp[2], fa[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        ka[ks] = TT::bload8(kc_rs, ((kb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
+        kp[ks] = TT::bload8(kp_rs, ((kb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
+        fa[ks] = TT::bload8(fp_rs, ((kb * 16 + r16) * 64 + ks * 32 + grp * 8) * 2, 0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sp = sc, ls = sc;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          TT::mma(sc, ka[ks], qf[hv][qb][ks]);
+          TT::mma(sp, kp[ks], qf[hv][qb][ks]);
+          TT::mma(ls, fa[ks], pq[qb][ks]);
+        }
+        const int r = hv * 32 + qb * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = kb * 16 + 4 * grp + i;
+          const bool sel = (selw >> (kb * 4 + i)) & 1u;
+          if (p <= r) smax[qb] = fmaxf(smax[qb], sc[i] * c1);
+          if (has_prev && (p > r || sel)) smax[qb] = fmaxf(smax[qb], sp[i] * c1);
+          if (has_prev && p <= r && !sel) lsum[qb] += ls[i];
+        }
+      }
+    }
+    // the prefix state's linear weight phi(q).z: every row of the A operand is z
+    frag zf[2];
+#pragma unroll
+    for (int fs = 0; fs < 2; ++fs) zf[fs] = TT::bload8(z_rs, (fs * 32 + grp * 8) * 2, 0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4 dz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int fs = 0; fs < 2; ++fs) TT::mma(dz, zf[fs], pq[qb][fs]);
+      const float la = xor_sum_groups(lsum[qb]) + dz[0];
+      const float mx = xor_max_groups(smax[qb]);
+      m0[hv][qb] = la > 0.f ? fmaxf(mx, __log2f(la)) : mx;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
+  using C = W64;
+  constexpr int QB = C::QB, HV = C::HV, NW = C::NW, NB = C::NB, D = C::D, KT = C::KT;
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  using SW = Swz<T, 64>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  T* L = reinterpret_cast<T*>(lds_raw);
+
+  const Dims& d = a.d;
+  const T* q = static_cast<const T*>(a.q);
+  const T* kk = static_cast<const T*>(a.k);
+  const T* vT = static_cast<const T*>(a.vT);
+  const T* phik = static_cast<const T*>(a.phik);
+  // work item: heaviest chunks first; within a chunk consecutive (b, h, head split), so each
+  // of the eight XCDs keeps a fixed set of KV heads in its L2
+  const int BHG = d.B * d.Hr * a.gsplit;
+  const int c = d.nC - 1 - static_cast<int>(blockIdx.x) / BHG;
+  const int bhg = static_cast<int>(blockIdx.x) % BHG;
+  const int gs = bhg % a.gsplit, bh = bhg / a.gsplit;
+  const int b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G;
+  const long long bkv = static_cast<long long>(b) * d.Hkv + h;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = rh * d.Gr + gs * NW + wave;  // every head of the split exists (Gr % 4 == 0)
+  const long long T_ = d.T;
+  const long long t0 = static_cast<long long>(c) * kChunk;
+  const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
+  const float c1 = kLog2e / sqrtf(static_cast<float>(D));
+  const bool has_prev = c >= 1, has_state = c >= 2;
+  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
+  const int nt_comp = (n_comp + 63) / 64;
+  const int kst = d.Hkv * D;  // row stride of k
+  const long long tp = has_prev ? t0 - kChunk : t0;
+
+  const T* kb_ptr = static_cast<const T*>(a.ksel) + static_cast<long long>(bh) * a.ntiles_sel * 64 * D;
+  const T* vb_ptr = static_cast<const T*>(a.vselT) + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
+  DmaTile<T, D, 64, NW> dk;
+  DmaTile<T, 64, D, NW> dv;
+  dk.init(D);
+  dv.init(64);
+  const auto krs = make_rsrc(kb_ptr, static_cast<uint32_t>(nt_comp) * KT * 2u);
+  const auto vrs = make_rsrc(vb_ptr, static_cast<uint32_t>(nt_comp) * KT * 2u);
+  auto issue = [&](int t, int stage) {
+    T* st = L + C::stage_off(stage);
+    dk.issue(st, krs, t * KT * 2);
+    dv.issue(st + KT, vrs, t * KT * 2);
+  };
+
+  // ---- 1. register operands: the queries and their own keys (B-operand layout), the tile
+  //      and window key-norm bounds, the selection of chunk c-1 ------------------------------
+  frag qf[HV][QB][2], kd[HV][QB][2];
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv) {
+    const long long q0 = t0 + hv * 32;
+    const long long nq = T_ - q0 < 32 ? T_ - q0 : 32;
+    const int qrow = d.Hq * D;
+    const auto qrs = make_rsrc(q + ((b * T_ + (nq > 0 ? q0 : 0)) * d.Hq + hq) * D,
+                               nq > 0 ? static_cast<uint32_t>(((nq - 1) * qrow + D) * 2) : 0u);
+    const auto krd = make_rsrc(kk + ((b * T_ + (nq > 0 ? q0 : 0)) * d.Hkv + h) * D,
+                               nq > 0 ? static_cast<uint32_t>(((nq - 1) * kst + D) * 2) : 0u);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        qf[hv][qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * 2, 0);
+        kd[hv][qb][ks] = TT::bload8(krd, ((qb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
+      }
+  }
+  float tb[4];
+  {
+    const int ntb = nt_comp < 256 ? nt_comp : 256;
+    const auto trs = make_rsrc(a.tilemax + static_cast<long long>(bh) * a.tm_stride, static_cast<uint32_t>(ntb) * 4u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tb[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, (64 * j + lane) * 4, 0, 0));
+  }
+  const auto selv = __builtin_amdgcn_raw_buffer_load_b64(
+      make_rsrc(a.selmask + static_cast<long long>(bh) * d.nC + (has_prev ? c - 1 : 0), has_prev ? 8u : 0u), 0, 0, 0);
+  const float kwin = fmaxf(a.kall[static_cast<long long>(bh) * d.nC + c],
+                           has_prev ? a.kall[static_cast<long long>(bh) * d.nC + c - 1] : 0.f);
+
+  // ---- 2. copies: the window tiles, the prefix state and W_h into their regions, then
+  //      compact tile 0 into stage 0 (zero-filled where absent) -------------------------------
+  const T* Sg = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (has_state ? c - 2 : 0)) * d.R;
+  const T* Wh = static_cast<const T*>(a.w) + static_cast<long long>(h) * 64 * D;
+  dma_tile<T, 64, 64, NW>(L + C::R_PHIP, phik + (bkv * T_ + tp) * 64, 64, has_prev ? 64 : 0);
+  dma_tile<T, 64, 64, NW>(L + C::R_VP, vT + (bkv * d.nC + (has_prev ? c - 1 : c)) * D * 64, 64, has_prev ? D : 0);
+  dma_tile<T, 64, 64, NW>(L + C::R_VC, vT + (bkv * d.nC + c) * D * 64, 64, D);
+  dma_tile<T, 64, 64, NW>(L + C::R_KC, kk + ((b * T_ + t0) * d.Hkv + h) * D, kst, nvalid);
+  dma_tile<T, 64, 64, NW>(L + C::R_KP, kk + ((b * T_ + tp) * d.Hkv + h) * D, kst, has_prev ? 64 : 0);
+  dma_tile<T, 64, 64, NW>(L + C::R_ST, Sg, 64, has_state ? D : 0);
+  dma_tile<T, 64, 64, NW>(L + C::R_W, Wh, D, 64);
+  issue(0, 0);
+  // z of the prefix state (A operand of the denominator, the same in every row)
+  frag zf[2];
+  {
+    const auto zrs = make_rsrc(Sg + 64 * D, has_state ? 64u * 2u : 0u);
+#pragma unroll
+    for (int fs = 0; fs < 2; ++fs) zf[fs] = TT::bload8(zrs, (fs * 32 + grp * 8) * 2, 0);
+  }
+
+  // ---- 3. the frame ---------------------------------------------------------------------
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NFIX + C::NL + 2));  // the register operands
+  const uint64_t selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
+  float kmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kmax = fmaxf(kmax, 64 * j + lane < nt_comp ? tb[j] : 0.f);
+  kmax = fmaxf(wave_max64(kmax), kwin);
+  float m0[HV][QB];
+  bool exact = nt_comp > 256;  // tiles past 256 carry no bound here
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float dq = 0.f, q2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dq = frag_dot(qf[hv][qb][ks], kd[hv][qb][ks], dq);
+        q2 = frag_dot(qf[hv][qb][ks], qf[hv][qb][ks], q2);
+      }
+      const float ref = xor_sum_groups(dq) * c1;                                      // the query's own logit
+      const float ub = __builtin_amdgcn_sqrtf(xor_sum_groups(q2)) * 1.001f * kmax;  // >= |q| |k|, any key
+      float m = fmaxf(ref, ub * c1 - kLazy);
+      if (ub > 0.f) m = fmaxf(m, __log2f(ub) - kLazy);
+      exact |= m - ref > kRaise;
+      m0[hv][qb] = m;
+    }
+  if (__builtin_amdgcn_ballot_w64(exact) != 0)
+    w64_exact_frame<T>(qf, m0, krs, n_comp,
+                       make_rsrc(kk + ((b * T_ + t0) * d.Hkv + h) * D, static_cast<uint32_t>(((nvalid - 1) * kst + D) * 2)),
+                       make_rsrc(kk + ((b * T_ + tp) * d.Hkv + h) * D, has_prev ? static_cast<uint32_t>((63 * kst + D) * 2) : 0u),
+                       kst, make_rsrc(phik + (bkv * T_ + tp) * 64, has_prev ? 64u * 64u * 2u : 0u), selprev, Wh,
+                       make_rsrc(Sg + 64 * D, has_state ? 64u * 2u : 0u), has_prev, c1);
+  f32x4 o[HV][NB][QB];
+  float lp[HV][QB];  // row sums: per-lane partials, summed over the lane groups at the end
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      lp[hv][qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) o[hv][db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));  // everything but compact tile 0
+  lds_barrier();
+
+  // ---- 5. per query half: phi(q), the prefix read-out, chunk c, chunk c-1 ----------------
+  const uint32_t selw = bits_word(selprev);
+  bool dmask[4];  // key position <= query position, on a diagonal block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv) {
+    frag pq[QB][2];
+    phi_q_frags<T, 64, 64, QB>(qf[hv], [&](int fb, int ks) { return SW::load8(L + C::R_W, fb * 16 + r16, ks * 32 + grp * 8); },
+                               pq);
+    // prefix read-out: N = S^T phi(q) (state rows d, PK features) and D = phi(q).z
+    if (has_state) {
+      f32x4 la[NB][QB], dz[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        dz[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NB; ++db) la[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int fs = 0; fs < 2; ++fs) {
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const frag sa = SW::load8(L + C::R_ST, db * 16 + r16, fs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TT::mma(la[db][qb], sa, pq[qb][fs]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TT::mma(dz[qb], zf[fs], pq[qb][fs]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float dt = dz[qb][0];
+        // weight D 2^-m0 taken in the log domain (D may be far outside 2^-m0's range)
+        const float wgt = dt > 0.f ? __builtin_amdgcn_exp2f(__log2f(dt) - m0[hv][qb]) : 0.f;
+        const float f = dt > 0.f ? wgt * __builtin_amdgcn_rcpf(dt) : 0.f;
+#pragma unroll
+        for (int db = 0; db < NB; ++db) o[hv][db][qb] += la[db][qb] * f;
+        if (grp == 0) lp[hv][qb] += wgt;
+      }
+    }
+    // chunk c: softmax keys p <= r
+    {
+      f32x4 s[4][QB];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const frag ka = SW::load8(L + C::R_KC, kb * 16 + r16, ks * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (kb <= 2 * hv + qb) TT::mma(s[kb][qb], ka, qf[hv][qb][ks]);
+        }
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        frag pf[QB];
+        bool live = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qblk = 2 * hv + qb;  // 16-query block of the chunk
+          live |= 2 * hs <= qblk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kb = 2 * hs + e / 4, i = e % 4;
+            float p = 0.f;
+            if (kb < qblk || (kb == qblk && dmask[i]))
+              p = __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
+            pf[qb][e] = TT::from_f(p);
+          }
+        }
+        if (!live) continue;
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const frag va = SW::load8(L + C::R_VC, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (2 * hs <= 2 * hv + qb) TT::mma(o[hv][db][qb], va, pf[qb]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (2 * hs <= 2 * hv + qb) lp[hv][qb] = row_sum_add(pf[qb], lp[hv][qb]);
+      }
+    }
+    // chunk c-1: softmax keys p > r or selected, linear keys the rest (one P for both)
+    if (has_prev) {
+      f32x4 s[4][QB], ls[4][QB];
+      qk_tile<T, D, QB>(L + C::R_KP, qf[hv], s);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int fs = 0; fs < 2; ++fs) {
+          const frag fa = SW::load8(L + C::R_PHIP, kb * 16 + r16, fs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (kb <= 2 * hv + qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+        }
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        frag pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qblk = 2 * hv + qb;
+          const float sh = __builtin_amdgcn_exp2f(-0.5f * m0[hv][qb]);  // 2^-m0 as two factors
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kb = 2 * hs + e / 4, i = e % 4;
+            const bool sel = (selw >> (kb * 4 + i)) & 1u;
+            // key p vs query r: p > r on blocks past the query block, and past the diagonal
+            const bool after = kb > qblk || (kb == qblk && !dmask[i]);
+            const float ev = __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
+            const float lv = (kb <= qblk) ? (ls[kb][qb][i] * sh) * sh : 0.f;
+            pf[qb][e] = TT::from_f((after || sel) ? ev : lv);
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const frag va = SW::load8(L + C::R_VP, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[qb]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = row_sum_add(pf[qb], lp[hv][qb]);
+      }
+    }
+  }
+
+  // ---- 4. the compact tiles: tile t in stage t % 4; tiles 1 and 2 are issued once every
+  //      wave is done with the window regions, tile t + 3 in step t (into the stage of tile
+  //      t - 1, free after the step's barrier). Step t waits for its own copies of tile t
+  //      (those of tiles t + 1 and t + 2 may still be in flight). -------------------------
+  if (nt_comp > 0) {
+    lds_barrier();  // every wave is done with the window regions
+    if (1 < nt_comp) issue(1, 1);
+    if (2 < nt_comp) issue(2, 2);
+    auto step = [&](int t, auto ragged) {
+      constexpr bool RAGGED = decltype(ragged)::value;
+      if (t + 2 < nt_comp)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::NL));
+      else if (t + 1 < nt_comp)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      if (t + 3 < nt_comp) issue(t + 3, (t + 3) & 3);
+      f32x4 sc[HV][4][QB];
+      qk_tile_hv<T, D, QB, HV>(L + C::stage_off(t & 3), qf, sc);
+      if constexpr (RAGGED) {
+        uint32_t kw[QB];
+        const uint32_t rw = range_word(0, n_comp - t * 64 - 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) kw[qb] = rw;
+#pragma unroll
+        for (int hv = 0; hv < HV; ++hv) mask_tile<QB>(sc[hv], kw);
+      }
+      sm_exp_pv_hv<T, D, QB, HV>(sc, L + C::stage_off(t & 3) + KT, o, lp, m0, c1);
+    };
+    const int nt_full = n_comp / 64;
+    for (int t = 0; t < nt_full; ++t) step(t, std::false_type{});
+    if (nt_full < nt_comp) step(nt_full, std::true_type{});
+  }
+
+  // ---- 6. normalise, stage in LDS as [position][4 heads x 64], store whole rows ----------
+  using SO = Swz<T, 4 * D>;
+  __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS is left in flight (an absent tile 0's included)
+  lds_barrier();                  // every wave is done with the tiles
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = xor_sum_groups(lp[hv][qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int r = hv * 32 + qb * 16 + r16;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        typename TT::quad ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = TT::from_f(o[hv][db][qb][i] * inv);
+        *reinterpret_cast<typename TT::quad*>(L + SO::off(r, wave * D + db * 16 + 4 * grp)) = ov;
+      }
+    }
+  __syncthreads();
+  T* out = static_cast<T*>(a.out) + ((b * T_ + t0) * d.Hq + rh * d.Gr + gs * NW) * D;
+#pragma unroll
+  for (int j = 0; j < 64 * 4 * D / 8 / 256; ++j) {
+    const int idx = j * 256 + tid, r = idx / 32, col = (idx % 32) * 8;
+    if (r < nvalid) TT::store8(out + static_cast<long long>(r) * d.Hq * D + col, SO::load8(L, r, col));
+  }
+}
+
 template <typename T, int D, int DF, int NH, bool BAND>
 static hipError_t attn_nhb(const AttnArgs& a, hipStream_t s) {
   using C = AttnCfg<T, D, DF, NH>;
@@ -1273,6 +1772,15 @@ static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
 
 template <typename T, int D, int DF>
 static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && D == 64 && DF == 64) {
+    if (a.nw == 4 && a.d.window == kChunk && a.d.Gr % 4 == 0) {
+      const dim3 grid(a.d.nC * a.d.B * a.d.Hr * a.gsplit);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_w64_kernel<T>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, W64::LDS_BYTES);
+      hipLaunchKernelGGL((attn_w64_kernel<T>), grid, dim3(256), W64::LDS_BYTES, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.nw == 4) return attn_nh<T, D, DF, 4>(a, s);
   if (a.nw == 2) return attn_nh<T, D, DF, 2>(a, s);
   if (a.nw == 1) return attn_nh<T, D, DF, 1>(a, s);

@@ -38,6 +38,7 @@ struct PrepArgs {
   void* vselT;                // [B,Hr,ntiles_sel,D,64]: compact V rows, same tile layout
   int ntiles_sel;             // compact tiles per (b, KV head): >= ceil(nCc*topk / 64)
   float* kmaxc;               // [B,Hr,nC]: largest |k| among each chunk's selected keys
+  float* kall;                // [B,Hr,nC]: largest |k| among all of each chunk's keys
 };
 
 struct AttnArgs {
@@ -54,6 +55,7 @@ struct AttnArgs {
   void* out;
   int ntiles_sel;
   const float* tilemax; // [B,Hkv,tm_stride]: largest |k| in each compact tile
+  const float* kall;    // [B,Hr,nC]: largest |k| among all of each chunk's keys
   int tm_stride;
   int nw;               // query heads per workgroup (1, 2 or 4)
   int gsplit;           // workgroups per (b, kv head, chunk)

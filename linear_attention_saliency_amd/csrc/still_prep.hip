@@ -152,10 +152,12 @@ void prep_kernel(PrepArgs a) {
     }
     // the largest key norm among the selected keys (xn2 holds |k|^2 of the chunk's rows)
     const float kn = wave_max64(((m >> lane) & 1ull) ? xn2[lane] : 0.f);
+    const float ka = wave_max64(xn2[lane]);  // every key of the chunk (rows past the end are zero)
     if (lane == 0) {
       s_mask = m;
       a.selmask[static_cast<long long>(bh) * d.nC + c] = m;
       a.kmaxc[static_cast<long long>(bh) * d.nC + c] = sqrtf(kn);
+      a.kall[static_cast<long long>(bh) * d.nC + c] = sqrtf(ka);
     }
     if ((m >> lane) & 1ull) {
       const int slot = __popcll(m & ((1ull << lane) - 1ull));
