@@ -291,6 +291,41 @@ __device__ __forceinline__ void compact_max(__amdgpu_buffer_rsrc_t kr, int n_com
     for (int qb = 0; qb < QB; ++qb) mx[hv][qb] = xor_max_groups(m[hv][qb]) * c1;
 }
 
+// sm_exp_pv_hv with the row sums riding along in the product: an all-ones A block adds every
+// probability of a query's column into every element of o[hv][D / 16][qb].
+template <typename T, int D, int QB, int HV>
+__device__ __forceinline__ void sm_exp_pv_ones_hv(const f32x4 (&s)[HV][4][QB], const T* lv,
+                                                  f32x4 (&o)[HV][D / 16 + 1][QB], const float (&m_run)[HV][QB],
+                                                  float c1) {
+  using TT = Tr<T>;
+  using frag = typename TT::frag;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
+  const frag one = ones_frag<T>();
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    frag pf[HV][QB];
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[hv][qb][e] = TT::from_f(__builtin_amdgcn_exp2f(s[hv][2 * hs + e / 4][qb][e % 4] * c1 - m_run[hv][qb]));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const frag va = Swz<T, 64>::load8(lv, db * 16 + r16, hs * 32 + grp * 8);
+#pragma unroll
+      for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[hv][qb]);
+    }
+#pragma unroll
+    for (int hv = 0; hv < HV; ++hv)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][D / 16][qb], one, pf[hv][qb]);
+  }
+}
+
 // Window tiles when the window equals the chunk (w = 64), for a wave whose queries start at
 // QOFF within the chunk. Lane (r16, grp) holds keys kb*16 + 4 grp + i of query
 // QOFF + qb*16 + r16, so a (key block, query block) pair is of one of three kinds, known at
@@ -1268,13 +1303,17 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 // kRaise above a_ii c1, the wave takes the exact largest log-weight over all of its terms
 // instead (global loads only: no LDS, no barrier). Then, with no max pass anywhere:
 //   1. per query half: phi(q) (W_h from LDS), the prefix read-out (one entry of weight
-//      D 2^-m0 and value N / D), chunk c (causal) and chunk c-1 (softmax keys p > r or
-//      selected, linear keys the rest, one P for both);
+//      D 2^-m0 and value N / D), chunk c (causal) and chunk c-1 (softmax keys p > r, linear
+//      keys p <= r, one P for both);
 //   2. the compact tiles through a four-stage LDS ring (stage 0 of its own, stages 1..3 over
-//      the window regions once the window is done), copies issued three tiles ahead;
+//      the window regions once the window is done), copies issued three tiles ahead. They
+//      include chunk c-1's selected keys, which are softmax keys for every query of chunk c,
+//      so chunk c-1's tile needs no per-key selection test: their V^T columns are zeroed in
+//      LDS and its row sums use a not-selected vector;
 //   3. the normalised output through LDS, so every position's four heads leave as one
 //      contiguous 512-byte row.
-// Every P is 2^(a c1 - m0) or phi(q).phi(k) 2^-m0; the row sums are per-lane dot2 partials.
+// Every P is 2^(a c1 - m0) or phi(q).phi(k) 2^-m0; the row sums ride along in the products
+// as an extra all-ones (or not-selected) A block.
 struct W64 {
   static constexpr int D = 64, QB = 2, HV = 2, NW = 4, NB = 4;
   static constexpr int KT = 64 * 64, STAGE = 2 * KT;  // a 64 x 64 tile; a compact stage (K, V^T)
@@ -1441,7 +1480,9 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
   const float c1 = kLog2e / sqrtf(static_cast<float>(D));
   const bool has_prev = c >= 1, has_state = c >= 2;
-  const int n_comp = c >= 2 ? (c - 1) * d.topk : 0;
+  // compact rows of chunks <= c-1: chunk c-1's selected keys are softmax keys for every query
+  // of chunk c, so they join the compact tiles (their rows follow chunk c-2's)
+  const int n_comp = c * d.topk;
   const int nt_comp = (n_comp + 63) / 64;
   const int kst = d.Hkv * D;  // row stride of k
   const long long tp = has_prev ? t0 - kChunk : t0;
@@ -1545,21 +1586,33 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
                        make_rsrc(kk + ((b * T_ + tp) * d.Hkv + h) * D, has_prev ? static_cast<uint32_t>((63 * kst + D) * 2) : 0u),
                        kst, make_rsrc(phik + (bkv * T_ + tp) * 64, has_prev ? 64u * 64u * 2u : 0u), selprev, Wh,
                        make_rsrc(Sg + 64 * D, has_state ? 64u * 2u : 0u), has_prev, c1);
-  f32x4 o[HV][NB][QB];
-  float lp[HV][QB];  // row sums: per-lane partials, summed over the lane groups at the end
+  // o[hv][NB]: the row sums, riding along in the products (an all-ones A block)
+  f32x4 o[HV][NB + 1][QB];
 #pragma unroll
   for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      lp[hv][qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int db = 0; db < NB; ++db) o[hv][db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int db = 0; db <= NB; ++db) o[hv][db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const frag ones = ones_frag<T>();
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));  // everything but compact tile 0
   lds_barrier();
+  // chunk c-1's selected keys are taken with the compact tiles: zero their V^T columns here,
+  // and count chunk c-1's row sums with a not-selected vector instead of ones
+  if (has_prev && selprev != 0) {
+    if (tid < 64)
+      for (uint64_t m = selprev; m != 0; m &= m - 1)
+        L[C::R_VP + SW::off(tid, pk_pos(static_cast<int>(__builtin_ctzll(m))))] = TT::from_f(0.f);
+    __syncthreads();
+  }
+  frag nsel[2];  // A operand: 1 for the keys of chunk c-1 that are not selected (PK order)
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      nsel[hs][e] = TT::from_f(((selprev >> (hs * 32 + 16 * (e / 4) + 4 * grp + e % 4)) & 1ull) ? 0.f : 1.f);
 
   // ---- 5. per query half: phi(q), the prefix read-out, chunk c, chunk c-1 ----------------
-  const uint32_t selw = bits_word(selprev);
   bool dmask[4];  // key position <= query position, on a diagonal block
 #pragma unroll
   for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
@@ -1596,7 +1649,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
         const float f = dt > 0.f ? wgt * __builtin_amdgcn_rcpf(dt) : 0.f;
 #pragma unroll
         for (int db = 0; db < NB; ++db) o[hv][db][qb] += la[db][qb] * f;
-        if (grp == 0) lp[hv][qb] += wgt;
+        o[hv][NB][qb] += wgt;
       }
     }
     // chunk c: softmax keys p <= r
@@ -1641,10 +1694,11 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          if (2 * hs <= 2 * hv + qb) lp[hv][qb] = row_sum_add(pf[qb], lp[hv][qb]);
+          if (2 * hs <= 2 * hv + qb) TT::mma(o[hv][NB][qb], ones, pf[qb]);
       }
     }
-    // chunk c-1: softmax keys p > r or selected, linear keys the rest (one P for both)
+    // chunk c-1: softmax keys p > r, linear keys p <= r (one P for both); the selected keys
+    // are in the compact tiles, and their columns here add nothing (zero V^T, zero in nsel)
     if (has_prev) {
       f32x4 s[4][QB], ls[4][QB];
       qk_tile<T, D, QB>(L + C::R_KP, qf[hv], s);
@@ -1670,12 +1724,15 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kb = 2 * hs + e / 4, i = e % 4;
-            const bool sel = (selw >> (kb * 4 + i)) & 1u;
             // key p vs query r: p > r on blocks past the query block, and past the diagonal
-            const bool after = kb > qblk || (kb == qblk && !dmask[i]);
-            const float ev = __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
-            const float lv = (kb <= qblk) ? (ls[kb][qb][i] * sh) * sh : 0.f;
-            pf[qb][e] = TT::from_f((after || sel) ? ev : lv);
+            float pv;
+            if (kb > qblk)
+              pv = __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
+            else if (kb < qblk)
+              pv = (ls[kb][qb][i] * sh) * sh;
+            else
+              pv = dmask[i] ? (ls[kb][qb][i] * sh) * sh : __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
+            pf[qb][e] = TT::from_f(pv);
           }
         }
 #pragma unroll
@@ -1685,7 +1742,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[qb]);
         }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) lp[hv][qb] = row_sum_add(pf[qb], lp[hv][qb]);
+        for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][NB][qb], nsel[hs], pf[qb]);
       }
     }
   }
@@ -1718,7 +1775,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
         for (int hv = 0; hv < HV; ++hv) mask_tile<QB>(sc[hv], kw);
       }
-      sm_exp_pv_hv<T, D, QB, HV>(sc, L + C::stage_off(t & 3) + KT, o, lp, m0, c1);
+      sm_exp_pv_ones_hv<T, D, QB, HV>(sc, L + C::stage_off(t & 3) + KT, o, m0, c1);
     };
     const int nt_full = n_comp / 64;
     for (int t = 0; t < nt_full; ++t) step(t, std::false_type{});
@@ -1733,7 +1790,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
   for (int hv = 0; hv < HV; ++hv)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float lt = xor_sum_groups(lp[hv][qb]);
+      const float lt = o[hv][NB][qb][0];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const int r = hv * 32 + qb * 16 + r16;
 #pragma unroll
