@@ -114,6 +114,17 @@ def algorithmic_work(wl, sel_idx: np.ndarray, score: str = "saliency") -> dict:
             "attn_flops": sa + la_q + np_q, "sa_pairs": pairs}
 
 
+def attention_kernel_name(wl, scope: str) -> str:
+    """The attention kernel the library launches for this layer: the fixed-frame kernel for
+    bf16 at head_dim = feat_dim = 64 with window = chunk and groups of four query heads per
+    routing head, else the general one."""
+    group = wl.n_q_heads // wl.n_kv_heads if scope == "kv_head" else 1
+    if (wl.dtype == "bf16" and wl.head_dim == 64 and wl.feat_dim == 64 and wl.window == wl.chunk
+            and group % 4 == 0):
+        return "attn_w64_kernel"
+    return "attn_kernel"
+
+
 def cpu_baseline(wl, q, k, v, w, sel_idx) -> dict:
     """The fp64 oracle on the whole layer (all KV heads, all tokens), timed on the host."""
     import threadpoolctl
@@ -212,7 +223,7 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
                    "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "feat_dim": wl.feat_dim,
                    "window": wl.window, "chunk": wl.chunk, "top_k": wl.top_k, "score": args.score,
                    "routing_scope": args.scope},
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": attn_ach / 1e12,
+        "roofline": {"bound": "mfma", "kernel": attention_kernel_name(wl, args.scope), "achieved": attn_ach / 1e12,
                      "peak": PEAK_BF16_MFMA / 1e12, "unit": "TFLOP/s", "frac": attn_ach / PEAK_BF16_MFMA,
                      "traffic": measured_traffic(wl.name, traffic_file(args.workload))},
         "layer_roofline": {"flops": work["flops"], "bytes": work["bytes"],

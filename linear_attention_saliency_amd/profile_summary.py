@@ -12,7 +12,7 @@ bench run, after the warm-up steps have brought the clocks up).
 (rocprofv3 --pmc ... -- python3 bench.py --calibrate-copy ...): the device-to-device copy
 of known size (the first dispatch of the runtime's copyBuffer kernel) gives the scale from
 counter units to bytes, which is applied to the mean per launch of the library kernel
-whose name contains `kernel` (default attn_kernel).
+whose name contains `kernel` (default attn_, the attention kernel the workload launches).
 
 `counters` merges the counter_collection CSVs of several --pmc passes (one directory per
 pass) into one row per library kernel (those whose name contains the --match substring):
@@ -65,7 +65,7 @@ def _per_kernel(dirpath: str, counter: str):
     return out
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn_kernel", others=()) -> str:
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernel: str = "attn_", others=()) -> str:
     """HBM bytes per launch of `kernel` (the machine-read line), then of each kernel in
     `others` (name substrings) as comment lines."""
     lines = []

@@ -110,3 +110,14 @@ def test_counter_summary_names_and_shares(tmp_path):
     assert cells[3] == "2.0"                 # VALU per MFMA
     assert cells[4] == "10.0%"               # 102400 / (1024 SIMDs * 8000 / 8)
     assert cells[6] == "25% of wave time"
+
+
+def test_attention_kernel_name_follows_the_launch_rule():
+    """bench.py names the attention kernel the library launches: the fixed-frame kernel for
+    bf16, head_dim = feat_dim = 64, window = chunk and four query heads per routing head."""
+    import bench
+    from linear_attention_saliency_amd import synth
+    assert bench.attention_kernel_name(synth.L1B_16K, "kv_head") == "attn_w64_kernel"
+    assert bench.attention_kernel_name(synth.L1B_16K, "query_head") == "attn_kernel"
+    assert bench.attention_kernel_name(synth.L1B_16K.replace(window=32), "kv_head") == "attn_kernel"
+    assert bench.attention_kernel_name(synth.TINY_F32, "kv_head") == "attn_kernel"
