@@ -116,12 +116,12 @@ def algorithmic_work(wl, sel_idx: np.ndarray, score: str = "saliency") -> dict:
 
 def attention_kernel_name(wl, scope: str) -> str:
     """The attention kernel the library launches for this layer: the fixed-frame kernel for
-    bf16 at head_dim = feat_dim = 64 with window = chunk and groups of four query heads per
-    routing head, else the general one."""
+    bf16 with head_dim = feat_dim (64 or 128), window = chunk and groups of four query heads
+    per routing head, else the general one."""
     group = wl.n_q_heads // wl.n_kv_heads if scope == "kv_head" else 1
-    if (wl.dtype == "bf16" and wl.head_dim == 64 and wl.feat_dim == 64 and wl.window == wl.chunk
+    if (wl.dtype == "bf16" and wl.head_dim == wl.feat_dim and wl.head_dim in (64, 128) and wl.window == wl.chunk
             and group % 4 == 0):
-        return "attn_w64_kernel"
+        return "attn_ff_kernel"
     return "attn_kernel"
 
 

@@ -1290,11 +1290,14 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 }
 
 // ======================================================================================
-// Window = chunk at bf16, head_dim = feat_dim = 64, four query heads per workgroup (the
-// Llama-3.2-1B-shaped layer), under a softmax frame fixed up front.
+// Window = chunk at bf16 with head_dim = feat_dim = D in {64, 128} and four query heads per
+// workgroup (the Llama-3.2-1B- and Llama-3.1-8B-shaped layers), under a softmax frame fixed
+// up front.
 //
-// A wave takes one query head and all 64 queries of chunk c (two 32-query halves). Before
-// any tile, each query's frame m0 (log2 units) is set so that no weight can pass 2^32 and
+// A wave takes one query head: at D = 64 all 64 queries of chunk c (two 32-query halves,
+// HV = 2) in a four-wave workgroup; at D = 128 one 32-query half (HV = 1) in an eight-wave
+// workgroup (wave w: head slot w % 4, half w / 4). Before any
+// tile, each query's frame m0 (log2 units) is set so that no weight can pass 2^32 and
 // nothing is ever rescaled: a softmax logit is at most |q| Kmax c1 and a linear weight
 // phi(q).phi(k) at most |q| Kmax (the NP-Map preserves norms), where Kmax is the largest key
 // norm of the window chunks (kall) and of the compact tiles (tilemax). So
@@ -1311,21 +1314,34 @@ __global__ __launch_bounds__((AttnCfg<T, D, DF, NH>::NTHR), (3 - AttnCfg<T, D, D
 //      so chunk c-1's tile needs no per-key selection test: their V^T columns are zeroed in
 //      LDS and its row sums use a not-selected vector;
 //   3. the normalised output through LDS, so every position's four heads leave as one
-//      contiguous 512-byte row.
+//      contiguous row.
 // Every P is 2^(a c1 - m0) or phi(q).phi(k) 2^-m0; the row sums ride along in the products
 // as an extra all-ones (or not-selected) A block.
-struct W64 {
-  static constexpr int D = 64, QB = 2, HV = 2, NW = 4, NB = 4;
-  static constexpr int KT = 64 * 64, STAGE = 2 * KT;  // a 64 x 64 tile; a compact stage (K, V^T)
-  // window regions (three compact stages' worth), then compact stage 0 and W_h
+template <int D>
+struct FF {
+  static constexpr int QB = 2, NB = D / 16;
+  static constexpr int HV = D == 64 ? 2 : 1;     // 32-query halves per wave
+  static constexpr int NW = D == 64 ? 4 : 8;     // waves per workgroup: 4 head slots x 64 / (32 HV) halves
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int KT = 64 * D, ST = D * D;  // a 64-row tile (K, V^T, phi(K)); the state S^T and W_h
+  static constexpr int STAGE = 2 * KT;           // a compact stage (K, V^T)
+  // window regions, then (D = 64) compact stage 0 and W_h, or (D = 128) W_h over compact
+  // stage 0, which takes compact tile 0 once every wave has its phi(q)
+  static constexpr bool W_IN_S0 = D == 128;
   static constexpr int R_PHIP = 0, R_VP = R_PHIP + KT, R_VC = R_VP + KT, R_KC = R_VC + KT, R_KP = R_KC + KT,
-                       R_ST = R_KP + KT, R_S0 = R_ST + KT, R_W = R_S0 + STAGE, LDS_ELEMS = R_W + KT;
-  static constexpr int LDS_BYTES = LDS_ELEMS * 2;  // 72 KiB: two workgroups per CU
-  static constexpr int NL = 4;                     // copy instructions per wave for one compact tile
-  static constexpr int NFIX = 14;                  // ... for the six window / state tiles and W_h
+                       R_ST = R_KP + KT, R_S0 = R_ST + ST, R_W = W_IN_S0 ? R_S0 : R_S0 + STAGE,
+                       LDS_ELEMS = W_IN_S0 ? R_S0 + STAGE : R_W + ST;
+  static constexpr int LDS_BYTES = LDS_ELEMS * 2;
+  static_assert(!W_IN_S0 || ST <= STAGE, "W_h fits in compact stage 0");
+  static_assert(3 * STAGE <= R_S0, "compact stages 1..3 fit over the window regions");
+  static_assert(LDS_BYTES <= (NW == 4 ? 80 : 160) * 1024, "two four-wave or one eight-wave workgroup per CU");
+  // copy instructions per wave: one compact tile; the window tiles and the state; W_h
+  static constexpr int NL = DmaTile<bf16, D, 64, NW>::PER_WAVE + DmaTile<bf16, 64, D, NW>::PER_WAVE;
+  static constexpr int NWIN = 3 * DmaTile<bf16, D, 64, NW>::PER_WAVE + 2 * DmaTile<bf16, 64, D, NW>::PER_WAVE +
+                              DmaTile<bf16, D, D, NW>::PER_WAVE;
+  static constexpr int NWH = DmaTile<bf16, D, D, NW>::PER_WAVE;
   static __device__ __forceinline__ int stage_off(int s) { return s == 0 ? R_S0 : (s - 1) * STAGE; }
 };
-static_assert(W64::LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 
 // acc + the dot product of two fragments (bf16: four dot2; fp32: fmas)
 template <typename F> __device__ __forceinline__ float frag_dot(const F& x, const F& y, float acc) {
@@ -1376,28 +1392,29 @@ __device__ __forceinline__ void phi_q_frags(const typename Tr<T>::frag (&qf)[QB]
   }
 }
 
-// The exact frame of W64's queries (one wave, both halves): the largest of the softmax logits
-// (compact keys, chunk c up to the query, chunk c-1 past the query or selected; times c1) and
-// of log2 of the whole linear weight (prefix state plus chunk c-1's other keys). Global loads
-// only, so the other waves are not held up.
-template <typename T>
-__device__ __forceinline__ void w64_exact_frame(
-    const typename Tr<T>::frag (&qf)[W64::HV][W64::QB][2], float (&m0)[W64::HV][W64::QB],
-    __amdgpu_buffer_rsrc_t krs, int n_comp, __amdgpu_buffer_rsrc_t kc_rs, __amdgpu_buffer_rsrc_t kp_rs, int kst,
-    __amdgpu_buffer_rsrc_t fp_rs, uint64_t selprev, const T* Wh, __amdgpu_buffer_rsrc_t z_rs, bool has_prev,
-    float c1) {
+// The exact frame of a wave's queries (half0: its first 32-query half): the largest of the
+// softmax logits (compact keys, chunk c up to the query, chunk c-1 past the query or
+// selected; times c1) and of log2 of the whole linear weight (prefix state plus chunk c-1's
+// other keys). Global loads only, so the other waves are not held up.
+template <typename T, int D>
+__device__ __forceinline__ void ff_exact_frame(const typename Tr<T>::frag (&qf)[FF<D>::HV][FF<D>::QB][D / 32],
+                                               float (&m0)[FF<D>::HV][FF<D>::QB], int half0,
+                                               __amdgpu_buffer_rsrc_t krs, int n_comp, __amdgpu_buffer_rsrc_t kc_rs,
+                                               __amdgpu_buffer_rsrc_t kp_rs, int kst, __amdgpu_buffer_rsrc_t fp_rs,
+                                               uint64_t selprev, const T* Wh, __amdgpu_buffer_rsrc_t z_rs,
+                                               bool has_prev, float c1) {
   using TT = Tr<T>;
   using frag = typename TT::frag;
-  constexpr int QB = W64::QB, HV = W64::HV;
+  constexpr int QB = FF<D>::QB, HV = FF<D>::HV, KS = D / 32;
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
   float cm[HV][QB];
-  compact_max<T, 64, QB, HV>(krs, n_comp, qf, cm, c1);
+  compact_max<T, D, QB, HV>(krs, n_comp, qf, cm, c1);
   const uint32_t selw = bits_word(selprev);
 #pragma unroll
   for (int hv = 0; hv < HV; ++hv) {
-    frag pq[QB][2];
-    phi_q_frags<T, 64, 64, QB>(qf[hv], [&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * 64 + ks * 32 + grp * 8); },
-                               pq);
+    frag pq[QB][KS];
+    phi_q_frags<T, D, D, QB>(qf[hv], [&](int fb, int ks) { return TT::load8(Wh + (fb * 16 + r16) * D + ks * 32 + grp * 8); },
+                             pq);
     float smax[QB], lsum[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -1406,23 +1423,23 @@ __device__ __forceinline__ void w64_exact_frame(
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      frag ka[2], kp[2], fa[2];
+      frag ka[KS], kp[KS], fa[KS];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         ka[ks] = TT::bload8(kc_rs, ((kb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
         kp[ks] = TT::bload8(kp_rs, ((kb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
-        fa[ks] = TT::bload8(fp_rs, ((kb * 16 + r16) * 64 + ks * 32 + grp * 8) * 2, 0);
+        fa[ks] = TT::bload8(fp_rs, ((kb * 16 + r16) * D + ks * 32 + grp * 8) * 2, 0);
       }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sp = sc, ls = sc;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
           TT::mma(sc, ka[ks], qf[hv][qb][ks]);
           TT::mma(sp, kp[ks], qf[hv][qb][ks]);
           TT::mma(ls, fa[ks], pq[qb][ks]);
         }
-        const int r = hv * 32 + qb * 16 + r16;
+        const int r = (half0 + hv) * 32 + qb * 16 + r16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = kb * 16 + 4 * grp + i;
@@ -1434,14 +1451,14 @@ __device__ __forceinline__ void w64_exact_frame(
       }
     }
     // the prefix state's linear weight phi(q).z: every row of the A operand is z
-    frag zf[2];
+    frag zf[KS];
 #pragma unroll
-    for (int fs = 0; fs < 2; ++fs) zf[fs] = TT::bload8(z_rs, (fs * 32 + grp * 8) * 2, 0);
+    for (int fs = 0; fs < KS; ++fs) zf[fs] = TT::bload8(z_rs, (fs * 32 + grp * 8) * 2, 0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x4 dz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int fs = 0; fs < 2; ++fs) TT::mma(dz, zf[fs], pq[qb][fs]);
+      for (int fs = 0; fs < KS; ++fs) TT::mma(dz, zf[fs], pq[qb][fs]);
       const float la = xor_sum_groups(lsum[qb]) + dz[0];
       const float mx = xor_max_groups(smax[qb]);
       m0[hv][qb] = la > 0.f ? fmaxf(mx, __log2f(la)) : mx;
@@ -1449,13 +1466,14 @@ __device__ __forceinline__ void w64_exact_frame(
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
-  using C = W64;
-  constexpr int QB = C::QB, HV = C::HV, NW = C::NW, NB = C::NB, D = C::D, KT = C::KT;
+template <typename T, int D>
+__global__ __launch_bounds__(FF<D>::NTHR, (FF<D>::NW == 4 ? 2 : 1)) void attn_ff_kernel(AttnArgs a) {
+  using C = FF<D>;
+  constexpr int QB = C::QB, HV = C::HV, NW = C::NW, NB = C::NB, KT = C::KT, KS = D / 32;
   using TT = Tr<T>;
   using frag = typename TT::frag;
-  using SW = Swz<T, 64>;
+  using SK = Swz<T, D>;   // K, phi(K) (64 rows), the state S^T and W_h (D rows): rows of D
+  using SV = Swz<T, 64>;  // V^T tiles: D rows of 64 keys
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   T* L = reinterpret_cast<T*>(lds_raw);
 
@@ -1474,7 +1492,9 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
   const long long bkv = static_cast<long long>(b) * d.Hkv + h;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hq = rh * d.Gr + gs * NW + wave;  // every head of the split exists (Gr % 4 == 0)
+  const int slot = NW == 4 ? wave : wave & 3;    // head slot
+  const int half0 = NW == 4 ? 0 : wave >> 2;     // first 32-query half of the wave
+  const int hq = rh * d.Gr + gs * 4 + slot;      // every head of the split exists (Gr % 4 == 0)
   const long long T_ = d.T;
   const long long t0 = static_cast<long long>(c) * kChunk;
   const int nvalid = static_cast<int>(T_ - t0 < kChunk ? T_ - t0 : kChunk);
@@ -1503,10 +1523,10 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 
   // ---- 1. register operands: the queries and their own keys (B-operand layout), the tile
   //      and window key-norm bounds, the selection of chunk c-1 ------------------------------
-  frag qf[HV][QB][2], kd[HV][QB][2];
+  frag qf[HV][QB][KS], kd[HV][QB][KS];
 #pragma unroll
   for (int hv = 0; hv < HV; ++hv) {
-    const long long q0 = t0 + hv * 32;
+    const long long q0 = t0 + (half0 + hv) * 32;
     const long long nq = T_ - q0 < 32 ? T_ - q0 : 32;
     const int qrow = d.Hq * D;
     const auto qrs = make_rsrc(q + ((b * T_ + (nq > 0 ? q0 : 0)) * d.Hq + hq) * D,
@@ -1516,7 +1536,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         qf[hv][qb][ks] = TT::bload8(qrs, ((qb * 16 + r16) * qrow + ks * 32 + grp * 8) * 2, 0);
         kd[hv][qb][ks] = TT::bload8(krd, ((qb * 16 + r16) * kst + ks * 32 + grp * 8) * 2, 0);
       }
@@ -1533,28 +1553,29 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
   const float kwin = fmaxf(a.kall[static_cast<long long>(bh) * d.nC + c],
                            has_prev ? a.kall[static_cast<long long>(bh) * d.nC + c - 1] : 0.f);
 
-  // ---- 2. copies: the window tiles, the prefix state and W_h into their regions, then
-  //      compact tile 0 into stage 0 (zero-filled where absent) -------------------------------
+  // ---- 2. copies: the window tiles, the prefix state and W_h into their regions, then (W_h
+  //      outside stage 0) compact tile 0 into stage 0 (zero-filled where absent) --------------
   const T* Sg = static_cast<const T*>(a.states) + (static_cast<long long>(bh) * d.nC + (has_state ? c - 2 : 0)) * d.R;
-  const T* Wh = static_cast<const T*>(a.w) + static_cast<long long>(h) * 64 * D;
-  dma_tile<T, 64, 64, NW>(L + C::R_PHIP, phik + (bkv * T_ + tp) * 64, 64, has_prev ? 64 : 0);
-  dma_tile<T, 64, 64, NW>(L + C::R_VP, vT + (bkv * d.nC + (has_prev ? c - 1 : c)) * D * 64, 64, has_prev ? D : 0);
-  dma_tile<T, 64, 64, NW>(L + C::R_VC, vT + (bkv * d.nC + c) * D * 64, 64, D);
-  dma_tile<T, 64, 64, NW>(L + C::R_KC, kk + ((b * T_ + t0) * d.Hkv + h) * D, kst, nvalid);
-  dma_tile<T, 64, 64, NW>(L + C::R_KP, kk + ((b * T_ + tp) * d.Hkv + h) * D, kst, has_prev ? 64 : 0);
-  dma_tile<T, 64, 64, NW>(L + C::R_ST, Sg, 64, has_state ? D : 0);
-  dma_tile<T, 64, 64, NW>(L + C::R_W, Wh, D, 64);
-  issue(0, 0);
+  const T* Wh = static_cast<const T*>(a.w) + static_cast<long long>(h) * D * D;
+  dma_tile<T, D, 64, NW>(L + C::R_PHIP, phik + (bkv * T_ + tp) * D, D, has_prev ? 64 : 0);
+  dma_tile<T, 64, D, NW>(L + C::R_VP, vT + (bkv * d.nC + (has_prev ? c - 1 : c)) * D * 64, 64, has_prev ? D : 0);
+  dma_tile<T, 64, D, NW>(L + C::R_VC, vT + (bkv * d.nC + c) * D * 64, 64, D);
+  dma_tile<T, D, 64, NW>(L + C::R_KC, kk + ((b * T_ + t0) * d.Hkv + h) * D, kst, nvalid);
+  dma_tile<T, D, 64, NW>(L + C::R_KP, kk + ((b * T_ + tp) * d.Hkv + h) * D, kst, has_prev ? 64 : 0);
+  dma_tile<T, D, D, NW>(L + C::R_ST, Sg, D, has_state ? D : 0);
+  dma_tile<T, D, D, NW>(L + C::R_W, Wh, D, D);
+  if constexpr (!C::W_IN_S0) issue(0, 0);
+  constexpr int N_AFTER_WIN = C::W_IN_S0 ? 0 : C::NL;  // copies issued after the window ones
   // z of the prefix state (A operand of the denominator, the same in every row)
-  frag zf[2];
+  frag zf[KS];
   {
-    const auto zrs = make_rsrc(Sg + 64 * D, has_state ? 64u * 2u : 0u);
+    const auto zrs = make_rsrc(Sg + D * D, has_state ? static_cast<uint32_t>(D) * 2u : 0u);
 #pragma unroll
-    for (int fs = 0; fs < 2; ++fs) zf[fs] = TT::bload8(zrs, (fs * 32 + grp * 8) * 2, 0);
+    for (int fs = 0; fs < KS; ++fs) zf[fs] = TT::bload8(zrs, (fs * 32 + grp * 8) * 2, 0);
   }
 
   // ---- 3. the frame ---------------------------------------------------------------------
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NFIX + C::NL + 2));  // the register operands
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NWIN + C::NWH + N_AFTER_WIN + KS));  // the register operands
   const uint64_t selprev = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[1]))) << 32) |
                            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(selv[0]));
   float kmax = 0.f;
@@ -1569,7 +1590,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       float dq = 0.f, q2 = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         dq = frag_dot(qf[hv][qb][ks], kd[hv][qb][ks], dq);
         q2 = frag_dot(qf[hv][qb][ks], qf[hv][qb][ks], q2);
       }
@@ -1581,11 +1602,12 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
       m0[hv][qb] = m;
     }
   if (__builtin_amdgcn_ballot_w64(exact) != 0)
-    w64_exact_frame<T>(qf, m0, krs, n_comp,
-                       make_rsrc(kk + ((b * T_ + t0) * d.Hkv + h) * D, static_cast<uint32_t>(((nvalid - 1) * kst + D) * 2)),
-                       make_rsrc(kk + ((b * T_ + tp) * d.Hkv + h) * D, has_prev ? static_cast<uint32_t>((63 * kst + D) * 2) : 0u),
-                       kst, make_rsrc(phik + (bkv * T_ + tp) * 64, has_prev ? 64u * 64u * 2u : 0u), selprev, Wh,
-                       make_rsrc(Sg + 64 * D, has_state ? 64u * 2u : 0u), has_prev, c1);
+    ff_exact_frame<T, D>(
+        qf, m0, half0, krs, n_comp,
+        make_rsrc(kk + ((b * T_ + t0) * d.Hkv + h) * D, static_cast<uint32_t>(((nvalid - 1) * kst + D) * 2)),
+        make_rsrc(kk + ((b * T_ + tp) * d.Hkv + h) * D, has_prev ? static_cast<uint32_t>((63 * kst + D) * 2) : 0u), kst,
+        make_rsrc(phik + (bkv * T_ + tp) * D, has_prev ? static_cast<uint32_t>(64 * D * 2) : 0u), selprev, Wh,
+        make_rsrc(Sg + D * D, has_state ? static_cast<uint32_t>(D) * 2u : 0u), has_prev, c1);
   // o[hv][NB]: the row sums, riding along in the products (an all-ones A block)
   f32x4 o[HV][NB + 1][QB];
 #pragma unroll
@@ -1595,14 +1617,14 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db <= NB; ++db) o[hv][db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const frag ones = ones_frag<T>();
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NL));  // everything but compact tile 0
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N_AFTER_WIN));  // the window regions, the state and W_h
   lds_barrier();
   // chunk c-1's selected keys are taken with the compact tiles: zero their V^T columns here,
   // and count chunk c-1's row sums with a not-selected vector instead of ones
   if (has_prev && selprev != 0) {
-    if (tid < 64)
+    if (tid < D)
       for (uint64_t m = selprev; m != 0; m &= m - 1)
-        L[C::R_VP + SW::off(tid, pk_pos(static_cast<int>(__builtin_ctzll(m))))] = TT::from_f(0.f);
+        L[C::R_VP + SV::off(tid, pk_pos(static_cast<int>(__builtin_ctzll(m))))] = TT::from_f(0.f);
     __syncthreads();
   }
   frag nsel[2];  // A operand: 1 for the keys of chunk c-1 that are not selected (PK order)
@@ -1612,15 +1634,22 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e)
       nsel[hs][e] = TT::from_f(((selprev >> (hs * 32 + 16 * (e / 4) + 4 * grp + e % 4)) & 1ull) ? 0.f : 1.f);
 
-  // ---- 5. per query half: phi(q), the prefix read-out, chunk c, chunk c-1 ----------------
+  // ---- 4. per query half: phi(q), the prefix read-out, chunk c, chunk c-1 ----------------
   bool dmask[4];  // key position <= query position, on a diagonal block
 #pragma unroll
   for (int i = 0; i < 4; ++i) dmask[i] = 4 * grp + i <= r16;
+  frag pq[HV][QB][KS];  // phi(q): PK-ordered B fragments over f
+#pragma unroll
+  for (int hv = 0; hv < HV; ++hv)
+    phi_q_frags<T, D, D, QB>(qf[hv], [&](int fb, int ks) { return SK::load8(L + C::R_W, fb * 16 + r16, ks * 32 + grp * 8); },
+                             pq[hv]);
+  if constexpr (C::W_IN_S0) {  // W_h's region becomes compact stage 0
+    lds_barrier();
+    issue(0, 0);
+  }
 #pragma unroll
   for (int hv = 0; hv < HV; ++hv) {
-    frag pq[QB][2];
-    phi_q_frags<T, 64, 64, QB>(qf[hv], [&](int fb, int ks) { return SW::load8(L + C::R_W, fb * 16 + r16, ks * 32 + grp * 8); },
-                               pq);
+    const int qh = half0 + hv;  // this 32-query half of the chunk (wave-uniform)
     // prefix read-out: N = S^T phi(q) (state rows d, PK features) and D = phi(q).z
     if (has_state) {
       f32x4 la[NB][QB], dz[QB];
@@ -1631,15 +1660,15 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
         for (int db = 0; db < NB; ++db) la[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int fs = 0; fs < 2; ++fs) {
+      for (int fs = 0; fs < KS; ++fs) {
 #pragma unroll
         for (int db = 0; db < NB; ++db) {
-          const frag sa = SW::load8(L + C::R_ST, db * 16 + r16, fs * 32 + grp * 8);
+          const frag sa = SK::load8(L + C::R_ST, db * 16 + r16, fs * 32 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) TT::mma(la[db][qb], sa, pq[qb][fs]);
+          for (int qb = 0; qb < QB; ++qb) TT::mma(la[db][qb], sa, pq[hv][qb][fs]);
         }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) TT::mma(dz[qb], zf[fs], pq[qb][fs]);
+        for (int qb = 0; qb < QB; ++qb) TT::mma(dz[qb], zf[fs], pq[hv][qb][fs]);
       }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -1660,21 +1689,20 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const frag ka = SW::load8(L + C::R_KC, kb * 16 + r16, ks * 32 + grp * 8);
+        for (int ks = 0; ks < KS; ++ks) {
+          const frag ka = SK::load8(L + C::R_KC, kb * 16 + r16, ks * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            if (kb <= 2 * hv + qb) TT::mma(s[kb][qb], ka, qf[hv][qb][ks]);
+            if (kb <= 2 * qh + qb) TT::mma(s[kb][qb], ka, qf[hv][qb][ks]);
         }
       }
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
+        if (2 * hs > 2 * qh + 1) continue;  // every key of this half lies past every query
         frag pf[QB];
-        bool live = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qblk = 2 * hv + qb;  // 16-query block of the chunk
-          live |= 2 * hs <= qblk;
+          const int qblk = 2 * qh + qb;  // 16-query block of the chunk
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kb = 2 * hs + e / 4, i = e % 4;
@@ -1684,17 +1712,16 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
             pf[qb][e] = TT::from_f(p);
           }
         }
-        if (!live) continue;
 #pragma unroll
         for (int db = 0; db < NB; ++db) {
-          const frag va = SW::load8(L + C::R_VC, db * 16 + r16, hs * 32 + grp * 8);
+          const frag va = SV::load8(L + C::R_VC, db * 16 + r16, hs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            if (2 * hs <= 2 * hv + qb) TT::mma(o[hv][db][qb], va, pf[qb]);
+            if (2 * hs <= 2 * qh + qb) TT::mma(o[hv][db][qb], va, pf[qb]);
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          if (2 * hs <= 2 * hv + qb) TT::mma(o[hv][NB][qb], ones, pf[qb]);
+          if (2 * hs <= 2 * qh + qb) TT::mma(o[hv][NB][qb], ones, pf[qb]);
       }
     }
     // chunk c-1: softmax keys p > r, linear keys p <= r (one P for both); the selected keys
@@ -1707,11 +1734,11 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) ls[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int fs = 0; fs < 2; ++fs) {
-          const frag fa = SW::load8(L + C::R_PHIP, kb * 16 + r16, fs * 32 + grp * 8);
+        for (int fs = 0; fs < KS; ++fs) {
+          const frag fa = SK::load8(L + C::R_PHIP, kb * 16 + r16, fs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            if (kb <= 2 * hv + qb) TT::mma(ls[kb][qb], fa, pq[qb][fs]);
+            if (kb <= 2 * qh + qb) TT::mma(ls[kb][qb], fa, pq[hv][qb][fs]);
         }
       }
 #pragma unroll
@@ -1719,12 +1746,13 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
         frag pf[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qblk = 2 * hv + qb;
+          const int qblk = 2 * qh + qb;
           const float sh = __builtin_amdgcn_exp2f(-0.5f * m0[hv][qb]);  // 2^-m0 as two factors
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kb = 2 * hs + e / 4, i = e % 4;
             // key p vs query r: p > r on blocks past the query block, and past the diagonal
+            // (qblk is a constant at D = 64, wave-uniform at D = 128: scalar branches)
             float pv;
             if (kb > qblk)
               pv = __builtin_amdgcn_exp2f(s[kb][qb][i] * c1 - m0[hv][qb]);
@@ -1737,7 +1765,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int db = 0; db < NB; ++db) {
-          const frag va = SW::load8(L + C::R_VP, db * 16 + r16, hs * 32 + grp * 8);
+          const frag va = SV::load8(L + C::R_VP, db * 16 + r16, hs * 32 + grp * 8);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) TT::mma(o[hv][db][qb], va, pf[qb]);
         }
@@ -1747,7 +1775,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
     }
   }
 
-  // ---- 4. the compact tiles: tile t in stage t % 4; tiles 1 and 2 are issued once every
+  // ---- 5. the compact tiles: tile t in stage t % 4; tiles 1 and 2 are issued once every
   //      wave is done with the window regions, tile t + 3 in step t (into the stage of tile
   //      t - 1, free after the step's barrier). Step t waits for its own copies of tile t
   //      (those of tiles t + 1 and t + 2 may still be in flight). -------------------------
@@ -1782,7 +1810,7 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
     if (nt_full < nt_comp) step(nt_full, std::true_type{});
   }
 
-  // ---- 6. normalise, stage in LDS as [position][4 heads x 64], store whole rows ----------
+  // ---- 6. normalise, stage in LDS as [position][4 heads x D], store whole rows -----------
   using SO = Swz<T, 4 * D>;
   __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS is left in flight (an absent tile 0's included)
   lds_barrier();                  // every wave is done with the tiles
@@ -1792,22 +1820,34 @@ __global__ __launch_bounds__(256, 2) void attn_w64_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       const float lt = o[hv][NB][qb][0];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int r = hv * 32 + qb * 16 + r16;
+      const int r = (half0 + hv) * 32 + qb * 16 + r16;
 #pragma unroll
       for (int db = 0; db < NB; ++db) {
         typename TT::quad ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = TT::from_f(o[hv][db][qb][i] * inv);
-        *reinterpret_cast<typename TT::quad*>(L + SO::off(r, wave * D + db * 16 + 4 * grp)) = ov;
+        *reinterpret_cast<typename TT::quad*>(L + SO::off(r, slot * D + db * 16 + 4 * grp)) = ov;
       }
     }
   __syncthreads();
-  T* out = static_cast<T*>(a.out) + ((b * T_ + t0) * d.Hq + rh * d.Gr + gs * NW) * D;
+  T* out = static_cast<T*>(a.out) + ((b * T_ + t0) * d.Hq + rh * d.Gr + gs * 4) * D;
+  constexpr int GPR = 4 * D / 8;  // 16-byte granules per output row
 #pragma unroll
-  for (int j = 0; j < 64 * 4 * D / 8 / 256; ++j) {
-    const int idx = j * 256 + tid, r = idx / 32, col = (idx % 32) * 8;
+  for (int j = 0; j < 64 * GPR / C::NTHR; ++j) {
+    const int idx = j * C::NTHR + tid, r = idx / GPR, col = (idx % GPR) * 8;
     if (r < nvalid) TT::store8(out + static_cast<long long>(r) * d.Hq * D + col, SO::load8(L, r, col));
   }
+}
+
+template <typename T, int D>
+static hipError_t attn_ff(const AttnArgs& a, hipStream_t s) {
+  using C = FF<D>;
+  const dim3 grid(a.d.nC * a.d.B * a.d.Hr * a.gsplit);
+  if (C::LDS_BYTES > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_ff_kernel<T, D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  hipLaunchKernelGGL((attn_ff_kernel<T, D>), grid, dim3(C::NTHR), C::LDS_BYTES, s, a);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int DF, int NH, bool BAND>
@@ -1829,15 +1869,9 @@ static hipError_t attn_nh(const AttnArgs& a, hipStream_t s) {
 
 template <typename T, int D, int DF>
 static hipError_t attn_t(const AttnArgs& a, hipStream_t s) {
-  if constexpr (sizeof(T) == 2 && D == 64 && DF == 64) {
-    if (a.nw == 4 && a.d.window == kChunk && a.d.Gr % 4 == 0) {
-      const dim3 grid(a.d.nC * a.d.B * a.d.Hr * a.gsplit);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_w64_kernel<T>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, W64::LDS_BYTES);
-      hipLaunchKernelGGL((attn_w64_kernel<T>), grid, dim3(256), W64::LDS_BYTES, s, a);
-      return hipGetLastError();
-    }
-  }
+  // the fixed-frame kernel: bf16, head_dim = feat_dim, window = chunk, groups of four
+  if constexpr (sizeof(T) == 2 && D == DF)
+    if (a.nw == 4 && a.d.window == kChunk && a.d.Gr % 4 == 0) return attn_ff<T, D>(a, s);
   if (a.nw == 4) return attn_nh<T, D, DF, 4>(a, s);
   if (a.nw == 2) return attn_nh<T, D, DF, 2>(a, s);
   if (a.nw == 1) return attn_nh<T, D, DF, 1>(a, s);

@@ -114,10 +114,13 @@ def test_counter_summary_names_and_shares(tmp_path):
 
 def test_attention_kernel_name_follows_the_launch_rule():
     """bench.py names the attention kernel the library launches: the fixed-frame kernel for
-    bf16, head_dim = feat_dim = 64, window = chunk and four query heads per routing head."""
+    bf16, head_dim = feat_dim (64 or 128), window = chunk and four query heads per routing
+    head."""
     import bench
     from linear_attention_saliency_amd import synth
-    assert bench.attention_kernel_name(synth.L1B_16K, "kv_head") == "attn_w64_kernel"
+    assert bench.attention_kernel_name(synth.L1B_16K, "kv_head") == "attn_ff_kernel"
+    assert bench.attention_kernel_name(synth.L8B_4K, "kv_head") == "attn_ff_kernel"
+    assert bench.attention_kernel_name(synth.L8B_4K.replace(feat_dim=64), "kv_head") == "attn_kernel"
     assert bench.attention_kernel_name(synth.L1B_16K, "query_head") == "attn_kernel"
     assert bench.attention_kernel_name(synth.L1B_16K.replace(window=32), "kv_head") == "attn_kernel"
     assert bench.attention_kernel_name(synth.TINY_F32, "kv_head") == "attn_kernel"
