@@ -114,17 +114,45 @@ __device__ __forceinline__ float np_backward(const NpRow<F>& n, f32x4 (&dphi)[F 
   return dr;
 }
 
+// tile[dd][pk_pos(f)] = src[f][dd]: the transpose of a row-major [F][D] matrix (in the
+// layer's dtype or fp32), features pk-permuted, into a Swz<T, F> LDS tile of D rows. A
+// thread takes the 8 features of one 8-position granule of the permuted order by 8 dims:
+// eight 8-element reads of the source, a transpose in registers, eight 8-element LDS
+// stores. Neighbouring threads take neighbouring granules of the same dims, so every store
+// instruction fills whole rows without bank conflicts.
+template <typename T, int D, int F, typename S>
+__device__ __forceinline__ void load_pk_transposed(T* lds, const S* src) {
+  constexpr int NG = F / 8;
+  for (int it = threadIdx.x; it < NG * (D / 8); it += blockDim.x) {
+    const int G = it % NG, dd0 = (it / NG) * 8;
+    // position 8 G + 4 hi + r of the permuted order holds feature fb + 16 hi + r
+    const int fb = (G / 4) * 32 + (G % 4) * 4;
+    typename Tr<T>::frag y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const S* row = src + (fb + (e / 4) * 16 + (e % 4)) * D + dd0;
+      if constexpr (sizeof(S) == 4) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(row), hi = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j][e] = Tr<T>::from_f(lo[j]);
+          y[j + 4][e] = Tr<T>::from_f(hi[j]);
+        }
+      } else {
+        const typename Tr<T>::frag x = Tr<T>::load8(row);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j][e] = x[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Swz<T, F>::store8(lds, dd0 + j, 8 * G, y[j]);
+  }
+}
+
 // W^T with the features pk-permuted, [dim][pk_pos(f)], into a Swz<T, F> LDS tile of D rows
-// (16-byte pieces of W's rows, a few in flight at a time)
 template <typename T, int D, int F>
 __device__ __forceinline__ void load_wt(T* lds, const T* W) {
-#pragma unroll 2
-  for (int e8 = threadIdx.x; e8 < F * D / 8; e8 += blockDim.x) {
-    const int f = e8 / (D / 8), dd = (e8 % (D / 8)) * 8, pf = pk_pos(f);
-    const typename Tr<T>::frag x = Tr<T>::load8(W + f * D + dd);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lds[Swz<T, F>::off(dd + j, pf)] = x[j];
-  }
+  load_pk_transposed<T, D, F, T>(lds, W);
 }
 
 // selection bit mask of complete chunk c from the ascending positions (entries outside
@@ -1010,10 +1038,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
     f32rows_x_frag<T, NF, D>(rv, rs, vf);  // (R v)[16 fb + 4 grp + e]
     T* const t_rt = lds;                   // R^T, D rows of F (features pk-permuted)
     __syncthreads();
-    for (int e = tid; e < F * D; e += 256) {
-      const int f = e / D, dd = e % D;
-      t_rt[Swz<T, F>::off(dd, pk_pos(f))] = TT::from_f(rs[e]);
-    }
+    load_pk_transposed<T, D, F, float>(t_rt, rs);
     __syncthreads();
     const float on = (kvalid && !selj) ? 1.f : 0.f;
 #pragma unroll
