@@ -48,10 +48,11 @@ namespace still {
 namespace {
 
 // NP-Map forward of one row per lane column, for the row held as B fragments xf (SK):
-// z[blk][i] = (W x)[16 blk + 4 grp + i]; also m = elu(z) + 1, |x| and 1/|m|.
+// m[blk][i] = elu(z) + 1 with z = (W x)[16 blk + 4 grp + i], |x| and 1/|m|. z itself is not
+// kept: elu'(z) = min(m, 1) (z > 0 gives m = z + 1 > 1 and slope 1, z <= 0 gives m = e^z <= 1,
+// its own slope).
 template <int F>
 struct NpRow {
-  f32x4 z[F / 16];
   f32x4 m[F / 16];
   float r, inv_nm;
 };
@@ -62,12 +63,12 @@ __device__ __forceinline__ void np_forward(NpRow<F>& n, const T* W, const typena
   const int lane = threadIdx.x & 63, r16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int fb = 0; fb < F / 16; ++fb) {
-    n.z[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    n.m[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       const typename Tr<T>::frag wf = TILE ? Swz<T, D>::load8(W, fb * 16 + r16, ks * 32 + grp * 8)
                                            : Tr<T>::load8(W + (fb * 16 + r16) * D + ks * 32 + grp * 8);
-      Tr<T>::mma(n.z[fb], wf, xf[ks]);
+      Tr<T>::mma(n.m[fb], wf, xf[ks]);
     }
   }
   float nm2 = 0.f, xn2 = 0.f;
@@ -75,7 +76,7 @@ __device__ __forceinline__ void np_forward(NpRow<F>& n, const T* W, const typena
   for (int fb = 0; fb < F / 16; ++fb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float zv = n.z[fb][i];
+      const float zv = n.m[fb][i];
       const float mv = zv > 0.f ? zv + 1.f : __builtin_amdgcn_exp2f(zv * kLog2e);
       n.m[fb][i] = mv;
       nm2 += mv * mv;
@@ -109,7 +110,7 @@ __device__ __forceinline__ float np_backward(const NpRow<F>& n, f32x4 (&dphi)[F 
     for (int i = 0; i < 4; ++i) {
       const float mh = n.m[fb][i] * n.inv_nm;
       const float dm = n.r * (dphi[fb][i] - mh * dr) * n.inv_nm;
-      dphi[fb][i] = dm * (n.z[fb][i] > 0.f ? 1.f : n.m[fb][i]);
+      dphi[fb][i] = dm * fminf(n.m[fb][i], 1.f);
     }
   return dr;
 }
@@ -349,11 +350,17 @@ __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(const float* apart, c
 }
 
 // ---------------------------------------------------------------------------------------
-// QH query heads of one KV head per workgroup: four waves, 16 queries per wave, the wave
-// taking the same 16 rows of each of its QH heads, so that every K, V and K^T fragment it
-// reads from LDS serves QH products.
-template <typename T, int D, int F, int QH>
-__global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_kernel(BwdArgs a) {
+// QH query heads of one KV head per four waves, 16 queries per wave, the wave taking the same
+// 16 rows of each of its QH heads, so that every K, V and K^T fragment it reads from LDS
+// serves QH products. With NWV = 8 (QH = 1, F = 128) a workgroup takes two heads, one per
+// group of four waves: both heads share every staged tile, and each SIMD runs two waves,
+// which the registers of two heads per wave would not allow at D = 128.
+template <typename T, int D, int F, int QH, int NWV>
+__global__ __launch_bounds__(NWV * 64, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(NWV == 4 || (NWV == 8 && QH == 1 && F % 128 == 0), "wave layout");
+  constexpr int HW = NWV / 4;     // heads side by side (groups of four waves)
+  constexpr int HPW = QH * HW;    // query heads per workgroup
+  constexpr int NT = NWV * 64;    // threads
   using TT = Tr<T>;
   using frag = typename TT::frag;
   using SW = Swz<T, 64>;
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
   // stays in a region of its own for the NP-Map forward of every head.
   __shared__ __attribute__((aligned(16))) T lds[6 * SLOT];
   __shared__ __attribute__((aligned(16))) T t_w[F * D];
-  __shared__ float s_red[4][F];
+  __shared__ float s_red[NWV][F];
   T* const t_k = lds;
   T* const t_v = lds + SLOT;
   T* const t_kt = lds + 2 * SLOT;
@@ -376,15 +383,18 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
   // work index: chunk fastest, then the group of QH query heads, then batch (the heads of one
   // KV head share its compact tiles). Divisions by run-time sizes leave the compiler unsure
   // that these are uniform; telling it keeps the buffer descriptors in scalar registers.
-  const int nhg = d.Hq / QH;
+  const int nhg = d.Hq / HPW;
   const int w = xcd_work(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int wq = wave & 3, hsub = __builtin_amdgcn_readfirstlane(wave >> 2);  // rows, group of heads
   const int c = __builtin_amdgcn_readfirstlane(w % d.nC);
-  const int hq0 = __builtin_amdgcn_readfirstlane((w / d.nC) % nhg) * QH;
+  const int hgi = __builtin_amdgcn_readfirstlane((w / d.nC) % nhg);
+  const int hqb = hgi * HPW;            // the workgroup's first query head
+  const int hq0 = hqb + hsub * QH;      // the wave's first query head
   const int b = __builtin_amdgcn_readfirstlane(w / (d.nC * nhg));
-  const int h = hq0 / d.G;
+  const int h = hqb / d.G;
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
-  const int qrow = wave * 16 + r16;
+  const int qrow = wq * 16 + r16;
   const long long i = 64LL * c + qrow;  // this lane column's query
   const bool qvalid = i < d.T;
   constexpr float isd = inv_sqrt_d<D>();
@@ -452,10 +462,10 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
   };
   // the compact tiles arrive by buffer -> LDS copies, one tile ahead; rows at or beyond
   // nsel_c read as zeros (the copies' range ends there)
-  using DmaR = DmaTile<T, D, 64, 4>;   // 64 rows of D
-  using DmaT = DmaTile<T, 64, D, 4>;   // D rows of 64 (K^T)
-  using DmaF = DmaTile<T, F, 64, 4>;   // 64 rows of F (phi(K))
-  using DmaFT = DmaTile<T, 64, F, 4>;  // F rows of 64 (phi(K)^T)
+  using DmaR = DmaTile<T, D, 64, NWV>;   // 64 rows of D
+  using DmaT = DmaTile<T, 64, D, NWV>;   // D rows of 64 (K^T)
+  using DmaF = DmaTile<T, F, 64, NWV>;   // 64 rows of F (phi(K))
+  using DmaFT = DmaTile<T, 64, F, NWV>;  // F rows of 64 (phi(K)^T)
   DmaR dmr;
   dmr.init(D);
   DmaT dmt;
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
     dmt.issue(sl + 2 * SLOT, rs_kt, t * D * 64 * ES);
   };
   {  // W into its own region, ahead of the first compact tile (copies complete in order)
-    DmaTile<T, D, F, 4> dmw;
+    DmaTile<T, D, F, NWV> dmw;
     dmw.init(D);
     dmw.issue(t_w, make_rsrc(W, static_cast<uint32_t>(F * D * ES)), 0);
   }
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
     for (int fb = 0; fb < NF; ++fb) dpt[g][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (c >= 2) {
     T* const t_s = lds;  // F rows of D, slots 0-1
-    for (int e8 = tid; e8 < F * D / 8; e8 += 256) {
+    for (int e8 = tid; e8 < F * D / 8; e8 += NT) {
       const int f = e8 / (D / 8), dd = (e8 % (D / 8)) * 8;
       Swz<T, D>::store8(t_s, f, dd, f32_frag<T>(st + f * D + dd));
     }
@@ -652,10 +662,68 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
   T* const e_dz = lds + 4 * SLOT;   // dz^T, F rows
   T* const e_q = lds + 5 * SLOT;    // q^T, D rows
   const int pq = pk_pos(qrow);
-  // the shares of R and of dW are kept per group of QH heads: the second head adds its share
-  // onto the first's (the same thread writes the same elements for both), so the reductions
-  // over the query heads read half as much
-  const long long gc = (static_cast<long long>(b) * nhg + hq0 / QH) * d.nC + c;
+  // the shares of R and of dW are kept per workgroup (its HPW heads): with four waves the
+  // second head adds its share onto the first's (the same thread writes the same elements for
+  // both); with eight the sums stay in registers. Either way the reductions over the query
+  // heads read 1 / HPW as much.
+  const long long gc = (static_cast<long long>(b) * nhg + hgi) * d.nC + c;
+  // e-tiles of a head: e^{-L} phi(q)^T (F rows), dout^T (D rows), dz^T (F rows), q^T (D rows).
+  // Four waves stage one head in slots 2-5; with eight, the second head takes slots 0-1 and
+  // W's region, free once every wave has its dz and dx.
+  auto e_tile = [&](int hs, int k) -> T* {  // k: 0 phi(q)^T, 1 dout^T, 2 dz^T, 3 q^T
+    return hs == 0 ? lds + (2 + k) * SLOT : (k < 2 ? lds + k * SLOT : t_w + (k - 2) * SLOT);
+  };
+  static_assert(NWV == 4 || (F * 64 <= SLOT && D * 64 <= SLOT && 2 * SLOT <= F * D), "e-tile room");
+  // e^{-L} phi(q) and dz transposed, dout and q transposed into the e-tiles of set hs (the
+  // wave's 16 query columns), and this wave's part of the a_c sums over its queries into s_red
+  auto stage_tiles = [&](int hs, const f32x4 (&ps4)[NF], const f32x4 (&dz)[NF], const frag (&xq8)[D / 32],
+                         const frag (&do8)[D / 32], float dlt) {
+    T* const tp = e_tile(hs, 0);
+    T* const tdo = e_tile(hs, 1);
+    T* const tdz = e_tile(hs, 2);
+    T* const tq = e_tile(hs, 3);
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = fb * 16 + 4 * grp + e;
+        tp[SW::off(f, pq)] = TT::from_f(ps4[fb][e]);
+        tdz[SW::off(f, pq)] = TT::from_f(dz[fb][e]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dd = ks * 32 + grp * 8 + e;
+        tdo[SW::off(dd, pq)] = do8[ks][e];
+        tq[SW::off(dd, pq)] = xq8[ks][e];
+      }
+#pragma unroll
+    for (int fb = 0; fb < NF; ++fb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = xor_sum_16(ps4[fb][e] * dlt);
+        if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
+      }
+  };
+  // the staged e-tiles of set hs (query head hq) to memory in 16-byte pieces (every thread)
+  auto store_tiles = [&](int hs, int hq) {
+    const long long qc = (static_cast<long long>(b) * d.Hq + hq) * d.nC + c;
+    T* phqt = static_cast<T*>(a.phiqt) + qc * F * 64;
+    T* qt = static_cast<T*>(a.qt) + qc * D * 64;
+    T* dot = static_cast<T*>(a.dot) + qc * D * 64;
+    for (int idx = tid; idx < F * 8; idx += NT) {
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      TT::store8(phqt + row * 64 + col, SW::load8(e_tile(hs, 0), row, col));
+    }
+    for (int idx = tid; idx < D * 8; idx += NT) {
+      const int row = idx >> 3, col = (idx & 7) * 8;
+      TT::store8(qt + row * 64 + col, SW::load8(e_tile(hs, 3), row, col));
+      TT::store8(dot + row * 64 + col, SW::load8(e_tile(hs, 1), row, col));
+    }
+  };
+  float* ap = a.apart + gc * R;
+  float* wp = a.dwq + gc * (F * D);
 #pragma unroll
   for (int g = 0; g < QH; ++g) {
     const int hq = hq0 + g;
@@ -682,23 +750,21 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb) dpt[g][fb] *= einv;
 
-    // the head's q and dout rows read again: the loops' copies end there, rather than living
-    // on (unpacked for the element stores below) through the loops
+    // the head's q rows read again: the loops' copies end there, rather than living on
+    // (unpacked for the element stores below) through the loops; dout likewise, further down
     frag xq8[D / 32], do8[D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+    for (int ks = 0; ks < D / 32; ++ks)
       xq8[ks] = qvalid ? TT::load8(static_cast<const T*>(a.q) + qoff + ks * 32 + grp * 8) : TT::zero();
-      do8[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
-    }
 
     // NP-Map backward and dq
     NpRow<F> nq;
     np_forward<T, D, F, true>(nq, t_w, xq8);
-    f32x4 phq[NF];
+    f32x4 ps4[NF];  // e^{-L} phi(q), the factor every key-side use takes
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) phq[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm;
+      for (int e = 0; e < 4; ++e) ps4[fb][e] = nq.r * nq.m[fb][e] * nq.inv_nm * einv;
     const float dr = np_backward<F>(nq, dpt[g]);  // dpt[g] now holds dz
     f32x4 dxt[ND] = {};
     rows_x_acc<T, ND, F>(dxt, t_wt, dpt[g]);  // dxt[db][e] = (W^T dz)[16 db + 4 grp + e]
@@ -716,65 +782,29 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
       }
     }
 
-    const long long qc = bhq * d.nC + c;
     if (grp == 0) {
       a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2] = L2;
       a.ld[(bhq * d.nC * 64 + 64LL * c + qrow) * 2 + 1] = qvalid ? delta[g] : 0.f;
     }
-    // phi(q) rows and phi(q)^T are stored times e^{-L}, the factor every key-side use takes
-    T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * F;
+    // phi(q) rows are stored times e^{-L}, like the transposed tile
     {
-      f32x4 ps4[NF];
-#pragma unroll
-      for (int fb = 0; fb < NF; ++fb) ps4[fb] = phq[fb] * einv;
+      T* phqr = static_cast<T*>(a.phiq) + (bhq * d.nC * 64 + 64LL * c + qrow) * F;
 #pragma unroll
       for (int s2 = 0; s2 < F / 32; ++s2) TT::store8(phqr + 32 * s2 + 8 * grp, pk_frag<T>(ps4[2 * s2], ps4[2 * s2 + 1]));
     }
-    T* phqt = static_cast<T*>(a.phiqt) + qc * F * 64;
-    T* qt = static_cast<T*>(a.qt) + qc * D * 64;
-    T* dot = static_cast<T*>(a.dot) + qc * D * 64;
-    if (g > 0) __syncthreads();  // the previous head's tiles and sums are no longer read
-#pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int f = fb * 16 + 4 * grp + e;
-        e_phq[SW::off(f, pq)] = TT::from_f(phq[fb][e] * einv);
-        e_dz[SW::off(f, pq)] = TT::from_f(dpt[g][fb][e]);
-      }
+    const float dlt = qvalid ? delta[g] : 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = ks * 32 + grp * 8 + e;
-        e_do[SW::off(dd, pq)] = do8[ks][e];
-        e_q[SW::off(dd, pq)] = xq8[ks][e];
+      do8[ks] = qvalid ? TT::load8(static_cast<const T*>(a.dout) + qoff + ks * 32 + grp * 8) : TT::zero();
+    if constexpr (NWV == 4) {
+      if (g > 0) __syncthreads();  // the previous head's tiles and sums are no longer read
+      stage_tiles(0, ps4, dpt[g], xq8, do8, dlt);
+      __syncthreads();
+      store_tiles(0, hq);
+      for (int f = tid; f < F; f += NT) {
+        const float v = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
+        ap[F * D + f] = g > 0 ? ap[F * D + f] + v : v;
       }
-    // a_c partial: sum over the head's 64 queries of e^{-L} Delta phi(q)
-#pragma unroll
-    for (int fb = 0; fb < NF; ++fb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = xor_sum_16(phq[fb][e] * einv * (qvalid ? delta[g] : 0.f));
-        if (r16 == 0) s_red[wave][fb * 16 + 4 * grp + e] = v;
-      }
-    __syncthreads();
-    // the transposed tiles to memory in 16-byte pieces
-    for (int idx = tid; idx < F * 8; idx += 256) {
-      const int row = idx >> 3, col = (idx & 7) * 8;
-      TT::store8(phqt + row * 64 + col, SW::load8(e_phq, row, col));
-    }
-    for (int idx = tid; idx < D * 8; idx += 256) {
-      const int row = idx >> 3, col = (idx & 7) * 8;
-      TT::store8(qt + row * 64 + col, SW::load8(e_q, row, col));
-      TT::store8(dot + row * 64 + col, SW::load8(e_do, row, col));
-    }
-    float* ap = a.apart + gc * R;
-    for (int f = tid; f < F; f += 256) {
-      const float v = ((s_red[0][f] + s_red[1][f]) + s_red[2][f]) + s_red[3][f];
-      ap[F * D + f] = g > 0 ? ap[F * D + f] + v : v;
-    }
-    {
       f32x4 acc[F / 64][D / 16];
       tile_x_tile<T, F, D>(acc, e_phq, e_do);  // A_c[f][d] = sum_q e^{-L} phi(q)[f] dout[d]
 #pragma unroll
@@ -787,7 +817,6 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
             *o = g > 0 ? *o + acc[rb][cb][e] : acc[rb][cb][e];
           }
       tile_x_tile<T, F, D>(acc, e_dz, e_q);  // dW[f][d] = sum_q dz[f] q[d]
-      float* wp = a.dwq + gc * (F * D);
 #pragma unroll
       for (int rb = 0; rb < F / 64; ++rb)
 #pragma unroll
@@ -796,6 +825,50 @@ __global__ __launch_bounds__(256, D == 64 ? (QH == 1 ? 3 : 2) : 1) void bwd_dq_k
           for (int e = 0; e < 4; ++e) {
             float* o = wp + ((wave + 4 * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16;
             *o = g > 0 ? *o + acc[rb][cb][e] : acc[rb][cb][e];
+          }
+    } else {
+      // both heads staged at once, then the block-wide part over the two sets; the products
+      // over the staged tiles are split by row block over all eight waves and summed over
+      // the heads in registers
+      __syncthreads();  // W and W^T are no longer read
+      stage_tiles(hsub, ps4, dpt[g], xq8, do8, dlt);
+      __syncthreads();
+      store_tiles(0, hqb);
+      store_tiles(1, hqb + 1);
+      float red8 = 0.f;
+      if (tid < F) {
+#pragma unroll
+        for (int w8 = 0; w8 < NWV; ++w8) red8 += s_red[w8][tid];
+      }
+      constexpr int NRB8 = F / (16 * NWV);
+      f32x4 acc_a[NRB8][D / 16], acc_w[NRB8][D / 16];
+#pragma unroll
+      for (int rb = 0; rb < NRB8; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) acc_a[rb][cb] = acc_w[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int rb = 0; rb < NRB8; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const int row = (wave + NWV * rb) * 16 + r16, col = cb * 16 + r16;
+              const int kc = ks * 32 + grp * 8;
+              Tr<T>::mma(acc_a[rb][cb], SW::load8(e_tile(hs, 0), row, kc), SW::load8(e_tile(hs, 1), col, kc));
+              Tr<T>::mma(acc_w[rb][cb], SW::load8(e_tile(hs, 2), row, kc), SW::load8(e_tile(hs, 3), col, kc));
+            }
+      if (tid < F) ap[F * D + tid] = red8;
+#pragma unroll
+      for (int rb = 0; rb < NRB8; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int o = ((wave + NWV * rb) * 16 + 4 * grp + e) * D + cb * 16 + r16;
+            ap[o] = acc_a[rb][cb][e];
+            wp[o] = acc_w[rb][cb][e];
           }
     }
   }
@@ -1188,10 +1261,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   // double the registers)
   const bool two = bwd_heads_per_wave(sizeof(T) == 2, d.G) == 2;
   const int Gp = two ? d.G / 2 : d.G;  // records of R and dW shares per KV head and chunk
+  // (at D = 128 the pair is one head per group of four waves, so that two waves share a SIMD)
   if constexpr (sizeof(T) == 2) {
-    if (two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 2>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(256), 0, s, a);
+    if (two) {
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1, 8>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 2, 4>), dim3(d.nC * (d.Hq / 2) * d.B), dim3(256), 0, s, a);
+    }
   }
-  if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
+  if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1, 4>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   {
     const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;

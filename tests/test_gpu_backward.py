@@ -105,8 +105,10 @@ def test_backward_matches_oracle(case):
 
 
 CASES_128 = [
-    # name, B, T, Hq, Hkv, w, k (bf16, head_dim = feat_dim = 128)
+    # name, B, T, Hq, Hkv, w, k (bf16, head_dim = feat_dim = 128); even groups take the
+    # query kernel's eight-wave form (two heads per workgroup), odd groups its four-wave form
     ("d128-gqa4-ragged", 1, 333, 8, 2, 64, 16),
+    ("d128-gqa3-ragged", 1, 270, 6, 2, 64, 8),
     ("d128-b2-window16", 2, 200, 4, 1, 16, 8),
     ("d128-k64", 1, 190, 4, 1, 64, 64),
 ]
