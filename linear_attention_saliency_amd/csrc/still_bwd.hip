@@ -349,6 +349,42 @@ __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(const float* apart, c
   }
 }
 
+// The same R_c in one pass where one thread per (b, KV head, element of R) already fills the
+// GPU: each thread runs down all chunks, with U chunks' loads in flight, so the per-chunk sums
+// are read once instead of twice.
+__global__ __launch_bounds__(256) void bwd_rev_full_kernel(const float* apart, float* rst, int nC, int G, int Hkv,
+                                                           int R, long long n_elems) {
+  const long long gid = blockIdx.x * 256LL + threadIdx.x;
+  if (gid >= n_elems) return;
+  const long long e = gid % R, bh = gid / R;
+  const long long b = bh / Hkv, h = bh % Hkv;
+  const long long hq0 = b * Hkv * G + h * G;
+  float* r = rst + bh * nC * R + e;
+  constexpr int U = 8;
+  float acc = 0.f;  // sum over the chunks >= c
+  for (int c0 = nC - 1; c0 >= 0; c0 -= U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const float* p = apart + (hq0 + g) * nC * R + e;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 - u >= 0) x[u] += p[static_cast<long long>(c0 - u) * R];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 - u;
+      if (c >= 0) {
+        acc += x[u];
+        if (c >= 2) r[static_cast<long long>(c - 2) * R] = acc;
+      }
+    }
+  }
+  r[static_cast<long long>(nC - 1) * R] = 0.f;  // no chunk lies two or more after the last two
+  if (nC >= 2) r[static_cast<long long>(nC - 2) * R] = 0.f;
+}
+
 // ---------------------------------------------------------------------------------------
 // QH query heads of one KV head per four waves, 16 queries per wave, the wave taking the same
 // 16 rows of each of its QH heads, so that every K, V and K^T fragment it reads from LDS
@@ -1272,7 +1308,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   }
   if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, F, 1, 4>), dim3(d.nC * d.Hq * d.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
-  {
+  if (ne >= (1LL << 19)) {  // one thread per (b, KV head, element) fills the GPU
+    hipLaunchKernelGGL(bwd_rev_full_kernel, gs, dim3(256), 0, s, a.apart, a.rstate, d.nC, Gp, d.Hkv, R, ne);
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
+  } else {
     const int nseg = (d.nC + kRevSeg - 1) / kRevSeg;
     const long long nr = ne * nseg;
     const dim3 gr(static_cast<unsigned>((nr + 255) / 256));

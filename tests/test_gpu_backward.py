@@ -113,6 +113,8 @@ CASES_128 = [
     # query kernel's eight-wave form (two heads per workgroup), odd groups its four-wave form
     ("d128-gqa4-ragged", 1, 333, 8, 2, 64, 16),
     ("d128-gqa3-ragged", 1, 270, 6, 2, 64, 8),
+    # 2 x 16 KV heads: enough (batch, KV head, element) threads for the one-pass reverse scan
+    ("d128-b2-kv16", 2, 150, 32, 16, 64, 8),
     ("d128-b2-window16", 2, 200, 4, 1, 16, 8),
     ("d128-k64", 1, 190, 4, 1, 64, 64),
 ]
