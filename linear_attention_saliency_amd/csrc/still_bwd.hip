@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T t_k[64 * D];
   __shared__ __attribute__((aligned(16))) T t_v[64 * D];
   __shared__ __attribute__((aligned(16))) T t_vt[D * 64];
+  __shared__ __attribute__((aligned(16))) T t_ph[64 * F];  // phi(k) rows, features pk-permuted
   __shared__ float m2part[4 * 64];
   __shared__ float xn2[64];
   __shared__ int selpos[64];  // position of the chunk's selected key of each rank
@@ -200,12 +201,19 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
   typename TT::frag wf[FPW][D / 32];
   np_map_load_w<T, D, F>(static_cast<const T*>(a.w) + static_cast<long long>(h) * F * D, wf);
   __syncthreads();
-  // V^T (keys pk-permuted) into LDS, K^T into memory
+  // V^T (keys pk-permuted) into LDS, K^T into memory, 8 positions at a time
   T* ktg = static_cast<T*>(a.kt) + (bh * d.nC + c) * (D * 64);
-  for (int e = tid; e < D * 64; e += 256) {
-    const int dd = e >> 6, p = e & 63, row = pk_index(p);
-    t_vt[Swz<T, 64>::off(dd, p)] = t_v[Swz<T, D>::off(row, dd)];
-    ktg[e] = t_k[Swz<T, D>::off(row, dd)];
+  for (int e8 = tid; e8 < D * 8; e8 += 256) {
+    const int dd = e8 >> 3, p0 = (e8 & 7) * 8;
+    typename TT::frag kv, vv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = pk_index(p0 + j);
+      kv[j] = t_k[Swz<T, D>::off(row, dd)];
+      vv[j] = t_v[Swz<T, D>::off(row, dd)];
+    }
+    Swz<T, 64>::store8(t_vt, dd, p0, vv);
+    TT::store8(ktg + dd * 64 + p0, kv);
   }
   f32x4 phi[4][FPW];
   np_map_rows64<T, D, F>(t_k, 0, wf, m2part, xn2, phi);  // synchronises the workgroup
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) phk[(kb * 16 + 4 * grp + i) * F + pk_pos(f)] = TT::from_f(phi[kb][fi][i]);
+      for (int i = 0; i < 4; ++i) t_ph[Swz<T, F>::off(kb * 16 + 4 * grp + i, pk_pos(f))] = TT::from_f(phi[kb][fi][i]);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       TT::store8(phkt + f * 64 + 32 * s + 8 * grp, pk_frag<T>(phi[2 * s][fi], phi[2 * s + 1][fi]));
@@ -240,6 +248,11 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(ust + f * D + db * 16 + 4 * grp) = u[db];
     if (grp == 0) ust[F * D + f] = zs;
+  }
+  __syncthreads();  // the phi(k) rows to memory in 16-byte pieces
+  for (int e8 = tid; e8 < 64 * F / 8; e8 += 256) {
+    const int row = e8 / (F / 8), col = (e8 % (F / 8)) * 8;
+    TT::store8(phk + row * F + col, Swz<T, F>::load8(t_ph, row, col));
   }
   // the selected rows, in position order (compact row c * top_k + rank, as the local-key
   // kernel looks them up), into the compact buffers
@@ -1232,36 +1245,37 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // dW = sum over batch, chunks and the group's query heads (q side) plus keys (k side):
-// gridDim.y slices of the item list, then a fixed-order sum of the slices.
+// gridDim.y slices of the item list, then a fixed-order sum of the slices. A thread takes 4
+// neighbouring elements, so that every load of a wave reads 1 KB in one piece.
 __global__ __launch_bounds__(256) void bwd_dw_part_kernel(const float* dwq, const float* dwk, float* part, int B,
                                                           int Hkv, int G, int nC, int FD) {
-  const int e = blockIdx.x * 256 + threadIdx.x;  // over Hkv * F * D
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // over Hkv * F * D
   const int h = e / FD, fd = e % FD;
   const int nq = B * G * nC, nitems = nq + B * nC;
   const int per = (nitems + gridDim.y - 1) / gridDim.y;
   const int i0 = blockIdx.y * per, i1 = min(nitems, i0 + per);
-  float acc = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   constexpr int U = 8;  // loads of U items in flight together
   for (int it0 = i0; it0 < i1; it0 += U) {
-    float x[U];
+    f32x4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int it = it0 + u;
-      x[u] = 0.f;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (it < i1) {
         if (it < nq) {
           const int b = it / (G * nC), g = (it / nC) % G, c = it % nC;
-          x[u] = dwq[((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * FD + fd];
+          x[u] = *reinterpret_cast<const f32x4*>(dwq + ((static_cast<long long>(b) * Hkv * G + h * G + g) * nC + c) * FD + fd);
         } else {
           const int it2 = it - nq, b = it2 / nC, c = it2 % nC;
-          x[u] = dwk[((static_cast<long long>(b) * Hkv + h) * nC + c) * FD + fd];
+          x[u] = *reinterpret_cast<const f32x4*>(dwk + ((static_cast<long long>(b) * Hkv + h) * nC + c) * FD + fd);
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc += x[u];
   }
-  part[static_cast<long long>(blockIdx.y) * Hkv * FD + e] = acc;
+  *reinterpret_cast<f32x4*>(part + static_cast<long long>(blockIdx.y) * Hkv * FD + e) = acc;
 }
 
 __global__ __launch_bounds__(256) void bwd_dw_sum_kernel(const float* part, float* dw, int n, int nparts) {
@@ -1330,7 +1344,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
   hipLaunchKernelGGL((bwd_dkv_local_kernel<T, D, F>), gk, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
   const int nw = d.Hkv * F * D;
-  hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 256, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
+  hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 1024, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
                      d.Hkv, Gp, d.nC, F * D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dw_sum_kernel, dim3((nw + 255) / 256), dim3(256), 0, s, a.dwpart, a.dw, nw, a.dw_parts);
