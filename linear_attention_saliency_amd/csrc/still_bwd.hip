@@ -122,7 +122,7 @@ __device__ __forceinline__ float np_backward(const NpRow<F>& n, f32x4 (&dphi)[F 
 // stores. Neighbouring threads take neighbouring granules of the same dims, so every store
 // instruction fills whole rows without bank conflicts.
 template <typename T, int D, int F, typename S>
-__device__ __forceinline__ void load_pk_transposed(T* lds, const S* src) {
+__device__ __forceinline__ void load_pk_transposed(T* lds, const S* src, T* rows = nullptr) {
   constexpr int NG = F / 8;
   for (int it = threadIdx.x; it < NG * (D / 8); it += blockDim.x) {
     const int G = it % NG, dd0 = (it / NG) * 8;
@@ -132,18 +132,21 @@ __device__ __forceinline__ void load_pk_transposed(T* lds, const S* src) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const S* row = src + (fb + (e / 4) * 16 + (e % 4)) * D + dd0;
+      typename Tr<T>::frag x;
       if constexpr (sizeof(S) == 4) {
         const f32x4 lo = *reinterpret_cast<const f32x4*>(row), hi = *reinterpret_cast<const f32x4*>(row + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          y[j][e] = Tr<T>::from_f(lo[j]);
-          y[j + 4][e] = Tr<T>::from_f(hi[j]);
+          x[j] = Tr<T>::from_f(lo[j]);
+          x[j + 4] = Tr<T>::from_f(hi[j]);
         }
       } else {
-        const typename Tr<T>::frag x = Tr<T>::load8(row);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y[j][e] = x[j];
+        x = Tr<T>::load8(row);
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j][e] = x[j];
+      // the same 8 elements untransposed, into a Swz<T, D> tile of F rows
+      if (rows != nullptr) Swz<T, D>::store8(rows, fb + (e / 4) * 16 + (e % 4), dd0, x);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) Swz<T, F>::store8(lds, dd0 + j, 8 * G, y[j]);
@@ -1065,8 +1068,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   constexpr int ES = static_cast<int>(sizeof(T));
   constexpr int ND = D / 16, NF = F / 16, R = F * D + F;
   constexpr int SLOT = (D > F ? D : F) * 64;
-  // per step: q rows, dout rows, q^T, dout^T, phi(q) rows, phi(q)^T of one (head, chunk)
-  __shared__ __attribute__((aligned(16))) T lds[6 * SLOT];
+  // per step: q rows, dout rows, q^T, dout^T, phi(q) rows, phi(q)^T of one (head, chunk);
+  // after the steps: R^T, R, W, W^T
+  constexpr int LDS_ELEMS = 6 * SLOT > 4 * D * F ? 6 * SLOT : 4 * D * F;
+  __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) float s_ld[2][64];  // [L, Delta][query]
   const Dims& d = a.d;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1153,15 +1158,33 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
     }
     lds_sync();
   }
+  // The closing products read R_c (rows and transposed), W and W^T from LDS, filled in one
+  // phase: R_c from its fp32 record in one read, W by a copy, W^T transposed from memory.
+  T* const t_rt = lds;              // R^T, D rows of F (features pk-permuted)
+  T* const t_r = lds + D * F;       // R, F rows of D
+  T* const t_wr = lds + 2 * D * F;  // W, F rows of D
+  T* const t_wt = lds + 3 * D * F;  // W^T, D rows of F (features pk-permuted)
+  const bool has_r = c + 2 < d.nC;
+  const float* rs = a.rstate + (bh * d.nC + c) * R;
+  {
+    DmaTile<T, D, F, 4> dmw;
+    dmw.init(D);
+    dmw.issue(t_wr, make_rsrc(W, static_cast<uint32_t>(F * D * ES)), 0);
+  }
+  if (has_r) load_pk_transposed<T, D, F, float>(t_rt, rs, t_r);
+  load_wt<T, D, F>(t_wt, W);
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  __syncthreads();
   // queries of chunks >= c+2 through R_c, r_c (unselected keys only)
-  if (c + 2 < d.nC) {
-    const float* rs = a.rstate + (bh * d.nC + c) * R;
-    f32x4 rv[NF] = {};
-    f32rows_x_frag<T, NF, D>(rv, rs, vf);  // (R v)[16 fb + 4 grp + e]
-    T* const t_rt = lds;                   // R^T, D rows of F (features pk-permuted)
-    __syncthreads();
-    load_pk_transposed<T, D, F, float>(t_rt, rs);
-    __syncthreads();
+  if (has_r) {
+    f32x4 rv[NF];  // (R v)[16 fb + 4 grp + e]
+#pragma unroll
+    for (int rb = 0; rb < F / 64; ++rb) {
+      f32x4 part[4];
+      rows_x_frag<T, D>(part, t_r + rb * 64 * D, vf);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) rv[rb * 4 + blk] = part[blk];
+    }
     const float on = (kvalid && !selj) ? 1.f : 0.f;
 #pragma unroll
     for (int fb = 0; fb < NF; ++fb)
@@ -1195,12 +1218,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   }
   // NP-Map backward and dk, dv
   NpRow<F> nk;
-  np_forward<T, D, F>(nk, W, kf);
+  np_forward<T, D, F, true>(nk, t_wr, kf);
   const float dr = np_backward<F>(nk, dpk);  // dpk now holds dz
-  __syncthreads();
-  T* const t_wt = lds;  // W^T, D rows of F
-  load_wt<T, D, F>(t_wt, W);
-  __syncthreads();
   f32x4 dxt[ND] = {};
   rows_x_acc<T, ND, F>(dxt, t_wt, dpk);
   if (kvalid) {
