@@ -209,10 +209,7 @@ int still_feature_map(const still_config* cfg, const void* x, const void* w_phi,
                       float* phi_out, hipStream_t stream);
 
 /* Bytes of device memory a decode cache of `max_tokens` tokens per sequence needs
- * (0 if the configuration is invalid or unsupported; cfg->seq_len is ignored). A cache whose
- * compact rows of one (sequence, routing head) would pass 2^31 - 1 bytes is unsupported
- * (the kernels address them with 32-bit offsets): bf16 at head_dim 128 and top_k = 64 allows
- * just under 2^23 tokens, proportionally more for smaller top_k. */
+ * (0 if the configuration is invalid or unsupported; cfg->seq_len is ignored). */
 size_t still_cache_bytes(const still_config* cfg, int64_t max_tokens);
 
 /* Carve a cache from `dev_buf` (256-byte aligned, >= still_cache_bytes bytes, owned by the

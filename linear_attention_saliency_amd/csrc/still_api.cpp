@@ -183,10 +183,6 @@ int check_cache_cfg(const still_config* c, int64_t max_tokens) {
   if (st != STILL_OK) return st;
   if (max_tokens < 1 || max_tokens > 0x7fffffffLL) return STILL_ERR_INVALID_ARG;
   if (c->n_q_heads / c->n_kv_heads > kMaxDecodeGroup) return STILL_ERR_UNSUPPORTED;
-  // the kernels address one (b, head)'s compact rows through a buffer resource whose range is
-  // a 32-bit byte count, and index them with signed 32-bit offsets
-  const int64_t sel_bytes = cache_layout(c, max_tokens).sel_capacity * c->head_dim * elem_bytes(c);
-  if (sel_bytes > 0x7fffffffLL) return STILL_ERR_UNSUPPORTED;
   return STILL_OK;
 }
 

@@ -130,23 +130,6 @@ def test_cache_bytes_layout():
     assert lib.still_decode_workspace_bytes(ctypes.byref(cfg), 65600) > 0
 
 
-def test_cache_rejects_compact_rows_past_32bit_range():
-    # one (b, KV head)'s compact rows are read through a 32-bit buffer range: bf16, D = 128,
-    # top_k = 64 keeps every token, so 2^23 tokens are 2^31 bytes of rows, one tile past the
-    # largest cache the library accepts
-    lib = still.load()
-    cfg = _cfg(head_dim=128, feat_dim=128, top_k=64)
-    ok = (1 << 23) - 2 * 64  # an odd tile count just below 2^31 bytes
-    assert lib.still_cache_bytes(ctypes.byref(cfg), ok) > 0
-    for tokens in (1 << 23, 1 << 24, (1 << 31) - 1):
-        assert lib.still_cache_bytes(ctypes.byref(cfg), tokens) == 0
-        out = still.Cache()
-        assert lib.still_cache_init(ctypes.byref(cfg), tokens, ctypes.c_void_p(1 << 20), 1 << 62,
-                                    ctypes.byref(out), None) == -2
-    f32 = _cfg(head_dim=128, feat_dim=128, top_k=64, dtype="f32")
-    assert lib.still_cache_bytes(ctypes.byref(f32), 1 << 22) == 0
-
-
 def test_cache_init_rejects_bad_buffers():
     lib = still.load()
     cfg = _cfg()
