@@ -228,11 +228,34 @@ void prep_kernel(PrepArgs a) {
     if (complete && d.topk > 0) {
       T* vs = static_cast<T*>(a.vselT) + static_cast<long long>(bh) * a.ntiles_sel * D * 64;
       const int nsel = __popcll(smask);
-      for (int idx = tid; idx < d.topk * D; idx += 256) {
-        const int slot = idx / D, dd = idx % D;
-        const long long r = static_cast<long long>(c) * d.topk + slot;  // compact row
-        const T x = slot < nsel ? bandc[SW::off(selpos[slot], dd)] : TT::from_f(0.f);
-        vs[((r / 64) * D + dd) * 64 + pk_pos(static_cast<int>(r % 64))] = x;
+      // The chunk's compact rows r0 .. r0 + topk - 1, by 4-aligned groups: the 4 rows of a
+      // group sit at 4 consecutive columns (pk_pos keeps k & 3), so a lane writes one piece of
+      // up to 4 elements of one V^T row, and the lanes of a row are adjacent. Rows of a group
+      // that belong to a neighbouring chunk are left alone.
+      const long long r0 = static_cast<long long>(c) * d.topk;
+      const long long g_lo = r0 / 4;
+      const int ng = static_cast<int>((r0 + d.topk - 1) / 4 - g_lo) + 1;
+      for (int idx = tid; idx < ng * D; idx += 256) {
+        const int gi = idx % ng, dd = idx / ng;
+        const long long r4 = 4 * (g_lo + gi);  // first compact row of the group
+        typename TT::quad x;
+        bool all = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const long long slot = r4 + j - r0;
+          all = all && slot >= 0 && slot < d.topk;
+          x[j] = slot >= 0 && slot < nsel ? bandc[SW::off(selpos[slot], dd)] : TT::from_f(0.f);
+        }
+        T* dst = vs + ((r4 / 64) * D + dd) * 64 + pk_pos(static_cast<int>(r4 % 64));
+        if (all) {
+          *reinterpret_cast<typename TT::quad*>(dst) = x;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const long long slot = r4 + j - r0;
+            if (slot >= 0 && slot < d.topk) dst[j] = x[j];
+          }
+        }
       }
       // the last compact tile's unused columns are zero (they meet zero weights)
       const long long n_rows = nsel_rows;
