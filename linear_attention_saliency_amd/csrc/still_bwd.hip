@@ -264,16 +264,41 @@ __global__ __launch_bounds__(256) void bwd_kprep_kernel(BwdArgs a) {
     T* ks = static_cast<T*>(a.ksel) + bh * a.ntiles * 64 * D;
     T* vs = static_cast<T*>(a.vsel) + bh * a.ntiles * 64 * D;
     T* kst = static_cast<T*>(a.kselt) + bh * a.ntiles * (D * 64);
-    for (int e = tid; e < d.topk * D; e += 256) {
-      const int r = e / D, dd = e % D;
+    // rows of K and V: 16-byte granules
+    for (int e8 = tid; e8 < d.topk * (D / 8); e8 += 256) {
+      const int r = e8 / (D / 8), col = (e8 % (D / 8)) * 8;
       const bool ok = r < nsel;
       const int pos = ok ? selpos[r] : 0;
-      const T kv = ok ? t_k[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
-      const T vv = ok ? t_v[Swz<T, D>::off(pos, dd)] : TT::from_f(0.f);
-      const int n = c * d.topk + r;
-      ks[static_cast<long long>(n) * D + dd] = kv;
-      vs[static_cast<long long>(n) * D + dd] = vv;
-      kst[(static_cast<long long>(n >> 6) * D + dd) * 64 + pk_pos(n & 63)] = kv;
+      const long long n = static_cast<long long>(c) * d.topk + r;
+      TT::store8(ks + n * D + col, ok ? Swz<T, D>::load8(t_k, pos, col) : TT::zero());
+      TT::store8(vs + n * D + col, ok ? Swz<T, D>::load8(t_v, pos, col) : TT::zero());
+    }
+    // K^T tiles: the 4 rows of a 4-aligned compact-row group sit at 4 consecutive columns
+    // (pk_pos keeps n & 3), so a lane writes one piece of up to 4 elements of one K^T row;
+    // rows of a group that belong to a neighbouring chunk are left alone
+    const long long n0 = static_cast<long long>(c) * d.topk, g_lo = n0 / 4;
+    const int ng = static_cast<int>((n0 + d.topk - 1) / 4 - g_lo) + 1;
+    for (int e = tid; e < ng * D; e += 256) {
+      const int gi = e % ng, dd = e / ng;
+      const long long n4 = 4 * (g_lo + gi);
+      typename TT::quad x;
+      bool all = true;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long long r = n4 + j - n0;
+        all = all && r >= 0 && r < d.topk;
+        x[j] = r >= 0 && r < nsel ? t_k[Swz<T, D>::off(selpos[r], dd)] : TT::from_f(0.f);
+      }
+      T* dst = kst + ((n4 >> 6) * D + dd) * 64 + pk_pos(static_cast<int>(n4 & 63));
+      if (all) {
+        *reinterpret_cast<typename TT::quad*>(dst) = x;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const long long r = n4 + j - n0;
+          if (r >= 0 && r < d.topk) dst[j] = x[j];
+        }
+      }
     }
   }
 }
