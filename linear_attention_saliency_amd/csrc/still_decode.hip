@@ -294,30 +294,60 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
 
   typename Tr<T>::frag wf[DF / 64][D / 32];  // NP-Map weights, loaded early
   np_map_load_w<T, D, DF>(wh, wf);
+  // this thread's share of the prefix state for the read-out of step 5, loaded now so the
+  // loads overlap steps 0-4: column dcol of S, features fh*FQ .. fh*FQ + FQ - 1 (the NFH
+  // feature slices of a column sit in adjacent lanes); z[tid] for tid < DF
+  constexpr int NFH = 256 / D, FQ = DF / NFH;
+  const int fh = tid % NFH, dcol = tid / NFH;
+  float sreg[FQ];
+  {
+    const float* S = a.c.state_s + static_cast<long long>(bh) * DF * D;
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) sreg[j] = S[(fh * FQ + j) * D + dcol];
+  }
+  const float zreg = tid < DF ? a.c.state_z[static_cast<long long>(bh) * DF + tid] : 0.f;
 
-  // 0. stage the ring (and the new token) in LDS; append the token to the ring
-  for (int idx = tid; idx < (RW + 1) * V8; idx += 256) {
-    const int row = idx / V8, c8 = idx % V8;
-    const long long ch = c - BL + row / 64;
-    const int p = row % 64;
-    frag xk = TT::zero(), xv = TT::zero();
-    if (row < 64 * BL) {
-      if (ch >= 0) {
-        xk = TT::load8(ring_k + (slot_of(ch) * 64 + p) * D + c8 * 8);
-        xv = TT::load8(ring_v + (slot_of(ch) * 64 + p) * D + c8 * 8);
+  // 0. stage the ring (and the new token) in LDS; append the token to the ring. The loads of
+  //    up to kBatch pieces per thread are issued before any of them is stored.
+  constexpr int NPIECE = (RW + 1) * V8, NIT = (NPIECE + 255) / 256, kBatch = 8;
+#pragma unroll
+  for (int it0 = 0; it0 < NIT; it0 += kBatch) {
+    frag xk[kBatch], xv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = tid + (it0 + j) * 256;
+      const int row = idx / V8, c8 = idx % V8;
+      const long long ch = c - BL + row / 64;
+      const int p = row % 64;
+      xk[j] = TT::zero();
+      xv[j] = TT::zero();
+      if (it0 + j >= NIT || idx >= NPIECE) continue;
+      if (row < 64 * BL) {
+        if (ch >= 0) {
+          xk[j] = TT::load8(ring_k + (slot_of(ch) * 64 + p) * D + c8 * 8);
+          xv[j] = TT::load8(ring_v + (slot_of(ch) * 64 + p) * D + c8 * 8);
+        }
+      } else if (row < RW && p < r) {
+        xk[j] = TT::load8(ring_k + (slot_cur * 64 + p) * D + c8 * 8);
+        xv[j] = TT::load8(ring_v + (slot_cur * 64 + p) * D + c8 * 8);
+      } else if (row < RW && p == r) {
+        xk[j] = TT::load8(knew + c8 * 8);
+        xv[j] = TT::load8(vnew + c8 * 8);
       }
-    } else if (row < RW && p < r) {
-      xk = TT::load8(ring_k + (slot_cur * 64 + p) * D + c8 * 8);
-      xv = TT::load8(ring_v + (slot_cur * 64 + p) * D + c8 * 8);
-    } else if (row < RW && p == r) {
-      xk = TT::load8(knew + c8 * 8);
-      xv = TT::load8(vnew + c8 * 8);
-      TT::store8(ring_k + (slot_cur * 64 + r) * D + c8 * 8, xk);
-      TT::store8(ring_v + (slot_cur * 64 + r) * D + c8 * 8, xv);
     }
-    SW::store8(kt, row, c8 * 8, xk);
-    if constexpr (L::VT_LDS)
-      if (row < RW) TT::store8(vt + row * D + c8 * 8, xv);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = tid + (it0 + j) * 256;
+      const int row = idx / V8, c8 = idx % V8;
+      if (it0 + j >= NIT || idx >= NPIECE) continue;
+      if (row < RW && row - 64 * BL == r) {
+        TT::store8(ring_k + (slot_cur * 64 + r) * D + c8 * 8, xk[j]);
+        TT::store8(ring_v + (slot_cur * 64 + r) * D + c8 * 8, xv[j]);
+      }
+      SW::store8(kt, row, c8 * 8, xk[j]);
+      if constexpr (L::VT_LDS)
+        if (row < RW) TT::store8(vt + row * D + c8 * 8, xv[j]);
+    }
   }
   for (int idx = tid; idx < G * D; idx += 256) qs[idx] = TT::to_f(q[idx]);
   __syncthreads();
@@ -348,8 +378,8 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   for (int idx = tid; idx < G * DF; idx += 256) {
     const int g = idx / DF, f = idx % DF;
     float z = 0.f;
-#pragma unroll 4
-    for (int c8 = 0; c8 < V8; ++c8) {
+#pragma unroll
+    for (int c8 = 0; c8 < V8; ++c8) {  // all of the row's loads in flight together
       const frag wv = TT::load8(wh + f * D + c8 * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) z += TT::to_f(wv[e]) * qs[g * D + c8 * 8 + e];
@@ -451,9 +481,29 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   __syncthreads();
 
   // 5. merge: ring softmax, the linear-attention entry (log-weight log2 D_LA, value N/D_LA)
-  //    and the compact-cache partials, one shared normaliser
-  const float* S = a.c.state_s + static_cast<long long>(bh) * DF * D;
-  const float* z = a.c.state_z + static_cast<long long>(bh) * DF;
+  //    and the compact-cache partials, one shared normaliser.
+  //    First the prefix state's read-out, phi(q_g)^T S and phi(q_g).z: each thread sums its
+  //    features of one column, the slices of a column are summed across adjacent lanes
+  //    (fixed order), into qs (free after step 4); z goes to m2part, then phi(q_g).z to xn2.
+  float* osl = qs;  // [G][D]
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) acc += phq[g * DF + fh * FQ + j] * sreg[j];
+#pragma unroll
+    for (int m = 1; m < NFH; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (fh == 0) osl[g * D + dcol] = acc;
+  }
+  if (tid < DF) m2part[tid] = zreg;
+  __syncthreads();
+  for (int g = wave; g < G; g += 4) {
+    float x = 0.f;
+    for (int f = lane; f < DF; f += 64) x += phq[g * DF + f] * m2part[f];
+    x = wave_sum(x);
+    if (lane == 0) xn2[g] = x;
+  }
+  __syncthreads();
   T* out = static_cast<T*>(a.out) + static_cast<long long>(b * d.Hq + rh * G) * D;
   const long long rec0 = static_cast<long long>(bh) * a.nsplit * G;
   const int nsplit = a.nsel > 0 ? a.nsplit : 0;
@@ -466,15 +516,11 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
       osa += ex[g * RW + row] * vv;
       ola += wla[g * RW + row] * vv;
     }
-    float dla = gden[g];
-#pragma unroll 16
-    for (int f = 0; f < DF; ++f) {
-      const float pq = phq[g * DF + f];
-      ola += pq * S[f * D + dd];
-      dla += pq * z[f];
-    }
+    ola += osl[g * D + dd];
+    const float dla = gden[g] + xn2[g];
     const float mla = dla > 0.f ? __log2f(dla) : -kInf;
     float M = fmaxf(gmax[g], mla);
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[(rec0 + s * G + g) * 2]);
     float Lsum = 0.f, O = 0.f;
     if (M > -kInf) {
@@ -488,6 +534,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
         Lsum += f;
         O += (ola / dla) * f;
       }
+#pragma unroll 8
       for (int s = 0; s < nsplit; ++s) {
         const float ms = a.part_ml[(rec0 + s * G + g) * 2];
         if (ms > -kInf) {
