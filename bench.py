@@ -76,6 +76,7 @@ def measured_traffic(workload: str, path: str, srcs=ATTN_SRCS):
         return None
     return float(kv["hbm_bytes_per_launch"])
 PEAK_BF16_MFMA = 2.5e15   # dense, FLOP/s
+SETTLE_STEPS = 100        # untimed prefill steps before the timed ones, --warmup included
 PEAK_HBM = 8.0e12         # bytes/s
 
 
@@ -178,7 +179,10 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     # the routing call, the warm-up and the timed steps run back to back; the host-side work
     # count (a few ms of NumPy) comes after the timed region
     call(tq, tk, tv, tw, out, sel_idx=sel)  # the routing the device chooses (for the work count)
-    for _ in range(args.warmup):
+    # clock settling: the GPU's clocks take tens of ms of load to reach their steady state, so
+    # at least SETTLE_STEPS untimed steps run before the timed ones, whatever --warmup asks
+    settle = max(0, SETTLE_STEPS - args.warmup)
+    for _ in range(settle + args.warmup):
         call(tq, tk, tv, tw, out)
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -213,6 +217,7 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
