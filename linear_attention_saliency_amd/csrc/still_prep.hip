@@ -50,8 +50,25 @@ void prep_kernel(PrepArgs a) {
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   const T* w = static_cast<const T*>(a.w);
-  const int c = blockIdx.x;
-  const int bh = blockIdx.y;  // (b, routing head) record
+  // work item: (chunk c, (b, routing head) record bh). Workgroups go to the eight XCDs in turn,
+  // so a one-dimensional grid takes the records in groups of eight (record fastest, then the
+  // chunk, then the group): every chunk of a record runs on the same XCD, right after the
+  // chunk before it, whose key rows (the band's chunk c-1) are then still in that XCD's L2.
+  // A record count that is not a multiple of 8 takes the chunks outermost; a grid too large
+  // for one dimension is launched as (chunks, records).
+  const int BHn = d.B * d.Hr;
+  int c, bh;
+  if (gridDim.y != 1) {
+    c = static_cast<int>(blockIdx.x);
+    bh = static_cast<int>(blockIdx.y);
+  } else if (BHn % 8 == 0) {
+    const int per = d.nC * 8, id = static_cast<int>(blockIdx.x);
+    c = (id % per) / 8;
+    bh = (id / per) * 8 + id % 8;
+  } else {
+    c = static_cast<int>(blockIdx.x) / BHn;
+    bh = static_cast<int>(blockIdx.x) % BHn;
+  }
   const int b = bh / d.Hr, rh = bh % d.Hr, h = rh * d.Gr / d.G;
   // phi(K) and V^T depend on the KV head alone: the first routing head of each KV head writes them
   const long long bkv = static_cast<long long>(b) * d.Hkv + h;
@@ -468,7 +485,9 @@ __global__ __launch_bounds__(256) void feature_map_kernel(Dims d, const void* xv
 
 template <typename T, int D, int DF>
 static hipError_t prep_t(const PrepArgs& a, hipStream_t s) {
-  dim3 grid(a.d.nC, a.d.B * a.d.Hr);
+  // one dimension (records fastest) while its work-item count fits 32 bits
+  const long long items = static_cast<long long>(a.d.nC) * a.d.B * a.d.Hr;
+  const dim3 grid = items * 256 < (1LL << 32) ? dim3(static_cast<unsigned>(items)) : dim3(a.d.nC, a.d.B * a.d.Hr);
   static_assert(kMaxBand == 2, "one prep instantiation per band length");
   if (band_chunks(a.d.window) == 1)
     hipLaunchKernelGGL((prep_kernel<T, D, DF, 1>), grid, dim3(256), 0, s, a);
