@@ -1099,7 +1099,29 @@ __global__ __launch_bounds__(256) void bwd_dkv_local_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) float s_ld[2][64];  // [L, Delta][query]
   const Dims& d = a.d;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // work item (chunk c, record (b, h)). Workgroups go to the eight XCDs in turn, so a
+  // one-dimensional grid takes the records in groups of eight (record fastest, then the chunk,
+  // then the group): chunks c and c + 1 of a record run on one XCD, one after the other, and
+  // the query tiles of chunk c + 1 that both read stay in its L2. Other record counts take the
+  // chunks outermost; a grid too large for one dimension is launched as (chunk, h, b).
+  int c, h, b;
+  {
+    const int BHn = d.B * d.Hkv, id = static_cast<int>(blockIdx.x);
+    int rec;
+    if (gridDim.y != 1 || gridDim.z != 1) {
+      c = id;
+      rec = static_cast<int>(blockIdx.z) * d.Hkv + static_cast<int>(blockIdx.y);
+    } else if (BHn % 8 == 0) {
+      const int per = d.nC * 8;
+      c = (id % per) / 8;
+      rec = (id / per) * 8 + id % 8;
+    } else {
+      c = id / BHn;
+      rec = id % BHn;
+    }
+    b = rec / d.Hkv;
+    h = rec % d.Hkv;
+  }
   const long long bh = static_cast<long long>(b) * d.Hkv + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   constexpr float isd = inv_sqrt_d<D>();
@@ -1385,7 +1407,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(5)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkv_local_kernel<T, D, F>), gk, dim3(256), 0, s, a);
+  {
+    const long long items = static_cast<long long>(d.nC) * d.Hkv * d.B;  // one dimension while it fits
+    const dim3 gl = items * 256 < (1LL << 32) ? dim3(static_cast<unsigned>(items)) : gk;
+    hipLaunchKernelGGL((bwd_dkv_local_kernel<T, D, F>), gl, dim3(256), 0, s, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
   const int nw = d.Hkv * F * D;
   hipLaunchKernelGGL(bwd_dw_part_kernel, dim3(nw / 1024, a.dw_parts), dim3(256), 0, s, a.dwq, a.dwk, a.dwpart, d.B,
