@@ -142,14 +142,12 @@ def cpu_baseline(wl, q, k, v, w, sel_idx) -> dict:
                       f"tokens) in {dt:.1f} s on a host with {os.cpu_count()} CPUs"}
 
 
-def _events(torch, n_steps, per_step):
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(per_step)] for _ in range(n_steps)]
-    stream = torch.cuda.current_stream()
-    for step in evs:  # torch creates the underlying HIP event on first record
-        for e in step:
-            e.record(stream)
+def _events(torch, still, n_steps, per_step):
+    """Timing events (device-scope release, so a record between kernels costs no system-scope
+    cache write-back) and their raw handles for the *_timed entry points."""
+    evs = [[still.TimingEvent() for _ in range(per_step)] for _ in range(n_steps)]
     import ctypes
-    handles = [(ctypes.c_void_p * per_step)(*[e.cuda_event for e in step]) for step in evs]
+    handles = [(ctypes.c_void_p * per_step)(*[e.handle for e in step]) for step in evs]
     torch.cuda.synchronize()
     return evs, handles
 
@@ -168,13 +166,13 @@ def run_prefill(wl, args, torch, still, synth) -> dict:
     stream = torch.cuda.current_stream()
     # inside the timed region only the attention kernel is bracketed (two events per step);
     # the other kernels' durations come from a short untimed pass with all four afterwards
-    evs, handles = _events(torch, args.steps, 2)
+    evs, handles = _events(torch, still, args.steps, 2)
     import ctypes
     attn_only = [(ctypes.c_void_p * 4)(None, None, h[0], h[1]) for h in handles]
     n_side = min(args.steps, 10)
-    side, side_h = _events(torch, n_side, 4)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    side, side_h = _events(torch, still, n_side, 4)
+    t_start = still.TimingEvent()
+    t_end = still.TimingEvent()
     torch.cuda.reset_peak_memory_stats()
     # the routing call, the warm-up and the timed steps run back to back; the host-side work
     # count (a few ms of NumPy) comes after the timed region
@@ -280,9 +278,9 @@ def run_backward(wl, args, torch, still, synth) -> dict:
     for _ in range(args.warmup):
         call(tq, tk, tv, tw, out, tdo, sel, dq, dk, dv, dw)
     stream = torch.cuda.current_stream()
-    evs, handles = _events(torch, args.steps, 8)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    evs, handles = _events(torch, still, args.steps, 8)
+    t_start = still.TimingEvent()
+    t_end = still.TimingEvent()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s_ in range(args.steps):
@@ -336,7 +334,7 @@ def run_fidelity(wl, args, torch, still, synth) -> dict:
     mass = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
         call(tq, tk, mass)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = still.TimingEvent(), still.TimingEvent()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record()
@@ -385,7 +383,7 @@ def run_decode(wl, args, torch, still, synth) -> dict:
     q, k, v, w = synth.make_inputs_device(wl, dev)
     out = torch.empty_like(q)
     call = still.Prefill(q, k, v, w, window=wl.window, top_k=wl.top_k, chunk=C, score=args.score)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = still.TimingEvent(), still.TimingEvent()
     e0.record()
     call(q, k, v, w, out, cache=cache)
     e1.record()
@@ -400,10 +398,10 @@ def run_decode(wl, args, torch, still, synth) -> dict:
     for t in range(args.warmup):
         cache.step(*toks[t], w, out)
     stream = torch.cuda.current_stream()
-    evs, handles = _events(torch, args.steps, 3)
+    evs, handles = _events(torch, still, args.steps, 3)
     pos0 = cache.n_tokens
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t_start = still.TimingEvent()
+    t_end = still.TimingEvent()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):

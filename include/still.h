@@ -259,6 +259,18 @@ int still_decode_step_noalloc(const still_config* cfg, still_cache* cache, const
                               const void* k, const void* v, const void* w_phi, void* out,
                               hipStream_t stream);
 
+/* Timing events for the *_timed entry points and for callers that time the library's work.
+ * They are created with a device-scope release (hipEventReleaseToDevice): recording one
+ * between two kernels does not write back and invalidate the caches at system scope, which a
+ * default event does and which would slow the kernel that follows and lengthen the measured
+ * interval. An elapsed time is valid once the caller has synchronised with the work (device
+ * or stream synchronisation); the events order nothing for other devices or the host.
+ * Each returns STILL_OK, STILL_ERR_INVALID_ARG for a null pointer, or STILL_ERR_HIP. */
+int still_timing_event_create(hipEvent_t* out);
+int still_timing_event_destroy(hipEvent_t ev);
+int still_timing_event_record(hipEvent_t ev, hipStream_t stream);
+int still_timing_event_elapsed_ms(hipEvent_t start, hipEvent_t end, float* ms);
+
 /* Bytes of scratch still_backward needs for `cfg` (0 if cfg is invalid or unsupported). */
 size_t still_backward_workspace_bytes(const still_config* cfg);
 

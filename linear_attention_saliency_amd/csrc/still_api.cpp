@@ -367,6 +367,30 @@ const char* still_status_string(int status) {
 
 int still_last_hip_error(void) { return static_cast<int>(t_last_hip); }
 
+int still_timing_event_create(hipEvent_t* out) {
+  if (!out) return STILL_ERR_INVALID_ARG;
+  STILL_HIP(hipEventCreateWithFlags(out, hipEventReleaseToDevice));
+  return STILL_OK;
+}
+
+int still_timing_event_destroy(hipEvent_t ev) {
+  if (!ev) return STILL_ERR_INVALID_ARG;
+  STILL_HIP(hipEventDestroy(ev));
+  return STILL_OK;
+}
+
+int still_timing_event_record(hipEvent_t ev, hipStream_t stream) {
+  if (!ev) return STILL_ERR_INVALID_ARG;
+  STILL_HIP(hipEventRecord(ev, stream));
+  return STILL_OK;
+}
+
+int still_timing_event_elapsed_ms(hipEvent_t start, hipEvent_t end, float* ms) {
+  if (!start || !end || !ms) return STILL_ERR_INVALID_ARG;
+  STILL_HIP(hipEventElapsedTime(ms, start, end));
+  return STILL_OK;
+}
+
 size_t still_prefill_workspace_bytes(const still_config* cfg) {
   if (check_cfg(cfg, true) != STILL_OK) return 0;
   return ws_layout(cfg).total;

@@ -25,7 +25,9 @@ EXPORTS = ("still_status_string", "still_prefill_workspace_bytes", "still_prefil
            "still_feature_map", "still_cache_bytes", "still_cache_init", "still_decode_workspace_bytes",
            "still_decode_step", "still_decode_step_timed", "still_backward_workspace_bytes", "still_backward",
            "still_backward_timed", "still_future_attention_mass_workspace_bytes", "still_future_attention_mass",
-           "still_selection_overlap", "still_last_hip_error", "still_decode_step_noalloc")
+           "still_selection_overlap", "still_last_hip_error", "still_decode_step_noalloc",
+           "still_timing_event_create", "still_timing_event_destroy", "still_timing_event_record",
+           "still_timing_event_elapsed_ms")
 
 
 class StillError(RuntimeError):
@@ -102,6 +104,14 @@ def load():
     lib.still_selection_overlap.restype = I
     lib.still_decode_step_noalloc.argtypes = [CP, KP, P, P, P, P, P, V]
     lib.still_decode_step_noalloc.restype = I
+    lib.still_timing_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.still_timing_event_create.restype = I
+    lib.still_timing_event_destroy.argtypes = [V]
+    lib.still_timing_event_destroy.restype = I
+    lib.still_timing_event_record.argtypes = [V, V]
+    lib.still_timing_event_record.restype = I
+    lib.still_timing_event_elapsed_ms.argtypes = [V, V, ctypes.POINTER(ctypes.c_float)]
+    lib.still_timing_event_elapsed_ms.restype = I
     lib.still_last_hip_error.argtypes = []
     lib.still_last_hip_error.restype = I
     _lib = lib
@@ -346,6 +356,31 @@ def feature_map(x, w_phi):
     rc = load().still_feature_map(ctypes.byref(cfg), _ptr(x), _ptr(w_phi), _ptr(phi), _stream())
     _check(rc, "still_feature_map")
     return phi
+
+
+class TimingEvent:
+    """A HIP event from still_timing_event_create (device-scope release): for timing the
+    library's kernels without a system-scope cache write-back at every record."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(load().still_timing_event_create(ctypes.byref(h)), "still_timing_event_create")
+        self.handle = h.value
+
+    def record(self, stream=None):
+        _check(load().still_timing_event_record(self.handle, _stream(stream)), "still_timing_event_record")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        """Milliseconds from this event to `end` (both completed: synchronise first)."""
+        ms = ctypes.c_float()
+        _check(load().still_timing_event_elapsed_ms(self.handle, end.handle, ctypes.byref(ms)),
+               "still_timing_event_elapsed_ms")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.still_timing_event_destroy(self.handle)
+            self.handle = None
 
 
 class DecodeCache:
