@@ -214,3 +214,14 @@ def test_routing_override_is_validated_on_the_host():
 def test_last_hip_error_starts_clear():
     lib = still.load()
     assert lib.still_last_hip_error() == 0
+
+
+def test_timing_event_helpers_reject_null_arguments():
+    # argument checks come before any HIP call, so they run without a GPU
+    lib = still.load()
+    assert lib.still_timing_event_create(None) == -1
+    assert lib.still_timing_event_destroy(None) == -1
+    assert lib.still_timing_event_record(None, None) == -1
+    ms = ctypes.c_float()
+    assert lib.still_timing_event_elapsed_ms(None, None, ctypes.byref(ms)) == -1
+    assert lib.still_timing_event_elapsed_ms(ctypes.c_void_p(16), ctypes.c_void_p(32), None) == -1
