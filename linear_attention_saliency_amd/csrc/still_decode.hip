@@ -507,8 +507,17 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
   T* out = static_cast<T*>(a.out) + static_cast<long long>(b * d.Hq + rh * G) * D;
   const long long rec0 = static_cast<long long>(bh) * a.nsplit * G;
   const int nsplit = a.nsel > 0 ? a.nsplit : 0;
+  constexpr int SB = 8;  // split partials loaded ahead of the ring loop (their latency overlaps it)
   for (int idx = tid; idx < G * D; idx += 256) {
     const int g = idx / D, dd = idx % D;
+    float pm[SB], pl[SB], po[SB];
+#pragma unroll
+    for (int s = 0; s < SB; ++s) {
+      const long long rec = rec0 + static_cast<long long>(s) * G + g;
+      pm[s] = s < nsplit ? a.part_ml[rec * 2] : -kInf;
+      pl[s] = s < nsplit ? a.part_ml[rec * 2 + 1] : 0.f;
+      po[s] = s < nsplit ? a.part_o[rec * D + dd] : 0.f;
+    }
     float osa = 0.f, ola = 0.f;
 #pragma unroll 8
     for (int row = 0; row < RW; ++row) {
@@ -520,8 +529,9 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
     const float dla = gden[g] + xn2[g];
     const float mla = dla > 0.f ? __log2f(dla) : -kInf;
     float M = fmaxf(gmax[g], mla);
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[(rec0 + s * G + g) * 2]);
+#pragma unroll
+    for (int s = 0; s < SB; ++s) M = fmaxf(M, pm[s]);
+    for (int s = SB; s < nsplit; ++s) M = fmaxf(M, a.part_ml[(rec0 + s * G + g) * 2]);
     float Lsum = 0.f, O = 0.f;
     if (M > -kInf) {
       if (gmax[g] > -kInf) {
@@ -534,8 +544,15 @@ __global__ __launch_bounds__(256) void decode_token_kernel(DecodeArgs a) {
         Lsum += f;
         O += (ola / dla) * f;
       }
-#pragma unroll 8
-      for (int s = 0; s < nsplit; ++s) {
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        if (pm[s] > -kInf) {
+          const float f = __builtin_amdgcn_exp2f(pm[s] - M);
+          Lsum += pl[s] * f;
+          O += po[s] * f;
+        }
+      }
+      for (int s = SB; s < nsplit; ++s) {
         const float ms = a.part_ml[(rec0 + s * G + g) * 2];
         if (ms > -kInf) {
           const float f = __builtin_amdgcn_exp2f(ms - M);
